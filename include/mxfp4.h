@@ -1,0 +1,190 @@
+/*
+ * libmxfp4 -- block-scaled FP4 (MXFP4: E2M1 x E8M0) expert MLP for AMD MI355X (gfx950).
+ *
+ * C ABI. Every tensor argument is a DEVICE pointer owned by the caller; the
+ * library never allocates device memory, never synchronises the host and never
+ * keeps a pointer after a call returns. Work is enqueued on the caller's HIP
+ * stream (`stream` is a hipStream_t; NULL means the default stream). Tensors are
+ * row-major and contiguous. bf16 tensors are passed as uint16_t bit patterns;
+ * FP4 codes and E8M0/E4M3 scales are raw bytes (a checkpoint's int8 storage is
+ * read as unsigned bytes).
+ *
+ * Formats, from the pages this library is built from:
+ *  - MXFP4 ("2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", sections "Script
+ *    update" item 2 and "FP4 (E2M1) expert weight format confirmed"): a logical
+ *    [R, C] matrix is stored as codes [R, C/2] (two E2M1 codes per byte, element
+ *    2j in the low nibble, code 8 = -0.0) and scales [R, C/32] (one E8M0 byte
+ *    2^(b-127) per row per 32 columns; 0xFF is NaN). Expert weights are w1/w3
+ *    [inter, hidden] and w2 [hidden, inter]; for the pages' model hidden = 7168,
+ *    inter = 3072 (codes [3072, 3584] + scales [3072, 224] -> [3072, 7168]).
+ *  - FP8 block ("Script update" item 1): float8_e4m3fn [R, C] with one E8M0
+ *    scale per 128 x 128 block, scales [ceil(R/128), ceil(C/128)] row-major;
+ *    value = e4m3 * 2^(b-127).
+ *  - NVFP4 (named, not defined, on "Current Bug: vLLM produces empty/garbage
+ *    output", "Revised Plan" Phases 1-2): E2M1 codes as above, one E4M3 scale
+ *    per 16 columns [R, C/16] and a positive fp32 global scale g passed by
+ *    value; value = e2m1 * e4m3 * g.
+ *
+ * The expert MLP ("Current Bug ...", "Revised Plan", Phase 1: L1 GEMM -> SiLU ->
+ * re-quant -> L2 GEMM; the shared expert is the MoE pipeline with one expert and
+ * no routing; Phase 3 keeps the SiLU output and the final scatter in BF16):
+ *      xq = MXFP4(x)                                  per token, per 32 columns
+ *      g  = xq . w1^T,  u = xq . w3^T                 FP4 x FP4, fp32 accumulation
+ *      h  = bf16(silu(g) * u)                         silu(g) = g / (1 + e^-g)
+ *      hq = MXFP4(h)  (or NVFP4(h, g_global))
+ *      y  = bf16(hq . w2^T)
+ * MXFP4(.) is the OCP MX rule: shared exponent floor(log2 amax) - 2 (clamped to
+ * the E8M0 range), E2M1 round to nearest even, saturating at 6, sign kept.
+ * The routed form sums k experts per token: y[t] = bf16(sum_j w[t,j] * y_j(t)).
+ *
+ * Errors: every entry point validates its arguments on the host before it
+ * enqueues anything. On a failed check it enqueues nothing and returns a
+ * non-zero mx_status; mx_last_error() then describes the failure (the text is
+ * per calling thread and stays valid until that thread's next call). A HIP
+ * launch error returns MX_ERR_HIP. Data that can only be checked on the device
+ * is not checked: E8M0 0xFF and E4M3 NaN codes propagate NaN, expert ids
+ * outside [0, E) are skipped (they belong to other ranks), non-finite
+ * activations give unspecified codes.
+ *
+ * Thread safety: calls on different streams may run concurrently; the library
+ * holds no mutable state besides the per-thread error text and the optional
+ * profiler (mx_profile_*), which must not be toggled while other threads call.
+ */
+#ifndef MXFP4_H_
+#define MXFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MX_API __attribute__((visibility("default")))
+#else
+#define MX_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,       /* a required pointer is NULL */
+  MX_ERR_SHAPE = 2,      /* a size is negative, not a required multiple, or too large */
+  MX_ERR_ALIGN = 3,      /* a pointer is not aligned as documented */
+  MX_ERR_FORMAT = 4,     /* format not valid for this entry point */
+  MX_ERR_WORKSPACE = 5,  /* workspace smaller than the matching *_workspace_size() */
+  MX_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
+  MX_ERR_VALUE = 7       /* a scalar argument is out of range (e.g. a non-finite global scale) */
+} mx_status;
+
+typedef enum mx_format {
+  MX_FMT_MXFP4 = 0,      /* E2M1 codes + E8M0 per 1x32 */
+  MX_FMT_FP8_B128 = 1,   /* float8_e4m3fn + E8M0 per 128x128 block (dequant only) */
+  MX_FMT_NVFP4 = 2       /* E2M1 codes + E4M3 per 1x16 + fp32 global scale */
+} mx_format;
+
+/*
+ * mx_dequant -- dequantise a block-scaled matrix to bf16.
+ *   MX_FMT_MXFP4:    codes [rows, cols/2], scales [rows, cols/32]; cols % 32 == 0.
+ *   MX_FMT_FP8_B128: codes [rows, cols] (e4m3fn), scales [ceil(rows/128), ceil(cols/128)];
+ *                    cols % 16 == 0.
+ *   MX_FMT_NVFP4:    codes [rows, cols/2], scales [rows, cols/16] (e4m3fn), global_scale = g;
+ *                    cols % 16 == 0.
+ * global_scale is ignored except for NVFP4. out_bf16 is [rows, cols].
+ * Exact: every MXFP4 and FP8 product is representable in bf16 unless it
+ * overflows (then +-inf); NVFP4 products are rounded to bf16 once (RNE).
+ * Alignment: codes and out_bf16 16 bytes (NVFP4 codes 8 bytes).
+ */
+MX_API mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales, float global_scale,
+                     int64_t rows, int64_t cols, uint16_t* out_bf16, void* stream);
+
+/*
+ * mx_quantize_act -- quantise bf16 activations x [rows, cols] per row.
+ *   MX_FMT_MXFP4: codes [rows, cols/2], scales [rows, cols/32] (E8M0); cols % 32 == 0.
+ *   MX_FMT_NVFP4: codes [rows, cols/2], scales [rows, cols/16] (E4M3), global_scale = g > 0
+ *                 finite and >= 2^-117. Steps in fp32: s = E4M3_RNE_sat(amax / (6 g)),
+ *                 code = E2M1_RNE_sat(x / (s g)); s == 0 gives signed zero codes.
+ * Alignment: x and codes 16 bytes (NVFP4 codes 8 bytes).
+ */
+MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                          float global_scale, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * mx_expert_mlp -- one expert (the shared expert), M tokens, no routing.
+ *   x  [M, hidden] bf16            w1, w3 codes [inter, hidden/2], scales [inter, hidden/32]
+ *   y  [M, hidden] bf16            w2 codes [hidden, inter/2], scales [hidden, inter/32]
+ * hidden % 128 == 0 and inter % 128 == 0. requant is MX_FMT_MXFP4 (NVFP4 is
+ * accepted once the bf16 L2 path exists; until then it returns MX_ERR_FORMAT).
+ * A stacked gate_up tensor [2*inter, hidden/2] is passed as w1 = w13 and
+ * w3 = w13 + inter*hidden/2 (scales likewise).
+ * workspace: device memory of at least mx_expert_mlp_workspace_size() bytes,
+ * 256-byte aligned; its contents are scratch. y must not alias x or workspace.
+ * Alignment: x, y, codes 16 bytes; scales 4 bytes.
+ */
+MX_API mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter,
+                        const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
+                        const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
+                        mx_format requant, float requant_global, uint16_t* y,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+MX_API size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter, mx_format requant);
+
+/*
+ * mx_grouped_expert_mlp -- E local routed experts as a ragged grouped GEMM.
+ *   x        [T, hidden] bf16 tokens
+ *   topk_ids [T, k] int32 expert of each (token, slot); ids outside [0, E) are skipped
+ *   topk_w   [T, k] fp32 gate weight of each (token, slot)
+ *   w1, w3   codes [E, inter, hidden/2], scales [E, inter, hidden/32]
+ *   w2       codes [E, hidden, inter/2], scales [E, hidden, inter/32]
+ *   y        [T, hidden] bf16: y[t] = bf16(sum_j topk_w[t,j] * expert_{ids[t,j]}(x[t]))
+ * Steps: x is quantised once per token; pairs are sorted by expert (stable in
+ * t*k + j order) with a ballot-based scan; the L1 GEMM gathers token rows and
+ * fuses SiLU*up and the re-quantisation; the L2 GEMM multiplies by the gate
+ * weight and writes one bf16 row per pair; a final pass sums each token's k
+ * rows in slot order in fp32 (deterministic: no atomics).
+ * 1 <= k <= E <= 1024; hidden % 128 == 0; inter % 128 == 0.
+ * Alignment as for mx_expert_mlp; topk_ids and topk_w 4 bytes.
+ */
+MX_API mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
+                                const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
+                                const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
+                                const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
+                                mx_format requant, float requant_global, uint16_t* y,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+MX_API size_t mx_grouped_expert_mlp_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k,
+                                            int32_t E, mx_format requant);
+
+/*
+ * mx_debug_gemm_f32 -- test hook, not part of the hot path: C[M, N] = A . B^T in fp32
+ * for MXFP4 A (codes [M, K/2], scales [M, K/32]) and B (codes [N, K/2], scales
+ * [N, K/32]) through the same scaled-MFMA kernel as the MLP. K % 128 == 0,
+ * N % 4 == 0. Alignment: codes and c 16 bytes, scales 4 bytes.
+ */
+MX_API mx_status mx_debug_gemm_f32(const uint8_t* a, const uint8_t* a_s, const uint8_t* b,
+                            const uint8_t* b_s, int64_t M, int64_t N, int64_t K, float* c,
+                            void* stream);
+
+/* Status text (static) and the calling thread's last error detail. */
+MX_API const char* mx_status_string(mx_status s);
+MX_API const char* mx_last_error(void);
+
+/*
+ * Profiler: while enabled, every kernel the library enqueues is bracketed by two
+ * hipEvents recorded on the same stream. mx_profile_stop() waits for them and
+ * returns, per kernel name, the summed duration and the launch count.
+ */
+typedef struct mx_phase_stat {
+  char name[32];
+  double total_ms;
+  int64_t launches;
+} mx_phase_stat;
+
+MX_API mx_status mx_profile_start(void);
+MX_API mx_status mx_profile_stop(mx_phase_stat* stats, int32_t max_stats, int32_t* n_stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H_ */

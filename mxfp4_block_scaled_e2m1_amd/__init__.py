@@ -1,0 +1,16 @@
+"""Block-scaled FP4 (MXFP4: E2M1 x E8M0) expert MLP for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libmxfp4.so`` (C ABI in
+``include/mxfp4.h``); ``binding`` marshals torch device tensors into it.
+"""
+
+from .binding import (  # noqa: F401
+    MxError, debug_gemm_f32, dequant, expert_mlp, expert_mlp_workspace_size, grouped_expert_mlp,
+    grouped_expert_mlp_workspace_size, lib, profile_start, profile_stop, quantize_act,
+)
+
+__all__ = [
+    "MxError", "debug_gemm_f32", "dequant", "expert_mlp", "expert_mlp_workspace_size",
+    "grouped_expert_mlp", "grouped_expert_mlp_workspace_size", "lib", "profile_start",
+    "profile_stop", "quantize_act",
+]

@@ -1,0 +1,187 @@
+"""Thin ctypes binding of libmxfp4 (include/mxfp4.h): argument marshalling only.
+
+Every step of the path runs in the HIP library; this module only turns torch
+device tensors into pointers and the current torch stream into a hipStream_t,
+and raises MxError when the library reports a failure. There is no fallback:
+if the library is missing, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxfp4.so")
+
+MX_FMT = {"mxfp4": 0, "fp8_b128": 1, "nvfp4": 2}
+STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_FORMAT",
+          5: "MX_ERR_WORKSPACE", 6: "MX_ERR_HIP", 7: "MX_ERR_VALUE"}
+
+#: name -> (restype, argtypes) for every symbol declared in include/mxfp4.h
+_P, _I64, _I32, _F, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+
+class PhaseStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("total_ms", ctypes.c_double), ("launches", ctypes.c_int64)]
+
+
+SIGNATURES = {
+    "mx_dequant": (_I32, [_I32, _P, _P, _F, _I64, _I64, _P, _P]),
+    "mx_quantize_act": (_I32, [_I32, _P, _I64, _I64, _F, _P, _P, _P]),
+    "mx_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I32, _F, _P, _P, _SZ, _P]),
+    "mx_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
+    "mx_grouped_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                     _I32, _F, _P, _P, _SZ, _P]),
+    "mx_grouped_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
+    "mx_debug_gemm_f32": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "mx_status_string": (ctypes.c_char_p, [_I32]),
+    "mx_last_error": (ctypes.c_char_p, []),
+    "mx_profile_start": (_I32, []),
+    "mx_profile_stop": (_I32, [ctypes.POINTER(PhaseStat), _I32, ctypes.POINTER(_I32)]),
+}
+
+_lib = None
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+def lib():
+    """Load libmxfp4.so (built in-tree). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mxfp4_block_scaled_e2m1_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MxError(status, lib().mx_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmxfp4 takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmxfp4 takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _fmt(f) -> int:
+    return MX_FMT[f] if isinstance(f, str) else int(f)
+
+
+# ---------------------------------------------------------------------------
+
+def dequant(fmt, codes, scales, rows: int, cols: int, global_scale: float = 0.0, out=None, stream=None):
+    """mx_dequant -> bf16 tensor [rows, cols]."""
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().mx_dequant(_fmt(fmt), _ptr(codes), _ptr(scales), float(global_scale), rows, cols,
+                            _ptr(out), _stream(stream)))
+    return out
+
+
+def quantize_act(fmt, x, global_scale: float = 0.0, codes=None, scales=None, stream=None):
+    """mx_quantize_act: bf16 x [rows, cols] -> (codes [rows, cols/2], scales)."""
+    rows, cols = x.shape
+    f = _fmt(fmt)
+    per = 16 if f == MX_FMT["nvfp4"] else 32
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // per), dtype=torch.uint8, device=x.device)
+    _check(lib().mx_quantize_act(f, _ptr(x), rows, cols, float(global_scale), _ptr(codes), _ptr(scales),
+                                 _stream(stream)))
+    return codes, scales
+
+
+def expert_mlp_workspace_size(M, hidden, inter, requant="mxfp4") -> int:
+    return int(lib().mx_expert_mlp_workspace_size(M, hidden, inter, _fmt(requant)))
+
+
+def grouped_expert_mlp_workspace_size(T, hidden, inter, k, E, requant="mxfp4") -> int:
+    return int(lib().mx_grouped_expert_mlp_workspace_size(T, hidden, inter, k, E, _fmt(requant)))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global: float = 0.0,
+               out=None, workspace=None, stream=None):
+    """mx_expert_mlp: the shared expert on bf16 x [M, hidden] -> bf16 y [M, hidden]."""
+    M, hidden = x.shape
+    inter = w1.shape[0]
+    if out is None:
+        out = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+    nbytes = expert_mlp_workspace_size(M, hidden, inter, requant)
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib().mx_expert_mlp(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s),
+                               _ptr(w2), _ptr(w2s), _fmt(requant), float(requant_global), _ptr(out),
+                               _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def grouped_expert_mlp(x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4",
+                       requant_global: float = 0.0, out=None, workspace=None, stream=None):
+    """mx_grouped_expert_mlp: routed experts, stacked weights [E, ...]."""
+    T, hidden = x.shape
+    k = topk_ids.shape[1]
+    E, inter = w1.shape[0], w1.shape[1]
+    if out is None:
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
+    nbytes = grouped_expert_mlp_workspace_size(T, hidden, inter, k, E, requant)
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib().mx_grouped_expert_mlp(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
+                                       _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2), _ptr(w2s),
+                                       _fmt(requant), float(requant_global), _ptr(out), _ptr(ws),
+                                       ws.numel(), _stream(stream)))
+    return out
+
+
+def debug_gemm_f32(a, a_s, b, b_s, out=None, stream=None):
+    """mx_debug_gemm_f32: C [M, N] = A . B^T for MXFP4 A [M, K/2] and B [N, K/2]."""
+    M, N, K = a.shape[0], b.shape[0], 2 * a.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    _check(lib().mx_debug_gemm_f32(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), M, N, K, _ptr(out),
+                                   _stream(stream)))
+    return out
+
+
+def profile_start():
+    _check(lib().mx_profile_start())
+
+
+def profile_stop():
+    """Returns {kernel name: (total_ms, launches)} for launches since profile_start()."""
+    buf = (PhaseStat * 64)()
+    n = _I32(0)
+    _check(lib().mx_profile_stop(buf, 64, ctypes.byref(n)))
+    return {buf[i].name.decode(): (buf[i].total_ms, int(buf[i].launches)) for i in range(min(n.value, 64))}

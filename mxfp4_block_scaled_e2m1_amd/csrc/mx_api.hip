@@ -1,0 +1,462 @@
+// C-ABI entry points of libmxfp4: host-side validation, workspace layout and
+// kernel sequencing. Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/mxfp4.h"
+#include "mx_internal.h"
+
+using namespace mx;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mx_status fail(mx_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mx_status ok() {
+  g_err[0] = 0;
+  return MX_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ---------------------------------------------------------------- profiler
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler g_prof;
+
+template <class F>
+hipError_t phase(const char* name, hipStream_t s, F&& launch) {
+  if (!g_prof.on) return launch();
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  hipEvent_t a = g_prof.get(), b = g_prof.get();
+  if (a) hipEventRecord(a, s);
+  hipError_t e = launch();
+  if (b) hipEventRecord(b, s);
+  if (a && b) g_prof.recs.push_back({name, a, b});
+  return e;
+}
+
+mx_status hip_fail(hipError_t e, const char* what) {
+  return fail(MX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- workspace
+struct Carve {
+  uint8_t* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base((uint8_t*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  }
+};
+
+struct DenseWs {
+  uint8_t *xq, *xs, *hq, *hs;
+  size_t bytes;
+};
+DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
+  Carve c(base);
+  DenseWs w;
+  w.xq = (uint8_t*)c.take((size_t)(M * H / 2));
+  w.xs = (uint8_t*)c.take((size_t)(M * H / 32));
+  w.hq = (uint8_t*)c.take((size_t)(M * I / 2));
+  w.hs = (uint8_t*)c.take((size_t)(M * I / (rq == MX_FMT_NVFP4 ? 16 : 32)));
+  w.bytes = c.off;
+  return w;
+}
+
+struct GroupWs {
+  uint8_t *xq, *xs, *hq, *hs;
+  uint16_t* o;
+  RouteBuffers rb;
+  size_t bytes;
+};
+GroupWs group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E, mx_format rq) {
+  Carve c(base);
+  GroupWs w;
+  const int64_t P = T * k;
+  const int64_t nblocks = (P + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+  w.xq = (uint8_t*)c.take((size_t)(T * H / 2));
+  w.xs = (uint8_t*)c.take((size_t)(T * H / 32));
+  w.rb.block_counts = (int32_t*)c.take((size_t)(nblocks * E * 4));
+  w.rb.expert_off = (int32_t*)c.take((size_t)(E + 1) * 4);
+  w.rb.tile_base = (int32_t*)c.take((size_t)(E + 1) * 4);
+  w.rb.row_token = (int32_t*)c.take((size_t)P * 4);
+  w.rb.row_slot = (int32_t*)c.take((size_t)P * 4);
+  w.hq = (uint8_t*)c.take((size_t)(P * I / 2));
+  w.hs = (uint8_t*)c.take((size_t)(P * I / (rq == MX_FMT_NVFP4 ? 16 : 32)));
+  w.o = (uint16_t*)c.take((size_t)(P * H * 2));
+  w.bytes = c.off;
+  return w;
+}
+
+// ---------------------------------------------------------------- checks
+mx_status check_mlp_dims(int64_t M, int64_t H, int64_t I) {
+  if (M < 0) return fail(MX_ERR_SHAPE, "token count %lld is negative", (long long)M);
+  if (H < 128 || H % 128 != 0) return fail(MX_ERR_SHAPE, "hidden %lld must be a positive multiple of 128", (long long)H);
+  if (I < 128 || I % 128 != 0) return fail(MX_ERR_SHAPE, "inter %lld must be a positive multiple of 128", (long long)I);
+  if (H > (1 << 20) || I > (1 << 20)) return fail(MX_ERR_SHAPE, "hidden/inter above 2^20");
+  if (M > ((int64_t)1 << 30)) return fail(MX_ERR_SHAPE, "token count %lld above 2^30", (long long)M);
+  return MX_OK;
+}
+
+mx_status check_requant(mx_format rq, float g) {
+  if (rq == MX_FMT_MXFP4) return MX_OK;
+  if (rq == MX_FMT_NVFP4)
+    return fail(MX_ERR_FORMAT, "NVFP4 re-quantisation needs the bf16 L2 path, which this build does not have");
+  (void)g;
+  return fail(MX_ERR_FORMAT, "requant format %d is not MXFP4 or NVFP4", (int)rq);
+}
+
+mx_status check_global(float g) {
+  if (!std::isfinite(g) || !(g >= 0x1p-117f))
+    return fail(MX_ERR_VALUE, "NVFP4 global scale %g must be finite and >= 2^-117", (double)g);
+  return MX_OK;
+}
+
+#define MX_REQUIRE_PTR(p) \
+  do { if ((p) == nullptr) return fail(MX_ERR_NULL, "%s is NULL", #p); } while (0)
+#define MX_REQUIRE_ALIGN(p, a) \
+  do { if (!aligned((p), (a))) return fail(MX_ERR_ALIGN, "%s is not %d-byte aligned", #p, (int)(a)); } while (0)
+#define MX_TRY(expr) \
+  do { mx_status st_ = (expr); if (st_ != MX_OK) return st_; } while (0)
+#define MX_HIP(expr, what) \
+  do { hipError_t e_ = (expr); if (e_ != hipSuccess) return hip_fail(e_, what); } while (0)
+
+GemmArgs base_args() {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(mx_status s) {
+  switch (s) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "null pointer";
+    case MX_ERR_SHAPE: return "bad shape";
+    case MX_ERR_ALIGN: return "misaligned pointer";
+    case MX_ERR_FORMAT: return "unsupported format";
+    case MX_ERR_WORKSPACE: return "workspace too small";
+    case MX_ERR_HIP: return "HIP error";
+    case MX_ERR_VALUE: return "bad value";
+  }
+  return "unknown status";
+}
+
+const char* mx_last_error(void) { return g_err; }
+
+mx_status mx_profile_start(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (auto& r : g_prof.recs) {
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  g_prof.on = true;
+  return ok();
+}
+
+mx_status mx_profile_stop(mx_phase_stat* stats, int32_t max_stats, int32_t* n_stats) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = false;
+  std::vector<mx_phase_stat> agg;
+  mx_status st = MX_OK;
+  for (auto& r : g_prof.recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) st = hip_fail(e, "profiler event");
+    size_t i = 0;
+    for (; i < agg.size(); ++i)
+      if (strcmp(agg[i].name, r.name) == 0) break;
+    if (i == agg.size()) {
+      mx_phase_stat z;
+      memset(&z, 0, sizeof(z));
+      snprintf(z.name, sizeof(z.name), "%s", r.name);
+      agg.push_back(z);
+    }
+    agg[i].total_ms += ms;
+    agg[i].launches += 1;
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  const int n = (int)agg.size() < max_stats ? (int)agg.size() : max_stats;
+  if (stats)
+    for (int i = 0; i < n; ++i) stats[i] = agg[i];
+  if (n_stats) *n_stats = (int32_t)agg.size();
+  if (st == MX_OK) ok();
+  return st;
+}
+
+mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales, float global_scale,
+                     int64_t rows, int64_t cols, uint16_t* out, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (rows < 0 || cols < 0) return fail(MX_ERR_SHAPE, "rows %lld / cols %lld negative", (long long)rows, (long long)cols);
+  if (rows * cols > ((int64_t)1 << 40)) return fail(MX_ERR_SHAPE, "matrix too large");
+  if (fmt == MX_FMT_MXFP4) {
+    if (cols % 32 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 32 != 0", (long long)cols);
+  } else if (fmt == MX_FMT_FP8_B128 || fmt == MX_FMT_NVFP4) {
+    if (cols % 16 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 16 != 0", (long long)cols);
+  } else {
+    return fail(MX_ERR_FORMAT, "unknown format %d", (int)fmt);
+  }
+  if (rows == 0 || cols == 0) return ok();
+  MX_REQUIRE_PTR(codes);
+  MX_REQUIRE_PTR(scales);
+  MX_REQUIRE_PTR(out);
+  MX_REQUIRE_ALIGN(out, 16);
+  hipError_t e;
+  if (fmt == MX_FMT_MXFP4) {
+    MX_REQUIRE_ALIGN(codes, 16);
+    e = phase("dequant_mxfp4", s, [&] {
+      return launch_dequant_mxfp4((const uint8_t*)codes, (const uint8_t*)scales, rows, cols, out, s);
+    });
+  } else if (fmt == MX_FMT_FP8_B128) {
+    MX_REQUIRE_ALIGN(codes, 16);
+    e = phase("dequant_fp8_block", s, [&] {
+      return launch_dequant_fp8_block((const uint8_t*)codes, (const uint8_t*)scales, rows, cols, out, s);
+    });
+  } else {
+    MX_TRY(check_global(global_scale));
+    MX_REQUIRE_ALIGN(codes, 8);
+    e = phase("dequant_nvfp4", s, [&] {
+      return launch_dequant_nvfp4((const uint8_t*)codes, (const uint8_t*)scales, global_scale, rows, cols,
+                                  out, s);
+    });
+  }
+  if (e != hipSuccess) return hip_fail(e, "dequant launch");
+  return ok();
+}
+
+mx_status mx_quantize_act(mx_format fmt, const uint16_t* x, int64_t rows, int64_t cols, float global_scale,
+                          uint8_t* codes, uint8_t* scales, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (rows < 0 || cols < 0) return fail(MX_ERR_SHAPE, "rows %lld / cols %lld negative", (long long)rows, (long long)cols);
+  if (rows * cols > ((int64_t)1 << 40)) return fail(MX_ERR_SHAPE, "matrix too large");
+  if (fmt == MX_FMT_MXFP4) {
+    if (cols % 32 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 32 != 0", (long long)cols);
+  } else if (fmt == MX_FMT_NVFP4) {
+    if (cols % 16 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 16 != 0", (long long)cols);
+    MX_TRY(check_global(global_scale));
+  } else {
+    return fail(MX_ERR_FORMAT, "quantize_act supports MXFP4 and NVFP4, not format %d", (int)fmt);
+  }
+  if (rows == 0 || cols == 0) return ok();
+  MX_REQUIRE_PTR(x);
+  MX_REQUIRE_PTR(codes);
+  MX_REQUIRE_PTR(scales);
+  MX_REQUIRE_ALIGN(x, 16);
+  hipError_t e;
+  if (fmt == MX_FMT_MXFP4) {
+    MX_REQUIRE_ALIGN(codes, 16);
+    e = phase("quant_mxfp4", s, [&] { return launch_quant_mxfp4(x, rows, cols, codes, scales, s); });
+  } else {
+    MX_REQUIRE_ALIGN(codes, 8);
+    e = phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, rows, cols, global_scale, codes, scales, s); });
+  }
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return ok();
+}
+
+size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter, mx_format requant) {
+  if (M < 0 || hidden < 0 || inter < 0) return 0;
+  return dense_ws(nullptr, M, hidden, inter, requant).bytes;
+}
+
+size_t mx_grouped_expert_mlp_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k, int32_t E,
+                                            mx_format requant) {
+  if (T < 0 || hidden < 0 || inter < 0 || k < 1 || E < 1) return 0;
+  return group_ws(nullptr, T, hidden, inter, k, E, requant).bytes;
+}
+
+static mx_status check_weights(const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
+                               const uint8_t* w2, const uint8_t* w2_s) {
+  MX_REQUIRE_PTR(w1);
+  MX_REQUIRE_PTR(w1_s);
+  MX_REQUIRE_PTR(w3);
+  MX_REQUIRE_PTR(w3_s);
+  MX_REQUIRE_PTR(w2);
+  MX_REQUIRE_PTR(w2_s);
+  MX_REQUIRE_ALIGN(w1, 16);
+  MX_REQUIRE_ALIGN(w3, 16);
+  MX_REQUIRE_ALIGN(w2, 16);
+  MX_REQUIRE_ALIGN(w1_s, 4);
+  MX_REQUIRE_ALIGN(w3_s, 4);
+  MX_REQUIRE_ALIGN(w2_s, 4);
+  return MX_OK;
+}
+
+mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, const uint8_t* w1,
+                        const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s, const uint8_t* w2,
+                        const uint8_t* w2_s, mx_format requant, float requant_global, uint16_t* y,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MX_TRY(check_mlp_dims(M, hidden, inter));
+  MX_TRY(check_requant(requant, requant_global));
+  if (M == 0) return ok();
+  MX_REQUIRE_PTR(x);
+  MX_REQUIRE_PTR(y);
+  MX_REQUIRE_ALIGN(x, 16);
+  MX_REQUIRE_ALIGN(y, 16);
+  MX_TRY(check_weights(w1, w1_s, w3, w3_s, w2, w2_s));
+  const size_t need = mx_expert_mlp_workspace_size(M, hidden, inter, requant);
+  MX_REQUIRE_PTR(workspace);
+  MX_REQUIRE_ALIGN(workspace, 256);
+  if (ws_bytes < need)
+    return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  DenseWs w = dense_ws(workspace, M, hidden, inter, requant);
+  const int H = (int)hidden, I = (int)inter, m = (int)M;
+
+  MX_HIP(phase("quant_x", s, [&] { return launch_quant_mxfp4(x, M, hidden, w.xq, w.xs, s); }), "quant_x");
+
+  GemmArgs l1 = base_args();
+  l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
+  l1.n_rows = I; l1.k = H;
+  l1.x = w.xq; l1.x_s = w.xs;
+  l1.m_rows = m; l1.n_experts = 1;
+  l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
+  l1.grid_tiles = ((m + BM - 1) / BM) * l1.n_tiles;
+  l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_global = requant_global;
+  MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(EPI_SWIGLU_MXFP4, l1, l1.grid_tiles, s); }), "l1_gemm");
+
+  GemmArgs l2 = base_args();
+  l2.wa = w2; l2.wa_s = w2_s;
+  l2.n_rows = H; l2.k = I;
+  l2.x = w.hq; l2.x_s = w.hs;
+  l2.m_rows = m; l2.n_experts = 1;
+  l2.n_tiles = (H + BN - 1) / BN;
+  l2.grid_tiles = ((m + BM - 1) / BM) * l2.n_tiles;
+  l2.out_bf16 = y;
+  MX_HIP(phase("l2_gemm", s, [&] { return launch_gemm(EPI_BF16, l2, l2.grid_tiles, s); }), "l2_gemm");
+  return ok();
+}
+
+mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
+                                const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
+                                const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
+                                const uint8_t* w2, const uint8_t* w2_s, mx_format requant, float requant_global,
+                                uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MX_TRY(check_mlp_dims(T, hidden, inter));
+  MX_TRY(check_requant(requant, requant_global));
+  if (E < 1 || E > ROUTE_MAX_EXPERTS) return fail(MX_ERR_SHAPE, "E %d outside [1, %d]", E, ROUTE_MAX_EXPERTS);
+  if (k < 1 || k > E) return fail(MX_ERR_SHAPE, "k %d outside [1, E=%d]", k, E);
+  if (T * (int64_t)k > ((int64_t)1 << 30)) return fail(MX_ERR_SHAPE, "T*k above 2^30");
+  if (T == 0) return ok();
+  MX_REQUIRE_PTR(x);
+  MX_REQUIRE_PTR(y);
+  MX_REQUIRE_PTR(topk_ids);
+  MX_REQUIRE_PTR(topk_w);
+  MX_REQUIRE_ALIGN(x, 16);
+  MX_REQUIRE_ALIGN(y, 16);
+  MX_REQUIRE_ALIGN(topk_ids, 4);
+  MX_REQUIRE_ALIGN(topk_w, 4);
+  MX_TRY(check_weights(w1, w1_s, w3, w3_s, w2, w2_s));
+  const size_t need = mx_grouped_expert_mlp_workspace_size(T, hidden, inter, k, E, requant);
+  MX_REQUIRE_PTR(workspace);
+  MX_REQUIRE_ALIGN(workspace, 256);
+  if (ws_bytes < need)
+    return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  GroupWs w = group_ws(workspace, T, hidden, inter, k, E, requant);
+  const int H = (int)hidden, I = (int)inter;
+  const int64_t P = T * k;
+  const int max_mtiles = (int)((P + (int64_t)E * (BM - 1)) / BM);
+
+  MX_HIP(phase("quant_x", s, [&] { return launch_quant_mxfp4(x, T, hidden, w.xq, w.xs, s); }), "quant_x");
+  MX_HIP(phase("route", s, [&] { return launch_route(topk_ids, T, k, E, w.rb, s); }), "route");
+
+  GemmArgs l1 = base_args();
+  l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
+  l1.w_estride = (int64_t)I * H / 2; l1.ws_estride = (int64_t)I * H / 32;
+  l1.n_rows = I; l1.k = H;
+  l1.x = w.xq; l1.x_s = w.xs; l1.row_token = w.rb.row_token;
+  l1.expert_off = w.rb.expert_off; l1.tile_base = w.rb.tile_base; l1.n_experts = E;
+  l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
+  l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_global = requant_global;
+  MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(EPI_SWIGLU_MXFP4, l1, max_mtiles * l1.n_tiles, s); }),
+         "l1_gemm");
+
+  GemmArgs l2 = base_args();
+  l2.wa = w2; l2.wa_s = w2_s;
+  l2.w_estride = (int64_t)H * I / 2; l2.ws_estride = (int64_t)H * I / 32;
+  l2.n_rows = H; l2.k = I;
+  l2.x = w.hq; l2.x_s = w.hs;
+  l2.expert_off = w.rb.expert_off; l2.tile_base = w.rb.tile_base; l2.n_experts = E;
+  l2.n_tiles = (H + BN - 1) / BN;
+  l2.out_bf16 = w.o; l2.row_slot = w.rb.row_slot; l2.slot_weight = topk_w;
+  MX_HIP(phase("l2_gemm", s, [&] { return launch_gemm(EPI_BF16, l2, max_mtiles * l2.n_tiles, s); }), "l2_gemm");
+
+  MX_HIP(phase("combine", s, [&] { return launch_combine(w.o, topk_ids, T, k, E, H, y, s); }), "combine");
+  return ok();
+}
+
+mx_status mx_debug_gemm_f32(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                            int64_t M, int64_t N, int64_t K, float* c, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (M < 0 || N < 0 || K < 0) return fail(MX_ERR_SHAPE, "negative size");
+  if (K < 128 || K % 128 != 0) return fail(MX_ERR_SHAPE, "K %lld must be a positive multiple of 128", (long long)K);
+  if (N % 4 != 0) return fail(MX_ERR_SHAPE, "N %lld %% 4 != 0", (long long)N);
+  if (M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30) || K > (1 << 20)) return fail(MX_ERR_SHAPE, "too large");
+  if (M == 0 || N == 0) return ok();
+  MX_REQUIRE_PTR(a);
+  MX_REQUIRE_PTR(a_s);
+  MX_REQUIRE_PTR(b);
+  MX_REQUIRE_PTR(b_s);
+  MX_REQUIRE_PTR(c);
+  MX_REQUIRE_ALIGN(a, 16);
+  MX_REQUIRE_ALIGN(b, 16);
+  MX_REQUIRE_ALIGN(c, 16);
+  MX_REQUIRE_ALIGN(a_s, 4);
+  MX_REQUIRE_ALIGN(b_s, 4);
+  GemmArgs g = base_args();
+  g.wa = b; g.wa_s = b_s;
+  g.n_rows = (int)N; g.k = (int)K;
+  g.x = a; g.x_s = a_s;
+  g.m_rows = (int)M; g.n_experts = 1;
+  g.n_tiles = (int)((N + BN - 1) / BN);
+  g.grid_tiles = (int)((M + BM - 1) / BM) * g.n_tiles;
+  g.c_f32 = c;
+  MX_HIP(phase("debug_gemm", s, [&] { return launch_gemm(EPI_F32, g, g.grid_tiles, s); }), "debug_gemm");
+  return ok();
+}
+
+}  // extern "C"

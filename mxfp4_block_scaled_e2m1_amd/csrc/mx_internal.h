@@ -1,0 +1,96 @@
+// Internal interfaces between the C-ABI layer (mx_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mx {
+
+// ---- GEMM tile geometry (block-scaled FP4 MFMA kernels) --------------------
+// One workgroup computes BN weight rows x BM token rows; the K loop moves
+// BK logical columns (BK/2 bytes per row) per LDS stage.
+constexpr int BN = 256;
+constexpr int BM = 128;
+constexpr int BK = 256;
+constexpr int NSTAGE = 3;
+constexpr int GEMM_THREADS = 256;
+constexpr int L1_J_PER_TILE = BN / 2;    // L1 tiles hold gate and up rows for 128 j
+
+// Epilogue kinds of the scaled-MFMA GEMM.
+enum Epilogue : int {
+  EPI_F32 = 0,          // C[m][n] fp32 (test hook)
+  EPI_SWIGLU_MXFP4 = 1, // L1: h = bf16(silu(g) * u) -> MXFP4 codes + E8M0 per 32 j
+  EPI_SWIGLU_NVFP4 = 2, // L1: h -> NVFP4 codes + E4M3 per 16 j (fp32 global)
+  EPI_BF16 = 3,         // L2: y[m][n] = bf16(acc) (dense) or o[slot][n] = bf16(w * acc) (grouped)
+};
+
+struct GemmArgs {
+  // MFMA A operand: weight rows (MXFP4). For L1 `wa` is w1 (gate) and `wb`
+  // is w3 (up); otherwise `wb` is null. Expert e starts at w + e * w_estride.
+  const uint8_t* wa;
+  const uint8_t* wa_s;
+  const uint8_t* wb;
+  const uint8_t* wb_s;
+  int64_t w_estride;    // bytes between experts' code matrices
+  int64_t ws_estride;   // bytes between experts' scale matrices
+  int n_rows;           // logical weight rows per matrix (inter for L1, hidden for L2)
+  int k;                // logical K (multiple of 128)
+
+  // MFMA B operand: token rows (MXFP4) [rows, k/2] + [rows, k/32].
+  const uint8_t* x;
+  const uint8_t* x_s;
+  const int32_t* row_token;   // grouped L1: sorted row -> token; null = identity
+
+  // Row groups: grouped mode has expert_off/tile_base on the device;
+  // dense mode (expert_off == null) is a single group of m_rows rows.
+  const int32_t* expert_off;  // [E+1] first sorted row of each expert
+  const int32_t* tile_base;   // [E+1] first m-tile of each expert
+  int n_experts;
+  int m_rows;                 // dense mode rows
+  int n_tiles;                // tiles along the weight rows
+  int grid_tiles;             // dense: exact count of tiles
+
+  // Outputs.
+  float* c_f32;               // EPI_F32: [m_rows, n_rows]
+  uint8_t* h_codes;           // L1: [rows, n_rows/2]
+  uint8_t* h_scales;          // L1: [rows, n_rows/32] (MXFP4) or [rows, n_rows/16] (NVFP4)
+  float nv_global;            // L1 NVFP4 global scale
+  uint16_t* out_bf16;         // EPI_BF16: dense y [m_rows, n_rows]; grouped o [slots, n_rows]
+  const int32_t* row_slot;    // grouped L2: sorted row -> slot (t*k + j)
+  const float* slot_weight;   // grouped L2: gate weight per slot
+};
+
+hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int grid, hipStream_t s);
+
+// ---- Elementwise kernels ---------------------------------------------------
+hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                int64_t cols, uint16_t* out, hipStream_t s);
+hipError_t launch_dequant_fp8_block(const uint8_t* q, const uint8_t* scales, int64_t rows,
+                                    int64_t cols, uint16_t* out, hipStream_t s);
+hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, float global,
+                                int64_t rows, int64_t cols, uint16_t* out, hipStream_t s);
+hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, float global,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
+
+// ---- Routing ----------------------------------------------------------------
+constexpr int ROUTE_CHUNK = 1024;    // pairs per counting/scatter block
+constexpr int ROUTE_MAX_EXPERTS = 1024;
+
+struct RouteBuffers {
+  int32_t* block_counts;   // [nblocks, E]
+  int32_t* expert_off;     // [E+1]
+  int32_t* tile_base;      // [E+1]
+  int32_t* row_token;      // [P]
+  int32_t* row_slot;       // [P]
+};
+
+hipError_t launch_route(const int32_t* topk_ids, int64_t tokens, int k, int n_experts,
+                        const RouteBuffers& rb, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* o, const int32_t* topk_ids, int64_t tokens, int k,
+                          int n_experts, int hidden, uint16_t* y, hipStream_t s);
+
+}  // namespace mx

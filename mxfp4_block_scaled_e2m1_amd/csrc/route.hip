@@ -1,0 +1,160 @@
+// Token -> expert permutation for the routed experts, and the weighted un-permute.
+//
+// The routed MoE adds routing, top-k and a scatter to the shared-expert pipeline
+// (page "Current Bug: vLLM produces empty/garbage output", section "Revised
+// Plan", Phase 1, which describes the shared expert as the MoE pipeline minus
+// those steps; 48 local experts per rank in "Config values"; the final scatter
+// stays in BF16 per Phase 3). Router logits and top-k selection are inputs.
+//
+// Route: pairs p = t*k + j (token t, slot j) are ordered by expert, and by p
+// within an expert (stable). Three small kernels:
+//   1. per-chunk expert histogram (LDS counters),
+//   2. one-block scan: per-chunk bases, expert offsets, per-expert m-tile bases,
+//   3. scatter: one wave per chunk walks its pairs 64 at a time in order; lanes
+//      with the same expert find their rank with a wave ballot + popcount of the
+//      lanes below them, and the first lane advances the expert's running count.
+// Ids outside [0, E) belong to experts on other ranks and are skipped.
+#include "mx_device.h"
+#include "mx_internal.h"
+
+namespace mx {
+
+namespace {
+
+__global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                     int32_t* __restrict__ block_counts) {
+  __shared__ int cnt[ROUTE_MAX_EXPERTS];
+  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * ROUTE_CHUNK;
+  for (int i = threadIdx.x; i < ROUTE_CHUNK; i += 256) {
+    const int64_t p = base + i;
+    if (p < P) {
+      const int e = ids[p];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) block_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(256) void k_route_scan(int32_t* __restrict__ block_counts, int nblocks, int E,
+                                                    int32_t* __restrict__ expert_off,
+                                                    int32_t* __restrict__ tile_base) {
+  __shared__ int tot[ROUTE_MAX_EXPERTS];
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int s = 0;
+    for (int b = 0; b < nblocks; ++b) {
+      const int c = block_counts[(int64_t)b * E + e];
+      block_counts[(int64_t)b * E + e] = s;   // becomes the chunk's base within expert e
+      s += c;
+    }
+    tot[e] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int off = 0, tiles = 0;
+    for (int e = 0; e < E; ++e) {
+      expert_off[e] = off;
+      tile_base[e] = tiles;
+      off += tot[e];
+      tiles += (tot[e] + BM - 1) / BM;
+    }
+    expert_off[E] = off;
+    tile_base[E] = tiles;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_route_scatter(const int32_t* __restrict__ ids, int64_t P, int k, int E,
+                                                      const int32_t* __restrict__ block_base,
+                                                      const int32_t* __restrict__ expert_off,
+                                                      int32_t* __restrict__ row_token,
+                                                      int32_t* __restrict__ row_slot) {
+  __shared__ int run[ROUTE_MAX_EXPERTS];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) run[e] = expert_off[e] + block_base[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * ROUTE_CHUNK;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = 0; i0 < ROUTE_CHUNK; i0 += 64) {
+    const int64_t p = base + i0 + lane;
+    const int e = (p < P) ? ids[p] : -1;
+    const bool valid = (p < P) && ((unsigned)e < (unsigned)E);
+    uint64_t todo = __ballot(valid);
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int ee = __shfl(e, leader);
+      const bool mine = valid && (e == ee);
+      const uint64_t m = __ballot(mine);
+      const int start = run[ee];
+      if (mine) {
+        const int pos = start + __popcll(m & below);
+        row_token[pos] = (int)(p / k);
+        row_slot[pos] = (int)p;
+      }
+      __syncthreads();   // single wave: orders the read of run[ee] before the update
+      if (lane == leader) run[ee] = start + __popcll(m);
+      __syncthreads();
+      todo &= ~m;
+    }
+  }
+}
+
+// y[t][n] = bf16( sum_j o[t*k + j][n] ) over slots j with a local expert, in j order.
+// o rows already carry the gate weight. One thread per 8 columns (16 bytes).
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
+                                                 const int32_t* __restrict__ ids, int64_t T, int k,
+                                                 int E, int H, uint16_t* __restrict__ y) {
+  const int per_row = H >> 3;
+  const int64_t n = T * per_row;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const int64_t t = i / per_row;
+    const int c = (int)(i - t * per_row) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[t * k + j];
+      if ((unsigned)e >= (unsigned)E) continue;
+      const uint4 v = *(const uint4*)(o + (t * k + j) * (int64_t)H + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(w[q] & 0xFFFFu);
+        acc[2 * q + 1] += bf16_to_f32(w[q] >> 16);
+      }
+    }
+    uint32_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = f32_to_bf16_rne(acc[2 * q]) | (f32_to_bf16_rne(acc[2 * q + 1]) << 16);
+    *(uint4*)(y + t * (int64_t)H + c) = make_uint4(r[0], r[1], r[2], r[3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const int32_t* topk_ids, int64_t tokens, int k, int n_experts,
+                        const RouteBuffers& rb, hipStream_t s) {
+  const int64_t P = tokens * k;
+  const int nblocks = (int)((P + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
+  if (nblocks > 0) {
+    k_route_count<<<nblocks, 256, 0, s>>>(topk_ids, P, n_experts, rb.block_counts);
+  }
+  k_route_scan<<<1, 256, 0, s>>>(rb.block_counts, nblocks, n_experts, rb.expert_off, rb.tile_base);
+  if (nblocks > 0) {
+    k_route_scatter<<<nblocks, 64, 0, s>>>(topk_ids, P, k, n_experts, rb.block_counts, rb.expert_off,
+                                           rb.row_token, rb.row_slot);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t* o, const int32_t* topk_ids, int64_t tokens, int k,
+                          int n_experts, int hidden, uint16_t* y, hipStream_t s) {
+  const int64_t n = tokens * (hidden / 8);
+  if (n == 0) return hipSuccess;
+  int64_t g = (n + 255) / 256;
+  if (g > 16384) g = 16384;
+  k_combine<<<(int)g, 256, 0, s>>>(o, topk_ids, tokens, k, n_experts, hidden, y);
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every symbol include/mxfp4.h declares, and
+its host-side validation rejects bad arguments before touching the GPU (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"MX_API\s+[\w\s\*]+?\b(mx_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mxfp4_block_scaled_e2m1_amd import binding, build
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding.lib()
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared())
+    for n in ("mx_dequant", "mx_quantize_act", "mx_expert_mlp", "mx_grouped_expert_mlp"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from mxfp4_block_scaled_e2m1_amd import binding
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert name in binding.SIGNATURES, name
+
+
+def _err(L):
+    return L.mx_last_error().decode()
+
+
+def test_status_strings(L):
+    assert L.mx_status_string(0) == b"ok"
+    assert L.mx_status_string(5) == b"workspace too small"
+
+
+def test_dequant_validation(L):
+    assert L.mx_dequant(0, None, None, 0.0, 4, 33, None, None) == 2 and "32" in _err(L)
+    assert L.mx_dequant(0, None, None, 0.0, 4, 64, None, None) == 1 and "codes" in _err(L)
+    assert L.mx_dequant(9, None, None, 0.0, 4, 64, None, None) == 4
+    assert L.mx_dequant(1, None, None, 0.0, 4, 24, None, None) == 2
+    assert L.mx_dequant(0, None, None, 0.0, -1, 64, None, None) == 2
+    assert L.mx_dequant(0, None, None, 0.0, 0, 64, None, None) == 0      # empty: nothing to do
+    # misaligned output pointer (never dereferenced: validation fails first)
+    assert L.mx_dequant(0, ctypes.c_void_p(16), ctypes.c_void_p(16), 0.0, 1, 64, ctypes.c_void_p(8), None) == 3
+    assert L.mx_dequant(2, ctypes.c_void_p(16), ctypes.c_void_p(16), float("nan"), 1, 64,
+                        ctypes.c_void_p(16), None) == 7
+
+
+def test_quantize_validation(L):
+    assert L.mx_quantize_act(1, None, 4, 64, 0.0, None, None, None) == 4        # FP8 is dequant-only
+    assert L.mx_quantize_act(0, None, 4, 48, 0.0, None, None, None) == 2
+    assert L.mx_quantize_act(2, None, 4, 64, 0.0, None, None, None) == 7        # NVFP4 needs g > 0
+    assert L.mx_quantize_act(2, None, 4, 64, float("inf"), None, None, None) == 7
+    assert L.mx_quantize_act(2, None, 4, 64, 1e-40, None, None, None) == 7
+    assert L.mx_quantize_act(0, None, 4, 64, 0.0, None, None, None) == 1
+
+
+def test_mlp_validation(L):
+    P = ctypes.c_void_p
+    z = [P(256)] * 6
+    # hidden not a multiple of 128
+    assert L.mx_expert_mlp(P(256), 4, 200, 128, *z, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
+    assert L.mx_expert_mlp(P(256), 4, 256, 96, *z, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
+    # NVFP4 re-quant is refused by this build, unknown formats too
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 2, 1.0, P(256), P(256), 1 << 30, None) == 4
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 1, 0.0, P(256), P(256), 1 << 30, None) == 4
+    # workspace too small
+    need = L.mx_expert_mlp_workspace_size(4, 256, 128, 0)
+    assert need > 0
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 0, 0.0, P(256), P(256), need - 1, None) == 5
+    # misaligned workspace, null weights
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 0, 0.0, P(256), P(128), need, None) == 3
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, None, *z[1:], 0, 0.0, P(256), P(256), need, None) == 1
+    # zero tokens is a no-op
+    assert L.mx_expert_mlp(None, 0, 256, 128, *([None] * 6), 0, 0.0, None, None, 0, None) == 0
+
+
+def test_grouped_validation(L):
+    P = ctypes.c_void_p
+    z = [P(256)] * 6
+    args = lambda k, E, ws: (P(256), 8, 256, 128, P(256), P(256), k, E, *z, 0, 0.0, P(256), P(256), ws, None)
+    assert L.mx_grouped_expert_mlp(*args(0, 4, 1 << 30)) == 2
+    assert L.mx_grouped_expert_mlp(*args(5, 4, 1 << 30)) == 2
+    assert L.mx_grouped_expert_mlp(*args(2, 2000, 1 << 30)) == 2
+    need = L.mx_grouped_expert_mlp_workspace_size(8, 256, 128, 2, 4, 0)
+    assert L.mx_grouped_expert_mlp(*args(2, 4, need - 1)) == 5
+    # workspace grows with tokens and with k
+    a = L.mx_grouped_expert_mlp_workspace_size(64, 256, 128, 2, 4, 0)
+    b = L.mx_grouped_expert_mlp_workspace_size(128, 256, 128, 2, 4, 0)
+    c = L.mx_grouped_expert_mlp_workspace_size(64, 256, 128, 4, 4, 0)
+    assert b > a and c > a
+
+
+def test_debug_gemm_validation(L):
+    P = ctypes.c_void_p
+    assert L.mx_debug_gemm_f32(P(256), P(256), P(256), P(256), 4, 6, 256, P(256), None) == 2
+    assert L.mx_debug_gemm_f32(P(256), P(256), P(256), P(256), 4, 8, 64, P(256), None) == 2
+    assert L.mx_debug_gemm_f32(None, P(256), P(256), P(256), 4, 8, 256, P(256), None) == 1
+    assert L.mx_debug_gemm_f32(P(257), P(256), P(256), P(256), 4, 8, 256, P(256), None) == 3

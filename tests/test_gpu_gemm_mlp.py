@@ -1,0 +1,145 @@
+"""Parity of the scaled-MFMA GEMM, the shared expert and the routed experts with the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import assert_mlp_close, assert_requant_close, bf16_t, bits, t
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import mxfp4_block_scaled_e2m1_amd as m
+    return m
+
+
+def _ws_slices(ws, M, H, I):
+    """Dense workspace layout of mx_expert_mlp: xq, xs, hq, hs, each 256-byte aligned."""
+    off, out = 0, []
+    for n in (M * H // 2, M * H // 32, M * I // 2, M * I // 32):
+        out.append(ws[off:off + n])
+        off += (n + 255) // 256 * 256
+    return out
+
+
+# ---------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("M,N,K", [(16, 256, 256), (130, 300, 384), (257, 512, 7168), (64, 7168, 3072),
+                                   (200, 3072, 128), (1, 4, 256)])
+def test_debug_gemm_f32(mx, M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    a, a_s = W.mxfp4_weight(rng, M, K)
+    b, b_s = W.mxfp4_weight(rng, N, K)
+    c = mx.debug_gemm_f32(t(a), t(a_s), t(b), t(b_s)).cpu().numpy().astype(np.float64)
+    ref = O.gemm_f64(O.mxfp4_dequant_f64(a, a_s), O.mxfp4_dequant_f64(b, b_s))
+    err = np.linalg.norm(c - ref) / np.linalg.norm(ref)
+    assert err <= 1e-5, err
+
+
+# ---------------------------------------------------------------- shared expert
+def _run_dense(mx, d, M, H, I):
+    x = d["x"]
+    nbytes = mx.expert_mlp_workspace_size(M, H, I)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = mx.expert_mlp(bf16_t(x), *(t(d[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")), workspace=ws)
+    torch.cuda.synchronize()
+    return bits(y), _ws_slices(ws, M, H, I)
+
+
+def test_tiny_expert_mlp(mx):
+    d = W.tiny_mlp(0)
+    y, (xq, xs, hq, hs) = _run_dense(mx, d, 16, 256, 128)
+    ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
+    assert np.array_equal(xq.cpu().numpy().reshape(16, 128), inter["xq"])
+    assert np.array_equal(xs.cpu().numpy().reshape(16, 8), inter["xs"])
+    assert_requant_close(hq.cpu().numpy().reshape(16, 64), hs.cpu().numpy().reshape(16, 4), inter["hq"], inter["hs"])
+    assert_mlp_close(y, ref)
+
+
+@pytest.mark.parametrize("M", [1, 8, 128, 300])
+def test_shared_expert_real_shape(mx, M):
+    d = W.shared_expert(M, seed=0)
+    y, (_, _, hq, hs) = _run_dense(mx, d, M, 7168, 3072)
+    ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
+    assert_requant_close(hq.cpu().numpy().reshape(M, 1536), hs.cpu().numpy().reshape(M, 96), inter["hq"], inter["hs"])
+    assert_mlp_close(y, ref)
+
+
+def test_shared_expert_prefill_sampled_rows(mx):
+    M = 4096
+    d = W.shared_expert(M, seed=0)
+    y, _ = _run_dense(mx, d, M, 7168, 3072)
+    rows = np.random.default_rng(3).choice(M, 24, replace=False)
+    ref = O.expert_mlp(d["x"][rows], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"])
+    assert_mlp_close(y[rows], ref)
+    assert np.all(np.isfinite(((y.astype(np.uint32) << 16).view(np.float32))))
+
+
+# ---------------------------------------------------------------- routed experts
+def _run_grouped(mx, d):
+    y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]),
+                              *(t(d[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")))
+    torch.cuda.synchronize()
+    return bits(y)
+
+
+def _oracle_grouped(d, tokens=None):
+    return O.grouped_expert_mlp(d["x"], d["ids"], d["w"], d["w1"], d["w1s"], d["w3"], d["w3s"],
+                                d["w2"], d["w2s"], tokens=tokens)
+
+
+def test_grouped_multi_tile(mx):
+    d = W.grouped(tokens=600, n_experts=8, k=4, seed=5, hidden=512, inter=256)
+    y = _run_grouped(mx, d)
+    assert_mlp_close(y, _oracle_grouped(d))
+
+
+def test_grouped_single_expert_equals_shared(mx):
+    d = W.shared_expert(200, seed=2, hidden=512, inter=256)
+    g = {n: d[n][None] for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")}
+    g["x"] = d["x"]
+    g["ids"] = np.zeros((200, 1), np.int32)
+    g["w"] = np.ones((200, 1), np.float32)
+    yg = _run_grouped(mx, g)
+    yd, _ = _run_dense(mx, d, 200, 512, 256)
+    assert np.array_equal(yg, yd)
+
+
+def test_grouped_permutation_empty_and_foreign_ids(mx):
+    d = W.grouped(tokens=300, n_experts=6, k=3, seed=9, hidden=256, inter=128)
+    d["ids"][d["ids"] == 5] = 4                 # expert 5 empty; duplicates within a token allowed
+    y = _run_grouped(mx, d)
+    perm = np.random.default_rng(1).permutation(300)
+    dp = dict(d, x=d["x"][perm], ids=d["ids"][perm], w=d["w"][perm])
+    yp = _run_grouped(mx, dp)
+    assert np.array_equal(yp, y[perm])
+    # ids outside [0, E) contribute nothing
+    d2 = dict(d, ids=d["ids"].copy())
+    d2["ids"][:, 2] = -1
+    d2["ids"][::2, 1] = 6
+    y2 = _run_grouped(mx, d2)
+    assert_mlp_close(y2, _oracle_grouped(d2))
+
+
+def test_grouped_headline_sampled_tokens(mx):
+    d = W.grouped(tokens=4096, n_experts=48, k=8, seed=0)
+    y = _run_grouped(mx, d)
+    tok = np.array([0, 1, 2, 4095])
+    assert_mlp_close(y[tok], _oracle_grouped(d, tokens=tok))
+    assert np.all(np.isfinite(((y.astype(np.uint32) << 16).view(np.float32))))
+
+
+def test_grouped_skewed_sampled_tokens(mx):
+    d = W.skewed(tokens=16384, seed=0)
+    counts = np.bincount(d["ids"].ravel(), minlength=48)
+    assert (counts == 0).sum() >= 1 and counts.max() > 4 * counts.mean()
+    y = _run_grouped(mx, d)
+    tok = np.array([7, 16383])
+    assert_mlp_close(y[tok], _oracle_grouped(d, tokens=tok))
+    # decode tail of 8 tokens over the same weights
+    tail = dict(d, x=d["x"][:8], ids=d["ids"][:8], w=d["w"][:8])
+    yt = _run_grouped(mx, tail)
+    assert_mlp_close(yt, _oracle_grouped(tail))
