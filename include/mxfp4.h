@@ -142,7 +142,7 @@ MX_API size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t in
  * fuses SiLU*up and the re-quantisation; the L2 GEMM multiplies by the gate
  * weight and writes one bf16 row per pair; a final pass sums each token's k
  * rows in slot order in fp32 (deterministic: no atomics).
- * 1 <= k <= E <= 1024; hidden % 128 == 0; inter % 128 == 0.
+ * 1 <= k <= E <= 512; hidden % 128 == 0; inter % 128 == 0.
  * Alignment as for mx_expert_mlp; topk_ids and topk_w 4 bytes.
  */
 MX_API mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,

@@ -11,21 +11,28 @@
 // SiLU, re-quant, L2 GEMM; Phase 3 keeps the SiLU output and the final scatter
 // in BF16).
 //
-// Design (gfx950):
-//  * One workgroup = 4 waves = a 256 (weight rows) x 128 (token rows) tile; each
-//    wave owns 128 x 64 = 4 x 2 MFMA blocks of 32 x 32 (128 fp32 accumulators).
+// Design (gfx950, one 512-thread workgroup per CU, two waves per SIMD):
+//  * Workgroup tile 256 weight rows x 256 token rows. Each of the 8 waves owns
+//    128 x 64 = 4 x 2 MFMA blocks of 32 x 32 (128 fp32 accumulators per lane).
+//    At FP4 rate the tile needs 32 B/clk/CU of operand bytes from L2.
 //  * The packed layout is already the MFMA operand layout: a lane holds 32
-//    consecutive K values of one row (16 bytes) and that block's E8M0 byte. Over a
-//    256-wide K stage, lane half h takes 32-column chunks 4h..4h+3 in its four
-//    MFMA steps, so each lane's scales for a stage are one aligned dword and the
-//    step index is the byte select (op_sel) of the instruction. Both operands
-//    use the same K order, so the sum is unchanged.
+//    consecutive K values of one row (16 bytes) and that block's E8M0 byte.
+//    A 256-wide K stage is four MFMA steps; in step s lane half h takes the
+//    32-column chunk 4h + s, so the lane's four scale bytes for the stage are one
+//    aligned dword and s is the byte select (op_sel) of the instruction.
+//    Both operands use the same K order, so the sum is unchanged.
 //  * Global -> LDS with GLOBAL_LOAD_LDS_DWORDX4 (16 B per lane, no VGPR staging),
-//    3 LDS stages in flight (51 KB each). Rows are 128 B in LDS; the 16-byte
-//    chunk c of row r sits at slot c ^ ((r >> 1) & 7) so that the 16 rows read
-//    by a quarter-wave spread over all banks.
+//    issued by one wave per SIMD while its partner wave keeps issuing MFMAs,
+//    2 LDS slots of 68 KB: each copy brings whole 128-byte lines (8 rows x 128 B
+//    per wave instruction), which doubles the bytes per outstanding L1 miss
+//    compared with half-line copies. LDS rows are 128 B; chunk c of row r sits at
+//    slot c ^ ((r >> 1) & 7) so the 16 rows a quarter-wave reads hit distinct banks.
+//  * Operand fragments are double-buffered in registers: the LDS reads of the
+//    next step are interleaved with the MFMAs of the current one.
 //  * blockIdx -> tile mapping is XCD aware: consecutive tiles (the m-tiles of one
 //    expert's weight n-tile) land on the same XCD and share its L2.
+#include <atomic>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -34,16 +41,25 @@ namespace mx {
 namespace {
 
 constexpr int ROW_BYTES = BK / 2;                     // 128 code bytes per row per stage
+constexpr int SC_BYTES = BK / 32;                     // 8 scale bytes per row per stage
 constexpr int W_BYTES = BN * ROW_BYTES;               // 32768
-constexpr int X_BYTES = BM * ROW_BYTES;               // 16384
-constexpr int WS_BYTES = BN * (BK / 32);              // 2048
-constexpr int XS_BYTES = BM * (BK / 32);              // 1024
+constexpr int X_BYTES = BM * ROW_BYTES;               // 32768
+constexpr int WS_BYTES = BN * SC_BYTES;               // 2048
+constexpr int XS_BYTES = BM * SC_BYTES;               // 2048
 constexpr int OFF_X = W_BYTES;
 constexpr int OFF_WS = W_BYTES + X_BYTES;
 constexpr int OFF_XS = OFF_WS + WS_BYTES;
-constexpr int STAGE_BYTES = OFF_XS + XS_BYTES;        // 52224
-constexpr int VM_PER_STAGE = 8 + 4 + 2 + 1;           // global_load_lds per thread per stage
+constexpr int STAGE_BYTES = OFF_XS + XS_BYTES;        // 69632
+constexpr int NWAVES = GEMM_THREADS / 64;             // 8: 2 along weight rows x 4 along tokens
+constexpr int W_DMA = W_BYTES / 1024 / NWAVES;        // 16-byte copies per wave per stage (W)
+constexpr int X_DMA = X_BYTES / 1024 / NWAVES;
+constexpr int VM_PER_STAGE = W_DMA + X_DMA + 2;       // + two dword copies of the scale tiles
+static_assert(VM_PER_STAGE == 10, "the vmcnt immediate below assumes 10 copies per stage");
+static_assert(NSTAGE == 2, "the pipeline below is written for 2 LDS slots");
+static_assert(WS_BYTES + XS_BYTES == GEMM_THREADS * 8, "two scale dwords per thread per stage");
 
+// Zero bytes for the upper half of a K stage when K % 256 == 128: zero codes with
+// zero scale bytes (2^-127) contribute exactly 0 to every sum.
 __device__ __attribute__((aligned(256))) uint8_t g_zero_page[256];
 
 struct Tile {
@@ -53,17 +69,16 @@ struct Tile {
   int rows;      // valid rows in the token tile
 };
 
-// Returns false when this workgroup has no tile.
-__device__ __forceinline__ bool map_tile(const GemmArgs& a, Tile& t) {
-  const int b = blockIdx.x;
-  const int xcd = b & 7, local = b >> 3;
-  int total;
-  if (a.expert_off == nullptr) total = a.grid_tiles;
-  else total = a.tile_base[a.n_experts] * a.n_tiles;
-  const int per = (total + 7) >> 3;
-  if (local >= per) return false;
-  const int L = xcd * per + local;
-  if (L >= total) return false;
+// Number of tiles of this launch (device-side for the routed experts).
+__device__ __forceinline__ int tile_count(const GemmArgs& a) {
+  if (a.expert_off == nullptr) return a.grid_tiles;
+  return a.tile_base[a.n_experts] * a.n_tiles;
+}
+
+// Tile L of the launch. Tiles are ordered (expert, n-tile, m-tile) with the
+// m-tile fastest, so consecutive tiles share their weight rows.
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& a, int L) {
+  Tile t;
   if (a.expert_off == nullptr) {
     const int mtiles = (a.m_rows + BM - 1) / BM;
     t.e = 0;
@@ -71,7 +86,7 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& a, Tile& t) {
     const int mt = L - t.nt * mtiles;
     t.row0 = mt * BM;
     t.rows = min(BM, a.m_rows - t.row0);
-    return true;
+    return t;
   }
   // expert e with tile_base[e] * n_tiles <= L < tile_base[e + 1] * n_tiles
   int lo = 0, hi = a.n_experts - 1;
@@ -89,14 +104,14 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& a, Tile& t) {
   const int off = a.expert_off[e];
   t.row0 = off + mt * BM;
   t.rows = min(BM, a.expert_off[e + 1] - t.row0);
-  return true;
+  return t;
 }
 
 // Global -> LDS copies. Lane i of the wave writes LDS bytes [m0 + i*size, +size).
 // They are issued as inline asm so that the compiler neither waits for them
 // before every LDS read nor at every barrier: the K loop waits for exactly the
-// stage it needs (s_waitcnt vmcnt) before its barrier. Code the compiler emits
-// itself can only wait longer because of them, never shorter.
+// stage it needs (s_waitcnt vmcnt) before its barrier. Waits the compiler
+// emits for its own loads can only become longer because of them, never shorter.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_off)
                : "memory", "m0");
@@ -109,55 +124,67 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-// One 64-wide K step of a wave's 4 x 2 block of 32 x 32 MFMAs from LDS stage `sb`.
-// S selects both the 32-column chunk (4*hh + S) and the scale byte (op_sel).
-template <int S>
-__device__ __forceinline__ void mfma_step(const uint8_t* sb, int wrow_off, int xrow_off, int hh, int swz,
-                                          const uint32_t (&sa)[4], const uint32_t (&sbx)[2],
-                                          f32x16 (&acc)[4][2]) {
-  const int coff = ((hh * 4 + S) ^ swz) * 16;
-  i32x8 A[4], B[2];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const uint4 v = *(const uint4*)(sb + wrow_off + f * 32 * ROW_BYTES + coff);
-    A[f] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const uint4 v = *(const uint4*)(sb + xrow_off + g * 32 * ROW_BYTES + coff);
-    B[g] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int f = 0; f < 4; ++f)
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-      acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[f], B[g], acc[f][g], 4, 4, S,
-                                                                 (int)sa[f], S, (int)sbx[g]);
+struct Frags {
+  uint4 A[4];   // weight rows wn*128 + f*32 + r32: 32 K values (16 bytes) each
+  uint4 B[2];   // token rows wm*64 + g*32 + r32
+};
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *(const uint4*)p; }
+
+__device__ __forceinline__ i32x8 opnd(const uint4& v) {
+  return i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
 }
 
+// The eight MFMAs of K step S (chunk 4*hh + S, scale byte S) from `cur`,
+// interleaved with the six LDS reads that fill `nxt` for the next step (when
+// READ), so that the reads issue while the matrix core is busy.
+template <int S, bool READ>
+__device__ __forceinline__ void k_step(const Frags& cur, Frags& nxt, const uint8_t* sbn, int coffn,
+                                       int wrow_off, int xrow_off, const uint32_t (&sa)[4],
+                                       const uint32_t (&sb)[2], f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd(cur.A[f]), opnd(cur.B[g]), acc[f][g], 4,
+                                                                 4, S, (int)sa[f], S, (int)sb[g]);
+      const int i = f * 2 + g;   // 0..7: reads after MFMAs 0..5
+      if (READ && i < 6) {
+        if (i < 4) nxt.A[i] = lds16(sbn + wrow_off + i * 32 * ROW_BYTES + coffn);
+        else nxt.B[i - 4] = lds16(sbn + xrow_off + (i - 4) * 32 * ROW_BYTES + coffn);
+      }
+    }
+  }
+  if (READ) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
+// One 256 x 256 output tile: K loop and epilogue. All LDS reads and copies of
+// the tile have completed when it returns.
 template <int EPI>
-__global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE_BYTES];
-
-  Tile t;
-  if (!map_tile(a, t)) return;
-
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint8_t* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave >> 2, wm = wave & 3;
   const int K = a.k;
   const int kb = K >> 1;                    // code bytes per row
   const int ks = K >> 5;                    // scale bytes per row
   const int nst = (K + BK - 1) / BK;
-  const bool half_tail = (K % BK) != 0;     // last stage holds 128 columns only
-  const bool l1 = (EPI == EPI_SWIGLU_MXFP4 || EPI == EPI_SWIGLU_NVFP4);
+  const bool half_tail = (K % BK) != 0;     // the last stage holds 128 columns only
+  constexpr bool l1 = (EPI == EPI_SWIGLU_MXFP4 || EPI == EPI_SWIGLU_NVFP4);
 
   const uint8_t* wa = a.wa + (int64_t)t.e * a.w_estride;
   const uint8_t* wa_s = a.wa_s + (int64_t)t.e * a.ws_estride;
   const uint8_t* wb = l1 ? a.wb + (int64_t)t.e * a.w_estride : nullptr;
   const uint8_t* wb_s = l1 ? a.wb_s + (int64_t)t.e * a.ws_estride : nullptr;
 
-  // ---- per-thread source rows for the stage loads ----
+  // ---- per-thread source rows of the stage copies ----
   // W tile row R -> (matrix, row). L1: R = wn*128 + f*32 + r holds gate rows
   // (f = 0, 1) and up rows (f = 2, 3) of the same j = j0 + wn*64 + (f&1)*32 + r.
   auto w_row = [&](int R, const uint8_t*& base, const uint8_t*& sbase) -> int {
@@ -179,64 +206,57 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
     return a.row_token ? a.row_token[r] : r;
   };
 
-  const uint8_t* wsrc[8];
-  int wchunk[8];
-  for (int i = 0; i < 8; ++i) {
-    const int q = wave * 8 + i;
-    const int R = q * 8 + (lane >> 3);
+  // Copy (wave, i) writes LDS bytes [(wave*W_DMA + i) * 1024, +1024): rows q*8 + lane/8,
+  // 16-byte slot lane%8 holding chunk (lane%8) ^ ((row >> 1) & 7).
+  const uint8_t* wsrc[W_DMA];
+  bool whi[W_DMA];   // chunk in the upper half of the stage (columns 128..255)
+#pragma unroll
+  for (int i = 0; i < W_DMA; ++i) {
+    const int R = (wave * W_DMA + i) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((R >> 1) & 7);
     const uint8_t *base, *sbase;
     const int row = w_row(R, base, sbase);
     wsrc[i] = base + (int64_t)row * kb + c * 16;
-    wchunk[i] = c;
+    whi[i] = c >= 4;
   }
-  const uint8_t* xsrc[4];
-  int xchunk[4];
-  for (int i = 0; i < 4; ++i) {
-    const int q = wave * 4 + i;
-    const int R = q * 8 + (lane >> 3);
+  const uint8_t* xsrc[X_DMA];
+  bool xhi[X_DMA];
+#pragma unroll
+  for (int i = 0; i < X_DMA; ++i) {
+    const int R = (wave * X_DMA + i) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((R >> 1) & 7);
     xsrc[i] = a.x + (int64_t)x_token(R) * kb + c * 16;
-    xchunk[i] = c;
+    xhi[i] = c >= 4;
   }
-  const uint8_t* wssrc[2];
-  int wshalf[2];
-  for (int i = 0; i < 2; ++i) {
-    const int d = (wave * 2 + i) * 64 + lane;
+  // Scale tiles (8 bytes per row per stage): thread tid copies dword tid & 1 of
+  // weight row tid / 2 and of token row tid / 2.
+  const uint8_t *wssrc, *xssrc;
+  {
+    const int tid = wave * 64 + lane;
     const uint8_t *base, *sbase;
-    const int row = w_row(d >> 1, base, sbase);
-    wssrc[i] = sbase + (int64_t)row * ks + (d & 1) * 4;
-    wshalf[i] = d & 1;
+    const int row = w_row(tid >> 1, base, sbase);
+    wssrc = sbase + (int64_t)row * ks + (tid & 1) * 4;
+    xssrc = a.x_s + (int64_t)x_token(tid >> 1) * ks + (tid & 1) * 4;
   }
-  const int dxs = wave * 64 + lane;
-  const uint8_t* xssrc = a.x_s + (int64_t)x_token(dxs >> 1) * ks + (dxs & 1) * 4;
-  const int xshalf = dxs & 1;
 
   const uint32_t lds0 = lds_addr(smem);
+  const bool shi = (lane & 1) != 0;   // scale dword of columns 128..255
   auto issue = [&](int st) {
     const uint32_t sb = lds0 + (st % NSTAGE) * STAGE_BYTES;
-    const bool tail = half_tail && st == nst - 1;
     const int ko = st * ROW_BYTES;
-    const int kso = st * (BK / 32);
+    const bool tail = half_tail && st == nst - 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const void* src = (tail && wchunk[i] >= 4) ? (const void*)g_zero_page : (const void*)(wsrc[i] + ko);
-      lds_dma16(src, sb + (wave * 8 + i) * 1024);
-    }
+    for (int i = 0; i < W_DMA; ++i)
+      lds_dma16((tail && whi[i]) ? (const void*)g_zero_page : (const void*)(wsrc[i] + ko),
+                sb + (wave * W_DMA + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const void* src = (tail && xchunk[i] >= 4) ? (const void*)g_zero_page : (const void*)(xsrc[i] + ko);
-      lds_dma16(src, sb + OFF_X + (wave * 4 + i) * 1024);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const void* src = (tail && wshalf[i]) ? (const void*)g_zero_page : (const void*)(wssrc[i] + kso);
-      lds_dma4(src, sb + OFF_WS + (wave * 2 + i) * 256);
-    }
-    {
-      const void* src = (tail && xshalf) ? (const void*)g_zero_page : (const void*)(xssrc + kso);
-      lds_dma4(src, sb + OFF_XS + wave * 256);
-    }
+    for (int i = 0; i < X_DMA; ++i)
+      lds_dma16((tail && xhi[i]) ? (const void*)g_zero_page : (const void*)(xsrc[i] + ko),
+                sb + OFF_X + (wave * X_DMA + i) * 1024);
+    lds_dma4((tail && shi) ? (const void*)g_zero_page : (const void*)(wssrc + st * SC_BYTES),
+             sb + OFF_WS + wave * 256);
+    lds_dma4((tail && shi) ? (const void*)g_zero_page : (const void*)(xssrc + st * SC_BYTES),
+             sb + OFF_XS + wave * 256);
   };
 
   f32x16 acc[4][2];
@@ -252,32 +272,58 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
   const int swz = (r32 >> 1) & 7;
   const int wrow_off = (wn * 128 + r32) * ROW_BYTES;
   const int xrow_off = OFF_X + (wm * 64 + r32) * ROW_BYTES;
-  const int wsc_off = OFF_WS + (wn * 128 + r32) * 8 + hh * 4;
-  const int xsc_off = OFF_XS + (wm * 64 + r32) * 8 + hh * 4;
+  const int wsc_off = OFF_WS + (wn * 128 + r32) * SC_BYTES + hh * 4;
+  const int xsc_off = OFF_XS + (wm * 64 + r32) * SC_BYTES + hh * 4;
+  int coff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) coff[q] = ((hh * 4 + q) ^ swz) * 16;
 
+  auto read_scales = [&](const uint8_t* sb, uint32_t (&sa)[4], uint32_t (&sx)[2]) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sa[f] = *(const uint32_t*)(sb + wsc_off + f * 32 * SC_BYTES);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) sx[g] = *(const uint32_t*)(sb + xsc_off + g * 32 * SC_BYTES);
+  };
+
+  // Prologue: stages 0 and 1 in flight; wait for stage 0 and read its first step.
   issue(0);
-  if (nst > 1) issue(1);
+  if (nst > 1) {
+    issue(1);
+    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+
+  Frags F0, F1;
+  uint32_t sa[4], sx[2];
+  read_scales(smem, sa, sx);
+#pragma unroll
+  for (int f = 0; f < 4; ++f) F0.A[f] = lds16(smem + wrow_off + f * 32 * ROW_BYTES + coff[0]);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) F0.B[g] = lds16(smem + xrow_off + g * 32 * ROW_BYTES + coff[0]);
 
   for (int st = 0; st < nst; ++st) {
-    // Stage st has landed once at most one younger stage (15 copies) is in flight;
-    // the barrier then publishes every wave's copies and retires the reads of the
-    // slot that the next issue overwrites (their MFMAs consumed them already).
-    if (st + 1 < nst) asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    static_assert(VM_PER_STAGE == 15, "vmcnt immediate above assumes 15 loads per stage");
-    if (st + 2 < nst) issue(st + 2);
-
     const uint8_t* sb = smem + (st % NSTAGE) * STAGE_BYTES;
-    uint32_t sa[4], sbx[2];
+    k_step<0, true>(F0, F1, sb, coff[1], wrow_off, xrow_off, sa, sx, acc);
+    k_step<1, true>(F1, F0, sb, coff[2], wrow_off, xrow_off, sa, sx, acc);
+    k_step<2, true>(F0, F1, sb, coff[3], wrow_off, xrow_off, sa, sx, acc);
+    if (st + 1 < nst) {
+      // Every read of this slot has been issued: retire them, wait for stage st+1
+      // (the only copies in flight), refill this slot with stage st+2 and read the
+      // first step of stage st+1 while the last step's MFMAs run.
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (st + 2 < nst) issue(st + 2);
+      const uint8_t* sbn = smem + ((st + 1) % NSTAGE) * STAGE_BYTES;
+      uint32_t san[4], sxn[2];
+      read_scales(sbn, san, sxn);
+      k_step<3, true>(F1, F0, sbn, coff[0], wrow_off, xrow_off, sa, sx, acc);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sa[f] = *(const uint32_t*)(sb + wsc_off + f * 32 * 8);
-#pragma unroll
-    for (int g = 0; g < 2; ++g) sbx[g] = *(const uint32_t*)(sb + xsc_off + g * 32 * 8);
-
-    mfma_step<0>(sb, wrow_off, xrow_off, hh, swz, sa, sbx, acc);
-    mfma_step<1>(sb, wrow_off, xrow_off, hh, swz, sa, sbx, acc);
-    mfma_step<2>(sb, wrow_off, xrow_off, hh, swz, sa, sbx, acc);
-    mfma_step<3>(sb, wrow_off, xrow_off, hh, swz, sa, sbx, acc);
+      for (int q = 0; q < 4; ++q) sa[q] = san[q];
+      sx[0] = sxn[0];
+      sx[1] = sxn[1];
+    } else {
+      k_step<3, false>(F1, F0, sb, 0, wrow_off, xrow_off, sa, sx, acc);
+    }
   }
 
   // ---------------------------------------------------------------- epilogues
@@ -340,7 +386,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
         const int ml = wm * 64 + g * 32 + r32;
         const bool valid = (ml < t.rows) && (j0 < I);
         const int row = t.row0 + ml;
-        // h as bf16 bit patterns, packed in pairs: hp[q*2 + 0] = (v=4q, 4q+1), hp[q*2+1] = (4q+2, 4q+3)
+        // h as bf16 pairs: hp[2q] = (v = 4q, 4q+1), hp[2q+1] = (4q+2, 4q+3)
         uint32_t hp[8];
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
@@ -356,7 +402,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
           am = max(am, (uint32_t)__shfl_xor((int)am, 32));
           const uint32_t sbyte = mx_scale_from_amax_bits(am);
           uint32_t w0 = 0, w1 = 0;
-          // byte order within (w0, w1): q=0 pair0, q=0 pair1, q=1 pair0, q=1 pair1 | q=2 ..., q=3 ...
           w0 = quant_pair_e8m0<0>(w0, hp[0], sbyte);
           w0 = quant_pair_e8m0<1>(w0, hp[1], sbyte);
           w0 = quant_pair_e8m0<2>(w0, hp[2], sbyte);
@@ -380,8 +425,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) am = max(am, amax2(hp[blk * 4 + i]));
             am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-            const float r = bf16_to_f32(am) / t6;
-            const uint32_t sbyte = e4m3_rne_satfinite(r);
+            const uint32_t sbyte = e4m3_rne_satfinite(bf16_to_f32(am) / t6);
             sbytes[blk] = sbyte;
             const float d = e4m3_to_f32(sbyte) * gsc;
             uint32_t w = 0;
@@ -389,8 +433,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
             for (int i = 0; i < 4; ++i) {
               const uint32_t pr = hp[blk * 4 + i];
               float v0 = bf16_to_f32(pr & 0xFFFFu), v1 = bf16_to_f32(pr >> 16);
-              if (sbyte == 0) { v0 *= 0.0f; v1 *= 0.0f; }
-              else {
+              if (sbyte == 0) {
+                v0 *= 0.0f;
+                v1 *= 0.0f;
+              } else {
                 v0 = fminf(fmaxf(v0 / d, -6.0f), 6.0f);
                 v1 = fminf(fmaxf(v1 / d, -6.0f), 6.0f);
               }
@@ -404,22 +450,20 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
           bytes_lo = w01[0];
           bytes_hi = w01[1];
           if (valid && hh == 0) {
-            uint16_t two = (uint16_t)(sbytes[0] | (sbytes[1] << 8));
+            const uint16_t two = (uint16_t)(sbytes[0] | (sbytes[1] << 8));
             *(uint16_t*)(a.h_scales + (int64_t)row * (I >> 4) + (j0 >> 4)) = two;
           }
         }
         // Lane hh=0 holds byte positions {0,1,4,5,8,9,12,13} of the 16-byte block row,
         // hh=1 holds {2,3,6,7,10,11,14,15}; bytes_lo = q0p0,q0p1,q1p0,q1p1, bytes_hi = q2.., q3...
-        // Exchange so hh=0 writes bytes 0..7 and hh=1 writes 8..15.
+        // Exchange so that hh=0 writes bytes 0..7 and hh=1 writes 8..15.
         const uint32_t send = hh ? bytes_lo : bytes_hi;
         const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
         uint32_t o0, o1;
         if (hh == 0) {
-          // positions 0,1 = my q0; 2,3 = peer q0; 4,5 = my q1; 6,7 = peer q1
           o0 = (bytes_lo & 0xFFFFu) | ((recv & 0xFFFFu) << 16);
           o1 = (bytes_lo >> 16) | (recv & 0xFFFF0000u);
         } else {
-          // positions 8,9 = peer q2; 10,11 = my q2; 12,13 = peer q3; 14,15 = my q3
           o0 = (recv & 0xFFFFu) | ((bytes_hi & 0xFFFFu) << 16);
           o1 = (recv >> 16) | (bytes_hi & 0xFFFF0000u);
         }
@@ -431,10 +475,46 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
   }
 }
 
+// Persistent kernel: one workgroup per CU. Workgroup b runs on XCD b % 8 (the
+// dispatcher deals workgroups to the XCDs in turn); the tiles are cut into 8
+// contiguous ranges, one per XCD, and the workgroups of an XCD walk their range
+// in lock-step rounds. The 32 tiles of a round share weight and token rows and
+// stream the same K slabs at the same time, so those slabs are read once into
+// the XCD's L2 and reused from there.
+template <int EPI>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE_BYTES];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3, per_xcd_wgs = gridDim.x >> 3;
+  const int total = tile_count(a);
+  const int per = (total + 7) >> 3;
+  const int end = min((xcd + 1) * per, total);
+  for (int L = xcd * per + local; L < end; L += per_xcd_wgs) {
+    gemm_tile<EPI>(a, decode_tile(a, L), smem);
+    // the next tile's first copies overwrite LDS that this tile's waves read
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 }  // namespace
 
-hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  // one workgroup per CU, at most as many as there can be tiles, a multiple of 8 (XCDs)
+  const int cus = cu_count();
+  int grid = max_tiles < cus ? max_tiles : cus;
   const int g8 = (grid + 7) & ~7;
   switch (epi) {
     case EPI_F32: k_gemm<EPI_F32><<<g8, GEMM_THREADS, 0, s>>>(a); break;

@@ -11,10 +11,10 @@ namespace mx {
 // One workgroup computes BN weight rows x BM token rows; the K loop moves
 // BK logical columns (BK/2 bytes per row) per LDS stage.
 constexpr int BN = 256;
-constexpr int BM = 128;
+constexpr int BM = 256;
 constexpr int BK = 256;
-constexpr int NSTAGE = 3;
-constexpr int GEMM_THREADS = 256;
+constexpr int NSTAGE = 2;
+constexpr int GEMM_THREADS = 512;
 constexpr int L1_J_PER_TILE = BN / 2;    // L1 tiles hold gate and up rows for 128 j
 
 // Epilogue kinds of the scaled-MFMA GEMM.
@@ -61,7 +61,9 @@ struct GemmArgs {
   const float* slot_weight;   // grouped L2: gate weight per slot
 };
 
-hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int grid, hipStream_t s);
+// max_tiles: an upper bound on the tiles of the launch (the routed case only knows
+// its exact count on the device); the kernel is persistent with one workgroup per CU.
+hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int max_tiles, hipStream_t s);
 
 // ---- Elementwise kernels ---------------------------------------------------
 hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows,
@@ -77,7 +79,7 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, flo
 
 // ---- Routing ----------------------------------------------------------------
 constexpr int ROUTE_CHUNK = 1024;    // pairs per counting/scatter block
-constexpr int ROUTE_MAX_EXPERTS = 1024;
+constexpr int ROUTE_MAX_EXPERTS = 512;   // LDS of the scatter: 19 * E ints
 
 struct RouteBuffers {
   int32_t* block_counts;   // [nblocks, E]

@@ -7,12 +7,9 @@
 // stays in BF16 per Phase 3). Router logits and top-k selection are inputs.
 //
 // Route: pairs p = t*k + j (token t, slot j) are ordered by expert, and by p
-// within an expert (stable). Three small kernels:
+// within an expert (stable, so the layout is the same on every run). Two kernels:
 //   1. per-chunk expert histogram (LDS counters),
-//   2. one-block scan: per-chunk bases, expert offsets, per-expert m-tile bases,
-//   3. scatter: one wave per chunk walks its pairs 64 at a time in order; lanes
-//      with the same expert find their rank with a wave ballot + popcount of the
-//      lanes below them, and the first lane advances the expert's running count.
+//   2. scatter with the scan folded in (see k_route_scatter).
 // Ids outside [0, E) belong to experts on other ranks and are skipped.
 #include "mx_device.h"
 #include "mx_internal.h"
@@ -38,65 +35,70 @@ __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__
   for (int e = threadIdx.x; e < E; e += 256) block_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-__global__ __launch_bounds__(256) void k_route_scan(int32_t* __restrict__ block_counts, int nblocks, int E,
-                                                    int32_t* __restrict__ expert_off,
-                                                    int32_t* __restrict__ tile_base) {
-  __shared__ int tot[ROUTE_MAX_EXPERTS];
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int s = 0;
-    for (int b = 0; b < nblocks; ++b) {
-      const int c = block_counts[(int64_t)b * E + e];
-      block_counts[(int64_t)b * E + e] = s;   // becomes the chunk's base within expert e
-      s += c;
-    }
-    tot[e] = s;
-  }
+// One block of ROUTE_CHUNK threads (16 waves) per chunk of pairs, one pair per
+// thread. Each block recomputes, from the chunk histograms, the expert totals
+// (-> expert offsets and m-tile bases, written by block 0) and its own base
+// within every expert. Inside the block a pair's rank among the earlier pairs
+// of its expert is the sum of the counts of the earlier waves plus its rank in
+// its own wave: lanes that share an expert find each other with a ballot and
+// count the set bits below them. Order within an expert is pair order.
+__global__ __launch_bounds__(ROUTE_CHUNK) void k_route_scatter(
+    const int32_t* __restrict__ ids, int64_t P, int k, int E, const int32_t* __restrict__ block_counts,
+    int nblocks, int32_t* __restrict__ expert_off, int32_t* __restrict__ tile_base,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot) {
+  extern __shared__ int sm[];
+  constexpr int NW = ROUTE_CHUNK / 64;
+  int* tot = sm;              // [E] pairs per expert (all chunks)
+  int* pre = sm + E;          // [E] pairs per expert in earlier chunks
+  int* off = sm + 2 * E;      // [E] exclusive prefix of tot
+  int* wc = sm + 3 * E;       // [NW][E] pairs per expert in each wave of this chunk
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.x;
+  for (int i = tid; i < (3 + NW) * E; i += ROUTE_CHUNK) sm[i] = 0;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int off = 0, tiles = 0;
-    for (int e = 0; e < E; ++e) {
-      expert_off[e] = off;
-      tile_base[e] = tiles;
-      off += tot[e];
-      tiles += (tot[e] + BM - 1) / BM;
-    }
-    expert_off[E] = off;
-    tile_base[E] = tiles;
+  for (int i = tid; i < nblocks * E; i += ROUTE_CHUNK) {
+    const int c = block_counts[i];
+    const int e = i % E;
+    atomicAdd(&tot[e], c);
+    if (i / E < b) atomicAdd(&pre[e], c);
   }
-}
-
-__global__ __launch_bounds__(64) void k_route_scatter(const int32_t* __restrict__ ids, int64_t P, int k, int E,
-                                                      const int32_t* __restrict__ block_base,
-                                                      const int32_t* __restrict__ expert_off,
-                                                      int32_t* __restrict__ row_token,
-                                                      int32_t* __restrict__ row_slot) {
-  __shared__ int run[ROUTE_MAX_EXPERTS];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) run[e] = expert_off[e] + block_base[(int64_t)blockIdx.x * E + e];
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * ROUTE_CHUNK;
+  const int64_t p = (int64_t)b * ROUTE_CHUNK + tid;
+  const int e = (p < P) ? ids[p] : -1;
+  const bool valid = (p < P) && ((unsigned)e < (unsigned)E);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i0 = 0; i0 < ROUTE_CHUNK; i0 += 64) {
-    const int64_t p = base + i0 + lane;
-    const int e = (p < P) ? ids[p] : -1;
-    const bool valid = (p < P) && ((unsigned)e < (unsigned)E);
-    uint64_t todo = __ballot(valid);
-    while (todo) {
-      const int leader = __ffsll((long long)todo) - 1;
-      const int ee = __shfl(e, leader);
-      const bool mine = valid && (e == ee);
-      const uint64_t m = __ballot(mine);
-      const int start = run[ee];
-      if (mine) {
-        const int pos = start + __popcll(m & below);
-        row_token[pos] = (int)(p / k);
-        row_slot[pos] = (int)p;
+  int rank = 0;
+  uint64_t todo = __ballot(valid);
+  while (todo) {
+    const int leader = __ffsll((long long)todo) - 1;
+    const int ee = __shfl(e, leader);
+    const uint64_t m = __ballot(valid && e == ee);
+    if (valid && e == ee) rank = __popcll(m & below);
+    if (lane == leader) wc[w * E + ee] = __popcll(m);
+    todo &= ~m;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, tb = 0;
+    for (int x = 0; x < E; ++x) {
+      off[x] = o;
+      if (b == 0) {
+        expert_off[x] = o;
+        tile_base[x] = tb;
       }
-      __syncthreads();   // single wave: orders the read of run[ee] before the update
-      if (lane == leader) run[ee] = start + __popcll(m);
-      __syncthreads();
-      todo &= ~m;
+      o += tot[x];
+      tb += (tot[x] + BM - 1) / BM;
     }
+    if (b == 0) {
+      expert_off[E] = o;
+      tile_base[E] = tb;
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    int pos = off[e] + pre[e] + rank;
+    for (int x = 0; x < w; ++x) pos += wc[x * E + e];
+    row_token[pos] = (int)(p / k);
+    row_slot[pos] = (int)p;
   }
 }
 
@@ -136,14 +138,11 @@ hipError_t launch_route(const int32_t* topk_ids, int64_t tokens, int k, int n_ex
                         const RouteBuffers& rb, hipStream_t s) {
   const int64_t P = tokens * k;
   const int nblocks = (int)((P + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
-  if (nblocks > 0) {
-    k_route_count<<<nblocks, 256, 0, s>>>(topk_ids, P, n_experts, rb.block_counts);
-  }
-  k_route_scan<<<1, 256, 0, s>>>(rb.block_counts, nblocks, n_experts, rb.expert_off, rb.tile_base);
-  if (nblocks > 0) {
-    k_route_scatter<<<nblocks, 64, 0, s>>>(topk_ids, P, k, n_experts, rb.block_counts, rb.expert_off,
-                                           rb.row_token, rb.row_slot);
-  }
+  if (nblocks == 0) return hipSuccess;
+  k_route_count<<<nblocks, 256, 0, s>>>(topk_ids, P, n_experts, rb.block_counts);
+  const size_t lds = (size_t)(3 + ROUTE_CHUNK / 64) * n_experts * sizeof(int);
+  k_route_scatter<<<nblocks, ROUTE_CHUNK, lds, s>>>(topk_ids, P, k, n_experts, rb.block_counts, nblocks,
+                                                    rb.expert_off, rb.tile_base, rb.row_token, rb.row_slot);
   return hipGetLastError();
 }
 
