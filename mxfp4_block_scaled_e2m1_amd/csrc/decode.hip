@@ -1,0 +1,345 @@
+// Expert MLP for a few tokens (M <= 8): the weight stream from HBM is the cost.
+//
+// Same arithmetic as the prefill path (page "Current Bug: vLLM produces
+// empty/garbage output", section "Revised Plan", Phase 1: L1 GEMM, SiLU,
+// re-quant, L2 GEMM; MXFP4 formats of page "2026-05-08 DeepSeek V4 Pro NVFP4
+// Quantization", sections "Script update" and "FP4 (E2M1) expert weight format
+// confirmed"), arranged for bandwidth instead of MFMA rate. Two kernels, each a
+// single pass over its weights:
+//  * L1: one workgroup per 8 intermediate columns j. Its 16 weight rows (8 of
+//    w1, 8 of w3) form one 16-row MFMA tile over the whole K = hidden, so the
+//    gate and the up value of a column meet in the same workgroup and SiLU(g)*u
+//    needs no second pass. 3072 / 8 = 384 workgroups.
+//  * L2: one workgroup per 16 output columns (16 rows of w2), 448 workgroups.
+//  * 8 waves; wave w owns a contiguous run of the 128-wide K steps and keeps
+//    that run's weight codes in registers (16 bytes per lane per step).
+//  * Every thread issues its loads in a fixed order: the activation blocks it
+//    will quantise, then its share of the rows' scales, then its weight codes.
+//    Memory loads of a wave complete in issue order, so the quantisation of the
+//    activations (x for L1, h for L2, with the conversions of the standalone
+//    MXFP4 quantiser) and the scale staging wait only for those first loads and
+//    run while the weight codes are still in flight.
+//  * V_MFMA_SCALE_F32_16X16X128_F8F6F4: weight rows are the 16-row A operand,
+//    tokens the 16 columns of B (columns >= M are zero operands). The 8 waves'
+//    partial sums meet in LDS, in wave order, and wave 0 writes the result:
+//    h = bf16(silu(g) * u) for L1, y = bf16(acc) for L2.
+#include "mx_device.h"
+#include "mx_internal.h"
+
+namespace mx {
+
+namespace {
+
+constexpr int DT = 512;             // threads per workgroup
+constexpr int DW = DT / 64;         // waves
+constexpr int MAX_STEPS = 8;        // K steps of 128 per wave held in registers
+constexpr int MAX_TOK = 8;          // tokens per call on this path
+
+__device__ __forceinline__ i32x8 opnd(const uint4& v) {
+  return i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+}
+
+// The thread's activation blocks (32 bf16 each): block b = tid + DT * r of the
+// row-major list of m * cols/32 blocks.
+template <int XR>
+struct XBlocks {
+  uint4 v[XR][4];
+};
+
+// Loads are unconditional (a thread past the end re-reads the last block):
+// the compiler counts outstanding loads exactly only when none is skipped by a
+// branch, and an exact count is what lets the later waits ignore the weights.
+template <int XR>
+__device__ __forceinline__ void load_x(const uint16_t* __restrict__ src, int m, int cols, XBlocks<XR>& xb) {
+  const int bpr = cols >> 5, nb = m * bpr;
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int b = min((int)threadIdx.x + DT * r, nb - 1);
+    const int row = b / bpr, c = b - row * bpr;
+    const uint4* p = (const uint4*)(src + (int64_t)row * cols + c * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xb.v[r][i] = p[i];
+  }
+}
+
+// MXFP4-quantise the loaded blocks into LDS: codes at row * cstride + c * 16,
+// scale bytes at row * (cols/32) + c. Every thread converts its blocks (those
+// past the end are re-read copies) and only the stores are conditional, so the
+// compiler has no branch to sink the loads into.
+template <int XR>
+__device__ __forceinline__ void quant_x_to_lds(const XBlocks<XR>& xb, int m, int cols, uint8_t* codes,
+                                               int cstride, uint8_t* scales) {
+  const int bpr = cols >> 5, nb = m * bpr;
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int b = threadIdx.x + DT * r;
+    {
+      const int row = b / bpr, c = b - row * bpr;
+      uint32_t w[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[4 * i] = xb.v[r][i].x; w[4 * i + 1] = xb.v[r][i].y;
+        w[4 * i + 2] = xb.v[r][i].z; w[4 * i + 3] = xb.v[r][i].w;
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am = max(am, amax2(w[i]));
+      const uint32_t sb = mx_scale_from_amax_bits(am);
+      uint32_t q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t v = 0;
+        v = quant_pair_e8m0<0>(v, w[4 * i], sb);
+        v = quant_pair_e8m0<1>(v, w[4 * i + 1], sb);
+        v = quant_pair_e8m0<2>(v, w[4 * i + 2], sb);
+        v = quant_pair_e8m0<3>(v, w[4 * i + 3], sb);
+        q[i] = v;
+      }
+      if (b < nb) {
+        *(uint4*)(codes + row * cstride + c * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+        scales[row * bpr + c] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+// Balanced split of `ksteps` K steps over the DW waves: wave w takes [s0, s0 + n).
+__device__ __forceinline__ void wave_steps(int ksteps, int& s0, int& n) {
+  const int wave = threadIdx.x >> 6;
+  const int base = ksteps / DW, extra = ksteps - base * DW;
+  n = base + (wave < extra ? 1 : 0);
+  s0 = wave * base + min(wave, extra);
+}
+
+// The 16 rows of a weight tile: rows 0..7 start at lo + r * stride, rows 8..15
+// at hi + (r - 8) * stride (the same matrix continued, or a second matrix).
+struct RowPair {
+  const uint8_t* lo;
+  const uint8_t* hi;
+  __device__ __forceinline__ const uint8_t* row(int r, int stride) const {
+    return (r < 8 ? lo : hi) + (int64_t)(r & 7) * stride;
+  }
+};
+
+// The tile rows' scale bytes (ks per row), two dwords per thread at most
+// (16 * ks <= 4 KB).
+struct ScaleRegs {
+  uint32_t v[2];
+};
+
+__device__ __forceinline__ void load_wscales(const RowPair& sp, int ks, ScaleRegs& sr) {
+  const int per_row = ks >> 2;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = min((int)threadIdx.x + DT * r, 16 * per_row - 1);   // unconditional, as load_x
+    const int row = i / per_row, c = i - row * per_row;
+    sr.v[r] = *(const uint32_t*)(sp.row(row, ks) + c * 4);
+  }
+}
+
+__device__ __forceinline__ void store_wscales(const ScaleRegs& sr, int ks, uint8_t* dst) {
+  const int per_row = ks >> 2;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int i = threadIdx.x + DT * r;
+    if (i < 16 * per_row) *(uint32_t*)(dst + i * 4) = sr.v[r];
+  }
+}
+
+// Workgroup barrier that does not wait for outstanding global loads (the
+// weight codes stay in flight); LDS writes are complete before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Shared body of both kernels: the wave's K-step run of one 16-row weight tile
+// (codes `wp`, scales `sp`) times the m tokens of `act` [m, K] bf16, quantised
+// into LDS. Wave 0 returns the workgroup's total for lane (token lane%16, tile
+// rows 4*(lane/16) + v).
+template <int XR, int NS>
+__device__ __forceinline__ f32x4 tile_times_tokens(const uint16_t* __restrict__ act, int m, int K, RowPair wp,
+                                                   RowPair sp, uint8_t* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int kb = K / 2, ks = K / 32, ksteps = K / 128;
+  const int xstride = kb + 16;   // pad: consecutive tokens start 4 banks apart
+  uint8_t* xq = lds;
+  uint8_t* xs = xq + MAX_TOK * xstride;
+  uint8_t* wsl = xs + ((MAX_TOK * ks + 15) & ~15);
+  f32x4* red = (f32x4*)(wsl + ((16 * ks + 15) & ~15));
+
+  // Loads, in completion order: activations, scales, weight codes.
+  XBlocks<XR> xb;
+  load_x<XR>(act, m, K, xb);
+  ScaleRegs sr;
+  load_wscales(sp, ks, sr);
+  __builtin_amdgcn_sched_barrier(0);
+  int s0, n;
+  wave_steps(ksteps, s0, n);
+  // NS >= n steps per wave; steps past the wave's run re-read a valid step
+  // (unconditional loads, as load_x) and are not multiplied.
+  uint4 wa[NS];
+  const uint8_t* myrow = wp.row(r16, kb);
+#pragma unroll
+  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)(myrow + min(s0 + k, ksteps - 1) * 64 + q * 16);
+  __builtin_amdgcn_sched_barrier(0);
+
+  quant_x_to_lds<XR>(xb, m, K, xq, xstride, xs);
+  store_wscales(sr, ks, wsl);
+  lds_barrier();
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool tok_ok = r16 < m;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    if (k < n) {
+      const int s = s0 + k;
+      uint4 b = make_uint4(0u, 0u, 0u, 0u);
+      int sb = 0;
+      if (tok_ok) {
+        b = *(const uint4*)(xq + r16 * xstride + s * 64 + q * 16);
+        sb = xs[r16 * ks + s * 4 + q];
+      }
+      const int sa = wsl[r16 * ks + s * 4 + q];
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(wa[k]), opnd(b), acc, 4, 4, 0, sa, 0, sb);
+    }
+  }
+  if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < DW - 1; ++w) {
+      const f32x4 o = red[w * 64 + lane];
+      acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
+    }
+  }
+  return acc;
+}
+
+// L1 for 8 intermediate columns j0 .. j0+7: tile rows 0..7 are w1 (gate), rows
+// 8..15 are w3 (up). h[m][j] = bf16(silu(g) * u).
+template <int XR, int NS>
+__global__ __launch_bounds__(DT, 1) void k_decode_l1(const uint16_t* __restrict__ x, int m, int H, int I,
+                                                     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ w1s,
+                                                     const uint8_t* __restrict__ w3, const uint8_t* __restrict__ w3s,
+                                                     uint16_t* __restrict__ h) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int j0 = blockIdx.x * 8;
+  const int kb = H / 2, ks = H / 32;
+  const RowPair wp{w1 + (int64_t)j0 * kb, w3 + (int64_t)j0 * kb};
+  const RowPair sp{w1s + (int64_t)j0 * ks, w3s + (int64_t)j0 * ks};
+  f32x4 acc = tile_times_tokens<XR, NS>(x, m, H, wp, sp, lds);
+  const int lane = threadIdx.x & 63;
+  // lane (token t, q): rows 4q + v; q = 0, 1 hold the gate of j = j0 + 4q + v
+  // and lane ^ 32 (q + 2) holds the up value of the same j.
+  float up[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) up[v] = __shfl_xor(acc[v], 32);
+  const int t = lane & 15, q = lane >> 4;
+  if ((threadIdx.x >> 6) == 0 && q < 2 && t < m) {
+    const uint32_t p0 = f32_to_bf16_rne(silu_mul(acc[0], up[0])) | (f32_to_bf16_rne(silu_mul(acc[1], up[1])) << 16);
+    const uint32_t p1 = f32_to_bf16_rne(silu_mul(acc[2], up[2])) | (f32_to_bf16_rne(silu_mul(acc[3], up[3])) << 16);
+    *(uint2*)(h + (int64_t)t * I + j0 + 4 * q) = make_uint2(p0, p1);
+  }
+}
+
+// L2 for 16 output columns n0 .. n0+15: y[m][n] = bf16(MXFP4(h) . w2[n]).
+template <int XR, int NS>
+__global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict__ h, int m, int H, int I,
+                                                     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
+                                                     uint16_t* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int n0 = blockIdx.x * 16;
+  const int kb = I / 2, ks = I / 32;
+  const RowPair wp{w2 + (int64_t)n0 * kb, w2 + (int64_t)(n0 + 8) * kb};
+  const RowPair sp{w2s + (int64_t)n0 * ks, w2s + (int64_t)(n0 + 8) * ks};
+  f32x4 acc = tile_times_tokens<XR, NS>(h, m, I, wp, sp, lds);
+  const int lane = threadIdx.x & 63;
+  const int t = lane & 15, q = lane >> 4;
+  if ((threadIdx.x >> 6) == 0 && t < m) {
+    const uint32_t p0 = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    const uint32_t p1 = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    *(uint2*)(y + (int64_t)t * H + n0 + 4 * q) = make_uint2(p0, p1);
+  }
+}
+
+size_t decode_lds(int cols) {
+  const size_t kb = cols / 2, ks = cols / 32;
+  return MAX_TOK * (kb + 16) + ((MAX_TOK * ks + 15) & ~(size_t)15) + ((16 * ks + 15) & ~(size_t)15) +
+         (size_t)(DW - 1) * 64 * sizeof(f32x4);
+}
+
+// Activation blocks per thread: m * cols/32 blocks over DT threads.
+int x_rounds(int m, int cols) { return (m * (cols / 32) + DT - 1) / DT; }
+
+// Register budget of a wave's K run, rounded up to an instantiated size:
+// 7 and 3 are the 7168- and 3072-wide K of the expert, 1 the tiny shapes.
+int steps_bucket(int cols) {
+  const int ns = (cols / 128 + DW - 1) / DW;
+  return ns <= 1 ? 1 : ns <= 3 ? 3 : ns <= 7 ? 7 : MAX_STEPS;
+}
+
+struct DecodeArgs {
+  const uint16_t* x; int m, H, I;
+  const uint8_t *w1, *w1s, *w3, *w3s, *w2, *w2s;
+  uint16_t *h, *y;
+};
+
+template <int XR, int NS>
+void launch_l1(const DecodeArgs& a, hipStream_t s) {
+  k_decode_l1<XR, NS><<<a.I / 8, DT, decode_lds(a.H), s>>>(a.x, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.h);
+}
+
+template <int XR, int NS>
+void launch_l2(const DecodeArgs& a, hipStream_t s) {
+  k_decode_l2<XR, NS><<<a.H / 16, DT, decode_lds(a.I), s>>>(a.h, a.m, a.H, a.I, a.w2, a.w2s, a.y);
+}
+
+template <int XR>
+void launch_l1_ns(const DecodeArgs& a, hipStream_t s) {
+  switch (steps_bucket(a.H)) {
+    case 1: launch_l1<XR, 1>(a, s); break;
+    case 3: launch_l1<XR, 3>(a, s); break;
+    case 7: launch_l1<XR, 7>(a, s); break;
+    default: launch_l1<XR, MAX_STEPS>(a, s); break;
+  }
+}
+
+template <int XR>
+void launch_l2_ns(const DecodeArgs& a, hipStream_t s) {
+  switch (steps_bucket(a.I)) {
+    case 1: launch_l2<XR, 1>(a, s); break;
+    case 3: launch_l2<XR, 3>(a, s); break;
+    case 7: launch_l2<XR, 7>(a, s); break;
+    default: launch_l2<XR, MAX_STEPS>(a, s); break;
+  }
+}
+
+}  // namespace
+
+bool decode_fits(int64_t m, int64_t hidden, int64_t inter) {
+  if (m < 1 || m > MAX_TOK) return false;
+  // every K step of a wave is held in registers
+  if (hidden > DW * MAX_STEPS * 128 || inter > DW * MAX_STEPS * 128) return false;
+  if (inter % 8 != 0 || hidden % 16 != 0) return false;
+  // at most 4 activation blocks and two scale dwords per thread
+  if (x_rounds((int)m, (int)hidden) > 4 || x_rounds((int)m, (int)inter) > 4) return false;
+  if (16 * (hidden / 32) > 8 * DT || 16 * (inter / 32) > 8 * DT) return false;
+  return decode_lds((int)hidden) <= 64 * 1024 && decode_lds((int)inter) <= 64 * 1024;
+}
+
+hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
+                             const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
+                             uint16_t* h, uint16_t* y, hipStream_t s) {
+  const DecodeArgs a{x, m, H, I, w1, w1s, w3, w3s, w2, w2s, h, y};
+  const int r1 = x_rounds(m, H), r2 = x_rounds(m, I);
+  if (r1 <= 1) launch_l1_ns<1>(a, s);
+  else if (r1 <= 2) launch_l1_ns<2>(a, s);
+  else launch_l1_ns<4>(a, s);
+  if (r2 <= 1) launch_l2_ns<1>(a, s);
+  else if (r2 <= 2) launch_l2_ns<2>(a, s);
+  else launch_l2_ns<4>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace mx

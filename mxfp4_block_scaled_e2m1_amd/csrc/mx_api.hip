@@ -84,17 +84,26 @@ struct Carve {
   }
 };
 
+// Dense (one expert) workspace. Prefill: xq, xs, hq, hs. Few-token path
+// (M <= 32): h, the bf16 SiLU output, at the same offset as xq.
 struct DenseWs {
   uint8_t *xq, *xs, *hq, *hs;
+  uint16_t* h;
   size_t bytes;
 };
 DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
   Carve c(base);
   DenseWs w;
-  w.xq = (uint8_t*)c.take((size_t)(M * H / 2));
-  w.xs = (uint8_t*)c.take((size_t)(M * H / 32));
-  w.hq = (uint8_t*)c.take((size_t)(M * I / 2));
-  w.hs = (uint8_t*)c.take((size_t)(M * I / (rq == MX_FMT_NVFP4 ? 16 : 32)));
+  if (decode_fits(M, H, I)) {
+    w.h = (uint16_t*)c.take((size_t)(M * I * 2));
+    w.xq = w.xs = w.hq = w.hs = nullptr;
+  } else {
+    w.h = nullptr;
+    w.xq = (uint8_t*)c.take((size_t)(M * H / 2));
+    w.xs = (uint8_t*)c.take((size_t)(M * H / 32));
+    w.hq = (uint8_t*)c.take((size_t)(M * I / 2));
+    w.hs = (uint8_t*)c.take((size_t)(M * I / (rq == MX_FMT_NVFP4 ? 16 : 32)));
+  }
   w.bytes = c.off;
   return w;
 }
@@ -345,6 +354,14 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
     return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   DenseWs w = dense_ws(workspace, M, hidden, inter, requant);
   const int H = (int)hidden, I = (int)inter, m = (int)M;
+
+  if (w.h != nullptr) {
+    // few tokens: two weight-streaming kernels, activations quantised in LDS
+    MX_HIP(phase("decode_mlp", s, [&] {
+             return launch_decode_mlp(x, m, H, I, w1, w1_s, w3, w3_s, w2, w2_s, w.h, y, s);
+           }), "decode_mlp");
+    return ok();
+  }
 
   MX_HIP(phase("quant_x", s, [&] { return launch_quant_mxfp4(x, M, hidden, w.xq, w.xs, s); }), "quant_x");
 

@@ -95,4 +95,11 @@ hipError_t launch_route(const int32_t* topk_ids, int64_t tokens, int k, int n_ex
 hipError_t launch_combine(const uint16_t* o, const int32_t* topk_ids, int64_t tokens, int k,
                           int n_experts, int hidden, uint16_t* y, hipStream_t s);
 
+// ---- Few-token path (M <= 32): weight streaming, see decode.hip ----------------
+bool decode_fits(int64_t m, int64_t hidden, int64_t inter);
+// h: bf16 scratch [m, inter]
+hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
+                             const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
+                             uint16_t* h, uint16_t* y, hipStream_t s);
+
 }  // namespace mx

@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import assert_mlp_close, assert_requant_close, bf16_t, bits, t
+from gpu_util import assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, t
 
 pytestmark = pytest.mark.gpu
 
@@ -17,13 +17,40 @@ def mx():
     return m
 
 
+DECODE_MAX_TOKENS = 8    # mx_expert_mlp streams the weights once for up to 8 tokens
+
+
 def _ws_slices(ws, M, H, I):
-    """Dense workspace layout of mx_expert_mlp: xq, xs, hq, hs, each 256-byte aligned."""
+    """Dense workspace layout of mx_expert_mlp, each region 256-byte aligned:
+    GEMM path (M > 8): xq, xs, hq, hs; few tokens: h (bf16 SiLU output)."""
+    if M <= DECODE_MAX_TOKENS:
+        return [ws[:M * I * 2]]
     off, out = 0, []
     for n in (M * H // 2, M * H // 32, M * I // 2, M * I // 32):
         out.append(ws[off:off + n])
         off += (n + 255) // 256 * 256
     return out
+
+
+H_TINY = 1e-30   # fp32 exp(-g) overflows for g < -88.7: silu(g) * u below ~1e-36 flushes to +-0
+
+
+def _check_h_and_requant(mx, h_slice, M, I, inter):
+    """Few-token path: h (bf16) against the oracle's, and its re-quantisation.
+
+    The GPU evaluates silu(g) * u in fp32 and rounds to bf16 once; the oracle
+    rounds the fp64 value. They agree bit for bit except near bf16 rounding
+    boundaries and for negligible values (|h| < 1e-30), which fp32 flushes."""
+    h = h_slice.view(torch.int16).view(M, I)
+    hb = h.cpu().numpy().view(np.uint16)
+    ref = inter["h"]
+    hv, rv = bf16_f64(hb), bf16_f64(ref)
+    big = np.abs(rv) >= H_TINY
+    same = np.mean(hb[big] == ref[big])
+    assert same >= 0.999, same
+    assert np.all(np.abs(hv - rv) <= np.abs(rv) * 2.0 ** -7 + H_TINY)
+    codes, scales = mx.quantize_act("mxfp4", h.view(torch.bfloat16))
+    assert_requant_close(codes.cpu().numpy(), scales.cpu().numpy(), inter["hq"], inter["hs"])
 
 
 # ---------------------------------------------------------------- GEMM
@@ -49,22 +76,48 @@ def _run_dense(mx, d, M, H, I):
     return bits(y), _ws_slices(ws, M, H, I)
 
 
-def test_tiny_expert_mlp(mx):
-    d = W.tiny_mlp(0)
-    y, (xq, xs, hq, hs) = _run_dense(mx, d, 16, 256, 128)
+def _check_gemm_path(mx, d, M, H, I):
+    y, (xq, xs, hq, hs) = _run_dense(mx, d, M, H, I)
     ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
-    assert np.array_equal(xq.cpu().numpy().reshape(16, 128), inter["xq"])
-    assert np.array_equal(xs.cpu().numpy().reshape(16, 8), inter["xs"])
-    assert_requant_close(hq.cpu().numpy().reshape(16, 64), hs.cpu().numpy().reshape(16, 4), inter["hq"], inter["hs"])
+    assert np.array_equal(xq.cpu().numpy().reshape(M, H // 2), inter["xq"])
+    assert np.array_equal(xs.cpu().numpy().reshape(M, H // 32), inter["xs"])
+    assert_requant_close(hq.cpu().numpy().reshape(M, I // 2), hs.cpu().numpy().reshape(M, I // 32),
+                         inter["hq"], inter["hs"])
     assert_mlp_close(y, ref)
 
 
-@pytest.mark.parametrize("M", [1, 8, 128, 300])
+def test_tiny_expert_mlp(mx):
+    """The tiny configuration: 16 tokens, hidden 256, intermediate 128 (GEMM path)."""
+    _check_gemm_path(mx, W.tiny_mlp(0), 16, 256, 128)
+
+
+def test_tiny_expert_mlp_48_tokens(mx):
+    d = W.tiny_mlp(0)
+    d["x"] = W.bf16_normal(np.random.default_rng(7), (48, 256))
+    _check_gemm_path(mx, d, 48, 256, 128)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_tiny_expert_mlp_few_tokens(mx, M):
+    """The tiny weights with the first M tokens: the weight-streaming path."""
+    d = W.tiny_mlp(0)
+    d["x"] = d["x"][:M]
+    y, (h,) = _run_dense(mx, d, M, 256, 128)
+    ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
+    _check_h_and_requant(mx, h, M, 128, inter)
+    assert_mlp_close(y, ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17, 32, 33, 128, 300])
 def test_shared_expert_real_shape(mx, M):
     d = W.shared_expert(M, seed=0)
-    y, (_, _, hq, hs) = _run_dense(mx, d, M, 7168, 3072)
+    y, sl = _run_dense(mx, d, M, 7168, 3072)
     ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
-    assert_requant_close(hq.cpu().numpy().reshape(M, 1536), hs.cpu().numpy().reshape(M, 96), inter["hq"], inter["hs"])
+    if M <= DECODE_MAX_TOKENS:
+        _check_h_and_requant(mx, sl[0], M, 3072, inter)
+    else:
+        _, _, hq, hs = sl
+        assert_requant_close(hq.cpu().numpy().reshape(M, 1536), hs.cpu().numpy().reshape(M, 96), inter["hq"], inter["hs"])
     assert_mlp_close(y, ref)
 
 
