@@ -113,8 +113,15 @@ MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t 
  * mx_expert_mlp -- one expert (the shared expert), M tokens, no routing.
  *   x  [M, hidden] bf16            w1, w3 codes [inter, hidden/2], scales [inter, hidden/32]
  *   y  [M, hidden] bf16            w2 codes [hidden, inter/2], scales [hidden, inter/32]
- * hidden % 128 == 0 and inter % 128 == 0. requant is MX_FMT_MXFP4 (NVFP4 is
- * accepted once the bf16 L2 path exists; until then it returns MX_ERR_FORMAT).
+ * hidden % 128 == 0 and inter % 128 == 0.
+ * requant selects the format of the intermediate h between the two GEMMs:
+ *   MX_FMT_MXFP4: E8M0 per 32 (requant_global ignored); both GEMMs run on FP4
+ *     matrix cores. M <= 8 takes the weight-streaming few-token kernels.
+ *   MX_FMT_NVFP4: E4M3 per 16 with the fp32 global scale requant_global = g
+ *     (finite, >= 2^-117, else MX_ERR_VALUE); the L2 GEMM runs on bf16 matrix
+ *     cores on exactly dequantised operands, y = bf16(g * sum (code*s)(w)).
+ *     Exact for w2 scale bytes <= 252 (6 * 2^126 exceeds bf16 above that).
+ *   anything else: MX_ERR_FORMAT.
  * A stacked gate_up tensor [2*inter, hidden/2] is passed as w1 = w13 and
  * w3 = w13 + inter*hidden/2 (scales likewise).
  * workspace: device memory of at least mx_expert_mlp_workspace_size() bytes,
@@ -142,7 +149,8 @@ MX_API size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t in
  * fuses SiLU*up and the re-quantisation; the L2 GEMM multiplies by the gate
  * weight and writes one bf16 row per pair; a final pass sums each token's k
  * rows in slot order in fp32 (deterministic: no atomics).
- * 1 <= k <= E <= 512; hidden % 128 == 0; inter % 128 == 0.
+ * 1 <= k <= E <= 512; hidden % 128 == 0; inter % 128 == 0. requant and
+ * requant_global as for mx_expert_mlp.
  * Alignment as for mx_expert_mlp; topk_ids and topk_w 4 bytes.
  */
 MX_API mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,

@@ -33,8 +33,7 @@
 //    expert's weight n-tile) land on the same XCD and share its L2.
 #include <atomic>
 
-#include "mx_device.h"
-#include "mx_internal.h"
+#include "gemm_common.h"
 
 namespace mx {
 
@@ -61,51 +60,6 @@ static_assert(WS_BYTES + XS_BYTES == GEMM_THREADS * 8, "two scale dwords per thr
 // Zero bytes for the upper half of a K stage when K % 256 == 128: zero codes with
 // zero scale bytes (2^-127) contribute exactly 0 to every sum.
 __device__ __attribute__((aligned(256))) uint8_t g_zero_page[256];
-
-struct Tile {
-  int e;         // expert
-  int nt;        // tile index along weight rows
-  int row0;      // first row (sorted order) of the token tile
-  int rows;      // valid rows in the token tile
-};
-
-// Number of tiles of this launch (device-side for the routed experts).
-__device__ __forceinline__ int tile_count(const GemmArgs& a) {
-  if (a.expert_off == nullptr) return a.grid_tiles;
-  return a.tile_base[a.n_experts] * a.n_tiles;
-}
-
-// Tile L of the launch. Tiles are ordered (expert, n-tile, m-tile) with the
-// m-tile fastest, so consecutive tiles share their weight rows.
-__device__ __forceinline__ Tile decode_tile(const GemmArgs& a, int L) {
-  Tile t;
-  if (a.expert_off == nullptr) {
-    const int mtiles = (a.m_rows + BM - 1) / BM;
-    t.e = 0;
-    t.nt = L / mtiles;
-    const int mt = L - t.nt * mtiles;
-    t.row0 = mt * BM;
-    t.rows = min(BM, a.m_rows - t.row0);
-    return t;
-  }
-  // expert e with tile_base[e] * n_tiles <= L < tile_base[e + 1] * n_tiles
-  int lo = 0, hi = a.n_experts - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.tile_base[mid] * a.n_tiles <= L) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int tb = a.tile_base[e];
-  const int nte = a.tile_base[e + 1] - tb;
-  const int r = L - tb * a.n_tiles;
-  t.e = e;
-  t.nt = r / nte;
-  const int mt = r - t.nt * nte;
-  const int off = a.expert_off[e];
-  t.row0 = off + mt * BM;
-  t.rows = min(BM, a.expert_off[e + 1] - t.row0);
-  return t;
-}
 
 // Global -> LDS copies. Lane i of the wave writes LDS bytes [m0 + i*size, +size).
 // They are issued as inline asm so that the compiler neither waits for them
@@ -348,33 +302,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
         }
     }
   } else if constexpr (EPI == EPI_BF16) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int ml = wm * 64 + g * 32 + r32;
-      if (ml >= t.rows) continue;
-      const int row = t.row0 + ml;
-      int64_t out_row = row;
-      float wgt = 1.0f;
-      if (a.row_slot != nullptr) {
-        const int slot = a.row_slot[row];
-        out_row = slot;
-        wgt = a.slot_weight[slot];
-      }
-      uint16_t* dst = a.out_bf16 + out_row * a.n_rows;
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = t.nt * BN + wn * 128 + f * 32 + 8 * q + 4 * hh;
-          if (n < a.n_rows) {
-            uint32_t p0 = f32_to_bf16_rne(acc[f][g][4 * q] * wgt) |
-                          (f32_to_bf16_rne(acc[f][g][4 * q + 1] * wgt) << 16);
-            uint32_t p1 = f32_to_bf16_rne(acc[f][g][4 * q + 2] * wgt) |
-                          (f32_to_bf16_rne(acc[f][g][4 * q + 3] * wgt) << 16);
-            *(uint2*)(dst + n) = make_uint2(p0, p1);
-          }
-        }
-    }
+    store_tile_bf16(a, t, acc, wn, wm, lane, 1.0f);
   } else {
     // L1: gate in acc[f][g], up in acc[f + 2][g] for f = 0, 1.
     const int I = a.n_rows;
@@ -496,6 +424,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
   }
 }
 
+}  // namespace
+
 // Compute units of the current device (cached per device).
 int cu_count() {
   static std::atomic<int> cache[64];
@@ -507,8 +437,6 @@ int cu_count() {
   cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
-
-}  // namespace
 
 hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;

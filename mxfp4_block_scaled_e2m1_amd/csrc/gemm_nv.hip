@@ -1,0 +1,185 @@
+// L2 down GEMM of the NVFP4 re-quantisation variant, on bf16 matrix cores.
+//
+// The intermediate h arrives as NVFP4: E2M1 codes, one E4M3 scale per 16
+// columns and an fp32 global scale g (page "Current Bug: vLLM produces
+// empty/garbage output", section "Revised Plan", Phase 1 names the warm-up
+// based global scale of the runner; the pages do not spell the format out, so
+// the block of 16 with an E4M3 scale is the plain reading of the name). The
+// weights stay MXFP4 (page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization",
+// section "FP4 (E2M1) expert weight format confirmed").
+//
+// The scaled FP4 MFMA of gfx950 takes one E8M0 (power of two) scale per 32 K
+// values, which cannot carry an E4M3 scale per 16. Both operands are therefore
+// dequantised into bf16, exactly:
+//  * w: code * 2^(e-127) has at most 2 significant bits; exact in bf16 for
+//    scale bytes up to 252 (above that, 6 * 2^126 exceeds the bf16 range).
+//  * h: code * s with s an E4M3 value: at most 2 + 4 significant bits, exact.
+// The product sum runs in fp32 (V_MFMA_F32_32X32X16_BF16) and the epilogue
+// multiplies by g (and, for routed experts, by the gate weight), so
+// y = g * sum_k (code_h * s_h)(code_w * 2^e_w) up to fp32 summation order.
+//
+// Design: persistent 512-thread workgroups on 256 x 256 tiles, the same tile
+// order and XCD mapping as the FP4 kernel. Per 64-wide K stage each thread
+// loads 16 code bytes of one weight row and 16 of one token row (plus their
+// scale bytes) into registers one stage ahead, and after the MFMAs of the
+// current stage converts them and writes the bf16 tile into the other of two
+// 64 KB LDS slots. Every operand element is converted once per workgroup.
+#include "gemm_common.h"
+
+namespace mx {
+
+namespace {
+
+constexpr int NV_BK = 64;                   // logical K per stage
+constexpr int NV_ROW = NV_BK * 2;           // 128 bytes of bf16 per row per stage
+constexpr int NV_OPND = BN * NV_ROW;        // 32 KB per operand tile
+constexpr int NV_SLOT = 2 * NV_OPND;        // weight tile + token tile
+static_assert(BN == 256 && BM == 256, "the copy assignment below assumes 256-row tiles");
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// LDS byte offset of 16-byte chunk c (0..7) of row r of an operand tile. The
+// chunk index is XORed with (r/2) % 8 so the 16 rows a quarter-wave reads for
+// one MFMA fall in distinct banks.
+__device__ __forceinline__ int nv_off(int r, int c) { return r * NV_ROW + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// One thread's raw bytes of a stage: 32 logical columns of a weight row and of
+// a token row.
+struct NvRaw {
+  uint4 wc;         // 16 MXFP4 code bytes
+  uint32_t we;      // their E8M0 scale byte
+  uint4 hc;         // 16 NVFP4 code bytes
+  uint32_t hs;      // their two E4M3 scale bytes (16 columns each)
+};
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// MXFP4 -> bf16 for one dword of codes (8 columns): code * 2^(e-127), exact.
+__device__ __forceinline__ uint4 w_to_bf16(uint32_t d, uint32_t e) {
+  if (e == 0xFFu) return make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);   // NaN scale
+  const float sc = e8m0_to_f32(e);
+  return make_uint4(dequant_pair<0>(d, sc), dequant_pair<1>(d, sc), dequant_pair<2>(d, sc),
+                    dequant_pair<3>(d, sc));
+}
+
+// NVFP4 codes -> bf16 for one dword (8 columns) with block scale s: code * s,
+// exact in fp32 and in bf16 (at most 6 significant bits).
+__device__ __forceinline__ uint4 h_to_bf16(uint32_t d, float s) {
+  uint32_t r[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f32x2 v;
+    if (b == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+    else if (b == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+    else if (b == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+    else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+    r[b] = bf16_pair(v[0] * s, v[1] * s);
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// One 256 x 256 tile of o = g * h . w^T (h NVFP4, w MXFP4).
+__device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_t* smem) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave >> 2, wm = wave & 3;
+  const int K = a.k;
+  const int kb = K >> 1, kse = K >> 5, ksn = K >> 4;   // code bytes, E8M0 and E4M3 bytes per row
+  const int nst = K / NV_BK;
+
+  // copy assignment: row R = tid / 2 of both tiles, columns (tid & 1) * 32 .. +31
+  const int R = tid >> 1, half = tid & 1;
+  const int wrow = min(t.nt * BN + R, a.n_rows - 1);
+  const uint8_t* wsrc = a.wa + (int64_t)t.e * a.w_estride + (int64_t)wrow * kb + half * 16;
+  const uint8_t* wesrc = a.wa_s + (int64_t)t.e * a.ws_estride + (int64_t)wrow * kse + half;
+  const int hrow = t.row0 + min(R, t.rows - 1);
+  const uint8_t* hsrc = a.x + (int64_t)hrow * kb + half * 16;
+  const uint8_t* hssrc = a.x_s + (int64_t)hrow * ksn + half * 2;
+
+  auto load = [&](int st, NvRaw& r) {
+    r.wc = *(const uint4*)(wsrc + st * (NV_BK / 2));
+    r.we = wesrc[st * (NV_BK / 32)];
+    r.hc = *(const uint4*)(hsrc + st * (NV_BK / 2));
+    r.hs = *(const uint16_t*)(hssrc + st * (NV_BK / 16));
+  };
+  auto store = [&](int slot, const NvRaw& r) {
+    uint8_t* wt = smem + slot * NV_SLOT;
+    uint8_t* ht = wt + NV_OPND;
+    const uint32_t wd[4] = {r.wc.x, r.wc.y, r.wc.z, r.wc.w};
+    const uint32_t hd[4] = {r.hc.x, r.hc.y, r.hc.z, r.hc.w};
+    const float s0 = e4m3_to_f32(r.hs & 0xFFu), s1 = e4m3_to_f32(r.hs >> 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(uint4*)(wt + nv_off(R, half * 4 + i)) = w_to_bf16(wd[i], r.we);
+      *(uint4*)(ht + nv_off(R, half * 4 + i)) = h_to_bf16(hd[i], i < 2 ? s0 : s1);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[f][g][v] = 0.0f;
+
+  const int r32 = lane & 31, hh = lane >> 5;
+  NvRaw raw;
+  load(0, raw);
+  store(0, raw);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const bool more = st + 1 < nst;
+    if (more) load(st + 1, raw);
+    const uint8_t* wt = smem + (st & 1) * NV_SLOT;
+    const uint8_t* ht = wt + NV_OPND;
+#pragma unroll
+    for (int k16 = 0; k16 < NV_BK / 16; ++k16) {
+      const int c = k16 * 2 + hh;   // lane half hh holds K values 8*hh .. 8*hh+7 of the step
+      uint4 A[4], B[2];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) A[f] = *(const uint4*)(wt + nv_off(wn * 128 + f * 32 + r32, c));
+#pragma unroll
+      for (int g = 0; g < 2; ++g) B[g] = *(const uint4*)(ht + nv_off(wm * 64 + g * 32 + r32, c));
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[f]), as_bf16x8(B[g]), acc[f][g], 0, 0, 0);
+    }
+    if (more) store((st + 1) & 1, raw);   // the other slot: its last reads were before the previous barrier
+    __syncthreads();
+  }
+  store_tile_bf16(a, t, acc, wn, wm, lane, a.nv_global);
+}
+
+// Persistent kernel with the tile order and XCD mapping of the FP4 GEMM.
+__global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm_nv(const GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_SLOT];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3, per_xcd_wgs = gridDim.x >> 3;
+  const int total = tile_count(a);
+  const int per = (total + 7) >> 3;
+  const int end = min((xcd + 1) * per, total);
+  for (int L = xcd * per + local; L < end; L += per_xcd_wgs) {
+    nv_tile(a, decode_tile(a, L), smem);
+    __syncthreads();   // the next tile's first stores overwrite slot 0
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nv_l2(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  const int cus = cu_count();
+  const int grid = ((max_tiles < cus ? max_tiles : cus) + 7) & ~7;
+  k_gemm_nv<<<grid, GEMM_THREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mx

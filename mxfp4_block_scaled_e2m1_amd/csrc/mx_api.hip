@@ -84,8 +84,8 @@ struct Carve {
   }
 };
 
-// Dense (one expert) workspace. Prefill: xq, xs, hq, hs. Few-token path
-// (M <= 32): h, the bf16 SiLU output, at the same offset as xq.
+// Dense (one expert) workspace. GEMM path: xq, xs, hq, hs. Few-token path
+// (M <= 8, MXFP4 re-quantisation): h, the bf16 SiLU output, at the offset of xq.
 struct DenseWs {
   uint8_t *xq, *xs, *hq, *hs;
   uint16_t* h;
@@ -94,7 +94,7 @@ struct DenseWs {
 DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
   Carve c(base);
   DenseWs w;
-  if (decode_fits(M, H, I)) {
+  if (rq == MX_FMT_MXFP4 && decode_fits(M, H, I)) {
     w.h = (uint16_t*)c.take((size_t)(M * I * 2));
     w.xq = w.xs = w.hq = w.hs = nullptr;
   } else {
@@ -143,18 +143,16 @@ mx_status check_mlp_dims(int64_t M, int64_t H, int64_t I) {
   return MX_OK;
 }
 
-mx_status check_requant(mx_format rq, float g) {
-  if (rq == MX_FMT_MXFP4) return MX_OK;
-  if (rq == MX_FMT_NVFP4)
-    return fail(MX_ERR_FORMAT, "NVFP4 re-quantisation needs the bf16 L2 path, which this build does not have");
-  (void)g;
-  return fail(MX_ERR_FORMAT, "requant format %d is not MXFP4 or NVFP4", (int)rq);
-}
-
 mx_status check_global(float g) {
   if (!std::isfinite(g) || !(g >= 0x1p-117f))
     return fail(MX_ERR_VALUE, "NVFP4 global scale %g must be finite and >= 2^-117", (double)g);
   return MX_OK;
+}
+
+mx_status check_requant(mx_format rq, float g) {
+  if (rq == MX_FMT_MXFP4) return MX_OK;
+  if (rq == MX_FMT_NVFP4) return check_global(g);
+  return fail(MX_ERR_FORMAT, "requant format %d is not MXFP4 or NVFP4", (int)rq);
 }
 
 #define MX_REQUIRE_PTR(p) \
@@ -373,7 +371,8 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
   l1.grid_tiles = ((m + BM - 1) / BM) * l1.n_tiles;
   l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_global = requant_global;
-  MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(EPI_SWIGLU_MXFP4, l1, l1.grid_tiles, s); }), "l1_gemm");
+  const Epilogue l1_epi = requant == MX_FMT_NVFP4 ? EPI_SWIGLU_NVFP4 : EPI_SWIGLU_MXFP4;
+  MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(l1_epi, l1, l1.grid_tiles, s); }), "l1_gemm");
 
   GemmArgs l2 = base_args();
   l2.wa = w2; l2.wa_s = w2_s;
@@ -383,7 +382,12 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   l2.n_tiles = (H + BN - 1) / BN;
   l2.grid_tiles = ((m + BM - 1) / BM) * l2.n_tiles;
   l2.out_bf16 = y;
-  MX_HIP(phase("l2_gemm", s, [&] { return launch_gemm(EPI_BF16, l2, l2.grid_tiles, s); }), "l2_gemm");
+  if (requant == MX_FMT_NVFP4) {
+    l2.nv_global = requant_global;
+    MX_HIP(phase("l2_gemm_bf16", s, [&] { return launch_gemm_nv_l2(l2, l2.grid_tiles, s); }), "l2_gemm_bf16");
+  } else {
+    MX_HIP(phase("l2_gemm", s, [&] { return launch_gemm(EPI_BF16, l2, l2.grid_tiles, s); }), "l2_gemm");
+  }
   return ok();
 }
 
@@ -429,8 +433,8 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l1.expert_off = w.rb.expert_off; l1.tile_base = w.rb.tile_base; l1.n_experts = E;
   l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
   l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_global = requant_global;
-  MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(EPI_SWIGLU_MXFP4, l1, max_mtiles * l1.n_tiles, s); }),
-         "l1_gemm");
+  const Epilogue l1_epi = requant == MX_FMT_NVFP4 ? EPI_SWIGLU_NVFP4 : EPI_SWIGLU_MXFP4;
+  MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(l1_epi, l1, max_mtiles * l1.n_tiles, s); }), "l1_gemm");
 
   GemmArgs l2 = base_args();
   l2.wa = w2; l2.wa_s = w2_s;
@@ -440,7 +444,13 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l2.expert_off = w.rb.expert_off; l2.tile_base = w.rb.tile_base; l2.n_experts = E;
   l2.n_tiles = (H + BN - 1) / BN;
   l2.out_bf16 = w.o; l2.row_slot = w.rb.row_slot; l2.slot_weight = topk_w;
-  MX_HIP(phase("l2_gemm", s, [&] { return launch_gemm(EPI_BF16, l2, max_mtiles * l2.n_tiles, s); }), "l2_gemm");
+  if (requant == MX_FMT_NVFP4) {
+    l2.nv_global = requant_global;
+    MX_HIP(phase("l2_gemm_bf16", s, [&] { return launch_gemm_nv_l2(l2, max_mtiles * l2.n_tiles, s); }),
+           "l2_gemm_bf16");
+  } else {
+    MX_HIP(phase("l2_gemm", s, [&] { return launch_gemm(EPI_BF16, l2, max_mtiles * l2.n_tiles, s); }), "l2_gemm");
+  }
 
   MX_HIP(phase("combine", s, [&] { return launch_combine(w.o, topk_ids, T, k, E, H, y, s); }), "combine");
   return ok();

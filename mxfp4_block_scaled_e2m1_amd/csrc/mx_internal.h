@@ -65,6 +65,14 @@ struct GemmArgs {
 // its exact count on the device); the kernel is persistent with one workgroup per CU.
 hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int max_tiles, hipStream_t s);
 
+// L2 of the NVFP4 re-quantisation variant: x/x_s are NVFP4 h codes and E4M3
+// scales per 16 columns, nv_global the fp32 global scale; bf16 matrix cores on
+// exactly dequantised operands, output as EPI_BF16 times nv_global.
+hipError_t launch_gemm_nv_l2(const GemmArgs& a, int max_tiles, hipStream_t s);
+
+// Compute units of the current device (cached per device).
+int cu_count();
+
 // ---- Elementwise kernels ---------------------------------------------------
 hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                 int64_t cols, uint16_t* out, hipStream_t s);

@@ -71,3 +71,20 @@ def assert_requant_close(gpu_codes, gpu_scales, ref_codes, ref_scales, min_equal
     step = 2.0 * np.ldexp(1.0, np.maximum(sg, sr) - 127)     # widest E2M1 step (4 -> 6)
     assert np.all(np.abs(ga - ra) <= step), np.abs(ga - ra).max()
     return frac
+
+
+def assert_nvfp4_requant_close(gpu_codes, gpu_scales, ref_codes, ref_scales, g, min_equal=0.999):
+    """NVFP4 re-quantised h: >= 99.9 % equal codes (+0 == -0) and E4M3 block
+    scales; each code mismatch within one E2M1 grid step at the larger of the two
+    dequantised block scales s * g."""
+    gn, rn = nibbles(gpu_codes), nibbles(ref_codes)
+    grid = np.array(pins.E2M1_GRID + [-v for v in pins.E2M1_GRID])
+    gv, rv = grid[gn], grid[rn]
+    frac = (gv == rv).mean()
+    assert frac >= min_equal, frac
+    assert (np.asarray(gpu_scales) == np.asarray(ref_scales)).mean() >= min_equal
+    sg = np.repeat(pins.e4m3_values()[np.asarray(gpu_scales, np.int64)], 16, axis=-1) * g
+    sr = np.repeat(pins.e4m3_values()[np.asarray(ref_scales, np.int64)], 16, axis=-1) * g
+    step = 2.0 * np.maximum(sg, sr)
+    assert np.all(np.abs(gv * sg - rv * sr) <= step), np.abs(gv * sg - rv * sr).max()
+    return frac

@@ -79,6 +79,12 @@ def _e4m3_fraction(b):
     return -mag if s else mag
 
 
+def e4m3_values():
+    """The 256 E4M3fn code values from the bit-field definition (NaN for 0x7F, 0xFF)."""
+    return np.array([float("nan") if _e4m3_fraction(b) is None else float(_e4m3_fraction(b))
+                     for b in range(256)])
+
+
 def check_e4m3(O):
     got = O.e4m3_decode(np.arange(256).astype(np.uint8))
     finite = 0

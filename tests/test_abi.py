@@ -74,9 +74,12 @@ def test_mlp_validation(L):
     # hidden not a multiple of 128
     assert L.mx_expert_mlp(P(256), 4, 200, 128, *z, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
     assert L.mx_expert_mlp(P(256), 4, 256, 96, *z, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
-    # NVFP4 re-quant is refused by this build, unknown formats too
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 2, 1.0, P(256), P(256), 1 << 30, None) == 4
+    # NVFP4 re-quant needs a finite global scale >= 2^-117; FP8 is not a re-quant format
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 2, 0.0, P(256), P(256), 1 << 30, None) == 7
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 2, float("nan"), P(256), P(256), 1 << 30, None) == 7
     assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 1, 0.0, P(256), P(256), 1 << 30, None) == 4
+    # NVFP4 keeps one E4M3 byte per 16 columns of h: a larger workspace than MXFP4
+    assert L.mx_expert_mlp_workspace_size(64, 256, 128, 2) > L.mx_expert_mlp_workspace_size(64, 256, 128, 0)
     # workspace too small
     need = L.mx_expert_mlp_workspace_size(4, 256, 128, 0)
     assert need > 0

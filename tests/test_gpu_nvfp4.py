@@ -1,0 +1,143 @@
+"""Parity of the NVFP4 re-quantisation variant (E4M3 per 16 + fp32 global scale
+between the two GEMMs; bf16 matrix cores for L2) with the oracle.
+
+The global scale g comes from the oracle's warm-up reading (max |h| / (6 * 448)
+over a warm-up pass): over every (token, expert) pair for the small cases and
+over the first tokens for the 16384-token case, whose full warm-up would take
+the fp64 oracle hours."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import assert_mlp_close, assert_nvfp4_requant_close, bf16_t, bits, t
+
+pytestmark = pytest.mark.gpu
+
+WNAMES = ("w1", "w1s", "w3", "w3s", "w2", "w2s")
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import mxfp4_block_scaled_e2m1_amd as m
+    return m
+
+
+def _warmup_dense(d):
+    _, inter = O.expert_mlp(d["x"], *(d[n] for n in WNAMES), intermediates=True)
+    return float(O.nvfp4_warmup_global(inter["h"]))
+
+
+def _warmup_grouped(d, tokens):
+    """max |h| over the (token, expert) pairs of `tokens` -> g."""
+    amax = 0.0
+    ids = d["ids"][tokens]
+    E = d["w1"].shape[0]
+    for e in range(E):
+        tt = np.nonzero((ids == e).any(axis=1))[0]
+        if tt.size == 0:
+            continue
+        we = {n: d[n][e] for n in WNAMES}
+        _, inter = O.expert_mlp(d["x"][tokens][tt], *(we[n] for n in WNAMES), intermediates=True)
+        amax = max(amax, float(np.abs(O.bf16_to_f64(inter["h"])).max()))
+    return float(np.float32(amax / (6.0 * 448.0)))
+
+
+def _run_dense_nv(mx, d, M, H, I, g):
+    nbytes = mx.expert_mlp_workspace_size(M, H, I, "nvfp4")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = mx.expert_mlp(bf16_t(d["x"]), *(t(d[n]) for n in WNAMES), requant="nvfp4", requant_global=g,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    # GEMM-path workspace: xq, xs, hq, hs (E4M3 per 16), regions 256-byte aligned
+    off, sl = 0, []
+    for n in (M * H // 2, M * H // 32, M * I // 2, M * I // 16):
+        sl.append(ws[off:off + n])
+        off += (n + 255) // 256 * 256
+    return bits(y), sl
+
+
+@pytest.mark.parametrize("M,H,I", [(16, 256, 128), (1, 256, 128), (48, 512, 256)])
+def test_nvfp4_dense_small(mx, M, H, I):
+    d = W.tiny_mlp(0) if H == 256 else W.shared_expert(M, seed=4, hidden=H, inter=I)
+    d["x"] = d["x"][:M]
+    g = _warmup_dense(d)
+    y, (xq, xs, hq, hs) = _run_dense_nv(mx, d, M, H, I, g)
+    ref, inter = O.expert_mlp(d["x"], *(d[n] for n in WNAMES), requant="nvfp4", nv_global=g, intermediates=True)
+    assert np.array_equal(xq.cpu().numpy().reshape(M, H // 2), inter["xq"])
+    assert_nvfp4_requant_close(hq.cpu().numpy().reshape(M, I // 2), hs.cpu().numpy().reshape(M, I // 16),
+                               inter["hq"], inter["hs"], g)
+    assert_mlp_close(y, ref)
+
+
+@pytest.mark.parametrize("M", [1, 8, 300])
+def test_nvfp4_shared_expert_real_shape(mx, M):
+    d = W.shared_expert(M, seed=0)
+    g = _warmup_dense(d)
+    y, (_, _, hq, hs) = _run_dense_nv(mx, d, M, 7168, 3072, g)
+    ref, inter = O.expert_mlp(d["x"], *(d[n] for n in WNAMES), requant="nvfp4", nv_global=g, intermediates=True)
+    assert_nvfp4_requant_close(hq.cpu().numpy().reshape(M, 1536), hs.cpu().numpy().reshape(M, 192),
+                               inter["hq"], inter["hs"], g)
+    assert_mlp_close(y, ref)
+
+
+def test_nvfp4_global_scale_is_linear(mx):
+    """Doubling g halves every E4M3 block scale exactly (while they stay normal:
+    s >= 2^-5 before halving) and leaves every code and every output bit as is:
+    the dequantised values code * s * g do not change."""
+    d = W.shared_expert(40, seed=6, hidden=512, inter=256)
+    g = _warmup_dense(d)
+    y1, (_, _, hq1, hs1) = _run_dense_nv(mx, d, 40, 512, 256, g)
+    y2, (_, _, hq2, hs2) = _run_dense_nv(mx, d, 40, 512, 256, 2 * g)
+    s1 = O.e4m3_decode(hs1.cpu().numpy())
+    s2 = O.e4m3_decode(hs2.cpu().numpy())
+    nz = s1 != 0
+    assert np.all(np.abs(s1[nz]) >= 2.0 ** -5)      # precondition of the exact halving
+    assert np.array_equal(s2[nz], s1[nz] / 2)
+    assert np.array_equal(hq1.cpu().numpy(), hq2.cpu().numpy())
+    assert np.array_equal(y1, y2)
+
+
+def _run_grouped_nv(mx, d, g):
+    y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]), *(t(d[n]) for n in WNAMES),
+                              requant="nvfp4", requant_global=g)
+    torch.cuda.synchronize()
+    return bits(y)
+
+
+def test_nvfp4_grouped_multi_tile(mx):
+    d = W.grouped(tokens=600, n_experts=8, k=4, seed=5, hidden=512, inter=256)
+    g = _warmup_grouped(d, np.arange(600))
+    y = _run_grouped_nv(mx, d, g)
+    ref = O.grouped_expert_mlp(d["x"], d["ids"], d["w"], *(d[n] for n in WNAMES), requant="nvfp4", nv_global=g)
+    assert_mlp_close(y, ref)
+
+
+def test_nvfp4_grouped_single_expert_equals_shared(mx):
+    d = W.shared_expert(200, seed=2, hidden=512, inter=256)
+    g = _warmup_dense(d)
+    gd = {n: d[n][None] for n in WNAMES}
+    gd.update(x=d["x"], ids=np.zeros((200, 1), np.int32), w=np.ones((200, 1), np.float32))
+    yg = _run_grouped_nv(mx, gd, g)
+    yd, _ = _run_dense_nv(mx, d, 200, 512, 256, g)
+    assert np.array_equal(yg, yd)
+
+
+def test_nvfp4_skewed_sampled_tokens_and_decode_tail(mx):
+    """The skewed 16384-token case with NVFP4 re-quantisation, plus its 8-token
+    decode tail over the same weights."""
+    d = W.skewed(tokens=16384, seed=0)
+    g = _warmup_grouped(d, np.arange(16))
+    y = _run_grouped_nv(mx, d, g)
+    tok = np.array([3, 16383])
+    ref = O.grouped_expert_mlp(d["x"], d["ids"], d["w"], *(d[n] for n in WNAMES), requant="nvfp4", nv_global=g,
+                               tokens=tok)
+    assert_mlp_close(y[tok], ref)
+    assert np.all(np.isfinite(((y.astype(np.uint32) << 16).view(np.float32))))
+    tail = dict(d, x=d["x"][:8], ids=d["ids"][:8], w=d["w"][:8])
+    yt = _run_grouped_nv(mx, tail, g)
+    reft = O.grouped_expert_mlp(tail["x"], tail["ids"], tail["w"], *(d[n] for n in WNAMES), requant="nvfp4",
+                                nv_global=g)
+    assert_mlp_close(yt, reft)
