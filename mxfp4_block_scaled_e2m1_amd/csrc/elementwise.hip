@@ -1,5 +1,5 @@
-// Streaming dequant / quantise kernels (HBM-bound): 16-byte loads, VALU decode,
-// 16-byte stores, grid-stride loops over blocks.
+// Streaming dequant / quantise kernels (HBM-bound): VALU decode between loads
+// and stores that are contiguous across the lanes of each wave instruction.
 //
 // * MXFP4 dequant: page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", section
 //   "Script update", item 2 (E2M1 codes two per byte, low nibble first, times the
@@ -21,6 +21,7 @@ namespace mx {
 namespace {
 
 constexpr int EW_THREADS = 256;
+constexpr int EW_UNROLL = 4;   // units per thread per pass: all loads of a pass are in flight together
 
 inline int ew_grid(int64_t work) {
   int64_t g = (work + EW_THREADS - 1) / EW_THREADS;
@@ -28,66 +29,91 @@ inline int ew_grid(int64_t work) {
   return (int)(g < 1 ? 1 : g);
 }
 
-// One thread per 32-element block: 16 code bytes + 1 scale byte -> 64 output bytes.
-__global__ __launch_bounds__(EW_THREADS) void k_dequant_mxfp4(const uint4* __restrict__ codes,
+// Grid for the unit kernels below: a workgroup pass covers EW_THREADS * EW_UNROLL units.
+inline int ew_grid_units(int64_t units) {
+  const int64_t per = (int64_t)EW_THREADS * EW_UNROLL;
+  int64_t g = (units + per - 1) / per;
+  if (g > 4096) g = 4096;
+  return (int)(g < 1 ? 1 : g);
+}
+
+// The unit kernels walk units u = pass base + j * EW_THREADS + tid (j < EW_UNROLL),
+// so every wave instruction touches one contiguous span: loads of 64 lanes x
+// 4..16 bytes and stores of 64 lanes x 4..16 bytes. Loads are unconditional
+// (clamped to the last unit) and only the stores test the bound.
+#define EW_FOR_PASSES(units)                                                               \
+  for (int64_t base = (int64_t)blockIdx.x * EW_THREADS * EW_UNROLL; base < (units);     \
+       base += (int64_t)gridDim.x * EW_THREADS * EW_UNROLL)
+
+// MXFP4 dequant. Unit u = code dword u: elements 8u .. 8u+7 -> 16 output bytes;
+// its scale is byte u / 4 (a 32-block is 4 dwords; rows hold whole blocks).
+__global__ __launch_bounds__(EW_THREADS) void k_dequant_mxfp4(const uint32_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ scales,
-                                                              uint4* __restrict__ out, int64_t nblk) {
-  const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
-  for (int64_t b = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; b < nblk; b += stride) {
-    const uint4 c = codes[b];
-    const uint32_t sb = scales[b];
-    uint4 o[4];
-    if (sb == 255u) {
-      const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-      o[0] = o[1] = o[2] = o[3] = nan4;
-    } else {
-      const float sc = e8m0_to_f32(sb);
-      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+                                                              uint4* __restrict__ out, int64_t units) {
+  EW_FOR_PASSES(units) {
+    uint32_t c[EW_UNROLL], sb[EW_UNROLL];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = make_uint4(dequant_pair<0>(w[i], sc), dequant_pair<1>(w[i], sc),
-                          dequant_pair<2>(w[i], sc), dequant_pair<3>(w[i], sc));
+    for (int j = 0; j < EW_UNROLL; ++j) {
+      const int64_t u = min(base + j * EW_THREADS + (int64_t)threadIdx.x, units - 1);
+      c[j] = codes[u];
+      sb[j] = scales[u >> 2];
     }
-    uint4* dst = out + b * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = o[i];
+    for (int j = 0; j < EW_UNROLL; ++j) {
+      const int64_t u = base + j * EW_THREADS + (int64_t)threadIdx.x;
+      uint4 o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);   // scale byte 255: NaN
+      if (sb[j] != 255u) {
+        const float sc = e8m0_to_f32(sb[j]);
+        o = make_uint4(dequant_pair<0>(c[j], sc), dequant_pair<1>(c[j], sc), dequant_pair<2>(c[j], sc),
+                       dequant_pair<3>(c[j], sc));
+      }
+      if (u < units) out[u] = o;
+    }
   }
 }
 
-// e4m3 x 2^(sb-127) -> bf16, exact in fp32 (fp32 denormals kept) then one RNE.
-__device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t byte, float sc) {
-  return f32_to_bf16_rne(e4m3_to_f32(byte) * sc);
+// Two E4M3 codes (low or high 16 bits of `w`) times the scale sc = 2^(sb-127)
+// -> a bf16 pair, rounded to nearest even (V_CVT_SCALEF32_PK_BF16_FP8). The NaN
+// codes (0x7F, 0xFF) give the canonical quiet NaN 0x7FC0 whatever their sign.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_pair_to_bf16(uint32_t w, float sc) {
+  uint32_t r = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, HI));
+  const uint32_t c = HI ? (w >> 16) : w;
+  if ((c & 0x7Fu) == 0x7Fu) r = (r & 0xFFFF0000u) | 0x7FC0u;
+  if (((c >> 8) & 0x7Fu) == 0x7Fu) r = (r & 0x0000FFFFu) | 0x7FC00000u;
+  return r;
 }
 
-// One thread per 16 elements (one 16-byte load) of a row; cols % 16 == 0.
-__global__ __launch_bounds__(EW_THREADS) void k_dequant_fp8_block(const uint4* __restrict__ q,
+// FP8 block dequant. Unit u = 8 codes (elements 8u .. 8u+7 of the row-major
+// matrix, one row and one 128-column block since cols % 128 == 0) -> 16 bytes.
+template <typename Idx>
+__global__ __launch_bounds__(EW_THREADS) void k_dequant_fp8_block(const uint2* __restrict__ q,
                                                                   const uint8_t* __restrict__ scales,
-                                                                  int64_t cols, int64_t gcols,
-                                                                  uint4* __restrict__ out, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
-  const int64_t per_row = cols >> 4;
-  for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < n16; i += stride) {
-    const int64_t r = i / per_row;
-    const int64_t c0 = (i - r * per_row) << 4;
-    const uint32_t sb = scales[(r >> 7) * gcols + (c0 >> 7)];
-    const uint4 v = q[i];
-    uint4 o0, o1;
-    if (sb == 255u) {
-      o0 = o1 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-    } else {
-      const float sc = e8m0_to_f32(sb);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t p[8];
+                                                                  Idx cols, Idx gcols, uint4* __restrict__ out,
+                                                                  int64_t units) {
+  EW_FOR_PASSES(units) {
+    uint2 v[EW_UNROLL];
+    uint32_t sb[EW_UNROLL];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        p[2 * k] = fp8_to_bf16(w[k] & 0xFFu, sc) | (fp8_to_bf16((w[k] >> 8) & 0xFFu, sc) << 16);
-        p[2 * k + 1] = fp8_to_bf16((w[k] >> 16) & 0xFFu, sc) | (fp8_to_bf16(w[k] >> 24, sc) << 16);
-      }
-      o0 = make_uint4(p[0], p[1], p[2], p[3]);
-      o1 = make_uint4(p[4], p[5], p[6], p[7]);
+    for (int j = 0; j < EW_UNROLL; ++j) {
+      const int64_t u = min(base + j * EW_THREADS + (int64_t)threadIdx.x, units - 1);
+      const Idx e = (Idx)u * 8;
+      const Idx r = e / cols, c = e - r * cols;
+      v[j] = q[u];
+      sb[j] = scales[(r >> 7) * gcols + (c >> 7)];
     }
-    out[2 * i] = o0;
-    out[2 * i + 1] = o1;
+#pragma unroll
+    for (int j = 0; j < EW_UNROLL; ++j) {
+      const int64_t u = base + j * EW_THREADS + (int64_t)threadIdx.x;
+      uint4 o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);   // scale byte 255: NaN
+      if (sb[j] != 255u) {
+        // hardware convert of two E4M3 codes times a power-of-two scale to bf16
+        const float sc = e8m0_to_f32(sb[j]);
+        o = make_uint4(fp8_pair_to_bf16<false>(v[j].x, sc), fp8_pair_to_bf16<true>(v[j].x, sc),
+                       fp8_pair_to_bf16<false>(v[j].y, sc), fp8_pair_to_bf16<true>(v[j].y, sc));
+      }
+      if (u < units) out[u] = o;
+    }
   }
 }
 
@@ -131,35 +157,34 @@ __global__ __launch_bounds__(EW_THREADS) void k_dequant_nvfp4(const uint2* __res
   }
 }
 
-// MXFP4 quantise: one thread per 32 elements (64 bytes of bf16 in, 16 code bytes
-// and one scale byte out).
+// MXFP4 quantise. Unit u = 8 elements (16 bytes of bf16 in, one code dword
+// out); the 4 units of a 32-block are 4 consecutive lanes, which combine their
+// amax with two lane exchanges. The first lane of the four writes the scale.
 __global__ __launch_bounds__(EW_THREADS) void k_quant_mxfp4(const uint4* __restrict__ x,
-                                                            uint4* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales, int64_t nblk) {
-  const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
-  for (int64_t b = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; b < nblk; b += stride) {
-    uint32_t w[16];
+                                                            uint32_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales, int64_t units) {
+  EW_FOR_PASSES(units) {
+    uint4 v[EW_UNROLL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = x[b * 4 + i];
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-    }
-    uint32_t am = 0;
+    for (int j = 0; j < EW_UNROLL; ++j) v[j] = x[min(base + j * EW_THREADS + (int64_t)threadIdx.x, units - 1)];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) am = max(am, amax2(w[i]));
-    const uint32_t sb = mx_scale_from_amax_bits(am);
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < EW_UNROLL; ++j) {
+      const int64_t u = base + j * EW_THREADS + (int64_t)threadIdx.x;
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      uint32_t am = max(max(amax2(w[0]), amax2(w[1])), max(amax2(w[2]), amax2(w[3])));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 2));
+      const uint32_t sb = mx_scale_from_amax_bits(am);
       uint32_t r = 0;
-      r = quant_pair_e8m0<0>(r, w[4 * i], sb);
-      r = quant_pair_e8m0<1>(r, w[4 * i + 1], sb);
-      r = quant_pair_e8m0<2>(r, w[4 * i + 2], sb);
-      r = quant_pair_e8m0<3>(r, w[4 * i + 3], sb);
-      o[i] = r;
+      r = quant_pair_e8m0<0>(r, w[0], sb);
+      r = quant_pair_e8m0<1>(r, w[1], sb);
+      r = quant_pair_e8m0<2>(r, w[2], sb);
+      r = quant_pair_e8m0<3>(r, w[3], sb);
+      if (u < units) {
+        codes[u] = r;
+        if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sb;
+      }
     }
-    codes[b] = make_uint4(o[0], o[1], o[2], o[3]);
-    scales[b] = (uint8_t)sb;
   }
 }
 
@@ -209,19 +234,24 @@ __global__ __launch_bounds__(EW_THREADS) void k_quant_nvfp4(const uint4* __restr
 
 hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                 int64_t cols, uint16_t* out, hipStream_t s) {
-  const int64_t nblk = rows * (cols / 32);
-  if (nblk == 0) return hipSuccess;
-  k_dequant_mxfp4<<<ew_grid(nblk), EW_THREADS, 0, s>>>((const uint4*)codes, scales, (uint4*)out, nblk);
+  const int64_t units = rows * (cols / 8);
+  if (units == 0) return hipSuccess;
+  k_dequant_mxfp4<<<ew_grid_units(units), EW_THREADS, 0, s>>>((const uint32_t*)codes, scales, (uint4*)out,
+                                                              units);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant_fp8_block(const uint8_t* q, const uint8_t* scales, int64_t rows,
                                     int64_t cols, uint16_t* out, hipStream_t s) {
-  const int64_t n16 = rows * (cols / 16);
-  if (n16 == 0) return hipSuccess;
+  const int64_t units = rows * (cols / 8);
+  if (units == 0) return hipSuccess;
   const int64_t gcols = (cols + 127) / 128;
-  k_dequant_fp8_block<<<ew_grid(n16), EW_THREADS, 0, s>>>((const uint4*)q, scales, cols, gcols,
-                                                          (uint4*)out, n16);
+  if (rows * cols < ((int64_t)1 << 32))   // 32-bit element indexes: cheaper division
+    k_dequant_fp8_block<uint32_t><<<ew_grid_units(units), EW_THREADS, 0, s>>>(
+        (const uint2*)q, scales, (uint32_t)cols, (uint32_t)gcols, (uint4*)out, units);
+  else
+    k_dequant_fp8_block<uint64_t><<<ew_grid_units(units), EW_THREADS, 0, s>>>(
+        (const uint2*)q, scales, (uint64_t)cols, (uint64_t)gcols, (uint4*)out, units);
   return hipGetLastError();
 }
 
@@ -236,9 +266,9 @@ hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, flo
 
 hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s) {
-  const int64_t nblk = rows * (cols / 32);
-  if (nblk == 0) return hipSuccess;
-  k_quant_mxfp4<<<ew_grid(nblk), EW_THREADS, 0, s>>>((const uint4*)x, (uint4*)codes, scales, nblk);
+  const int64_t units = rows * (cols / 8);
+  if (units == 0) return hipSuccess;
+  k_quant_mxfp4<<<ew_grid_units(units), EW_THREADS, 0, s>>>((const uint4*)x, (uint32_t*)codes, scales, units);
   return hipGetLastError();
 }
 
