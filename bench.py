@@ -10,13 +10,21 @@ activations, all synthetic and resident in HBM before timing starts.
 Prints one JSON line. `value` is TFLOP/s over 6 * tokens * k * hidden * inter
 algorithmic FLOPs per step. `roofline` is for the dominant kernel (the L1
 GEMM), timed with HIP events recorded on the stream it runs on, during the
-timed steps. `cpu_baseline` times the CPU oracle on a bounded sample (all
-pairs routed to the first few experts).
+timed steps; its `traffic` is the HBM byte count per launch from rocprofv3
+FETCH_SIZE / WRITE_SIZE runs scaled by a copy of known size (see
+`L1_TRAFFIC`), reported only while the GEMM sources are the ones it was
+measured on. `cpu_baseline` times the CPU oracle on a bounded sample (all
+pairs routed to the first few experts). `secondary` holds the other
+configurations: the shared expert (few-token sizes replayed from a hipGraph
+over 16 rotating weight copies, so the weights come from HBM), the skewed
+16384-token batch with NVFP4 re-quantisation and its 8-token tail, and the
+dequant kernels.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,7 +37,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "expert-MLP TFLOP/s & frac of FP4 peak, 48 experts x 4096 tok top-8 (1 GPU)"
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+CALIB_COPY_BYTES = 1 << 28    # --calibration-copy: one device copy of 256 MiB (read 256 MiB, write 256 MiB)
+
+# HBM traffic of one L1 GEMM launch (48 x 4096 x top-8), from two rocprofv3 --pmc
+# runs of `bench.py --steps 2 --warmup 1 --no-secondary --no-cpu-baseline
+# --calibration-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same
+# counter reads for the calibration copy. Valid for the GEMM sources whose
+# digest is recorded; None otherwise.
+L1_TRAFFIC = None
+GEMM_SOURCES = ("gemm.hip", "gemm_common.h", "mx_device.h", "mx_internal.h")
 
 
 def parse():
@@ -39,9 +57,19 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=4,
+    ap.add_argument("--cpu-experts", type=int, default=16,
                     help="experts in the oracle's bounded CPU sample")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="run one device copy of known size first (for PMC byte-counter scaling)")
     return ap.parse_args()
+
+
+def gemm_digest():
+    h = hashlib.sha256()
+    for n in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mxfp4_block_scaled_e2m1_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def dev_tensors(torch, d, names):
@@ -67,50 +95,127 @@ def time_steps(torch, fn, steps, warmup, profile=None):
     return (t1 - t0) * 1e3 / steps, stats
 
 
+def graph_replay_us(torch, calls, reps=20):
+    """Capture `calls` (one list entry per rotating input set) into a hipGraph and
+    return the mean microseconds per call over `reps` replays."""
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls[0]()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+
+
 def secondary(torch, mx, workloads):
-    """Shared expert at decode/prefill sizes and dequant bandwidth (context lines)."""
+    """Shared expert, skewed NVFP4 batch and dequant bandwidth (context lines)."""
     out = {}
     H, I = workloads.HIDDEN, workloads.INTER
     d = workloads.expert_weights(0)
-    w = dev_tensors(torch, d, ("w1", "w1s", "w3", "w3s", "w2", "w2s"))
-    wbytes = sum(v.numel() for v in w.values())
-    for M in (1, 8, 128, 4096):
+    w0 = dev_tensors(torch, d, ("w1", "w1s", "w3", "w3s", "w2", "w2s"))
+    wbytes = sum(v.numel() for v in w0.values())
+    # 16 weight copies (~561 MB) so that successive calls miss the 256 MB cache
+    copies = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(15)]
+    for M in (1, 8, 128):
         x = bf16_dev(torch, workloads.activations(1, M))
         ws = torch.empty(mx.expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
         y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
-        fn = lambda: mx.expert_mlp(x, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"], out=y, workspace=ws)
-        ms, _ = time_steps(torch, fn, 20, 3)
-        flops = 6.0 * M * H * I
-        out[f"shared_expert_M{M}"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
-                                      "weight_GB/s": round(wbytes / ms / 1e6, 1)}
+        calls = [lambda w=w: mx.expert_mlp(x, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"], out=y,
+                                           workspace=ws) for w in copies]
+        us = graph_replay_us(torch, calls)
+        out[f"shared_expert_M{M}"] = {"us_per_call": round(us, 2), "weight_GB/s": round(wbytes / us / 1e3, 1),
+                                      "hbm_frac": round(wbytes / us / 1e3 / PEAK_HBM_GBS, 3),
+                                      "timing": "hipGraph replay, 16 rotating weight copies"}
+    del copies
+    M = 4096
+    x = bf16_dev(torch, workloads.activations(1, M))
+    ws = torch.empty(mx.expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: mx.expert_mlp(x, w0["w1"], w0["w1s"], w0["w3"], w0["w3s"], w0["w2"], w0["w2s"], out=y, workspace=ws)
+    ms, _ = time_steps(torch, fn, 20, 3)
+    flops = 6.0 * M * H * I
+    out["shared_expert_M4096"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
+                                  "frac_of_fp4_peak": round(flops / ms / 1e9 / PEAK_FP4_TFLOPS, 4)}
+    out.update(skewed_nvfp4(torch, mx, workloads))
     # dequant (8 rotating buffer sets so the working set exceeds the 256 MB cache)
     dq = workloads.dequant_inputs(0)
     c = torch.from_numpy(dq["w1"]).cuda()
     s = torch.from_numpy(dq["w1s"]).cuda()
     sets = [(c.clone(), s.clone(), torch.empty((3072, 7168), dtype=torch.bfloat16, device="cuda")) for _ in range(8)]
-    it = [0]
-
-    def deq():
-        cc, ss, oo = sets[it[0] % 8]
-        it[0] += 1
-        mx.dequant("mxfp4", cc, ss, 3072, 7168, out=oo)
-    ms, _ = time_steps(torch, deq, 40, 8)
+    calls = [lambda cc=cc, ss=ss, oo=oo: mx.dequant("mxfp4", cc, ss, 3072, 7168, out=oo) for cc, ss, oo in sets]
+    us = graph_replay_us(torch, calls)
     nbytes = c.numel() + s.numel() + 3072 * 7168 * 2
-    out["dequant_mxfp4_w1"] = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
-                               "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    out["dequant_mxfp4_w1"] = {"us_per_call": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                               "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3),
+                               "timing": "hipGraph replay, 8 rotating buffer sets"}
+    del sets
     q = torch.from_numpy(dq["fp8"]).cuda()
     qs = torch.from_numpy(dq["fp8s"]).cuda()
     qsets = [(q.clone(), qs.clone(), torch.empty((7168, 1536), dtype=torch.bfloat16, device="cuda")) for _ in range(8)]
-
-    def deq8():
-        cc, ss, oo = qsets[it[0] % 8]
-        it[0] += 1
-        mx.dequant("fp8_b128", cc, ss, 7168, 1536, out=oo)
-    ms, _ = time_steps(torch, deq8, 40, 8)
+    calls = [lambda cc=cc, ss=ss, oo=oo: mx.dequant("fp8_b128", cc, ss, 7168, 1536, out=oo) for cc, ss, oo in qsets]
+    us = graph_replay_us(torch, calls)
     nbytes = q.numel() + qs.numel() + 7168 * 1536 * 2
-    out["dequant_fp8_block"] = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
-                                "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    out["dequant_fp8_block"] = {"us_per_call": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3),
+                                "timing": "hipGraph replay, 8 rotating buffer sets"}
     return out
+
+
+def skewed_nvfp4(torch, mx, workloads):
+    """16384 tokens, Zipf(1.2) routing over 48 experts, NVFP4 re-quantisation of h.
+
+    The global scale is an input of the call; its value does not change the work
+    done, so a fixed power of two stands in for the warm-up value here."""
+    T, E, K = 16384, workloads.N_LOCAL_EXPERTS, workloads.TOP_K
+    H, I = workloads.HIDDEN, workloads.INTER
+    g = 2.0 ** -6
+    d = workloads.skewed(tokens=T, seed=0)
+    w = dev_tensors(torch, d, ("w1", "w1s", "w3", "w3s", "w2", "w2s", "ids", "w"))
+    x = bf16_dev(torch, d["x"])
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.grouped_expert_mlp_workspace_size(T, H, I, K, E, "nvfp4"), dtype=torch.uint8, device="cuda")
+
+    def step():
+        mx.grouped_expert_mlp(x, w["ids"], w["w"], w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
+                              requant="nvfp4", requant_global=g, out=y, workspace=ws)
+    ms, phases = time_steps(torch, step, 5, 2, profile=(mx.profile_start, mx.profile_stop))
+    P = T * K
+    flops = 6.0 * P * H * I
+    ideal_ms = (4.0 * P * H * I / (PEAK_FP4_TFLOPS * 1e9)) + (2.0 * P * H * I / (PEAK_BF16_TFLOPS * 1e9))
+    rec = {"skewed_e48_t16384_nvfp4": {
+        "ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
+        "frac_of_mixed_peak": round(ideal_ms / ms, 4),
+        "mixed_peak_note": "L1 (2/3 of the FLOPs) at the FP4 peak, L2 (1/3) at the bf16 peak",
+        "phases_ms_per_step": {k: round(v[0] / v[1], 4) for k, v in phases.items()}}}
+    # decode tail: the first 8 tokens over the same weights
+    xt = x[:8].contiguous()
+    yt = torch.empty((8, H), dtype=torch.bfloat16, device="cuda")
+    idt, wt = w["ids"][:8].contiguous(), w["w"][:8].contiguous()
+    wst = torch.empty(mx.grouped_expert_mlp_workspace_size(8, H, I, K, E, "nvfp4"), dtype=torch.uint8,
+                      device="cuda")
+    tail = lambda: mx.grouped_expert_mlp(xt, idt, wt, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
+                                         requant="nvfp4", requant_global=g, out=yt, workspace=wst)
+    us = graph_replay_us(torch, [tail])
+    n_active = int(np.unique(d["ids"][:8]).size)
+    tbytes = n_active * 35094528
+    rec["skewed_decode_tail_t8_nvfp4"] = {"us_per_call": round(us, 2), "active_experts": n_active,
+                                          "weight_GB/s": round(tbytes / us / 1e3, 1),
+                                          "timing": "hipGraph replay (weights of the active experts)"}
+    return rec
 
 
 def cpu_baseline(d, n_exp):
@@ -156,6 +261,12 @@ def main():
         mx.grouped_expert_mlp(x, w["ids"], w["w"], w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
                               out=y, workspace=ws)
 
+    if a.calibration_copy:
+        src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms, phases = time_steps(torch, step, a.steps, a.warmup, profile=(mx.profile_start, mx.profile_stop))
     flops = 6.0 * T * K * H * I
     value = flops / ms / 1e9   # TFLOP/s
@@ -163,6 +274,9 @@ def main():
     l1_avg = l1_ms / l1_n
     l1_flops = 2.0 * T * K * (2 * I) * H
     achieved = l1_flops / l1_avg / 1e9
+    traffic = None
+    if L1_TRAFFIC is not None and L1_TRAFFIC["gemm_digest"] == gemm_digest():
+        traffic = L1_TRAFFIC["bytes_per_launch"]
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
@@ -175,7 +289,7 @@ def main():
         "frac_of_fp4_peak": round(value / PEAK_FP4_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "l1_gemm (gate/up GEMM + SiLU*up + MXFP4 re-quant)",
                      "achieved": round(achieved, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": l1_flops, "avg_launch_ms": round(l1_avg, 4)},
         "phases_ms_per_step": {k: round(v[0] / v[1], 4) for k, v in phases.items()},
     }
