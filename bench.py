@@ -46,7 +46,11 @@ CALIB_COPY_BYTES = 1 << 28    # --calibration-copy: one device copy of 256 MiB (
 # --calibration-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same
 # counter reads for the calibration copy. Valid for the GEMM sources whose
 # digest is recorded; None otherwise.
-L1_TRAFFIC = None
+L1_TRAFFIC = {
+    "gemm_digest": "a29d0419b4e38675",
+    "bytes_per_launch": 1686001766,          # 794571 KiB fetched x 1.9997 + 57599 KiB written x 1.0
+    "profile": "profiles/grouped_e48_t4096_hbm_bytes.md",
+}
 GEMM_SOURCES = ("gemm.hip", "gemm_common.h", "mx_device.h", "mx_internal.h")
 
 
