@@ -102,10 +102,15 @@ __device__ __forceinline__ void k_step(const Frags& cur, Frags& nxt, const uint8
     for (int g = 0; g < 2; ++g) {
       acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd(cur.A[f]), opnd(cur.B[g]), acc[f][g], 4,
                                                                  4, S, (int)sa[f], S, (int)sb[g]);
-      const int i = f * 2 + g;   // 0..7: reads after MFMAs 0..5
+      // After MFMA i (0..5) read fragment i of the next step, in the order the
+      // next step's MFMAs consume them (A0 B0 B1 A1 A2 A3): every read then has
+      // at least six MFMAs of this wave before its first use.
+      const int i = f * 2 + g;
       if (READ && i < 6) {
-        if (i < 4) nxt.A[i] = lds16(sbn + wrow_off + i * 32 * ROW_BYTES + coffn);
-        else nxt.B[i - 4] = lds16(sbn + xrow_off + (i - 4) * 32 * ROW_BYTES + coffn);
+        if (i == 0) nxt.A[0] = lds16(sbn + wrow_off + coffn);
+        else if (i == 1) nxt.B[0] = lds16(sbn + xrow_off + coffn);
+        else if (i == 2) nxt.B[1] = lds16(sbn + xrow_off + 32 * ROW_BYTES + coffn);
+        else nxt.A[i - 2] = lds16(sbn + wrow_off + (i - 2) * 32 * ROW_BYTES + coffn);
       }
     }
   }
