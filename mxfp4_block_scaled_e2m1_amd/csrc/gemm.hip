@@ -56,6 +56,7 @@ constexpr int VM_PER_STAGE = W_DMA + X_DMA + 2;       // + two dword copies of t
 static_assert(VM_PER_STAGE == 10, "the vmcnt immediate below assumes 10 copies per stage");
 static_assert(NSTAGE == 2, "the pipeline below is written for 2 LDS slots");
 static_assert(WS_BYTES + XS_BYTES == GEMM_THREADS * 8, "two scale dwords per thread per stage");
+static_assert(NSTAGE * STAGE_BYTES >= TILE_LDS_TOTAL, "the bf16 epilogue stages its tile in the K-loop LDS");
 
 // Zero bytes for the upper half of a K stage when K % 256 == 128: zero codes with
 // zero scale bytes (2^-127) contribute exactly 0 to every sum.
@@ -244,6 +245,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     for (int g = 0; g < 2; ++g) sx[g] = *(const uint32_t*)(sb + xsc_off + g * 32 * SC_BYTES);
   };
 
+  // Output rows and gate weights of the bf16 epilogue, loaded now so that their
+  // latency hides behind the K loop (they complete before stage 0's copies,
+  // which the prologue waits for).
+  TileRows<2> rows;
+  if constexpr (EPI == EPI_BF16) rows = load_tile_rows<2>(a, t, wm, lane);
+
   // Prologue: stages 0 and 1 in flight; wait for stage 0 and read its first step.
   issue(0);
   if (nst > 1) {
@@ -307,7 +314,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
         }
     }
   } else if constexpr (EPI == EPI_BF16) {
-    store_tile_bf16(a, t, acc, wn, wm, lane, 1.0f);
+    store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, 1.0f, smem, GEMM_THREADS);
   } else {
     // L1: gate in acc[f][g], up in acc[f + 2][g] for f = 0, 1.
     const int I = a.n_rows;
@@ -417,13 +424,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
 template <int EPI>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE_BYTES];
+  __shared__ TileTables tt;
+  load_tile_tables(a, tt);
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3, per_xcd_wgs = gridDim.x >> 3;
-  const int total = tile_count(a);
+  const int total = tile_count(a, tt);
   const int per = (total + 7) >> 3;
   const int end = min((xcd + 1) * per, total);
   for (int L = xcd * per + local; L < end; L += per_xcd_wgs) {
-    gemm_tile<EPI>(a, decode_tile(a, L), smem);
+    gemm_tile<EPI>(a, decode_tile(a, tt, L), smem);
     // the next tile's first copies overwrite LDS that this tile's waves read
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }

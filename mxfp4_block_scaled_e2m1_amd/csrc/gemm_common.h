@@ -14,15 +14,35 @@ struct Tile {
   int rows;      // valid rows in the token tile
 };
 
+// Routed launches keep the expert offsets and m-tile bases (E+1 each) in LDS:
+// the tile decode at the start of every tile then reads LDS instead of a chain
+// of dependent global loads (a binary search and the offsets). Dense launches
+// need neither.
+struct TileTables {
+  int tile_base[ROUTE_MAX_EXPERTS + 1];
+  int expert_off[ROUTE_MAX_EXPERTS + 1];
+};
+
+// Fill the tables (all threads of the workgroup; ends with a barrier).
+static __device__ __forceinline__ void load_tile_tables(const GemmArgs& a, TileTables& tt) {
+  if (a.expert_off != nullptr) {
+    for (int i = threadIdx.x; i <= a.n_experts; i += blockDim.x) {
+      tt.tile_base[i] = a.tile_base[i];
+      tt.expert_off[i] = a.expert_off[i];
+    }
+  }
+  __syncthreads();
+}
+
 // Number of tiles of this launch (device-side for the routed experts).
-static __device__ __forceinline__ int tile_count(const GemmArgs& a) {
+static __device__ __forceinline__ int tile_count(const GemmArgs& a, const TileTables& tt) {
   if (a.expert_off == nullptr) return a.grid_tiles;
-  return a.tile_base[a.n_experts] * a.n_tiles;
+  return tt.tile_base[a.n_experts] * a.n_tiles;
 }
 
 // Tile L of the launch. Tiles are ordered (expert, n-tile, m-tile) with the
 // m-tile fastest, so consecutive tiles share their weight rows.
-static __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, int L) {
+static __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const TileTables& tt, int L) {
   Tile t;
   if (a.expert_off == nullptr) {
     const int mtiles = (a.m_rows + BM - 1) / BM;
@@ -37,53 +57,97 @@ static __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, int L) {
   int lo = 0, hi = a.n_experts - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (a.tile_base[mid] * a.n_tiles <= L) lo = mid; else hi = mid - 1;
+    if (tt.tile_base[mid] * a.n_tiles <= L) lo = mid; else hi = mid - 1;
   }
   const int e = lo;
-  const int tb = a.tile_base[e];
-  const int nte = a.tile_base[e + 1] - tb;
+  const int tb = tt.tile_base[e];
+  const int nte = tt.tile_base[e + 1] - tb;
   const int r = L - tb * a.n_tiles;
   t.e = e;
   t.nt = r / nte;
   const int mt = r - t.nt * nte;
-  const int off = a.expert_off[e];
+  const int off = tt.expert_off[e];
   t.row0 = off + mt * BM;
-  t.rows = min(BM, a.expert_off[e + 1] - t.row0);
+  t.rows = min(BM, tt.expert_off[e + 1] - t.row0);
   return t;
 }
 
-// bf16 output of a 256 x 256 tile held as 8 waves x (4 x 2) 32x32 MFMA blocks:
-// acc[f][g][v] is D[n][m] with n = nt*BN + wn*128 + f*32 + 8*(v/4) + 4*(lane/32) + v%4
-// and m = wm*64 + g*32 + lane%32 within the token tile. Dense: y[m][n] =
-// bf16(scale * D). Routed: o[slot(m)][n] = bf16(scale * D * gate_weight[slot]).
-static __device__ __forceinline__ void store_tile_bf16(const GemmArgs& a, const Tile& t, const f32x16 (&acc)[4][2],
-                                                       int wn, int wm, int lane, float scale) {
-  const int r32 = lane & 31, hh = lane >> 5;
+// bf16 output of a 256 x 256 tile whose waves each hold 128 weight rows x
+// NG*32 token rows as 4 x NG 32x32 MFMA blocks: acc[f][g][v] is D[n][m] with
+// n = nt*BN + wn*128 + f*32 + 8*(v/4) + 4*(lane/32) + v%4 and
+// m = wm*NG*32 + g*32 + lane%32 within the token tile. Dense: y[m][n] =
+// bf16(scale * D). Routed: o[row_slot[m]][n] = bf16(scale * D * row_weight[m]).
+//
+// The tile goes through LDS: the waves put their bf16 values into a row-major
+// [256 token rows][256 columns] tile in `smem` (row stride TILE_LDS_STRIDE: the
+// 16 bytes of padding spread the 32 rows a wave writes at once over the banks),
+// then every thread copies 16-byte chunks, so each output row leaves as one
+// contiguous 512-byte run. The per-row output slots and gate weights are loaded
+// by the caller at the start of the tile (TileRows), so no load latency is
+// exposed here. `smem` must hold TILE_LDS_TOTAL bytes; this function begins
+// with a barrier (the K loop's last LDS reads) and the caller must place a
+// barrier before the next use of `smem`.
+constexpr int TILE_LDS_STRIDE = 256 * 2 + 16;
+constexpr int TILE_LDS_BYTES = 256 * TILE_LDS_STRIDE;
+constexpr int TILE_LDS_TOTAL = TILE_LDS_BYTES + 256 * 4;   // + the output row of each token row
+
+// Per-thread rows of a tile's bf16 epilogue: the gate weights of this lane's NG
+// token rows, and (threads < 256) the output row of token row threadIdx.x.
+template <int NG>
+struct TileRows {
+  float w[NG];
+  int out_row;
+};
+
+template <int NG>
+static __device__ __forceinline__ TileRows<NG> load_tile_rows(const GemmArgs& a, const Tile& t, int wm, int lane) {
+  TileRows<NG> r;
+  const int r32 = lane & 31;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int ml = wm * 64 + g * 32 + r32;
-    if (ml >= t.rows) continue;
-    const int row = t.row0 + ml;
-    int64_t out_row = row;
-    float wgt = scale;
-    if (a.row_slot != nullptr) {
-      const int slot = a.row_slot[row];
-      out_row = slot;
-      wgt = scale * a.slot_weight[slot];
-    }
-    uint16_t* dst = a.out_bf16 + out_row * a.n_rows;
+  for (int g = 0; g < NG; ++g) r.w[g] = 1.0f;
+  r.out_row = t.row0 + min((int)threadIdx.x, t.rows - 1);
+  if (a.row_slot != nullptr) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) r.w[g] = a.row_weight[t.row0 + min(wm * NG * 32 + g * 32 + r32, t.rows - 1)];
+    if (threadIdx.x < 256) r.out_row = a.row_slot[r.out_row];
+  }
+  return r;
+}
+
+template <int NG>
+static __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& a, const Tile& t,
+                                                           const f32x16 (&acc)[4][NG], const TileRows<NG>& rows,
+                                                           int wn, int wm, int lane, float scale, uint8_t* smem,
+                                                           int nthreads) {
+  const int r32 = lane & 31, hh = lane >> 5;
+  int* out_rows = (int*)(smem + TILE_LDS_BYTES);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (threadIdx.x < 256) out_rows[threadIdx.x] = rows.out_row;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int ml = wm * NG * 32 + g * 32 + r32;
+    const float wgt = scale * rows.w[g];
+    uint8_t* trow = smem + ml * TILE_LDS_STRIDE;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = t.nt * BN + wn * 128 + f * 32 + 8 * q + 4 * hh;
-        if (n < a.n_rows) {
-          uint32_t p0 = f32_to_bf16_rne(acc[f][g][4 * q] * wgt) | (f32_to_bf16_rne(acc[f][g][4 * q + 1] * wgt) << 16);
-          uint32_t p1 =
-              f32_to_bf16_rne(acc[f][g][4 * q + 2] * wgt) | (f32_to_bf16_rne(acc[f][g][4 * q + 3] * wgt) << 16);
-          *(uint2*)(dst + n) = make_uint2(p0, p1);
-        }
+        const int nl = wn * 128 + f * 32 + 8 * q + 4 * hh;
+        const uint32_t p0 =
+            f32_to_bf16_rne(acc[f][g][4 * q] * wgt) | (f32_to_bf16_rne(acc[f][g][4 * q + 1] * wgt) << 16);
+        const uint32_t p1 =
+            f32_to_bf16_rne(acc[f][g][4 * q + 2] * wgt) | (f32_to_bf16_rne(acc[f][g][4 * q + 3] * wgt) << 16);
+        *(uint2*)(trow + nl * 2) = make_uint2(p0, p1);
       }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // 256 rows x 32 chunks of 16 bytes
+  const int c = threadIdx.x & 31;
+  const int n = t.nt * BN + c * 8;
+  if (n < a.n_rows) {
+#pragma unroll 4
+    for (int r = threadIdx.x >> 5; r < t.rows; r += nthreads / 32)
+      *(uint4*)(a.out_bf16 + (int64_t)out_rows[r] * a.n_rows + n) = *(const uint4*)(smem + r * TILE_LDS_STRIDE + c * 16);
   }
 }
 

@@ -129,6 +129,7 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
       for (int v = 0; v < 16; ++v) acc[f][g][v] = 0.0f;
 
   const int r32 = lane & 31, hh = lane >> 5;
+  const TileRows<2> rows = load_tile_rows<2>(a, t, wm, lane);   // for the epilogue, loaded early
   NvRaw raw;
   load(0, raw);
   store(0, raw);
@@ -155,19 +156,22 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
     if (more) store((st + 1) & 1, raw);   // the other slot: its last reads were before the previous barrier
     __syncthreads();
   }
-  store_tile_bf16(a, t, acc, wn, wm, lane, a.nv_global);
+  store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, a.nv_global, smem, GEMM_THREADS);
 }
 
 // Persistent kernel with the tile order and XCD mapping of the FP4 GEMM.
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm_nv(const GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_SLOT];
+  // the two K-stage slots, or the bf16 output tile of the epilogue
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_SLOT > TILE_LDS_TOTAL ? 2 * NV_SLOT : TILE_LDS_TOTAL];
+  __shared__ TileTables tt;
+  load_tile_tables(a, tt);
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3, per_xcd_wgs = gridDim.x >> 3;
-  const int total = tile_count(a);
+  const int total = tile_count(a, tt);
   const int per = (total + 7) >> 3;
   const int end = min((xcd + 1) * per, total);
   for (int L = xcd * per + local; L < end; L += per_xcd_wgs) {
-    nv_tile(a, decode_tile(a, L), smem);
+    nv_tile(a, decode_tile(a, tt, L), smem);
     __syncthreads();   // the next tile's first stores overwrite slot 0
   }
 }

@@ -126,6 +126,7 @@ GroupWs group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E, mx_f
   w.rb.tile_base = (int32_t*)c.take((size_t)(E + 1) * 4);
   w.rb.row_token = (int32_t*)c.take((size_t)P * 4);
   w.rb.row_slot = (int32_t*)c.take((size_t)P * 4);
+  w.rb.row_weight = (float*)c.take((size_t)P * 4);
   w.hq = (uint8_t*)c.take((size_t)(P * I / 2));
   w.hs = (uint8_t*)c.take((size_t)(P * I / (rq == MX_FMT_NVFP4 ? 16 : 32)));
   w.o = (uint16_t*)c.take((size_t)(P * H * 2));
@@ -423,7 +424,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   const int max_mtiles = (int)((P + (int64_t)E * (BM - 1)) / BM);
 
   MX_HIP(phase("quant_x", s, [&] { return launch_quant_mxfp4(x, T, hidden, w.xq, w.xs, s); }), "quant_x");
-  MX_HIP(phase("route", s, [&] { return launch_route(topk_ids, T, k, E, w.rb, s); }), "route");
+  MX_HIP(phase("route", s, [&] { return launch_route(topk_ids, topk_w, T, k, E, w.rb, s); }), "route");
 
   GemmArgs l1 = base_args();
   l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
@@ -443,7 +444,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l2.x = w.hq; l2.x_s = w.hs;
   l2.expert_off = w.rb.expert_off; l2.tile_base = w.rb.tile_base; l2.n_experts = E;
   l2.n_tiles = (H + BN - 1) / BN;
-  l2.out_bf16 = w.o; l2.row_slot = w.rb.row_slot; l2.slot_weight = topk_w;
+  l2.out_bf16 = w.o; l2.row_slot = w.rb.row_slot; l2.row_weight = w.rb.row_weight;
   if (requant == MX_FMT_NVFP4) {
     l2.nv_global = requant_global;
     MX_HIP(phase("l2_gemm_bf16", s, [&] { return launch_gemm_nv_l2(l2, max_mtiles * l2.n_tiles, s); }),

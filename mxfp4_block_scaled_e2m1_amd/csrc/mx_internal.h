@@ -58,7 +58,7 @@ struct GemmArgs {
   float nv_global;            // L1 NVFP4 global scale
   uint16_t* out_bf16;         // EPI_BF16: dense y [m_rows, n_rows]; grouped o [slots, n_rows]
   const int32_t* row_slot;    // grouped L2: sorted row -> slot (t*k + j)
-  const float* slot_weight;   // grouped L2: gate weight per slot
+  const float* row_weight;    // grouped L2: gate weight of each sorted row
 };
 
 // max_tiles: an upper bound on the tiles of the launch (the routed case only knows
@@ -95,9 +95,10 @@ struct RouteBuffers {
   int32_t* tile_base;      // [E+1]
   int32_t* row_token;      // [P]
   int32_t* row_slot;       // [P]
+  float* row_weight;       // [P] gate weight of each sorted row
 };
 
-hipError_t launch_route(const int32_t* topk_ids, int64_t tokens, int k, int n_experts,
+hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, int64_t tokens, int k, int n_experts,
                         const RouteBuffers& rb, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* o, const int32_t* topk_ids, int64_t tokens, int k,

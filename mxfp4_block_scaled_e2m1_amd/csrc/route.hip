@@ -43,9 +43,10 @@ __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__
 // its own wave: lanes that share an expert find each other with a ballot and
 // count the set bits below them. Order within an expert is pair order.
 __global__ __launch_bounds__(ROUTE_CHUNK) void k_route_scatter(
-    const int32_t* __restrict__ ids, int64_t P, int k, int E, const int32_t* __restrict__ block_counts,
-    int nblocks, int32_t* __restrict__ expert_off, int32_t* __restrict__ tile_base,
-    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot) {
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t P, int k, int E,
+    const int32_t* __restrict__ block_counts, int nblocks, int32_t* __restrict__ expert_off,
+    int32_t* __restrict__ tile_base, int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
+    float* __restrict__ row_weight) {
   extern __shared__ int sm[];
   constexpr int NW = ROUTE_CHUNK / 64;
   int* tot = sm;              // [E] pairs per expert (all chunks)
@@ -99,6 +100,7 @@ __global__ __launch_bounds__(ROUTE_CHUNK) void k_route_scatter(
     for (int x = 0; x < w; ++x) pos += wc[x * E + e];
     row_token[pos] = (int)(p / k);
     row_slot[pos] = (int)p;
+    row_weight[pos] = wts[p];
   }
 }
 
@@ -134,15 +136,16 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
 
 }  // namespace
 
-hipError_t launch_route(const int32_t* topk_ids, int64_t tokens, int k, int n_experts,
+hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, int64_t tokens, int k, int n_experts,
                         const RouteBuffers& rb, hipStream_t s) {
   const int64_t P = tokens * k;
   const int nblocks = (int)((P + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
   if (nblocks == 0) return hipSuccess;
   k_route_count<<<nblocks, 256, 0, s>>>(topk_ids, P, n_experts, rb.block_counts);
   const size_t lds = (size_t)(3 + ROUTE_CHUNK / 64) * n_experts * sizeof(int);
-  k_route_scatter<<<nblocks, ROUTE_CHUNK, lds, s>>>(topk_ids, P, k, n_experts, rb.block_counts, nblocks,
-                                                    rb.expert_off, rb.tile_base, rb.row_token, rb.row_slot);
+  k_route_scatter<<<nblocks, ROUTE_CHUNK, lds, s>>>(topk_ids, topk_w, P, k, n_experts, rb.block_counts, nblocks,
+                                                    rb.expert_off, rb.tile_base, rb.row_token, rb.row_slot,
+                                                    rb.row_weight);
   return hipGetLastError();
 }
 
