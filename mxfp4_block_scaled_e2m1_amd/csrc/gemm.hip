@@ -131,7 +131,12 @@ template <int EPI>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint8_t* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave >> 2, wm = wave & 3;
+  // wave -> (wn, wm): consecutive waves share a token block, so the token blocks
+  // of a partly filled tile are spread over the SIMDs (wave w runs on SIMD w % 4)
+  const int wn = wave & 1, wm = wave >> 1;
+  // a wave whose 64 token rows are all past the tile's rows skips its MFMAs and
+  // fragment reads (it still copies and meets every barrier)
+  const bool act = wm * 64 < t.rows;
   const int K = a.k;
   const int kb = K >> 1;                    // code bytes per row
   const int ks = K >> 5;                    // scale bytes per row
@@ -260,35 +265,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
-  Frags F0, F1;
-  uint32_t sa[4], sx[2];
-  read_scales(smem, sa, sx);
+  if (act) {
+    Frags F0, F1;
+    uint32_t sa[4], sx[2];
+    read_scales(smem, sa, sx);
 #pragma unroll
-  for (int f = 0; f < 4; ++f) F0.A[f] = lds16(smem + wrow_off + f * 32 * ROW_BYTES + coff[0]);
+    for (int f = 0; f < 4; ++f) F0.A[f] = lds16(smem + wrow_off + f * 32 * ROW_BYTES + coff[0]);
 #pragma unroll
-  for (int g = 0; g < 2; ++g) F0.B[g] = lds16(smem + xrow_off + g * 32 * ROW_BYTES + coff[0]);
+    for (int g = 0; g < 2; ++g) F0.B[g] = lds16(smem + xrow_off + g * 32 * ROW_BYTES + coff[0]);
 
-  for (int st = 0; st < nst; ++st) {
-    const uint8_t* sb = smem + (st % NSTAGE) * STAGE_BYTES;
-    k_step<0, true>(F0, F1, sb, coff[1], wrow_off, xrow_off, sa, sx, acc);
-    k_step<1, true>(F1, F0, sb, coff[2], wrow_off, xrow_off, sa, sx, acc);
-    k_step<2, true>(F0, F1, sb, coff[3], wrow_off, xrow_off, sa, sx, acc);
-    if (st + 1 < nst) {
-      // Every read of this slot has been issued: retire them, wait for stage st+1
-      // (the only copies in flight), refill this slot with stage st+2 and read the
-      // first step of stage st+1 while the last step's MFMAs run.
+    for (int st = 0; st < nst; ++st) {
+      const uint8_t* sb = smem + (st % NSTAGE) * STAGE_BYTES;
+      k_step<0, true>(F0, F1, sb, coff[1], wrow_off, xrow_off, sa, sx, acc);
+      k_step<1, true>(F1, F0, sb, coff[2], wrow_off, xrow_off, sa, sx, acc);
+      k_step<2, true>(F0, F1, sb, coff[3], wrow_off, xrow_off, sa, sx, acc);
+      if (st + 1 < nst) {
+        // Every read of this slot has been issued: retire them, wait for stage st+1
+        // (the only copies in flight), refill this slot with stage st+2 and read the
+        // first step of stage st+1 while the last step's MFMAs run.
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (st + 2 < nst) issue(st + 2);
+        const uint8_t* sbn = smem + ((st + 1) % NSTAGE) * STAGE_BYTES;
+        uint32_t san[4], sxn[2];
+        read_scales(sbn, san, sxn);
+        k_step<3, true>(F1, F0, sbn, coff[0], wrow_off, xrow_off, sa, sx, acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sa[q] = san[q];
+        sx[0] = sxn[0];
+        sx[1] = sxn[1];
+      } else {
+        k_step<3, false>(F1, F0, sb, 0, wrow_off, xrow_off, sa, sx, acc);
+      }
+    }
+  } else {
+    // the same copies and barriers, without MFMAs (accumulators stay zero)
+    for (int st = 0; st + 1 < nst; ++st) {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (st + 2 < nst) issue(st + 2);
-      const uint8_t* sbn = smem + ((st + 1) % NSTAGE) * STAGE_BYTES;
-      uint32_t san[4], sxn[2];
-      read_scales(sbn, san, sxn);
-      k_step<3, true>(F1, F0, sbn, coff[0], wrow_off, xrow_off, sa, sx, acc);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sa[q] = san[q];
-      sx[0] = sxn[0];
-      sx[1] = sxn[1];
-    } else {
-      k_step<3, false>(F1, F0, sb, 0, wrow_off, xrow_off, sa, sx, acc);
     }
   }
 

@@ -87,7 +87,8 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave >> 2, wm = wave & 3;
+  const int wn = wave & 1, wm = wave >> 1;   // token blocks of a partly filled tile spread over the SIMDs
+  const bool act = wm * 64 < t.rows;         // else this wave's token rows are all padding: no MFMAs
   const int K = a.k;
   const int kb = K >> 1, kse = K >> 5, ksn = K >> 4;   // code bytes, E8M0 and E4M3 bytes per row
   const int nst = K / NV_BK;
@@ -141,6 +142,7 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
     const uint8_t* ht = wt + NV_OPND;
 #pragma unroll
     for (int k16 = 0; k16 < NV_BK / 16; ++k16) {
+      if (!act) break;
       const int c = k16 * 2 + hh;   // lane half hh holds K values 8*hh .. 8*hh+7 of the step
       uint4 A[4], B[2];
 #pragma unroll
