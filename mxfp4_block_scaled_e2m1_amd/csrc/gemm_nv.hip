@@ -21,9 +21,10 @@
 // Design: persistent 512-thread workgroups on 256 x 256 tiles, the same tile
 // order and XCD mapping as the FP4 kernel. Per 64-wide K stage each thread
 // loads 16 code bytes of one weight row and 16 of one token row (plus their
-// scale bytes) into registers one stage ahead, and after the MFMAs of the
-// current stage converts them and writes the bf16 tile into the other of two
-// 64 KB LDS slots. Every operand element is converted once per workgroup.
+// scale bytes) into registers two stages ahead, and after the MFMAs of the
+// current stage converts the next stage's bytes and writes the bf16 tile into
+// the other of two 64 KB LDS slots. Every operand element is converted once
+// per workgroup.
 #include "gemm_common.h"
 
 namespace mx {
@@ -131,32 +132,40 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
 
   const int r32 = lane & 31, hh = lane >> 5;
   const TileRows<2> rows = load_tile_rows<2>(a, t, wm, lane);   // for the epilogue, loaded early
-  NvRaw raw;
-  load(0, raw);
-  store(0, raw);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const bool more = st + 1 < nst;
-    if (more) load(st + 1, raw);
+  // raw bytes of two stages in flight: stage st+2 is loaded while stage st is
+  // multiplied and stage st+1 converted, so the loads have two stages of MFMAs
+  // to arrive in. `cur` held stage st (already in LDS), `nxt` holds stage st+1.
+  auto stage = [&](int st, NvRaw& cur, NvRaw& nxt) {
+    if (st + 2 < nst) load(st + 2, cur);
     const uint8_t* wt = smem + (st & 1) * NV_SLOT;
     const uint8_t* ht = wt + NV_OPND;
+    if (act) {
 #pragma unroll
-    for (int k16 = 0; k16 < NV_BK / 16; ++k16) {
-      if (!act) break;
-      const int c = k16 * 2 + hh;   // lane half hh holds K values 8*hh .. 8*hh+7 of the step
-      uint4 A[4], B[2];
+      for (int k16 = 0; k16 < NV_BK / 16; ++k16) {
+        const int c = k16 * 2 + hh;   // lane half hh holds K values 8*hh .. 8*hh+7 of the step
+        uint4 A[4], B[2];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) A[f] = *(const uint4*)(wt + nv_off(wn * 128 + f * 32 + r32, c));
+        for (int f = 0; f < 4; ++f) A[f] = *(const uint4*)(wt + nv_off(wn * 128 + f * 32 + r32, c));
 #pragma unroll
-      for (int g = 0; g < 2; ++g) B[g] = *(const uint4*)(ht + nv_off(wm * 64 + g * 32 + r32, c));
+        for (int g = 0; g < 2; ++g) B[g] = *(const uint4*)(ht + nv_off(wm * 64 + g * 32 + r32, c));
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
-          acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[f]), as_bf16x8(B[g]), acc[f][g], 0, 0, 0);
+          for (int g = 0; g < 2; ++g)
+            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[f]), as_bf16x8(B[g]), acc[f][g], 0, 0, 0);
+      }
     }
-    if (more) store((st + 1) & 1, raw);   // the other slot: its last reads were before the previous barrier
+    if (st + 1 < nst) store((st + 1) & 1, nxt);   // the other slot: its last reads were before the previous barrier
     __syncthreads();
+  };
+  NvRaw ra, rb;
+  load(0, ra);
+  if (nst > 1) load(1, rb);
+  store(0, ra);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, ra, rb);
+    if (st + 1 < nst) stage(st + 1, rb, ra);
   }
   store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, a.nv_global, smem, GEMM_THREADS);
 }
