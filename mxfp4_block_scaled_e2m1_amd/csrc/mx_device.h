@@ -112,8 +112,14 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return s ? -mag : mag;
 }
 
+// silu(g) * u = g / (1 + e^-g) * u in fp32 with the hardware exp2 and
+// reciprocal (a few ulp of fp32): the result is rounded to bf16 afterwards, so
+// only values within a few fp32 ulp of a bf16 rounding boundary can round
+// differently from the exact value. For g < -88.7 e^-g overflows and the
+// product flushes to +-0 (the exact value is below 1e-36 there).
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 }  // namespace mx

@@ -1,0 +1,88 @@
+"""hipGraph capture and replay of the library calls (the pages' runner is
+graph-safe: page "Current Bug: vLLM produces empty/garbage output", section
+"Revised Plan", Phase 1). The calls allocate nothing and never synchronise, so
+they can be captured; every replay must reproduce the eager result bit for bit,
+with eager work and synchronisations between the replays."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import bf16_t, bits, t
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import mxfp4_block_scaled_e2m1_amd as m
+    return m
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def _check_replays(g, out, ref, scratch):
+    for i in range(3):
+        out.zero_()
+        scratch.normal_()                 # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), ref), f"replay {i}"
+
+
+@pytest.mark.parametrize("M", [1, 8, 300])
+def test_graph_shared_expert(mx, M):
+    d = W.shared_expert(M, seed=3, hidden=1024, inter=512)
+    w = {n: t(d[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")}
+    x = bf16_t(d["x"])
+    y = torch.empty((M, 1024), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.expert_mlp_workspace_size(M, 1024, 512), dtype=torch.uint8, device="cuda")
+    fn = lambda: mx.expert_mlp(x, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"], out=y, workspace=ws)
+    fn()
+    torch.cuda.synchronize()
+    ref = bits(y)
+    g = _capture(fn)
+    _check_replays(g, y, ref, torch.empty(1 << 20, device="cuda"))
+
+
+@pytest.mark.parametrize("requant", ["mxfp4", "nvfp4"])
+def test_graph_grouped(mx, requant):
+    d = W.grouped(tokens=300, n_experts=6, k=3, seed=9, hidden=512, inter=256)
+    w = {n: t(d[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s", "ids", "w")}
+    x = bf16_t(d["x"])
+    y = torch.empty((300, 512), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.grouped_expert_mlp_workspace_size(300, 512, 256, 3, 6, requant), dtype=torch.uint8,
+                     device="cuda")
+    g_scale = 2.0 ** -6
+    fn = lambda: mx.grouped_expert_mlp(x, w["ids"], w["w"], w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
+                                       requant=requant, requant_global=g_scale, out=y, workspace=ws)
+    fn()
+    torch.cuda.synchronize()
+    ref = bits(y)
+    g = _capture(fn)
+    _check_replays(g, y, ref, torch.empty(1 << 20, device="cuda"))
+
+
+def test_graph_dequant_quant(mx):
+    dq = W.dequant_inputs(0)
+    c, s = t(dq["w2"]), t(dq["w2s"])
+    out = torch.empty((7168, 3072), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: mx.dequant("mxfp4", c, s, 7168, 3072, out=out)
+    fn()
+    torch.cuda.synchronize()
+    ref = bits(out)
+    g = _capture(fn)
+    _check_replays(g, out, ref, torch.empty(1 << 20, device="cuda"))
