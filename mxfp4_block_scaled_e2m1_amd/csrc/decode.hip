@@ -263,6 +263,131 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- 9 <= M <= 96
+// Same weight stream, with the activations quantised beforehand by the MXFP4
+// quantiser: the token rows are read as MFMA operands straight from memory
+// (they are small and stay in the L2), 16 tokens at a time. A wave keeps its
+// K run of the 16 weight rows in registers and walks the NC token chunks, the
+// loads of chunk c+1 in flight during the MFMAs of chunk c. The 8 waves'
+// partial sums meet in LDS and wave c finishes chunk c.
+constexpr int SK_MAX_CHUNKS = 8;     // up to 128 tokens per launch
+
+struct SkinnyLds {
+  uint8_t wscale[16 * 256];                        // the tile rows' E8M0 bytes, K <= 8192
+  f32x4 red[DW][SK_MAX_CHUNKS][64];                // partial sums per wave, chunk, lane
+};
+
+template <int NC, int NS>
+__device__ __forceinline__ f32x4 tile_times_qtokens(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
+                                                    int m, int K, RowPair wp, RowPair sp, SkinnyLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int kb = K / 2, ks = K / 32, ksteps = K / 128;
+
+  ScaleRegs sr;
+  load_wscales(sp, ks, sr);
+  int s0, n;
+  wave_steps(ksteps, s0, n);
+  uint4 wa[NS];
+  const uint8_t* myrow = wp.row(r16, kb);
+#pragma unroll
+  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)(myrow + min(s0 + k, ksteps - 1) * 64 + q * 16);
+  store_wscales(sr, ks, L.wscale);
+  lds_barrier();
+
+  // token operands of chunk c, step k: token c*16 + r16 (clamped, zeroed past m)
+  uint4 b[2][NS];
+  uint32_t bsc[2][NS];
+  auto load_chunk = [&](int c, uint4 (&bb)[NS], uint32_t (&ss)[NS]) {
+    const int tok = min(c * 16 + r16, m - 1);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int s = min(s0 + k, ksteps - 1);
+      bb[k] = *(const uint4*)(aq + (int64_t)tok * kb + s * 64 + q * 16);
+      ss[k] = as[(int64_t)tok * ks + s * 4 + q];
+    }
+  };
+  f32x4 acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load_chunk(0, b[0], bsc[0]);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + 1 < NC) load_chunk(c + 1, b[(c + 1) & 1], bsc[(c + 1) & 1]);
+    const bool tok_ok = c * 16 + r16 < m;
+    // steps past the wave's run (k >= n) multiply zero codes: no branch around
+    // the MFMAs, which would make the compiler copy the accumulators
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      const uint4 bz = tok_ok ? b[c & 1][k] : z;
+      const uint4 az = k < n ? wa[k] : z;
+      const int sa = L.wscale[r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc[c], 4, 4, 0, sa, 0,
+                                                               (int)bsc[c & 1][k]);
+    }
+    // keep the loads of later chunks where they are written (one chunk ahead):
+    // hoisting them all would hold every chunk's operands in registers
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) L.red[wave][c][lane] = acc[c];
+  __syncthreads();
+  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wave < NC) {
+#pragma unroll
+    for (int w = 0; w < DW; ++w) {
+      const f32x4 o = L.red[w][wave][lane];
+      tot[0] += o[0]; tot[1] += o[1]; tot[2] += o[2]; tot[3] += o[3];
+    }
+  }
+  return tot;
+}
+
+// L1: chunk `wave` of the tokens -> h (bf16), as k_decode_l1.
+template <int NC, int NS>
+__global__ __launch_bounds__(DT, 1) void k_skinny_l1(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                                                     int m, int H, int I, const uint8_t* __restrict__ w1,
+                                                     const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ w3,
+                                                     const uint8_t* __restrict__ w3s, uint16_t* __restrict__ h) {
+  __shared__ SkinnyLds L;
+  const int j0 = blockIdx.x * 8;
+  const int kb = H / 2, ks = H / 32;
+  const RowPair wp{w1 + (int64_t)j0 * kb, w3 + (int64_t)j0 * kb};
+  const RowPair sp{w1s + (int64_t)j0 * ks, w3s + (int64_t)j0 * ks};
+  const f32x4 acc = tile_times_qtokens<NC, NS>(xq, xs, m, H, wp, sp, L);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float up[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) up[v] = __shfl_xor(acc[v], 32);
+  const int t = wave * 16 + (lane & 15), q = lane >> 4;
+  if (wave < NC && q < 2 && t < m) {
+    const uint32_t p0 = f32_to_bf16_rne(silu_mul(acc[0], up[0])) | (f32_to_bf16_rne(silu_mul(acc[1], up[1])) << 16);
+    const uint32_t p1 = f32_to_bf16_rne(silu_mul(acc[2], up[2])) | (f32_to_bf16_rne(silu_mul(acc[3], up[3])) << 16);
+    *(uint2*)(h + (int64_t)t * I + j0 + 4 * q) = make_uint2(p0, p1);
+  }
+}
+
+// L2: chunk `wave` of the tokens -> y (bf16), as k_decode_l2.
+template <int NC, int NS>
+__global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
+                                                     int m, int H, int I, const uint8_t* __restrict__ w2,
+                                                     const uint8_t* __restrict__ w2s, uint16_t* __restrict__ y) {
+  __shared__ SkinnyLds L;
+  const int n0 = blockIdx.x * 16;
+  const int kb = I / 2, ks = I / 32;
+  const RowPair wp{w2 + (int64_t)n0 * kb, w2 + (int64_t)(n0 + 8) * kb};
+  const RowPair sp{w2s + (int64_t)n0 * ks, w2s + (int64_t)(n0 + 8) * ks};
+  const f32x4 acc = tile_times_qtokens<NC, NS>(hq, hs, m, I, wp, sp, L);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = wave * 16 + (lane & 15), q = lane >> 4;
+  if (wave < NC && t < m) {
+    const uint32_t p0 = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    const uint32_t p1 = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    *(uint2*)(y + (int64_t)t * H + n0 + 4 * q) = make_uint2(p0, p1);
+  }
+}
+
 size_t decode_lds(int cols) {
   const size_t kb = cols / 2, ks = cols / 32;
   return MAX_TOK * (kb + 16) + ((MAX_TOK * ks + 15) & ~(size_t)15) + ((16 * ks + 15) & ~(size_t)15) +
@@ -315,7 +440,70 @@ void launch_l2_ns(const DecodeArgs& a, hipStream_t s) {
   }
 }
 
+template <int NC, int NS>
+void launch_skinny_l1(const DecodeArgs& a, const uint8_t* xq, const uint8_t* xs, hipStream_t s) {
+  k_skinny_l1<NC, NS><<<a.I / 8, DT, 0, s>>>(xq, xs, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.h);
+}
+
+template <int NC, int NS>
+void launch_skinny_l2(const DecodeArgs& a, const uint8_t* hq, const uint8_t* hs, hipStream_t s) {
+  k_skinny_l2<NC, NS><<<a.H / 16, DT, 0, s>>>(hq, hs, a.m, a.H, a.I, a.w2, a.w2s, a.y);
+}
+
+template <int NC>
+void launch_skinny_l1_ns(const DecodeArgs& a, const uint8_t* xq, const uint8_t* xs, hipStream_t s) {
+  switch (steps_bucket(a.H)) {
+    case 1: launch_skinny_l1<NC, 1>(a, xq, xs, s); break;
+    case 3: launch_skinny_l1<NC, 3>(a, xq, xs, s); break;
+    case 7: launch_skinny_l1<NC, 7>(a, xq, xs, s); break;
+    default: launch_skinny_l1<NC, MAX_STEPS>(a, xq, xs, s); break;
+  }
+}
+
+template <int NC>
+void launch_skinny_l2_ns(const DecodeArgs& a, const uint8_t* hq, const uint8_t* hs, hipStream_t s) {
+  switch (steps_bucket(a.I)) {
+    case 1: launch_skinny_l2<NC, 1>(a, hq, hs, s); break;
+    case 3: launch_skinny_l2<NC, 3>(a, hq, hs, s); break;
+    case 7: launch_skinny_l2<NC, 7>(a, hq, hs, s); break;
+    default: launch_skinny_l2<NC, MAX_STEPS>(a, hq, hs, s); break;
+  }
+}
+
 }  // namespace
+
+// Every workgroup reads all m token rows, so the token traffic grows with m;
+// above 96 tokens the 256 x 256 GEMM (whose time hardly depends on m at this
+// size) is faster.
+constexpr int SK_MAX_TOKENS = 96;
+
+bool skinny_fits(int64_t m, int64_t hidden, int64_t inter) {
+  if (m < 1 || m > SK_MAX_TOKENS) return false;
+  if (hidden > DW * MAX_STEPS * 128 || inter > DW * MAX_STEPS * 128) return false;
+  if (inter % 8 != 0 || hidden % 16 != 0) return false;
+  return 16 * (hidden / 32) <= 8 * DT && 16 * (inter / 32) <= 8 * DT;
+}
+
+hipError_t launch_skinny_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
+                             const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
+                             uint8_t* xq, uint8_t* xs, uint16_t* h, uint8_t* hq, uint8_t* hs, uint16_t* y,
+                             hipStream_t s) {
+  const DecodeArgs a{x, m, H, I, w1, w1s, w3, w3s, w2, w2s, h, y};
+  hipError_t e = launch_quant_mxfp4(x, m, H, xq, xs, s);
+  if (e != hipSuccess) return e;
+  const int nc = (m + 15) / 16;
+  if (nc <= 1) launch_skinny_l1_ns<1>(a, xq, xs, s);
+  else if (nc <= 2) launch_skinny_l1_ns<2>(a, xq, xs, s);
+  else if (nc <= 4) launch_skinny_l1_ns<4>(a, xq, xs, s);
+  else launch_skinny_l1_ns<8>(a, xq, xs, s);
+  e = launch_quant_mxfp4(h, m, I, hq, hs, s);
+  if (e != hipSuccess) return e;
+  if (nc <= 1) launch_skinny_l2_ns<1>(a, hq, hs, s);
+  else if (nc <= 2) launch_skinny_l2_ns<2>(a, hq, hs, s);
+  else if (nc <= 4) launch_skinny_l2_ns<4>(a, hq, hs, s);
+  else launch_skinny_l2_ns<8>(a, hq, hs, s);
+  return hipGetLastError();
+}
 
 bool decode_fits(int64_t m, int64_t hidden, int64_t inter) {
   if (m < 1 || m > MAX_TOK) return false;

@@ -84,9 +84,14 @@ struct Carve {
   }
 };
 
-// Dense (one expert) workspace. GEMM path: xq, xs, hq, hs. Few-token path
-// (M <= 8, MXFP4 re-quantisation): h, the bf16 SiLU output, at the offset of xq.
+// Dense (one expert) workspace, by path (MXFP4 re-quantisation picks the
+// weight-streaming paths for small M):
+//   few tokens (M <= 8): h, the bf16 SiLU output;
+//   9 <= M <= 96:        xq, xs, hq, hs, then h;
+//   GEMM path:           xq, xs, hq, hs.
+enum DensePath { DENSE_DECODE, DENSE_SKINNY, DENSE_GEMM };
 struct DenseWs {
+  DensePath path;
   uint8_t *xq, *xs, *hq, *hs;
   uint16_t* h;
   size_t bytes;
@@ -94,15 +99,18 @@ struct DenseWs {
 DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
   Carve c(base);
   DenseWs w;
+  w.xq = w.xs = w.hq = w.hs = nullptr;
+  w.h = nullptr;
   if (rq == MX_FMT_MXFP4 && decode_fits(M, H, I)) {
+    w.path = DENSE_DECODE;
     w.h = (uint16_t*)c.take((size_t)(M * I * 2));
-    w.xq = w.xs = w.hq = w.hs = nullptr;
   } else {
-    w.h = nullptr;
+    w.path = (rq == MX_FMT_MXFP4 && skinny_fits(M, H, I)) ? DENSE_SKINNY : DENSE_GEMM;
     w.xq = (uint8_t*)c.take((size_t)(M * H / 2));
     w.xs = (uint8_t*)c.take((size_t)(M * H / 32));
     w.hq = (uint8_t*)c.take((size_t)(M * I / 2));
     w.hs = (uint8_t*)c.take((size_t)(M * I / (rq == MX_FMT_NVFP4 ? 16 : 32)));
+    if (w.path == DENSE_SKINNY) w.h = (uint16_t*)c.take((size_t)(M * I * 2));
   }
   w.bytes = c.off;
   return w;
@@ -354,11 +362,19 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   DenseWs w = dense_ws(workspace, M, hidden, inter, requant);
   const int H = (int)hidden, I = (int)inter, m = (int)M;
 
-  if (w.h != nullptr) {
+  if (w.path == DENSE_DECODE) {
     // few tokens: two weight-streaming kernels, activations quantised in LDS
     MX_HIP(phase("decode_mlp", s, [&] {
              return launch_decode_mlp(x, m, H, I, w1, w1_s, w3, w3_s, w2, w2_s, w.h, y, s);
            }), "decode_mlp");
+    return ok();
+  }
+  if (w.path == DENSE_SKINNY) {
+    // up to 96 tokens: quantise x, stream the weights with the token rows as
+    // operands, quantise h, stream w2
+    MX_HIP(phase("skinny_mlp", s, [&] {
+             return launch_skinny_mlp(x, m, H, I, w1, w1_s, w3, w3_s, w2, w2_s, w.xq, w.xs, w.h, w.hq, w.hs, y, s);
+           }), "skinny_mlp");
     return ok();
   }
 

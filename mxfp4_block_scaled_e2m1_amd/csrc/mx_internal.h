@@ -107,6 +107,14 @@ hipError_t launch_combine(const uint16_t* o, const int32_t* topk_ids, int64_t to
 // ---- Few-token path (M <= 32): weight streaming, see decode.hip ----------------
 bool decode_fits(int64_t m, int64_t hidden, int64_t inter);
 // h: bf16 scratch [m, inter]
+// 9 <= M <= 96: x and h quantised by the MXFP4 quantiser into the workspace,
+// the weights streamed once by two kernels that read the token rows as MFMA
+// operands, 16 at a time (see decode.hip).
+bool skinny_fits(int64_t m, int64_t hidden, int64_t inter);
+hipError_t launch_skinny_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
+                             const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
+                             uint8_t* xq, uint8_t* xs, uint16_t* h, uint8_t* hq, uint8_t* hs, uint16_t* y,
+                             hipStream_t s);
 hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
                              const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
                              uint16_t* h, uint16_t* y, hipStream_t s);

@@ -22,7 +22,7 @@ DECODE_MAX_TOKENS = 8    # mx_expert_mlp streams the weights once for up to 8 to
 
 def _ws_slices(ws, M, H, I):
     """Dense workspace layout of mx_expert_mlp, each region 256-byte aligned:
-    GEMM path (M > 8): xq, xs, hq, hs; few tokens: h (bf16 SiLU output)."""
+    M > 8: xq, xs, hq, hs (then h for M <= 96); few tokens: h (bf16 SiLU output)."""
     if M <= DECODE_MAX_TOKENS:
         return [ws[:M * I * 2]]
     off, out = 0, []
@@ -108,7 +108,7 @@ def test_tiny_expert_mlp_few_tokens(mx, M):
     assert_mlp_close(y, ref)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17, 32, 33, 128, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17, 32, 33, 96, 97, 128, 300])
 def test_shared_expert_real_shape(mx, M):
     d = W.shared_expert(M, seed=0)
     y, sl = _run_dense(mx, d, M, 7168, 3072)

@@ -43,7 +43,7 @@ def _check_replays(g, out, ref, scratch):
         assert np.array_equal(bits(out), ref), f"replay {i}"
 
 
-@pytest.mark.parametrize("M", [1, 8, 300])
+@pytest.mark.parametrize("M", [1, 8, 40, 300])
 def test_graph_shared_expert(mx, M):
     d = W.shared_expert(M, seed=3, hidden=1024, inter=512)
     w = {n: t(d[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")}
