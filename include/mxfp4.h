@@ -124,6 +124,9 @@ MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t 
  *   anything else: MX_ERR_FORMAT.
  * A stacked gate_up tensor [2*inter, hidden/2] is passed as w1 = w13 and
  * w3 = w13 + inter*hidden/2 (scales likewise).
+ * packed_scales: NULL, or the output of mx_pack_weight_scales() for these
+ * weights (E = 1, same hidden and inter), 256-byte aligned. The GEMM path then
+ * reads the weight scales from it; the results are identical either way.
  * workspace: device memory of at least mx_expert_mlp_workspace_size() bytes,
  * 256-byte aligned; its contents are scratch. y must not alias x or workspace.
  * Alignment: x, y, codes 16 bytes; scales 4 bytes.
@@ -131,8 +134,8 @@ MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t 
 MX_API mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter,
                         const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                         const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                        mx_format requant, float requant_global, uint16_t* y,
-                        void* workspace, size_t ws_bytes, void* stream);
+                        const uint8_t* packed_scales, mx_format requant, float requant_global,
+                        uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
 
 MX_API size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter, mx_format requant);
 
@@ -149,19 +152,41 @@ MX_API size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t in
  * fuses SiLU*up and the re-quantisation; the L2 GEMM multiplies by the gate
  * weight and writes one bf16 row per pair; a final pass sums each token's k
  * rows in slot order in fp32 (deterministic: no atomics).
- * 1 <= k <= E <= 512; hidden % 128 == 0; inter % 128 == 0. requant and
- * requant_global as for mx_expert_mlp.
+ * 1 <= k <= E <= 512; hidden % 128 == 0; inter % 128 == 0. requant,
+ * requant_global and packed_scales (here for all E experts) as for
+ * mx_expert_mlp.
  * Alignment as for mx_expert_mlp; topk_ids and topk_w 4 bytes.
  */
 MX_API mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
                                 const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                 const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                                 const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                                mx_format requant, float requant_global, uint16_t* y,
-                                void* workspace, size_t ws_bytes, void* stream);
+                                const uint8_t* packed_scales, mx_format requant, float requant_global,
+                                uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
 
 MX_API size_t mx_grouped_expert_mlp_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k,
                                             int32_t E, mx_format requant);
+
+/*
+ * mx_pack_weight_scales -- re-lay the E8M0 weight scales of E experts once,
+ * after the weights are loaded, in the order the FP4 GEMM copies them: for
+ * each 256-row weight tile and 256-wide K stage, the 8 scale bytes of the
+ * tile's rows are contiguous (2 KB), so that a stage's scales arrive in a
+ * few whole cache lines instead of 256 separate 8-byte pieces. The runner on
+ * the pages prepares its weights once before serving (page "Current Bug: vLLM
+ * produces empty/garbage output", section "Revised Plan", Phase 1).
+ *   w1_s, w3_s [E, inter, hidden/32]; w2_s [E, hidden, inter/32] (E8M0 bytes).
+ *   packed: device buffer of mx_packed_weight_scales_size(hidden, inter, E)
+ *   bytes, 256-byte aligned, owned by the caller and passed to mx_expert_mlp
+ *   (E = 1) or mx_grouped_expert_mlp as packed_scales. Its layout is internal.
+ * Shapes as for mx_grouped_expert_mlp; MX_ERR_WORKSPACE if packed_bytes is
+ * too small. Alignment: scales 4 bytes.
+ */
+MX_API mx_status mx_pack_weight_scales(const uint8_t* w1_s, const uint8_t* w3_s, const uint8_t* w2_s,
+                                       int64_t hidden, int64_t inter, int32_t E, uint8_t* packed,
+                                       size_t packed_bytes, void* stream);
+
+MX_API size_t mx_packed_weight_scales_size(int64_t hidden, int64_t inter, int32_t E);
 
 /*
  * mx_debug_gemm_f32 -- test hook, not part of the hot path: C[M, N] = A . B^T in fp32

@@ -32,11 +32,13 @@ class PhaseStat(ctypes.Structure):
 SIGNATURES = {
     "mx_dequant": (_I32, [_I32, _P, _P, _F, _I64, _I64, _P, _P]),
     "mx_quantize_act": (_I32, [_I32, _P, _I64, _I64, _F, _P, _P, _P]),
-    "mx_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I32, _F, _P, _P, _SZ, _P]),
+    "mx_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _F, _P, _P, _SZ, _P]),
     "mx_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "mx_grouped_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                     _I32, _F, _P, _P, _SZ, _P]),
+                                     _P, _I32, _F, _P, _P, _SZ, _P]),
     "mx_grouped_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
+    "mx_pack_weight_scales": (_I32, [_P, _P, _P, _I64, _I64, _I32, _P, _SZ, _P]),
+    "mx_packed_weight_scales_size": (_SZ, [_I64, _I64, _I32]),
     "mx_debug_gemm_f32": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "mx_status_string": (ctypes.c_char_p, [_I32]),
     "mx_last_error": (ctypes.c_char_p, []),
@@ -133,8 +135,25 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
+def packed_weight_scales_size(hidden, inter, E=1) -> int:
+    return int(lib().mx_packed_weight_scales_size(hidden, inter, E))
+
+
+def pack_weight_scales(w1s, w3s, w2s, out=None, stream=None):
+    """mx_pack_weight_scales: tile-major copy of the weight scales of one expert
+    (w1s [inter, hidden/32]) or of E stacked experts (w1s [E, inter, hidden/32])."""
+    E = w1s.shape[0] if w1s.dim() == 3 else 1
+    inter, hidden = w1s.shape[-2], 32 * w1s.shape[-1]
+    nbytes = packed_weight_scales_size(hidden, inter, E)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w1s.device)
+    _check(lib().mx_pack_weight_scales(_ptr(w1s), _ptr(w3s), _ptr(w2s), hidden, inter, E, _ptr(out),
+                                       out.numel(), _stream(stream)))
+    return out
+
+
 def expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global: float = 0.0,
-               out=None, workspace=None, stream=None):
+               out=None, workspace=None, stream=None, packed_scales=None):
     """mx_expert_mlp: the shared expert on bf16 x [M, hidden] -> bf16 y [M, hidden]."""
     M, hidden = x.shape
     inter = w1.shape[0]
@@ -143,13 +162,13 @@ def expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global: fl
     nbytes = expert_mlp_workspace_size(M, hidden, inter, requant)
     ws = _workspace(nbytes, x.device, workspace)
     _check(lib().mx_expert_mlp(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s),
-                               _ptr(w2), _ptr(w2s), _fmt(requant), float(requant_global), _ptr(out),
-                               _ptr(ws), ws.numel(), _stream(stream)))
+                               _ptr(w2), _ptr(w2s), _ptr(packed_scales), _fmt(requant), float(requant_global),
+                               _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
 def grouped_expert_mlp(x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4",
-                       requant_global: float = 0.0, out=None, workspace=None, stream=None):
+                       requant_global: float = 0.0, out=None, workspace=None, stream=None, packed_scales=None):
     """mx_grouped_expert_mlp: routed experts, stacked weights [E, ...]."""
     T, hidden = x.shape
     k = topk_ids.shape[1]
@@ -160,8 +179,8 @@ def grouped_expert_mlp(x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="
     ws = _workspace(nbytes, x.device, workspace)
     _check(lib().mx_grouped_expert_mlp(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
                                        _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2), _ptr(w2s),
-                                       _fmt(requant), float(requant_global), _ptr(out), _ptr(ws),
-                                       ws.numel(), _stream(stream)))
+                                       _ptr(packed_scales), _fmt(requant), float(requant_global), _ptr(out),
+                                       _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

@@ -49,6 +49,7 @@ constexpr int OFF_X = W_BYTES;
 constexpr int OFF_WS = W_BYTES + X_BYTES;
 constexpr int OFF_XS = OFF_WS + WS_BYTES;
 constexpr int STAGE_BYTES = OFF_XS + XS_BYTES;        // 69632
+constexpr int SMEM_BYTES = NSTAGE * STAGE_BYTES;
 constexpr int NWAVES = GEMM_THREADS / 64;             // 8: 2 along weight rows x 4 along tokens
 constexpr int W_DMA = W_BYTES / 1024 / NWAVES;        // 16-byte copies per wave per stage (W)
 constexpr int X_DMA = X_BYTES / 1024 / NWAVES;
@@ -56,7 +57,7 @@ constexpr int VM_PER_STAGE = W_DMA + X_DMA + 2;       // + two dword copies of t
 static_assert(VM_PER_STAGE == 10, "the vmcnt immediate below assumes 10 copies per stage");
 static_assert(NSTAGE == 2, "the pipeline below is written for 2 LDS slots");
 static_assert(WS_BYTES + XS_BYTES == GEMM_THREADS * 8, "two scale dwords per thread per stage");
-static_assert(NSTAGE * STAGE_BYTES >= TILE_LDS_TOTAL, "the bf16 epilogue stages its tile in the K-loop LDS");
+static_assert(SMEM_BYTES >= TILE_LDS_TOTAL, "the bf16 epilogue stages its tile in the K-loop LDS");
 
 // Zero bytes for the upper half of a K stage when K % 256 == 128: zero codes with
 // zero scale bytes (2^-127) contribute exactly 0 to every sum.
@@ -90,23 +91,31 @@ __device__ __forceinline__ i32x8 opnd(const uint4& v) {
   return i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
 }
 
+// No stage copies between the MFMAs of a step.
+struct NoCopy {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 // The eight MFMAs of K step S (chunk 4*hh + S, scale byte S) from `cur`,
 // interleaved with the six LDS reads that fill `nxt` for the next step (when
-// READ), so that the reads issue while the matrix core is busy.
-template <int S, bool READ>
+// READ), so that the reads issue while the matrix core is busy. `copy(i)` runs
+// before MFMA i: the last step of a stage spreads the next slot's global -> LDS
+// copies over its MFMAs this way.
+template <int S, bool READ, class Copy>
 __device__ __forceinline__ void k_step(const Frags& cur, Frags& nxt, const uint8_t* sbn, int coffn,
                                        int wrow_off, int xrow_off, const uint32_t (&sa)[4],
-                                       const uint32_t (&sb)[2], f32x16 (&acc)[4][2]) {
+                                       const uint32_t (&sb)[2], f32x16 (&acc)[4][2], const Copy& copy) {
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
+      const int i = f * 2 + g;
+      copy(i);
       acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd(cur.A[f]), opnd(cur.B[g]), acc[f][g], 4,
                                                                  4, S, (int)sa[f], S, (int)sb[g]);
       // After MFMA i (0..5) read fragment i of the next step, in the order the
       // next step's MFMAs consume them (A0 B0 B1 A1 A2 A3): every read then has
       // at least six MFMAs of this wave before its first use.
-      const int i = f * 2 + g;
       if (READ && i < 6) {
         if (i == 0) nxt.A[0] = lds16(sbn + wrow_off + coffn);
         else if (i == 1) nxt.B[0] = lds16(sbn + xrow_off + coffn);
@@ -194,34 +203,61 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     xhi[i] = c >= 4;
   }
   // Scale tiles (8 bytes per row per stage): thread tid copies dword tid & 1 of
-  // weight row tid / 2 and of token row tid / 2.
+  // weight row tid / 2 and of token row tid / 2, from the row-major scales
+  // (stage stride 8 bytes) or from a tile-major copy, where a stage of the
+  // tile is 2 KB in one piece (stage stride 2 KB).
   const uint8_t *wssrc, *xssrc;
+  int wsc_stride = SC_BYTES, xsc_stride = SC_BYTES;
   {
     const int tid = wave * 64 + lane;
-    const uint8_t *base, *sbase;
-    const int row = w_row(tid >> 1, base, sbase);
-    wssrc = sbase + (int64_t)row * ks + (tid & 1) * 4;
-    xssrc = a.x_s + (int64_t)x_token(tid >> 1) * ks + (tid & 1) * 4;
+    if (a.w_spk != nullptr) {
+      wssrc = a.w_spk + (int64_t)t.e * a.wspk_estride + (int64_t)t.nt * nst * SC_TILE_STAGE_BYTES + tid * 4;
+      wsc_stride = SC_TILE_STAGE_BYTES;
+    } else {
+      const uint8_t *base, *sbase;
+      const int row = w_row(tid >> 1, base, sbase);
+      wssrc = sbase + (int64_t)row * ks + (tid & 1) * 4;
+    }
+    if (a.x_s_packed) {
+      // rows past the tile's end read the last valid row, as the code copies do
+      xssrc = a.x_s + (int64_t)t.mt * nst * SC_TILE_STAGE_BYTES + min(tid >> 1, t.rows - 1) * SC_BYTES + (tid & 1) * 4;
+      xsc_stride = SC_TILE_STAGE_BYTES;
+    } else {
+      xssrc = a.x_s + (int64_t)x_token(tid >> 1) * ks + (tid & 1) * 4;
+    }
   }
 
   const uint32_t lds0 = lds_addr(smem);
+  // the zero page's address, taken once: referenced inside the K loop, the
+  // compiler reloads it there with a scalar load whose wait (lgkmcnt(0)) also
+  // drains the LDS reads in flight
+  const uint8_t* zpage = g_zero_page;
+  asm volatile("" : "+s"(zpage));
   const bool shi = (lane & 1) != 0;   // scale dword of columns 128..255
-  auto issue = [&](int st) {
+  // Copy c (0..9) of stage st: W_DMA weight copies, X_DMA token copies, then
+  // the two scale dwords.
+  auto copy_one = [&](int st, int c) {
     const uint32_t sb = lds0 + (st % NSTAGE) * STAGE_BYTES;
     const int ko = st * ROW_BYTES;
     const bool tail = half_tail && st == nst - 1;
-#pragma unroll
-    for (int i = 0; i < W_DMA; ++i)
-      lds_dma16((tail && whi[i]) ? (const void*)g_zero_page : (const void*)(wsrc[i] + ko),
-                sb + (wave * W_DMA + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < X_DMA; ++i)
-      lds_dma16((tail && xhi[i]) ? (const void*)g_zero_page : (const void*)(xsrc[i] + ko),
+    if (c < W_DMA) {
+      lds_dma16((tail && whi[c]) ? (const void*)zpage : (const void*)(wsrc[c] + ko),
+                sb + (wave * W_DMA + c) * 1024);
+    } else if (c < W_DMA + X_DMA) {
+      const int i = c - W_DMA;
+      lds_dma16((tail && xhi[i]) ? (const void*)zpage : (const void*)(xsrc[i] + ko),
                 sb + OFF_X + (wave * X_DMA + i) * 1024);
-    lds_dma4((tail && shi) ? (const void*)g_zero_page : (const void*)(wssrc + st * SC_BYTES),
-             sb + OFF_WS + wave * 256);
-    lds_dma4((tail && shi) ? (const void*)g_zero_page : (const void*)(xssrc + st * SC_BYTES),
-             sb + OFF_XS + wave * 256);
+    } else if (c == W_DMA + X_DMA) {
+      lds_dma4((tail && shi) ? (const void*)zpage : (const void*)(wssrc + st * wsc_stride),
+               sb + OFF_WS + wave * 256);
+    } else {
+      lds_dma4((tail && shi) ? (const void*)zpage : (const void*)(xssrc + st * xsc_stride),
+               sb + OFF_XS + wave * 256);
+    }
+  };
+  auto issue = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < VM_PER_STAGE; ++c) copy_one(st, c);
   };
 
   f32x16 acc[4][2];
@@ -243,11 +279,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
 #pragma unroll
   for (int q = 0; q < 4; ++q) coff[q] = ((hh * 4 + q) ^ swz) * 16;
 
-  auto read_scales = [&](const uint8_t* sb, uint32_t (&sa)[4], uint32_t (&sx)[2]) {
+  // this lane's scale dwords of stage s
+  auto read_scales = [&](int s, uint32_t (&sa)[4], uint32_t (&sx)[2]) {
+    const uint8_t* rs = smem + (s % NSTAGE) * STAGE_BYTES;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sa[f] = *(const uint32_t*)(sb + wsc_off + f * 32 * SC_BYTES);
+    for (int f = 0; f < 4; ++f) sa[f] = *(const uint32_t*)(rs + wsc_off + f * 32 * SC_BYTES);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) sx[g] = *(const uint32_t*)(sb + xsc_off + g * 32 * SC_BYTES);
+    for (int g = 0; g < 2; ++g) sx[g] = *(const uint32_t*)(rs + xsc_off + g * 32 * SC_BYTES);
   };
 
   // Output rows and gate weights of the bf16 epilogue, loaded now so that their
@@ -268,38 +306,51 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
   if (act) {
     Frags F0, F1;
     uint32_t sa[4], sx[2];
-    read_scales(smem, sa, sx);
-#pragma unroll
-    for (int f = 0; f < 4; ++f) F0.A[f] = lds16(smem + wrow_off + f * 32 * ROW_BYTES + coff[0]);
+    read_scales(0, sa, sx);
+    // the order of the K loop's reads (A0 B0 B1 A1 A2 A3), so the loop entry
+    // needs no longer wait than its back edge
+    F0.A[0] = lds16(smem + wrow_off + coff[0]);
 #pragma unroll
     for (int g = 0; g < 2; ++g) F0.B[g] = lds16(smem + xrow_off + g * 32 * ROW_BYTES + coff[0]);
-
-    for (int st = 0; st < nst; ++st) {
-      const uint8_t* sb = smem + (st % NSTAGE) * STAGE_BYTES;
-      k_step<0, true>(F0, F1, sb, coff[1], wrow_off, xrow_off, sa, sx, acc);
-      k_step<1, true>(F1, F0, sb, coff[2], wrow_off, xrow_off, sa, sx, acc);
-      k_step<2, true>(F0, F1, sb, coff[3], wrow_off, xrow_off, sa, sx, acc);
-      if (st + 1 < nst) {
-        // Every read of this slot has been issued: retire them, wait for stage st+1
-        // (the only copies in flight), refill this slot with stage st+2 and read the
-        // first step of stage st+1 while the last step's MFMAs run.
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (st + 2 < nst) issue(st + 2);
-        const uint8_t* sbn = smem + ((st + 1) % NSTAGE) * STAGE_BYTES;
-        uint32_t san[4], sxn[2];
-        read_scales(sbn, san, sxn);
-        k_step<3, true>(F1, F0, sbn, coff[0], wrow_off, xrow_off, sa, sx, acc);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sa[q] = san[q];
-        sx[0] = sxn[0];
-        sx[1] = sxn[1];
-      } else {
-        k_step<3, false>(F1, F0, sb, 0, wrow_off, xrow_off, sa, sx, acc);
-      }
+    for (int f = 1; f < 4; ++f) F0.A[f] = lds16(smem + wrow_off + f * 32 * ROW_BYTES + coff[0]);
+
+    // One K stage. Every read of slot st is issued by the end of step 2: retire
+    // them, wait for stage st+1 (the only copies in flight) and run the last
+    // step, whose MFMAs overlap `copy` (the refill of slot st with stage st+2)
+    // and the reads of stage st+1's first step. In the last stage those reads
+    // fetch bytes that are never used.
+    auto stage = [&](int st, const auto& copy) {
+      const uint8_t* sb = smem + (st % NSTAGE) * STAGE_BYTES;
+      k_step<0, true>(F0, F1, sb, coff[1], wrow_off, xrow_off, sa, sx, acc, NoCopy{});
+      k_step<1, true>(F1, F0, sb, coff[2], wrow_off, xrow_off, sa, sx, acc, NoCopy{});
+      k_step<2, true>(F0, F1, sb, coff[3], wrow_off, xrow_off, sa, sx, acc, NoCopy{});
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const uint8_t* sbn = smem + ((st + 1) % NSTAGE) * STAGE_BYTES;
+      uint32_t san[4], sxn[2];
+      read_scales(st + 1, san, sxn);
+      k_step<3, true>(F1, F0, sbn, coff[0], wrow_off, xrow_off, sa, sx, acc, copy);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sa[q] = san[q];
+      sx[0] = sxn[0];
+      sx[1] = sxn[1];
+    };
+    // Two loops rather than a branch per stage: with a branch the compiler hoists
+    // the last step's MFMAs (identical on both sides) above the barrier, and the
+    // copies and reads after it no longer overlap any matrix work.
+    int st = 0;
+    for (; st + 2 < nst; ++st) {
+      const int nx = st + 2;
+      stage(st, [&](int i) {   // copies 2i and 2i+1 of stage st+2 before MFMA i
+        if (2 * i < VM_PER_STAGE) copy_one(nx, 2 * i);
+        if (2 * i + 1 < VM_PER_STAGE) copy_one(nx, 2 * i + 1);
+      });
     }
+    for (; st < nst; ++st) stage(st, NoCopy{});
   } else {
-    // the same copies and barriers, without MFMAs (accumulators stay zero)
-    for (int st = 0; st + 1 < nst; ++st) {
+    // the same copies and barriers as `stage`, without MFMAs (accumulators stay
+    // zero): one barrier per stage, so that every wave meets the same barriers
+    for (int st = 0; st < nst; ++st) {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (st + 2 < nst) issue(st + 2);
     }
@@ -365,7 +416,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
           w1 = quant_pair_e8m0<3>(w1, hp[7], sbyte);
           bytes_lo = w0;
           bytes_hi = w1;
-          if (valid && hh == 0) a.h_scales[(int64_t)row * (I >> 5) + (j0 >> 5)] = (uint8_t)sbyte;
+          if (valid && hh == 0) {
+            // row-major [rows][I/32], or tile-major for the L2's copies: m-tile
+            // t.mt, L2 stage j0/256, tile row ml, byte (j0/32) % 8
+            const int64_t at = a.h_scales_packed
+                                   ? ((int64_t)t.mt * ((I + BK - 1) / BK) + (j0 >> 8)) * SC_TILE_STAGE_BYTES +
+                                         ml * SC_BYTES + ((j0 >> 5) & 7)
+                                   : (int64_t)row * (I >> 5) + (j0 >> 5);
+            a.h_scales[at] = (uint8_t)sbyte;
+          }
         } else {
           // NVFP4: 16-blocks j0..j0+15 (v = 0..7) and j0+16..j0+31 (v = 8..15).
           const float gsc = a.nv_global;
@@ -436,7 +495,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
 // the XCD's L2 and reused from there.
 template <int EPI>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
   __shared__ TileTables tt;
   load_tile_tables(a, tt);
   const int b = blockIdx.x;

@@ -12,6 +12,7 @@ struct Tile {
   int nt;        // tile index along weight rows
   int row0;      // first row (sorted order) of the token tile
   int rows;      // valid rows in the token tile
+  int mt;        // m-tile index within the launch (tile-major scale layouts)
 };
 
 // Routed launches keep the expert offsets and m-tile bases (E+1 each) in LDS:
@@ -51,6 +52,7 @@ static __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Tile
     const int mt = L - t.nt * mtiles;
     t.row0 = mt * BM;
     t.rows = min(BM, a.m_rows - t.row0);
+    t.mt = mt;
     return t;
   }
   // expert e with tile_base[e] * n_tiles <= L < tile_base[e + 1] * n_tiles
@@ -69,6 +71,7 @@ static __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Tile
   const int off = tt.expert_off[e];
   t.row0 = off + mt * BM;
   t.rows = min(BM, tt.expert_off[e + 1] - t.row0);
+  t.mt = tb + mt;
   return t;
 }
 

@@ -88,45 +88,59 @@ struct Carve {
 // weight-streaming paths for small M):
 //   few tokens (M <= 8): h, the bf16 SiLU output;
 //   9 <= M <= 96:        xq, xs, hq, hs, then h;
-//   GEMM path:           xq, xs, hq, hs.
+//   GEMM path:           xq, xs, hq, hs, xs_pk.
+// On the GEMM path xs_pk is the tile-major copy of xs that L1 reads, and with
+// MXFP4 re-quantisation hs is tile-major over the m-tiles (L2 reads it so);
+// with NVFP4 hs is row-major E4M3 per 16.
 enum DensePath { DENSE_DECODE, DENSE_SKINNY, DENSE_GEMM };
 struct DenseWs {
   DensePath path;
-  uint8_t *xq, *xs, *hq, *hs;
+  uint8_t *xq, *xs, *hq, *hs, *xs_pk;
   uint16_t* h;
   size_t bytes;
 };
 DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
   Carve c(base);
   DenseWs w;
-  w.xq = w.xs = w.hq = w.hs = nullptr;
+  w.xq = w.xs = w.hq = w.hs = w.xs_pk = nullptr;
   w.h = nullptr;
   if (rq == MX_FMT_MXFP4 && decode_fits(M, H, I)) {
     w.path = DENSE_DECODE;
     w.h = (uint16_t*)c.take((size_t)(M * I * 2));
   } else {
     w.path = (rq == MX_FMT_MXFP4 && skinny_fits(M, H, I)) ? DENSE_SKINNY : DENSE_GEMM;
+    const int64_t mtiles = (M + BM - 1) / BM;
     w.xq = (uint8_t*)c.take((size_t)(M * H / 2));
     w.xs = (uint8_t*)c.take((size_t)(M * H / 32));
     w.hq = (uint8_t*)c.take((size_t)(M * I / 2));
-    w.hs = (uint8_t*)c.take((size_t)(M * I / (rq == MX_FMT_NVFP4 ? 16 : 32)));
+    if (rq == MX_FMT_NVFP4) w.hs = (uint8_t*)c.take((size_t)(M * I / 16));
+    else if (w.path == DENSE_GEMM) w.hs = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, I));
+    else w.hs = (uint8_t*)c.take((size_t)(M * I / 32));
     if (w.path == DENSE_SKINNY) w.h = (uint16_t*)c.take((size_t)(M * I * 2));
+    else w.xs_pk = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, H));
   }
   w.bytes = c.off;
   return w;
 }
 
+// Routed workspace: xq, xs, the route buffers, hq, hs, o, xs_pk. As on the
+// dense GEMM path, xs_pk is the tile-major copy of the gathered xs and, with
+// MXFP4 re-quantisation, hs is tile-major over the m-tiles.
 struct GroupWs {
-  uint8_t *xq, *xs, *hq, *hs;
+  uint8_t *xq, *xs, *hq, *hs, *xs_pk;
   uint16_t* o;
   RouteBuffers rb;
   size_t bytes;
 };
+// Upper bound of the m-tiles of a routed launch: every expert adds at most one
+// partly filled tile.
+int64_t max_route_mtiles(int64_t P, int E) { return (P + (int64_t)E * (BM - 1)) / BM; }
 GroupWs group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E, mx_format rq) {
   Carve c(base);
   GroupWs w;
   const int64_t P = T * k;
   const int64_t nblocks = (P + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+  const int64_t mtiles = max_route_mtiles(P, E);
   w.xq = (uint8_t*)c.take((size_t)(T * H / 2));
   w.xs = (uint8_t*)c.take((size_t)(T * H / 32));
   w.rb.block_counts = (int32_t*)c.take((size_t)(nblocks * E * 4));
@@ -136,10 +150,26 @@ GroupWs group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E, mx_f
   w.rb.row_slot = (int32_t*)c.take((size_t)P * 4);
   w.rb.row_weight = (float*)c.take((size_t)P * 4);
   w.hq = (uint8_t*)c.take((size_t)(P * I / 2));
-  w.hs = (uint8_t*)c.take((size_t)(P * I / (rq == MX_FMT_NVFP4 ? 16 : 32)));
+  w.hs = (uint8_t*)c.take(rq == MX_FMT_NVFP4 ? (size_t)(P * I / 16) : (size_t)packed_scale_bytes(mtiles, I));
   w.o = (uint16_t*)c.take((size_t)(P * H * 2));
+  w.xs_pk = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, H));
   w.bytes = c.off;
   return w;
+}
+
+// The tile-major weight scales written by mx_pack_weight_scales: for each
+// expert, L1 (gate/up pairs, tiles of 128 j) and then, after all experts' L1
+// parts, L2 (tiles of 256 rows).
+struct PackedWeights {
+  int64_t l1_estride, l2_estride, l1_bytes, bytes;
+};
+PackedWeights packed_weights(int64_t H, int64_t I, int64_t E) {
+  PackedWeights p;
+  p.l1_estride = packed_scale_bytes((I + L1_J_PER_TILE - 1) / L1_J_PER_TILE, H);
+  p.l2_estride = packed_scale_bytes((H + BN - 1) / BN, I);
+  p.l1_bytes = E * p.l1_estride;
+  p.bytes = p.l1_bytes + E * p.l2_estride;
+  return p;
 }
 
 // ---------------------------------------------------------------- checks
@@ -341,10 +371,39 @@ static mx_status check_weights(const uint8_t* w1, const uint8_t* w1_s, const uin
   return MX_OK;
 }
 
+size_t mx_packed_weight_scales_size(int64_t hidden, int64_t inter, int32_t E) {
+  if (hidden < 0 || inter < 0 || E < 1) return 0;
+  return (size_t)packed_weights(hidden, inter, E).bytes;
+}
+
+mx_status mx_pack_weight_scales(const uint8_t* w1_s, const uint8_t* w3_s, const uint8_t* w2_s, int64_t hidden,
+                                int64_t inter, int32_t E, uint8_t* packed, size_t packed_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MX_TRY(check_mlp_dims(0, hidden, inter));
+  if (E < 1 || E > ROUTE_MAX_EXPERTS) return fail(MX_ERR_SHAPE, "E %d outside [1, %d]", E, ROUTE_MAX_EXPERTS);
+  MX_REQUIRE_PTR(w1_s);
+  MX_REQUIRE_PTR(w3_s);
+  MX_REQUIRE_PTR(w2_s);
+  MX_REQUIRE_PTR(packed);
+  MX_REQUIRE_ALIGN(w1_s, 4);
+  MX_REQUIRE_ALIGN(w3_s, 4);
+  MX_REQUIRE_ALIGN(w2_s, 4);
+  MX_REQUIRE_ALIGN(packed, 256);
+  const PackedWeights pw = packed_weights(hidden, inter, E);
+  if (packed_bytes < (size_t)pw.bytes)
+    return fail(MX_ERR_WORKSPACE, "packed buffer %zu bytes < required %lld", packed_bytes, (long long)pw.bytes);
+  MX_HIP(phase("pack_w_scales", s, [&] {
+           hipError_t e = launch_pack_weight_scales(w1_s, w3_s, E, (int)inter, (int)hidden, packed, s);
+           if (e != hipSuccess) return e;
+           return launch_pack_weight_scales(w2_s, nullptr, E, (int)hidden, (int)inter, packed + pw.l1_bytes, s);
+         }), "pack_w_scales");
+  return ok();
+}
+
 mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, const uint8_t* w1,
                         const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s, const uint8_t* w2,
-                        const uint8_t* w2_s, mx_format requant, float requant_global, uint16_t* y,
-                        void* workspace, size_t ws_bytes, void* stream) {
+                        const uint8_t* w2_s, const uint8_t* packed_scales, mx_format requant, float requant_global,
+                        uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   MX_TRY(check_mlp_dims(M, hidden, inter));
   MX_TRY(check_requant(requant, requant_global));
@@ -354,6 +413,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   MX_REQUIRE_ALIGN(x, 16);
   MX_REQUIRE_ALIGN(y, 16);
   MX_TRY(check_weights(w1, w1_s, w3, w3_s, w2, w2_s));
+  MX_REQUIRE_ALIGN(packed_scales, 256);
   const size_t need = mx_expert_mlp_workspace_size(M, hidden, inter, requant);
   MX_REQUIRE_PTR(workspace);
   MX_REQUIRE_ALIGN(workspace, 256);
@@ -378,26 +438,35 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
     return ok();
   }
 
-  MX_HIP(phase("quant_x", s, [&] { return launch_quant_mxfp4(x, M, hidden, w.xq, w.xs, s); }), "quant_x");
+  const int mtiles = (m + BM - 1) / BM;
+  const PackedWeights pw = packed_weights(hidden, inter, 1);
+  MX_HIP(phase("quant_x", s, [&] {
+           hipError_t e = launch_quant_mxfp4(x, M, hidden, w.xq, w.xs, s);
+           if (e != hipSuccess) return e;
+           return launch_pack_act_scales(w.xs, H, nullptr, nullptr, nullptr, 1, m, mtiles, w.xs_pk, s);
+         }), "quant_x");
 
   GemmArgs l1 = base_args();
   l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
+  l1.w_spk = packed_scales; l1.wspk_estride = pw.l1_estride;
   l1.n_rows = I; l1.k = H;
-  l1.x = w.xq; l1.x_s = w.xs;
+  l1.x = w.xq; l1.x_s = w.xs_pk; l1.x_s_packed = 1;
   l1.m_rows = m; l1.n_experts = 1;
   l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
-  l1.grid_tiles = ((m + BM - 1) / BM) * l1.n_tiles;
+  l1.grid_tiles = mtiles * l1.n_tiles;
   l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_global = requant_global;
+  l1.h_scales_packed = requant == MX_FMT_MXFP4;
   const Epilogue l1_epi = requant == MX_FMT_NVFP4 ? EPI_SWIGLU_NVFP4 : EPI_SWIGLU_MXFP4;
   MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(l1_epi, l1, l1.grid_tiles, s); }), "l1_gemm");
 
   GemmArgs l2 = base_args();
   l2.wa = w2; l2.wa_s = w2_s;
+  l2.w_spk = packed_scales ? packed_scales + pw.l1_bytes : nullptr; l2.wspk_estride = pw.l2_estride;
   l2.n_rows = H; l2.k = I;
-  l2.x = w.hq; l2.x_s = w.hs;
+  l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4;
   l2.m_rows = m; l2.n_experts = 1;
   l2.n_tiles = (H + BN - 1) / BN;
-  l2.grid_tiles = ((m + BM - 1) / BM) * l2.n_tiles;
+  l2.grid_tiles = mtiles * l2.n_tiles;
   l2.out_bf16 = y;
   if (requant == MX_FMT_NVFP4) {
     l2.nv_global = requant_global;
@@ -411,8 +480,9 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
 mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
                                 const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                 const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
-                                const uint8_t* w2, const uint8_t* w2_s, mx_format requant, float requant_global,
-                                uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+                                const uint8_t* w2, const uint8_t* w2_s, const uint8_t* packed_scales,
+                                mx_format requant, float requant_global, uint16_t* y, void* workspace,
+                                size_t ws_bytes, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   MX_TRY(check_mlp_dims(T, hidden, inter));
   MX_TRY(check_requant(requant, requant_global));
@@ -429,6 +499,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   MX_REQUIRE_ALIGN(topk_ids, 4);
   MX_REQUIRE_ALIGN(topk_w, 4);
   MX_TRY(check_weights(w1, w1_s, w3, w3_s, w2, w2_s));
+  MX_REQUIRE_ALIGN(packed_scales, 256);
   const size_t need = mx_grouped_expert_mlp_workspace_size(T, hidden, inter, k, E, requant);
   MX_REQUIRE_PTR(workspace);
   MX_REQUIRE_ALIGN(workspace, 256);
@@ -437,27 +508,36 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   GroupWs w = group_ws(workspace, T, hidden, inter, k, E, requant);
   const int H = (int)hidden, I = (int)inter;
   const int64_t P = T * k;
-  const int max_mtiles = (int)((P + (int64_t)E * (BM - 1)) / BM);
+  const int max_mtiles = (int)max_route_mtiles(P, E);
+  const PackedWeights pw = packed_weights(hidden, inter, E);
 
   MX_HIP(phase("quant_x", s, [&] { return launch_quant_mxfp4(x, T, hidden, w.xq, w.xs, s); }), "quant_x");
-  MX_HIP(phase("route", s, [&] { return launch_route(topk_ids, topk_w, T, k, E, w.rb, s); }), "route");
+  MX_HIP(phase("route", s, [&] {
+           hipError_t e = launch_route(topk_ids, topk_w, T, k, E, w.rb, s);
+           if (e != hipSuccess) return e;
+           return launch_pack_act_scales(w.xs, H, w.rb.row_token, w.rb.expert_off, w.rb.tile_base, E, 0,
+                                         max_mtiles, w.xs_pk, s);
+         }), "route");
 
   GemmArgs l1 = base_args();
   l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
   l1.w_estride = (int64_t)I * H / 2; l1.ws_estride = (int64_t)I * H / 32;
+  l1.w_spk = packed_scales; l1.wspk_estride = pw.l1_estride;
   l1.n_rows = I; l1.k = H;
-  l1.x = w.xq; l1.x_s = w.xs; l1.row_token = w.rb.row_token;
+  l1.x = w.xq; l1.x_s = w.xs_pk; l1.x_s_packed = 1; l1.row_token = w.rb.row_token;
   l1.expert_off = w.rb.expert_off; l1.tile_base = w.rb.tile_base; l1.n_experts = E;
   l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
   l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_global = requant_global;
+  l1.h_scales_packed = requant == MX_FMT_MXFP4;
   const Epilogue l1_epi = requant == MX_FMT_NVFP4 ? EPI_SWIGLU_NVFP4 : EPI_SWIGLU_MXFP4;
   MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(l1_epi, l1, max_mtiles * l1.n_tiles, s); }), "l1_gemm");
 
   GemmArgs l2 = base_args();
   l2.wa = w2; l2.wa_s = w2_s;
   l2.w_estride = (int64_t)H * I / 2; l2.ws_estride = (int64_t)H * I / 32;
+  l2.w_spk = packed_scales ? packed_scales + pw.l1_bytes : nullptr; l2.wspk_estride = pw.l2_estride;
   l2.n_rows = H; l2.k = I;
-  l2.x = w.hq; l2.x_s = w.hs;
+  l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4;
   l2.expert_off = w.rb.expert_off; l2.tile_base = w.rb.tile_base; l2.n_experts = E;
   l2.n_tiles = (H + BN - 1) / BN;
   l2.out_bf16 = w.o; l2.row_slot = w.rb.row_slot; l2.row_weight = w.rb.row_weight;

@@ -17,6 +17,13 @@ constexpr int NSTAGE = 2;
 constexpr int GEMM_THREADS = 512;
 constexpr int L1_J_PER_TILE = BN / 2;    // L1 tiles hold gate and up rows for 128 j
 
+// Tile-major scale layout (pack.hip): per tile and K stage, the 8 scale bytes
+// of each of the tile's 256 rows, contiguous.
+constexpr int SC_STAGE_BYTES = BK / 32;                           // 8
+constexpr int SC_TILE_STAGE_BYTES = 256 * SC_STAGE_BYTES;         // 2048
+// Bytes of the tile-major layout of `tiles` tiles over K.
+constexpr int64_t packed_scale_bytes(int64_t tiles, int64_t k) { return tiles * ((k + BK - 1) / BK) * SC_TILE_STAGE_BYTES; }
+
 // Epilogue kinds of the scaled-MFMA GEMM.
 enum Epilogue : int {
   EPI_F32 = 0,          // C[m][n] fp32 (test hook)
@@ -34,13 +41,18 @@ struct GemmArgs {
   const uint8_t* wb_s;
   int64_t w_estride;    // bytes between experts' code matrices
   int64_t ws_estride;   // bytes between experts' scale matrices
+  // Optional tile-major copy of the weight scales (pack.hip): when set, the
+  // GEMM reads it instead of wa_s/wb_s. Expert e starts at w_spk + e * wspk_estride.
+  const uint8_t* w_spk;
+  int64_t wspk_estride;
   int n_rows;           // logical weight rows per matrix (inter for L1, hidden for L2)
   int k;                // logical K (multiple of 128)
 
   // MFMA B operand: token rows (MXFP4) [rows, k/2] + [rows, k/32].
   const uint8_t* x;
-  const uint8_t* x_s;
+  const uint8_t* x_s;         // [rows, k/32], or tile-major over the m-tiles when x_s_packed
   const int32_t* row_token;   // grouped L1: sorted row -> token; null = identity
+  int x_s_packed;
 
   // Row groups: grouped mode has expert_off/tile_base on the device;
   // dense mode (expert_off == null) is a single group of m_rows rows.
@@ -55,6 +67,7 @@ struct GemmArgs {
   float* c_f32;               // EPI_F32: [m_rows, n_rows]
   uint8_t* h_codes;           // L1: [rows, n_rows/2]
   uint8_t* h_scales;          // L1: [rows, n_rows/32] (MXFP4) or [rows, n_rows/16] (NVFP4)
+  int h_scales_packed;        // L1 MXFP4: h_scales tile-major over the m-tiles (the L2's x_s)
   float nv_global;            // L1 NVFP4 global scale
   uint16_t* out_bf16;         // EPI_BF16: dense y [m_rows, n_rows]; grouped o [slots, n_rows]
   const int32_t* row_slot;    // grouped L2: sorted row -> slot (t*k + j)
@@ -72,6 +85,17 @@ hipError_t launch_gemm_nv_l2(const GemmArgs& a, int max_tiles, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int cu_count();
+
+// Tile-major scale copies (pack.hip). Weights: b_s null for a plain matrix of
+// n_rows rows (tiles of 256 rows), else the L1 pair (a_s gate, b_s up, tiles
+// of 128 rows of each); out holds n_experts * tiles * stages * 2048 bytes.
+hipError_t launch_pack_weight_scales(const uint8_t* a_s, const uint8_t* b_s, int n_experts, int n_rows, int k,
+                                     uint8_t* out, hipStream_t s);
+// Activations: the m-tiles of a routed (expert_off set, tokens via row_token)
+// or dense (m_rows rows) launch; out holds max_mtiles * stages * 2048 bytes.
+hipError_t launch_pack_act_scales(const uint8_t* x_s, int k, const int32_t* row_token, const int32_t* expert_off,
+                                  const int32_t* tile_base, int n_experts, int m_rows, int max_mtiles,
+                                  uint8_t* out, hipStream_t s);
 
 // ---- Elementwise kernels ---------------------------------------------------
 hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows,

@@ -88,3 +88,55 @@ def assert_nvfp4_requant_close(gpu_codes, gpu_scales, ref_codes, ref_scales, g, 
     step = 2.0 * np.maximum(sg, sr)
     assert np.all(np.abs(gv * sg - rv * sr) <= step), np.abs(gv * sg - rv * sr).max()
     return frac
+
+
+def as_np(a):
+    """device tensor or numpy array -> numpy array."""
+    return a.cpu().numpy() if isinstance(a, torch.Tensor) else np.asarray(a)
+
+
+# Tile-major scale layout of the GEMM (the library's pack.hip): per tile of 256
+# rows and per 256-wide K stage, 8 scale bytes of each row, contiguous.
+def packed_scale_bytes(tiles, k):
+    return tiles * ((k + 255) // 256) * 2048
+
+
+def unpack_tile_major(buf, rows, k):
+    """Tile-major bytes of row tiles [tiles][stage][256][8] -> row-major [rows, k/32]."""
+    nst, ks = (k + 255) // 256, k // 32
+    tiles = (rows + 255) // 256
+    a = np.asarray(buf, np.uint8)[:tiles * nst * 2048].reshape(tiles, nst, 256, 8)
+    full = a.transpose(0, 2, 1, 3).reshape(tiles * 256, nst * 8)
+    return full[:rows, :ks]
+
+
+def pack_weight_scales_ref(w1s, w3s, w2s):
+    """Expected output of mx_pack_weight_scales (layout only: byte moves) for
+    stacked scales w1s/w3s [E, I, H/32], w2s [E, H, I/32]."""
+    E, I, hs = w1s.shape
+    H = 32 * hs
+
+    # L1 tiles: 128 j per tile; tile row r -> gate (w1) rows for (r/32)%4 < 2, else up (w3)
+    nst1, ks1 = (H + 255) // 256, H // 32
+    g = np.zeros((E, I, nst1 * 8), np.uint8)
+    g[:, :, :ks1] = w1s
+    u = np.zeros((E, I, nst1 * 8), np.uint8)
+    u[:, :, :ks1] = w3s
+    nt1 = (I + 127) // 128
+    l1 = np.zeros((E, nt1, nst1, 256, 8), np.uint8)
+    for nt in range(nt1):
+        for r in range(256):
+            f = (r >> 5) & 3
+            row = min(nt * 128 + (r >> 7) * 64 + (f & 1) * 32 + (r & 31), I - 1)
+            src = g if f < 2 else u
+            l1[:, nt, :, r, :] = src[:, row].reshape(E, nst1, 8)
+    nst2, ks2 = (I + 255) // 256, I // 32
+    d = np.zeros((E, H, nst2 * 8), np.uint8)
+    d[:, :, :ks2] = w2s
+    nt2 = (H + 255) // 256
+    l2 = np.zeros((E, nt2, nst2, 256, 8), np.uint8)
+    for nt in range(nt2):
+        for r in range(256):
+            row = min(nt * 256 + r, H - 1)
+            l2[:, nt, :, r, :] = d[:, row].reshape(E, nst2, 8)
+    return np.concatenate([l1.reshape(-1), l2.reshape(-1)])

@@ -72,29 +72,44 @@ def test_mlp_validation(L):
     P = ctypes.c_void_p
     z = [P(256)] * 6
     # hidden not a multiple of 128
-    assert L.mx_expert_mlp(P(256), 4, 200, 128, *z, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
-    assert L.mx_expert_mlp(P(256), 4, 256, 96, *z, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
+    assert L.mx_expert_mlp(P(256), 4, 200, 128, *z, None, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
+    assert L.mx_expert_mlp(P(256), 4, 256, 96, *z, None, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
     # NVFP4 re-quant needs a finite global scale >= 2^-117; FP8 is not a re-quant format
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 2, 0.0, P(256), P(256), 1 << 30, None) == 7
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 2, float("nan"), P(256), P(256), 1 << 30, None) == 7
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 1, 0.0, P(256), P(256), 1 << 30, None) == 4
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 2, 0.0, P(256), P(256), 1 << 30, None) == 7
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 2, float("nan"), P(256), P(256), 1 << 30, None) == 7
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 1, 0.0, P(256), P(256), 1 << 30, None) == 4
     # NVFP4 keeps one E4M3 byte per 16 columns of h: a larger workspace than MXFP4
-    assert L.mx_expert_mlp_workspace_size(64, 256, 128, 2) > L.mx_expert_mlp_workspace_size(64, 256, 128, 0)
+    assert L.mx_expert_mlp_workspace_size(4096, 7168, 3072, 2) > L.mx_expert_mlp_workspace_size(4096, 7168, 3072, 0)
     # workspace too small
     need = L.mx_expert_mlp_workspace_size(4, 256, 128, 0)
     assert need > 0
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 0, 0.0, P(256), P(256), need - 1, None) == 5
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 0, 0.0, P(256), P(256), need - 1, None) == 5
     # misaligned workspace, null weights
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, 0, 0.0, P(256), P(128), need, None) == 3
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, None, *z[1:], 0, 0.0, P(256), P(256), need, None) == 1
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 0, 0.0, P(256), P(128), need, None) == 3
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, None, *z[1:], None, 0, 0.0, P(256), P(256), need, None) == 1
     # zero tokens is a no-op
-    assert L.mx_expert_mlp(None, 0, 256, 128, *([None] * 6), 0, 0.0, None, None, 0, None) == 0
+    assert L.mx_expert_mlp(None, 0, 256, 128, *([None] * 7), 0, 0.0, None, None, 0, None) == 0
+    # packed weight scales must be 256-byte aligned (NULL selects the row-major scales)
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, P(128), 0, 0.0, P(256), P(256), need, None) == 3
+
+
+def test_pack_weight_scales_validation(L):
+    P = ctypes.c_void_p
+    need = L.mx_packed_weight_scales_size(256, 128, 4)
+    # per expert: L1 one tile of 128 j x 1 stage, L2 one tile of 256 rows x 1 stage, 2 KB each
+    assert need == 4 * (2048 + 2048)
+    assert L.mx_packed_weight_scales_size(7168, 3072, 48) == 48 * (24 * 28 + 28 * 12) * 2048
+    assert L.mx_pack_weight_scales(P(256), P(256), P(256), 200, 128, 4, P(256), need, None) == 2
+    assert L.mx_pack_weight_scales(P(256), P(256), P(256), 256, 128, 0, P(256), need, None) == 2
+    assert L.mx_pack_weight_scales(None, P(256), P(256), 256, 128, 4, P(256), need, None) == 1
+    assert L.mx_pack_weight_scales(P(256), P(256), P(256), 256, 128, 4, P(128), need, None) == 3
+    assert L.mx_pack_weight_scales(P(256), P(256), P(256), 256, 128, 4, P(256), need - 1, None) == 5
 
 
 def test_grouped_validation(L):
     P = ctypes.c_void_p
     z = [P(256)] * 6
-    args = lambda k, E, ws: (P(256), 8, 256, 128, P(256), P(256), k, E, *z, 0, 0.0, P(256), P(256), ws, None)
+    args = lambda k, E, ws: (P(256), 8, 256, 128, P(256), P(256), k, E, *z, None, 0, 0.0, P(256), P(256), ws, None)
     assert L.mx_grouped_expert_mlp(*args(0, 4, 1 << 30)) == 2
     assert L.mx_grouped_expert_mlp(*args(5, 4, 1 << 30)) == 2
     assert L.mx_grouped_expert_mlp(*args(2, 2000, 1 << 30)) == 2

@@ -6,7 +6,11 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, t
+from gpu_util import (as_np, assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, pack_weight_scales_ref,
+                      packed_scale_bytes, t, unpack_tile_major)
+
+_np = as_np
+WN = ("w1", "w1s", "w3", "w3s", "w2", "w2s")
 
 pytestmark = pytest.mark.gpu
 
@@ -20,15 +24,27 @@ def mx():
 DECODE_MAX_TOKENS = 8    # mx_expert_mlp streams the weights once for up to 8 tokens
 
 
-def _ws_slices(ws, M, H, I):
+def _align(n):
+    return (n + 255) // 256 * 256
+
+
+def _ws_slices(mx, ws, M, H, I):
     """Dense workspace layout of mx_expert_mlp, each region 256-byte aligned:
-    M > 8: xq, xs, hq, hs (then h for M <= 96); few tokens: h (bf16 SiLU output)."""
+    few tokens: h (bf16 SiLU output); weight-streaming path (9..96 tokens): xq,
+    xs, hq, hs (row-major), h; GEMM path: xq, xs, hq, hs (tile-major), xs_pk.
+    Returns (xq, xs, hq, hs) with hs row-major [M, I/32], or (h,)."""
     if M <= DECODE_MAX_TOKENS:
         return [ws[:M * I * 2]]
+    mt = (M + 255) // 256
+    gemm = [M * H // 2, M * H // 32, M * I // 2, packed_scale_bytes(mt, I), packed_scale_bytes(mt, H)]
+    tile_major = sum(_align(n) for n in gemm) == mx.expert_mlp_workspace_size(M, H, I)
+    sizes = gemm[:4] if tile_major else [M * H // 2, M * H // 32, M * I // 2, M * I // 32]
     off, out = 0, []
-    for n in (M * H // 2, M * H // 32, M * I // 2, M * I // 32):
+    for n in sizes:
         out.append(ws[off:off + n])
-        off += (n + 255) // 256 * 256
+        off += _align(n)
+    if tile_major:
+        out[3] = unpack_tile_major(out[3].cpu().numpy(), M, I)
     return out
 
 
@@ -67,13 +83,15 @@ def test_debug_gemm_f32(mx, M, N, K):
 
 
 # ---------------------------------------------------------------- shared expert
-def _run_dense(mx, d, M, H, I):
+def _run_dense(mx, d, M, H, I, packed=False):
     x = d["x"]
     nbytes = mx.expert_mlp_workspace_size(M, H, I)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    y = mx.expert_mlp(bf16_t(x), *(t(d[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")), workspace=ws)
+    wd = [t(d[n]) for n in WN]
+    pk = mx.pack_weight_scales(wd[1], wd[3], wd[5]) if packed else None
+    y = mx.expert_mlp(bf16_t(x), *wd, workspace=ws, packed_scales=pk)
     torch.cuda.synchronize()
-    return bits(y), _ws_slices(ws, M, H, I)
+    return bits(y), _ws_slices(mx, ws, M, H, I)
 
 
 def _check_gemm_path(mx, d, M, H, I):
@@ -81,7 +99,7 @@ def _check_gemm_path(mx, d, M, H, I):
     ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
     assert np.array_equal(xq.cpu().numpy().reshape(M, H // 2), inter["xq"])
     assert np.array_equal(xs.cpu().numpy().reshape(M, H // 32), inter["xs"])
-    assert_requant_close(hq.cpu().numpy().reshape(M, I // 2), hs.cpu().numpy().reshape(M, I // 32),
+    assert_requant_close(hq.cpu().numpy().reshape(M, I // 2), _np(hs).reshape(M, I // 32),
                          inter["hq"], inter["hs"])
     assert_mlp_close(y, ref)
 
@@ -117,7 +135,7 @@ def test_shared_expert_real_shape(mx, M):
         _check_h_and_requant(mx, sl[0], M, 3072, inter)
     else:
         _, _, hq, hs = sl
-        assert_requant_close(hq.cpu().numpy().reshape(M, 1536), hs.cpu().numpy().reshape(M, 96), inter["hq"], inter["hs"])
+        assert_requant_close(hq.cpu().numpy().reshape(M, 1536), _np(hs).reshape(M, 96), inter["hq"], inter["hs"])
     assert_mlp_close(y, ref)
 
 
@@ -132,9 +150,11 @@ def test_shared_expert_prefill_sampled_rows(mx):
 
 
 # ---------------------------------------------------------------- routed experts
-def _run_grouped(mx, d):
-    y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]),
-                              *(t(d[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")))
+def _run_grouped(mx, d, packed=False, requant="mxfp4", g=0.0):
+    wd = [t(d[n]) for n in WN]
+    pk = mx.pack_weight_scales(wd[1], wd[3], wd[5]) if packed else None
+    y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]), *wd, requant=requant, requant_global=g,
+                              packed_scales=pk)
     torch.cuda.synchronize()
     return bits(y)
 
@@ -179,7 +199,7 @@ def test_grouped_permutation_empty_and_foreign_ids(mx):
 
 def test_grouped_headline_sampled_tokens(mx):
     d = W.grouped(tokens=4096, n_experts=48, k=8, seed=0)
-    y = _run_grouped(mx, d)
+    y = _run_grouped(mx, d, packed=True)
     tok = np.array([0, 1, 2, 4095])
     assert_mlp_close(y[tok], _oracle_grouped(d, tokens=tok))
     assert np.all(np.isfinite(((y.astype(np.uint32) << 16).view(np.float32))))
@@ -196,3 +216,40 @@ def test_grouped_skewed_sampled_tokens(mx):
     tail = dict(d, x=d["x"][:8], ids=d["ids"][:8], w=d["w"][:8])
     yt = _run_grouped(mx, tail)
     assert_mlp_close(yt, _oracle_grouped(tail))
+
+
+# ---------------------------------------------------------------- tile-major weight scales
+@pytest.mark.parametrize("E,H,I", [(3, 384, 256), (2, 512, 384), (1, 7168, 3072)])
+def test_pack_weight_scales_layout(mx, E, H, I):
+    """mx_pack_weight_scales moves bytes only: compare with the layout written out in numpy
+    (rows past the end repeat the last row; bytes past a row's end are zero)."""
+    rng = np.random.default_rng(E * 1000 + H + I)
+    w1s = rng.integers(0, 256, (E, I, H // 32), dtype=np.uint8)
+    w3s = rng.integers(0, 256, (E, I, H // 32), dtype=np.uint8)
+    w2s = rng.integers(0, 256, (E, H, I // 32), dtype=np.uint8)
+    pk = mx.pack_weight_scales(t(w1s), t(w3s), t(w2s))
+    assert pk.numel() == mx.packed_weight_scales_size(H, I, E)
+    assert np.array_equal(pk.cpu().numpy(), pack_weight_scales_ref(w1s, w3s, w2s))
+
+
+@pytest.mark.parametrize("M,H,I", [(16, 256, 128), (300, 384, 384), (128, 7168, 3072)])
+def test_packed_scales_same_result_dense(mx, M, H, I):
+    """The tile-major weight scales feed the same MFMAs the same bytes: bit-identical output."""
+    d = W.tiny_mlp(0) if H == 256 else W.shared_expert(M, seed=11, hidden=H, inter=I)
+    d["x"] = d["x"][:M]
+    y0, _ = _run_dense(mx, d, M, H, I)
+    y1, _ = _run_dense(mx, d, M, H, I, packed=True)
+    assert np.array_equal(y0, y1)
+    ref = O.expert_mlp(d["x"], *(d[n] for n in WN))
+    assert_mlp_close(y1, ref)
+
+
+@pytest.mark.parametrize("requant", ["mxfp4", "nvfp4"])
+def test_packed_scales_same_result_grouped(mx, requant):
+    d = W.grouped(tokens=600, n_experts=8, k=4, seed=5, hidden=512, inter=256)
+    g = 0.05 if requant == "nvfp4" else 0.0
+    y0 = _run_grouped(mx, d, requant=requant, g=g)
+    y1 = _run_grouped(mx, d, packed=True, requant=requant, g=g)
+    assert np.array_equal(y0, y1)
+    if requant == "mxfp4":
+        assert_mlp_close(y1, _oracle_grouped(d))
