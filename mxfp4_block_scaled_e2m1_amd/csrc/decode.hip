@@ -237,8 +237,8 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l1(const uint16_t* __restrict_
   for (int v = 0; v < 4; ++v) up[v] = __shfl_xor(acc[v], 32);
   const int t = lane & 15, q = lane >> 4;
   if ((threadIdx.x >> 6) == 0 && q < 2 && t < m) {
-    const uint32_t p0 = f32_to_bf16_rne(silu_mul(acc[0], up[0])) | (f32_to_bf16_rne(silu_mul(acc[1], up[1])) << 16);
-    const uint32_t p1 = f32_to_bf16_rne(silu_mul(acc[2], up[2])) | (f32_to_bf16_rne(silu_mul(acc[3], up[3])) << 16);
+    const uint32_t p0 = bf16x2_rne(silu_mul(acc[0], up[0]), silu_mul(acc[1], up[1]));
+    const uint32_t p1 = bf16x2_rne(silu_mul(acc[2], up[2]), silu_mul(acc[3], up[3]));
     *(uint2*)(h + (int64_t)t * I + j0 + 4 * q) = make_uint2(p0, p1);
   }
 }
@@ -257,8 +257,8 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict_
   const int lane = threadIdx.x & 63;
   const int t = lane & 15, q = lane >> 4;
   if ((threadIdx.x >> 6) == 0 && t < m) {
-    const uint32_t p0 = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    const uint32_t p1 = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    const uint32_t p0 = bf16x2_rne(acc[0], acc[1]);
+    const uint32_t p1 = bf16x2_rne(acc[2], acc[3]);
     *(uint2*)(y + (int64_t)t * H + n0 + 4 * q) = make_uint2(p0, p1);
   }
 }
@@ -362,8 +362,8 @@ __global__ __launch_bounds__(DT, 1) void k_skinny_l1(const uint8_t* __restrict__
   for (int v = 0; v < 4; ++v) up[v] = __shfl_xor(acc[v], 32);
   const int t = wave * 16 + (lane & 15), q = lane >> 4;
   if (wave < NC && q < 2 && t < m) {
-    const uint32_t p0 = f32_to_bf16_rne(silu_mul(acc[0], up[0])) | (f32_to_bf16_rne(silu_mul(acc[1], up[1])) << 16);
-    const uint32_t p1 = f32_to_bf16_rne(silu_mul(acc[2], up[2])) | (f32_to_bf16_rne(silu_mul(acc[3], up[3])) << 16);
+    const uint32_t p0 = bf16x2_rne(silu_mul(acc[0], up[0]), silu_mul(acc[1], up[1]));
+    const uint32_t p1 = bf16x2_rne(silu_mul(acc[2], up[2]), silu_mul(acc[3], up[3]));
     *(uint2*)(h + (int64_t)t * I + j0 + 4 * q) = make_uint2(p0, p1);
   }
 }
@@ -382,8 +382,8 @@ __global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = wave * 16 + (lane & 15), q = lane >> 4;
   if (wave < NC && t < m) {
-    const uint32_t p0 = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    const uint32_t p1 = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    const uint32_t p0 = bf16x2_rne(acc[0], acc[1]);
+    const uint32_t p1 = bf16x2_rne(acc[2], acc[3]);
     *(uint2*)(y + (int64_t)t * H + n0 + 4 * q) = make_uint2(p0, p1);
   }
 }

@@ -394,9 +394,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
         uint32_t hp[8];
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
-          const uint32_t lo = f32_to_bf16_rne(silu_mul(acc[f][g][v], acc[f + 2][g][v]));
-          const uint32_t hi = f32_to_bf16_rne(silu_mul(acc[f][g][v + 1], acc[f + 2][g][v + 1]));
-          hp[v >> 1] = lo | (hi << 16);
+          hp[v >> 1] = bf16x2_rne(silu_mul(acc[f][g][v], acc[f + 2][g][v]),
+                                  silu_mul(acc[f][g][v + 1], acc[f + 2][g][v + 1]));
         }
         uint32_t bytes_lo, bytes_hi;   // this lane's 8 code bytes (positions 4q + 2hh + {0,1})
         if constexpr (EPI == EPI_SWIGLU_MXFP4) {

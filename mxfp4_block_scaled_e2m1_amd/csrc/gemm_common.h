@@ -136,10 +136,8 @@ static __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& a, co
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nl = wn * 128 + f * 32 + 8 * q + 4 * hh;
-        const uint32_t p0 =
-            f32_to_bf16_rne(acc[f][g][4 * q] * wgt) | (f32_to_bf16_rne(acc[f][g][4 * q + 1] * wgt) << 16);
-        const uint32_t p1 =
-            f32_to_bf16_rne(acc[f][g][4 * q + 2] * wgt) | (f32_to_bf16_rne(acc[f][g][4 * q + 3] * wgt) << 16);
+        const uint32_t p0 = bf16x2_rne(acc[f][g][4 * q] * wgt, acc[f][g][4 * q + 1] * wgt);
+        const uint32_t p1 = bf16x2_rne(acc[f][g][4 * q + 2] * wgt, acc[f][g][4 * q + 3] * wgt);
         *(uint2*)(trow + nl * 2) = make_uint2(p0, p1);
       }
   }

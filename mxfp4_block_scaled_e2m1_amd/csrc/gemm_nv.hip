@@ -54,7 +54,7 @@ struct NvRaw {
 };
 
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  return bf16x2_rne(lo, hi);
 }
 
 // MXFP4 -> bf16 for one dword of codes (8 columns): code * 2^(e-127), exact.

@@ -42,6 +42,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two fp32 -> two bf16 in a dword (lo in the low half), round to nearest even,
+// with the gfx950 conversion instruction (one instruction instead of five per
+// value). Finite values round exactly as f32_to_bf16_rne; a NaN stays a NaN
+// but keeps the sign and payload bits the hardware gives it, where
+// f32_to_bf16_rne returns 0x7FC0 (the dequant kernels, whose NaN output is
+// compared bit for bit, use that one).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // Two E2M1 codes (byte `sel` of `src`) times 2^(sb-127) -> two bf16 packed in a dword.
 template <int SEL>
 __device__ __forceinline__ uint32_t dequant_pair(uint32_t src, float scale) {

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
     }
     uint32_t r[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = f32_to_bf16_rne(acc[2 * q]) | (f32_to_bf16_rne(acc[2 * q + 1]) << 16);
+    for (int q = 0; q < 4; ++q) r[q] = bf16x2_rne(acc[2 * q], acc[2 * q + 1]);
     *(uint4*)(y + t * (int64_t)H + c) = make_uint4(r[0], r[1], r[2], r[3]);
   }
 }
