@@ -53,26 +53,32 @@ __global__ __launch_bounds__(256) void k_pack_weight_scales(const uint8_t* __res
   *(uint2*)(out + (((int64_t)e * ntiles + nt) * nst + st) * SC_TILE_STAGE_BYTES + r * SC_STAGE_BYTES) = v;
 }
 
-// Activation scales of the token tiles of a launch: block = global m-tile,
-// thread r = tile row. Routed: m-tile mt of expert e (tile_base[e] <= mt <
-// tile_base[e+1]) covers sorted rows expert_off[e] + 256*(mt - tile_base[e]) +
-// r, whose token is row_token[row]. Dense: rows 256*mt + r. Rows past the
-// tile's end are not written (the GEMM reads the last valid row for them).
+// Activation scales of the token tiles of a launch: block (m-tile, group of
+// ACT_STAGES stages), thread r = tile row. Routed: m-tile mt of expert e
+// (tile_base[e] <= mt < tile_base[e+1]) covers sorted rows expert_off[e] +
+// 256*(mt - tile_base[e]) + r, whose token is row_token[row]. Dense: rows
+// 256*mt + r. Rows past the tile's end are not written (the GEMM reads the last
+// valid row for them). The tile bases go through LDS so that the search for
+// the expert costs one round trip to memory instead of one per step.
+constexpr int ACT_STAGES = 4;
 __global__ __launch_bounds__(256) void k_pack_act_scales(const uint8_t* __restrict__ x_s, int ks, int nst,
                                                          const int32_t* __restrict__ row_token,
                                                          const int32_t* __restrict__ expert_off,
                                                          const int32_t* __restrict__ tile_base, int n_experts,
                                                          int m_rows, uint8_t* __restrict__ out) {
-  const int mt = blockIdx.x, r = threadIdx.x;
+  __shared__ int tb[ROUTE_MAX_EXPERTS + 1];
+  const int mt = blockIdx.x, st0 = blockIdx.y * ACT_STAGES, r = threadIdx.x;
   int row0, rows;
   if (expert_off != nullptr) {
-    if (mt >= tile_base[n_experts]) return;
-    int lo = 0, hi = n_experts - 1;   // expert e with tile_base[e] <= mt < tile_base[e + 1]
+    for (int i = r; i <= n_experts; i += 256) tb[i] = tile_base[i];
+    __syncthreads();
+    if (mt >= tb[n_experts]) return;
+    int lo = 0, hi = n_experts - 1;   // expert e with tb[e] <= mt < tb[e + 1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (tile_base[mid] <= mt) lo = mid; else hi = mid - 1;
+      if (tb[mid] <= mt) lo = mid; else hi = mid - 1;
     }
-    row0 = expert_off[lo] + (mt - tile_base[lo]) * BM;
+    row0 = expert_off[lo] + (mt - tb[lo]) * BM;
     rows = expert_off[lo + 1] - row0;
   } else {
     row0 = mt * BM;
@@ -81,8 +87,13 @@ __global__ __launch_bounds__(256) void k_pack_act_scales(const uint8_t* __restri
   if (r >= rows) return;
   const int64_t src_row = row_token != nullptr ? row_token[row0 + r] : row0 + r;
   const uint8_t* src = x_s + src_row * ks;
-  uint8_t* dst = out + (int64_t)mt * nst * SC_TILE_STAGE_BYTES + r * SC_STAGE_BYTES;
-  for (int st = 0; st < nst; ++st) *(uint2*)(dst + st * SC_TILE_STAGE_BYTES) = stage_bytes(src, ks, st);
+  uint2 v[ACT_STAGES];
+#pragma unroll
+  for (int i = 0; i < ACT_STAGES; ++i) v[i] = stage_bytes(src, ks, min(st0 + i, nst - 1));
+#pragma unroll
+  for (int i = 0; i < ACT_STAGES; ++i)
+    if (st0 + i < nst)
+      *(uint2*)(out + ((int64_t)mt * nst + st0 + i) * SC_TILE_STAGE_BYTES + r * SC_STAGE_BYTES) = v[i];
 }
 
 }  // namespace
@@ -103,8 +114,8 @@ hipError_t launch_pack_act_scales(const uint8_t* x_s, int k, const int32_t* row_
                                   uint8_t* out, hipStream_t s) {
   if (max_mtiles <= 0) return hipSuccess;
   const int nst = (k + BK - 1) / BK, ks = k / 32;
-  k_pack_act_scales<<<max_mtiles, 256, 0, s>>>(x_s, ks, nst, row_token, expert_off, tile_base, n_experts, m_rows,
-                                               out);
+  const dim3 grid(max_mtiles, (nst + ACT_STAGES - 1) / ACT_STAGES);
+  k_pack_act_scales<<<grid, 256, 0, s>>>(x_s, ks, nst, row_token, expert_off, tile_base, n_experts, m_rows, out);
   return hipGetLastError();
 }
 
