@@ -61,6 +61,7 @@ __global__ __launch_bounds__(256) void k_pack_weight_scales(const uint8_t* __res
 // valid row for them). The tile bases go through LDS so that the search for
 // the expert costs one round trip to memory instead of one per step.
 constexpr int ACT_STAGES = 4;
+static_assert(ACT_STAGES == 4, "the 16-byte load path below fills four stages");
 __global__ __launch_bounds__(256) void k_pack_act_scales(const uint8_t* __restrict__ x_s, int ks, int nst,
                                                          const int32_t* __restrict__ row_token,
                                                          const int32_t* __restrict__ expert_off,
@@ -88,8 +89,16 @@ __global__ __launch_bounds__(256) void k_pack_act_scales(const uint8_t* __restri
   const int64_t src_row = row_token != nullptr ? row_token[row0 + r] : row0 + r;
   const uint8_t* src = x_s + src_row * ks;
   uint2 v[ACT_STAGES];
+  if (ks % (ACT_STAGES * SC_STAGE_BYTES) == 0) {
+    // whole 32-byte groups (K % 1024 == 0, the model's shapes): two 16-byte loads
+    const uint4 a = *(const uint4*)(src + st0 * SC_STAGE_BYTES);
+    const uint4 b = *(const uint4*)(src + st0 * SC_STAGE_BYTES + 16);
+    v[0] = make_uint2(a.x, a.y); v[1] = make_uint2(a.z, a.w);
+    v[2] = make_uint2(b.x, b.y); v[3] = make_uint2(b.z, b.w);
+  } else {
 #pragma unroll
-  for (int i = 0; i < ACT_STAGES; ++i) v[i] = stage_bytes(src, ks, min(st0 + i, nst - 1));
+    for (int i = 0; i < ACT_STAGES; ++i) v[i] = stage_bytes(src, ks, min(st0 + i, nst - 1));
+  }
 #pragma unroll
   for (int i = 0; i < ACT_STAGES; ++i)
     if (st0 + i < nst)
