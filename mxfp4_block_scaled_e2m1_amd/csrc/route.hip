@@ -104,6 +104,8 @@ __global__ __launch_bounds__(ROUTE_CHUNK) void k_route_scatter(
   }
 }
 
+constexpr int COMBINE_BATCH = 8;   // slots whose rows are loaded together
+
 // y[t][n] = bf16( sum_j o[t*k + j][n] ) over slots j with a local expert, in j order.
 // o rows already carry the gate weight. One thread per 8 columns (16 bytes).
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
@@ -116,15 +118,27 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
     const int64_t t = i / per_row;
     const int c = (int)(i - t * per_row) * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int e = ids[t * k + j];
-      if ((unsigned)e >= (unsigned)E) continue;
-      const uint4 v = *(const uint4*)(o + (t * k + j) * (int64_t)H + c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // Eight slots at a time, all loads issued before any sum: the row of every
+    // slot exists (skipped slots' rows are simply not added), so no load waits
+    // for an id check.
+    for (int j0 = 0; j0 < k; j0 += COMBINE_BATCH) {
+      uint4 v[COMBINE_BATCH];
+      bool ok[COMBINE_BATCH];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += bf16_to_f32(w[q] & 0xFFFFu);
-        acc[2 * q + 1] += bf16_to_f32(w[q] >> 16);
+      for (int q = 0; q < COMBINE_BATCH; ++q) {
+        const int j = min(j0 + q, k - 1);
+        ok[q] = j0 + q < k && (unsigned)ids[t * k + j] < (unsigned)E;
+        v[q] = *(const uint4*)(o + (t * k + j) * (int64_t)H + c);
+      }
+#pragma unroll
+      for (int q = 0; q < COMBINE_BATCH; ++q) {
+        if (!ok[q]) continue;
+        const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += bf16_to_f32(w[i] & 0xFFFFu);
+          acc[2 * i + 1] += bf16_to_f32(w[i] >> 16);
+        }
       }
     }
     uint32_t r[4];
