@@ -86,15 +86,7 @@ __device__ __forceinline__ void quant_x_to_lds(const XBlocks<XR>& xb, int m, int
       for (int i = 0; i < 16; ++i) am = max(am, amax2(w[i]));
       const uint32_t sb = mx_scale_from_amax_bits(am);
       uint32_t q[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t v = 0;
-        v = quant_pair_e8m0<0>(v, w[4 * i], sb);
-        v = quant_pair_e8m0<1>(v, w[4 * i + 1], sb);
-        v = quant_pair_e8m0<2>(v, w[4 * i + 2], sb);
-        v = quant_pair_e8m0<3>(v, w[4 * i + 3], sb);
-        q[i] = v;
-      }
+      quant_pairs_e8m0<16>(w, sb, q);
       if (b < nb) {
         *(uint4*)(codes + row * cstride + c * 16) = make_uint4(q[0], q[1], q[2], q[3]);
         scales[row * bpr + c] = (uint8_t)sb;

@@ -175,11 +175,8 @@ __global__ __launch_bounds__(EW_THREADS) void k_quant_mxfp4(const uint4* __restr
       am = max(am, (uint32_t)__shfl_xor((int)am, 1));
       am = max(am, (uint32_t)__shfl_xor((int)am, 2));
       const uint32_t sb = mx_scale_from_amax_bits(am);
-      uint32_t r = 0;
-      r = quant_pair_e8m0<0>(r, w[0], sb);
-      r = quant_pair_e8m0<1>(r, w[1], sb);
-      r = quant_pair_e8m0<2>(r, w[2], sb);
-      r = quant_pair_e8m0<3>(r, w[3], sb);
+      uint32_t r;
+      quant_pairs_e8m0<4>(w, sb, &r);
       if (u < units) {
         codes[u] = r;
         if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sb;

@@ -404,17 +404,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
           for (int i = 0; i < 8; ++i) am = max(am, amax2(hp[i]));
           am = max(am, (uint32_t)__shfl_xor((int)am, 32));
           const uint32_t sbyte = mx_scale_from_amax_bits(am);
-          uint32_t w0 = 0, w1 = 0;
-          w0 = quant_pair_e8m0<0>(w0, hp[0], sbyte);
-          w0 = quant_pair_e8m0<1>(w0, hp[1], sbyte);
-          w0 = quant_pair_e8m0<2>(w0, hp[2], sbyte);
-          w0 = quant_pair_e8m0<3>(w0, hp[3], sbyte);
-          w1 = quant_pair_e8m0<0>(w1, hp[4], sbyte);
-          w1 = quant_pair_e8m0<1>(w1, hp[5], sbyte);
-          w1 = quant_pair_e8m0<2>(w1, hp[6], sbyte);
-          w1 = quant_pair_e8m0<3>(w1, hp[7], sbyte);
-          bytes_lo = w0;
-          bytes_hi = w1;
+          uint32_t w01[2];
+          quant_pairs_e8m0<8>(hp, sbyte, w01);
+          bytes_lo = w01[0];
+          bytes_hi = w01[1];
           if (valid && hh == 0) {
             // row-major [rows][I/32], or tile-major for the L2's copies: m-tile
             // t.mt, L2 stage j0/256, tile row ml, byte (j0/32) % 8

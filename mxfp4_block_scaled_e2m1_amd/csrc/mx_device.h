@@ -83,6 +83,37 @@ __device__ __forceinline__ uint32_t quant_pair_e8m0(uint32_t old, uint32_t pair,
   return quant_pair_f32_unit<SEL>(old, bf16_to_f32(pair & 0xFFFFu) * up, bf16_to_f32(pair >> 16) * up);
 }
 
+// Quantise N bf16 pairs (N a multiple of 4) sharing the E8M0 scale byte sb
+// into N/4 code dwords, as quant_pair_e8m0 per pair but with one branch for
+// the whole group instead of one per pair (a divergent branch per pair costs
+// more than the conversions it guards).
+template <int N>
+__device__ __forceinline__ void quant_pairs_e8m0(const uint32_t* p, uint32_t sb, uint32_t* out) {
+  static_assert(N % 4 == 0, "whole code dwords");
+  if (sb != 0) {
+    const float x = __uint_as_float(sb << 23);
+#pragma unroll
+    for (int d = 0; d < N / 4; ++d) {
+      uint32_t v = 0;
+      v = quant_pair_bf16<0>(v, p[4 * d], x);
+      v = quant_pair_bf16<1>(v, p[4 * d + 1], x);
+      v = quant_pair_bf16<2>(v, p[4 * d + 2], x);
+      v = quant_pair_bf16<3>(v, p[4 * d + 3], x);
+      out[d] = v;
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < N / 4; ++d) {
+      uint32_t v = 0;
+      v = quant_pair_e8m0<0>(v, p[4 * d], 0u);
+      v = quant_pair_e8m0<1>(v, p[4 * d + 1], 0u);
+      v = quant_pair_e8m0<2>(v, p[4 * d + 2], 0u);
+      v = quant_pair_e8m0<3>(v, p[4 * d + 3], 0u);
+      out[d] = v;
+    }
+  }
+}
+
 // MXFP4 shared-exponent scale byte from the bf16 bit pattern of the block's
 // largest magnitude: floor(log2 amax) - 2 + 127, clamped at 0. For a bf16
 // amax with exponent field ef this is max(ef - 2, 0); zero and subnormal
