@@ -22,7 +22,7 @@
 //    aligned dword and s is the byte select (op_sel) of the instruction.
 //    Both operands use the same K order, so the sum is unchanged.
 //  * Global -> LDS with GLOBAL_LOAD_LDS_DWORDX4 (16 B per lane, no VGPR staging),
-//    issued by one wave per SIMD while its partner wave keeps issuing MFMAs,
+//    issued by every wave between its MFMAs of a stage's last K step,
 //    2 LDS slots of 68 KB: each copy brings whole 128-byte lines (8 rows x 128 B
 //    per wave instruction), which doubles the bytes per outstanding L1 miss
 //    compared with half-line copies. LDS rows are 128 B; chunk c of row r sits at
@@ -141,7 +141,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // wave -> (wn, wm): consecutive waves share a token block, so the token blocks
-  // of a partly filled tile are spread over the SIMDs (wave w runs on SIMD w % 4)
+  // of a partly filled tile are spread over the SIMDs (waves 0-3 run on four
+  // different SIMDs, and wave w + 4 on the SIMD of wave w)
   const int wn = wave & 1, wm = wave >> 1;
   // a wave whose 64 token rows are all past the tile's rows skips its MFMAs and
   // fragment reads (it still copies and meets every barrier)
