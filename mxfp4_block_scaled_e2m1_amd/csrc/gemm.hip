@@ -134,6 +134,101 @@ __device__ __forceinline__ void k_step(const Frags& cur, Frags& nxt, const uint8
   }
 }
 
+// One 32 x 32 block of the L1 epilogue, as this lane holds it: gate `ga` and up
+// `ua` are D[n][m] of token row ml within the tile and j = j0 + 8*(v/4) + 4*hh + v%4.
+// h = bf16(silu(g) * u) is re-quantised per 32 j (MXFP4: one E8M0 byte; NVFP4:
+// two E4M3 bytes per 16 j and the fp32 global scale) and stored with the codes.
+template <int EPI>
+__device__ __forceinline__ void l1_block(const GemmArgs& a, const Tile& t, const f32x16& ga, const f32x16& ua,
+                                         int j0, int ml, int hh) {
+  const int I = a.n_rows;
+  const bool valid = (ml < t.rows) && (j0 < I);
+  const int row = t.row0 + ml;
+  // h as bf16 pairs: hp[2q] = (v = 4q, 4q+1), hp[2q+1] = (4q+2, 4q+3)
+  uint32_t hp[8];
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) {
+    hp[v >> 1] = bf16x2_rne(silu_mul(ga[v], ua[v]), silu_mul(ga[v + 1], ua[v + 1]));
+  }
+  uint32_t bytes_lo, bytes_hi;   // this lane's 8 code bytes (positions 4q + 2hh + {0,1})
+  if constexpr (EPI == EPI_SWIGLU_MXFP4) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, amax2(hp[i]));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+    const uint32_t sbyte = mx_scale_from_amax_bits(am);
+    uint32_t w01[2];
+    quant_pairs_e8m0<8>(hp, sbyte, w01);
+    bytes_lo = w01[0];
+    bytes_hi = w01[1];
+    if (valid && hh == 0) {
+      // row-major [rows][I/32], or tile-major for the L2's copies: m-tile
+      // t.mt, L2 stage j0/256, tile row ml, byte (j0/32) % 8
+      const int64_t at = a.h_scales_packed
+                             ? ((int64_t)t.mt * ((I + BK - 1) / BK) + (j0 >> 8)) * SC_TILE_STAGE_BYTES +
+                                   ml * SC_BYTES + ((j0 >> 5) & 7)
+                             : (int64_t)row * (I >> 5) + (j0 >> 5);
+      a.h_scales[at] = (uint8_t)sbyte;
+    }
+  } else {
+    // NVFP4: 16-blocks j0..j0+15 (v = 0..7) and j0+16..j0+31 (v = 8..15).
+    const float gsc = a.nv_global;
+    const float t6 = 6.0f * gsc;
+    uint32_t w01[2];
+    uint32_t sbytes[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am = max(am, amax2(hp[blk * 4 + i]));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+      const uint32_t sbyte = e4m3_rne_satfinite(bf16_to_f32(am) / t6);
+      sbytes[blk] = sbyte;
+      const float d = e4m3_to_f32(sbyte) * gsc;
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t pr = hp[blk * 4 + i];
+        float v0 = bf16_to_f32(pr & 0xFFFFu), v1 = bf16_to_f32(pr >> 16);
+        if (sbyte == 0) {
+          v0 *= 0.0f;
+          v1 *= 0.0f;
+        } else {
+          v0 = fminf(fmaxf(v0 / d, -6.0f), 6.0f);
+          v1 = fminf(fmaxf(v1 / d, -6.0f), 6.0f);
+        }
+        if (i == 0) w = quant_pair_f32_unit<0>(w, v0, v1);
+        else if (i == 1) w = quant_pair_f32_unit<1>(w, v0, v1);
+        else if (i == 2) w = quant_pair_f32_unit<2>(w, v0, v1);
+        else w = quant_pair_f32_unit<3>(w, v0, v1);
+      }
+      w01[blk] = w;
+    }
+    bytes_lo = w01[0];
+    bytes_hi = w01[1];
+    if (valid && hh == 0) {
+      const uint16_t two = (uint16_t)(sbytes[0] | (sbytes[1] << 8));
+      *(uint16_t*)(a.h_scales + (int64_t)row * (I >> 4) + (j0 >> 4)) = two;
+    }
+  }
+  // Lane hh=0 holds byte positions {0,1,4,5,8,9,12,13} of the 16-byte block row,
+  // hh=1 holds {2,3,6,7,10,11,14,15}; bytes_lo = q0p0,q0p1,q1p0,q1p1, bytes_hi = q2.., q3...
+  // Exchange so that hh=0 writes bytes 0..7 and hh=1 writes 8..15.
+  const uint32_t send = hh ? bytes_lo : bytes_hi;
+  const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+  uint32_t o0, o1;
+  if (hh == 0) {
+    o0 = (bytes_lo & 0xFFFFu) | ((recv & 0xFFFFu) << 16);
+    o1 = (bytes_lo >> 16) | (recv & 0xFFFF0000u);
+  } else {
+    o0 = (recv & 0xFFFFu) | ((bytes_hi & 0xFFFFu) << 16);
+    o1 = (recv >> 16) | (bytes_hi & 0xFFFF0000u);
+  }
+  if (valid) {
+    *(uint2*)(a.h_codes + (int64_t)row * (I >> 1) + (j0 >> 1) + hh * 8) = make_uint2(o0, o1);
+  }
+}
+
 // One 256 x 256 output tile: K loop and epilogue. All LDS reads and copies of
 // the tile have completed when it returns.
 template <int EPI>
@@ -150,9 +245,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
   const int K = a.k;
   const int kb = K >> 1;                    // code bytes per row
   const int ks = K >> 5;                    // scale bytes per row
-  const int nst = (K + BK - 1) / BK;
-  const bool half_tail = (K % BK) != 0;     // the last stage holds 128 columns only
-  constexpr bool l1 = (EPI == EPI_SWIGLU_MXFP4 || EPI == EPI_SWIGLU_NVFP4);
+  const int nst_all = (K + BK - 1) / BK;
+  // this tile's K stages [ks0, ks1): all of them, or one split's share
+  const int nst = t.ks1 - t.ks0;
+  const int kc0 = t.ks0 * ROW_BYTES;        // code byte offset of the first stage
+  const bool half_tail = (K % BK) != 0 && t.ks1 == nst_all;   // the last stage holds 128 columns only
+  constexpr bool l1 = (EPI == EPI_SWIGLU_MXFP4 || EPI == EPI_SWIGLU_NVFP4 || EPI == EPI_PART_L1);
 
   const uint8_t* wa = a.wa + (int64_t)t.e * a.w_estride;
   const uint8_t* wa_s = a.wa_s + (int64_t)t.e * a.ws_estride;
@@ -191,7 +289,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     const int c = (lane & 7) ^ ((R >> 1) & 7);
     const uint8_t *base, *sbase;
     const int row = w_row(R, base, sbase);
-    wsrc[i] = base + (int64_t)row * kb + c * 16;
+    wsrc[i] = base + (int64_t)row * kb + kc0 + c * 16;
     whi[i] = c >= 4;
   }
   const uint8_t* xsrc[X_DMA];
@@ -200,7 +298,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
   for (int i = 0; i < X_DMA; ++i) {
     const int R = (wave * X_DMA + i) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((R >> 1) & 7);
-    xsrc[i] = a.x + (int64_t)x_token(R) * kb + c * 16;
+    xsrc[i] = a.x + (int64_t)x_token(R) * kb + kc0 + c * 16;
     xhi[i] = c >= 4;
   }
   // Scale tiles (8 bytes per row per stage): thread tid copies dword tid & 1 of
@@ -212,19 +310,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
   {
     const int tid = wave * 64 + lane;
     if (a.w_spk != nullptr) {
-      wssrc = a.w_spk + (int64_t)t.e * a.wspk_estride + (int64_t)t.nt * nst * SC_TILE_STAGE_BYTES + tid * 4;
+      wssrc = a.w_spk + (int64_t)t.e * a.wspk_estride + ((int64_t)t.nt * nst_all + t.ks0) * SC_TILE_STAGE_BYTES +
+              tid * 4;
       wsc_stride = SC_TILE_STAGE_BYTES;
     } else {
       const uint8_t *base, *sbase;
       const int row = w_row(tid >> 1, base, sbase);
-      wssrc = sbase + (int64_t)row * ks + (tid & 1) * 4;
+      wssrc = sbase + (int64_t)row * ks + t.ks0 * SC_BYTES + (tid & 1) * 4;
     }
     if (a.x_s_packed) {
       // rows past the tile's end read the last valid row, as the code copies do
-      xssrc = a.x_s + (int64_t)t.mt * nst * SC_TILE_STAGE_BYTES + min(tid >> 1, t.rows - 1) * SC_BYTES + (tid & 1) * 4;
+      xssrc = a.x_s + ((int64_t)t.mt * nst_all + t.ks0) * SC_TILE_STAGE_BYTES + min(tid >> 1, t.rows - 1) * SC_BYTES +
+              (tid & 1) * 4;
       xsc_stride = SC_TILE_STAGE_BYTES;
     } else {
-      xssrc = a.x_s + (int64_t)x_token(tid >> 1) * ks + (tid & 1) * 4;
+      xssrc = a.x_s + (int64_t)x_token(tid >> 1) * ks + t.ks0 * SC_BYTES + (tid & 1) * 4;
     }
   }
 
@@ -380,102 +480,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     }
   } else if constexpr (EPI == EPI_BF16) {
     store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, 1.0f, smem, GEMM_THREADS);
+  } else if constexpr (EPI == EPI_PART_L1) {
+    // split-K partial: the accumulators as this lane holds them, 64 contiguous
+    // bytes per lane and block (waves of all-padding token rows write nothing)
+    if (act) {
+      const int mtiles = (a.m_rows + BM - 1) / BM;
+      const int tiles = a.grid_tiles / a.k_splits;
+      float* pb = a.c_f32 + (((int64_t)t.sp * tiles + t.nt * mtiles + t.mt) * 8 + wave) * (8 * 64 * 16);
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) *(f32x16*)(pb + ((f * 2 + g) * 64 + lane) * 16) = acc[f][g];
+    }
   } else {
     // L1: gate in acc[f][g], up in acc[f + 2][g] for f = 0, 1.
-    const int I = a.n_rows;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       const int j0 = t.nt * L1_J_PER_TILE + wn * 64 + f * 32;   // 32-aligned block of j
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int ml = wm * 64 + g * 32 + r32;
-        const bool valid = (ml < t.rows) && (j0 < I);
-        const int row = t.row0 + ml;
-        // h as bf16 pairs: hp[2q] = (v = 4q, 4q+1), hp[2q+1] = (4q+2, 4q+3)
-        uint32_t hp[8];
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          hp[v >> 1] = bf16x2_rne(silu_mul(acc[f][g][v], acc[f + 2][g][v]),
-                                  silu_mul(acc[f][g][v + 1], acc[f + 2][g][v + 1]));
-        }
-        uint32_t bytes_lo, bytes_hi;   // this lane's 8 code bytes (positions 4q + 2hh + {0,1})
-        if constexpr (EPI == EPI_SWIGLU_MXFP4) {
-          uint32_t am = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) am = max(am, amax2(hp[i]));
-          am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-          const uint32_t sbyte = mx_scale_from_amax_bits(am);
-          uint32_t w01[2];
-          quant_pairs_e8m0<8>(hp, sbyte, w01);
-          bytes_lo = w01[0];
-          bytes_hi = w01[1];
-          if (valid && hh == 0) {
-            // row-major [rows][I/32], or tile-major for the L2's copies: m-tile
-            // t.mt, L2 stage j0/256, tile row ml, byte (j0/32) % 8
-            const int64_t at = a.h_scales_packed
-                                   ? ((int64_t)t.mt * ((I + BK - 1) / BK) + (j0 >> 8)) * SC_TILE_STAGE_BYTES +
-                                         ml * SC_BYTES + ((j0 >> 5) & 7)
-                                   : (int64_t)row * (I >> 5) + (j0 >> 5);
-            a.h_scales[at] = (uint8_t)sbyte;
-          }
-        } else {
-          // NVFP4: 16-blocks j0..j0+15 (v = 0..7) and j0+16..j0+31 (v = 8..15).
-          const float gsc = a.nv_global;
-          const float t6 = 6.0f * gsc;
-          uint32_t w01[2];
-          uint32_t sbytes[2];
-#pragma unroll
-          for (int blk = 0; blk < 2; ++blk) {
-            uint32_t am = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) am = max(am, amax2(hp[blk * 4 + i]));
-            am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-            const uint32_t sbyte = e4m3_rne_satfinite(bf16_to_f32(am) / t6);
-            sbytes[blk] = sbyte;
-            const float d = e4m3_to_f32(sbyte) * gsc;
-            uint32_t w = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t pr = hp[blk * 4 + i];
-              float v0 = bf16_to_f32(pr & 0xFFFFu), v1 = bf16_to_f32(pr >> 16);
-              if (sbyte == 0) {
-                v0 *= 0.0f;
-                v1 *= 0.0f;
-              } else {
-                v0 = fminf(fmaxf(v0 / d, -6.0f), 6.0f);
-                v1 = fminf(fmaxf(v1 / d, -6.0f), 6.0f);
-              }
-              if (i == 0) w = quant_pair_f32_unit<0>(w, v0, v1);
-              else if (i == 1) w = quant_pair_f32_unit<1>(w, v0, v1);
-              else if (i == 2) w = quant_pair_f32_unit<2>(w, v0, v1);
-              else w = quant_pair_f32_unit<3>(w, v0, v1);
-            }
-            w01[blk] = w;
-          }
-          bytes_lo = w01[0];
-          bytes_hi = w01[1];
-          if (valid && hh == 0) {
-            const uint16_t two = (uint16_t)(sbytes[0] | (sbytes[1] << 8));
-            *(uint16_t*)(a.h_scales + (int64_t)row * (I >> 4) + (j0 >> 4)) = two;
-          }
-        }
-        // Lane hh=0 holds byte positions {0,1,4,5,8,9,12,13} of the 16-byte block row,
-        // hh=1 holds {2,3,6,7,10,11,14,15}; bytes_lo = q0p0,q0p1,q1p0,q1p1, bytes_hi = q2.., q3...
-        // Exchange so that hh=0 writes bytes 0..7 and hh=1 writes 8..15.
-        const uint32_t send = hh ? bytes_lo : bytes_hi;
-        const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
-        uint32_t o0, o1;
-        if (hh == 0) {
-          o0 = (bytes_lo & 0xFFFFu) | ((recv & 0xFFFFu) << 16);
-          o1 = (bytes_lo >> 16) | (recv & 0xFFFF0000u);
-        } else {
-          o0 = (recv & 0xFFFFu) | ((bytes_hi & 0xFFFFu) << 16);
-          o1 = (recv >> 16) | (bytes_hi & 0xFFFF0000u);
-        }
-        if (valid) {
-          *(uint2*)(a.h_codes + (int64_t)row * (I >> 1) + (j0 >> 1) + hh * 8) = make_uint2(o0, o1);
-        }
-      }
+      for (int g = 0; g < 2; ++g) l1_block<EPI>(a, t, acc[f][g], acc[f + 2][g], j0, wm * 64 + g * 32 + r32, hh);
     }
   }
 }
@@ -503,7 +526,76 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm(const GemmArgs a) {
   }
 }
 
+// Split-K sum of L1. One 64-thread block per (tile, wave, gate block (f, g)
+// with f < 2) of the GEMM's layout: each lane adds the k_splits partials of its
+// 16 gate and 16 up accumulators in split order (fixed, so the result does not
+// depend on timing), then runs the epilogue the unsplit GEMM runs on its registers.
+__device__ __forceinline__ Tile part_tile(const GemmArgs& a, int tix) {
+  const int mtiles = (a.m_rows + BM - 1) / BM;
+  Tile t;
+  t.e = 0;
+  t.nt = tix / mtiles;
+  t.mt = tix - t.nt * mtiles;
+  t.row0 = t.mt * BM;
+  t.rows = min(BM, a.m_rows - t.row0);
+  t.sp = 0;
+  t.ks0 = t.ks1 = 0;
+  return t;
+}
+
+// Sum of blocks blk0 and blk1 over the splits. The loads of four splits are
+// issued before their additions, which stay in split order.
+__device__ __forceinline__ void part_sum2(const GemmArgs& a, int tix, int wave, int blk0, int blk1, int lane,
+                                          f32x16& s0, f32x16& s1) {
+  const int tiles = a.grid_tiles / a.k_splits;
+  const int64_t split_stride = (int64_t)tiles * PART_TILE_FLOATS;
+  const float* p = a.c_f32 + ((int64_t)tix * 8 + wave) * (8 * 64 * 16) + lane * 16;
+  const float* p0 = p + blk0 * 64 * 16;
+  const float* p1 = p + blk1 * 64 * 16;
+  s0 = f32x16{};
+  s1 = f32x16{};
+  int sp = 0;
+  for (; sp + 4 <= a.k_splits; sp += 4) {
+    f32x16 u0[4], u1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u0[i] = *(const f32x16*)(p0 + (sp + i) * split_stride);
+      u1[i] = *(const f32x16*)(p1 + (sp + i) * split_stride);
+    }
+    asm volatile("" ::: "memory");   // all eight loads in flight before the first addition
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s0 += u0[i];
+      s1 += u1[i];
+    }
+  }
+  for (; sp < a.k_splits; ++sp) {
+    s0 += *(const f32x16*)(p0 + sp * split_stride);
+    s1 += *(const f32x16*)(p1 + sp * split_stride);
+  }
+}
+
+// L1: blocks (f, g) with f < 2; gate in block (f, g), up in (f + 2, g).
+__global__ __launch_bounds__(64) void k_part_l1(const GemmArgs a) {
+  const int lane = threadIdx.x;
+  const int fg = blockIdx.x & 3, wave = (blockIdx.x >> 2) & 7, tix = blockIdx.x >> 5;
+  const int f = fg >> 1, g = fg & 1, wn = wave & 1, wm = wave >> 1;
+  const Tile t = part_tile(a, tix);
+  if (wm * 64 + g * 32 >= t.rows) return;   // token rows all padding: no partials were written
+  f32x16 ga, ua;
+  part_sum2(a, tix, wave, f * 2 + g, (f + 2) * 2 + g, lane, ga, ua);
+  l1_block<EPI_SWIGLU_MXFP4>(a, t, ga, ua, t.nt * L1_J_PER_TILE + wn * 64 + f * 32, wm * 64 + g * 32 + (lane & 31),
+                             lane >> 5);
+}
+
 }  // namespace
+
+hipError_t launch_part_l1(const GemmArgs& a, hipStream_t s) {
+  const int tiles = a.grid_tiles / a.k_splits;
+  if (tiles <= 0) return hipSuccess;
+  k_part_l1<<<tiles * 8 * 4, 64, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 // Compute units of the current device (cached per device).
 int cu_count() {
@@ -528,6 +620,7 @@ hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int max_tiles, hipStream
     case EPI_SWIGLU_MXFP4: k_gemm<EPI_SWIGLU_MXFP4><<<g8, GEMM_THREADS, 0, s>>>(a); break;
     case EPI_SWIGLU_NVFP4: k_gemm<EPI_SWIGLU_NVFP4><<<g8, GEMM_THREADS, 0, s>>>(a); break;
     case EPI_BF16: k_gemm<EPI_BF16><<<g8, GEMM_THREADS, 0, s>>>(a); break;
+    case EPI_PART_L1: k_gemm<EPI_PART_L1><<<g8, GEMM_THREADS, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -13,6 +13,8 @@ struct Tile {
   int row0;      // first row (sorted order) of the token tile
   int rows;      // valid rows in the token tile
   int mt;        // m-tile index within the launch (tile-major scale layouts)
+  int sp;        // K split of a split-K launch (0 otherwise)
+  int ks0, ks1;  // the split's K stages [ks0, ks1) of 256 columns
 };
 
 // Routed launches keep the expert offsets and m-tile bases (E+1 each) in LDS:
@@ -45,8 +47,21 @@ static __device__ __forceinline__ int tile_count(const GemmArgs& a, const TileTa
 // m-tile fastest, so consecutive tiles share their weight rows.
 static __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const TileTables& tt, int L) {
   Tile t;
+  const int nst = (a.k + BK - 1) / BK;
+  t.sp = 0;
+  t.ks0 = 0;
+  t.ks1 = nst;
   if (a.expert_off == nullptr) {
     const int mtiles = (a.m_rows + BM - 1) / BM;
+    if (a.k_splits > 1) {
+      // split-K: tile L + sp * (tiles of one split) covers stages
+      // [sp * nst / S, (sp + 1) * nst / S)
+      const int per_split = a.grid_tiles / a.k_splits;
+      t.sp = L / per_split;
+      L -= t.sp * per_split;
+      t.ks0 = t.sp * nst / a.k_splits;
+      t.ks1 = (t.sp + 1) * nst / a.k_splits;
+    }
     t.e = 0;
     t.nt = L / mtiles;
     const int mt = L - t.nt * mtiles;

@@ -30,7 +30,12 @@ enum Epilogue : int {
   EPI_SWIGLU_MXFP4 = 1, // L1: h = bf16(silu(g) * u) -> MXFP4 codes + E8M0 per 32 j
   EPI_SWIGLU_NVFP4 = 2, // L1: h -> NVFP4 codes + E4M3 per 16 j (fp32 global)
   EPI_BF16 = 3,         // L2: y[m][n] = bf16(acc) (dense) or o[slot][n] = bf16(w * acc) (grouped)
+  EPI_PART_L1 = 4,      // split-K partial of L1 (gate/up rows): fp32 accumulators as the lanes hold them
 };
+
+// Split-K partial layout: per split, tile (nt * m-tiles + mt), wave, 32 x 32
+// block (f * 2 + g) and lane, the lane's 16 fp32 accumulators (64 bytes).
+constexpr int64_t PART_TILE_FLOATS = 8 * 8 * 64 * 16;   // 256 KB per tile and split
 
 struct GemmArgs {
   // MFMA A operand: weight rows (MXFP4). For L1 `wa` is w1 (gate) and `wb`
@@ -61,10 +66,11 @@ struct GemmArgs {
   int n_experts;
   int m_rows;                 // dense mode rows
   int n_tiles;                // tiles along the weight rows
-  int grid_tiles;             // dense: exact count of tiles
+  int grid_tiles;             // dense: exact count of tiles (times k_splits)
+  int k_splits;               // dense: K splits (0 or 1: none); EPI_PART_L1: c_f32 holds the partials
 
   // Outputs.
-  float* c_f32;               // EPI_F32: [m_rows, n_rows]
+  float* c_f32;               // EPI_F32: [m_rows, n_rows]; EPI_PART_L1: split-K partials
   uint8_t* h_codes;           // L1: [rows, n_rows/2]
   uint8_t* h_scales;          // L1: [rows, n_rows/32] (MXFP4) or [rows, n_rows/16] (NVFP4)
   int h_scales_packed;        // L1 MXFP4: h_scales tile-major over the m-tiles (the L2's x_s)
@@ -82,6 +88,11 @@ hipError_t launch_gemm(Epilogue epi, const GemmArgs& a, int max_tiles, hipStream
 // scales per 16 columns, nv_global the fp32 global scale; bf16 matrix cores on
 // exactly dequantised operands, output as EPI_BF16 times nv_global.
 hipError_t launch_gemm_nv_l2(const GemmArgs& a, int max_tiles, hipStream_t s);
+
+// Split-K sum of a dense L1 launch `a` (its k_splits partials in a.c_f32),
+// followed by the SiLU * up and MXFP4 re-quantisation epilogue (a.h_codes,
+// a.h_scales, tile-major when a.h_scales_packed).
+hipError_t launch_part_l1(const GemmArgs& a, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int cu_count();

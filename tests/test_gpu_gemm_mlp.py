@@ -31,14 +31,16 @@ def _align(n):
 def _ws_slices(mx, ws, M, H, I):
     """Dense workspace layout of mx_expert_mlp, each region 256-byte aligned:
     few tokens: h (bf16 SiLU output); weight-streaming path (9..96 tokens): xq,
-    xs, hq, hs (row-major), h; GEMM path: xq, xs, hq, hs (tile-major), xs_pk.
+    xs, hq, hs (row-major), h; GEMM path: xq, xs, hq, hs (tile-major), xs_pk,
+    and split-K partials when a GEMM is split.
     Returns (xq, xs, hq, hs) with hs row-major [M, I/32], or (h,)."""
     if M <= DECODE_MAX_TOKENS:
         return [ws[:M * I * 2]]
     mt = (M + 255) // 256
-    gemm = [M * H // 2, M * H // 32, M * I // 2, packed_scale_bytes(mt, I), packed_scale_bytes(mt, H)]
-    tile_major = sum(_align(n) for n in gemm) == mx.expert_mlp_workspace_size(M, H, I)
-    sizes = gemm[:4] if tile_major else [M * H // 2, M * H // 32, M * I // 2, M * I // 32]
+    skinny = [M * H // 2, M * H // 32, M * I // 2, M * I // 32, M * I * 2]
+    tile_major = sum(_align(n) for n in skinny) != mx.expert_mlp_workspace_size(M, H, I)
+    gemm = [M * H // 2, M * H // 32, M * I // 2, packed_scale_bytes(mt, I)]
+    sizes = gemm if tile_major else skinny[:4]
     off, out = 0, []
     for n in sizes:
         out.append(ws[off:off + n])
@@ -136,6 +138,21 @@ def test_shared_expert_real_shape(mx, M):
     else:
         _, _, hq, hs = sl
         assert_requant_close(hq.cpu().numpy().reshape(M, 1536), _np(hs).reshape(M, 96), inter["hq"], inter["hs"])
+    assert_mlp_close(y, ref)
+
+
+@pytest.mark.parametrize("M,H,I", [(130, 2176, 384), (200, 4224, 256), (256, 7168, 3072), (257, 7168, 3072)])
+def test_shared_expert_split_k(mx, M, H, I):
+    """A dense L1 of one m-tile splits K over several workgroups (fp32 partials
+    summed in split order, then the usual epilogue): 2 splits of 8.5 stages
+    (H = 2176) and 4 of 16.5 (H = 4224), each ending in a half-width stage, and
+    7 splits over a full m-tile at the real shape. M = 257 (two m-tiles, the
+    second of one row) takes the unsplit path next to it."""
+    d = W.shared_expert(M, seed=4, hidden=H, inter=I)
+    y, sl = _run_dense(mx, d, M, H, I)
+    ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
+    _, _, hq, hs = sl
+    assert_requant_close(hq.cpu().numpy().reshape(M, I // 2), _np(hs).reshape(M, I // 32), inter["hq"], inter["hs"])
     assert_mlp_close(y, ref)
 
 
