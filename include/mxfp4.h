@@ -189,6 +189,35 @@ MX_API mx_status mx_pack_weight_scales(const uint8_t* w1_s, const uint8_t* w3_s,
 MX_API size_t mx_packed_weight_scales_size(int64_t hidden, int64_t inter, int32_t E);
 
 /*
+ * mx_nvfp4_global_warmup -- the fp32 global scale g of the NVFP4 re-quantisation
+ * of h, from a warm-up batch, computed on the device: g = f32(max |h| / (6 * 448))
+ * over every (token, expert) pair of the batch, or 1 when h is all zero. h is
+ * bf16(silu(x . w1^T) * (x . w3^T)) as the MLP computes it (x quantised to
+ * MXFP4, the FP4 L1 GEMM, the same SiLU and rounding), so the largest |h| maps
+ * onto the largest E2M1 value (6) times the largest E4M3 scale (448). The pages'
+ * runner plans a global scale taken from a warm-up pass, computed once before
+ * serving (page "Current Bug: vLLM produces empty/garbage output", section
+ * "Revised Plan", Phase 1); the mapping is the plain reading of that plan.
+ *   topk_ids == NULL: one expert (the shared expert), T token rows; k must be 0
+ *     and topk_w, E are ignored (packed_scales then holds one expert).
+ *   otherwise: routed exactly as mx_grouped_expert_mlp (topk_ids, topk_w, k, E).
+ *   w1, w3 (and scales) as for mx_expert_mlp / mx_grouped_expert_mlp; w2 is not read.
+ *   global_out: one fp32 in device memory, written by the call in stream order
+ *     (read it back once, then pass it as requant_global).
+ * workspace: mx_nvfp4_global_warmup_workspace_size(T, hidden, inter, k, E) bytes
+ * (k = 0 for one expert), 256-byte aligned; contents are scratch.
+ * Alignment as for the MLP entry points; global_out 4 bytes.
+ */
+MX_API mx_status mx_nvfp4_global_warmup(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
+                                        const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
+                                        const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
+                                        const uint8_t* w3_s, const uint8_t* packed_scales, float* global_out,
+                                        void* workspace, size_t ws_bytes, void* stream);
+
+MX_API size_t mx_nvfp4_global_warmup_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k,
+                                                    int32_t E);
+
+/*
  * mx_debug_gemm_f32 -- test hook, not part of the hot path: C[M, N] = A . B^T in fp32
  * for MXFP4 A (codes [M, K/2], scales [M, K/32]) and B (codes [N, K/2], scales
  * [N, K/32]) through the same scaled-MFMA kernel as the MLP. K % 128 == 0,

@@ -33,6 +33,9 @@ SIGNATURES = {
     "mx_dequant": (_I32, [_I32, _P, _P, _F, _I64, _I64, _P, _P]),
     "mx_quantize_act": (_I32, [_I32, _P, _I64, _I64, _F, _P, _P, _P]),
     "mx_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _F, _P, _P, _SZ, _P]),
+    "mx_nvfp4_global_warmup": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                      _P]),
+    "mx_nvfp4_global_warmup_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "mx_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "mx_grouped_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                      _P, _I32, _F, _P, _P, _SZ, _P]),
@@ -181,6 +184,26 @@ def grouped_expert_mlp(x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="
                                        _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2), _ptr(w2s),
                                        _ptr(packed_scales), _fmt(requant), float(requant_global), _ptr(out),
                                        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def nvfp4_global_warmup(x, w1, w1s, w3, w3s, topk_ids=None, topk_w=None, packed_scales=None, out=None,
+                        workspace=None, stream=None):
+    """mx_nvfp4_global_warmup: g = f32(max |h| / (6 * 448)) of a warm-up batch, as a
+    one-element fp32 device tensor. One expert (w1 [inter, hidden/2]) when
+    topk_ids is None, else routed over stacked weights [E, ...]."""
+    T, hidden = x.shape
+    routed = topk_ids is not None
+    inter = w1.shape[-2]
+    k = topk_ids.shape[1] if routed else 0
+    E = w1.shape[0] if routed else 1
+    if out is None:
+        out = torch.empty((1,), dtype=torch.float32, device=x.device)
+    nbytes = int(lib().mx_nvfp4_global_warmup_workspace_size(T, hidden, inter, k, E))
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib().mx_nvfp4_global_warmup(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
+                                        _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(packed_scales), _ptr(out),
+                                        _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

@@ -227,6 +227,21 @@ __global__ __launch_bounds__(EW_THREADS) void k_quant_nvfp4(const uint4* __restr
   }
 }
 
+// NVFP4 warm-up: the running max of |h| (bf16 magnitude bits, so that an
+// unsigned max orders them as values) starts at zero ...
+__global__ void k_amax_clear(uint32_t* amax) {
+  if (threadIdx.x == 0) *amax = 0u;
+}
+
+// ... and becomes g = f32(max |h| / (6 * 448)) (IEEE fp32 division), or 1 when
+// h is all zero.
+__global__ void k_nvfp4_global(const uint32_t* amax, float* g) {
+  if (threadIdx.x == 0) {
+    const uint32_t a = *amax;
+    *g = a != 0u ? bf16_to_f32(a) / (6.0f * 448.0f) : 1.0f;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows,
@@ -266,6 +281,16 @@ hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uin
   const int64_t units = rows * (cols / 8);
   if (units == 0) return hipSuccess;
   k_quant_mxfp4<<<ew_grid_units(units), EW_THREADS, 0, s>>>((const uint4*)x, (uint32_t*)codes, scales, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_clear(uint32_t* amax, hipStream_t s) {
+  k_amax_clear<<<1, 64, 0, s>>>(amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_global(const uint32_t* amax, float* g, hipStream_t s) {
+  k_nvfp4_global<<<1, 64, 0, s>>>(amax, g);
   return hipGetLastError();
 }
 

@@ -138,9 +138,10 @@ __device__ __forceinline__ void k_step(const Frags& cur, Frags& nxt, const uint8
 // `ua` are D[n][m] of token row ml within the tile and j = j0 + 8*(v/4) + 4*hh + v%4.
 // h = bf16(silu(g) * u) is re-quantised per 32 j (MXFP4: one E8M0 byte; NVFP4:
 // two E4M3 bytes per 16 j and the fp32 global scale) and stored with the codes.
+// Returns (MXFP4) the max |h| of the block row as bf16 bits, 0 for padding rows.
 template <int EPI>
-__device__ __forceinline__ void l1_block(const GemmArgs& a, const Tile& t, const f32x16& ga, const f32x16& ua,
-                                         int j0, int ml, int hh) {
+__device__ __forceinline__ uint32_t l1_block(const GemmArgs& a, const Tile& t, const f32x16& ga, const f32x16& ua,
+                                             int j0, int ml, int hh) {
   const int I = a.n_rows;
   const bool valid = (ml < t.rows) && (j0 < I);
   const int row = t.row0 + ml;
@@ -151,12 +152,14 @@ __device__ __forceinline__ void l1_block(const GemmArgs& a, const Tile& t, const
     hp[v >> 1] = bf16x2_rne(silu_mul(ga[v], ua[v]), silu_mul(ga[v + 1], ua[v + 1]));
   }
   uint32_t bytes_lo, bytes_hi;   // this lane's 8 code bytes (positions 4q + 2hh + {0,1})
+  uint32_t block_amax = 0;
   if constexpr (EPI == EPI_SWIGLU_MXFP4) {
     uint32_t am = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) am = max(am, amax2(hp[i]));
     am = max(am, (uint32_t)__shfl_xor((int)am, 32));
     const uint32_t sbyte = mx_scale_from_amax_bits(am);
+    block_amax = valid ? am : 0u;
     uint32_t w01[2];
     quant_pairs_e8m0<8>(hp, sbyte, w01);
     bytes_lo = w01[0];
@@ -227,6 +230,14 @@ __device__ __forceinline__ void l1_block(const GemmArgs& a, const Tile& t, const
   if (valid) {
     *(uint2*)(a.h_codes + (int64_t)row * (I >> 1) + (j0 >> 1) + hh * 8) = make_uint2(o0, o1);
   }
+  return block_amax;
+}
+
+// NVFP4 warm-up: fold this wave's max |h| into *amax (one atomic per wave).
+__device__ __forceinline__ void wave_amax_atomic(uint32_t* amax, uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax, v);
 }
 
 // One 256 x 256 output tile: K loop and epilogue. All LDS reads and copies of
@@ -494,12 +505,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     }
   } else {
     // L1: gate in acc[f][g], up in acc[f + 2][g] for f = 0, 1.
+    uint32_t amax = 0;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       const int j0 = t.nt * L1_J_PER_TILE + wn * 64 + f * 32;   // 32-aligned block of j
 #pragma unroll
-      for (int g = 0; g < 2; ++g) l1_block<EPI>(a, t, acc[f][g], acc[f + 2][g], j0, wm * 64 + g * 32 + r32, hh);
+      for (int g = 0; g < 2; ++g)
+        amax = max(amax, l1_block<EPI>(a, t, acc[f][g], acc[f + 2][g], j0, wm * 64 + g * 32 + r32, hh));
     }
+    if (a.h_amax != nullptr) wave_amax_atomic(a.h_amax, amax);
   }
 }
 
@@ -584,8 +598,9 @@ __global__ __launch_bounds__(64) void k_part_l1(const GemmArgs a) {
   if (wm * 64 + g * 32 >= t.rows) return;   // token rows all padding: no partials were written
   f32x16 ga, ua;
   part_sum2(a, tix, wave, f * 2 + g, (f + 2) * 2 + g, lane, ga, ua);
-  l1_block<EPI_SWIGLU_MXFP4>(a, t, ga, ua, t.nt * L1_J_PER_TILE + wn * 64 + f * 32, wm * 64 + g * 32 + (lane & 31),
-                             lane >> 5);
+  const uint32_t amax = l1_block<EPI_SWIGLU_MXFP4>(a, t, ga, ua, t.nt * L1_J_PER_TILE + wn * 64 + f * 32,
+                                                   wm * 64 + g * 32 + (lane & 31), lane >> 5);
+  if (a.h_amax != nullptr) wave_amax_atomic(a.h_amax, amax);
 }
 
 }  // namespace

@@ -595,6 +595,130 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// NVFP4 warm-up workspace: the L1 inputs and outputs of the MXFP4 path (no L2
+// rows), then the |h| max word. k == 0: one expert, T token rows.
+struct WarmWs {
+  uint8_t *xq, *xs, *hq, *hs, *xs_pk;
+  RouteBuffers rb;
+  uint32_t* amax;
+  size_t bytes;
+};
+WarmWs warm_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E) {
+  Carve c(base);
+  WarmWs w;
+  memset(&w, 0, sizeof(w));
+  const bool routed = k > 0;
+  const int64_t P = routed ? T * k : T;
+  const int64_t mtiles = routed ? max_route_mtiles(P, E) : (T + BM - 1) / BM;
+  w.xq = (uint8_t*)c.take((size_t)(T * H / 2));
+  w.xs = (uint8_t*)c.take((size_t)(T * H / 32));
+  if (routed) {
+    const int64_t nblocks = (P + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+    w.rb.block_counts = (int32_t*)c.take((size_t)(nblocks * E * 4));
+    w.rb.expert_off = (int32_t*)c.take((size_t)(E + 1) * 4);
+    w.rb.tile_base = (int32_t*)c.take((size_t)(E + 1) * 4);
+    w.rb.row_token = (int32_t*)c.take((size_t)P * 4);
+    w.rb.row_slot = (int32_t*)c.take((size_t)P * 4);
+    w.rb.row_weight = (float*)c.take((size_t)P * 4);
+  }
+  w.hq = (uint8_t*)c.take((size_t)(P * I / 2));
+  w.hs = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, I));
+  w.xs_pk = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, H));
+  w.amax = (uint32_t*)c.take(4);
+  w.bytes = c.off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mx_nvfp4_global_warmup_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k, int32_t E) {
+  if (T < 0 || hidden < 0 || inter < 0 || k < 0 || (k > 0 && E < 1)) return 0;
+  return warm_ws(nullptr, T, hidden, inter, k, E).bytes;
+}
+
+mx_status mx_nvfp4_global_warmup(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
+                                 const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
+                                 const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
+                                 const uint8_t* packed_scales, float* global_out, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MX_TRY(check_mlp_dims(T, hidden, inter));
+  const bool routed = topk_ids != nullptr;
+  if (routed) {
+    if (E < 1 || E > ROUTE_MAX_EXPERTS) return fail(MX_ERR_SHAPE, "E %d outside [1, %d]", E, ROUTE_MAX_EXPERTS);
+    if (k < 1 || k > E) return fail(MX_ERR_SHAPE, "k %d outside [1, E=%d]", k, E);
+    if (T * (int64_t)k > ((int64_t)1 << 30)) return fail(MX_ERR_SHAPE, "T*k above 2^30");
+    MX_REQUIRE_PTR(topk_w);
+    MX_REQUIRE_ALIGN(topk_ids, 4);
+    MX_REQUIRE_ALIGN(topk_w, 4);
+  } else if (k != 0) {
+    return fail(MX_ERR_SHAPE, "k %d: without topk_ids (one expert) k must be 0", k);
+  }
+  MX_REQUIRE_PTR(global_out);
+  MX_REQUIRE_ALIGN(global_out, 4);
+  MX_REQUIRE_PTR(w1);
+  MX_REQUIRE_PTR(w1_s);
+  MX_REQUIRE_PTR(w3);
+  MX_REQUIRE_PTR(w3_s);
+  MX_REQUIRE_ALIGN(w1, 16);
+  MX_REQUIRE_ALIGN(w3, 16);
+  MX_REQUIRE_ALIGN(w1_s, 4);
+  MX_REQUIRE_ALIGN(w3_s, 4);
+  MX_REQUIRE_ALIGN(packed_scales, 256);
+  if (T > 0) {
+    MX_REQUIRE_PTR(x);
+    MX_REQUIRE_ALIGN(x, 16);
+  }
+  const size_t need = mx_nvfp4_global_warmup_workspace_size(T, hidden, inter, routed ? k : 0, routed ? E : 1);
+  MX_REQUIRE_PTR(workspace);
+  MX_REQUIRE_ALIGN(workspace, 256);
+  if (ws_bytes < need)
+    return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  const int ne = routed ? E : 1;
+  WarmWs w = warm_ws(workspace, T, hidden, inter, routed ? k : 0, ne);
+  const int H = (int)hidden, I = (int)inter;
+  MX_HIP(launch_amax_clear(w.amax, s), "amax_clear");
+  if (T > 0) {
+    const int64_t P = routed ? T * k : T;
+    const int mtiles = routed ? (int)max_route_mtiles(P, ne) : (int)((T + BM - 1) / BM);
+    MX_HIP(launch_quant_mxfp4(x, T, hidden, w.xq, w.xs, s), "quant_x");
+    if (routed) {
+      MX_HIP(launch_route(topk_ids, topk_w, T, k, E, w.rb, s), "route");
+      MX_HIP(launch_pack_act_scales(w.xs, H, w.rb.row_token, w.rb.expert_off, w.rb.tile_base, E, 0, mtiles, w.xs_pk,
+                                    s), "pack_act_scales");
+    } else {
+      MX_HIP(launch_pack_act_scales(w.xs, H, nullptr, nullptr, nullptr, 1, (int)T, mtiles, w.xs_pk, s),
+             "pack_act_scales");
+    }
+    const PackedWeights pw = packed_weights(hidden, inter, ne);
+    GemmArgs l1 = base_args();
+    l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
+    l1.w_estride = (int64_t)I * H / 2; l1.ws_estride = (int64_t)I * H / 32;
+    l1.w_spk = packed_scales; l1.wspk_estride = pw.l1_estride;
+    l1.n_rows = I; l1.k = H;
+    l1.x = w.xq; l1.x_s = w.xs_pk; l1.x_s_packed = 1;
+    l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
+    l1.h_codes = w.hq; l1.h_scales = w.hs; l1.h_scales_packed = 1;
+    l1.h_amax = w.amax;
+    if (routed) {
+      l1.row_token = w.rb.row_token;
+      l1.expert_off = w.rb.expert_off; l1.tile_base = w.rb.tile_base; l1.n_experts = E;
+    } else {
+      l1.m_rows = (int)T; l1.n_experts = 1;
+      l1.grid_tiles = mtiles * l1.n_tiles;
+    }
+    MX_HIP(launch_gemm(EPI_SWIGLU_MXFP4, l1, mtiles * l1.n_tiles, s), "l1_gemm");
+  }
+  MX_HIP(launch_nvfp4_global(w.amax, global_out, s), "nvfp4_global");
+  return ok();
+}
+
 mx_status mx_debug_gemm_f32(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
                             int64_t M, int64_t N, int64_t K, float* c, void* stream) {
   hipStream_t s = (hipStream_t)stream;

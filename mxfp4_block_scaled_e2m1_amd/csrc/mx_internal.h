@@ -75,6 +75,7 @@ struct GemmArgs {
   uint8_t* h_scales;          // L1: [rows, n_rows/32] (MXFP4) or [rows, n_rows/16] (NVFP4)
   int h_scales_packed;        // L1 MXFP4: h_scales tile-major over the m-tiles (the L2's x_s)
   float nv_global;            // L1 NVFP4 global scale
+  uint32_t* h_amax;           // L1 MXFP4, optional: running max of |h| (bf16 bits) over the valid rows
   uint16_t* out_bf16;         // EPI_BF16: dense y [m_rows, n_rows]; grouped o [slots, n_rows]
   const int32_t* row_slot;    // grouped L2: sorted row -> slot (t*k + j)
   const float* row_weight;    // grouped L2: gate weight of each sorted row
@@ -119,6 +120,9 @@ hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uin
                               uint8_t* scales, hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, float global,
                               uint8_t* codes, uint8_t* scales, hipStream_t s);
+// NVFP4 warm-up: clear the |h| max word; turn it into g = f32(max / (6 * 448)).
+hipError_t launch_amax_clear(uint32_t* amax, hipStream_t s);
+hipError_t launch_nvfp4_global(const uint32_t* amax, float* g, hipStream_t s);
 
 // ---- Routing ----------------------------------------------------------------
 constexpr int ROUTE_CHUNK = 1024;    // pairs per counting/scatter block

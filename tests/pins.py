@@ -442,6 +442,36 @@ def check_nvfp4_grid(O, seed=19):
     assert np.array_equal(nib, want)
 
 
+def _f32_nearest(q):
+    """The fp32 number nearest to the rational q > 0 (ties to the even
+    significand), by exact comparison with Fractions."""
+    v = np.float32(float(q))
+    best = None
+    for c in (np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))):
+        key = (abs(Fraction(float(c)) - q), int(np.array([c]).view(np.uint32)[0]) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def check_nvfp4_warmup_global(O):
+    """Warm-up global g = f32(max |h| / (6 * 448)): against the exact quotient
+    rounded once to fp32, for every positive finite bf16 value as the maximum
+    (signs and smaller entries must not matter), and g = 1 for all-zero h. The
+    same values also equal an fp32 IEEE division of the bf16 value by 2688, the
+    one-rounding form a device computes."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    for i in range(0, len(bits), 97):                   # a spread of maxima, exact
+        b = int(bits[i])
+        h = np.array([[b | 0x8000, b >> 1, 0, 0x8000]], np.uint16)   # -a, a smaller value, +0, -0
+        assert O.nvfp4_warmup_global(h) == _f32_nearest(Fraction(float(vals[i])) / 2688), hex(b)
+    ones = np.array([O.nvfp4_warmup_global(np.array([[b]], np.uint16)) for b in bits], np.float32)
+    assert np.array_equal(ones, vals / np.float32(2688.0))
+    assert O.nvfp4_warmup_global(np.zeros((3, 16), np.uint16)) == np.float32(1.0)
+    assert O.nvfp4_warmup_global(np.full((2, 16), 0x8000, np.uint16)) == np.float32(1.0)
+
+
 def check_nvfp4_error_bound(O, seed=23):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((64, 256)).astype(np.float32) * np.float32(3.0)

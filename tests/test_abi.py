@@ -122,6 +122,25 @@ def test_grouped_validation(L):
     assert b > a and c > a
 
 
+def test_nvfp4_global_warmup_validation(L):
+    P = ctypes.c_void_p
+    z = [P(256)] * 4
+
+    def call(ids, k, E, g, ws):
+        return L.mx_nvfp4_global_warmup(P(256), 8, 256, 128, ids, P(256), k, E, *z, None, g, P(256), ws, None)
+    need_dense = L.mx_nvfp4_global_warmup_workspace_size(8, 256, 128, 0, 1)
+    need_routed = L.mx_nvfp4_global_warmup_workspace_size(8, 256, 128, 2, 4)
+    assert 0 < need_dense < need_routed
+    assert call(None, 2, 4, P(256), 1 << 30) == 2           # one expert takes k = 0
+    assert call(P(256), 0, 4, P(256), 1 << 30) == 2         # routed: 1 <= k <= E
+    assert call(P(256), 5, 4, P(256), 1 << 30) == 2
+    assert call(None, 0, 1, None, 1 << 30) == 1             # no output word
+    assert call(None, 0, 1, P(258), 1 << 30) == 3           # misaligned output word
+    assert call(None, 0, 1, P(256), need_dense - 1) == 5
+    assert call(P(256), 2, 4, P(256), need_routed - 1) == 5
+    assert "workspace" in _err(L)
+
+
 def test_debug_gemm_validation(L):
     P = ctypes.c_void_p
     assert L.mx_debug_gemm_f32(P(256), P(256), P(256), P(256), 4, 6, 256, P(256), None) == 2

@@ -100,6 +100,50 @@ def test_nvfp4_global_scale_is_linear(mx):
     assert np.array_equal(y1, y2)
 
 
+def _device_warmup(mx, d, routed):
+    args = (bf16_t(d["x"]), t(d["w1"]), t(d["w1s"]), t(d["w3"]), t(d["w3s"]))
+    if routed:
+        g = mx.nvfp4_global_warmup(*args, topk_ids=t(d["ids"]), topk_w=t(d["w"]))
+    else:
+        g = mx.nvfp4_global_warmup(*args)
+    torch.cuda.synchronize()
+    return float(g.cpu().numpy()[0])
+
+
+def _assert_same_global(g_dev, g_ref):
+    """The device takes max |h| over its own bf16 h, which can differ from the
+    oracle's by one bf16 step where a value sits at a rounding boundary; g then
+    differs by that step. Otherwise it is the same fp32 number."""
+    assert g_dev == g_ref or abs(g_dev - g_ref) <= g_ref * 2.0 ** -7, (g_dev, g_ref)
+
+
+@pytest.mark.parametrize("M,H,I", [(37, 512, 256), (300, 384, 384), (64, 7168, 3072)])
+def test_device_warmup_global_dense(mx, M, H, I):
+    d = W.shared_expert(M, seed=6, hidden=H, inter=I)
+    _assert_same_global(_device_warmup(mx, d, routed=False), _warmup_dense(d))
+
+
+def test_device_warmup_global_routed_then_mlp(mx):
+    """g from the device warm-up over a routed batch, then the NVFP4 MLP with it."""
+    d = W.grouped(tokens=600, n_experts=8, k=4, seed=5, hidden=512, inter=256)
+    g_ref = _warmup_grouped(d, np.arange(600))
+    g = _device_warmup(mx, d, routed=True)
+    _assert_same_global(g, g_ref)
+    y = _run_grouped_nv(mx, d, g)
+    ref = O.grouped_expert_mlp(d["x"], d["ids"], d["w"], *(d[n] for n in WNAMES), requant="nvfp4", nv_global=g)
+    assert_mlp_close(y, ref)
+
+
+def test_device_warmup_global_degenerate(mx):
+    """All-zero h (zero activations) and an empty batch give g = 1, as the oracle's rule."""
+    d = W.shared_expert(40, seed=1, hidden=256, inter=128)
+    d["x"] = np.zeros_like(d["x"])
+    assert _device_warmup(mx, d, routed=False) == 1.0
+    assert float(O.nvfp4_warmup_global(np.zeros((4, 128), np.uint16))) == 1.0
+    d["x"] = d["x"][:0]
+    assert _device_warmup(mx, d, routed=False) == 1.0
+
+
 def _run_grouped_nv(mx, d, g):
     y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]), *(t(d[n]) for n in WNAMES),
                               requant="nvfp4", requant_global=g)

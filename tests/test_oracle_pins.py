@@ -26,6 +26,7 @@ CHECKS = [
     pins.check_e4m3_rne,
     pins.check_nvfp4_grid,
     pins.check_nvfp4_error_bound,
+    pins.check_nvfp4_warmup_global,
     pins.check_gemm_integer,
     pins.check_gemm_bruteforce,
     pins.check_silu,
