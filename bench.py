@@ -213,16 +213,18 @@ def skewed_nvfp4(torch, mx, workloads):
     xt = x[:8].contiguous()
     yt = torch.empty((8, H), dtype=torch.bfloat16, device="cuda")
     idt, wt = w["ids"][:8].contiguous(), w["w"][:8].contiguous()
-    wst = torch.empty(mx.grouped_expert_mlp_workspace_size(8, H, I, K, E, "nvfp4"), dtype=torch.uint8,
-                      device="cuda")
-    tail = lambda: mx.grouped_expert_mlp(xt, idt, wt, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
-                                         requant="nvfp4", requant_global=g, out=yt, workspace=wst, packed_scales=pk)
-    us = graph_replay_us(torch, [tail])
     n_active = int(np.unique(d["ids"][:8]).size)
     tbytes = n_active * 35094528
-    rec["skewed_decode_tail_t8_nvfp4"] = {"us_per_call": round(us, 2), "active_experts": n_active,
-                                          "weight_GB/s": round(tbytes / us / 1e3, 1),
-                                          "timing": "hipGraph replay (weights of the active experts)"}
+    for rq in ("nvfp4", "mxfp4"):
+        wst = torch.empty(mx.grouped_expert_mlp_workspace_size(8, H, I, K, E, rq), dtype=torch.uint8, device="cuda")
+        tail = lambda: mx.grouped_expert_mlp(xt, idt, wt, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
+                                             requant=rq, requant_global=g, out=yt, workspace=wst,
+                                             packed_scales=pk)
+        us = graph_replay_us(torch, [tail])
+        rec[f"skewed_decode_tail_t8_{rq}"] = {
+            "us_per_call": round(us, 2), "active_experts": n_active, "weight_GB/s": round(tbytes / us / 1e3, 1),
+            "hbm_frac": round(tbytes / us / 1e3 / PEAK_HBM_GBS, 3),
+            "timing": "hipGraph replay (weights of the active experts)"}
     return rec
 
 

@@ -380,6 +380,192 @@ __global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__
   }
 }
 
+// ---------------------------------------------------------------- routed, few tokens
+// Routed experts with few rows each (a decode step, or the tail of a batch):
+// the tiled GEMM would give each (expert, weight tile) a 256-row token tile
+// holding a handful of rows and wait out one copy latency per K stage, so the
+// weights are streamed once instead, as on the dense few-token path. The rows
+// of expert e are the sorted pair rows expert_off[e] .. expert_off[e+1] of the
+// route kernels. Grid: (16-row weight tiles) x (experts); the workgroups of
+// experts without rows leave at once. A workgroup keeps its weight tile in
+// registers (each wave a run of K steps) and multiplies it by the expert's
+// rows 16 at a time; the 8 waves' partial sums meet in LDS in wave order.
+//  * L1 gathers the MXFP4 token rows by row_token and writes h (bf16) in
+//    sorted row order.
+//  * L2 reads re-quantised h rows in sorted order: MXFP4 codes through the
+//    scaled FP4 MFMA, or (NVFP4 re-quantisation, whose E4M3 per-16 scale an
+//    E8M0 MFMA scale cannot carry) the exactly dequantised bf16 rows through
+//    V_MFMA_F32_16X16X32_BF16, with the weight codes converted exactly to bf16
+//    in registers. The output row of pair p is o[row_slot[p]] =
+//    bf16(acc * (scale * row_weight[p])), scale 1 or the NVFP4 global g, as in
+//    the GEMM's epilogue.
+enum RoutedOperand { RT_FP4 = 0, RT_BF16 = 1 };
+
+struct RoutedLds {
+  uint8_t wscale[16 * 256];     // the tile rows' E8M0 bytes, K <= 8192
+  f32x4 red[2][DW][64];         // partial sums per chunk parity, wave, lane
+};
+
+__device__ __forceinline__ uint4 dequant16_bf16(uint32_t codes, float scale) {
+  return make_uint4(dequant_pair<0>(codes, scale), dequant_pair<1>(codes, scale), dequant_pair<2>(codes, scale),
+                    dequant_pair<3>(codes, scale));
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// The expert's `rows` token rows times one 16-row weight tile. Token row i of
+// the expert is row gather[base + i] (gather != nullptr) or base + i of the
+// operand: FP4 codes `aq` [.., K/2] with E8M0 scales `as` [.., K/32], or bf16
+// `ad` [.., K]. `emit(c0, tot)` runs in wave 0 for every chunk of 16 rows
+// starting at c0, with lane (row c0 + lane%16, tile rows 4*(lane/16) + v).
+template <int OP, int NS, class Emit>
+__device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
+                                                 const uint16_t* __restrict__ ad, const int32_t* __restrict__ gather,
+                                                 int base, int rows, int K, RowPair wp, RowPair sp, RoutedLds& L,
+                                                 Emit&& emit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int kb = K / 2, ks = K / 32, ksteps = K / 128;
+
+  ScaleRegs sr;
+  load_wscales(sp, ks, sr);
+  int s0, n;
+  wave_steps(ksteps, s0, n);
+  uint4 wa[NS];
+  const uint8_t* myrow = wp.row(r16, kb);
+#pragma unroll
+  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)(myrow + min(s0 + k, ksteps - 1) * 64 + q * 16);
+  store_wscales(sr, ks, L.wscale);
+  lds_barrier();
+  int sa[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) sa[k] = L.wscale[r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
+
+  for (int c0 = 0, par = 0; c0 < rows; c0 += 16, par ^= 1) {
+    const int i = min(c0 + r16, rows - 1);
+    const int64_t tok = gather != nullptr ? (int64_t)gather[base + i] : (int64_t)(base + i);
+    const bool tok_ok = c0 + r16 < rows;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (OP == RT_FP4) {
+      uint4 b[NS];
+      int sb[NS];
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int s = min(s0 + k, ksteps - 1);
+        b[k] = *(const uint4*)(aq + tok * kb + s * 64 + q * 16);
+        sb[k] = as[tok * ks + s * 4 + q];
+      }
+      // steps past the wave's run (k >= n) multiply zero codes: no branch
+      // around the MFMAs
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const uint4 bz = tok_ok ? b[k] : z;
+        const uint4 az = k < n ? wa[k] : z;
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc, 4, 4, 0, sa[k], 0, sb[k]);
+      }
+    } else {
+      // A lane's 32 K values of a step (K = 128 s + 32 q + 0..31) feed four
+      // 16x16x32 MFMAs, values 8 j .. 8 j + 7 in the j-th; the token row uses
+      // the same order, so each MFMA contracts matching K.
+      uint4 b[NS][4];
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int s = min(s0 + k, ksteps - 1);
+        const uint4* src = (const uint4*)(ad + tok * K + s * 128 + q * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[k][j] = src[j];
+      }
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const float scale = e8m0_to_f32((uint32_t)sa[k]);
+        const uint32_t wv[4] = {wa[k].x, wa[k].y, wa[k].z, wa[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 av = k < n ? dequant16_bf16(wv[j], scale) : z;
+          const uint4 bv = tok_ok ? b[k][j] : z;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                        __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+        }
+      }
+    }
+    L.red[par][wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < DW; ++w) {
+        const f32x4 o = L.red[par][w][lane];
+        tot[0] += o[0]; tot[1] += o[1]; tot[2] += o[2]; tot[3] += o[3];
+      }
+      emit(c0, tot);
+    }
+  }
+}
+
+// L1 of expert blockIdx.y for 8 intermediate columns j0 .. j0+7 (tile rows
+// 0..7 of w1, 8..15 of w3): h[r][j] = bf16(silu(g) * u) for its sorted rows r.
+template <int NS>
+__global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                                                     const int32_t* __restrict__ row_token,
+                                                     const int32_t* __restrict__ expert_off, int H, int I,
+                                                     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ w1s,
+                                                     const uint8_t* __restrict__ w3, const uint8_t* __restrict__ w3s,
+                                                     uint16_t* __restrict__ h) {
+  __shared__ RoutedLds L;
+  const int e = blockIdx.y;
+  const int base = expert_off[e], rows = expert_off[e + 1] - base;
+  if (rows <= 0) return;
+  const int j0 = blockIdx.x * 8;
+  const int64_t kb = H / 2, ks = H / 32;
+  const int64_t we = (int64_t)e * I * kb, se = (int64_t)e * I * ks;
+  const RowPair wp{w1 + we + j0 * kb, w3 + we + j0 * kb};
+  const RowPair sp{w1s + se + j0 * ks, w3s + se + j0 * ks};
+  routed_tile_rows<RT_FP4, NS>(xq, xs, nullptr, row_token, base, rows, H, wp, sp, L, [&](int c0, const f32x4& acc) {
+    const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
+    float up[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) up[v] = __shfl_xor(acc[v], 32);
+    if (q < 2 && c0 + t < rows) {
+      const uint32_t p0 = bf16x2_rne(silu_mul(acc[0], up[0]), silu_mul(acc[1], up[1]));
+      const uint32_t p1 = bf16x2_rne(silu_mul(acc[2], up[2]), silu_mul(acc[3], up[3]));
+      *(uint2*)(h + (int64_t)(base + c0 + t) * I + j0 + 4 * q) = make_uint2(p0, p1);
+    }
+  });
+}
+
+// L2 of expert blockIdx.y for 16 output columns n0 .. n0+15, from the
+// re-quantised h rows (FP4 codes + E8M0, or bf16): o[row_slot[r]][n] =
+// bf16(acc * (scale * row_weight[r])).
+template <int OP, int NS>
+__global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
+                                                     const uint16_t* __restrict__ hd,
+                                                     const int32_t* __restrict__ expert_off,
+                                                     const int32_t* __restrict__ row_slot,
+                                                     const float* __restrict__ row_weight, float scale, int H, int I,
+                                                     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
+                                                     uint16_t* __restrict__ o) {
+  __shared__ RoutedLds L;
+  const int e = blockIdx.y;
+  const int base = expert_off[e], rows = expert_off[e + 1] - base;
+  if (rows <= 0) return;
+  const int n0 = blockIdx.x * 16;
+  const int64_t kb = I / 2, ks = I / 32;
+  const int64_t we = (int64_t)e * H * kb, se = (int64_t)e * H * ks;
+  const RowPair wp{w2 + we + n0 * kb, w2 + we + (n0 + 8) * kb};
+  const RowPair sp{w2s + se + n0 * ks, w2s + se + (n0 + 8) * ks};
+  routed_tile_rows<OP, NS>(hq, hs, hd, nullptr, base, rows, I, wp, sp, L, [&](int c0, const f32x4& acc) {
+    const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
+    if (c0 + t < rows) {
+      const int r = base + c0 + t;
+      const float wgt = scale * row_weight[r];
+      const uint32_t p0 = bf16x2_rne(acc[0] * wgt, acc[1] * wgt);
+      const uint32_t p1 = bf16x2_rne(acc[2] * wgt, acc[3] * wgt);
+      *(uint2*)(o + (int64_t)row_slot[r] * H + n0 + 4 * q) = make_uint2(p0, p1);
+    }
+  });
+}
+
 size_t decode_lds(int cols) {
   const size_t kb = cols / 2, ks = cols / 32;
   return MAX_TOK * (kb + 16) + ((MAX_TOK * ks + 15) & ~(size_t)15) + ((16 * ks + 15) & ~(size_t)15) +
@@ -462,6 +648,28 @@ void launch_skinny_l2_ns(const DecodeArgs& a, const uint8_t* hq, const uint8_t* 
   }
 }
 
+template <int NS>
+void launch_routed_l1_ns(const RoutedArgs& a, hipStream_t s) {
+  k_routed_l1<NS><<<dim3(a.I / 8, a.E), DT, 0, s>>>(a.xq, a.xs, a.row_token, a.expert_off, a.H, a.I, a.w1, a.w1s,
+                                                      a.w3, a.w3s, a.h);
+}
+
+template <int OP, int NS>
+void launch_routed_l2_ns(const RoutedArgs& a, hipStream_t s) {
+  k_routed_l2<OP, NS><<<dim3(a.H / 16, a.E), DT, 0, s>>>(a.hq, a.hs, a.hd, a.expert_off, a.row_slot, a.row_weight,
+                                                          a.scale, a.H, a.I, a.w2, a.w2s, a.o);
+}
+
+template <int OP>
+void launch_routed_l2_op(const RoutedArgs& a, hipStream_t s) {
+  switch (steps_bucket(a.I)) {
+    case 1: launch_routed_l2_ns<OP, 1>(a, s); break;
+    case 3: launch_routed_l2_ns<OP, 3>(a, s); break;
+    case 7: launch_routed_l2_ns<OP, 7>(a, s); break;
+    default: launch_routed_l2_ns<OP, MAX_STEPS>(a, s); break;
+  }
+}
+
 }  // namespace
 
 // Every workgroup reads all m token rows, so the token traffic grows with m;
@@ -519,6 +727,42 @@ hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8
   if (r2 <= 1) launch_l2_ns<1>(a, s);
   else if (r2 <= 2) launch_l2_ns<2>(a, s);
   else launch_l2_ns<4>(a, s);
+  return hipGetLastError();
+}
+
+// Mean rows per expert up to which the routed weight-streaming kernels run
+// instead of the tiled GEMMs. Each workgroup reads all rows of its expert, so
+// their load instructions and MFMAs grow with the rows, while the GEMMs' time
+// at this size hardly depends on them. Measured over 48 experts of 7168 x 3072
+// (hipGraph replay, uniform top-8): with MXFP4 re-quantisation the two paths
+// meet near 2 rows per expert (8 tokens: 331 against 344 us, 16 tokens: 406
+// against 395 us); with NVFP4, whose GEMM L2 converts both operands to bf16
+// per tile, near 13 (8 tokens: 390 against 589 us, 64 tokens: 641 against
+// 715 us, 96 tokens: 762 against 719 us).
+constexpr int64_t RT_MAX_MEAN_ROWS_MXFP4 = 2;
+constexpr int64_t RT_MAX_MEAN_ROWS_NVFP4 = 12;
+
+bool routed_stream_fits(int64_t T, int64_t hidden, int64_t inter, int k, int E, bool nvfp4) {
+  const int64_t mean_rows = nvfp4 ? RT_MAX_MEAN_ROWS_NVFP4 : RT_MAX_MEAN_ROWS_MXFP4;
+  if (T < 1 || T * (int64_t)k > mean_rows * E) return false;
+  if (hidden > DW * MAX_STEPS * 128 || inter > DW * MAX_STEPS * 128) return false;
+  if (inter % 8 != 0 || hidden % 16 != 0) return false;
+  return 16 * (hidden / 32) <= 8 * DT && 16 * (inter / 32) <= 8 * DT;
+}
+
+hipError_t launch_routed_l1(const RoutedArgs& a, hipStream_t s) {
+  switch (steps_bucket(a.H)) {
+    case 1: launch_routed_l1_ns<1>(a, s); break;
+    case 3: launch_routed_l1_ns<3>(a, s); break;
+    case 7: launch_routed_l1_ns<7>(a, s); break;
+    default: launch_routed_l1_ns<MAX_STEPS>(a, s); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_routed_l2(const RoutedArgs& a, hipStream_t s) {
+  if (a.hd != nullptr) launch_routed_l2_op<RT_BF16>(a, s);
+  else launch_routed_l2_op<RT_FP4>(a, s);
   return hipGetLastError();
 }
 

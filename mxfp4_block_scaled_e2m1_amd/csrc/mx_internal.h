@@ -158,4 +158,27 @@ hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8
                              const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
                              uint16_t* h, uint16_t* y, hipStream_t s);
 
+// Routed experts with few rows each (mean T*k/E at most 2 with MXFP4, 12 with
+// NVFP4 re-quantisation): the weights of each
+// expert with rows streamed once by two kernels (see decode.hip). L1 writes
+// h (bf16, [P, inter], sorted row order); the caller re-quantises it into
+// hq/hs row-major (MXFP4), or into NVFP4 and then dequantises it at global
+// scale 1 into hd (bf16, exact), in which case L2 takes hd and multiplies by
+// `scale` = g. L2 writes o[row_slot[p]] rows, as the GEMM's routed epilogue.
+struct RoutedArgs {
+  int H, I, E;
+  const uint8_t *xq, *xs;
+  const int32_t *row_token, *row_slot, *expert_off;
+  const float* row_weight;
+  const uint8_t *w1, *w1s, *w3, *w3s, *w2, *w2s;
+  uint16_t* h;
+  const uint8_t *hq, *hs;
+  const uint16_t* hd;   // NVFP4 re-quantisation: dequantised h, else nullptr
+  float scale;
+  uint16_t* o;
+};
+bool routed_stream_fits(int64_t T, int64_t hidden, int64_t inter, int k, int E, bool nvfp4);
+hipError_t launch_routed_l1(const RoutedArgs& a, hipStream_t s);
+hipError_t launch_routed_l2(const RoutedArgs& a, hipStream_t s);
+
 }  // namespace mx

@@ -236,6 +236,111 @@ def test_grouped_skewed_sampled_tokens(mx):
 
 
 # ---------------------------------------------------------------- tile-major weight scales
+# ---------------------------------------------------------------- routed, few rows per expert
+# The routed weight-streaming kernels run while T * k <= mean_rows * E:
+STREAM_MEAN_ROWS = {"mxfp4": 2, "nvfp4": 12}
+
+
+def _stream_ws_h(ws, T, H, I, k, E):
+    """Routed weight-streaming workspace (regions 256-byte aligned): xq, xs,
+    block counts, expert offsets, tile bases, row_token, row_slot, row_weight,
+    h (bf16 [P, I], sorted rows), ... Returns (expert_off, row_token, h)."""
+    P = T * k
+    sizes = [T * H // 2, T * H // 32, -(-P // 1024) * E * 4, (E + 1) * 4, (E + 1) * 4, P * 4, P * 4, P * 4,
+             P * I * 2]
+    off, sl = 0, []
+    for n in sizes:
+        sl.append(ws[off:off + n])
+        off += _align(n)
+    eo = sl[3].cpu().numpy().view(np.int32)
+    rt = sl[5].cpu().numpy().view(np.int32)
+    h = sl[8].cpu().numpy().view(np.uint16).reshape(P, I)
+    return eo, rt, h
+
+
+def _stream_case(seed, T=16, E=16, k=2, H=256, I=128):
+    d = W.grouped(tokens=T, n_experts=E, k=k, seed=seed, hidden=H, inter=I)
+    d["ids"][:, 0] = 0              # expert 0: every token, and twice for the first three
+    d["ids"][:3, 1] = 0             # (duplicates within a token allowed): two chunks of 16 rows
+    d["ids"][d["ids"] == E - 1] = E - 2     # the last expert empty
+    assert T * k <= STREAM_MEAN_ROWS["mxfp4"] * E
+    return d
+
+
+def test_grouped_stream_matches_oracle_and_h(mx):
+    """Few rows per expert: the weight-streaming kernels. Output against the
+    oracle, and h of every sorted row against the oracle's h of its (token,
+    expert) pair, bit for bit on >= 99.9 % (the fp32 SiLU near bf16 rounding
+    boundaries aside)."""
+    T, E, k, H, I = 16, 16, 2, 256, 128
+    d = _stream_case(3, T, E, k, H, I)
+    wd = [t(d[n]) for n in WN]
+    ws = torch.empty(mx.grouped_expert_mlp_workspace_size(T, H, I, k, E), dtype=torch.uint8, device="cuda")
+    y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]), *wd, workspace=ws)
+    torch.cuda.synchronize()
+    assert_mlp_close(bits(y), _oracle_grouped(d))
+    eo, rt, h = _stream_ws_h(ws, T, H, I, k, E)
+    counts = np.bincount(d["ids"].ravel(), minlength=E)
+    assert np.array_equal(np.diff(eo), counts) and counts[0] > 16 and counts[E - 1] == 0
+    hb, rb = [], []
+    for e in range(E):
+        if counts[e] == 0:
+            continue
+        rows = np.arange(eo[e], eo[e + 1])
+        _, inter = O.expert_mlp(d["x"][rt[rows]], *(d[n][e] for n in WN), intermediates=True)
+        hb.append(h[rows])
+        rb.append(inter["h"])
+    hb, rb = np.concatenate(hb), np.concatenate(rb)
+    hv, rv = bf16_f64(hb), bf16_f64(rb)
+    big = np.abs(rv) >= H_TINY
+    assert np.mean(hb[big] == rb[big]) >= 0.999
+    assert np.all(np.abs(hv - rv) <= np.abs(rv) * 2.0 ** -7 + H_TINY)
+
+
+def test_grouped_stream_permutation_and_foreign_ids(mx):
+    d = _stream_case(4)
+    y = _run_grouped(mx, d)
+    perm = np.random.default_rng(2).permutation(16)
+    dp = dict(d, x=d["x"][perm], ids=d["ids"][perm], w=d["w"][perm])
+    assert np.array_equal(_run_grouped(mx, dp), y[perm])
+    d2 = dict(d, ids=d["ids"].copy())
+    d2["ids"][::2, 1] = -1
+    d2["ids"][1::4, 1] = 16
+    assert_mlp_close(_run_grouped(mx, d2), _oracle_grouped(d2))
+
+
+def test_grouped_stream_single_expert_equals_shared(mx):
+    """E = 1, k = 1, w = 1 over 2 tokens: the routed weight-streaming kernels
+    against the dense few-token kernels, which sum in the same order."""
+    d = W.shared_expert(2, seed=6, hidden=512, inter=256)
+    g = {n: d[n][None] for n in WN}
+    g.update(x=d["x"], ids=np.zeros((2, 1), np.int32), w=np.ones((2, 1), np.float32))
+    yg = _run_grouped(mx, g)
+    yd, _ = _run_dense(mx, d, 2, 512, 256)
+    assert np.array_equal(yg, yd)
+    assert_mlp_close(yg, _oracle_grouped(g))
+
+
+@pytest.mark.parametrize("requant,T", [("mxfp4", 4), ("mxfp4", 5), ("nvfp4", 24), ("nvfp4", 25)])
+def test_grouped_stream_threshold(mx, requant, T):
+    """T * k = mean_rows * E runs the weight-streaming kernels, one token more the GEMMs."""
+    d = W.grouped(tokens=T, n_experts=4, k=2, seed=8, hidden=384, inter=256)
+    assert (T * 2 <= STREAM_MEAN_ROWS[requant] * 4) == (T in (4, 24))
+    g = 0.0
+    if requant == "nvfp4":
+        h = [O.expert_mlp(d["x"], *(d[n][e] for n in WN), intermediates=True)[1]["h"] for e in range(4)]
+        g = float(O.nvfp4_warmup_global(np.concatenate(h)))
+    ref = O.grouped_expert_mlp(d["x"], d["ids"], d["w"], *(d[n] for n in WN), requant=requant, nv_global=g)
+    assert_mlp_close(_run_grouped(mx, d, packed=True, requant=requant, g=g), ref)
+
+
+def test_grouped_stream_decode_real_shape(mx):
+    """8 tokens of the uniformly routed 48-expert batch at the real shape."""
+    d = W.grouped(tokens=4096, n_experts=48, k=8, seed=0)
+    tail = dict(d, x=d["x"][:8], ids=d["ids"][:8], w=d["w"][:8])
+    assert_mlp_close(_run_grouped(mx, tail, packed=True), _oracle_grouped(tail))
+
+
 @pytest.mark.parametrize("E,H,I", [(3, 384, 256), (2, 512, 384), (1, 7168, 3072)])
 def test_pack_weight_scales_layout(mx, E, H, I):
     """mx_pack_weight_scales moves bytes only: compare with the layout written out in numpy

@@ -185,3 +185,29 @@ def test_nvfp4_skewed_sampled_tokens_and_decode_tail(mx):
     reft = O.grouped_expert_mlp(tail["x"], tail["ids"], tail["w"], *(d[n] for n in WNAMES), requant="nvfp4",
                                 nv_global=g)
     assert_mlp_close(yt, reft)
+
+
+def test_nvfp4_grouped_stream(mx):
+    """Few rows per expert with NVFP4 re-quantisation: the weight-streaming L2
+    on the exactly dequantised h (bf16 matrix cores), against the oracle; one
+    expert with more than 16 rows, one empty, foreign ids."""
+    d = W.grouped(tokens=20, n_experts=6, k=3, seed=11, hidden=256, inter=128)
+    d["ids"][:, 0] = 0
+    d["ids"][d["ids"] == 5] = 4
+    d["ids"][::3, 2] = -1
+    g = _warmup_grouped(d, np.arange(20))
+    y = _run_grouped_nv(mx, d, g)
+    ref = O.grouped_expert_mlp(d["x"], d["ids"], d["w"], *(d[n] for n in WNAMES), requant="nvfp4", nv_global=g)
+    assert_mlp_close(y, ref)
+
+
+def test_nvfp4_grouped_stream_single_expert_close_to_shared(mx):
+    """E = 1 over 12 tokens: the weight-streaming path against the dense
+    NVFP4 path (tiled GEMMs): the same quantisation, sums in another order."""
+    d = W.shared_expert(12, seed=7, hidden=512, inter=256)
+    g = _warmup_dense(d)
+    gd = {n: d[n][None] for n in WNAMES}
+    gd.update(x=d["x"], ids=np.zeros((12, 1), np.int32), w=np.ones((12, 1), np.float32))
+    yg = _run_grouped_nv(mx, gd, g)
+    yd, _ = _run_dense_nv(mx, d, 12, 512, 256, g)
+    assert_mlp_close(yg, yd, cos_min=0.99999)
