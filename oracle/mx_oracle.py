@@ -35,7 +35,7 @@ __all__ = [
     "e2m1_code_rne_sat", "mxfp4_quantize",
     "e4m3_rne_satfinite", "e4m3_encode_exact", "nvfp4_quantize", "nvfp4_dequant_f64",
     "gemm_f64", "silu_mul_bf16", "expert_mlp", "grouped_expert_mlp",
-    "nvfp4_warmup_global",
+    "nvfp4_warmup_global", "mxfp8_quantize", "mxfp8_dequant_f64", "fp8_block_linear",
 ]
 
 # ---------------------------------------------------------------------------
@@ -275,8 +275,9 @@ def e4m3_encode_exact(val):
 def e4m3_rne_satfinite(r):
     """fp32 r >= 0 -> (E4M3 byte, its value fp64): nearest, ties to even, clamp to 448.
 
-    Reading (NVFP4 is never defined on the pages; see ``nvfp4_quantize``):
-    round-to-nearest-even on the E4M3 grid (quantum 2**(E-3) in binade E,
+    Reading (NVFP4 is never defined on the pages; see ``nvfp4_quantize``;
+    the MXFP8 activation quantiser uses it too): round-to-nearest-even on the
+    E4M3 grid (quantum 2**(E-3) in binade E,
     2**-9 below 2**-6), and any result above 448 saturates to 448.
     """
     r = np.asarray(r, dtype=np.float32).astype(np.float64)
@@ -286,6 +287,50 @@ def e4m3_rne_satfinite(r):
     q_exp = np.maximum(e - 1, -6) - 3
     val = np.minimum(np.rint(np.ldexp(r, -q_exp)) * np.ldexp(1.0, q_exp), 448.0)
     return e4m3_encode_exact(val), val
+
+
+def mxfp8_quantize(x_bits):
+    """bf16 [R, C] -> (E4M3 codes uint8 [R, C], E8M0 uint8 [R, C/32]).
+
+    The activation side of the FP8 block-scaled linear (``fp8_block_linear``).
+    Per row and 32-column block: amax = max |x|; shared exponent
+    E = floor(log2 amax) (from frexp); scale byte = clamp(E - 8 + 127, 0, 254),
+    8 being the largest E4M3 exponent; each element x / 2**(byte-127) (exact)
+    is rounded to the nearest E4M3 value, ties to the even code, magnitudes
+    above 448 saturating to 448 (they reach up to 512 under this scale); the
+    sign bit is x's, so a negative value that rounds to zero is byte 0x80. A
+    block of zeros gets scale byte 0.
+
+    Reading: the pages name the FP8 linear of the shared expert but never its
+    activation quantiser. The plainest one that the rest supports is the rule
+    already taken for the MXFP4 activations (OCP shared exponent, round to
+    nearest even, saturate) with E4M3 elements and 32-column E8M0 blocks.
+    Inputs must be finite.
+    """
+    x = bf16_to_f64(x_bits)
+    if x.ndim != 2 or x.shape[1] % 32 != 0:
+        raise ValueError("mxfp8_quantize wants [R, C] with C % 32 == 0")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input")
+    R, C = x.shape
+    blk = x.reshape(R, C // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    _, e = np.frexp(amax)
+    biased = np.clip((e - 1) - 8 + 127, 0, 254)
+    biased = np.where(amax == 0, 0, biased).astype(np.int64)
+    v = blk / np.ldexp(1.0, biased - 127)[..., None]
+    mag, _ = e4m3_rne_satfinite(np.abs(v))
+    codes = (mag & 0x7F) | (np.signbit(blk).astype(np.uint8) << 7)
+    return codes.reshape(R, C).astype(np.uint8), biased.astype(np.uint8)
+
+
+def mxfp8_dequant_f64(codes, scales):
+    """E4M3 codes [R, C] with one E8M0 byte per 32 columns -> fp64 [R, C]."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    if scales.shape != (codes.shape[0], codes.shape[1] // 32):
+        raise ValueError(f"scales {scales.shape} do not match codes {codes.shape}")
+    return e4m3_decode(codes) * np.repeat(e8m0_decode(scales), 32, axis=1)
 
 
 def nvfp4_quantize(x_bits, g):
@@ -351,6 +396,24 @@ def nvfp4_warmup_global(h_bits):
 def gemm_f64(a, b):
     """C = A @ B^T in fp64 (BLAS dgemm). A [M, K], B [N, K]."""
     return np.asarray(a, np.float64) @ np.asarray(b, np.float64).T
+
+
+def fp8_block_linear(x_bits, w, w_s, block=128):
+    """y = bf16(MXFP8(x) . W^T): the FP8 linear of the original checkpoint's shared expert.
+
+    W is FP8 E4M3 [N, K] with one E8M0 scale per 128 x 128 tile
+    (``fp8_block_dequant_f64``), as the checkpoint stores the shared experts
+    ([Q0508] "Status": FP8 float8_e4m3fn with float8_e8m0fnu scales) and as
+    the serving stack runs them through an FP8 block-scaled GEMM ([SRV0511]
+    "Architecture Map": shared expert on the FP8 linear; "What We Fixed"
+    item 1: 128 x 128 blocks with E8M0 scales). x is quantised by
+    ``mxfp8_quantize`` (reading there), the product is fp64 (BLAS dgemm),
+    the result rounded once to bf16.
+    """
+    xq, xs = mxfp8_quantize(x_bits)
+    a = mxfp8_dequant_f64(xq, xs)
+    b = fp8_block_dequant_f64(w, w_s, block)
+    return f64_to_bf16(gemm_f64(a, b))
 
 
 def silu_mul_bf16(g, u):

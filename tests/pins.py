@@ -415,6 +415,151 @@ def check_e4m3_rne(O, seed=17):
         assert _e4m3_fraction(int(bi)) == want
 
 
+def e4m3_bruteforce(a):
+    """|v| values -> nearest non-negative E4M3 byte; ties to the even byte; above 448 -> 448.
+
+    The grid comes from the bit-field definition (``_e4m3_fraction``)."""
+    bytes_ = np.array([b for b in range(127)])
+    grid = np.array([float(_e4m3_fraction(int(b))) for b in bytes_])
+    a = np.asarray(a, np.float64)
+    out = np.empty(a.shape, np.int64)
+    for i0 in range(0, a.size, 4096):
+        aa = a.ravel()[i0:i0 + 4096]
+        d = np.abs(aa[:, None] - grid[None, :])
+        best = d.min(axis=1, keepdims=True)
+        cand = d == best
+        even = cand & (bytes_[None, :] % 2 == 0)
+        pick = np.where(even.any(axis=1) & (cand.sum(axis=1) > 1), even.argmax(axis=1), cand.argmax(axis=1))
+        pick = np.where(aa > 448.0, 126, pick)
+        out.ravel()[i0:i0 + 4096] = bytes_[pick]
+    return out
+
+
+def _mxfp8_sweep(O, anchor_bits, cand_bits):
+    """Blocks [anchor, 31 candidates]: scale byte and E4M3 codes against brute force."""
+    anchor = bf16_value(anchor_bits)
+    n = len(cand_bits)
+    cb = np.concatenate([cand_bits, np.zeros((-n) % 31, np.uint16)])
+    blocks = cb.reshape(-1, 31)
+    x = np.concatenate([np.full((blocks.shape[0], 1), anchor_bits, np.uint16), blocks], axis=1)
+    codes, sc = O.mxfp8_quantize(x)
+    if anchor == 0:
+        want_byte = 0
+    else:
+        _, ex = math.frexp(abs(anchor))
+        want_byte = min(max(ex - 1 - 8 + 127, 0), 254)       # 8: largest E4M3 exponent
+    assert np.all(sc == want_byte), (anchor, np.unique(sc), want_byte)
+    X = math.ldexp(1.0, want_byte - 127)
+    vals = ((x.astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+    want = e4m3_bruteforce(np.abs(vals.ravel()) / X).reshape(x.shape)
+    want = want | (np.signbit(vals).astype(np.int64) << 7)
+    bad = np.argwhere(codes.astype(np.int64) != want)
+    assert bad.size == 0, [(vals[i, j], codes[i, j], want[i, j], want_byte) for i, j in bad[:5]]
+
+
+def check_mxfp8_quantize_exhaustive(O):
+    """Every finite bf16 pattern as a block element of an MXFP8 block, for anchors
+    in every binade (candidates within 2**-12 of the anchor, the rest round to 0)."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    e = (allbits >> 7) & 0xFF
+    finite = allbits[e != 0xFF]
+    mags = finite & 0x7FFF
+    _mxfp8_sweep(O, np.uint16(0x7F7F), finite)
+    _mxfp8_sweep(O, np.uint16(0x007F), finite[mags <= 0x007F])
+    for ea in range(1, 255, 3):
+        abits = np.uint16((ea << 7) | 0x55)
+        lo = max(ea - 12, 0) << 7
+        _mxfp8_sweep(O, abits, finite[(mags <= int(abits)) & (mags >= lo)])
+
+
+def check_mxfp8_examples(O):
+    """Hand-worked blocks: scale 2**(floor(log2 amax) - 8), saturation, kept sign of zero."""
+    def q(vals):
+        x = np.array(list(vals) + [0.0] * (32 - len(vals)), np.float32).reshape(1, 32)
+        return O.mxfp8_quantize((x.view(np.uint32) >> 16).astype(np.uint16))
+    c, s = q([1.0])                     # amax 1: X = 2**-8, 1 / X = 256 = 2**8 -> e 15, m 0
+    assert int(s[0, 0]) == 119 and int(c[0, 0]) == 0x78 and int(c[0, 1]) == 0
+    c, s = q([1.75, -1.0])              # 448 exactly; -256
+    assert int(s[0, 0]) == 119 and int(c[0, 0]) == 0x7E and int(c[0, 1]) == 0xF8
+    c, s = q([1.9375, 1.8125])          # 496 and 464 saturate to 448 (no NaN code)
+    assert int(c[0, 0]) == 0x7E and int(c[0, 1]) == 0x7E
+    c, s = q([1.0, -2.0 ** -20])        # -2**-12 under the scale: below half the subnormal step
+    assert int(c[0, 1]) == 0x80
+    c, s = q([1.0, 2.0 ** -16])         # 2**-8 = 2 * 2**-9: subnormal byte 2
+    assert int(c[0, 1]) == 0x02
+    c, s = q([0.0, -0.0])               # zero block: scale byte 0, signs kept
+    assert int(s[0, 0]) == 0 and int(c[0, 0]) == 0 and int(c[0, 1]) == 0x80
+
+
+def check_mxfp8_roundtrip(O, seed=47):
+    """quant(dequant(c, s)) == (c, s) when a block's largest code lies in [256, 448];
+    dequant(quant(dequant)) == dequant for any finite codes."""
+    rng = np.random.default_rng(seed)
+    R, C = 32, 256
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    codes = rng.choice(finite, size=(R, C)).astype(np.uint8)
+    cb = codes.reshape(R, C // 32, 32)
+    top = np.arange(0x78, 0x7F, dtype=np.uint8)
+    cb[:, :, 0] = rng.choice(top, size=(R, C // 32)) | (rng.integers(0, 2, (R, C // 32)) << 7).astype(np.uint8)
+    codes = cb.reshape(R, C)
+    # the largest code must be the one forced into [256, 448]
+    mag = codes.reshape(R, C // 32, 32) & 0x7F
+    mag[:, :, 1:] = np.minimum(mag[:, :, 1:], mag[:, :, :1])
+    codes = (mag.reshape(R, C) | (codes & 0x80)).astype(np.uint8)
+    scales = rng.integers(20, 230, (R, C // 32)).astype(np.uint8)
+    vals = np.array([float("nan") if _e4m3_fraction(b) is None else float(_e4m3_fraction(b)) for b in range(256)])
+    deq = vals[codes] * np.ldexp(1.0, np.repeat(scales.astype(np.int64), 32, axis=1) - 127)
+    bits = (deq.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(((bits.astype(np.uint32) << 16).view(np.float32)).astype(np.float64), deq)
+    q2, s2 = O.mxfp8_quantize(bits)
+    assert np.array_equal(s2, scales)
+    nz = (codes & 0x7F) != 0
+    assert np.array_equal(q2[nz], codes[nz])
+    d2 = O.mxfp8_dequant_f64(q2, s2)
+    assert np.array_equal(d2, deq)
+
+
+def check_fp8_linear_bruteforce(O, seed=53):
+    """FP8 linear on a ragged tiny shape (two 128-row scale blocks, the second
+    partial; two K blocks) against exact Fractions from the bit fields, rounded
+    by the table-search bf16 reference."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 2, 130, 256
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    w = rng.choice(finite, size=(N, K)).astype(np.uint8)
+    ws = rng.integers(118, 135, (2, 2)).astype(np.uint8)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    y = O.fp8_block_linear(xb, w, ws)
+    xq, xs = O.mxfp8_quantize(xb)          # pinned by the MXFP8 checks
+    P2 = [Fraction(2) ** (e - 127) for e in range(256)]
+    wf = [[_e4m3_fraction(int(w[n, k])) * P2[int(ws[n // 128, k // 128])] for k in range(K)] for n in range(N)]
+    want = []
+    for m in range(M):
+        xf = [_e4m3_fraction(int(xq[m, k])) * P2[int(xs[m, k // 32])] for k in range(K)]
+        for n in range(N):
+            want.append(float(sum(a * b for a, b in zip(xf, wf[n]))))
+    ref = bf16_rne_reference(np.array(want)).reshape(M, N)
+    assert np.array_equal(y, ref)
+
+
+def check_fp8_linear_unit_rows(O):
+    """x = unit rows e_k (exact in MXFP8): y = the bf16 FP8-block dequant of W's columns k."""
+    rng = np.random.default_rng(59)
+    N, K = 256, 384
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    w = rng.choice(finite, size=(N, K)).astype(np.uint8)
+    ws = rng.integers(118, 135, (2, 3)).astype(np.uint8)
+    ks = np.array([0, 5, 127, 128, 200, 383])
+    x = np.zeros((len(ks), K), np.uint16)
+    x[np.arange(len(ks)), ks] = 0x3F80                  # bf16 1.0
+    y = O.fp8_block_linear(x, w, ws)
+    deq = O.fp8_block_dequant_bf16(w, ws)               # pinned by the FP8 block checks
+    # as values: a -0 weight times 1 plus the +0 products of the other columns is +0
+    tof = lambda b: ((b.astype(np.uint32) << 16).view(np.float32))
+    assert np.array_equal(tof(y), tof(np.ascontiguousarray(deq[:, ks].T)))
+
+
 def check_nvfp4_grid(O, seed=19):
     """Exhaustive bf16 magnitudes against brute-force nearest grid at fixed (s, g)."""
     g = np.float32(0.0123)

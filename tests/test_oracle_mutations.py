@@ -137,6 +137,35 @@ def _fp8_scale_transposed_index(q, s, block=128):
     return O.e4m3_decode(q) * sv[(j * gr + i) % sv.size]
 
 
+def _mxfp8_emax7(x_bits):
+    # shared exponent floor(log2 amax) - 7: the largest values leave the E4M3 range
+    x = O.bf16_to_f64(x_bits)
+    R, C = x.shape
+    blk = x.reshape(R, C // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    _, e = np.frexp(amax)
+    b = np.where(amax == 0, 0, np.clip(e - 1 - 7 + 127, 0, 254)).astype(np.int64)
+    v = blk / np.ldexp(1.0, b - 127)[..., None]
+    mag, _ = O.e4m3_rne_satfinite(np.abs(v))
+    return ((mag & 0x7F) | (np.signbit(blk).astype(np.uint8) << 7)).reshape(R, C).astype(np.uint8), b.astype(np.uint8)
+
+
+def _mxfp8_no_saturation(x_bits):
+    # values above 448 become the NaN code instead of saturating
+    codes, sc = _orig["mxfp8_quantize"](x_bits)
+    x = O.bf16_to_f64(x_bits)
+    R, C = x.shape
+    v = np.abs(x) / np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+    return np.where(v > 448, codes | 0x7F, codes).astype(np.uint8), sc
+
+
+def _fp8_linear_scale_per_row(x_bits, w, w_s, block=128):
+    # weight scale indexed [n // 128] only (first K block's scale for every K)
+    ws = np.asarray(w_s)
+    flat = np.repeat(ws[:, :1], ws.shape[1], axis=1)
+    return _orig["fp8_block_linear"](x_bits, w, flat, block)
+
+
 LUT_POS_ZERO = np.array([0.0, 0.5, 1, 1.5, 2, 3, 4, 6, 0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
 
 MUTATIONS = [
@@ -161,6 +190,10 @@ MUTATIONS = [
     ("re-quant skipped", "_requant", _requant_skipped, pins.check_mlp_bruteforce),
     ("gate weights ignored", "grouped_expert_mlp", _grouped_ignore_weights,
      pins.check_grouped_reductions),
+    ("MXFP8 shared exponent off by one", "mxfp8_quantize", _mxfp8_emax7, pins.check_mxfp8_examples),
+    ("MXFP8 without saturation", "mxfp8_quantize", _mxfp8_no_saturation, pins.check_mxfp8_quantize_exhaustive),
+    ("FP8 linear weight scale per row block only", "fp8_block_linear", _fp8_linear_scale_per_row,
+     pins.check_fp8_linear_unit_rows),
 ]
 
 

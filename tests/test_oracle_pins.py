@@ -32,6 +32,11 @@ CHECKS = [
     pins.check_silu,
     pins.check_mlp_bruteforce,
     pins.check_grouped_reductions,
+    pins.check_mxfp8_examples,
+    pins.check_mxfp8_quantize_exhaustive,
+    pins.check_mxfp8_roundtrip,
+    pins.check_fp8_linear_bruteforce,
+    pins.check_fp8_linear_unit_rows,
 ]
 
 
