@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "expert-MLP TFLOP/s & frac of FP4 peak, 48 experts x 4096 tok top-8 (1 GPU)"
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CALIB_COPY_BYTES = 1 << 28    # --calibration-copy: one device copy of 256 MiB (read 256 MiB, write 256 MiB)
 
@@ -158,6 +159,7 @@ def secondary(torch, mx, workloads):
     out["shared_expert_M4096"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
                                   "frac_of_fp4_peak": round(flops / ms / 1e9 / PEAK_FP4_TFLOPS, 4)}
     out.update(skewed_nvfp4(torch, mx, workloads))
+    out.update(fp8_linear(torch, mx, workloads))
     # dequant (8 rotating buffer sets so the working set exceeds the 256 MB cache)
     dq = workloads.dequant_inputs(0)
     c = torch.from_numpy(dq["w1"]).cuda()
@@ -179,6 +181,32 @@ def secondary(torch, mx, workloads):
     out["dequant_fp8_block"] = {"us_per_call": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
                                 "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3),
                                 "timing": "hipGraph replay, 8 rotating buffer sets"}
+    return out
+
+
+def fp8_linear(torch, mx, workloads):
+    """FP8 block-scaled linear (MXFP8 activations, E4M3 weights with 128 x 128
+    E8M0 scales) over 4096 tokens: the pages' FP8 matrix [7168, 1536] and the
+    shared expert's gate/up [6144, 7168] and down [7168, 3072] shapes. Per-phase
+    times from HIP events on the launch stream (quantiser and GEMM)."""
+    out = {}
+    M = 4096
+    for N, K in ((7168, 1536), (6144, 7168), (7168, 3072)):
+        d = workloads.fp8_linear(M, N, K, seed=0)
+        x = bf16_dev(torch, d["x"])
+        w = torch.from_numpy(d["w"]).cuda()
+        wsc = torch.from_numpy(d["ws"]).cuda()
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mx.fp8_block_linear_workspace_size(M, K), dtype=torch.uint8, device="cuda")
+        fn = lambda: mx.fp8_block_linear(x, w, wsc, out=y, workspace=ws)
+        ms, phases = time_steps(torch, fn, 20, 3, profile=(mx.profile_start, mx.profile_stop))
+        flops = 2.0 * M * N * K
+        gemm_ms = phases["fp8_gemm"][0] / phases["fp8_gemm"][1]
+        out[f"fp8_block_linear_M{M}_N{N}_K{K}"] = {
+            "ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
+            "gemm_ms": round(gemm_ms, 4), "gemm_TFLOP/s": round(flops / gemm_ms / 1e9, 2),
+            "gemm_frac_of_fp8_peak": round(flops / gemm_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "quant_ms": round(phases["quant_x8"][0] / phases["quant_x8"][1], 4)}
     return out
 
 

@@ -80,7 +80,8 @@ typedef enum mx_status {
 typedef enum mx_format {
   MX_FMT_MXFP4 = 0,      /* E2M1 codes + E8M0 per 1x32 */
   MX_FMT_FP8_B128 = 1,   /* float8_e4m3fn + E8M0 per 128x128 block (dequant only) */
-  MX_FMT_NVFP4 = 2       /* E2M1 codes + E4M3 per 1x16 + fp32 global scale */
+  MX_FMT_NVFP4 = 2,      /* E2M1 codes + E4M3 per 1x16 + fp32 global scale */
+  MX_FMT_MXFP8 = 3       /* float8_e4m3fn codes + E8M0 per 1x32 (activation quantisation only) */
 } mx_format;
 
 /*
@@ -104,6 +105,9 @@ MX_API mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales
  *   MX_FMT_NVFP4: codes [rows, cols/2], scales [rows, cols/16] (E4M3), global_scale = g > 0
  *                 finite and >= 2^-117. Steps in fp32: s = E4M3_RNE_sat(amax / (6 g)),
  *                 code = E2M1_RNE_sat(x / (s g)); s == 0 gives signed zero codes.
+ *   MX_FMT_MXFP8: codes [rows, cols] (e4m3fn), scales [rows, cols/32] (E8M0); cols % 32 == 0.
+ *                 Scale byte clamp(floor(log2 amax) - 8 + 127, 0, 254); elements
+ *                 rounded to nearest even E4M3, saturating at +-448, sign kept.
  * Alignment: x and codes 16 bytes (NVFP4 codes 8 bytes).
  */
 MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t rows, int64_t cols,
@@ -216,6 +220,27 @@ MX_API mx_status mx_nvfp4_global_warmup(const uint16_t* x, int64_t T, int64_t hi
 
 MX_API size_t mx_nvfp4_global_warmup_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k,
                                                     int32_t E);
+
+/*
+ * mx_fp8_block_linear -- y = bf16(MXFP8(x) . W^T): the FP8 block-scaled linear
+ * of the original checkpoint's shared expert (page "2026-05-11 - DeepSeek V4
+ * NVFP4 vLLM Serving: Full End-to-End", "Architecture Map" and "What We
+ * Fixed" item 1; page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization",
+ * "Status").
+ *   x   [M, K] bf16, quantised per row and 32 columns to MXFP8 as
+ *       mx_quantize_act(MX_FMT_MXFP8) does (into the workspace)
+ *   w   [N, K] float8_e4m3fn codes, row-major
+ *   w_s [N/128, K/128] E8M0, one byte per 128 x 128 tile (multiplies)
+ *   y   [M, N] bf16, fp32 accumulation rounded once
+ * K % 128 == 0, K <= 8192, N % 128 == 0; M >= 0 (M == 0 does nothing).
+ * workspace: at least mx_fp8_block_linear_workspace_size(M, K) bytes, 256-byte
+ * aligned; scratch. y must not alias x, w or the workspace.
+ * Alignment: x, w and y 16 bytes. E4M3 NaN codes or E8M0 byte 255 give NaN.
+ */
+MX_API mx_status mx_fp8_block_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w,
+                                     const uint8_t* w_s, int64_t N, uint16_t* y, void* workspace,
+                                     size_t ws_bytes, void* stream);
+MX_API size_t mx_fp8_block_linear_workspace_size(int64_t M, int64_t K);
 
 /*
  * mx_debug_gemm_f32 -- test hook, not part of the hot path: C[M, N] = A . B^T in fp32

@@ -17,7 +17,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmxfp4.so")
 
-MX_FMT = {"mxfp4": 0, "fp8_b128": 1, "nvfp4": 2}
+MX_FMT = {"mxfp4": 0, "fp8_b128": 1, "nvfp4": 2, "mxfp8": 3}
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_FORMAT",
           5: "MX_ERR_WORKSPACE", 6: "MX_ERR_HIP", 7: "MX_ERR_VALUE"}
 
@@ -43,6 +43,8 @@ SIGNATURES = {
     "mx_pack_weight_scales": (_I32, [_P, _P, _P, _I64, _I64, _I32, _P, _SZ, _P]),
     "mx_packed_weight_scales_size": (_SZ, [_I64, _I64, _I32]),
     "mx_debug_gemm_f32": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "mx_fp8_block_linear": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "mx_fp8_block_linear_workspace_size": (_SZ, [_I64, _I64]),
     "mx_status_string": (ctypes.c_char_p, [_I32]),
     "mx_last_error": (ctypes.c_char_p, []),
     "mx_profile_start": (_I32, []),
@@ -111,12 +113,14 @@ def dequant(fmt, codes, scales, rows: int, cols: int, global_scale: float = 0.0,
 
 
 def quantize_act(fmt, x, global_scale: float = 0.0, codes=None, scales=None, stream=None):
-    """mx_quantize_act: bf16 x [rows, cols] -> (codes [rows, cols/2], scales)."""
+    """mx_quantize_act: bf16 x [rows, cols] -> (codes [rows, cols/2], or [rows, cols]
+    for MXFP8, scales)."""
     rows, cols = x.shape
     f = _fmt(fmt)
     per = 16 if f == MX_FMT["nvfp4"] else 32
     if codes is None:
-        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        width = cols if f == MX_FMT["mxfp8"] else cols // 2
+        codes = torch.empty((rows, width), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, cols // per), dtype=torch.uint8, device=x.device)
     _check(lib().mx_quantize_act(f, _ptr(x), rows, cols, float(global_scale), _ptr(codes), _ptr(scales),
@@ -227,3 +231,19 @@ def profile_stop():
     n = _I32(0)
     _check(lib().mx_profile_stop(buf, 64, ctypes.byref(n)))
     return {buf[i].name.decode(): (buf[i].total_ms, int(buf[i].launches)) for i in range(min(n.value, 64))}
+
+
+def fp8_block_linear_workspace_size(M, K) -> int:
+    return int(lib().mx_fp8_block_linear_workspace_size(M, K))
+
+
+def fp8_block_linear(x, w, w_s, out=None, workspace=None, stream=None):
+    """mx_fp8_block_linear: bf16 x [M, K], E4M3 w [N, K], E8M0 w_s [N/128, K/128] -> bf16 y [M, N]."""
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws = _workspace(fp8_block_linear_workspace_size(M, K), x.device, workspace)
+    _check(lib().mx_fp8_block_linear(_ptr(x), M, K, _ptr(w), _ptr(w_s), N, _ptr(out), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+    return out

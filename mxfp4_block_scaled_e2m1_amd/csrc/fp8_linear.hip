@@ -1,0 +1,266 @@
+// FP8 block-scaled linear: y = bf16(MXFP8(x) . W^T) with W in FP8 E4M3 and
+// one E8M0 scale per 128 x 128 tile.
+//
+// The original checkpoint stores the shared experts in FP8 E4M3 with E8M0
+// block scales (page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", section
+// "Status") and the serving stack runs them through an FP8 block-scaled GEMM
+// (page "2026-05-11 - DeepSeek V4 NVFP4 vLLM Serving: Full End-to-End",
+// sections "Architecture Map" and "What We Fixed" item 1: 128 x 128 blocks,
+// E8M0 scales). The pages leave the activation side open; x is quantised to
+// MXFP8: per row and 32 columns an E8M0 byte clamp(floor(log2 amax) - 8 + 127,
+// 0, 254) and E4M3 elements rounded to nearest even, saturating at 448, the
+// sign kept (the OCP shared-exponent rule with E4M3 elements).
+//
+// Both operands are then what gfx950's scaled MFMA takes natively: FP8 codes
+// with one E8M0 byte per 32 K values. A weight row's byte for a 32-wide K
+// chunk is its 128 x 128 tile's byte, so W is used as stored.
+//
+// GEMM design:
+//  * 512-thread workgroups on 256 (weight rows) x 256 (token rows) tiles,
+//    K stage 128 (one weight-scale column); 8 waves of 128 x 64, each 4 x 2
+//    blocks of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP8 E4M3 A and B).
+//  * Each stage is 2 x 32 KB of codes in LDS, two slots. The copies of the
+//    next stage go straight from global memory into the other slot
+//    (GLOBAL_LOAD_LDS_DWORDX4) while the current stage's MFMAs run; one
+//    barrier per stage. Rows are 128 bytes, 16-byte chunk c of row r stored
+//    at chunk c ^ (r % 8), so the 32 rows read by a half-wave spread over all
+//    banks.
+//  * The tile's weight scales (2 block rows x K/128 bytes) sit in LDS for the
+//    whole K loop; a wave's 128 weight rows share one byte per stage. Token
+//    scales: one dword (4 chunks) per row and stage, loaded a stage ahead.
+//  * Tiles: m fastest, cut into 8 contiguous ranges, workgroup b on XCD b % 8
+//    taking range b % 8, so the workgroups of one XCD share weight tiles.
+#include "mx_device.h"
+#include "mx_internal.h"
+
+namespace mx {
+
+namespace {
+
+constexpr int F8_THREADS = 512;
+constexpr int F8_BN = 256;            // weight rows per tile
+constexpr int F8_BM = 256;            // token rows per tile
+constexpr int F8_BK = 128;            // K per stage (bytes per row)
+constexpr int F8_OPND = 256 * F8_BK;  // 32 KB per operand and stage
+constexpr int F8_SLOT = 2 * F8_OPND;  // weights + tokens
+constexpr int F8_MAX_KB = 64;         // K / 128 <= 64: weight-scale rows in LDS
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ quantiser
+// One thread per 32-element block: 64 bytes in, 32 code bytes and a scale out.
+__global__ __launch_bounds__(256) void k_quant_mxfp8(const uint4* __restrict__ x, uint4* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales, int64_t nblk) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += stride) {
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = x[4 * b + i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = max(am, amax2(w[i]));
+    // floor(log2 amax) - 8 + 127 from the bf16 exponent field ef: ef - 8, at least 0
+    const int ef = (int)((am >> 7) & 0xFFu);
+    const uint32_t sb = (uint32_t)(ef > 8 ? ef - 8 : 0);
+    const float inv = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb), exact multiply
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t e = (w[2 * i + (j >> 1)] >> (16 * (j & 1))) & 0xFFFFu;
+        const float v = bf16_to_f32(e & 0x7FFFu) * inv;
+        const uint32_t c = e4m3_rne_satfinite(v) | ((e >> 8) & 0x80u);
+        d |= c << (8 * j);
+      }
+      q[i] = d;
+    }
+    codes[2 * b] = make_uint4(q[0], q[1], q[2], q[3]);
+    codes[2 * b + 1] = make_uint4(q[4], q[5], q[6], q[7]);
+    scales[b] = (uint8_t)sb;
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+struct F8Args {
+  const uint8_t* w;      // [N, K] E4M3
+  const uint8_t* ws;     // [N/128, K/128] E8M0
+  const uint8_t* xq;     // [M, K] E4M3
+  const uint8_t* xs;     // [M, K/32] E8M0
+  uint16_t* y;           // [M, N] bf16
+  int M, N, K;
+  int tiles_n, tiles_m, per_xcd;
+};
+
+// Global -> LDS copy of 16 bytes per lane: lane i writes LDS bytes
+// [m0 + 16 i, +16). Issued as inline asm so that the compiler does not wait
+// for it before every LDS read; the K loop waits for it explicitly.
+__device__ __forceinline__ void f8_dma16(const void* src, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_off) : "memory", "m0");
+}
+
+// LDS byte offset of 16-byte chunk c of row r in an operand tile.
+__device__ __forceinline__ int f8_off(int r, int c) { return r * F8_BK + ((c ^ (r & 7)) << 4); }
+
+__global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * F8_SLOT];
+  __shared__ uint8_t wsc[2][F8_MAX_KB];
+  const int b = blockIdx.x;
+  const int L = (b & 7) * a.per_xcd + (b >> 3);
+  if (L >= a.tiles_n * a.tiles_m) return;
+  const int nt = L / a.tiles_m, mt = L - nt * a.tiles_m;
+  const int n0 = nt * F8_BN, m0 = mt * F8_BM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int K = a.K, kb128 = K / F8_BK, nst = kb128;
+
+  // weight scales of the tile's two 128-row blocks (the second clamped at the end of W)
+  for (int i = tid; i < 2 * kb128; i += F8_THREADS) {
+    const int br = min(n0 / 128 + i / kb128, a.N / 128 - 1);
+    wsc[i / kb128][i % kb128] = a.ws[(int64_t)br * kb128 + i % kb128];
+  }
+
+  // Global -> LDS copies (GLOBAL_LOAD_LDS_DWORDX4): wave instruction c of wave
+  // w writes 16-byte chunks p = (4 w + c) * 64 + lane of an operand tile, which
+  // is stored chunk position p % 8 of row p / 8, i.e. logical chunk
+  // (p % 8) ^ (row % 8) of that row. Eight lanes cover one 128-byte row.
+  // Rows past the end of W or x re-read the last row.
+  const uint8_t* __restrict__ wbase = a.w + (int64_t)n0 * K;
+  const uint8_t* __restrict__ xbase = a.xq + (int64_t)m0 * K;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t woff[4], xoff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int p = (wave * 4 + c) * 64 + lane;
+    const int r = p >> 3, lc = (p & 7) ^ (r & 7);
+    woff[c] = (uint32_t)((min(n0 + r, a.N - 1) - n0) * K + lc * 16);
+    xoff[c] = (uint32_t)((min(m0 + r, a.M - 1) - m0) * K + lc * 16);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)smem;
+  auto issue = [&](int st) {
+    const uint32_t sb = lds0 + (st & 1) * F8_SLOT + wu * 4 * 1024;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) f8_dma16(wbase + woff[c] + st * F8_BK, sb + c * 1024);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) f8_dma16(xbase + xoff[c] + st * F8_BK, sb + F8_OPND + c * 1024);
+  };
+  // token scales of this lane's two 32-row blocks: one dword per row and stage
+  const int r32 = lane & 31, half = lane >> 5;
+  const uint32_t* __restrict__ xs32 = (const uint32_t*)a.xs;
+  uint32_t xsoff[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) xsoff[g] = (uint32_t)(min(m0 + wm * 64 + g * 32 + r32, a.M - 1) * (K / 128));
+  uint32_t xsd[2], xsn[2];
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[f][g][v] = 0.f;
+
+  issue(0);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) xsn[g] = xs32[(int64_t)xsoff[g]];
+
+  for (int st = 0; st < nst; ++st) {
+    // stage st is in LDS (all waves' copies), and every wave's reads of the
+    // other slot (stage st - 1) are done: refill it with stage st + 1
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    xsd[0] = xsn[0];
+    xsd[1] = xsn[1];
+    if (st + 1 < nst) {
+      issue(st + 1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) xsn[g] = xs32[(int64_t)xsoff[g] + st + 1];
+    }
+    const uint8_t* sw = smem + (st & 1) * F8_SLOT;
+    const uint8_t* sx = sw + F8_OPND;
+    const int sa = wsc[wn][st];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // FP8 operand layout of the 32x32x64 scaled MFMA (checked on the device):
+      // lane (row, h) holds K = 16 h .. 16 h + 15 in its first 16 bytes and
+      // K = 32 + 16 h .. 32 + 16 h + 15 in the next 16, and supplies the scale
+      // byte of the 32-wide block h. So this lane reads 16-byte chunks 4 ks + h
+      // and 4 ks + 2 + h of the stage, and passes the scale of chunk pair 2 ks + h.
+      const int c0 = ks * 4 + half, c1 = c0 + 2;
+      i32x8_t B[2];
+      int sb[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int r = wm * 64 + g * 32 + r32;
+        const uint4 lo = *(const uint4*)(sx + f8_off(r, c0));
+        const uint4 hi = *(const uint4*)(sx + f8_off(r, c1));
+        B[g] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sb[g] = (int)((xsd[g] >> (8 * (2 * ks + half))) & 0xFFu);
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int r = wn * 128 + f * 32 + r32;
+        const uint4 lo = *(const uint4*)(sw + f8_off(r, c0));
+        const uint4 hi = *(const uint4*)(sw + f8_off(r, c1));
+        const i32x8_t A = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B[g], acc[f][g], 0, 0, 0, sa, 0, sb[g]);
+      }
+    }
+  }
+
+  // lane holds token m = m0 + 64 wm + 32 g + lane%32 and weight rows
+  // n = n0 + 128 wn + 32 f + 8 (v/4) + 4 (lane/32) + v%4
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int m = m0 + wm * 64 + g * 32 + r32;
+    if (m >= a.M) continue;
+    uint16_t* yrow = a.y + (int64_t)m * a.N;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 128 + f * 32 + 8 * q + 4 * half;
+        if (n < a.N) {
+          const uint32_t p0 = bf16x2_rne(acc[f][g][4 * q], acc[f][g][4 * q + 1]);
+          const uint32_t p1 = bf16x2_rne(acc[f][g][4 * q + 2], acc[f][g][4 * q + 3]);
+          *(uint2*)(yrow + n) = make_uint2(p0, p1);
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_mxfp8(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s) {
+  const int64_t nblk = rows * (cols / 32);
+  if (nblk == 0) return hipSuccess;
+  int64_t g = (nblk + 255) / 256;
+  if (g > 8192) g = 8192;
+  k_quant_mxfp8<<<(int)g, 256, 0, s>>>((const uint4*)x, (uint4*)codes, scales, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* ws, int M, int N,
+                           int K, uint16_t* y, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  F8Args a;
+  a.w = w; a.ws = ws; a.xq = xq; a.xs = xs; a.y = y;
+  a.M = M; a.N = N; a.K = K;
+  a.tiles_n = (N + F8_BN - 1) / F8_BN;
+  a.tiles_m = (M + F8_BM - 1) / F8_BM;
+  const int total = a.tiles_n * a.tiles_m;
+  a.per_xcd = (total + 7) / 8;
+  k_fp8_gemm<<<8 * a.per_xcd, F8_THREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+bool fp8_linear_fits(int64_t K) { return K / F8_BK <= F8_MAX_KB; }
+
+}  // namespace mx

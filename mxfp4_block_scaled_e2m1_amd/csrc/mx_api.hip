@@ -371,8 +371,10 @@ mx_status mx_quantize_act(mx_format fmt, const uint16_t* x, int64_t rows, int64_
   } else if (fmt == MX_FMT_NVFP4) {
     if (cols % 16 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 16 != 0", (long long)cols);
     MX_TRY(check_global(global_scale));
+  } else if (fmt == MX_FMT_MXFP8) {
+    if (cols % 32 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 32 != 0", (long long)cols);
   } else {
-    return fail(MX_ERR_FORMAT, "quantize_act supports MXFP4 and NVFP4, not format %d", (int)fmt);
+    return fail(MX_ERR_FORMAT, "quantize_act supports MXFP4, NVFP4 and MXFP8, not format %d", (int)fmt);
   }
   if (rows == 0 || cols == 0) return ok();
   MX_REQUIRE_PTR(x);
@@ -383,6 +385,9 @@ mx_status mx_quantize_act(mx_format fmt, const uint16_t* x, int64_t rows, int64_
   if (fmt == MX_FMT_MXFP4) {
     MX_REQUIRE_ALIGN(codes, 16);
     e = phase("quant_mxfp4", s, [&] { return launch_quant_mxfp4(x, rows, cols, codes, scales, s); });
+  } else if (fmt == MX_FMT_MXFP8) {
+    MX_REQUIRE_ALIGN(codes, 16);
+    e = phase("quant_mxfp8", s, [&] { return launch_quant_mxfp8(x, rows, cols, codes, scales, s); });
   } else {
     MX_REQUIRE_ALIGN(codes, 8);
     e = phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, rows, cols, global_scale, codes, scales, s); });
@@ -756,6 +761,44 @@ mx_status mx_nvfp4_global_warmup(const uint16_t* x, int64_t T, int64_t hidden, i
     MX_HIP(launch_gemm(EPI_SWIGLU_MXFP4, l1, mtiles * l1.n_tiles, s), "l1_gemm");
   }
   MX_HIP(launch_nvfp4_global(w.amax, global_out, s), "nvfp4_global");
+  return ok();
+}
+
+size_t mx_fp8_block_linear_workspace_size(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  Carve c(nullptr);
+  c.take((size_t)(M * K));
+  c.take((size_t)(M * (K / 32)));
+  return c.off;
+}
+
+mx_status mx_fp8_block_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, const uint8_t* w_s,
+                              int64_t N, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (M < 0 || K < 0 || N < 0) return fail(MX_ERR_SHAPE, "negative size");
+  if (K < 128 || K % 128 != 0) return fail(MX_ERR_SHAPE, "K %lld must be a positive multiple of 128", (long long)K);
+  if (!fp8_linear_fits(K)) return fail(MX_ERR_SHAPE, "K %lld above 8192", (long long)K);
+  if (N < 128 || N % 128 != 0) return fail(MX_ERR_SHAPE, "N %lld must be a positive multiple of 128", (long long)N);
+  if (N > (1 << 20) || M > ((int64_t)1 << 30) || M * K > ((int64_t)1 << 40) || M * N > ((int64_t)1 << 40))
+    return fail(MX_ERR_SHAPE, "matrix too large");
+  if (M == 0) return ok();
+  MX_REQUIRE_PTR(x);
+  MX_REQUIRE_PTR(w);
+  MX_REQUIRE_PTR(w_s);
+  MX_REQUIRE_PTR(y);
+  MX_REQUIRE_ALIGN(x, 16);
+  MX_REQUIRE_ALIGN(w, 16);
+  MX_REQUIRE_ALIGN(y, 16);
+  MX_REQUIRE_PTR(workspace);
+  MX_REQUIRE_ALIGN(workspace, 256);
+  const size_t need = mx_fp8_block_linear_workspace_size(M, K);
+  if (ws_bytes < need) return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  Carve c(workspace);
+  uint8_t* xq = (uint8_t*)c.take((size_t)(M * K));
+  uint8_t* xs = (uint8_t*)c.take((size_t)(M * (K / 32)));
+  MX_HIP(phase("quant_x8", s, [&] { return launch_quant_mxfp8(x, M, K, xq, xs, s); }), "quant_x8");
+  MX_HIP(phase("fp8_gemm", s, [&] { return launch_fp8_gemm(xq, xs, w, w_s, (int)M, (int)N, (int)K, y, s); }),
+         "fp8_gemm");
   return ok();
 }
 

@@ -181,4 +181,12 @@ bool routed_stream_fits(int64_t T, int64_t hidden, int64_t inter, int k, int E, 
 hipError_t launch_routed_l1(const RoutedArgs& a, hipStream_t s);
 hipError_t launch_routed_l2(const RoutedArgs& a, hipStream_t s);
 
+// ---- FP8 block-scaled linear (fp8_linear.hip) -----------------------------
+hipError_t launch_quant_mxfp8(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+// y [M, N] = bf16(dequant(xq, xs) . dequant(w, ws)^T); K % 128 == 0, N % 128 == 0.
+hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* ws, int M, int N,
+                           int K, uint16_t* y, hipStream_t s);
+bool fp8_linear_fits(int64_t K);
+
 }  // namespace mx

@@ -147,3 +147,28 @@ def test_debug_gemm_validation(L):
     assert L.mx_debug_gemm_f32(P(256), P(256), P(256), P(256), 4, 8, 64, P(256), None) == 2
     assert L.mx_debug_gemm_f32(None, P(256), P(256), P(256), 4, 8, 256, P(256), None) == 1
     assert L.mx_debug_gemm_f32(P(257), P(256), P(256), P(256), 4, 8, 256, P(256), None) == 3
+
+
+def test_fp8_linear_validation(L):
+    P = ctypes.c_void_p
+
+    def call(M, K, N, ws, x=P(256), w=P(256), y=P(256)):
+        return L.mx_fp8_block_linear(x, M, K, w, P(256), N, y, P(256), ws, None)
+    need = L.mx_fp8_block_linear_workspace_size(8, 256)
+    assert need >= 8 * 256 + 8 * 8
+    assert call(8, 200, 128, 1 << 30) == 2            # K % 128
+    assert call(8, 256, 100, 1 << 30) == 2            # N % 128
+    assert call(8, 8320, 128, 1 << 30) == 2           # K above 8192
+    assert call(0, 256, 128, 0) == 0                  # nothing to do
+    assert call(8, 256, 128, 1 << 30, x=None) == 1
+    assert call(8, 256, 128, 1 << 30, w=P(264)) == 3
+    assert call(8, 256, 128, need - 1) == 5
+    assert "workspace" in _err(L)
+
+
+def test_quantize_mxfp8_validation(L):
+    P = ctypes.c_void_p
+    assert L.mx_quantize_act(3, P(256), 4, 48, 0.0, P(256), P(256), None) == 2     # cols % 32
+    assert L.mx_quantize_act(3, P(256), 4, 64, 0.0, P(264), P(256), None) == 3     # codes alignment
+    assert L.mx_quantize_act(9, P(256), 4, 64, 0.0, P(256), P(256), None) == 4     # unknown format
+

@@ -159,3 +159,15 @@ def skewed(tokens=16384, n_experts=N_LOCAL_EXPERTS, k=TOP_K, seed=0,
     d["x"] = activations(seed + 1, tokens, hidden)
     d["ids"], d["w"] = zipf_routing(seed + 2, tokens, n_experts, k)
     return d
+
+
+def fp8_linear(tokens, n=HIDDEN, k=1536, seed=0, lo=118, hi=134):
+    """FP8 block-scaled linear: E4M3 weights [n, k] uniform over the finite codes,
+    E8M0 128 x 128 block scales uniform in [lo, hi] (weights seed), bf16
+    activations N(0, 1) [tokens, k] (seed + 1). The default shape is the pages'
+    FP8 matrix [7168, 1536]."""
+    rng = np.random.default_rng(seed)
+    w = e4m3_finite_codes(rng, (n, k))
+    ws = e8m0_scales(rng, (n // 128, k // 128), lo, hi)
+    return dict(w=w, ws=ws, x=activations(seed + 1, tokens, k))
+
