@@ -252,6 +252,36 @@ MX_API mx_status mx_debug_gemm_f32(const uint8_t* a, const uint8_t* a_s, const u
                             const uint8_t* b_s, int64_t M, int64_t N, int64_t K, float* c,
                             void* stream);
 
+/*
+ * mx_moe_runner -- the routed experts as a serving runner: its workspace is
+ * allocated once (hipMalloc at creation) and one mx_grouped_expert_mlp call
+ * over fixed device buffers is captured once into a hipGraph, which
+ * mx_moe_runner_replay launches on any stream. The pages' serving plan is a
+ * runner with pre-allocated buffers whose calls are CUDA-graph safe (page
+ * "Current Bug: vLLM produces empty/garbage output", section "Revised Plan",
+ * Phase 1).
+ *   create: the arguments of mx_grouped_expert_mlp (T >= 1) without workspace
+ *     and stream. It runs the call once eagerly (validating every argument; on
+ *     failure nothing is captured and *out stays NULL), synchronises, then
+ *     captures it on a private stream. requant_global and every pointer are
+ *     fixed in the graph. Fails with MX_ERR_VALUE while mx_profile_start() is on.
+ *   replay: the captured call on `stream`, reading the current contents of x,
+ *     topk_ids and topk_w (the caller refreshes them in place) and writing y.
+ *     Replays on one runner must not overlap (they share the workspace).
+ *   destroy: waits for the runner's stream, frees the graph and the workspace.
+ *     The caller must have finished its replays (synchronise their streams).
+ * The bound buffers must outlive the runner.
+ */
+typedef struct mx_moe_runner mx_moe_runner;
+MX_API mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
+                                      const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
+                                      const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
+                                      const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
+                                      const uint8_t* packed_scales, mx_format requant, float requant_global,
+                                      uint16_t* y, mx_moe_runner** out);
+MX_API mx_status mx_moe_runner_replay(mx_moe_runner* r, void* stream);
+MX_API mx_status mx_moe_runner_destroy(mx_moe_runner* r);
+
 /* Status text (static) and the calling thread's last error detail. */
 MX_API const char* mx_status_string(mx_status s);
 MX_API const char* mx_last_error(void);

@@ -45,6 +45,10 @@ SIGNATURES = {
     "mx_debug_gemm_f32": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "mx_fp8_block_linear": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
     "mx_fp8_block_linear_workspace_size": (_SZ, [_I64, _I64]),
+    "mx_moe_runner_create": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32,
+                                    _F, _P, ctypes.POINTER(_P)]),
+    "mx_moe_runner_replay": (_I32, [_P, _P]),
+    "mx_moe_runner_destroy": (_I32, [_P]),
     "mx_status_string": (ctypes.c_char_p, [_I32]),
     "mx_last_error": (ctypes.c_char_p, []),
     "mx_profile_start": (_I32, []),
@@ -247,3 +251,33 @@ def fp8_block_linear(x, w, w_s, out=None, workspace=None, stream=None):
     _check(lib().mx_fp8_block_linear(_ptr(x), M, K, _ptr(w), _ptr(w_s), N, _ptr(out), _ptr(ws), ws.numel(),
                                      _stream(stream)))
     return out
+
+
+class MoeRunner:
+    """mx_moe_runner: the routed experts over fixed device buffers, captured once
+    into a hipGraph. Refresh x, topk_ids and topk_w in place, then replay()."""
+
+    def __init__(self, x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4",
+                 requant_global: float = 0.0, out=None, packed_scales=None):
+        T, hidden = x.shape
+        k = topk_ids.shape[1]
+        E, inter = w1.shape[0], w1.shape[1]
+        self.out = out if out is not None else torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
+        # keep the bound tensors alive as long as the runner
+        self._bound = (x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, packed_scales, self.out)
+        h = _P()
+        _check(lib().mx_moe_runner_create(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
+                                          _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2), _ptr(w2s),
+                                          _ptr(packed_scales), _fmt(requant), float(requant_global),
+                                          _ptr(self.out), ctypes.byref(h)))
+        self._h = h
+
+    def replay(self, stream=None):
+        _check(lib().mx_moe_runner_replay(self._h, _stream(stream)))
+        return self.out
+
+    def close(self):
+        if self._h is not None and self._h.value is not None:
+            _check(lib().mx_moe_runner_destroy(self._h))
+        self._h = None
+

@@ -150,10 +150,10 @@ __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
   };
   // token scales of this lane's two 32-row blocks: one dword per row and stage
   const int r32 = lane & 31, half = lane >> 5;
-  const uint32_t* __restrict__ xs32 = (const uint32_t*)a.xs;
-  uint32_t xsoff[2];
+  const uint32_t* xsrow[2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) xsoff[g] = (uint32_t)(min(m0 + wm * 64 + g * 32 + r32, a.M - 1) * (K / 128));
+  for (int g = 0; g < 2; ++g)
+    xsrow[g] = (const uint32_t*)a.xs + (int64_t)min(m0 + wm * 64 + g * 32 + r32, a.M - 1) * (K / 128);
   uint32_t xsd[2], xsn[2];
 
   f32x16 acc[4][2];
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
 
   issue(0);
 #pragma unroll
-  for (int g = 0; g < 2; ++g) xsn[g] = xs32[(int64_t)xsoff[g]];
+  for (int g = 0; g < 2; ++g) xsn[g] = xsrow[g][0];
 
   for (int st = 0; st < nst; ++st) {
     // stage st is in LDS (all waves' copies), and every wave's reads of the
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
     if (st + 1 < nst) {
       issue(st + 1);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) xsn[g] = xs32[(int64_t)xsoff[g] + st + 1];
+      for (int g = 0; g < 2; ++g) xsn[g] = xsrow[g][st + 1];
     }
     const uint8_t* sw = smem + (st & 1) * F8_SLOT;
     const uint8_t* sx = sw + F8_OPND;

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <new>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -833,3 +834,103 @@ mx_status mx_debug_gemm_f32(const uint8_t* a, const uint8_t* a_s, const uint8_t*
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- runner
+// Routed-expert runner: workspace allocated once, the whole call captured once
+// into a hipGraph and replayed. The pages' serving plan is a runner with
+// pre-allocated buffers whose calls are CUDA-graph safe (page "Current Bug:
+// vLLM produces empty/garbage output", section "Revised Plan", Phase 1);
+// mx_grouped_expert_mlp allocates nothing and never synchronises the host, so
+// the runner only owns its workspace and a graph of one call over fixed device
+// buffers, whose contents the caller refreshes in place between replays.
+struct mx_moe_runner {
+  void* workspace = nullptr;
+  hipStream_t capture = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+void runner_release(mx_moe_runner* r) {
+  if (r->exec) hipGraphExecDestroy(r->exec);
+  if (r->graph) hipGraphDestroy(r->graph);
+  if (r->capture) hipStreamDestroy(r->capture);
+  if (r->workspace) hipFree(r->workspace);
+  delete r;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
+                               const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
+                               const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
+                               const uint8_t* w2, const uint8_t* w2_s, const uint8_t* packed_scales,
+                               mx_format requant, float requant_global, uint16_t* y, mx_moe_runner** out) {
+  MX_REQUIRE_PTR(out);
+  *out = nullptr;
+  if (T < 1) return fail(MX_ERR_SHAPE, "runner token count %lld must be positive", (long long)T);
+  if (g_prof.on) return fail(MX_ERR_VALUE, "profiling is on: stop it before capturing a runner");
+  MX_TRY(check_mlp_dims(T, hidden, inter));
+  if (E < 1 || E > ROUTE_MAX_EXPERTS || k < 1 || k > E) return fail(MX_ERR_SHAPE, "k %d / E %d out of range", k, E);
+  const size_t bytes = mx_grouped_expert_mlp_workspace_size(T, hidden, inter, k, E, requant);
+  mx_moe_runner* r = new (std::nothrow) mx_moe_runner;
+  if (r == nullptr) return fail(MX_ERR_HIP, "runner: out of host memory");
+  hipError_t e = hipMalloc(&r->workspace, bytes);
+  if (e != hipSuccess) {
+    runner_release(r);
+    return hip_fail(e, "runner workspace");
+  }
+  // a private stream of default priority for the capture
+  e = hipStreamCreateWithFlags(&r->capture, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    runner_release(r);
+    return hip_fail(e, "runner stream");
+  }
+  // one eager call first: it validates every argument (nothing is captured if
+  // it fails) and leaves y valid
+  mx_status st = mx_grouped_expert_mlp(x, T, hidden, inter, topk_ids, topk_w, k, E, w1, w1_s, w3, w3_s, w2, w2_s,
+                                       packed_scales, requant, requant_global, y, r->workspace, bytes, r->capture);
+  if (st != MX_OK) {
+    runner_release(r);
+    return st;
+  }
+  e = hipStreamSynchronize(r->capture);
+  if (e == hipSuccess) e = hipStreamBeginCapture(r->capture, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    runner_release(r);
+    return hip_fail(e, "runner capture");
+  }
+  st = mx_grouped_expert_mlp(x, T, hidden, inter, topk_ids, topk_w, k, E, w1, w1_s, w3, w3_s, w2, w2_s,
+                             packed_scales, requant, requant_global, y, r->workspace, bytes, r->capture);
+  e = hipStreamEndCapture(r->capture, &r->graph);
+  if (st != MX_OK) {
+    runner_release(r);
+    return st;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&r->exec, r->graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    runner_release(r);
+    return hip_fail(e, "runner graph");
+  }
+  *out = r;
+  return ok();
+}
+
+mx_status mx_moe_runner_replay(mx_moe_runner* r, void* stream) {
+  MX_REQUIRE_PTR(r);
+  MX_HIP(hipGraphLaunch(r->exec, (hipStream_t)stream), "runner replay");
+  return ok();
+}
+
+mx_status mx_moe_runner_destroy(mx_moe_runner* r) {
+  if (r == nullptr) return ok();
+  MX_HIP(hipStreamSynchronize(r->capture), "runner destroy");
+  runner_release(r);
+  return ok();
+}
+
+}  // extern "C"
+

@@ -172,3 +172,18 @@ def test_quantize_mxfp8_validation(L):
     assert L.mx_quantize_act(3, P(256), 4, 64, 0.0, P(264), P(256), None) == 3     # codes alignment
     assert L.mx_quantize_act(9, P(256), 4, 64, 0.0, P(256), P(256), None) == 4     # unknown format
 
+
+def test_runner_validation(L):
+    P = ctypes.c_void_p
+    z = [P(256)] * 6
+    out = P()
+
+    def create(T, k, E, x=P(256), o=True):
+        return L.mx_moe_runner_create(x, T, 256, 128, P(256), P(256), k, E, *z, None, 0, 0.0, P(256),
+                                      ctypes.byref(out) if o else None)
+    assert create(8, 2, 4, o=False) == 1
+    assert create(0, 2, 4) == 2 and out.value is None
+    assert create(8, 5, 4) == 2
+    assert L.mx_moe_runner_replay(None, None) == 1
+    assert L.mx_moe_runner_destroy(None) == 0
+

@@ -58,13 +58,14 @@ def test_graph_shared_expert(mx, M):
     _check_replays(g, y, ref, torch.empty(1 << 20, device="cuda"))
 
 
-@pytest.mark.parametrize("requant", ["mxfp4", "nvfp4"])
-def test_graph_grouped(mx, requant):
-    d = W.grouped(tokens=300, n_experts=6, k=3, seed=9, hidden=512, inter=256)
+@pytest.mark.parametrize("requant,T", [("mxfp4", 300), ("nvfp4", 300), ("mxfp4", 4), ("nvfp4", 20)])
+def test_graph_grouped(mx, requant, T):
+    """Tiled GEMMs (300 tokens) and the routed weight-streaming kernels (few rows per expert)."""
+    d = W.grouped(tokens=T, n_experts=6, k=3, seed=9, hidden=512, inter=256)
     w = {n: t(d[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s", "ids", "w")}
     x = bf16_t(d["x"])
-    y = torch.empty((300, 512), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(mx.grouped_expert_mlp_workspace_size(300, 512, 256, 3, 6, requant), dtype=torch.uint8,
+    y = torch.empty((T, 512), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.grouped_expert_mlp_workspace_size(T, 512, 256, 3, 6, requant), dtype=torch.uint8,
                      device="cuda")
     g_scale = 2.0 ** -6
     fn = lambda: mx.grouped_expert_mlp(x, w["ids"], w["w"], w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
@@ -86,3 +87,49 @@ def test_graph_dequant_quant(mx):
     ref = bits(out)
     g = _capture(fn)
     _check_replays(g, out, ref, torch.empty(1 << 20, device="cuda"))
+
+
+def test_graph_fp8_linear(mx):
+    d = W.fp8_linear(300, 384, 512, seed=4)
+    x, w, wsc = bf16_t(d["x"]), t(d["w"]), t(d["ws"])
+    y = torch.empty((300, 384), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.fp8_block_linear_workspace_size(300, 512), dtype=torch.uint8, device="cuda")
+    fn = lambda: mx.fp8_block_linear(x, w, wsc, out=y, workspace=ws)
+    fn()
+    torch.cuda.synchronize()
+    ref = bits(y)
+    g = _capture(fn)
+    _check_replays(g, y, ref, torch.empty(1 << 20, device="cuda"))
+
+
+@pytest.mark.parametrize("requant,T", [("mxfp4", 300), ("nvfp4", 20)])
+def test_runner_replays_match_eager(mx, requant, T):
+    """mx_moe_runner: buffers bound once, graph captured once; after refreshing
+    x, ids and weights in place each replay equals an eager call on the new
+    contents, bit for bit, also on another stream."""
+    E, k, H, I = 6, 3, 512, 256
+    d0 = W.grouped(tokens=T, n_experts=E, k=k, seed=9, hidden=H, inter=I)
+    w = {n: t(d0[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")}
+    x, ids, gw = bf16_t(d0["x"]), t(d0["ids"]), t(d0["w"])
+    g_scale = 2.0 ** -6
+    r = mx.MoeRunner(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"], requant=requant,
+                     requant_global=g_scale)
+    try:
+        for seed in (9, 21, 33):
+            d = W.grouped(tokens=T, n_experts=E, k=k, seed=seed, hidden=H, inter=I)
+            x.copy_(bf16_t(d["x"]))
+            ids.copy_(t(d["ids"]))
+            gw.copy_(t(d["w"]))
+            torch.cuda.synchronize()
+            ref = bits(mx.grouped_expert_mlp(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
+                                             requant=requant, requant_global=g_scale))
+            r.out.zero_()
+            s = torch.cuda.Stream() if seed == 33 else torch.cuda.current_stream()
+            s.wait_stream(torch.cuda.current_stream())
+            r.replay(stream=s)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(r.out), ref), seed
+    finally:
+        torch.cuda.synchronize()
+        r.close()
+
