@@ -394,12 +394,13 @@ __global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__
 //    sorted row order.
 //  * L2 reads re-quantised h rows in sorted order: MXFP4 codes through the
 //    scaled FP4 MFMA, or (NVFP4 re-quantisation, whose E4M3 per-16 scale an
-//    E8M0 MFMA scale cannot carry) the exactly dequantised bf16 rows through
-//    V_MFMA_F32_16X16X32_BF16, with the weight codes converted exactly to bf16
-//    in registers. The output row of pair p is o[row_slot[p]] =
+//    E8M0 MFMA scale cannot carry) NVFP4 codes and E4M3 scales converted in
+//    registers to code * s in bf16 (exact: at most 6 significant bits), with
+//    the weight codes converted exactly to bf16 too, through
+//    V_MFMA_F32_16X16X32_BF16. The output row of pair p is o[row_slot[p]] =
 //    bf16(acc * (scale * row_weight[p])), scale 1 or the NVFP4 global g, as in
 //    the GEMM's epilogue.
-enum RoutedOperand { RT_FP4 = 0, RT_BF16 = 1 };
+enum RoutedOperand { RT_FP4 = 0, RT_NV = 1 };
 
 struct RoutedLds {
   uint8_t wscale[16 * 256];     // the tile rows' E8M0 bytes, K <= 8192
@@ -411,16 +412,27 @@ __device__ __forceinline__ uint4 dequant16_bf16(uint32_t codes, float scale) {
                     dequant_pair<3>(codes, scale));
 }
 
+// Eight NVFP4 codes (one dword) times their E4M3 block scale s -> eight bf16,
+// exact: code * s has at most 2 + 4 significant bits.
+__device__ __forceinline__ uint4 nv8_bf16(uint32_t d, float s) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+  return make_uint4(bf16x2_rne(v0[0] * s, v0[1] * s), bf16x2_rne(v1[0] * s, v1[1] * s),
+                    bf16x2_rne(v2[0] * s, v2[1] * s), bf16x2_rne(v3[0] * s, v3[1] * s));
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // The expert's `rows` token rows times one 16-row weight tile. Token row i of
 // the expert is row gather[base + i] (gather != nullptr) or base + i of the
-// operand: FP4 codes `aq` [.., K/2] with E8M0 scales `as` [.., K/32], or bf16
-// `ad` [.., K]. `emit(c0, tot)` runs in wave 0 for every chunk of 16 rows
+// operand: FP4 codes `aq` [.., K/2] with E8M0 scales `as` [.., K/32] (RT_FP4)
+// or E4M3 scales `as` [.., K/16] (RT_NV). `emit(c0, tot)` runs in wave 0 for every chunk of 16 rows
 // starting at c0, with lane (row c0 + lane%16, tile rows 4*(lane/16) + v).
 template <int OP, int NS, class Emit>
 __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
-                                                 const uint16_t* __restrict__ ad, const int32_t* __restrict__ gather,
+                                                 const int32_t* __restrict__ gather,
                                                  int base, int rows, int K, RowPair wp, RowPair sp, RoutedLds& L,
                                                  Emit&& emit) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -465,25 +477,28 @@ __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq,
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc, 4, 4, 0, sa[k], 0, sb[k]);
       }
     } else {
-      // A lane's 32 K values of a step (K = 128 s + 32 q + 0..31) feed four
-      // 16x16x32 MFMAs, values 8 j .. 8 j + 7 in the j-th; the token row uses
-      // the same order, so each MFMA contracts matching K.
-      uint4 b[NS][4];
+      // A lane's 32 K values of a step (K = 128 s + 32 q + 0..31, code dwords
+      // j = 0..3 of 8 values each, NVFP4 blocks j / 2) feed four 16x16x32
+      // MFMAs, dword j in the j-th; the token row uses the same order, so each
+      // MFMA contracts matching K.
+      uint4 b[NS];
+      uint32_t bs[NS];
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         const int s = min(s0 + k, ksteps - 1);
-        const uint4* src = (const uint4*)(ad + tok * K + s * 128 + q * 32);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[k][j] = src[j];
+        b[k] = *(const uint4*)(aq + tok * kb + s * 64 + q * 16);
+        bs[k] = *(const uint16_t*)(as + tok * (K / 16) + s * 8 + q * 2);
       }
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         const float scale = e8m0_to_f32((uint32_t)sa[k]);
         const uint32_t wv[4] = {wa[k].x, wa[k].y, wa[k].z, wa[k].w};
+        const uint32_t hv[4] = {b[k].x, b[k].y, b[k].z, b[k].w};
+        const float hs0 = e4m3_to_f32(bs[k] & 0xFFu), hs1 = e4m3_to_f32(bs[k] >> 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint4 av = k < n ? dequant16_bf16(wv[j], scale) : z;
-          const uint4 bv = tok_ok ? b[k][j] : z;
+          const uint4 bv = tok_ok ? nv8_bf16(hv[j], j < 2 ? hs0 : hs1) : z;
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                         __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
         }
@@ -521,7 +536,7 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__
   const int64_t we = (int64_t)e * I * kb, se = (int64_t)e * I * ks;
   const RowPair wp{w1 + we + j0 * kb, w3 + we + j0 * kb};
   const RowPair sp{w1s + se + j0 * ks, w3s + se + j0 * ks};
-  routed_tile_rows<RT_FP4, NS>(xq, xs, nullptr, row_token, base, rows, H, wp, sp, L, [&](int c0, const f32x4& acc) {
+  routed_tile_rows<RT_FP4, NS>(xq, xs, row_token, base, rows, H, wp, sp, L, [&](int c0, const f32x4& acc) {
     const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
     float up[4];
 #pragma unroll
@@ -535,11 +550,10 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__
 }
 
 // L2 of expert blockIdx.y for 16 output columns n0 .. n0+15, from the
-// re-quantised h rows (FP4 codes + E8M0, or bf16): o[row_slot[r]][n] =
+// re-quantised h rows (FP4 codes + E8M0 or E4M3 scales): o[row_slot[r]][n] =
 // bf16(acc * (scale * row_weight[r])).
 template <int OP, int NS>
 __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
-                                                     const uint16_t* __restrict__ hd,
                                                      const int32_t* __restrict__ expert_off,
                                                      const int32_t* __restrict__ row_slot,
                                                      const float* __restrict__ row_weight, float scale, int H, int I,
@@ -554,7 +568,7 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__
   const int64_t we = (int64_t)e * H * kb, se = (int64_t)e * H * ks;
   const RowPair wp{w2 + we + n0 * kb, w2 + we + (n0 + 8) * kb};
   const RowPair sp{w2s + se + n0 * ks, w2s + se + (n0 + 8) * ks};
-  routed_tile_rows<OP, NS>(hq, hs, hd, nullptr, base, rows, I, wp, sp, L, [&](int c0, const f32x4& acc) {
+  routed_tile_rows<OP, NS>(hq, hs, nullptr, base, rows, I, wp, sp, L, [&](int c0, const f32x4& acc) {
     const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
     if (c0 + t < rows) {
       const int r = base + c0 + t;
@@ -656,7 +670,7 @@ void launch_routed_l1_ns(const RoutedArgs& a, hipStream_t s) {
 
 template <int OP, int NS>
 void launch_routed_l2_ns(const RoutedArgs& a, hipStream_t s) {
-  k_routed_l2<OP, NS><<<dim3(a.H / 16, a.E), DT, 0, s>>>(a.hq, a.hs, a.hd, a.expert_off, a.row_slot, a.row_weight,
+  k_routed_l2<OP, NS><<<dim3(a.H / 16, a.E), DT, 0, s>>>(a.hq, a.hs, a.expert_off, a.row_slot, a.row_weight,
                                                           a.scale, a.H, a.I, a.w2, a.w2s, a.o);
 }
 
@@ -761,7 +775,7 @@ hipError_t launch_routed_l1(const RoutedArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_routed_l2(const RoutedArgs& a, hipStream_t s) {
-  if (a.hd != nullptr) launch_routed_l2_op<RT_BF16>(a, s);
+  if (a.nvfp4) launch_routed_l2_op<RT_NV>(a, s);
   else launch_routed_l2_op<RT_FP4>(a, s);
   return hipGetLastError();
 }

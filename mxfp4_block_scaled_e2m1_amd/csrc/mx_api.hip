@@ -160,12 +160,11 @@ DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
 //
 // With few rows per expert (routed_stream_fits) the weight-streaming kernels
 // run instead of the GEMMs: xq, xs, the route buffers, h (bf16), hq, hs
-// (row-major), with NVFP4 re-quantisation hd (h dequantised at global scale
-// 1, bf16), then o; no xs_pk.
+// (row-major, E8M0 per 32 or E4M3 per 16), then o; no xs_pk.
 struct GroupWs {
   bool stream;
   uint8_t *xq, *xs, *hq, *hs, *xs_pk;
-  uint16_t *o, *h, *hd;
+  uint16_t *o, *h;
   RouteBuffers rb;
   size_t bytes;
 };
@@ -179,7 +178,7 @@ GroupWs group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E, mx_f
   const int64_t nblocks = (P + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
   const int64_t mtiles = max_route_mtiles(P, E);
   w.stream = routed_stream_fits(T, H, I, k, E, rq == MX_FMT_NVFP4);
-  w.h = w.hd = nullptr;
+  w.h = nullptr;
   w.xs_pk = nullptr;
   w.xq = (uint8_t*)c.take((size_t)(T * H / 2));
   w.xs = (uint8_t*)c.take((size_t)(T * H / 32));
@@ -193,7 +192,6 @@ GroupWs group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E, mx_f
     w.h = (uint16_t*)c.take((size_t)(P * I * 2));
     w.hq = (uint8_t*)c.take((size_t)(P * I / 2));
     w.hs = (uint8_t*)c.take(rq == MX_FMT_NVFP4 ? (size_t)(P * I / 16) : (size_t)(P * I / 32));
-    if (rq == MX_FMT_NVFP4) w.hd = (uint16_t*)c.take((size_t)(P * I * 2));
     w.o = (uint16_t*)c.take((size_t)(P * H * 2));
     w.bytes = c.off;
     return w;
@@ -586,15 +584,13 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
     ra.row_token = w.rb.row_token; ra.row_slot = w.rb.row_slot; ra.expert_off = w.rb.expert_off;
     ra.row_weight = w.rb.row_weight;
     ra.w1 = w1; ra.w1s = w1_s; ra.w3 = w3; ra.w3s = w3_s; ra.w2 = w2; ra.w2s = w2_s;
-    ra.h = w.h; ra.hq = w.hq; ra.hs = w.hs; ra.hd = w.hd;
+    ra.h = w.h; ra.hq = w.hq; ra.hs = w.hs; ra.nvfp4 = requant == MX_FMT_NVFP4;
     ra.scale = requant == MX_FMT_NVFP4 ? requant_global : 1.0f;
     ra.o = w.o;
     MX_HIP(phase("l1_stream", s, [&] { return launch_routed_l1(ra, s); }), "l1_stream");
     MX_HIP(phase("requant_h", s, [&] {
              if (requant == MX_FMT_MXFP4) return launch_quant_mxfp4(w.h, P, inter, w.hq, w.hs, s);
-             hipError_t e = launch_quant_nvfp4(w.h, P, inter, requant_global, w.hq, w.hs, s);
-             if (e != hipSuccess) return e;
-             return launch_dequant_nvfp4(w.hq, w.hs, 1.0f, P, inter, w.hd, s);
+             return launch_quant_nvfp4(w.h, P, inter, requant_global, w.hq, w.hs, s);
            }), "requant_h");
     MX_HIP(phase("l2_stream", s, [&] { return launch_routed_l2(ra, s); }), "l2_stream");
     MX_HIP(phase("combine", s, [&] { return launch_combine(w.o, topk_ids, T, k, E, H, y, s); }), "combine");

@@ -162,9 +162,9 @@ hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8
 // NVFP4 re-quantisation): the weights of each
 // expert with rows streamed once by two kernels (see decode.hip). L1 writes
 // h (bf16, [P, inter], sorted row order); the caller re-quantises it into
-// hq/hs row-major (MXFP4), or into NVFP4 and then dequantises it at global
-// scale 1 into hd (bf16, exact), in which case L2 takes hd and multiplies by
-// `scale` = g. L2 writes o[row_slot[p]] rows, as the GEMM's routed epilogue.
+// hq/hs row-major, MXFP4 or (nvfp4) NVFP4, in which case L2 converts code *
+// s to bf16 and multiplies by `scale` = g. L2 writes o[row_slot[p]] rows, as
+// the GEMM's routed epilogue.
 struct RoutedArgs {
   int H, I, E;
   const uint8_t *xq, *xs;
@@ -173,7 +173,7 @@ struct RoutedArgs {
   const uint8_t *w1, *w1s, *w3, *w3s, *w2, *w2s;
   uint16_t* h;
   const uint8_t *hq, *hs;
-  const uint16_t* hd;   // NVFP4 re-quantisation: dequantised h, else nullptr
+  bool nvfp4;           // hq/hs are NVFP4 (E4M3 per 16), else MXFP4
   float scale;
   uint16_t* o;
 };
