@@ -35,7 +35,7 @@ __all__ = [
     "e2m1_code_rne_sat", "mxfp4_quantize",
     "e4m3_rne_satfinite", "e4m3_encode_exact", "nvfp4_quantize", "nvfp4_dequant_f64",
     "gemm_f64", "silu_mul_bf16", "expert_mlp", "grouped_expert_mlp",
-    "nvfp4_warmup_global", "mxfp8_quantize", "mxfp8_dequant_f64", "fp8_block_linear",
+    "nvfp4_warmup_global", "mxfp8_quantize", "mxfp8_dequant_f64", "fp8_block_linear", "fp8_expert_mlp",
 ]
 
 # ---------------------------------------------------------------------------
@@ -504,3 +504,24 @@ def grouped_expert_mlp(x_bits, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s,
         y_pair = gemm_f64(hd, mxfp4_dequant_f64(w2[e], w2s[e]))
         np.add.at(acc, t_idx, wts[t_idx, k_idx][:, None] * y_pair)
     return f64_to_bf16(acc)
+
+
+def fp8_expert_mlp(x_bits, w1, w1s, w3, w3s, w2, w2s):
+    """The shared expert in the original checkpoint's FP8 format: three FP8 block-
+    scaled linears around SiLU * up.
+
+    g = fp8_block_linear(x, W1), u = fp8_block_linear(x, W3) (bf16 outputs),
+    h = bf16(silu(g) * u) evaluated in fp64 from those bf16 values, and
+    y = fp8_block_linear(h, W2). W1, W3 [inter, hidden] and W2 [hidden, inter]
+    are FP8 E4M3 with 128 x 128 E8M0 block scales ([Q0508] "Status": the
+    shared experts are FP8; [SRV0511] "Architecture Map": they run on the FP8
+    linear). The MLP steps are those of [BUG0518] "Revised Plan", Phase 1.
+    Reading: each linear rounds its output to bf16, as a standalone FP8 linear
+    does, so g and u are bf16 before the SiLU here (unlike the fused MXFP4
+    epilogue); h is re-quantised by the linear's MXFP8 activation quantiser.
+    """
+    g = fp8_block_linear(x_bits, w1, w1s)
+    u = fp8_block_linear(x_bits, w3, w3s)
+    h = silu_mul_bf16(bf16_to_f64(g), bf16_to_f64(u))
+    return fp8_block_linear(h, w2, w2s)
+

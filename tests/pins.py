@@ -825,3 +825,29 @@ def check_grouped_reductions(O, seed=43):
     # subset of tokens equals the same rows of the full result
     ysub = O.grouped_expert_mlp(x, ids, wts, tokens=[3, 1], **w)
     assert np.array_equal(ysub, y[[3, 1]])
+
+
+def check_fp8_mlp_bruteforce(O, seed=71):
+    """The FP8 shared-expert MLP on a tiny shape: every step by hand from pinned
+    pieces (the FP8 linear, SiLU) and the table-search bf16 rounding, plus the
+    composition of the oracle's own pinned linears."""
+    rng = np.random.default_rng(seed)
+    M, H, I = 3, 256, 128
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    w1 = rng.choice(finite, size=(I, H)).astype(np.uint8)
+    w3 = rng.choice(finite, size=(I, H)).astype(np.uint8)
+    w2 = rng.choice(finite, size=(H, I)).astype(np.uint8)
+    s1 = rng.integers(110, 118, (1, 2)).astype(np.uint8)
+    s3 = rng.integers(110, 118, (1, 2)).astype(np.uint8)
+    s2 = rng.integers(110, 118, (2, 1)).astype(np.uint8)
+    x = (rng.standard_normal((M, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = O.fp8_expert_mlp(x, w1, s1, w3, s3, w2, s2)
+    g = O.fp8_block_linear(x, w1, s1)
+    u = O.fp8_block_linear(x, w3, s3)
+    gv = np.array([bf16_value(b) for b in g.ravel()])
+    uv = np.array([bf16_value(b) for b in u.ravel()])
+    hv = [float(Fraction(a) / (1 + Fraction(math.exp(-a))) * Fraction(b)) for a, b in zip(gv, uv)]
+    h = bf16_rne_reference(np.array(hv)).reshape(M, I)
+    assert np.array_equal(O.fp8_block_linear(h, w2, s2), y)
+    assert y.shape == (M, H) and np.all(np.isfinite(((y.astype(np.uint32) << 16).view(np.float32))))
+

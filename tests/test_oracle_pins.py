@@ -37,6 +37,7 @@ CHECKS = [
     pins.check_mxfp8_roundtrip,
     pins.check_fp8_linear_bruteforce,
     pins.check_fp8_linear_unit_rows,
+    pins.check_fp8_mlp_bruteforce,
 ]
 
 
