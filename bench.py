@@ -207,6 +207,21 @@ def fp8_linear(torch, mx, workloads):
             "gemm_ms": round(gemm_ms, 4), "gemm_TFLOP/s": round(flops / gemm_ms / 1e9, 2),
             "gemm_frac_of_fp8_peak": round(flops / gemm_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
             "quant_ms": round(phases["quant_x8"][0] / phases["quant_x8"][1], 4)}
+    # the FP8 shared expert (three FP8 linears around SiLU * up), 4096 tokens
+    H, I = workloads.HIDDEN, workloads.INTER
+    d = workloads.fp8_expert(M, H, I, seed=0)
+    wd = {n: torch.from_numpy(d[n]).cuda() for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")}
+    x = bf16_dev(torch, d["x"])
+    y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.fp8_expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
+    fn = lambda: mx.fp8_expert_mlp(x, wd["w1"], wd["w1s"], wd["w3"], wd["w3s"], wd["w2"], wd["w2s"], out=y,
+                                   workspace=ws)
+    ms, phases = time_steps(torch, fn, 20, 3, profile=(mx.profile_start, mx.profile_stop))
+    flops = 6.0 * M * H * I
+    out[f"fp8_shared_expert_M{M}"] = {
+        "ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
+        "frac_of_fp8_peak": round(flops / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+        "phases_ms_per_step": {k: round(v[0] / 20, 4) for k, v in phases.items()}}
     return out
 
 

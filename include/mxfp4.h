@@ -243,6 +243,25 @@ MX_API mx_status mx_fp8_block_linear(const uint16_t* x, int64_t M, int64_t K, co
 MX_API size_t mx_fp8_block_linear_workspace_size(int64_t M, int64_t K);
 
 /*
+ * mx_fp8_expert_mlp -- the shared expert in the original checkpoint's FP8
+ * format (page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", "Status"):
+ *   g = FP8LIN(x, w1), u = FP8LIN(x, w3), h = bf16(silu(g) * u), y = FP8LIN(h, w2)
+ * with FP8LIN the mx_fp8_block_linear computation (MXFP8 activations, bf16
+ * output), so g and u are bf16 before the SiLU.
+ *   x  [M, hidden] bf16; y [M, hidden] bf16
+ *   w1, w3 [inter, hidden] e4m3fn, scales [inter/128, hidden/128] E8M0
+ *   w2 [hidden, inter] e4m3fn, scales [hidden/128, inter/128] E8M0
+ * hidden, inter multiples of 128 and <= 8192. workspace: at least
+ * mx_fp8_expert_mlp_workspace_size(M, hidden, inter) bytes, 256-byte aligned.
+ * Alignment: x, y and weight codes 16 bytes.
+ */
+MX_API mx_status mx_fp8_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter,
+                                   const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
+                                   const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* y,
+                                   void* workspace, size_t ws_bytes, void* stream);
+MX_API size_t mx_fp8_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter);
+
+/*
  * mx_debug_gemm_f32 -- test hook, not part of the hot path: C[M, N] = A . B^T in fp32
  * for MXFP4 A (codes [M, K/2], scales [M, K/32]) and B (codes [N, K/2], scales
  * [N, K/32]) through the same scaled-MFMA kernel as the MLP. K % 128 == 0,

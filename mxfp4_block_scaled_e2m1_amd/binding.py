@@ -45,6 +45,8 @@ SIGNATURES = {
     "mx_debug_gemm_f32": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "mx_fp8_block_linear": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
     "mx_fp8_block_linear_workspace_size": (_SZ, [_I64, _I64]),
+    "mx_fp8_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mx_fp8_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "mx_moe_runner_create": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32,
                                     _F, _P, ctypes.POINTER(_P)]),
     "mx_moe_runner_replay": (_I32, [_P, _P]),
@@ -250,6 +252,22 @@ def fp8_block_linear(x, w, w_s, out=None, workspace=None, stream=None):
     ws = _workspace(fp8_block_linear_workspace_size(M, K), x.device, workspace)
     _check(lib().mx_fp8_block_linear(_ptr(x), M, K, _ptr(w), _ptr(w_s), N, _ptr(out), _ptr(ws), ws.numel(),
                                      _stream(stream)))
+    return out
+
+
+def fp8_expert_mlp_workspace_size(M, hidden, inter) -> int:
+    return int(lib().mx_fp8_expert_mlp_workspace_size(M, hidden, inter))
+
+
+def fp8_expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, out=None, workspace=None, stream=None):
+    """mx_fp8_expert_mlp: the FP8 shared expert on bf16 x [M, hidden] -> bf16 y [M, hidden]."""
+    M, hidden = x.shape
+    inter = w1.shape[0]
+    if out is None:
+        out = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+    ws = _workspace(fp8_expert_mlp_workspace_size(M, hidden, inter), x.device, workspace)
+    _check(lib().mx_fp8_expert_mlp(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2),
+                                   _ptr(w2s), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

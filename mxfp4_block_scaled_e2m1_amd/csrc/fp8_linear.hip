@@ -85,6 +85,26 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const uint4* __restrict__ x
   }
 }
 
+// ------------------------------------------------------------------ SiLU * up
+// h = bf16(silu(g) * u) from bf16 g and u, 8 elements per thread: the step
+// between the FP8 gate/up linears and the down linear of the FP8 shared expert
+// (page "Current Bug: vLLM produces empty/garbage output", section "Revised
+// Plan", Phase 1). silu_mul is the fused MXFP4 epilogue's fp32 evaluation.
+__global__ __launch_bounds__(256) void k_silu_mul_bf16(const uint4* __restrict__ g, const uint4* __restrict__ u,
+                                                       uint4* __restrict__ h, int64_t n8) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const uint4 a = g[i], b = u[i];
+    const uint32_t ga[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r[q] = bf16x2_rne(silu_mul(bf16_to_f32(ga[q] & 0xFFFFu), bf16_to_f32(ub[q] & 0xFFFFu)),
+                        silu_mul(bf16_to_f32(ga[q] >> 16), bf16_to_f32(ub[q] >> 16)));
+    h[i] = make_uint4(r[0], r[1], r[2], r[3]);
+  }
+}
+
 // ------------------------------------------------------------------ GEMM
 struct F8Args {
   const uint8_t* w;      // [N, K] E4M3
@@ -262,5 +282,14 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* xs, const uint8_t* 
 }
 
 bool fp8_linear_fits(int64_t K) { return K / F8_BK <= F8_MAX_KB; }
+
+hipError_t launch_silu_mul_bf16(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* h, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  int64_t grid = (n8 + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  k_silu_mul_bf16<<<(int)grid, 256, 0, s>>>((const uint4*)g, (const uint4*)u, (uint4*)h, n8);
+  return hipGetLastError();
+}
 
 }  // namespace mx

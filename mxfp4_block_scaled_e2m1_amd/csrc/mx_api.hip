@@ -799,6 +799,61 @@ mx_status mx_fp8_block_linear(const uint16_t* x, int64_t M, int64_t K, const uin
   return ok();
 }
 
+size_t mx_fp8_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter) {
+  if (M < 0 || hidden < 0 || inter < 0) return 0;
+  Carve c(nullptr);
+  c.take((size_t)(M * hidden));
+  c.take((size_t)(M * (hidden / 32)));
+  for (int i = 0; i < 3; ++i) c.take((size_t)(M * inter * 2));   // g, u, h
+  c.take((size_t)(M * inter));
+  c.take((size_t)(M * (inter / 32)));
+  return c.off;
+}
+
+mx_status mx_fp8_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, const uint8_t* w1,
+                            const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s, const uint8_t* w2,
+                            const uint8_t* w2_s, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MX_TRY(check_mlp_dims(M, hidden, inter));
+  if (!fp8_linear_fits(hidden) || !fp8_linear_fits(inter))
+    return fail(MX_ERR_SHAPE, "hidden %lld / inter %lld above 8192", (long long)hidden, (long long)inter);
+  if (M * hidden > ((int64_t)1 << 40) || M * inter > ((int64_t)1 << 40)) return fail(MX_ERR_SHAPE, "matrix too large");
+  if (M == 0) return ok();
+  MX_REQUIRE_PTR(x);
+  MX_REQUIRE_PTR(y);
+  MX_REQUIRE_ALIGN(x, 16);
+  MX_REQUIRE_ALIGN(y, 16);
+  const uint8_t* wp[6] = {w1, w1_s, w3, w3_s, w2, w2_s};
+  for (int i = 0; i < 6; ++i)
+    if (wp[i] == nullptr) return fail(MX_ERR_NULL, "FP8 weight or scale pointer %d is NULL", i);
+  MX_REQUIRE_ALIGN(w1, 16);
+  MX_REQUIRE_ALIGN(w3, 16);
+  MX_REQUIRE_ALIGN(w2, 16);
+  MX_REQUIRE_PTR(workspace);
+  MX_REQUIRE_ALIGN(workspace, 256);
+  const size_t need = mx_fp8_expert_mlp_workspace_size(M, hidden, inter);
+  if (ws_bytes < need) return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  Carve c(workspace);
+  uint8_t* xq = (uint8_t*)c.take((size_t)(M * hidden));
+  uint8_t* xs = (uint8_t*)c.take((size_t)(M * (hidden / 32)));
+  uint16_t* g = (uint16_t*)c.take((size_t)(M * inter * 2));
+  uint16_t* u = (uint16_t*)c.take((size_t)(M * inter * 2));
+  uint16_t* h = (uint16_t*)c.take((size_t)(M * inter * 2));
+  uint8_t* hq = (uint8_t*)c.take((size_t)(M * inter));
+  uint8_t* hs = (uint8_t*)c.take((size_t)(M * (inter / 32)));
+  const int m = (int)M, H = (int)hidden, I = (int)inter;
+  MX_HIP(phase("quant_x8", s, [&] { return launch_quant_mxfp8(x, M, hidden, xq, xs, s); }), "quant_x8");
+  MX_HIP(phase("fp8_gemm", s, [&] {
+           hipError_t e = launch_fp8_gemm(xq, xs, w1, w1_s, m, I, H, g, s);
+           if (e != hipSuccess) return e;
+           return launch_fp8_gemm(xq, xs, w3, w3_s, m, I, H, u, s);
+         }), "fp8_gemm_l1");
+  MX_HIP(phase("silu_mul", s, [&] { return launch_silu_mul_bf16(g, u, M * inter, h, s); }), "silu_mul");
+  MX_HIP(phase("quant_x8", s, [&] { return launch_quant_mxfp8(h, M, inter, hq, hs, s); }), "quant_h8");
+  MX_HIP(phase("fp8_gemm", s, [&] { return launch_fp8_gemm(hq, hs, w2, w2_s, m, H, I, y, s); }), "fp8_gemm_l2");
+  return ok();
+}
+
 mx_status mx_debug_gemm_f32(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
                             int64_t M, int64_t N, int64_t K, float* c, void* stream) {
   hipStream_t s = (hipStream_t)stream;

@@ -188,5 +188,7 @@ hipError_t launch_quant_mxfp8(const uint16_t* x, int64_t rows, int64_t cols, uin
 hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* ws, int M, int N,
                            int K, uint16_t* y, hipStream_t s);
 bool fp8_linear_fits(int64_t K);
+// h = bf16(silu(g) * u) elementwise over n values (n % 8 == 0, 16-byte aligned).
+hipError_t launch_silu_mul_bf16(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* h, hipStream_t s);
 
 }  // namespace mx

@@ -187,3 +187,18 @@ def test_runner_validation(L):
     assert L.mx_moe_runner_replay(None, None) == 1
     assert L.mx_moe_runner_destroy(None) == 0
 
+
+def test_fp8_expert_mlp_validation(L):
+    P = ctypes.c_void_p
+    z = [P(256)] * 6
+
+    def call(M, H, I, ws, x=P(256)):
+        return L.mx_fp8_expert_mlp(x, M, H, I, *z, P(256), P(256), ws, None)
+    need = L.mx_fp8_expert_mlp_workspace_size(8, 256, 128)
+    assert need > 0
+    assert call(8, 200, 128, 1 << 30) == 2
+    assert call(8, 256, 8320, 1 << 30) == 2
+    assert call(0, 256, 128, 0) == 0
+    assert call(8, 256, 128, 1 << 30, x=None) == 1
+    assert call(8, 256, 128, need - 1) == 5
+

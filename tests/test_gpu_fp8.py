@@ -11,6 +11,8 @@ from gpu_util import bf16_f64, bf16_t, bits, t
 
 pytestmark = pytest.mark.gpu
 
+H_TINY = 1e-30   # fp32 exp(-g) overflows for g < -88.7: silu(g) * u below ~1e-36 flushes to +-0
+
 
 @pytest.fixture(scope="module")
 def mx():
@@ -125,3 +127,54 @@ def test_fp8_linear_empty(mx):
     y = mx.fp8_block_linear(bf16_t(d["x"][:0]), t(d["w"]), t(d["ws"]))
     torch.cuda.synchronize()
     assert y.shape == (0, 128)
+
+
+# ---------------------------------------------------------------- FP8 shared expert
+FP8_WN = ("w1", "w1s", "w3", "w3s", "w2", "w2s")
+
+
+@pytest.mark.parametrize("M,H,I", [(5, 256, 128), (300, 512, 384), (64, 7168, 3072)])
+def test_fp8_expert_mlp_matches_oracle(mx, M, H, I):
+    """Every stage against the oracle applied to the GPU's own input of that
+    stage (from the workspace): g and u to the FP8 linear's bar; h bit-equal
+    to bf16(silu(g) * u) except near bf16 rounding boundaries (fp32 SiLU);
+    the MXFP8 codes of h bit-exact; y to the linear's bar given h. End to end
+    the cosine stays >= 0.9999; the largest error is allowed 5e-2 of max |y|,
+    since a one-step difference in g or u (the FP8 MFMA's own summation error)
+    can move an element of h across an E4M3 rounding boundary, a step of up to
+    2^-3 of that element."""
+    from gpu_util import assert_mlp_close, bf16_f64
+    d = W.fp8_expert(M, H, I, seed=M + H)
+    ws = torch.empty(mx.fp8_expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
+    y = bits(mx.fp8_expert_mlp(bf16_t(d["x"]), *(t(d[n]) for n in FP8_WN), workspace=ws))
+    torch.cuda.synchronize()
+    al = lambda n: (n + 255) // 256 * 256
+    sizes = [M * H, M * H // 32, M * I * 2, M * I * 2, M * I * 2, M * I, M * I // 32]
+    off, sl = 0, []
+    for n in sizes:
+        sl.append(ws[off:off + n].cpu().numpy())
+        off += al(n)
+    g = sl[2].view(np.uint16).reshape(M, I)
+    u = sl[3].view(np.uint16).reshape(M, I)
+    h = sl[4].view(np.uint16).reshape(M, I)
+    hq, hs = sl[5].reshape(M, I), sl[6].reshape(M, I // 32)
+    _check_linear(g, O.fp8_block_linear(d["x"], d["w1"], d["w1s"]), *_exact_and_magnitude(d["x"], d["w1"], d["w1s"]))
+    _check_linear(u, O.fp8_block_linear(d["x"], d["w3"], d["w3s"]), *_exact_and_magnitude(d["x"], d["w3"], d["w3s"]))
+    # h: the GPU's fp32 SiLU (hardware exp2 and reciprocal, a few tens of fp32
+    # ulps at worst for large |g|) may round the other way only where the exact
+    # value lies within 2^-16 of a bf16 rounding midpoint (bf16 g and u often
+    # make g * u an exact midpoint); values below 1e-30 flush in fp32 (e^-g
+    # overflows for g < -88.7) and are not compared
+    gv, uv = bf16_f64(g), bf16_f64(u)
+    rh = O.silu_mul_bf16(gv, uv)
+    with np.errstate(over="ignore"):
+        exact = gv / (1.0 + np.exp(-gv)) * uv
+    diff = (h != rh) & (np.abs(exact) >= H_TINY)
+    assert np.mean(diff) <= 0.01
+    mid = (bf16_f64(h) + bf16_f64(rh)) / 2
+    assert np.all(np.abs(exact[diff] - mid[diff]) <= np.abs(exact[diff]) * 2.0 ** -16)
+    rq, rs = O.mxfp8_quantize(h)
+    assert np.array_equal(hq, rq) and np.array_equal(hs, rs)
+    _check_linear(y, O.fp8_block_linear(h, d["w2"], d["w2s"]), *_exact_and_magnitude(h, d["w2"], d["w2s"]))
+    assert_mlp_close(y, O.fp8_expert_mlp(d["x"], *(d[n] for n in FP8_WN)), rel_max=5e-2)
+

@@ -171,3 +171,17 @@ def fp8_linear(tokens, n=HIDDEN, k=1536, seed=0, lo=118, hi=134):
     ws = e8m0_scales(rng, (n // 128, k // 128), lo, hi)
     return dict(w=w, ws=ws, x=activations(seed + 1, tokens, k))
 
+
+def fp8_expert(tokens, hidden=HIDDEN, inter=INTER, seed=0, lo=112, hi=120):
+    """FP8 shared expert: E4M3 w1, w3 [inter, hidden] and w2 [hidden, inter] uniform
+    over the finite codes with 128 x 128 E8M0 block scales uniform in [lo, hi]
+    (weights seed; the lower exponents keep the gate values near the SiLU's
+    active range for N(0, 1) inputs), bf16 activations N(0, 1) (seed + 1)."""
+    rng = np.random.default_rng(seed)
+    d = {}
+    for n, (r, c) in (("w1", (inter, hidden)), ("w3", (inter, hidden)), ("w2", (hidden, inter))):
+        d[n] = e4m3_finite_codes(rng, (r, c))
+        d[n + "s"] = e8m0_scales(rng, (r // 128, c // 128), lo, hi)
+    d["x"] = activations(seed + 1, tokens, hidden)
+    return d
+
