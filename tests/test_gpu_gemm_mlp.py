@@ -334,6 +334,19 @@ def test_grouped_stream_threshold(mx, requant, T):
     assert_mlp_close(_run_grouped(mx, d, packed=True, requant=requant, g=g), ref)
 
 
+@pytest.mark.parametrize("requant", ["mxfp4", "nvfp4"])
+def test_grouped_stream_max_experts(mx, requant):
+    """The largest expert count (512) with two tokens: a grid of 512 experts,
+    almost all without rows."""
+    d = W.grouped(tokens=2, n_experts=512, k=8, seed=12, hidden=128, inter=128)
+    g = 0.0
+    if requant == "nvfp4":
+        h = [O.expert_mlp(d["x"], *(d[n][e] for n in WN), intermediates=True)[1]["h"] for e in np.unique(d["ids"])]
+        g = float(O.nvfp4_warmup_global(np.concatenate(h)))
+    ref = O.grouped_expert_mlp(d["x"], d["ids"], d["w"], *(d[n] for n in WN), requant=requant, nv_global=g)
+    assert_mlp_close(_run_grouped(mx, d, requant=requant, g=g), ref)
+
+
 def test_grouped_stream_decode_real_shape(mx):
     """8 tokens of the uniformly routed 48-expert batch at the real shape."""
     d = W.grouped(tokens=4096, n_experts=48, k=8, seed=0)
