@@ -36,6 +36,7 @@ __all__ = [
     "e4m3_rne_satfinite", "e4m3_encode_exact", "nvfp4_quantize", "nvfp4_dequant_f64",
     "gemm_f64", "silu_mul_bf16", "expert_mlp", "grouped_expert_mlp",
     "nvfp4_warmup_global", "mxfp8_quantize", "mxfp8_dequant_f64", "fp8_block_linear", "fp8_expert_mlp",
+    "nvfp4_linear",
 ]
 
 # ---------------------------------------------------------------------------
@@ -524,4 +525,22 @@ def fp8_expert_mlp(x_bits, w1, w1s, w3, w3s, w2, w2s):
     u = fp8_block_linear(x_bits, w3, w3s)
     h = silu_mul_bf16(bf16_to_f64(g), bf16_to_f64(u))
     return fp8_block_linear(h, w2, w2s)
+
+
+def nvfp4_linear(x_bits, w, w_s, w_global, x_global):
+    """y = bf16(NVFP4(x) . W^T) for NVFP4 weights: the GEMM of the routed experts
+    as the pages run them on B200 (MoE w13/w2 in NVFP4: [SRV0511] "Architecture
+    Map"; per-matrix global scales weight_scale_2 and the activations' input
+    scale: [BUG0518] "Revised Plan", Phase 2).
+
+    W: E2M1 codes [N, K/2] (low nibble first) with one E4M3 scale per 16
+    columns [N, K/16] and the fp32 global w_global; x is quantised by
+    ``nvfp4_quantize`` with the fp32 global x_global. Reading: the weight
+    format is the NVFP4 reading of ``nvfp4_quantize`` (R7) applied to the
+    weights, value = code * s * w_global. Product in fp64, rounded once to bf16.
+    """
+    xq, xs = nvfp4_quantize(x_bits, x_global)
+    a = nvfp4_dequant_f64(xq, xs, x_global)
+    b = nvfp4_dequant_f64(w, w_s, w_global)
+    return f64_to_bf16(gemm_f64(a, b))
 

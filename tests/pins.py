@@ -851,3 +851,27 @@ def check_fp8_mlp_bruteforce(O, seed=71):
     assert np.array_equal(O.fp8_block_linear(h, w2, s2), y)
     assert y.shape == (M, H) and np.all(np.isfinite(((y.astype(np.uint32) << 16).view(np.float32))))
 
+
+def check_nvfp4_linear_bruteforce(O, seed=73):
+    """NVFP4-weight linear on a tiny shape against exact Fractions from the bit
+    fields (E2M1 grid, E4M3 bit fields, the fp32 globals), rounded by the
+    table-search bf16 reference; x's NVFP4 codes come from the pinned quantiser."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 2, 24, 64
+    w = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    finite = np.array([b for b in range(127) if b != 0], np.uint8)
+    ws = rng.choice(finite, size=(N, K // 16)).astype(np.uint8)
+    gw, gx = np.float32(0.0123), np.float32(0.75)
+    x = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = O.nvfp4_linear(x, w, ws, gw, gx)
+    xq, xs = O.nvfp4_quantize(x, gx)
+
+    def val(codes, scales, g, r, k):
+        byte = int(codes[r, k // 2])
+        nib = (byte >> 4) if k % 2 else (byte & 15)
+        mag = Fraction(E2M1_GRID[nib & 7])
+        return (-mag if nib & 8 else mag) * _e4m3_fraction(int(scales[r, k // 16])) * Fraction(float(g))
+    want = [float(sum(val(xq, xs, gx, m, k) * val(w, ws, gw, n, k) for k in range(K)))
+            for m in range(M) for n in range(N)]
+    assert np.array_equal(y, bf16_rne_reference(np.array(want)).reshape(M, N))
+

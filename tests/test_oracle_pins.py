@@ -38,6 +38,7 @@ CHECKS = [
     pins.check_fp8_linear_bruteforce,
     pins.check_fp8_linear_unit_rows,
     pins.check_fp8_mlp_bruteforce,
+    pins.check_nvfp4_linear_bruteforce,
 ]
 
 
