@@ -160,6 +160,7 @@ def secondary(torch, mx, workloads):
                                   "frac_of_fp4_peak": round(flops / ms / 1e9 / PEAK_FP4_TFLOPS, 4)}
     out.update(skewed_nvfp4(torch, mx, workloads))
     out.update(fp8_linear(torch, mx, workloads))
+    out.update(nvfp4_linear(torch, mx, workloads))
     # dequant (8 rotating buffer sets so the working set exceeds the 256 MB cache)
     dq = workloads.dequant_inputs(0)
     c = torch.from_numpy(dq["w1"]).cuda()
@@ -223,6 +224,28 @@ def fp8_linear(torch, mx, workloads):
         "frac_of_fp8_peak": round(flops / ms / 1e9 / PEAK_FP8_TFLOPS, 4),
         "phases_ms_per_step": {k: round(v[0] / 20, 4) for k, v in phases.items()}}
     return out
+
+
+def nvfp4_linear(torch, mx, workloads):
+    """NVFP4-weight linear (NVFP4 activations) over 4096 tokens at the down
+    projection's shape [7168, 3072], on bf16 matrix cores (NVFP4's E4M3 block
+    scale has no MFMA form on gfx950)."""
+    M, N, K = 4096, workloads.HIDDEN, workloads.INTER
+    d = workloads.nvfp4_linear(M, N, K, seed=0)
+    x = bf16_dev(torch, d["x"])
+    w = torch.from_numpy(d["w"]).cuda()
+    wsc = torch.from_numpy(d["ws"]).cuda()
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.nvfp4_linear_workspace_size(M, K), dtype=torch.uint8, device="cuda")
+    fn = lambda: mx.nvfp4_linear(x, w, wsc, float(d["wg"]), float(d["xg"]), out=y, workspace=ws)
+    ms, phases = time_steps(torch, fn, 20, 3, profile=(mx.profile_start, mx.profile_stop))
+    flops = 2.0 * M * N * K
+    gemm_ms = phases["nv_gemm"][0] / phases["nv_gemm"][1]
+    return {f"nvfp4_linear_M{M}_N{N}_K{K}": {
+        "ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2), "gemm_ms": round(gemm_ms, 4),
+        "gemm_TFLOP/s": round(flops / gemm_ms / 1e9, 2),
+        "gemm_frac_of_bf16_peak": round(flops / gemm_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "quant_ms": round(phases["quant_nvfp4"][0] / phases["quant_nvfp4"][1], 4)}}
 
 
 def skewed_nvfp4(torch, mx, workloads):

@@ -243,6 +243,27 @@ MX_API mx_status mx_fp8_block_linear(const uint16_t* x, int64_t M, int64_t K, co
 MX_API size_t mx_fp8_block_linear_workspace_size(int64_t M, int64_t K);
 
 /*
+ * mx_nvfp4_linear -- y = bf16(NVFP4(x) . W^T) with NVFP4 weights: the GEMM of
+ * the routed experts as the pages run them on B200 (w13/w2 in NVFP4: page
+ * "2026-05-11 - DeepSeek V4 NVFP4 vLLM Serving: Full End-to-End", "Architecture
+ * Map"; per-matrix weight_scale_2 and the activations' input scale: page
+ * "Current Bug: vLLM produces empty/garbage output", "Revised Plan", Phase 2).
+ *   x   [M, K] bf16, quantised to NVFP4 with the fp32 global x_global exactly
+ *       as mx_quantize_act(MX_FMT_NVFP4) does (into the workspace)
+ *   w   [N, K/2] E2M1 codes (low nibble first), w_s [N, K/16] E4M3 scales,
+ *       w_global the fp32 weight global scale: value = code * s * w_global
+ *   y   [M, N] bf16 = bf16((x_global * w_global) * sum (code s)(code s)),
+ *       on bf16 matrix cores (code * s is exact in bf16)
+ * K % 128 == 0, N % 128 == 0. x_global finite and >= 2^-117, w_global finite
+ * and > 0 (else MX_ERR_VALUE). workspace: mx_nvfp4_linear_workspace_size(M, K)
+ * bytes, 256-byte aligned. Alignment: x, w, y 16 bytes; w_s 2 bytes.
+ */
+MX_API mx_status mx_nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w,
+                                 const uint8_t* w_s, float w_global, int64_t N, float x_global, uint16_t* y,
+                                 void* workspace, size_t ws_bytes, void* stream);
+MX_API size_t mx_nvfp4_linear_workspace_size(int64_t M, int64_t K);
+
+/*
  * mx_fp8_expert_mlp -- the shared expert in the original checkpoint's FP8
  * format (page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", "Status"):
  *   g = FP8LIN(x, w1), u = FP8LIN(x, w3), h = bf16(silu(g) * u), y = FP8LIN(h, w2)

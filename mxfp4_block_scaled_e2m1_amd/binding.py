@@ -45,6 +45,8 @@ SIGNATURES = {
     "mx_debug_gemm_f32": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "mx_fp8_block_linear": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
     "mx_fp8_block_linear_workspace_size": (_SZ, [_I64, _I64]),
+    "mx_nvfp4_linear": (_I32, [_P, _I64, _I64, _P, _P, _F, _I64, _F, _P, _P, _SZ, _P]),
+    "mx_nvfp4_linear_workspace_size": (_SZ, [_I64, _I64]),
     "mx_fp8_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mx_fp8_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "mx_moe_runner_create": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32,
@@ -252,6 +254,22 @@ def fp8_block_linear(x, w, w_s, out=None, workspace=None, stream=None):
     ws = _workspace(fp8_block_linear_workspace_size(M, K), x.device, workspace)
     _check(lib().mx_fp8_block_linear(_ptr(x), M, K, _ptr(w), _ptr(w_s), N, _ptr(out), _ptr(ws), ws.numel(),
                                      _stream(stream)))
+    return out
+
+
+def nvfp4_linear_workspace_size(M, K) -> int:
+    return int(lib().mx_nvfp4_linear_workspace_size(M, K))
+
+
+def nvfp4_linear(x, w, w_s, w_global: float, x_global: float, out=None, workspace=None, stream=None):
+    """mx_nvfp4_linear: bf16 x [M, K], NVFP4 w [N, K/2] + E4M3 w_s [N, K/16] + w_global -> bf16 y [M, N]."""
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws = _workspace(nvfp4_linear_workspace_size(M, K), x.device, workspace)
+    _check(lib().mx_nvfp4_linear(_ptr(x), M, K, _ptr(w), _ptr(w_s), float(w_global), N, float(x_global), _ptr(out),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

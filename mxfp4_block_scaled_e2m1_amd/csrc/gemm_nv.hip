@@ -26,6 +26,7 @@
 // the other of two 64 KB LDS slots. Every operand element is converted once
 // per workgroup.
 #include "gemm_common.h"
+#include "nv_linear.h"
 
 namespace mx {
 
@@ -47,8 +48,8 @@ __device__ __forceinline__ int nv_off(int r, int c) { return r * NV_ROW + ((c ^ 
 // One thread's raw bytes of a stage: 32 logical columns of a weight row and of
 // a token row.
 struct NvRaw {
-  uint4 wc;         // 16 MXFP4 code bytes
-  uint32_t we;      // their E8M0 scale byte
+  uint4 wc;         // 16 weight code bytes
+  uint32_t we;      // their E8M0 scale byte (MXFP4 weights) or two E4M3 bytes (NVFP4 weights)
   uint4 hc;         // 16 NVFP4 code bytes
   uint32_t hs;      // their two E4M3 scale bytes (16 columns each)
 };
@@ -83,7 +84,10 @@ __device__ __forceinline__ uint4 h_to_bf16(uint32_t d, float s) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// One 256 x 256 tile of o = g * h . w^T (h NVFP4, w MXFP4).
+// One 256 x 256 tile of o = g * h . w^T (h NVFP4; w MXFP4, or NVFP4 when NVW,
+// whose E4M3 scales [rows, k/16] are in wa_s and whose global scale is folded
+// into g by the caller).
+template <bool NVW>
 __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -98,14 +102,16 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
   const int R = tid >> 1, half = tid & 1;
   const int wrow = min(t.nt * BN + R, a.n_rows - 1);
   const uint8_t* wsrc = a.wa + (int64_t)t.e * a.w_estride + (int64_t)wrow * kb + half * 16;
-  const uint8_t* wesrc = a.wa_s + (int64_t)t.e * a.ws_estride + (int64_t)wrow * kse + half;
+  const uint8_t* wesrc = NVW ? a.wa_s + (int64_t)t.e * a.ws_estride + (int64_t)wrow * ksn + half * 2
+                             : a.wa_s + (int64_t)t.e * a.ws_estride + (int64_t)wrow * kse + half;
   const int hrow = t.row0 + min(R, t.rows - 1);
   const uint8_t* hsrc = a.x + (int64_t)hrow * kb + half * 16;
   const uint8_t* hssrc = a.x_s + (int64_t)hrow * ksn + half * 2;
 
   auto load = [&](int st, NvRaw& r) {
     r.wc = *(const uint4*)(wsrc + st * (NV_BK / 2));
-    r.we = wesrc[st * (NV_BK / 32)];
+    if constexpr (NVW) r.we = *(const uint16_t*)(wesrc + st * (NV_BK / 16));
+    else r.we = wesrc[st * (NV_BK / 32)];
     r.hc = *(const uint4*)(hsrc + st * (NV_BK / 2));
     r.hs = *(const uint16_t*)(hssrc + st * (NV_BK / 16));
   };
@@ -115,9 +121,15 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
     const uint32_t wd[4] = {r.wc.x, r.wc.y, r.wc.z, r.wc.w};
     const uint32_t hd[4] = {r.hc.x, r.hc.y, r.hc.z, r.hc.w};
     const float s0 = e4m3_to_f32(r.hs & 0xFFu), s1 = e4m3_to_f32(r.hs >> 8);
+    float w0 = 0.f, w1 = 0.f;
+    if constexpr (NVW) {
+      w0 = e4m3_to_f32(r.we & 0xFFu);
+      w1 = e4m3_to_f32(r.we >> 8);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *(uint4*)(wt + nv_off(R, half * 4 + i)) = w_to_bf16(wd[i], r.we);
+      if constexpr (NVW) *(uint4*)(wt + nv_off(R, half * 4 + i)) = h_to_bf16(wd[i], i < 2 ? w0 : w1);
+      else *(uint4*)(wt + nv_off(R, half * 4 + i)) = w_to_bf16(wd[i], r.we);
       *(uint4*)(ht + nv_off(R, half * 4 + i)) = h_to_bf16(hd[i], i < 2 ? s0 : s1);
     }
   };
@@ -171,6 +183,7 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
 }
 
 // Persistent kernel with the tile order and XCD mapping of the FP4 GEMM.
+template <bool NVW>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm_nv(const GemmArgs a) {
   // the two K-stage slots, or the bf16 output tile of the epilogue
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_SLOT > TILE_LDS_TOTAL ? 2 * NV_SLOT : TILE_LDS_TOTAL];
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm_nv(const GemmArgs a) {
   const int per = (total + 7) >> 3;
   const int end = min((xcd + 1) * per, total);
   for (int L = xcd * per + local; L < end; L += per_xcd_wgs) {
-    nv_tile(a, decode_tile(a, tt, L), smem);
+    nv_tile<NVW>(a, decode_tile(a, tt, L), smem);
     __syncthreads();   // the next tile's first stores overwrite slot 0
   }
 }
@@ -193,7 +206,15 @@ hipError_t launch_gemm_nv_l2(const GemmArgs& a, int max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const int cus = cu_count();
   const int grid = ((max_tiles < cus ? max_tiles : cus) + 7) & ~7;
-  k_gemm_nv<<<grid, GEMM_THREADS, 0, s>>>(a);
+  k_gemm_nv<false><<<grid, GEMM_THREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nv_w(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  const int cus = cu_count();
+  const int grid = ((max_tiles < cus ? max_tiles : cus) + 7) & ~7;
+  k_gemm_nv<true><<<grid, GEMM_THREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@
 
 #include "../../include/mxfp4.h"
 #include "mx_internal.h"
+#include "nv_linear.h"
 
 using namespace mx;
 
@@ -796,6 +797,58 @@ mx_status mx_fp8_block_linear(const uint16_t* x, int64_t M, int64_t K, const uin
   MX_HIP(phase("quant_x8", s, [&] { return launch_quant_mxfp8(x, M, K, xq, xs, s); }), "quant_x8");
   MX_HIP(phase("fp8_gemm", s, [&] { return launch_fp8_gemm(xq, xs, w, w_s, (int)M, (int)N, (int)K, y, s); }),
          "fp8_gemm");
+  return ok();
+}
+
+size_t mx_nvfp4_linear_workspace_size(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  Carve c(nullptr);
+  c.take((size_t)(M * K / 2));
+  c.take((size_t)(M * (K / 16)));
+  return c.off;
+}
+
+mx_status mx_nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w, const uint8_t* w_s,
+                          float w_global, int64_t N, float x_global, uint16_t* y, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (M < 0 || K < 0 || N < 0) return fail(MX_ERR_SHAPE, "negative size");
+  if (K < 128 || K % 128 != 0) return fail(MX_ERR_SHAPE, "K %lld must be a positive multiple of 128", (long long)K);
+  if (N < 128 || N % 128 != 0) return fail(MX_ERR_SHAPE, "N %lld must be a positive multiple of 128", (long long)N);
+  if (K > (1 << 20) || N > (1 << 20) || M > ((int64_t)1 << 30) || M * K > ((int64_t)1 << 40))
+    return fail(MX_ERR_SHAPE, "matrix too large");
+  MX_TRY(check_global(x_global));
+  if (!std::isfinite(w_global) || !(w_global > 0.f))
+    return fail(MX_ERR_VALUE, "weight global scale %g must be finite and positive", (double)w_global);
+  const float g = x_global * w_global;
+  if (!std::isfinite(g)) return fail(MX_ERR_VALUE, "product of the global scales overflows");
+  if (M == 0) return ok();
+  MX_REQUIRE_PTR(x);
+  MX_REQUIRE_PTR(w);
+  MX_REQUIRE_PTR(w_s);
+  MX_REQUIRE_PTR(y);
+  MX_REQUIRE_ALIGN(x, 16);
+  MX_REQUIRE_ALIGN(w, 16);
+  MX_REQUIRE_ALIGN(w_s, 2);
+  MX_REQUIRE_ALIGN(y, 16);
+  MX_REQUIRE_PTR(workspace);
+  MX_REQUIRE_ALIGN(workspace, 256);
+  const size_t need = mx_nvfp4_linear_workspace_size(M, K);
+  if (ws_bytes < need) return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  Carve c(workspace);
+  uint8_t* xq = (uint8_t*)c.take((size_t)(M * K / 2));
+  uint8_t* xs = (uint8_t*)c.take((size_t)(M * (K / 16)));
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, M, K, x_global, xq, xs, s); }), "quant_x");
+  GemmArgs a = base_args();
+  a.wa = w; a.wa_s = w_s;
+  a.n_rows = (int)N; a.k = (int)K;
+  a.x = xq; a.x_s = xs;
+  a.m_rows = (int)M; a.n_experts = 1;
+  a.n_tiles = (int)((N + BN - 1) / BN);
+  a.grid_tiles = (int)((M + BM - 1) / BM) * a.n_tiles;
+  a.out_bf16 = y;
+  a.nv_global = g;
+  MX_HIP(phase("nv_gemm", s, [&] { return launch_gemm_nv_w(a, a.grid_tiles, s); }), "nv_gemm");
   return ok();
 }
 

@@ -202,3 +202,20 @@ def test_fp8_expert_mlp_validation(L):
     assert call(8, 256, 128, 1 << 30, x=None) == 1
     assert call(8, 256, 128, need - 1) == 5
 
+
+def test_nvfp4_linear_validation(L):
+    P = ctypes.c_void_p
+
+    def call(M, K, N, wg, xg, ws, x=P(256), wsc=P(256)):
+        return L.mx_nvfp4_linear(x, M, K, P(256), wsc, wg, N, xg, P(256), P(256), ws, None)
+    need = L.mx_nvfp4_linear_workspace_size(8, 256)
+    assert need >= 8 * 128 + 8 * 16
+    assert call(8, 200, 128, 1.0, 1.0, 1 << 30) == 2
+    assert call(8, 256, 100, 1.0, 1.0, 1 << 30) == 2
+    assert call(8, 256, 128, 1.0, 0.0, 1 << 30) == 7          # activation global
+    assert call(8, 256, 128, float("inf"), 1.0, 1 << 30) == 7  # weight global
+    assert call(0, 256, 128, 1.0, 1.0, 0) == 0
+    assert call(8, 256, 128, 1.0, 1.0, 1 << 30, x=None) == 1
+    assert call(8, 256, 128, 1.0, 1.0, 1 << 30, wsc=P(257)) == 3
+    assert call(8, 256, 128, 1.0, 1.0, need - 1) == 5
+

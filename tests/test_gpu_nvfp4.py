@@ -211,3 +211,39 @@ def test_nvfp4_grouped_stream_single_expert_close_to_shared(mx):
     yg = _run_grouped_nv(mx, gd, g)
     yd, _ = _run_dense_nv(mx, d, 12, 512, 256, g)
     assert_mlp_close(yg, yd, cos_min=0.99999)
+
+
+# ---------------------------------------------------------------- NVFP4 weights
+def _nv_linear_check(y_bits, d, rows=None):
+    """Identical NVFP4 operands on both sides, bf16 products exact, fp32 sums:
+    outputs equal the oracle's correctly rounded value or lie one step from
+    it, with |y - e| <= 2^-8 |e| + 2^-16 S (S: sum of the products' magnitudes)."""
+    from gpu_util import bf16_f64
+    x = d["x"] if rows is None else d["x"][rows]
+    ref = O.nvfp4_linear(x, d["w"], d["ws"], d["wg"], d["xg"])
+    xq, xs = O.nvfp4_quantize(x, d["xg"])
+    a = O.nvfp4_dequant_f64(xq, xs, d["xg"])
+    b = O.nvfp4_dequant_f64(d["w"], d["ws"], d["wg"])
+    exact, mag = O.gemm_f64(a, b), O.gemm_f64(np.abs(a), np.abs(b))
+    yv = bf16_f64(y_bits)
+    assert np.all(np.isfinite(yv))
+    assert np.mean(y_bits == ref) >= 0.99
+    assert np.all(np.abs(yv - exact) <= np.abs(exact) * 2.0 ** -8 + mag * 2.0 ** -16)
+    assert np.linalg.norm(yv - exact) / np.linalg.norm(exact) <= 4e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (37, 384, 256), (300, 640, 1152), (64, 3072, 7168)])
+def test_nvfp4_linear_matches_oracle(mx, M, N, K):
+    d = W.nvfp4_linear(M, N, K, seed=M + N)
+    y = mx.nvfp4_linear(bf16_t(d["x"]), t(d["w"]), t(d["ws"]), float(d["wg"]), float(d["xg"]))
+    torch.cuda.synchronize()
+    _nv_linear_check(bits(y), d)
+
+
+def test_nvfp4_linear_real_shape_sampled_rows(mx):
+    """4096 tokens through the down projection's shape [7168, 3072]; rows from every m-tile."""
+    d = W.nvfp4_linear(4096, seed=0)
+    y = bits(mx.nvfp4_linear(bf16_t(d["x"]), t(d["w"]), t(d["ws"]), float(d["wg"]), float(d["xg"])))
+    rows = np.array([0, 255, 256, 1000, 2047, 3333, 4095])
+    _nv_linear_check(y[rows], d, rows)
+

@@ -185,3 +185,16 @@ def fp8_expert(tokens, hidden=HIDDEN, inter=INTER, seed=0, lo=112, hi=120):
     d["x"] = activations(seed + 1, tokens, hidden)
     return d
 
+
+def nvfp4_linear(tokens, n=HIDDEN, k=INTER, seed=0):
+    """NVFP4-weight linear: E2M1 code bytes uniform (all 16 nibbles), E4M3 block
+    scales uniform over the codes with exponent field 4..10 (2^-3 .. 2^3 times
+    the mantissa), fp32 weight global 2^-6 (weights seed); bf16 activations
+    N(0, 1) [tokens, k] (seed + 1) with the fixed activation global 2^-9 (a
+    block maximum up to 6 * 448 * 2^-9 = 5.25 needs no saturation). The default
+    shape is the down projection [7168, 3072]."""
+    rng = np.random.default_rng(seed)
+    w = rng.integers(0, 256, (n, k // 2)).astype(np.uint8)
+    ws = rng.integers(0x20, 0x58, (n, k // 16)).astype(np.uint8)
+    return dict(w=w, ws=ws, wg=np.float32(2.0 ** -6), x=activations(seed + 1, tokens, k), xg=np.float32(2.0 ** -9))
+
