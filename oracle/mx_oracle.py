@@ -36,7 +36,7 @@ __all__ = [
     "e4m3_rne_satfinite", "e4m3_encode_exact", "nvfp4_quantize", "nvfp4_dequant_f64",
     "gemm_f64", "silu_mul_bf16", "expert_mlp", "grouped_expert_mlp",
     "nvfp4_warmup_global", "mxfp8_quantize", "mxfp8_dequant_f64", "fp8_block_linear", "fp8_expert_mlp",
-    "nvfp4_linear",
+    "nvfp4_linear", "nvfp4_expert_mlp",
 ]
 
 # ---------------------------------------------------------------------------
@@ -543,4 +543,17 @@ def nvfp4_linear(x_bits, w, w_s, w_global, x_global):
     a = nvfp4_dequant_f64(xq, xs, x_global)
     b = nvfp4_dequant_f64(w, w_s, w_global)
     return f64_to_bf16(gemm_f64(a, b))
+
+
+def nvfp4_expert_mlp(x_bits, w1, w1s, g1, w3, w3s, g3, w2, w2s, g2, x_global, h_global):
+    """One expert with NVFP4 weights: gate and up NVFP4 linears with their own
+    weight globals g1, g3 (the pages' dual gate/up weight_scale_2, [BUG0518]
+    "Revised Plan", Phase 2) over x quantised with x_global, h = bf16(silu(g) *
+    u) from their bf16 outputs, h quantised to NVFP4 with h_global, and the down
+    NVFP4 linear with g2. Reading: as for ``fp8_expert_mlp``, each linear
+    rounds its output to bf16."""
+    g = nvfp4_linear(x_bits, w1, w1s, g1, x_global)
+    u = nvfp4_linear(x_bits, w3, w3s, g3, x_global)
+    h = silu_mul_bf16(bf16_to_f64(g), bf16_to_f64(u))
+    return nvfp4_linear(h, w2, w2s, g2, h_global)
 

@@ -875,3 +875,27 @@ def check_nvfp4_linear_bruteforce(O, seed=73):
             for m in range(M) for n in range(N)]
     assert np.array_equal(y, bf16_rne_reference(np.array(want)).reshape(M, N))
 
+
+def check_nvfp4_mlp_composition(O, seed=79):
+    """The NVFP4-weight expert on a tiny shape: gate and up use their own
+    globals (swapping them changes the result), and the steps compose from the
+    pinned linear, SiLU and quantiser."""
+    rng = np.random.default_rng(seed)
+    M, H, I = 3, 128, 128
+    w = {n: rng.integers(0, 256, (r, c // 2)).astype(np.uint8) for n, (r, c) in
+         (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I)))}
+    sc = {n: rng.integers(0x20, 0x58, (r, c // 16)).astype(np.uint8) for n, (r, c) in
+          (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I)))}
+    g1, g3, g2, gx, gh = (np.float32(v) for v in (2.0 ** -6, 2.0 ** -4, 2.0 ** -5, 2.0 ** -9, 2.0 ** -3))
+    x = (rng.standard_normal((M, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = O.nvfp4_expert_mlp(x, w["w1"], sc["w1"], g1, w["w3"], sc["w3"], g3, w["w2"], sc["w2"], g2, gx, gh)
+    g = O.nvfp4_linear(x, w["w1"], sc["w1"], g1, gx)
+    u = O.nvfp4_linear(x, w["w3"], sc["w3"], g3, gx)
+    gv = np.array([bf16_value(b) for b in g.ravel()])
+    uv = np.array([bf16_value(b) for b in u.ravel()])
+    hv = [float(Fraction(a) / (1 + Fraction(math.exp(-a))) * Fraction(b)) for a, b in zip(gv, uv)]
+    h = bf16_rne_reference(np.array(hv)).reshape(M, I)
+    assert np.array_equal(O.nvfp4_linear(h, w["w2"], sc["w2"], g2, gh), y)
+    swapped = O.nvfp4_expert_mlp(x, w["w1"], sc["w1"], g3, w["w3"], sc["w3"], g1, w["w2"], sc["w2"], g2, gx, gh)
+    assert not np.array_equal(swapped, y)
+

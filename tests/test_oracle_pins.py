@@ -39,6 +39,7 @@ CHECKS = [
     pins.check_fp8_linear_unit_rows,
     pins.check_fp8_mlp_bruteforce,
     pins.check_nvfp4_linear_bruteforce,
+    pins.check_nvfp4_mlp_composition,
 ]
 
 
