@@ -241,11 +241,27 @@ def nvfp4_linear(torch, mx, workloads):
     ms, phases = time_steps(torch, fn, 20, 3, profile=(mx.profile_start, mx.profile_stop))
     flops = 2.0 * M * N * K
     gemm_ms = phases["nv_gemm"][0] / phases["nv_gemm"][1]
-    return {f"nvfp4_linear_M{M}_N{N}_K{K}": {
+    out = {f"nvfp4_linear_M{M}_N{N}_K{K}": {
         "ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2), "gemm_ms": round(gemm_ms, 4),
         "gemm_TFLOP/s": round(flops / gemm_ms / 1e9, 2),
         "gemm_frac_of_bf16_peak": round(flops / gemm_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
         "quant_ms": round(phases["quant_nvfp4"][0] / phases["quant_nvfp4"][1], 4)}}
+    # one expert with NVFP4 weights (dual gate/up globals), 4096 tokens
+    H, I = workloads.HIDDEN, workloads.INTER
+    d = workloads.nvfp4_expert(M, H, I, seed=0)
+    names = ("w1", "w1s", "w1g", "w3", "w3s", "w3g", "w2", "w2s", "w2g")
+    args = [float(d[n]) if n.endswith("g") else torch.from_numpy(d[n]).cuda() for n in names]
+    x = bf16_dev(torch, d["x"])
+    y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.nvfp4_expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
+    fn = lambda: mx.nvfp4_expert_mlp(x, *args, float(d["xg"]), float(d["hg"]), out=y, workspace=ws)
+    ms, phases = time_steps(torch, fn, 20, 3, profile=(mx.profile_start, mx.profile_stop))
+    flops = 6.0 * M * H * I
+    out[f"nvfp4_weight_expert_M{M}"] = {
+        "ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
+        "frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "phases_ms_per_step": {k: round(v[0] / 20, 4) for k, v in phases.items()}}
+    return out
 
 
 def skewed_nvfp4(torch, mx, workloads):

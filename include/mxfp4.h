@@ -264,6 +264,28 @@ MX_API mx_status mx_nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const 
 MX_API size_t mx_nvfp4_linear_workspace_size(int64_t M, int64_t K);
 
 /*
+ * mx_nvfp4_expert_mlp -- one expert with NVFP4 weights, as the pages run the
+ * experts on B200 (gate and up with their own weight_scale_2: page "Current
+ * Bug: vLLM produces empty/garbage output", "Revised Plan", Phase 2):
+ *   g = NVLIN(x, w1, w1_global), u = NVLIN(x, w3, w3_global) (x quantised to
+ *   NVFP4 with x_global), h = bf16(silu(g) * u), y = NVLIN(h, w2, w2_global)
+ *   with h quantised to NVFP4 with h_global; NVLIN is the mx_nvfp4_linear
+ *   computation, so g and u are bf16 before the SiLU.
+ *   w1, w3 [inter, hidden/2] codes + [inter, hidden/16] E4M3; w2 [hidden, inter/2] + [hidden, inter/16].
+ * hidden, inter multiples of 128. x_global, h_global finite and >= 2^-117;
+ * weight globals finite and > 0 (else MX_ERR_VALUE). workspace:
+ * mx_nvfp4_expert_mlp_workspace_size(M, hidden, inter) bytes, 256-byte aligned.
+ * Alignment: x, y, codes 16 bytes; E4M3 scales 2 bytes.
+ */
+MX_API mx_status mx_nvfp4_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter,
+                                     const uint8_t* w1, const uint8_t* w1_s, float w1_global,
+                                     const uint8_t* w3, const uint8_t* w3_s, float w3_global,
+                                     const uint8_t* w2, const uint8_t* w2_s, float w2_global,
+                                     float x_global, float h_global, uint16_t* y, void* workspace,
+                                     size_t ws_bytes, void* stream);
+MX_API size_t mx_nvfp4_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter);
+
+/*
  * mx_fp8_expert_mlp -- the shared expert in the original checkpoint's FP8
  * format (page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", "Status"):
  *   g = FP8LIN(x, w1), u = FP8LIN(x, w3), h = bf16(silu(g) * u), y = FP8LIN(h, w2)

@@ -47,6 +47,9 @@ SIGNATURES = {
     "mx_fp8_block_linear_workspace_size": (_SZ, [_I64, _I64]),
     "mx_nvfp4_linear": (_I32, [_P, _I64, _I64, _P, _P, _F, _I64, _F, _P, _P, _SZ, _P]),
     "mx_nvfp4_linear_workspace_size": (_SZ, [_I64, _I64]),
+    "mx_nvfp4_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _F, _P, _P, _F, _P, _P, _F, _F, _F, _P, _P, _SZ,
+                                   _P]),
+    "mx_nvfp4_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "mx_fp8_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mx_fp8_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "mx_moe_runner_create": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32,
@@ -270,6 +273,24 @@ def nvfp4_linear(x, w, w_s, w_global: float, x_global: float, out=None, workspac
     ws = _workspace(nvfp4_linear_workspace_size(M, K), x.device, workspace)
     _check(lib().mx_nvfp4_linear(_ptr(x), M, K, _ptr(w), _ptr(w_s), float(w_global), N, float(x_global), _ptr(out),
                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def nvfp4_expert_mlp_workspace_size(M, hidden, inter) -> int:
+    return int(lib().mx_nvfp4_expert_mlp_workspace_size(M, hidden, inter))
+
+
+def nvfp4_expert_mlp(x, w1, w1s, w1g, w3, w3s, w3g, w2, w2s, w2g, x_global, h_global, out=None, workspace=None,
+                     stream=None):
+    """mx_nvfp4_expert_mlp: one expert with NVFP4 weights on bf16 x [M, hidden] -> bf16 y [M, hidden]."""
+    M, hidden = x.shape
+    inter = w1.shape[0]
+    if out is None:
+        out = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+    ws = _workspace(nvfp4_expert_mlp_workspace_size(M, hidden, inter), x.device, workspace)
+    _check(lib().mx_nvfp4_expert_mlp(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), float(w1g), _ptr(w3),
+                                     _ptr(w3s), float(w3g), _ptr(w2), _ptr(w2s), float(w2g), float(x_global),
+                                     float(h_global), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

@@ -852,6 +852,80 @@ mx_status mx_nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t
   return ok();
 }
 
+size_t mx_nvfp4_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter) {
+  if (M < 0 || hidden < 0 || inter < 0) return 0;
+  Carve c(nullptr);
+  c.take((size_t)(M * hidden / 2));
+  c.take((size_t)(M * (hidden / 16)));
+  for (int i = 0; i < 3; ++i) c.take((size_t)(M * inter * 2));   // g, u, h
+  c.take((size_t)(M * inter / 2));
+  c.take((size_t)(M * (inter / 16)));
+  return c.off;
+}
+
+mx_status mx_nvfp4_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, const uint8_t* w1,
+                              const uint8_t* w1_s, float w1_global, const uint8_t* w3, const uint8_t* w3_s,
+                              float w3_global, const uint8_t* w2, const uint8_t* w2_s, float w2_global,
+                              float x_global, float h_global, uint16_t* y, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MX_TRY(check_mlp_dims(M, hidden, inter));
+  if (M * hidden > ((int64_t)1 << 40) || M * inter > ((int64_t)1 << 40)) return fail(MX_ERR_SHAPE, "matrix too large");
+  MX_TRY(check_global(x_global));
+  MX_TRY(check_global(h_global));
+  const float wg[3] = {w1_global, w3_global, w2_global};
+  for (int i = 0; i < 3; ++i)
+    if (!std::isfinite(wg[i]) || !(wg[i] > 0.f) || !std::isfinite(wg[i] * (i < 2 ? x_global : h_global)))
+      return fail(MX_ERR_VALUE, "weight global scale %d (%g) must be finite and positive, and its product "
+                                "with the activation global finite", i, (double)wg[i]);
+  if (M == 0) return ok();
+  MX_REQUIRE_PTR(x);
+  MX_REQUIRE_PTR(y);
+  MX_REQUIRE_ALIGN(x, 16);
+  MX_REQUIRE_ALIGN(y, 16);
+  const uint8_t* wp[6] = {w1, w1_s, w3, w3_s, w2, w2_s};
+  for (int i = 0; i < 6; ++i) {
+    if (wp[i] == nullptr) return fail(MX_ERR_NULL, "NVFP4 weight or scale pointer %d is NULL", i);
+    if (!aligned(wp[i], i % 2 ? 2 : 16)) return fail(MX_ERR_ALIGN, "NVFP4 weight or scale pointer %d misaligned", i);
+  }
+  MX_REQUIRE_PTR(workspace);
+  MX_REQUIRE_ALIGN(workspace, 256);
+  const size_t need = mx_nvfp4_expert_mlp_workspace_size(M, hidden, inter);
+  if (ws_bytes < need) return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  Carve c(workspace);
+  uint8_t* xq = (uint8_t*)c.take((size_t)(M * hidden / 2));
+  uint8_t* xs = (uint8_t*)c.take((size_t)(M * (hidden / 16)));
+  uint16_t* g = (uint16_t*)c.take((size_t)(M * inter * 2));
+  uint16_t* u = (uint16_t*)c.take((size_t)(M * inter * 2));
+  uint16_t* h = (uint16_t*)c.take((size_t)(M * inter * 2));
+  uint8_t* hq = (uint8_t*)c.take((size_t)(M * inter / 2));
+  uint8_t* hs = (uint8_t*)c.take((size_t)(M * (inter / 16)));
+  auto gemm = [&](const uint8_t* aq, const uint8_t* as, const uint8_t* w, const uint8_t* ws, int64_t N, int64_t K,
+                  float gscale, uint16_t* out) {
+    GemmArgs a = base_args();
+    a.wa = w; a.wa_s = ws;
+    a.n_rows = (int)N; a.k = (int)K;
+    a.x = aq; a.x_s = as;
+    a.m_rows = (int)M; a.n_experts = 1;
+    a.n_tiles = (int)((N + BN - 1) / BN);
+    a.grid_tiles = (int)((M + BM - 1) / BM) * a.n_tiles;
+    a.out_bf16 = out;
+    a.nv_global = gscale;
+    return launch_gemm_nv_w(a, a.grid_tiles, s);
+  };
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, M, hidden, x_global, xq, xs, s); }), "quant_x");
+  MX_HIP(phase("nv_gemm", s, [&] {
+           hipError_t e = gemm(xq, xs, w1, w1_s, inter, hidden, x_global * w1_global, g);
+           if (e != hipSuccess) return e;
+           return gemm(xq, xs, w3, w3_s, inter, hidden, x_global * w3_global, u);
+         }), "nv_gemm_l1");
+  MX_HIP(phase("silu_mul", s, [&] { return launch_silu_mul_bf16(g, u, M * inter, h, s); }), "silu_mul");
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(h, M, inter, h_global, hq, hs, s); }), "quant_h");
+  MX_HIP(phase("nv_gemm", s, [&] { return gemm(hq, hs, w2, w2_s, hidden, inter, h_global * w2_global, y); }),
+         "nv_gemm_l2");
+  return ok();
+}
+
 size_t mx_fp8_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter) {
   if (M < 0 || hidden < 0 || inter < 0) return 0;
   Carve c(nullptr);

@@ -219,3 +219,20 @@ def test_nvfp4_linear_validation(L):
     assert call(8, 256, 128, 1.0, 1.0, 1 << 30, wsc=P(257)) == 3
     assert call(8, 256, 128, 1.0, 1.0, need - 1) == 5
 
+
+def test_nvfp4_expert_mlp_validation(L):
+    P = ctypes.c_void_p
+
+    def call(M, H, I, ws, wg=1.0, hg=1.0, x=P(256), s3=P(256)):
+        return L.mx_nvfp4_expert_mlp(x, M, H, I, P(256), P(256), wg, P(256), s3, 1.0, P(256), P(256), 1.0,
+                                     1.0, hg, P(256), P(256), ws, None)
+    need = L.mx_nvfp4_expert_mlp_workspace_size(8, 256, 128)
+    assert need > 0
+    assert call(8, 200, 128, 1 << 30) == 2
+    assert call(8, 256, 128, 1 << 30, wg=0.0) == 7
+    assert call(8, 256, 128, 1 << 30, hg=float("nan")) == 7
+    assert call(0, 256, 128, 0) == 0
+    assert call(8, 256, 128, 1 << 30, x=None) == 1
+    assert call(8, 256, 128, 1 << 30, s3=P(257)) == 3
+    assert call(8, 256, 128, need - 1) == 5
+

@@ -215,15 +215,19 @@ def test_nvfp4_grouped_stream_single_expert_close_to_shared(mx):
 
 # ---------------------------------------------------------------- NVFP4 weights
 def _nv_linear_check(y_bits, d, rows=None):
+    x = d["x"] if rows is None else d["x"][rows]
+    _nv_bar(y_bits, x, d["w"], d["ws"], d["wg"], d["xg"])
+
+
+def _nv_bar(y_bits, x, w, ws, wg, xg):
     """Identical NVFP4 operands on both sides, bf16 products exact, fp32 sums:
     outputs equal the oracle's correctly rounded value or lie one step from
     it, with |y - e| <= 2^-8 |e| + 2^-16 S (S: sum of the products' magnitudes)."""
     from gpu_util import bf16_f64
-    x = d["x"] if rows is None else d["x"][rows]
-    ref = O.nvfp4_linear(x, d["w"], d["ws"], d["wg"], d["xg"])
-    xq, xs = O.nvfp4_quantize(x, d["xg"])
-    a = O.nvfp4_dequant_f64(xq, xs, d["xg"])
-    b = O.nvfp4_dequant_f64(d["w"], d["ws"], d["wg"])
+    ref = O.nvfp4_linear(x, w, ws, wg, xg)
+    xq, xs = O.nvfp4_quantize(x, xg)
+    a = O.nvfp4_dequant_f64(xq, xs, xg)
+    b = O.nvfp4_dequant_f64(w, ws, wg)
     exact, mag = O.gemm_f64(a, b), O.gemm_f64(np.abs(a), np.abs(b))
     yv = bf16_f64(y_bits)
     assert np.all(np.isfinite(yv))
@@ -246,4 +250,46 @@ def test_nvfp4_linear_real_shape_sampled_rows(mx):
     y = bits(mx.nvfp4_linear(bf16_t(d["x"]), t(d["w"]), t(d["ws"]), float(d["wg"]), float(d["xg"])))
     rows = np.array([0, 255, 256, 1000, 2047, 3333, 4095])
     _nv_linear_check(y[rows], d, rows)
+
+
+NV_WN = ("w1", "w1s", "w1g", "w3", "w3s", "w3g", "w2", "w2s", "w2g")
+
+
+@pytest.mark.parametrize("M,H,I", [(5, 256, 128), (300, 512, 384), (64, 7168, 3072)])
+def test_nvfp4_expert_mlp_matches_oracle(mx, M, H, I):
+    """Every stage against the oracle on the GPU's own stage input (workspace):
+    g and u to the NVFP4 linear's bar (own weight globals), h bit-equal to
+    bf16(silu(g) * u) except within 2^-16 of a bf16 midpoint, the NVFP4 codes
+    and scales of h bit-exact, y to the linear's bar; end to end cosine >=
+    0.9999 and max error <= 5e-2 of max |y| (a one-step difference in g or u
+    can move an element of h across an E2M1 rounding boundary)."""
+    from gpu_util import bf16_f64
+    d = W.nvfp4_expert(M, H, I, seed=M + I)
+    args = [t(d[n]) if not n.endswith("g") else float(d[n]) for n in NV_WN]
+    ws = torch.empty(mx.nvfp4_expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
+    y = bits(mx.nvfp4_expert_mlp(bf16_t(d["x"]), *args, float(d["xg"]), float(d["hg"]), workspace=ws))
+    torch.cuda.synchronize()
+    al = lambda n: (n + 255) // 256 * 256
+    sizes = [M * H // 2, M * H // 16, M * I * 2, M * I * 2, M * I * 2, M * I // 2, M * I // 16]
+    off, sl = 0, []
+    for n in sizes:
+        sl.append(ws[off:off + n].cpu().numpy())
+        off += al(n)
+    g, u, h = (sl[i].view(np.uint16).reshape(M, I) for i in (2, 3, 4))
+    hq, hs = sl[5].reshape(M, I // 2), sl[6].reshape(M, I // 16)
+    _nv_bar(g, d["x"], d["w1"], d["w1s"], d["w1g"], d["xg"])
+    _nv_bar(u, d["x"], d["w3"], d["w3s"], d["w3g"], d["xg"])
+    gv, uv = bf16_f64(g), bf16_f64(u)
+    rh = O.silu_mul_bf16(gv, uv)
+    with np.errstate(over="ignore"):
+        exact = gv / (1.0 + np.exp(-gv)) * uv
+    diff = (h != rh) & (np.abs(exact) >= 1e-30)
+    assert np.mean(diff) <= 0.01
+    mid = (bf16_f64(h) + bf16_f64(rh)) / 2
+    assert np.all(np.abs(exact[diff] - mid[diff]) <= np.abs(exact[diff]) * 2.0 ** -16)
+    rq, rs = O.nvfp4_quantize(h, d["hg"])
+    assert np.array_equal(hq, rq) and np.array_equal(hs, rs)
+    _nv_bar(y, h, d["w2"], d["w2s"], d["w2g"], d["hg"])
+    ref = O.nvfp4_expert_mlp(d["x"], *(d[n] for n in NV_WN), d["xg"], d["hg"])
+    assert_mlp_close(y, ref, rel_max=5e-2)
 

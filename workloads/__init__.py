@@ -198,3 +198,18 @@ def nvfp4_linear(tokens, n=HIDDEN, k=INTER, seed=0):
     ws = rng.integers(0x20, 0x58, (n, k // 16)).astype(np.uint8)
     return dict(w=w, ws=ws, wg=np.float32(2.0 ** -6), x=activations(seed + 1, tokens, k), xg=np.float32(2.0 ** -9))
 
+
+def nvfp4_expert(tokens, hidden=HIDDEN, inter=INTER, seed=0):
+    """One expert with NVFP4 weights: codes and E4M3 scales as ``nvfp4_linear``,
+    weight globals 2^-6 (w1), 2^-5 (w3, a different one: the dual gate/up
+    globals) and 2^-6 (w2) (weights seed); bf16 activations N(0, 1) (seed + 1)
+    with activation global 2^-9 and intermediate global 1."""
+    rng = np.random.default_rng(seed)
+    d = {}
+    for n, (r, c) in (("w1", (inter, hidden)), ("w3", (inter, hidden)), ("w2", (hidden, inter))):
+        d[n] = rng.integers(0, 256, (r, c // 2)).astype(np.uint8)
+        d[n + "s"] = rng.integers(0x20, 0x58, (r, c // 16)).astype(np.uint8)
+    d.update(w1g=np.float32(2.0 ** -6), w3g=np.float32(2.0 ** -5), w2g=np.float32(2.0 ** -6),
+             xg=np.float32(2.0 ** -9), hg=np.float32(1.0), x=activations(seed + 1, tokens, hidden))
+    return d
+
