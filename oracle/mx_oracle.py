@@ -36,7 +36,7 @@ __all__ = [
     "e4m3_rne_satfinite", "e4m3_encode_exact", "nvfp4_quantize", "nvfp4_dequant_f64",
     "gemm_f64", "silu_mul_bf16", "expert_mlp", "grouped_expert_mlp",
     "nvfp4_warmup_global", "mxfp8_quantize", "mxfp8_dequant_f64", "fp8_block_linear", "fp8_expert_mlp",
-    "nvfp4_linear", "nvfp4_expert_mlp",
+    "nvfp4_linear", "nvfp4_expert_mlp", "grouped_nvfp4_expert_mlp",
 ]
 
 # ---------------------------------------------------------------------------
@@ -556,4 +556,38 @@ def nvfp4_expert_mlp(x_bits, w1, w1s, g1, w3, w3s, g3, w2, w2s, g2, x_global, h_
     u = nvfp4_linear(x_bits, w3, w3s, g3, x_global)
     h = silu_mul_bf16(bf16_to_f64(g), bf16_to_f64(u))
     return nvfp4_linear(h, w2, w2s, g2, h_global)
+
+
+def grouped_nvfp4_expert_mlp(x_bits, topk_ids, topk_w, w1, w1s, g1, w3, w3s, g3, w2, w2s, g2, x_global,
+                             h_global, tokens=None):
+    """Routed experts with NVFP4 weights, as the pages run the MoE on B200 (w13/w2
+    in NVFP4 with per-expert weight_scale_2: [SRV0511] "Architecture Map",
+    [BUG0518] "Revised Plan", Phase 2): y[t] = bf16(sum_k w[t,k] *
+    expert_{ids[t,k]}(x[t])). Each pair runs the steps of ``nvfp4_expert_mlp``
+    with its expert's globals g1[e], g3[e], g2[e] (arrays of E fp32); the
+    down product is kept in fp64 and the weighted sum rounded to bf16 once, as
+    in ``grouped_expert_mlp``. Ids outside [0, E) are skipped; ``tokens``
+    restricts the work to those token indices."""
+    x_bits = np.asarray(x_bits)
+    ids = np.asarray(topk_ids).astype(np.int64)
+    wts = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        x_bits, ids, wts = x_bits[tokens], ids[tokens], wts[tokens]
+    T, k = ids.shape
+    E = w1.shape[0]
+    H = x_bits.shape[1]
+    acc = np.zeros((T, H), dtype=np.float64)
+    for e in range(E):
+        t_idx, k_idx = np.nonzero(ids == e)
+        if t_idx.size == 0:
+            continue
+        xe = x_bits[t_idx]
+        g = nvfp4_linear(xe, w1[e], w1s[e], g1[e], x_global)
+        u = nvfp4_linear(xe, w3[e], w3s[e], g3[e], x_global)
+        h = silu_mul_bf16(bf16_to_f64(g), bf16_to_f64(u))
+        hq, hs = nvfp4_quantize(h, h_global)
+        y_pair = gemm_f64(nvfp4_dequant_f64(hq, hs, h_global), nvfp4_dequant_f64(w2[e], w2s[e], g2[e]))
+        np.add.at(acc, t_idx, wts[t_idx, k_idx][:, None] * y_pair)
+    return f64_to_bf16(acc)
 

@@ -899,3 +899,47 @@ def check_nvfp4_mlp_composition(O, seed=79):
     swapped = O.nvfp4_expert_mlp(x, w["w1"], sc["w1"], g3, w["w3"], sc["w3"], g1, w["w2"], sc["w2"], g2, gx, gh)
     assert not np.array_equal(swapped, y)
 
+
+def check_grouped_nvfp4_reductions(O, seed=83):
+    """Routed NVFP4-weight experts: one expert with k = 1 and w = 1 reduces to the
+    single NVFP4-weight expert; the result is linear in the gate weights;
+    foreign ids contribute nothing; each expert's own globals are used."""
+    rng = np.random.default_rng(seed)
+    E, T, k, H, I = 3, 5, 2, 128, 128
+    w = {n: rng.integers(0, 256, (E, r, c // 2)).astype(np.uint8) for n, (r, c) in
+         (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I)))}
+    sc = {n: rng.integers(0x20, 0x58, (E, r, c // 16)).astype(np.uint8) for n, (r, c) in
+          (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I)))}
+    g1 = np.array([2.0 ** -6, 2.0 ** -5, 2.0 ** -7], np.float32)
+    g3 = np.array([2.0 ** -5, 2.0 ** -6, 2.0 ** -6], np.float32)
+    g2 = np.array([2.0 ** -6, 2.0 ** -4, 2.0 ** -5], np.float32)
+    gx, gh = np.float32(2.0 ** -9), np.float32(1.0)
+    x = (rng.standard_normal((T, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    args = lambda gg1: (w["w1"], sc["w1"], gg1, w["w3"], sc["w3"], g3, w["w2"], sc["w2"], g2, gx, gh)
+    ids = np.array([[0, 1], [2, 0], [1, 2], [0, 0], [2, 1]], np.int32)
+    wt = rng.random((T, k)).astype(np.float32)
+    y = O.grouped_nvfp4_expert_mlp(x, ids, wt, *args(g1))
+    # single expert: ids all e, k = 1, w = 1
+    for e in range(E):
+        one = O.grouped_nvfp4_expert_mlp(x, np.full((T, 1), e, np.int32), np.ones((T, 1), np.float32), *args(g1))
+        single = O.nvfp4_expert_mlp(x, w["w1"][e], sc["w1"][e], g1[e], w["w3"][e], sc["w3"][e], g3[e],
+                                    w["w2"][e], sc["w2"][e], g2[e], gx, gh)
+        assert np.max(np.abs(bf16_to_f64_local(one) - bf16_to_f64_local(single))
+                      / (np.abs(bf16_to_f64_local(single)) + 1e-30)) <= 2.0 ** -7
+    # linear in the weights; foreign ids skipped
+    y2 = O.grouped_nvfp4_expert_mlp(x, ids, 2 * wt, *args(g1))
+    assert np.allclose(bf16_to_f64_local(y2), 2 * bf16_to_f64_local(y), rtol=2.0 ** -7, atol=0)
+    ids_f = ids.copy()
+    ids_f[:, 1] = -1
+    yf = O.grouped_nvfp4_expert_mlp(x, ids_f, wt, *args(g1))
+    yk = O.grouped_nvfp4_expert_mlp(x, ids[:, :1], wt[:, :1], *args(g1))
+    assert np.array_equal(yf, yk)
+    # per-expert globals matter: change expert 1's gate global
+    g1b = g1.copy()
+    g1b[1] *= 2
+    assert not np.array_equal(O.grouped_nvfp4_expert_mlp(x, ids, wt, *args(g1b)), y)
+
+
+def bf16_to_f64_local(bits):
+    return ((np.asarray(bits).astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+

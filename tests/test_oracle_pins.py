@@ -40,6 +40,7 @@ CHECKS = [
     pins.check_fp8_mlp_bruteforce,
     pins.check_nvfp4_linear_bruteforce,
     pins.check_nvfp4_mlp_composition,
+    pins.check_grouped_nvfp4_reductions,
 ]
 
 
