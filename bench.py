@@ -261,6 +261,22 @@ def nvfp4_linear(torch, mx, workloads):
         "ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
         "frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
         "phases_ms_per_step": {k: round(v[0] / 20, 4) for k, v in phases.items()}}
+    del args, x, y, ws
+    # the headline batch (48 experts x 4096 tokens, top-8) with NVFP4 weights
+    T, E, K = 4096, workloads.N_LOCAL_EXPERTS, workloads.TOP_K
+    d = workloads.grouped_nvfp4(tokens=T, seed=0)
+    args = [torch.from_numpy(np.ascontiguousarray(d[n])).cuda() for n in names]
+    x = bf16_dev(torch, d["x"])
+    ids, gw = torch.from_numpy(d["ids"]).cuda(), torch.from_numpy(d["w"]).cuda()
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.grouped_nvfp4_expert_mlp_workspace_size(T, H, I, K, E), dtype=torch.uint8, device="cuda")
+    fn = lambda: mx.grouped_nvfp4_expert_mlp(x, ids, gw, *args, float(d["xg"]), float(d["hg"]), out=y, workspace=ws)
+    ms, phases = time_steps(torch, fn, 5, 2, profile=(mx.profile_start, mx.profile_stop))
+    flops = 6.0 * T * K * H * I
+    out["grouped_nvfp4_weights_e48_t4096"] = {
+        "ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
+        "frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "phases_ms_per_step": {k: round(v[0] / 5, 4) for k, v in phases.items()}}
     return out
 
 

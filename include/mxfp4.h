@@ -286,6 +286,32 @@ MX_API mx_status mx_nvfp4_expert_mlp(const uint16_t* x, int64_t M, int64_t hidde
 MX_API size_t mx_nvfp4_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter);
 
 /*
+ * mx_grouped_nvfp4_expert_mlp -- E routed experts with NVFP4 weights, as the
+ * pages run the MoE on B200 (w13/w2 in NVFP4 with per-expert weight_scale_2).
+ * Routing, gate weights, ids outside [0, E) and the combine as for
+ * mx_grouped_expert_mlp; each pair runs the steps of mx_nvfp4_expert_mlp with
+ * its expert's globals:
+ *   w1, w3 codes [E, inter, hidden/2], E4M3 scales [E, inter, hidden/16]
+ *   w2 codes [E, hidden, inter/2], E4M3 scales [E, hidden, inter/16]
+ *   w1_global, w3_global, w2_global: DEVICE arrays of E fp32 (finite, > 0;
+ *     not checked on the host)
+ *   x_global, h_global: fp32 activation and intermediate globals (host values)
+ * 1 <= k <= E <= 512; hidden % 128 == 0; inter % 128 == 0. workspace:
+ * mx_grouped_nvfp4_expert_mlp_workspace_size(T, hidden, inter, k, E) bytes,
+ * 256-byte aligned. Alignment: x, y, codes 16 bytes; E4M3 scales 2 bytes;
+ * ids, gate weights and globals 4 bytes.
+ */
+MX_API mx_status mx_grouped_nvfp4_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
+                                             const int32_t* topk_ids, const float* topk_w, int32_t k,
+                                             int32_t E, const uint8_t* w1, const uint8_t* w1_s,
+                                             const float* w1_global, const uint8_t* w3, const uint8_t* w3_s,
+                                             const float* w3_global, const uint8_t* w2, const uint8_t* w2_s,
+                                             const float* w2_global, float x_global, float h_global,
+                                             uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+MX_API size_t mx_grouped_nvfp4_expert_mlp_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k,
+                                                         int32_t E);
+
+/*
  * mx_fp8_expert_mlp -- the shared expert in the original checkpoint's FP8
  * format (page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", "Status"):
  *   g = FP8LIN(x, w1), u = FP8LIN(x, w3), h = bf16(silu(g) * u), y = FP8LIN(h, w2)

@@ -50,6 +50,9 @@ SIGNATURES = {
     "mx_nvfp4_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _F, _P, _P, _F, _P, _P, _F, _F, _F, _P, _P, _SZ,
                                    _P]),
     "mx_nvfp4_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "mx_grouped_nvfp4_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _F, _F, _P, _P, _SZ, _P]),
+    "mx_grouped_nvfp4_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "mx_fp8_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mx_fp8_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "mx_moe_runner_create": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32,
@@ -291,6 +294,26 @@ def nvfp4_expert_mlp(x, w1, w1s, w1g, w3, w3s, w3g, w2, w2s, w2g, x_global, h_gl
     _check(lib().mx_nvfp4_expert_mlp(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), float(w1g), _ptr(w3),
                                      _ptr(w3s), float(w3g), _ptr(w2), _ptr(w2s), float(w2g), float(x_global),
                                      float(h_global), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def grouped_nvfp4_expert_mlp_workspace_size(T, hidden, inter, k, E) -> int:
+    return int(lib().mx_grouped_nvfp4_expert_mlp_workspace_size(T, hidden, inter, k, E))
+
+
+def grouped_nvfp4_expert_mlp(x, topk_ids, topk_w, w1, w1s, w1g, w3, w3s, w3g, w2, w2s, w2g, x_global, h_global,
+                             out=None, workspace=None, stream=None):
+    """mx_grouped_nvfp4_expert_mlp: routed experts with NVFP4 weights; w*g are device fp32 [E] tensors."""
+    T, hidden = x.shape
+    k = topk_ids.shape[1]
+    E, inter = w1.shape[0], w1.shape[1]
+    if out is None:
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
+    ws = _workspace(grouped_nvfp4_expert_mlp_workspace_size(T, hidden, inter, k, E), x.device, workspace)
+    _check(lib().mx_grouped_nvfp4_expert_mlp(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
+                                             _ptr(w1), _ptr(w1s), _ptr(w1g), _ptr(w3), _ptr(w3s), _ptr(w3g),
+                                             _ptr(w2), _ptr(w2s), _ptr(w2g), float(x_global), float(h_global),
+                                             _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

@@ -179,7 +179,8 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
     stage(st, ra, rb);
     if (st + 1 < nst) stage(st + 1, rb, ra);
   }
-  store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, a.nv_global, smem, GEMM_THREADS);
+  const float scale = a.e_global != nullptr ? a.nv_global * a.e_global[t.e] : a.nv_global;
+  store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, scale, smem, GEMM_THREADS);
 }
 
 // Persistent kernel with the tile order and XCD mapping of the FP4 GEMM.

@@ -926,6 +926,129 @@ mx_status mx_nvfp4_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int6
   return ok();
 }
 
+namespace {
+// Routed NVFP4-weight workspace: xq, xs (per token), the route buffers, the
+// gathered xq/xs (sorted rows), g, u, h (bf16), hq, hs, o (per pair row).
+struct NvGroupWs {
+  uint8_t *xq, *xs, *gq, *gs, *hq, *hs;
+  uint16_t *g, *u, *h, *o;
+  RouteBuffers rb;
+  size_t bytes;
+};
+NvGroupWs nv_group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E) {
+  Carve c(base);
+  NvGroupWs w;
+  const int64_t P = T * k;
+  const int64_t nblocks = (P + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+  w.xq = (uint8_t*)c.take((size_t)(T * H / 2));
+  w.xs = (uint8_t*)c.take((size_t)(T * H / 16));
+  w.rb.block_counts = (int32_t*)c.take((size_t)(nblocks * E * 4));
+  w.rb.expert_off = (int32_t*)c.take((size_t)(E + 1) * 4);
+  w.rb.tile_base = (int32_t*)c.take((size_t)(E + 1) * 4);
+  w.rb.row_token = (int32_t*)c.take((size_t)P * 4);
+  w.rb.row_slot = (int32_t*)c.take((size_t)P * 4);
+  w.rb.row_weight = (float*)c.take((size_t)P * 4);
+  w.gq = (uint8_t*)c.take((size_t)(P * H / 2));
+  w.gs = (uint8_t*)c.take((size_t)(P * H / 16));
+  w.g = (uint16_t*)c.take((size_t)(P * I * 2));
+  w.u = (uint16_t*)c.take((size_t)(P * I * 2));
+  w.h = (uint16_t*)c.take((size_t)(P * I * 2));
+  w.hq = (uint8_t*)c.take((size_t)(P * I / 2));
+  w.hs = (uint8_t*)c.take((size_t)(P * I / 16));
+  w.o = (uint16_t*)c.take((size_t)(P * H * 2));
+  w.bytes = c.off;
+  return w;
+}
+}  // namespace
+
+size_t mx_grouped_nvfp4_expert_mlp_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k, int32_t E) {
+  if (T < 0 || hidden < 0 || inter < 0 || k < 1 || E < 1) return 0;
+  return nv_group_ws(nullptr, T, hidden, inter, k, E).bytes;
+}
+
+mx_status mx_grouped_nvfp4_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
+                                      const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
+                                      const uint8_t* w1, const uint8_t* w1_s, const float* w1_global,
+                                      const uint8_t* w3, const uint8_t* w3_s, const float* w3_global,
+                                      const uint8_t* w2, const uint8_t* w2_s, const float* w2_global,
+                                      float x_global, float h_global, uint16_t* y, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MX_TRY(check_mlp_dims(T, hidden, inter));
+  MX_TRY(check_global(x_global));
+  MX_TRY(check_global(h_global));
+  if (E < 1 || E > ROUTE_MAX_EXPERTS) return fail(MX_ERR_SHAPE, "E %d outside [1, %d]", E, ROUTE_MAX_EXPERTS);
+  if (k < 1 || k > E) return fail(MX_ERR_SHAPE, "k %d outside [1, E=%d]", k, E);
+  if (T * (int64_t)k > ((int64_t)1 << 30)) return fail(MX_ERR_SHAPE, "T*k above 2^30");
+  if (T == 0) return ok();
+  MX_REQUIRE_PTR(x);
+  MX_REQUIRE_PTR(y);
+  MX_REQUIRE_PTR(topk_ids);
+  MX_REQUIRE_PTR(topk_w);
+  MX_REQUIRE_ALIGN(x, 16);
+  MX_REQUIRE_ALIGN(y, 16);
+  MX_REQUIRE_ALIGN(topk_ids, 4);
+  MX_REQUIRE_ALIGN(topk_w, 4);
+  const uint8_t* wp[6] = {w1, w1_s, w3, w3_s, w2, w2_s};
+  for (int i = 0; i < 6; ++i) {
+    if (wp[i] == nullptr) return fail(MX_ERR_NULL, "NVFP4 weight or scale pointer %d is NULL", i);
+    if (!aligned(wp[i], i % 2 ? 2 : 16)) return fail(MX_ERR_ALIGN, "NVFP4 weight or scale pointer %d misaligned", i);
+  }
+  MX_REQUIRE_PTR(w1_global);
+  MX_REQUIRE_PTR(w3_global);
+  MX_REQUIRE_PTR(w2_global);
+  MX_REQUIRE_ALIGN(w1_global, 4);
+  MX_REQUIRE_ALIGN(w3_global, 4);
+  MX_REQUIRE_ALIGN(w2_global, 4);
+  MX_REQUIRE_PTR(workspace);
+  MX_REQUIRE_ALIGN(workspace, 256);
+  const size_t need = mx_grouped_nvfp4_expert_mlp_workspace_size(T, hidden, inter, k, E);
+  if (ws_bytes < need) return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  NvGroupWs w = nv_group_ws(workspace, T, hidden, inter, k, E);
+  const int64_t P = T * k;
+  const int max_mtiles = (int)max_route_mtiles(P, E);
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, T, hidden, x_global, w.xq, w.xs, s); }),
+         "quant_x");
+  MX_HIP(phase("route", s, [&] {
+           hipError_t e = launch_route(topk_ids, topk_w, T, k, E, w.rb, s);
+           if (e != hipSuccess) return e;
+           e = launch_gather_rows(w.xq, (int)(hidden / 2), w.rb.row_token, w.rb.expert_off + E, P, w.gq, s);
+           if (e != hipSuccess) return e;
+           return launch_gather_rows(w.xs, (int)(hidden / 16), w.rb.row_token, w.rb.expert_off + E, P, w.gs, s);
+         }), "route");
+  auto gemm = [&](const uint8_t* aq, const uint8_t* as, const uint8_t* wc, const uint8_t* wsc, const float* eg,
+                  int64_t N, int64_t K, float gscale, uint16_t* out, bool pairs) {
+    GemmArgs a = base_args();
+    a.wa = wc; a.wa_s = wsc;
+    a.w_estride = N * K / 2; a.ws_estride = N * K / 16;
+    a.n_rows = (int)N; a.k = (int)K;
+    a.x = aq; a.x_s = as;
+    a.expert_off = w.rb.expert_off; a.tile_base = w.rb.tile_base; a.n_experts = E;
+    a.n_tiles = (int)((N + BN - 1) / BN);
+    a.out_bf16 = out;
+    if (pairs) {
+      a.row_slot = w.rb.row_slot;
+      a.row_weight = w.rb.row_weight;
+    }
+    a.nv_global = gscale;
+    a.e_global = eg;
+    return launch_gemm_nv_w(a, max_mtiles * a.n_tiles, s);
+  };
+  MX_HIP(phase("nv_gemm", s, [&] {
+           hipError_t e = gemm(w.gq, w.gs, w1, w1_s, w1_global, inter, hidden, x_global, w.g, false);
+           if (e != hipSuccess) return e;
+           return gemm(w.gq, w.gs, w3, w3_s, w3_global, inter, hidden, x_global, w.u, false);
+         }), "nv_gemm_l1");
+  MX_HIP(phase("silu_mul", s, [&] { return launch_silu_mul_bf16(w.g, w.u, P * inter, w.h, s); }), "silu_mul");
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(w.h, P, inter, h_global, w.hq, w.hs, s); }),
+         "quant_h");
+  MX_HIP(phase("nv_gemm", s, [&] {
+           return gemm(w.hq, w.hs, w2, w2_s, w2_global, hidden, inter, h_global, w.o, true);
+         }), "nv_gemm_l2");
+  MX_HIP(phase("combine", s, [&] { return launch_combine(w.o, topk_ids, T, k, E, (int)hidden, y, s); }), "combine");
+  return ok();
+}
+
 size_t mx_fp8_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter) {
   if (M < 0 || hidden < 0 || inter < 0) return 0;
   Carve c(nullptr);

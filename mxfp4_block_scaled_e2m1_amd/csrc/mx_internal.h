@@ -74,7 +74,8 @@ struct GemmArgs {
   uint8_t* h_codes;           // L1: [rows, n_rows/2]
   uint8_t* h_scales;          // L1: [rows, n_rows/32] (MXFP4) or [rows, n_rows/16] (NVFP4)
   int h_scales_packed;        // L1 MXFP4: h_scales tile-major over the m-tiles (the L2's x_s)
-  float nv_global;            // L1 NVFP4 global scale
+  float nv_global;            // L1 NVFP4 global scale; bf16-MFMA GEMMs: epilogue scale
+  const float* e_global;      // bf16-MFMA GEMMs, optional: per-expert factor on nv_global [E]
   uint32_t* h_amax;           // L1 MXFP4, optional: running max of |h| (bf16 bits) over the valid rows
   uint16_t* out_bf16;         // EPI_BF16: dense y [m_rows, n_rows]; grouped o [slots, n_rows]
   const int32_t* row_slot;    // grouped L2: sorted row -> slot (t*k + j)
@@ -139,6 +140,11 @@ struct RouteBuffers {
 
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, int64_t tokens, int k, int n_experts,
                         const RouteBuffers& rb, hipStream_t s);
+
+// dst[r] = src[row_token[r]] for the *n_valid sorted rows (n_valid: the route's
+// expert_off[E], on the device); rows are `width` bytes, width % 8 == 0.
+hipError_t launch_gather_rows(const uint8_t* src, int width, const int32_t* row_token, const int32_t* n_valid,
+                              int64_t P, uint8_t* dst, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* o, const int32_t* topk_ids, int64_t tokens, int k,
                           int n_experts, int hidden, uint16_t* y, hipStream_t s);

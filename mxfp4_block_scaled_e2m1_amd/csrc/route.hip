@@ -106,6 +106,24 @@ __global__ __launch_bounds__(ROUTE_CHUNK) void k_route_scatter(
 
 constexpr int COMBINE_BATCH = 8;   // slots whose rows are loaded together
 
+// Sorted row r of the routed pairs gets token row_token[r] of a row-major
+// [T, width] byte matrix (width a multiple of 8): one thread per 8 bytes.
+// Rows past the last routed pair (ids on other ranks) are left as they are.
+__global__ __launch_bounds__(256) void k_gather_rows(const uint8_t* __restrict__ src, int width,
+                                                     const int32_t* __restrict__ row_token,
+                                                     const int32_t* __restrict__ n_valid, int64_t P,
+                                                     uint8_t* __restrict__ dst) {
+  const int per = width >> 3;
+  const int64_t rows = min((int64_t)*n_valid, P);
+  const int64_t n = rows * per;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / per;
+    const int c = (int)(i - r * per);
+    *(uint2*)(dst + r * width + c * 8) = *(const uint2*)(src + (int64_t)row_token[r] * width + c * 8);
+  }
+}
+
 // y[t][n] = bf16( sum_j o[t*k + j][n] ) over slots j with a local expert, in j order.
 // o rows already carry the gate weight. One thread per 8 columns (16 bytes).
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
@@ -160,6 +178,16 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, int64_t to
   k_route_scatter<<<nblocks, ROUTE_CHUNK, lds, s>>>(topk_ids, topk_w, P, k, n_experts, rb.block_counts, nblocks,
                                                     rb.expert_off, rb.tile_base, rb.row_token, rb.row_slot,
                                                     rb.row_weight);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const uint8_t* src, int width, const int32_t* row_token, const int32_t* n_valid,
+                              int64_t P, uint8_t* dst, hipStream_t s) {
+  const int64_t n = P * (width / 8);
+  if (n == 0) return hipSuccess;
+  int64_t g = (n + 255) / 256;
+  if (g > 8192) g = 8192;
+  k_gather_rows<<<(int)g, 256, 0, s>>>(src, width, row_token, n_valid, P, dst);
   return hipGetLastError();
 }
 

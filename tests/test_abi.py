@@ -236,3 +236,20 @@ def test_nvfp4_expert_mlp_validation(L):
     assert call(8, 256, 128, 1 << 30, s3=P(257)) == 3
     assert call(8, 256, 128, need - 1) == 5
 
+
+def test_grouped_nvfp4_validation(L):
+    P = ctypes.c_void_p
+
+    def call(k, E, ws, xg=1.0, g1=P(256), s1=P(256)):
+        return L.mx_grouped_nvfp4_expert_mlp(P(256), 8, 256, 128, P(256), P(256), k, E, P(256), s1, g1, P(256),
+                                             P(256), P(256), P(256), P(256), P(256), xg, 1.0, P(256), P(256), ws,
+                                             None)
+    need = L.mx_grouped_nvfp4_expert_mlp_workspace_size(8, 256, 128, 2, 4)
+    assert need > 0
+    assert call(0, 4, 1 << 30) == 2
+    assert call(5, 4, 1 << 30) == 2
+    assert call(2, 4, 1 << 30, xg=0.0) == 7
+    assert call(2, 4, 1 << 30, g1=None) == 1
+    assert call(2, 4, 1 << 30, s1=P(257)) == 3
+    assert call(2, 4, need - 1) == 5
+

@@ -293,3 +293,46 @@ def test_nvfp4_expert_mlp_matches_oracle(mx, M, H, I):
     ref = O.nvfp4_expert_mlp(d["x"], *(d[n] for n in NV_WN), d["xg"], d["hg"])
     assert_mlp_close(y, ref, rel_max=5e-2)
 
+
+# ---------------------------------------------------------------- routed, NVFP4 weights
+def _run_grouped_nvw(mx, d):
+    args = [t(d[n]) for n in NV_WN]
+    y = mx.grouped_nvfp4_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]), *args, float(d["xg"]), float(d["hg"]))
+    torch.cuda.synchronize()
+    return bits(y)
+
+
+def _oracle_grouped_nvw(d, tokens=None):
+    return O.grouped_nvfp4_expert_mlp(d["x"], d["ids"], d["w"], *(d[n] for n in NV_WN), d["xg"], d["hg"],
+                                      tokens=tokens)
+
+
+def test_grouped_nvfp4_weights_matches_oracle(mx):
+    """Per-expert weight globals, an expert with more rows than a tile, an
+    empty expert, duplicated and foreign ids; end-to-end bar of R21."""
+    d = W.grouped_nvfp4(tokens=300, n_experts=6, k=3, seed=4, hidden=256, inter=128)
+    d["ids"][:, 0] = 0                # expert 0: every token (two 256-row tiles)
+    d["ids"][d["ids"] == 5] = 4       # expert 5 empty
+    d["ids"][::7, 2] = -1             # other ranks
+    assert_mlp_close(_run_grouped_nvw(mx, d), _oracle_grouped_nvw(d), rel_max=5e-2)
+    perm = np.random.default_rng(3).permutation(300)
+    dp = dict(d, x=d["x"][perm], ids=d["ids"][perm], w=d["w"][perm])
+    assert np.array_equal(_run_grouped_nvw(mx, dp), _run_grouped_nvw(mx, d)[perm])
+
+
+def test_grouped_nvfp4_weights_single_expert_equals_dense(mx):
+    """E = 1, k = 1, w = 1: the routed path (gathered rows, per-expert globals
+    on the device) equals mx_nvfp4_expert_mlp bit for bit."""
+    d = W.grouped_nvfp4(tokens=300, n_experts=1, k=1, seed=5, hidden=512, inter=256)
+    d["w"] = np.ones_like(d["w"])
+    yg = _run_grouped_nvw(mx, d)
+    args = [t(d[n][0]) if not n.endswith("g") else float(d[n][0]) for n in NV_WN]
+    yd = bits(mx.nvfp4_expert_mlp(bf16_t(d["x"]), *args, float(d["xg"]), float(d["hg"])))
+    assert np.array_equal(yg, yd)
+
+
+def test_grouped_nvfp4_weights_real_shape(mx):
+    """48 experts at 7168 x 3072 with NVFP4 weights: two tokens of a top-8 batch."""
+    d = W.grouped_nvfp4(tokens=2, seed=0)
+    assert_mlp_close(_run_grouped_nvw(mx, d), _oracle_grouped_nvw(d), rel_max=5e-2)
+

@@ -213,3 +213,24 @@ def nvfp4_expert(tokens, hidden=HIDDEN, inter=INTER, seed=0):
              xg=np.float32(2.0 ** -9), hg=np.float32(1.0), x=activations(seed + 1, tokens, hidden))
     return d
 
+
+def grouped_nvfp4(tokens=4096, n_experts=N_LOCAL_EXPERTS, k=TOP_K, seed=0, hidden=HIDDEN, inter=INTER):
+    """Routed experts with NVFP4 weights: per expert, codes and E4M3 scales as
+    ``nvfp4_linear`` and fp32 globals 2^-6 * (1 + (e mod 4) / 4) for w1,
+    2^-5 * (1 + (e mod 3) / 3) for w3 and 2^-6 for w2 (weights seed);
+    activations N(0, 1) (seed + 1) with globals 2^-9 (x) and 1 (h); uniform
+    top-k routing (seed + 2)."""
+    rng = np.random.default_rng(seed)
+    d = {}
+    for n, (r, c) in (("w1", (inter, hidden)), ("w3", (inter, hidden)), ("w2", (hidden, inter))):
+        d[n] = rng.integers(0, 256, (n_experts, r, c // 2), dtype=np.uint8)
+        d[n + "s"] = rng.integers(0x20, 0x58, (n_experts, r, c // 16), dtype=np.uint8)
+    e = np.arange(n_experts)
+    d["w1g"] = (2.0 ** -6 * (1 + (e % 4) / 4)).astype(np.float32)
+    d["w3g"] = (2.0 ** -5 * (1 + (e % 3) / 3)).astype(np.float32)
+    d["w2g"] = np.full(n_experts, 2.0 ** -6, np.float32)
+    d["xg"], d["hg"] = np.float32(2.0 ** -9), np.float32(1.0)
+    d["x"] = activations(seed + 1, tokens, hidden)
+    d["ids"], d["w"] = uniform_routing(seed + 2, tokens, n_experts, k)
+    return d
+
