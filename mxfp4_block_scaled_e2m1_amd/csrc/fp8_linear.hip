@@ -23,8 +23,8 @@
 //    next stage go straight from global memory into the other slot
 //    (GLOBAL_LOAD_LDS_DWORDX4) while the current stage's MFMAs run; one
 //    barrier per stage. Rows are 128 bytes, 16-byte chunk c of row r stored
-//    at chunk c ^ (r % 8), so the 32 rows read by a half-wave spread over all
-//    banks.
+//    at chunk c ^ ((r / 2) % 8), so the 16 rows a quarter-wave reads spread
+//    over all banks.
 //  * The tile's weight scales (2 block rows x K/128 bytes) sit in LDS for the
 //    whole K loop; a wave's 128 weight rows share one byte per stage. Token
 //    scales: one dword (4 chunks) per row and stage, loaded a stage ahead.
@@ -123,8 +123,10 @@ __device__ __forceinline__ void f8_dma16(const void* src, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_off) : "memory", "m0");
 }
 
-// LDS byte offset of 16-byte chunk c of row r in an operand tile.
-__device__ __forceinline__ int f8_off(int r, int c) { return r * F8_BK + ((c ^ (r & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c of row r in an operand tile: the chunk
+// index is XORed with (r / 2) % 8, so the 16 rows that a quarter-wave reads at
+// one chunk fall in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int f8_off(int r, int c) { return r * F8_BK + ((c ^ ((r >> 1) & 7)) << 4); }
 
 __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * F8_SLOT];
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int p = (wave * 4 + c) * 64 + lane;
-    const int r = p >> 3, lc = (p & 7) ^ (r & 7);
+    const int r = p >> 3, lc = (p & 7) ^ ((r >> 1) & 7);
     woff[c] = (uint32_t)((min(n0 + r, a.N - 1) - n0) * K + lc * 16);
     xoff[c] = (uint32_t)((min(m0 + r, a.M - 1) - m0) * K + lc * 16);
   }
