@@ -3,7 +3,9 @@
  *
  * C ABI. Every tensor argument is a DEVICE pointer owned by the caller; the
  * library never allocates device memory, never synchronises the host and never
- * keeps a pointer after a call returns. Work is enqueued on the caller's HIP
+ * keeps a pointer after a call returns -- except the runner (mx_moe_runner_*),
+ * which allocates its workspace and synchronises once when it is created and
+ * destroyed, and keeps the buffers it was created over. Work is enqueued on the caller's HIP
  * stream (`stream` is a hipStream_t; NULL means the default stream). Tensors are
  * row-major and contiguous. bf16 tensors are passed as uint16_t bit patterns;
  * FP4 codes and E8M0/E4M3 scales are raw bytes (a checkpoint's int8 storage is
@@ -23,7 +25,10 @@
  *  - NVFP4 (named, not defined, on "Current Bug: vLLM produces empty/garbage
  *    output", "Revised Plan" Phases 1-2): E2M1 codes as above, one E4M3 scale
  *    per 16 columns [R, C/16] and a positive fp32 global scale g passed by
- *    value; value = e2m1 * e4m3 * g.
+ *    value; value = e2m1 * e4m3 * g. Used for the re-quantised intermediate,
+ *    and for weights and activations by the mx_*nvfp4_* entry points.
+ *  - MXFP8 (activations of the FP8 linear): float8_e4m3fn [R, C] with one E8M0
+ *    scale per 32 columns [R, C/32], shared exponent floor(log2 amax) - 8.
  *
  * The expert MLP ("Current Bug ...", "Revised Plan", Phase 1: L1 GEMM -> SiLU ->
  * re-quant -> L2 GEMM; the shared expert is the MoE pipeline with one expert and
