@@ -141,6 +141,37 @@ def test_shared_expert_real_shape(mx, M):
     assert_mlp_close(y, ref)
 
 
+@pytest.mark.parametrize("M,H,I", [(2, 2048, 1024), (8, 2048, 1024), (8, 1024, 512), (4, 512, 1024)])
+def test_few_tokens_other_shapes(mx, M, H, I):
+    """Few tokens at shapes besides the expert's: 2-step K runs per wave at
+    hidden 2048, one step at hidden 1024 and 512 (intermediate 1024: more
+    weight rows than the hidden size)."""
+    d = W.shared_expert(M, seed=5, hidden=H, inter=I)
+    y, (h,) = _run_dense(mx, d, M, H, I)
+    ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
+    _check_h_and_requant(mx, h, M, I, inter)
+    assert_mlp_close(y, ref)
+
+
+def test_few_tokens_calls_in_a_row(mx):
+    """Calls in a row on one workspace, with different token counts, give the
+    results of calls on fresh workspaces, bit for bit: nothing a call leaves in
+    the workspace (h) leaks into the next."""
+    H, I = 7168, 3072
+    d = W.expert_weights(0)
+    wd = [t(d[n]) for n in WN]
+    xs = {M: bf16_t(W.activations(10 + M, M)) for M in (1, 3, 8)}
+    fresh = {}
+    for M, x in xs.items():
+        ws = torch.empty(mx.expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
+        fresh[M] = bits(mx.expert_mlp(x, *wd, workspace=ws))
+    shared = torch.empty(mx.expert_mlp_workspace_size(8, H, I), dtype=torch.uint8, device="cuda")
+    for M in (8, 1, 3, 8, 1):
+        y = bits(mx.expert_mlp(xs[M], *wd, workspace=shared))
+        assert np.array_equal(y, fresh[M]), M
+    assert_mlp_close(fresh[3], O.expert_mlp(W.activations(13, 3), *[d[n] for n in WN]))
+
+
 @pytest.mark.parametrize("M,H,I", [(130, 2176, 384), (200, 4224, 256), (256, 7168, 3072), (257, 7168, 3072)])
 def test_shared_expert_split_k(mx, M, H, I):
     """A dense L1 of one m-tile splits K over several workgroups (fp32 partials
