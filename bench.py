@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=16,
+    ap.add_argument("--cpu-experts", type=int, default=24,
                     help="experts in the oracle's bounded CPU sample")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one device copy of known size first (for PMC byte-counter scaling)")
@@ -326,12 +326,29 @@ def skewed_nvfp4(torch, mx, workloads):
     return rec
 
 
+def gpu_clocks():
+    """Current shader and memory clocks of card 0 as rocm-smi reports them (None if
+    rocm-smi is missing or fails). Read right after the timed steps."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=10)
+        cards = json.loads(r.stdout)
+        card = cards[sorted(cards)[0]]
+        keep = {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+        return keep or None
+    except Exception:
+        return None
+
+
 def cpu_baseline(d, n_exp):
     """The oracle, untuned, on all pairs routed to experts 0..n_exp-1."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in info}))
     except Exception:
         threads = len(os.sched_getaffinity(0))
     ids = d["ids"].copy()
@@ -342,7 +359,7 @@ def cpu_baseline(d, n_exp):
     sec = time.perf_counter() - t0
     flops = 6.0 * pairs * d["x"].shape[1] * d["w1"].shape[1]
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(sec, 2),
+            "kind": "oracle", "seconds": round(sec, 2), "blas": blas,
             "sample": f"all {pairs} token-expert pairs routed to experts 0..{n_exp - 1} of the same "
                       f"batch (fp64 NumPy oracle, {len(os.sched_getaffinity(0))} host cores visible)"}
 
@@ -379,6 +396,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     ms, phases = time_steps(torch, step, a.steps, a.warmup, profile=(mx.profile_start, mx.profile_stop))
+    clocks = gpu_clocks()
     flops = 6.0 * T * K * H * I
     value = flops / ms / 1e9   # TFLOP/s
     l1_ms, l1_n = phases["l1_gemm"]
@@ -405,6 +423,7 @@ def main():
                      "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": l1_flops, "avg_launch_ms": round(l1_avg, 4)},
         "phases_ms_per_step": {k: round(v[0] / v[1], 4) for k, v in phases.items()},
+        "gpu_clocks_after_timed_steps": clocks,
     }
     if not a.no_secondary:
         rec["secondary"] = secondary(torch, mx, workloads)
