@@ -44,6 +44,11 @@ constexpr int F8_BK = 128;            // K per stage (bytes per row)
 constexpr int F8_OPND = 256 * F8_BK;  // 32 KB per operand and stage
 constexpr int F8_SLOT = 2 * F8_OPND;  // weights + tokens
 constexpr int F8_MAX_KB = 64;         // K / 128 <= 64: weight-scale rows in LDS
+// The bf16 output tile is staged in the K loop's LDS before it is stored:
+// 256 token rows of 512 bytes, pitch 520 so that the 32 rows a wave writes at
+// one column fall in distinct banks (130 dwords = 2 mod 64).
+constexpr int F8_YPITCH = F8_BN * 2 + 8;
+constexpr int F8_SMEM = (2 * F8_SLOT > F8_BM * F8_YPITCH) ? 2 * F8_SLOT : F8_BM * F8_YPITCH;
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -129,7 +134,7 @@ __device__ __forceinline__ void f8_dma16(const void* src, uint32_t lds_off) {
 __device__ __forceinline__ int f8_off(int r, int c) { return r * F8_BK + ((c ^ ((r >> 1) & 7)) << 4); }
 
 __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * F8_SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[F8_SMEM];
   __shared__ uint8_t wsc[2][F8_MAX_KB];
   const int b = blockIdx.x;
   const int L = (b & 7) * a.per_xcd + (b >> 3);
@@ -236,24 +241,31 @@ __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
     }
   }
 
-  // lane holds token m = m0 + 64 wm + 32 g + lane%32 and weight rows
-  // n = n0 + 128 wn + 32 f + 8 (v/4) + 4 (lane/32) + v%4
+  // lane holds token m = 64 wm + 32 g + lane%32 of the tile and weight rows
+  // n = 128 wn + 32 f + 8 (v/4) + 4 (lane/32) + v%4: into LDS as the bf16
+  // tile [m][n], then out in whole rows (a wave stores two 512-byte rows per
+  // instruction instead of 16 bytes in each of 32 rows).
+  __syncthreads();   // every wave's last fragment reads are done
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int m = m0 + wm * 64 + g * 32 + r32;
-    if (m >= a.M) continue;
-    uint16_t* yrow = a.y + (int64_t)m * a.N;
+    uint8_t* yl = smem + (wm * 64 + g * 32 + r32) * F8_YPITCH;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 128 + f * 32 + 8 * q + 4 * half;
-        if (n < a.N) {
-          const uint32_t p0 = bf16x2_rne(acc[f][g][4 * q], acc[f][g][4 * q + 1]);
-          const uint32_t p1 = bf16x2_rne(acc[f][g][4 * q + 2], acc[f][g][4 * q + 3]);
-          *(uint2*)(yrow + n) = make_uint2(p0, p1);
-        }
+        const int n = wn * 128 + f * 32 + 8 * q + 4 * half;
+        const uint32_t p0 = bf16x2_rne(acc[f][g][4 * q], acc[f][g][4 * q + 1]);
+        const uint32_t p1 = bf16x2_rne(acc[f][g][4 * q + 2], acc[f][g][4 * q + 3]);
+        *(uint2*)(yl + n * 2) = make_uint2(p0, p1);
       }
+  }
+  __syncthreads();
+  // 16-byte chunk i of the tile: row i / 32, columns 8 (i % 32) .. + 7
+#pragma unroll 4
+  for (int i = tid; i < F8_BM * 32; i += F8_THREADS) {
+    const int r = i >> 5, c = (i & 31) * 8;
+    const int m = m0 + r, n = n0 + c;
+    if (m < a.M && n < a.N) *(uint4*)(a.y + (int64_t)m * a.N + n) = *(const uint4*)(smem + r * F8_YPITCH + c * 2);
   }
 }
 
