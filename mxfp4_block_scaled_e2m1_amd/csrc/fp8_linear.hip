@@ -32,6 +32,7 @@
 //    taking range b % 8, so the workgroups of one XCD share weight tiles.
 #include "mx_device.h"
 #include "mx_internal.h"
+#include "fp8_linear.h"
 
 namespace mx {
 
@@ -112,8 +113,10 @@ __global__ __launch_bounds__(256) void k_silu_mul_bf16(const uint4* __restrict__
 
 // ------------------------------------------------------------------ GEMM
 struct F8Args {
-  const uint8_t* w;      // [N, K] E4M3
+  const uint8_t* w;      // [N, K] E4M3 (SwiGLU: w1 [N, K])
   const uint8_t* ws;     // [N/128, K/128] E8M0
+  const uint8_t* w3;     // SwiGLU: w3 [N, K] and its scales
+  const uint8_t* w3s;
   const uint8_t* xq;     // [M, K] E4M3
   const uint8_t* xs;     // [M, K/32] E8M0
   uint16_t* y;           // [M, N] bf16
@@ -133,6 +136,14 @@ __device__ __forceinline__ void f8_dma16(const void* src, uint32_t lds_off) {
 // one chunk fall in 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int f8_off(int r, int c) { return r * F8_BK + ((c ^ ((r >> 1) & 7)) << 4); }
 
+// SWIGLU: the tile's 256 weight rows are 128 rows j0 .. j0 + 127 of w1 (gate,
+// tile rows 0..127, waves with wn = 0) and the same rows of w3 (up, tile rows
+// 128..255), j0 = 128 * (n-tile). The epilogue rounds g and u to bf16 in the
+// staged tile, exactly as the plain GEMM stores them, and writes
+// h = bf16(silu(g) * u) with the arithmetic of k_silu_mul_bf16, so the result
+// is that of the two GEMMs and the elementwise kernel, bit for bit, without
+// the g and u round trip through memory.
+template <bool SWIGLU>
 __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[F8_SMEM];
   __shared__ uint8_t wsc[2][F8_MAX_KB];
@@ -140,15 +151,21 @@ __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
   const int L = (b & 7) * a.per_xcd + (b >> 3);
   if (L >= a.tiles_n * a.tiles_m) return;
   const int nt = L / a.tiles_m, mt = L - nt * a.tiles_m;
-  const int n0 = nt * F8_BN, m0 = mt * F8_BM;
+  const int n0 = nt * (SWIGLU ? 128 : F8_BN), m0 = mt * F8_BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int K = a.K, kb128 = K / F8_BK, nst = kb128;
 
-  // weight scales of the tile's two 128-row blocks (the second clamped at the end of W)
+  // weight scales of the tile's two 128-row blocks (the second clamped at the
+  // end of W; SwiGLU: w1's and w3's block of rows n0 .. n0 + 127)
   for (int i = tid; i < 2 * kb128; i += F8_THREADS) {
-    const int br = min(n0 / 128 + i / kb128, a.N / 128 - 1);
-    wsc[i / kb128][i % kb128] = a.ws[(int64_t)br * kb128 + i % kb128];
+    const int blk = i / kb128, col = i - blk * kb128;
+    if constexpr (SWIGLU) {
+      wsc[blk][col] = (blk ? a.w3s : a.ws)[(int64_t)(n0 / 128) * kb128 + col];
+    } else {
+      const int br = min(n0 / 128 + blk, a.N / 128 - 1);
+      wsc[blk][col] = a.ws[(int64_t)br * kb128 + col];
+    }
   }
 
   // Global -> LDS copies (GLOBAL_LOAD_LDS_DWORDX4): wave instruction c of wave
@@ -156,15 +173,18 @@ __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
   // is stored chunk position p % 8 of row p / 8, i.e. logical chunk
   // (p % 8) ^ (row % 8) of that row. Eight lanes cover one 128-byte row.
   // Rows past the end of W or x re-read the last row.
-  const uint8_t* __restrict__ wbase = a.w + (int64_t)n0 * K;
-  const uint8_t* __restrict__ xbase = a.xq + (int64_t)m0 * K;
+  // (SwiGLU: the copies of waves 0..3 are tile rows 0..127, from w1, those of
+  // waves 4..7 rows 128..255, from w3.)
   const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const uint8_t* __restrict__ wbase =
+      SWIGLU ? (wu < 4 ? a.w : a.w3) + (int64_t)n0 * K : a.w + (int64_t)n0 * K;
+  const uint8_t* __restrict__ xbase = a.xq + (int64_t)m0 * K;
   uint32_t woff[4], xoff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int p = (wave * 4 + c) * 64 + lane;
     const int r = p >> 3, lc = (p & 7) ^ ((r >> 1) & 7);
-    woff[c] = (uint32_t)((min(n0 + r, a.N - 1) - n0) * K + lc * 16);
+    woff[c] = (uint32_t)((SWIGLU ? (r & 127) : min(n0 + r, a.N - 1) - n0) * K + lc * 16);
     xoff[c] = (uint32_t)((min(m0 + r, a.M - 1) - m0) * K + lc * 16);
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)smem;
@@ -260,12 +280,32 @@ __global__ __launch_bounds__(F8_THREADS, 1) void k_fp8_gemm(const F8Args a) {
       }
   }
   __syncthreads();
-  // 16-byte chunk i of the tile: row i / 32, columns 8 (i % 32) .. + 7
+  if constexpr (SWIGLU) {
+    // 16-byte chunk i of h: row i / 16, columns 8 (i % 16) .. + 7, from g at
+    // those tile columns and u 128 columns further
 #pragma unroll 4
-  for (int i = tid; i < F8_BM * 32; i += F8_THREADS) {
-    const int r = i >> 5, c = (i & 31) * 8;
-    const int m = m0 + r, n = n0 + c;
-    if (m < a.M && n < a.N) *(uint4*)(a.y + (int64_t)m * a.N + n) = *(const uint4*)(smem + r * F8_YPITCH + c * 2);
+    for (int i = tid; i < F8_BM * 16; i += F8_THREADS) {
+      const int r = i >> 4, c = (i & 15) * 8;
+      const int m = m0 + r;
+      if (m >= a.M) continue;
+      const uint4 gv = *(const uint4*)(smem + r * F8_YPITCH + c * 2);
+      const uint4 uv = *(const uint4*)(smem + r * F8_YPITCH + (128 + c) * 2);
+      const uint32_t ga[4] = {gv.x, gv.y, gv.z, gv.w}, ub[4] = {uv.x, uv.y, uv.z, uv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = bf16x2_rne(silu_mul(bf16_to_f32(ga[q] & 0xFFFFu), bf16_to_f32(ub[q] & 0xFFFFu)),
+                          silu_mul(bf16_to_f32(ga[q] >> 16), bf16_to_f32(ub[q] >> 16)));
+      *(uint4*)(a.y + (int64_t)m * a.N + n0 + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  } else {
+    // 16-byte chunk i of the tile: row i / 32, columns 8 (i % 32) .. + 7
+#pragma unroll 4
+    for (int i = tid; i < F8_BM * 32; i += F8_THREADS) {
+      const int r = i >> 5, c = (i & 31) * 8;
+      const int m = m0 + r, n = n0 + c;
+      if (m < a.M && n < a.N) *(uint4*)(a.y + (int64_t)m * a.N + n) = *(const uint4*)(smem + r * F8_YPITCH + c * 2);
+    }
   }
 }
 
@@ -285,13 +325,29 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* xs, const uint8_t* 
                            int K, uint16_t* y, hipStream_t s) {
   if (M == 0) return hipSuccess;
   F8Args a;
-  a.w = w; a.ws = ws; a.xq = xq; a.xs = xs; a.y = y;
+  a.w = w; a.ws = ws; a.w3 = nullptr; a.w3s = nullptr; a.xq = xq; a.xs = xs; a.y = y;
   a.M = M; a.N = N; a.K = K;
   a.tiles_n = (N + F8_BN - 1) / F8_BN;
   a.tiles_m = (M + F8_BM - 1) / F8_BM;
   const int total = a.tiles_n * a.tiles_m;
   a.per_xcd = (total + 7) / 8;
-  k_fp8_gemm<<<8 * a.per_xcd, F8_THREADS, 0, s>>>(a);
+  k_fp8_gemm<false><<<8 * a.per_xcd, F8_THREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_swiglu(const uint8_t* xq, const uint8_t* xs, const uint8_t* w1, const uint8_t* w1s,
+                             const uint8_t* w3, const uint8_t* w3s, int M, int I, int K, uint16_t* h,
+                             hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (I % 128 != 0) return hipErrorInvalidValue;
+  F8Args a;
+  a.w = w1; a.ws = w1s; a.w3 = w3; a.w3s = w3s; a.xq = xq; a.xs = xs; a.y = h;
+  a.M = M; a.N = I; a.K = K;
+  a.tiles_n = I / 128;
+  a.tiles_m = (M + F8_BM - 1) / F8_BM;
+  const int total = a.tiles_n * a.tiles_m;
+  a.per_xcd = (total + 7) / 8;
+  k_fp8_gemm<true><<<8 * a.per_xcd, F8_THREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@
 #include "../../include/mxfp4.h"
 #include "mx_internal.h"
 #include "nv_linear.h"
+#include "fp8_linear.h"
 
 using namespace mx;
 
@@ -1054,7 +1055,7 @@ size_t mx_fp8_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter
   Carve c(nullptr);
   c.take((size_t)(M * hidden));
   c.take((size_t)(M * (hidden / 32)));
-  for (int i = 0; i < 3; ++i) c.take((size_t)(M * inter * 2));   // g, u, h
+  c.take((size_t)(M * inter * 2));   // h
   c.take((size_t)(M * inter));
   c.take((size_t)(M * (inter / 32)));
   return c.off;
@@ -1086,19 +1087,14 @@ mx_status mx_fp8_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_
   Carve c(workspace);
   uint8_t* xq = (uint8_t*)c.take((size_t)(M * hidden));
   uint8_t* xs = (uint8_t*)c.take((size_t)(M * (hidden / 32)));
-  uint16_t* g = (uint16_t*)c.take((size_t)(M * inter * 2));
-  uint16_t* u = (uint16_t*)c.take((size_t)(M * inter * 2));
   uint16_t* h = (uint16_t*)c.take((size_t)(M * inter * 2));
   uint8_t* hq = (uint8_t*)c.take((size_t)(M * inter));
   uint8_t* hs = (uint8_t*)c.take((size_t)(M * (inter / 32)));
   const int m = (int)M, H = (int)hidden, I = (int)inter;
   MX_HIP(phase("quant_x8", s, [&] { return launch_quant_mxfp8(x, M, hidden, xq, xs, s); }), "quant_x8");
-  MX_HIP(phase("fp8_gemm", s, [&] {
-           hipError_t e = launch_fp8_gemm(xq, xs, w1, w1_s, m, I, H, g, s);
-           if (e != hipSuccess) return e;
-           return launch_fp8_gemm(xq, xs, w3, w3_s, m, I, H, u, s);
-         }), "fp8_gemm_l1");
-  MX_HIP(phase("silu_mul", s, [&] { return launch_silu_mul_bf16(g, u, M * inter, h, s); }), "silu_mul");
+  // gate and up in one GEMM whose epilogue applies SiLU * up to their bf16 outputs
+  MX_HIP(phase("fp8_swiglu", s, [&] { return launch_fp8_swiglu(xq, xs, w1, w1_s, w3, w3_s, m, I, H, h, s); }),
+         "fp8_swiglu");
   MX_HIP(phase("quant_x8", s, [&] { return launch_quant_mxfp8(h, M, inter, hq, hs, s); }), "quant_h8");
   MX_HIP(phase("fp8_gemm", s, [&] { return launch_fp8_gemm(hq, hs, w2, w2_s, m, H, I, y, s); }), "fp8_gemm_l2");
   return ok();

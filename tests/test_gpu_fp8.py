@@ -136,28 +136,32 @@ FP8_WN = ("w1", "w1s", "w3", "w3s", "w2", "w2s")
 @pytest.mark.parametrize("M,H,I", [(5, 256, 128), (300, 512, 384), (64, 7168, 3072)])
 def test_fp8_expert_mlp_matches_oracle(mx, M, H, I):
     """Every stage against the oracle applied to the GPU's own input of that
-    stage (from the workspace): g and u to the FP8 linear's bar; h bit-equal
-    to bf16(silu(g) * u) except near bf16 rounding boundaries (fp32 SiLU);
-    the MXFP8 codes of h bit-exact; y to the linear's bar given h. End to end
-    the cosine stays >= 0.9999; the largest error is allowed 5e-2 of max |y|,
-    since a one-step difference in g or u (the FP8 MFMA's own summation error)
-    can move an element of h across an E4M3 rounding boundary, a step of up to
-    2^-3 of that element."""
+    stage: g and u (the plain FP8 linear on the GPU: the same quantiser and K
+    loop as the gate/up GEMM, whose epilogue rounds them the same way) to the
+    FP8 linear's bar; h (from the workspace) bit-equal to bf16(silu(g) * u)
+    except near bf16 rounding boundaries (fp32 SiLU); the MXFP8 codes of h
+    bit-exact; y to the linear's bar given h. End to end the cosine stays >=
+    0.9999; the largest error is allowed 5e-2 of max |y|, since a one-step
+    difference in g or u (the FP8 MFMA's own summation error) can move an
+    element of h across an E4M3 rounding boundary, a step of up to 2^-3 of
+    that element."""
     from gpu_util import assert_mlp_close, bf16_f64
     d = W.fp8_expert(M, H, I, seed=M + H)
     ws = torch.empty(mx.fp8_expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
-    y = bits(mx.fp8_expert_mlp(bf16_t(d["x"]), *(t(d[n]) for n in FP8_WN), workspace=ws))
+    x = bf16_t(d["x"])
+    y = bits(mx.fp8_expert_mlp(x, *(t(d[n]) for n in FP8_WN), workspace=ws))
     torch.cuda.synchronize()
     al = lambda n: (n + 255) // 256 * 256
-    sizes = [M * H, M * H // 32, M * I * 2, M * I * 2, M * I * 2, M * I, M * I // 32]
+    sizes = [M * H, M * H // 32, M * I * 2, M * I, M * I // 32]
     off, sl = 0, []
     for n in sizes:
         sl.append(ws[off:off + n].cpu().numpy())
         off += al(n)
-    g = sl[2].view(np.uint16).reshape(M, I)
-    u = sl[3].view(np.uint16).reshape(M, I)
-    h = sl[4].view(np.uint16).reshape(M, I)
-    hq, hs = sl[5].reshape(M, I), sl[6].reshape(M, I // 32)
+    assert off == mx.fp8_expert_mlp_workspace_size(M, H, I)
+    g = bits(mx.fp8_block_linear(x, t(d["w1"]), t(d["w1s"])))
+    u = bits(mx.fp8_block_linear(x, t(d["w3"]), t(d["w3s"])))
+    h = sl[2].view(np.uint16).reshape(M, I)
+    hq, hs = sl[3].reshape(M, I), sl[4].reshape(M, I // 32)
     _check_linear(g, O.fp8_block_linear(d["x"], d["w1"], d["w1s"]), *_exact_and_magnitude(d["x"], d["w1"], d["w1s"]))
     _check_linear(u, O.fp8_block_linear(d["x"], d["w3"], d["w3s"]), *_exact_and_magnitude(d["x"], d["w3"], d["w3s"]))
     # h: the GPU's fp32 SiLU (hardware exp2 and reciprocal, a few tens of fp32
