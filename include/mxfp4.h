@@ -321,7 +321,9 @@ MX_API size_t mx_grouped_nvfp4_expert_mlp_workspace_size(int64_t T, int64_t hidd
  * format (page "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", "Status"):
  *   g = FP8LIN(x, w1), u = FP8LIN(x, w3), h = bf16(silu(g) * u), y = FP8LIN(h, w2)
  * with FP8LIN the mx_fp8_block_linear computation (MXFP8 activations, bf16
- * output), so g and u are bf16 before the SiLU.
+ * output), so g and u are bf16 before the SiLU. g and u come from one GEMM
+ * over w1 and w3 whose epilogue forms h, so they are never stored; the
+ * workspace holds the MXFP8 x, h and the MXFP8 h.
  *   x  [M, hidden] bf16; y [M, hidden] bf16
  *   w1, w3 [inter, hidden] e4m3fn, scales [inter/128, hidden/128] E8M0
  *   w2 [hidden, inter] e4m3fn, scales [hidden/128, inter/128] E8M0
