@@ -327,17 +327,23 @@ def skewed_nvfp4(torch, mx, workloads):
 
 
 def gpu_clocks():
-    """Current shader and memory clocks of card 0 as rocm-smi reports them (None if
-    rocm-smi is missing or fails). Read right after the timed steps."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=10)
-        cards = json.loads(r.stdout)
-        card = cards[sorted(cards)[0]]
-        keep = {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
-        return keep or None
-    except Exception:
-        return None
+    """Current shader and memory clock levels of the first GPU, read from the
+    amdgpu sysfs tables that rocm-smi reports (the level marked '*'), right
+    after the timed steps. File reads only: no child process. None where the
+    files are missing."""
+    import glob
+    out = {}
+    for key, name in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/{name}")):
+            try:
+                cur = [ln.split(":", 1)[1].replace("*", "").strip() for ln in open(path).read().splitlines()
+                       if ln.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[key] = cur[0]
+                break
+    return out or None
 
 
 def cpu_baseline(d, n_exp):
