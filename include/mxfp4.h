@@ -24,9 +24,12 @@
  *    value = e4m3 * 2^(b-127).
  *  - NVFP4 (named, not defined, on "Current Bug: vLLM produces empty/garbage
  *    output", "Revised Plan" Phases 1-2): E2M1 codes as above, one E4M3 scale
- *    per 16 columns [R, C/16] and a positive fp32 global scale g passed by
- *    value; value = e2m1 * e4m3 * g. Used for the re-quantised intermediate,
- *    and for weights and activations by the mx_*nvfp4_* entry points.
+ *    per 16 columns [R, C/16] and a positive fp32 global scale g; value =
+ *    e2m1 * e4m3 * g. Used for the re-quantised intermediate (g in DEVICE
+ *    memory: mx_dequant, mx_quantize_act, the MLP entry points and the runner
+ *    take `const float*` and read g in stream order, so the value written by
+ *    mx_nvfp4_global_warmup feeds them without a host read-back), and for
+ *    weights and activations by the mx_*nvfp4_* entry points (host values).
  *  - MXFP8 (activations of the FP8 linear): float8_e4m3fn [R, C] with one E8M0
  *    scale per 32 columns [R, C/32], shared exponent floor(log2 amax) - 8.
  *
@@ -90,45 +93,62 @@ typedef enum mx_format {
 } mx_format;
 
 /*
- * mx_dequant -- dequantise a block-scaled matrix to bf16.
+ * mx_dequant -- dequantise a block-scaled matrix to bf16. The operation is the
+ * pages' offline dequant script: the FP8 weights times their 128 x 128 block
+ * scale, and the packed E2M1 experts through the E2M1 table times 2^(e-127)
+ * with the width doubled ("2026-05-08 DeepSeek V4 Pro NVFP4 Quantization",
+ * section "Script update", items 1-2; shapes in "FP4 (E2M1) expert weight
+ * format confirmed").
  *   MX_FMT_MXFP4:    codes [rows, cols/2], scales [rows, cols/32]; cols % 32 == 0.
  *   MX_FMT_FP8_B128: codes [rows, cols] (e4m3fn), scales [ceil(rows/128), ceil(cols/128)];
  *                    cols % 16 == 0.
- *   MX_FMT_NVFP4:    codes [rows, cols/2], scales [rows, cols/16] (e4m3fn), global_scale = g;
- *                    cols % 16 == 0.
- * global_scale is ignored except for NVFP4. out_bf16 is [rows, cols].
+ *   MX_FMT_NVFP4:    codes [rows, cols/2], scales [rows, cols/16] (e4m3fn), global_scale:
+ *                    DEVICE pointer to g (required: MX_ERR_NULL if NULL); cols % 16 == 0.
+ * global_scale is ignored (may be NULL) except for NVFP4. out_bf16 is [rows, cols].
  * Exact: every MXFP4 and FP8 product is representable in bf16 unless it
  * overflows (then +-inf); NVFP4 products are rounded to bf16 once (RNE).
- * Alignment: codes and out_bf16 16 bytes (NVFP4 codes 8 bytes).
+ * Alignment: codes and out_bf16 16 bytes (NVFP4 codes 8 bytes), global_scale 4.
  */
-MX_API mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales, float global_scale,
+MX_API mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales, const float* global_scale,
                      int64_t rows, int64_t cols, uint16_t* out_bf16, void* stream);
 
 /*
- * mx_quantize_act -- quantise bf16 activations x [rows, cols] per row.
+ * mx_quantize_act -- quantise bf16 activations x [rows, cols] per row: the
+ * quantisation step before each FP4 GEMM of the pages' pipeline (page
+ * "Current Bug: vLLM produces empty/garbage output", section "Revised Plan",
+ * Phase 1: L1 GEMM, SiLU, re-quant, L2 GEMM), in the MXFP4 format of
+ * "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", "Script update" item 2.
  *   MX_FMT_MXFP4: codes [rows, cols/2], scales [rows, cols/32] (E8M0); cols % 32 == 0.
- *   MX_FMT_NVFP4: codes [rows, cols/2], scales [rows, cols/16] (E4M3), global_scale = g > 0
- *                 finite and >= 2^-117. Steps in fp32: s = E4M3_RNE_sat(amax / (6 g)),
+ *   MX_FMT_NVFP4: codes [rows, cols/2], scales [rows, cols/16] (E4M3), global_scale: DEVICE
+ *                 pointer to g (required), g > 0 finite and >= 2^-117 (not checked: the
+ *                 value lives on the device). Steps in fp32: s = E4M3_RNE_sat(amax / (6 g)),
  *                 code = E2M1_RNE_sat(x / (s g)); s == 0 gives signed zero codes.
  *   MX_FMT_MXFP8: codes [rows, cols] (e4m3fn), scales [rows, cols/32] (E8M0); cols % 32 == 0.
  *                 Scale byte clamp(floor(log2 amax) - 8 + 127, 0, 254); elements
  *                 rounded to nearest even E4M3, saturating at +-448, sign kept.
- * Alignment: x and codes 16 bytes (NVFP4 codes 8 bytes).
+ * Alignment: x and codes 16 bytes (NVFP4 codes 8 bytes), global_scale 4.
  */
 MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t rows, int64_t cols,
-                          float global_scale, uint8_t* codes, uint8_t* scales, void* stream);
+                          const float* global_scale, uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
- * mx_expert_mlp -- one expert (the shared expert), M tokens, no routing.
+ * mx_expert_mlp -- one expert (the shared expert), M tokens, no routing: the
+ * pages' shared-expert pipeline L1 GEMM -> SiLU -> re-quant -> L2 GEMM, the MoE
+ * pipeline with one group and no routing (page "Current Bug: vLLM produces
+ * empty/garbage output", section "Revised Plan", Phase 1; BF16 SiLU output per
+ * Phase 3; weight shapes from "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization",
+ * "FP4 (E2M1) expert weight format confirmed").
  *   x  [M, hidden] bf16            w1, w3 codes [inter, hidden/2], scales [inter, hidden/32]
  *   y  [M, hidden] bf16            w2 codes [hidden, inter/2], scales [hidden, inter/32]
  * hidden % 128 == 0 and inter % 128 == 0.
  * requant selects the format of the intermediate h between the two GEMMs:
  *   MX_FMT_MXFP4: E8M0 per 32 (requant_global ignored); both GEMMs run on FP4
  *     matrix cores. M <= 8 takes the weight-streaming few-token kernels.
- *   MX_FMT_NVFP4: E4M3 per 16 with the fp32 global scale requant_global = g
- *     (finite, >= 2^-117, else MX_ERR_VALUE); the L2 GEMM runs on bf16 matrix
- *     cores on exactly dequantised operands, y = bf16(g * sum (code*s)(w)).
+ *   MX_FMT_NVFP4: E4M3 per 16 with the fp32 global scale g at the DEVICE
+ *     pointer requant_global (required; g finite and >= 2^-117, not checked,
+ *     read in stream order, e.g. straight from mx_nvfp4_global_warmup); the L2
+ *     GEMM runs on bf16 matrix cores on exactly dequantised operands,
+ *     y = bf16(g * sum (code*s)(w)).
  *     Exact for w2 scale bytes <= 252 (6 * 2^126 exceeds bf16 above that).
  *   anything else: MX_ERR_FORMAT.
  * A stacked gate_up tensor [2*inter, hidden/2] is passed as w1 = w13 and
@@ -138,18 +158,25 @@ MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t 
  * reads the weight scales from it; the results are identical either way.
  * workspace: device memory of at least mx_expert_mlp_workspace_size() bytes,
  * 256-byte aligned; its contents are scratch. y must not alias x or workspace.
- * Alignment: x, y, codes 16 bytes; scales 4 bytes.
+ * Alignment: x, y, codes 16 bytes; scales and requant_global 4 bytes.
  */
 MX_API mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter,
                         const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                         const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                        const uint8_t* packed_scales, mx_format requant, float requant_global,
+                        const uint8_t* packed_scales, mx_format requant, const float* requant_global,
                         uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of mx_expert_mlp for these sizes (the caller-owned scratch of
+ * the pages' pre-allocated runner: "Current Bug ...", "Revised Plan", Phase 1);
+ * 0 for negative sizes. */
 MX_API size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter, mx_format requant);
 
 /*
- * mx_grouped_expert_mlp -- E local routed experts as a ragged grouped GEMM.
+ * mx_grouped_expert_mlp -- E local routed experts as a ragged grouped GEMM: the
+ * pages' MoE pipeline (routing, top-k, scatter around the same L1 GEMM -> SiLU
+ * -> re-quant -> L2 GEMM; page "Current Bug: vLLM produces empty/garbage
+ * output", section "Revised Plan", Phase 1, with the final scatter in BF16 per
+ * Phase 3), for the 48 experts of one expert-parallel rank ("Config values").
  *   x        [T, hidden] bf16 tokens
  *   topk_ids [T, k] int32 expert of each (token, slot); ids outside [0, E) are skipped
  *   topk_w   [T, k] fp32 gate weight of each (token, slot)
@@ -170,9 +197,11 @@ MX_API mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hid
                                 const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                 const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                                 const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                                const uint8_t* packed_scales, mx_format requant, float requant_global,
+                                const uint8_t* packed_scales, mx_format requant, const float* requant_global,
                                 uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of mx_grouped_expert_mlp for these sizes (caller-owned
+ * scratch, as for mx_expert_mlp_workspace_size); 0 for invalid sizes. */
 MX_API size_t mx_grouped_expert_mlp_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k,
                                             int32_t E, mx_format requant);
 
@@ -211,8 +240,8 @@ MX_API size_t mx_packed_weight_scales_size(int64_t hidden, int64_t inter, int32_
  *     and topk_w, E are ignored (packed_scales then holds one expert).
  *   otherwise: routed exactly as mx_grouped_expert_mlp (topk_ids, topk_w, k, E).
  *   w1, w3 (and scales) as for mx_expert_mlp / mx_grouped_expert_mlp; w2 is not read.
- *   global_out: one fp32 in device memory, written by the call in stream order
- *     (read it back once, then pass it as requant_global).
+ *   global_out: one fp32 in device memory, written by the call in stream order;
+ *     pass the same pointer as requant_global (no host read-back needed).
  * workspace: mx_nvfp4_global_warmup_workspace_size(T, hidden, inter, k, E) bytes
  * (k = 0 for one expert), 256-byte aligned; contents are scratch.
  * Alignment as for the MLP entry points; global_out 4 bytes.
@@ -338,7 +367,9 @@ MX_API mx_status mx_fp8_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden,
 MX_API size_t mx_fp8_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter);
 
 /*
- * mx_debug_gemm_f32 -- test hook, not part of the hot path: C[M, N] = A . B^T in fp32
+ * mx_debug_gemm_f32 -- test hook, not part of the hot path: the L1/L2 contraction of
+ * the pages' pipeline ("Current Bug ...", "Revised Plan", Phase 1) with an fp32
+ * output instead of the fused epilogues: C[M, N] = A . B^T in fp32
  * for MXFP4 A (codes [M, K/2], scales [M, K/32]) and B (codes [N, K/2], scales
  * [N, K/32]) through the same scaled-MFMA kernel as the MLP. K % 128 == 0,
  * N % 4 == 0. Alignment: codes and c 16 bytes, scales 4 bytes.
@@ -356,12 +387,16 @@ MX_API mx_status mx_debug_gemm_f32(const uint8_t* a, const uint8_t* a_s, const u
  * "Current Bug: vLLM produces empty/garbage output", section "Revised Plan",
  * Phase 1).
  *   create: the arguments of mx_grouped_expert_mlp (T >= 1) without workspace
- *     and stream. It runs the call once eagerly (validating every argument; on
- *     failure nothing is captured and *out stays NULL), synchronises, then
- *     captures it on a private stream. requant_global and every pointer are
- *     fixed in the graph. Fails with MX_ERR_VALUE while mx_profile_start() is on.
+ *     and stream. It waits for the device to finish the work already enqueued
+ *     (so inputs just written on any stream are seen), runs the call once
+ *     eagerly on a private stream (validating every argument; on failure nothing
+ *     is captured and *out stays NULL), synchronises, then captures it. Every
+ *     pointer is fixed in the graph; the NVFP4 global is read from
+ *     *requant_global at each replay. Fails with MX_ERR_VALUE while
+ *     mx_profile_start() is on.
  *   replay: the captured call on `stream`, reading the current contents of x,
- *     topk_ids and topk_w (the caller refreshes them in place) and writing y.
+ *     topk_ids, topk_w and *requant_global (the caller refreshes them in place)
+ *     and writing y.
  *     Replays on one runner must not overlap (they share the workspace).
  *   destroy: waits for the runner's stream, frees the graph and the workspace.
  *     The caller must have finished its replays (synchronise their streams).
@@ -372,17 +407,21 @@ MX_API mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidd
                                       const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                       const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                                       const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                                      const uint8_t* packed_scales, mx_format requant, float requant_global,
-                                      uint16_t* y, mx_moe_runner** out);
+                                      const uint8_t* packed_scales, mx_format requant,
+                                      const float* requant_global, uint16_t* y, mx_moe_runner** out);
 MX_API mx_status mx_moe_runner_replay(mx_moe_runner* r, void* stream);
 MX_API mx_status mx_moe_runner_destroy(mx_moe_runner* r);
 
-/* Status text (static) and the calling thread's last error detail. */
+/* Status text (static) and the calling thread's last error detail: the clear
+ * failure messages the pages' debugging history calls for (wrong scale
+ * handling, shape mistakes: "2026-05-11 - DeepSeek V4 NVFP4 vLLM Serving: Full
+ * End-to-End", "What We Fixed" and "Outstanding Issues"). */
 MX_API const char* mx_status_string(mx_status s);
 MX_API const char* mx_last_error(void);
 
 /*
- * Profiler: while enabled, every kernel the library enqueues is bracketed by two
+ * Profiler (measurement support, not a step of the pages' pipeline): while
+ * enabled, every kernel the library enqueues is bracketed by two
  * hipEvents recorded on the same stream. mx_profile_stop() waits for them and
  * returns, per kernel name, the summed duration and the launch count.
  */

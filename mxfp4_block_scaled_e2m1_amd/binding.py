@@ -30,15 +30,15 @@ class PhaseStat(ctypes.Structure):
 
 
 SIGNATURES = {
-    "mx_dequant": (_I32, [_I32, _P, _P, _F, _I64, _I64, _P, _P]),
-    "mx_quantize_act": (_I32, [_I32, _P, _I64, _I64, _F, _P, _P, _P]),
-    "mx_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _F, _P, _P, _SZ, _P]),
+    "mx_dequant": (_I32, [_I32, _P, _P, _P, _I64, _I64, _P, _P]),
+    "mx_quantize_act": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P, _P]),
+    "mx_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "mx_nvfp4_global_warmup": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                       _P]),
     "mx_nvfp4_global_warmup_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "mx_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "mx_grouped_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                     _P, _I32, _F, _P, _P, _SZ, _P]),
+                                     _P, _I32, _P, _P, _P, _SZ, _P]),
     "mx_grouped_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
     "mx_pack_weight_scales": (_I32, [_P, _P, _P, _I64, _I64, _I32, _P, _SZ, _P]),
     "mx_packed_weight_scales_size": (_SZ, [_I64, _I64, _I32]),
@@ -56,7 +56,7 @@ SIGNATURES = {
     "mx_fp8_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mx_fp8_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "mx_moe_runner_create": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32,
-                                    _F, _P, ctypes.POINTER(_P)]),
+                                    _P, _P, ctypes.POINTER(_P)]),
     "mx_moe_runner_replay": (_I32, [_P, _P]),
     "mx_moe_runner_destroy": (_I32, [_P]),
     "mx_status_string": (ctypes.c_char_p, [_I32]),
@@ -115,20 +115,36 @@ def _fmt(f) -> int:
     return MX_FMT[f] if isinstance(f, str) else int(f)
 
 
+def _global(g, device):
+    """An NVFP4 global scale as the library takes it: a one-element fp32 device
+    tensor (passed through), a Python float (copied into a new device tensor),
+    or None. Returns the tensor, which the caller keeps alive until the call
+    that reads it has run (stream order makes a temporary safe)."""
+    if g is None:
+        return None
+    if isinstance(g, torch.Tensor):
+        if g.dtype != torch.float32 or g.numel() != 1:
+            raise ValueError("a global scale tensor must hold one fp32 value")
+        return g
+    return torch.tensor([float(g)], dtype=torch.float32, device=device)
+
+
 # ---------------------------------------------------------------------------
 
-def dequant(fmt, codes, scales, rows: int, cols: int, global_scale: float = 0.0, out=None, stream=None):
-    """mx_dequant -> bf16 tensor [rows, cols]."""
+def dequant(fmt, codes, scales, rows: int, cols: int, global_scale=None, out=None, stream=None):
+    """mx_dequant -> bf16 tensor [rows, cols]. global_scale (NVFP4): float or
+    one-element fp32 device tensor."""
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
-    _check(lib().mx_dequant(_fmt(fmt), _ptr(codes), _ptr(scales), float(global_scale), rows, cols,
+    g = _global(global_scale, codes.device)
+    _check(lib().mx_dequant(_fmt(fmt), _ptr(codes), _ptr(scales), _ptr(g), rows, cols,
                             _ptr(out), _stream(stream)))
     return out
 
 
-def quantize_act(fmt, x, global_scale: float = 0.0, codes=None, scales=None, stream=None):
+def quantize_act(fmt, x, global_scale=None, codes=None, scales=None, stream=None):
     """mx_quantize_act: bf16 x [rows, cols] -> (codes [rows, cols/2], or [rows, cols]
-    for MXFP8, scales)."""
+    for MXFP8, scales). global_scale (NVFP4): float or one-element fp32 device tensor."""
     rows, cols = x.shape
     f = _fmt(fmt)
     per = 16 if f == MX_FMT["nvfp4"] else 32
@@ -137,7 +153,8 @@ def quantize_act(fmt, x, global_scale: float = 0.0, codes=None, scales=None, str
         codes = torch.empty((rows, width), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, cols // per), dtype=torch.uint8, device=x.device)
-    _check(lib().mx_quantize_act(f, _ptr(x), rows, cols, float(global_scale), _ptr(codes), _ptr(scales),
+    g = _global(global_scale, x.device)
+    _check(lib().mx_quantize_act(f, _ptr(x), rows, cols, _ptr(g), _ptr(codes), _ptr(scales),
                                  _stream(stream)))
     return codes, scales
 
@@ -173,24 +190,27 @@ def pack_weight_scales(w1s, w3s, w2s, out=None, stream=None):
     return out
 
 
-def expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global: float = 0.0,
+def expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global=None,
                out=None, workspace=None, stream=None, packed_scales=None):
-    """mx_expert_mlp: the shared expert on bf16 x [M, hidden] -> bf16 y [M, hidden]."""
+    """mx_expert_mlp: the shared expert on bf16 x [M, hidden] -> bf16 y [M, hidden].
+    requant_global (NVFP4): float or one-element fp32 device tensor."""
     M, hidden = x.shape
     inter = w1.shape[0]
     if out is None:
         out = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
     nbytes = expert_mlp_workspace_size(M, hidden, inter, requant)
     ws = _workspace(nbytes, x.device, workspace)
+    g = _global(requant_global, x.device)
     _check(lib().mx_expert_mlp(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s),
-                               _ptr(w2), _ptr(w2s), _ptr(packed_scales), _fmt(requant), float(requant_global),
+                               _ptr(w2), _ptr(w2s), _ptr(packed_scales), _fmt(requant), _ptr(g),
                                _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
 def grouped_expert_mlp(x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4",
-                       requant_global: float = 0.0, out=None, workspace=None, stream=None, packed_scales=None):
-    """mx_grouped_expert_mlp: routed experts, stacked weights [E, ...]."""
+                       requant_global=None, out=None, workspace=None, stream=None, packed_scales=None):
+    """mx_grouped_expert_mlp: routed experts, stacked weights [E, ...]. requant_global
+    (NVFP4): float or one-element fp32 device tensor."""
     T, hidden = x.shape
     k = topk_ids.shape[1]
     E, inter = w1.shape[0], w1.shape[1]
@@ -198,9 +218,10 @@ def grouped_expert_mlp(x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="
         out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
     nbytes = grouped_expert_mlp_workspace_size(T, hidden, inter, k, E, requant)
     ws = _workspace(nbytes, x.device, workspace)
+    g = _global(requant_global, x.device)
     _check(lib().mx_grouped_expert_mlp(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
                                        _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2), _ptr(w2s),
-                                       _ptr(packed_scales), _fmt(requant), float(requant_global), _ptr(out),
+                                       _ptr(packed_scales), _fmt(requant), _ptr(g), _ptr(out),
                                        _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
@@ -335,20 +356,22 @@ def fp8_expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, out=None, workspace=None, strea
 
 class MoeRunner:
     """mx_moe_runner: the routed experts over fixed device buffers, captured once
-    into a hipGraph. Refresh x, topk_ids and topk_w in place, then replay()."""
+    into a hipGraph. Refresh x, topk_ids, topk_w (and the NVFP4 global tensor) in
+    place, then replay()."""
 
     def __init__(self, x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4",
-                 requant_global: float = 0.0, out=None, packed_scales=None):
+                 requant_global=None, out=None, packed_scales=None):
         T, hidden = x.shape
         k = topk_ids.shape[1]
         E, inter = w1.shape[0], w1.shape[1]
         self.out = out if out is not None else torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
+        g = _global(requant_global, x.device)
         # keep the bound tensors alive as long as the runner
-        self._bound = (x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, packed_scales, self.out)
+        self._bound = (x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, packed_scales, self.out, g)
         h = _P()
         _check(lib().mx_moe_runner_create(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
                                           _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2), _ptr(w2s),
-                                          _ptr(packed_scales), _fmt(requant), float(requant_global),
+                                          _ptr(packed_scales), _fmt(requant), _ptr(g),
                                           _ptr(self.out), ctypes.byref(h)))
         self._h = h
 

@@ -556,13 +556,15 @@ template <int OP, int NS>
 __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
                                                      const int32_t* __restrict__ expert_off,
                                                      const int32_t* __restrict__ row_slot,
-                                                     const float* __restrict__ row_weight, float scale, int H, int I,
+                                                     const float* __restrict__ row_weight, float scale_val,
+                                                     const float* __restrict__ scale_ptr, int H, int I,
                                                      const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
                                                      uint16_t* __restrict__ o) {
   __shared__ RoutedLds L;
   const int e = blockIdx.y;
   const int base = expert_off[e], rows = expert_off[e + 1] - base;
   if (rows <= 0) return;
+  const float scale = scale_ptr != nullptr ? *scale_ptr : scale_val;
   const int n0 = blockIdx.x * 16;
   const int64_t kb = I / 2, ks = I / 32;
   const int64_t we = (int64_t)e * H * kb, se = (int64_t)e * H * ks;
@@ -671,7 +673,7 @@ void launch_routed_l1_ns(const RoutedArgs& a, hipStream_t s) {
 template <int OP, int NS>
 void launch_routed_l2_ns(const RoutedArgs& a, hipStream_t s) {
   k_routed_l2<OP, NS><<<dim3(a.H / 16, a.E), DT, 0, s>>>(a.hq, a.hs, a.expert_off, a.row_slot, a.row_weight,
-                                                          a.scale, a.H, a.I, a.w2, a.w2s, a.o);
+                                                          a.scale, a.scale_ptr, a.H, a.I, a.w2, a.w2s, a.o);
 }
 
 template <int OP>

@@ -133,10 +133,10 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
 // NVFP4 dequant: one thread per 16 elements (8 code bytes, 1 E4M3 scale byte).
 __global__ __launch_bounds__(EW_THREADS) void k_dequant_nvfp4(const uint2* __restrict__ codes,
                                                               const uint8_t* __restrict__ scales,
-                                                              float global, uint4* __restrict__ out,
-                                                              int64_t nblk) {
+                                                              float global, const float* __restrict__ gptr,
+                                                              uint4* __restrict__ out, int64_t nblk) {
   const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
-  const double g = (double)global;
+  const double g = (double)(gptr != nullptr ? *gptr : global);
   for (int64_t b = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; b < nblk; b += stride) {
     const uint2 c = codes[b];
     const double s = (double)e4m3_to_f32(scales[b]) * g;   // exact: 4 x 24 significant bits
@@ -188,10 +188,12 @@ __global__ __launch_bounds__(EW_THREADS) void k_quant_mxfp4(const uint4* __restr
 // NVFP4 quantise: one thread per 16 elements (32 bytes in, 8 code bytes + one
 // E4M3 byte out). fp32 steps: t = 6 g; r = amax / t; s = E4M3(r); d = s g;
 // v = x / d; code = E2M1(v) (|v| clamped to 6, which is what saturation gives).
-__global__ __launch_bounds__(EW_THREADS) void k_quant_nvfp4(const uint4* __restrict__ x, float g,
+__global__ __launch_bounds__(EW_THREADS) void k_quant_nvfp4(const uint4* __restrict__ x, float gval,
+                                                            const float* __restrict__ gptr,
                                                             uint2* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, int64_t nblk) {
   const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
+  const float g = gptr != nullptr ? *gptr : gval;
   const float t6 = 6.0f * g;
   for (int64_t b = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; b < nblk; b += stride) {
     uint32_t w[8];
@@ -267,11 +269,11 @@ hipError_t launch_dequant_fp8_block(const uint8_t* q, const uint8_t* scales, int
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, float global,
+hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, float global, const float* gptr,
                                 int64_t rows, int64_t cols, uint16_t* out, hipStream_t s) {
   const int64_t nblk = rows * (cols / 16);
   if (nblk == 0) return hipSuccess;
-  k_dequant_nvfp4<<<ew_grid(nblk), EW_THREADS, 0, s>>>((const uint2*)codes, scales, global,
+  k_dequant_nvfp4<<<ew_grid(nblk), EW_THREADS, 0, s>>>((const uint2*)codes, scales, global, gptr,
                                                        (uint4*)out, nblk);
   return hipGetLastError();
 }
@@ -294,11 +296,11 @@ hipError_t launch_nvfp4_global(const uint32_t* amax, float* g, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, float global,
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, float global, const float* gptr,
                               uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const int64_t nblk = rows * (cols / 16);
   if (nblk == 0) return hipSuccess;
-  k_quant_nvfp4<<<ew_grid(nblk), EW_THREADS, 0, s>>>((const uint4*)x, global, (uint2*)codes, scales,
+  k_quant_nvfp4<<<ew_grid(nblk), EW_THREADS, 0, s>>>((const uint4*)x, global, gptr, (uint2*)codes, scales,
                                                      nblk);
   return hipGetLastError();
 }

@@ -175,7 +175,7 @@ __device__ __forceinline__ uint32_t l1_block(const GemmArgs& a, const Tile& t, c
     }
   } else {
     // NVFP4: 16-blocks j0..j0+15 (v = 0..7) and j0+16..j0+31 (v = 8..15).
-    const float gsc = a.nv_global;
+    const float gsc = a.nv_gptr != nullptr ? *a.nv_gptr : a.nv_global;
     const float t6 = 6.0f * gsc;
     uint32_t w01[2];
     uint32_t sbytes[2];

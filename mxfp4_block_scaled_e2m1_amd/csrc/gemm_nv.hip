@@ -179,7 +179,8 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
     stage(st, ra, rb);
     if (st + 1 < nst) stage(st + 1, rb, ra);
   }
-  const float scale = a.e_global != nullptr ? a.nv_global * a.e_global[t.e] : a.nv_global;
+  const float g = a.nv_gptr != nullptr ? *a.nv_gptr : a.nv_global;
+  const float scale = a.e_global != nullptr ? g * a.e_global[t.e] : g;
   store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, scale, smem, GEMM_THREADS);
 }
 

@@ -237,9 +237,17 @@ mx_status check_global(float g) {
   return MX_OK;
 }
 
-mx_status check_requant(mx_format rq, float g) {
+// A global scale in device memory: present and 4-byte aligned. Its value is
+// read by the kernels in stream order, so the host cannot check it.
+mx_status check_global_ptr(const float* g) {
+  if (g == nullptr) return fail(MX_ERR_NULL, "the NVFP4 global scale pointer is NULL");
+  if (!aligned(g, 4)) return fail(MX_ERR_ALIGN, "the NVFP4 global scale pointer is not 4-byte aligned");
+  return MX_OK;
+}
+
+mx_status check_requant(mx_format rq, const float* g) {
   if (rq == MX_FMT_MXFP4) return MX_OK;
-  if (rq == MX_FMT_NVFP4) return check_global(g);
+  if (rq == MX_FMT_NVFP4) return check_global_ptr(g);
   return fail(MX_ERR_FORMAT, "requant format %d is not MXFP4 or NVFP4", (int)rq);
 }
 
@@ -322,7 +330,7 @@ mx_status mx_profile_stop(mx_phase_stat* stats, int32_t max_stats, int32_t* n_st
   return st;
 }
 
-mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales, float global_scale,
+mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales, const float* global_scale,
                      int64_t rows, int64_t cols, uint16_t* out, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (rows < 0 || cols < 0) return fail(MX_ERR_SHAPE, "rows %lld / cols %lld negative", (long long)rows, (long long)cols);
@@ -351,10 +359,10 @@ mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales, float
       return launch_dequant_fp8_block((const uint8_t*)codes, (const uint8_t*)scales, rows, cols, out, s);
     });
   } else {
-    MX_TRY(check_global(global_scale));
+    MX_TRY(check_global_ptr(global_scale));
     MX_REQUIRE_ALIGN(codes, 8);
     e = phase("dequant_nvfp4", s, [&] {
-      return launch_dequant_nvfp4((const uint8_t*)codes, (const uint8_t*)scales, global_scale, rows, cols,
+      return launch_dequant_nvfp4((const uint8_t*)codes, (const uint8_t*)scales, 0.0f, global_scale, rows, cols,
                                   out, s);
     });
   }
@@ -362,8 +370,8 @@ mx_status mx_dequant(mx_format fmt, const void* codes, const void* scales, float
   return ok();
 }
 
-mx_status mx_quantize_act(mx_format fmt, const uint16_t* x, int64_t rows, int64_t cols, float global_scale,
-                          uint8_t* codes, uint8_t* scales, void* stream) {
+mx_status mx_quantize_act(mx_format fmt, const uint16_t* x, int64_t rows, int64_t cols,
+                          const float* global_scale, uint8_t* codes, uint8_t* scales, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (rows < 0 || cols < 0) return fail(MX_ERR_SHAPE, "rows %lld / cols %lld negative", (long long)rows, (long long)cols);
   if (rows * cols > ((int64_t)1 << 40)) return fail(MX_ERR_SHAPE, "matrix too large");
@@ -371,7 +379,7 @@ mx_status mx_quantize_act(mx_format fmt, const uint16_t* x, int64_t rows, int64_
     if (cols % 32 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 32 != 0", (long long)cols);
   } else if (fmt == MX_FMT_NVFP4) {
     if (cols % 16 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 16 != 0", (long long)cols);
-    MX_TRY(check_global(global_scale));
+    MX_TRY(check_global_ptr(global_scale));
   } else if (fmt == MX_FMT_MXFP8) {
     if (cols % 32 != 0) return fail(MX_ERR_SHAPE, "cols %lld %% 32 != 0", (long long)cols);
   } else {
@@ -391,7 +399,7 @@ mx_status mx_quantize_act(mx_format fmt, const uint16_t* x, int64_t rows, int64_
     e = phase("quant_mxfp8", s, [&] { return launch_quant_mxfp8(x, rows, cols, codes, scales, s); });
   } else {
     MX_REQUIRE_ALIGN(codes, 8);
-    e = phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, rows, cols, global_scale, codes, scales, s); });
+    e = phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, rows, cols, 0.0f, global_scale, codes, scales, s); });
   }
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return ok();
@@ -456,8 +464,8 @@ mx_status mx_pack_weight_scales(const uint8_t* w1_s, const uint8_t* w3_s, const 
 
 mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, const uint8_t* w1,
                         const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s, const uint8_t* w2,
-                        const uint8_t* w2_s, const uint8_t* packed_scales, mx_format requant, float requant_global,
-                        uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+                        const uint8_t* w2_s, const uint8_t* packed_scales, mx_format requant,
+                        const float* requant_global, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   MX_TRY(check_mlp_dims(M, hidden, inter));
   MX_TRY(check_requant(requant, requant_global));
@@ -508,7 +516,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   l1.m_rows = m; l1.n_experts = 1;
   l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
   l1.grid_tiles = mtiles * l1.n_tiles;
-  l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_global = requant_global;
+  l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_gptr = requant_global;
   l1.h_scales_packed = requant == MX_FMT_MXFP4;
   const Epilogue l1_epi = requant == MX_FMT_NVFP4 ? EPI_SWIGLU_NVFP4 : EPI_SWIGLU_MXFP4;
   if (w.l1_split > 1) {
@@ -535,7 +543,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   l2.grid_tiles = mtiles * l2.n_tiles;
   l2.out_bf16 = y;
   if (requant == MX_FMT_NVFP4) {
-    l2.nv_global = requant_global;
+    l2.nv_gptr = requant_global;
     MX_HIP(phase("l2_gemm_bf16", s, [&] { return launch_gemm_nv_l2(l2, l2.grid_tiles, s); }), "l2_gemm_bf16");
   } else {
     MX_HIP(phase("l2_gemm", s, [&] { return launch_gemm(EPI_BF16, l2, l2.grid_tiles, s); }), "l2_gemm");
@@ -547,7 +555,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
                                 const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                 const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
                                 const uint8_t* w2, const uint8_t* w2_s, const uint8_t* packed_scales,
-                                mx_format requant, float requant_global, uint16_t* y, void* workspace,
+                                mx_format requant, const float* requant_global, uint16_t* y, void* workspace,
                                 size_t ws_bytes, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   MX_TRY(check_mlp_dims(T, hidden, inter));
@@ -587,12 +595,13 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
     ra.row_weight = w.rb.row_weight;
     ra.w1 = w1; ra.w1s = w1_s; ra.w3 = w3; ra.w3s = w3_s; ra.w2 = w2; ra.w2s = w2_s;
     ra.h = w.h; ra.hq = w.hq; ra.hs = w.hs; ra.nvfp4 = requant == MX_FMT_NVFP4;
-    ra.scale = requant == MX_FMT_NVFP4 ? requant_global : 1.0f;
+    ra.scale = 1.0f;
+    ra.scale_ptr = requant == MX_FMT_NVFP4 ? requant_global : nullptr;
     ra.o = w.o;
     MX_HIP(phase("l1_stream", s, [&] { return launch_routed_l1(ra, s); }), "l1_stream");
     MX_HIP(phase("requant_h", s, [&] {
              if (requant == MX_FMT_MXFP4) return launch_quant_mxfp4(w.h, P, inter, w.hq, w.hs, s);
-             return launch_quant_nvfp4(w.h, P, inter, requant_global, w.hq, w.hs, s);
+             return launch_quant_nvfp4(w.h, P, inter, 0.0f, requant_global, w.hq, w.hs, s);
            }), "requant_h");
     MX_HIP(phase("l2_stream", s, [&] { return launch_routed_l2(ra, s); }), "l2_stream");
     MX_HIP(phase("combine", s, [&] { return launch_combine(w.o, topk_ids, T, k, E, H, y, s); }), "combine");
@@ -613,7 +622,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l1.x = w.xq; l1.x_s = w.xs_pk; l1.x_s_packed = 1; l1.row_token = w.rb.row_token;
   l1.expert_off = w.rb.expert_off; l1.tile_base = w.rb.tile_base; l1.n_experts = E;
   l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
-  l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_global = requant_global;
+  l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_gptr = requant_global;
   l1.h_scales_packed = requant == MX_FMT_MXFP4;
   const Epilogue l1_epi = requant == MX_FMT_NVFP4 ? EPI_SWIGLU_NVFP4 : EPI_SWIGLU_MXFP4;
   MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(l1_epi, l1, max_mtiles * l1.n_tiles, s); }), "l1_gemm");
@@ -628,7 +637,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l2.n_tiles = (H + BN - 1) / BN;
   l2.out_bf16 = w.o; l2.row_slot = w.rb.row_slot; l2.row_weight = w.rb.row_weight;
   if (requant == MX_FMT_NVFP4) {
-    l2.nv_global = requant_global;
+    l2.nv_gptr = requant_global;
     MX_HIP(phase("l2_gemm_bf16", s, [&] { return launch_gemm_nv_l2(l2, max_mtiles * l2.n_tiles, s); }),
            "l2_gemm_bf16");
   } else {
@@ -839,7 +848,7 @@ mx_status mx_nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t
   Carve c(workspace);
   uint8_t* xq = (uint8_t*)c.take((size_t)(M * K / 2));
   uint8_t* xs = (uint8_t*)c.take((size_t)(M * (K / 16)));
-  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, M, K, x_global, xq, xs, s); }), "quant_x");
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, M, K, x_global, nullptr, xq, xs, s); }), "quant_x");
   GemmArgs a = base_args();
   a.wa = w; a.wa_s = w_s;
   a.n_rows = (int)N; a.k = (int)K;
@@ -914,14 +923,14 @@ mx_status mx_nvfp4_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int6
     a.nv_global = gscale;
     return launch_gemm_nv_w(a, a.grid_tiles, s);
   };
-  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, M, hidden, x_global, xq, xs, s); }), "quant_x");
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, M, hidden, x_global, nullptr, xq, xs, s); }), "quant_x");
   MX_HIP(phase("nv_gemm", s, [&] {
            hipError_t e = gemm(xq, xs, w1, w1_s, inter, hidden, x_global * w1_global, g);
            if (e != hipSuccess) return e;
            return gemm(xq, xs, w3, w3_s, inter, hidden, x_global * w3_global, u);
          }), "nv_gemm_l1");
   MX_HIP(phase("silu_mul", s, [&] { return launch_silu_mul_bf16(g, u, M * inter, h, s); }), "silu_mul");
-  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(h, M, inter, h_global, hq, hs, s); }), "quant_h");
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(h, M, inter, h_global, nullptr, hq, hs, s); }), "quant_h");
   MX_HIP(phase("nv_gemm", s, [&] { return gemm(hq, hs, w2, w2_s, hidden, inter, h_global * w2_global, y); }),
          "nv_gemm_l2");
   return ok();
@@ -1008,7 +1017,7 @@ mx_status mx_grouped_nvfp4_expert_mlp(const uint16_t* x, int64_t T, int64_t hidd
   NvGroupWs w = nv_group_ws(workspace, T, hidden, inter, k, E);
   const int64_t P = T * k;
   const int max_mtiles = (int)max_route_mtiles(P, E);
-  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, T, hidden, x_global, w.xq, w.xs, s); }),
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, T, hidden, x_global, nullptr, w.xq, w.xs, s); }),
          "quant_x");
   MX_HIP(phase("route", s, [&] {
            hipError_t e = launch_route(topk_ids, topk_w, T, k, E, w.rb, s);
@@ -1041,7 +1050,7 @@ mx_status mx_grouped_nvfp4_expert_mlp(const uint16_t* x, int64_t T, int64_t hidd
            return gemm(w.gq, w.gs, w3, w3_s, w3_global, inter, hidden, x_global, w.u, false);
          }), "nv_gemm_l1");
   MX_HIP(phase("silu_mul", s, [&] { return launch_silu_mul_bf16(w.g, w.u, P * inter, w.h, s); }), "silu_mul");
-  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(w.h, P, inter, h_global, w.hq, w.hs, s); }),
+  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(w.h, P, inter, h_global, nullptr, w.hq, w.hs, s); }),
          "quant_h");
   MX_HIP(phase("nv_gemm", s, [&] {
            return gemm(w.hq, w.hs, w2, w2_s, w2_global, hidden, inter, h_global, w.o, true);
@@ -1165,7 +1174,8 @@ mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidden, int
                                const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
                                const uint8_t* w2, const uint8_t* w2_s, const uint8_t* packed_scales,
-                               mx_format requant, float requant_global, uint16_t* y, mx_moe_runner** out) {
+                               mx_format requant, const float* requant_global, uint16_t* y,
+                               mx_moe_runner** out) {
   MX_REQUIRE_PTR(out);
   *out = nullptr;
   if (T < 1) return fail(MX_ERR_SHAPE, "runner token count %lld must be positive", (long long)T);
@@ -1179,6 +1189,14 @@ mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidden, int
   if (e != hipSuccess) {
     runner_release(r);
     return hip_fail(e, "runner workspace");
+  }
+  // The eager call below runs on a private stream that is not ordered after the
+  // caller's streams: wait for all work already enqueued on the device (the
+  // caller may just have written x, topk_ids, topk_w or the global scale).
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    runner_release(r);
+    return hip_fail(e, "runner set-up synchronisation");
   }
   // a private stream of default priority for the capture
   e = hipStreamCreateWithFlags(&r->capture, hipStreamNonBlocking);

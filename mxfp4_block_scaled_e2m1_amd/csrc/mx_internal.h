@@ -75,6 +75,7 @@ struct GemmArgs {
   uint8_t* h_scales;          // L1: [rows, n_rows/32] (MXFP4) or [rows, n_rows/16] (NVFP4)
   int h_scales_packed;        // L1 MXFP4: h_scales tile-major over the m-tiles (the L2's x_s)
   float nv_global;            // L1 NVFP4 global scale; bf16-MFMA GEMMs: epilogue scale
+  const float* nv_gptr;       // when set, the kernel reads nv_global from this device float
   const float* e_global;      // bf16-MFMA GEMMs, optional: per-expert factor on nv_global [E]
   uint32_t* h_amax;           // L1 MXFP4, optional: running max of |h| (bf16 bits) over the valid rows
   uint16_t* out_bf16;         // EPI_BF16: dense y [m_rows, n_rows]; grouped o [slots, n_rows]
@@ -115,11 +116,13 @@ hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int
                                 int64_t cols, uint16_t* out, hipStream_t s);
 hipError_t launch_dequant_fp8_block(const uint8_t* q, const uint8_t* scales, int64_t rows,
                                     int64_t cols, uint16_t* out, hipStream_t s);
-hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, float global,
+// NVFP4 kernels take their fp32 global either as a value or, when gptr is not
+// null, from device memory (*gptr, read in stream order).
+hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, float global, const float* gptr,
                                 int64_t rows, int64_t cols, uint16_t* out, hipStream_t s);
 hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
-hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, float global,
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, float global, const float* gptr,
                               uint8_t* codes, uint8_t* scales, hipStream_t s);
 // NVFP4 warm-up: clear the |h| max word; turn it into g = f32(max / (6 * 448)).
 hipError_t launch_amax_clear(uint32_t* amax, hipStream_t s);
@@ -181,6 +184,7 @@ struct RoutedArgs {
   const uint8_t *hq, *hs;
   bool nvfp4;           // hq/hs are NVFP4 (E4M3 per 16), else MXFP4
   float scale;
+  const float* scale_ptr;   // when set, L2 reads `scale` from this device float
   uint16_t* o;
 };
 bool routed_stream_fits(int64_t T, int64_t hidden, int64_t inter, int k, int E, bool nvfp4);

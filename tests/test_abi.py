@@ -47,50 +47,52 @@ def test_status_strings(L):
 
 
 def test_dequant_validation(L):
-    assert L.mx_dequant(0, None, None, 0.0, 4, 33, None, None) == 2 and "32" in _err(L)
-    assert L.mx_dequant(0, None, None, 0.0, 4, 64, None, None) == 1 and "codes" in _err(L)
-    assert L.mx_dequant(9, None, None, 0.0, 4, 64, None, None) == 4
-    assert L.mx_dequant(1, None, None, 0.0, 4, 24, None, None) == 2
-    assert L.mx_dequant(0, None, None, 0.0, -1, 64, None, None) == 2
-    assert L.mx_dequant(0, None, None, 0.0, 0, 64, None, None) == 0      # empty: nothing to do
+    P = ctypes.c_void_p
+    assert L.mx_dequant(0, None, None, None, 4, 33, None, None) == 2 and "32" in _err(L)
+    assert L.mx_dequant(0, None, None, None, 4, 64, None, None) == 1 and "codes" in _err(L)
+    assert L.mx_dequant(9, None, None, None, 4, 64, None, None) == 4
+    assert L.mx_dequant(1, None, None, None, 4, 24, None, None) == 2
+    assert L.mx_dequant(0, None, None, None, -1, 64, None, None) == 2
+    assert L.mx_dequant(0, None, None, None, 0, 64, None, None) == 0      # empty: nothing to do
     # misaligned output pointer (never dereferenced: validation fails first)
-    assert L.mx_dequant(0, ctypes.c_void_p(16), ctypes.c_void_p(16), 0.0, 1, 64, ctypes.c_void_p(8), None) == 3
-    assert L.mx_dequant(2, ctypes.c_void_p(16), ctypes.c_void_p(16), float("nan"), 1, 64,
-                        ctypes.c_void_p(16), None) == 7
+    assert L.mx_dequant(0, P(16), P(16), None, 1, 64, P(8), None) == 3
+    # NVFP4: the global scale is a device pointer, required and 4-byte aligned
+    assert L.mx_dequant(2, P(16), P(16), None, 1, 64, P(16), None) == 1 and "global" in _err(L)
+    assert L.mx_dequant(2, P(16), P(16), P(18), 1, 64, P(16), None) == 3
 
 
 def test_quantize_validation(L):
-    assert L.mx_quantize_act(1, None, 4, 64, 0.0, None, None, None) == 4        # FP8 is dequant-only
-    assert L.mx_quantize_act(0, None, 4, 48, 0.0, None, None, None) == 2
-    assert L.mx_quantize_act(2, None, 4, 64, 0.0, None, None, None) == 7        # NVFP4 needs g > 0
-    assert L.mx_quantize_act(2, None, 4, 64, float("inf"), None, None, None) == 7
-    assert L.mx_quantize_act(2, None, 4, 64, 1e-40, None, None, None) == 7
-    assert L.mx_quantize_act(0, None, 4, 64, 0.0, None, None, None) == 1
+    P = ctypes.c_void_p
+    assert L.mx_quantize_act(1, None, 4, 64, None, None, None, None) == 4        # FP8 is dequant-only
+    assert L.mx_quantize_act(0, None, 4, 48, None, None, None, None) == 2
+    assert L.mx_quantize_act(2, None, 4, 64, None, None, None, None) == 1        # NVFP4 needs its global
+    assert L.mx_quantize_act(2, None, 4, 64, P(258), None, None, None) == 3     # ... 4-byte aligned
+    assert L.mx_quantize_act(0, None, 4, 64, None, None, None, None) == 1
 
 
 def test_mlp_validation(L):
     P = ctypes.c_void_p
     z = [P(256)] * 6
     # hidden not a multiple of 128
-    assert L.mx_expert_mlp(P(256), 4, 200, 128, *z, None, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
-    assert L.mx_expert_mlp(P(256), 4, 256, 96, *z, None, 0, 0.0, P(256), P(256), 1 << 30, None) == 2
-    # NVFP4 re-quant needs a finite global scale >= 2^-117; FP8 is not a re-quant format
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 2, 0.0, P(256), P(256), 1 << 30, None) == 7
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 2, float("nan"), P(256), P(256), 1 << 30, None) == 7
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 1, 0.0, P(256), P(256), 1 << 30, None) == 4
+    assert L.mx_expert_mlp(P(256), 4, 200, 128, *z, None, 0, None, P(256), P(256), 1 << 30, None) == 2
+    assert L.mx_expert_mlp(P(256), 4, 256, 96, *z, None, 0, None, P(256), P(256), 1 << 30, None) == 2
+    # NVFP4 re-quant needs its global scale (a device pointer); FP8 is not a re-quant format
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 2, None, P(256), P(256), 1 << 30, None) == 1
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 2, P(257), P(256), P(256), 1 << 30, None) == 3
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 1, None, P(256), P(256), 1 << 30, None) == 4
     # NVFP4 keeps one E4M3 byte per 16 columns of h: a larger workspace than MXFP4
     assert L.mx_expert_mlp_workspace_size(4096, 7168, 3072, 2) > L.mx_expert_mlp_workspace_size(4096, 7168, 3072, 0)
     # workspace too small
     need = L.mx_expert_mlp_workspace_size(4, 256, 128, 0)
     assert need > 0
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 0, 0.0, P(256), P(256), need - 1, None) == 5
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 0, None, P(256), P(256), need - 1, None) == 5
     # misaligned workspace, null weights
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 0, 0.0, P(256), P(128), need, None) == 3
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, None, *z[1:], None, 0, 0.0, P(256), P(256), need, None) == 1
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 0, None, P(256), P(128), need, None) == 3
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, None, *z[1:], None, 0, None, P(256), P(256), need, None) == 1
     # zero tokens is a no-op
-    assert L.mx_expert_mlp(None, 0, 256, 128, *([None] * 7), 0, 0.0, None, None, 0, None) == 0
+    assert L.mx_expert_mlp(None, 0, 256, 128, *([None] * 7), 0, None, None, None, 0, None) == 0
     # packed weight scales must be 256-byte aligned (NULL selects the row-major scales)
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, P(128), 0, 0.0, P(256), P(256), need, None) == 3
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, P(128), 0, None, P(256), P(256), need, None) == 3
 
 
 def test_pack_weight_scales_validation(L):
@@ -109,12 +111,15 @@ def test_pack_weight_scales_validation(L):
 def test_grouped_validation(L):
     P = ctypes.c_void_p
     z = [P(256)] * 6
-    args = lambda k, E, ws: (P(256), 8, 256, 128, P(256), P(256), k, E, *z, None, 0, 0.0, P(256), P(256), ws, None)
+    args = lambda k, E, ws: (P(256), 8, 256, 128, P(256), P(256), k, E, *z, None, 0, None, P(256), P(256), ws, None)
     assert L.mx_grouped_expert_mlp(*args(0, 4, 1 << 30)) == 2
     assert L.mx_grouped_expert_mlp(*args(5, 4, 1 << 30)) == 2
     assert L.mx_grouped_expert_mlp(*args(2, 2000, 1 << 30)) == 2
     need = L.mx_grouped_expert_mlp_workspace_size(8, 256, 128, 2, 4, 0)
     assert L.mx_grouped_expert_mlp(*args(2, 4, need - 1)) == 5
+    nv = lambda g: (P(256), 8, 256, 128, P(256), P(256), 2, 4, *z, None, 2, g, P(256), P(256), 1 << 30, None)
+    assert L.mx_grouped_expert_mlp(*nv(None)) == 1                  # NVFP4 without its global
+    assert L.mx_grouped_expert_mlp(*nv(P(258))) == 3
     # workspace grows with tokens and with k
     a = L.mx_grouped_expert_mlp_workspace_size(64, 256, 128, 2, 4, 0)
     b = L.mx_grouped_expert_mlp_workspace_size(128, 256, 128, 2, 4, 0)
@@ -168,9 +173,9 @@ def test_fp8_linear_validation(L):
 
 def test_quantize_mxfp8_validation(L):
     P = ctypes.c_void_p
-    assert L.mx_quantize_act(3, P(256), 4, 48, 0.0, P(256), P(256), None) == 2     # cols % 32
-    assert L.mx_quantize_act(3, P(256), 4, 64, 0.0, P(264), P(256), None) == 3     # codes alignment
-    assert L.mx_quantize_act(9, P(256), 4, 64, 0.0, P(256), P(256), None) == 4     # unknown format
+    assert L.mx_quantize_act(3, P(256), 4, 48, None, P(256), P(256), None) == 2     # cols % 32
+    assert L.mx_quantize_act(3, P(256), 4, 64, None, P(264), P(256), None) == 3     # codes alignment
+    assert L.mx_quantize_act(9, P(256), 4, 64, None, P(256), P(256), None) == 4     # unknown format
 
 
 def test_runner_validation(L):
@@ -179,7 +184,7 @@ def test_runner_validation(L):
     out = P()
 
     def create(T, k, E, x=P(256), o=True):
-        return L.mx_moe_runner_create(x, T, 256, 128, P(256), P(256), k, E, *z, None, 0, 0.0, P(256),
+        return L.mx_moe_runner_create(x, T, 256, 128, P(256), P(256), k, E, *z, None, 0, None, P(256),
                                       ctypes.byref(out) if o else None)
     assert create(8, 2, 4, o=False) == 1
     assert create(0, 2, 4) == 2 and out.value is None
@@ -252,4 +257,5 @@ def test_grouped_nvfp4_validation(L):
     assert call(2, 4, 1 << 30, g1=None) == 1
     assert call(2, 4, 1 << 30, s1=P(257)) == 3
     assert call(2, 4, need - 1) == 5
+
 

@@ -67,7 +67,7 @@ def test_graph_grouped(mx, requant, T):
     y = torch.empty((T, 512), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mx.grouped_expert_mlp_workspace_size(T, 512, 256, 3, 6, requant), dtype=torch.uint8,
                      device="cuda")
-    g_scale = 2.0 ** -6
+    g_scale = torch.tensor([2.0 ** -6], dtype=torch.float32, device="cuda")   # device global: no copy in capture
     fn = lambda: mx.grouped_expert_mlp(x, w["ids"], w["w"], w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
                                        requant=requant, requant_global=g_scale, out=y, workspace=ws)
     fn()
@@ -111,7 +111,7 @@ def test_runner_replays_match_eager(mx, requant, T):
     d0 = W.grouped(tokens=T, n_experts=E, k=k, seed=9, hidden=H, inter=I)
     w = {n: t(d0[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")}
     x, ids, gw = bf16_t(d0["x"]), t(d0["ids"]), t(d0["w"])
-    g_scale = 2.0 ** -6
+    g_scale = torch.tensor([2.0 ** -6], dtype=torch.float32, device="cuda")
     r = mx.MoeRunner(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"], requant=requant,
                      requant_global=g_scale)
     try:
@@ -120,6 +120,7 @@ def test_runner_replays_match_eager(mx, requant, T):
             x.copy_(bf16_t(d["x"]))
             ids.copy_(t(d["ids"]))
             gw.copy_(t(d["w"]))
+            g_scale.fill_(2.0 ** -6 if seed != 21 else 2.0 ** -5 * 1.5)   # the global is read at each replay
             torch.cuda.synchronize()
             ref = bits(mx.grouped_expert_mlp(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
                                              requant=requant, requant_global=g_scale))
@@ -133,3 +134,49 @@ def test_runner_replays_match_eager(mx, requant, T):
         torch.cuda.synchronize()
         r.close()
 
+
+
+@pytest.mark.parametrize("T", [300, 20])
+def test_runner_after_device_writes_and_warmup_without_sync(mx, T):
+    """Inputs written by device kernels on the caller's stream, the NVFP4 global from
+    the on-device warm-up, then the runner created with no host synchronisation in
+    between: its first output (the eager call of create) and its replays equal eager
+    calls bit for bit. The global goes from the warm-up to the runner as a device
+    pointer, never read back to the host."""
+    E, k, H, I = 6, 3, 512, 256
+    d0 = W.grouped(tokens=T, n_experts=E, k=k, seed=41, hidden=H, inter=I)
+    w = {n: t(d0[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")}
+    src_x, src_ids, src_gw = bf16_t(d0["x"]), t(d0["ids"]), t(d0["w"])
+    torch.cuda.synchronize()
+    x = torch.zeros_like(src_x)
+    ids = torch.zeros_like(src_ids)
+    gw = torch.zeros_like(src_gw)
+    x.copy_(src_x)          # device-to-device copies, enqueued on the current stream
+    ids.copy_(src_ids)
+    gw.copy_(src_gw)
+    g = mx.nvfp4_global_warmup(x, w["w1"], w["w1s"], w["w3"], w["w3s"], topk_ids=ids, topk_w=gw)
+    r = mx.MoeRunner(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"], requant="nvfp4",
+                     requant_global=g)
+    try:
+        first = bits(r.out)
+        ref = bits(mx.grouped_expert_mlp(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
+                                         requant="nvfp4", requant_global=g))
+        assert np.array_equal(first, ref)
+        # the same global as a host value gives the same output
+        ref_host = bits(mx.grouped_expert_mlp(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"],
+                                              w["w2s"], requant="nvfp4", requant_global=float(g.item())))
+        assert np.array_equal(ref_host, ref)
+        # new inputs and a new warm-up global on the device, then a replay, still without a host sync
+        d1 = W.grouped(tokens=T, n_experts=E, k=k, seed=42, hidden=H, inter=I)
+        src_x.copy_(bf16_t(d1["x"]))
+        torch.cuda.synchronize()
+        x.copy_(src_x)
+        mx.nvfp4_global_warmup(x, w["w1"], w["w1s"], w["w3"], w["w3s"], topk_ids=ids, topk_w=gw, out=g)
+        r.replay()
+        rep = bits(r.out)
+        ref1 = bits(mx.grouped_expert_mlp(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
+                                          requant="nvfp4", requant_global=g))
+        assert np.array_equal(rep, ref1)
+    finally:
+        torch.cuda.synchronize()
+        r.close()
