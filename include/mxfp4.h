@@ -172,6 +172,32 @@ MX_API mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int
 MX_API size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t inter, mx_format requant);
 
 /*
+ * mx_expert_mlp_noalloc -- mx_expert_mlp for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation and results, with the workspace
+ * taken from a fixed device array inside the library instead of a caller
+ * buffer. The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).
+ *   Arguments, formats, alignment and errors as for mx_expert_mlp, without
+ *   workspace and ws_bytes.
+ *   Limit: the sizes must need at most mx_expert_mlp_noalloc_max_bytes()
+ *   (64 MiB) of workspace, i.e. mx_expert_mlp_workspace_size(M, hidden, inter,
+ *   requant) <= 64 MiB (M = 4096 at hidden 7168, inter 3072 needs 23 MiB);
+ *   larger sizes return MX_ERR_WORKSPACE and enqueue nothing.
+ *   Each GPU holds its own 64 MiB array for the life of the process (its
+ *   address is looked up on the first call on that device). Every call on one
+ *   GPU uses that GPU's array: calls that overlap in time on one GPU (different
+ *   streams, different threads without ordering) race and give wrong results.
+ */
+MX_API mx_status mx_expert_mlp_noalloc(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter,
+                                       const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
+                                       const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
+                                       const uint8_t* packed_scales, mx_format requant,
+                                       const float* requant_global, uint16_t* y, void* stream);
+/* Bytes of the fixed device array behind mx_expert_mlp_noalloc (64 MiB). */
+MX_API size_t mx_expert_mlp_noalloc_max_bytes(void);
+
+/*
  * mx_grouped_expert_mlp -- E local routed experts as a ragged grouped GEMM: the
  * pages' MoE pipeline (routing, top-k, scatter around the same L1 GEMM -> SiLU
  * -> re-quant -> L2 GEMM; page "Current Bug: vLLM produces empty/garbage

@@ -5,7 +5,7 @@ The compute path is the HIP library ``libmxfp4.so`` (C ABI in
 """
 
 from .binding import (  # noqa: F401
-    MoeRunner, MxError, debug_gemm_f32, dequant, expert_mlp, expert_mlp_workspace_size,
+    MoeRunner, MxError, debug_gemm_f32, dequant, expert_mlp, expert_mlp_noalloc, expert_mlp_workspace_size,
     fp8_block_linear,
     fp8_block_linear_workspace_size, fp8_expert_mlp, fp8_expert_mlp_workspace_size, grouped_expert_mlp,
     grouped_expert_mlp_workspace_size, grouped_nvfp4_expert_mlp, grouped_nvfp4_expert_mlp_workspace_size, lib, nvfp4_global_warmup, nvfp4_linear, nvfp4_linear_workspace_size,
@@ -14,7 +14,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "MoeRunner", "MxError", "debug_gemm_f32", "dequant", "expert_mlp", "expert_mlp_workspace_size",
+    "MoeRunner", "MxError", "debug_gemm_f32", "dequant", "expert_mlp", "expert_mlp_noalloc", "expert_mlp_workspace_size",
     "fp8_block_linear",
     "fp8_block_linear_workspace_size", "fp8_expert_mlp", "fp8_expert_mlp_workspace_size",
     "grouped_expert_mlp", "grouped_expert_mlp_workspace_size",

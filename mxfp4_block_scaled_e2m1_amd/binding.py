@@ -37,6 +37,8 @@ SIGNATURES = {
                                       _P]),
     "mx_nvfp4_global_warmup_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "mx_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
+    "mx_expert_mlp_noalloc": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]),
+    "mx_expert_mlp_noalloc_max_bytes": (_SZ, []),
     "mx_grouped_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                      _P, _I32, _P, _P, _P, _SZ, _P]),
     "mx_grouped_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
@@ -204,6 +206,21 @@ def expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global=Non
     _check(lib().mx_expert_mlp(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s),
                                _ptr(w2), _ptr(w2s), _ptr(packed_scales), _fmt(requant), _ptr(g),
                                _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def expert_mlp_noalloc(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global=None, out=None,
+                       stream=None, packed_scales=None):
+    """mx_expert_mlp_noalloc: mx_expert_mlp on the library's fixed device scratch
+    (no workspace argument; calls on one GPU must not overlap)."""
+    M, hidden = x.shape
+    inter = w1.shape[0]
+    if out is None:
+        out = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+    g = _global(requant_global, x.device)
+    _check(lib().mx_expert_mlp_noalloc(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s),
+                                       _ptr(w2), _ptr(w2s), _ptr(packed_scales), _fmt(requant), _ptr(g),
+                                       _ptr(out), _stream(stream)))
     return out
 
 

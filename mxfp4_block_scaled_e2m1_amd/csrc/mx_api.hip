@@ -1141,6 +1141,68 @@ mx_status mx_debug_gemm_f32(const uint8_t* a, const uint8_t* a_s, const uint8_t*
 
 }  // extern "C"
 
+// ---------------------------------------------------------------- no-allocation entry point
+// mx_expert_mlp_noalloc runs mx_expert_mlp on a file-scope device array instead
+// of a caller workspace, for callers that cannot allocate device memory. Each
+// device holds its own copy of the array (64 MiB, for as long as the process
+// runs); its address on a device is looked up once, with that device current,
+// and kept. Host code never passes `scratch` itself to a kernel: in host code
+// the name is a stand-in, not a device address.
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+
+// The current device's copy of `scratch`, looked up on its first use.
+mx_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return fail(MX_ERR_HIP, "device %d above the supported %d", dev,
+                                                         NOALLOC_MAX_DEVICES);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MX_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mx_expert_mlp_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+mx_status mx_expert_mlp_noalloc(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, const uint8_t* w1,
+                                const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s, const uint8_t* w2,
+                                const uint8_t* w2_s, const uint8_t* packed_scales, mx_format requant,
+                                const float* requant_global, uint16_t* y, void* stream) {
+  MX_TRY(check_mlp_dims(M, hidden, inter));
+  MX_TRY(check_requant(requant, requant_global));
+  if (M == 0) return ok();
+  const size_t need = mx_expert_mlp_workspace_size(M, hidden, inter, requant);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(MX_ERR_WORKSPACE,
+                "M %lld, hidden %lld, inter %lld need %zu bytes of scratch, above the %zu bytes of the "
+                "no-allocation entry point (use mx_expert_mlp with a workspace)",
+                (long long)M, (long long)hidden, (long long)inter, need, NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  MX_TRY(scratch_ptr(&ws));
+  return mx_expert_mlp(x, M, hidden, inter, w1, w1_s, w3, w3_s, w2, w2_s, packed_scales, requant, requant_global, y,
+                       ws, NOALLOC_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"
+
 // ---------------------------------------------------------------- runner
 // Routed-expert runner: workspace allocated once, the whole call captured once
 // into a hipGraph and replayed. The pages' serving plan is a runner with

@@ -259,3 +259,19 @@ def test_grouped_nvfp4_validation(L):
     assert call(2, 4, need - 1) == 5
 
 
+
+def test_noalloc_validation(L):
+    """The no-allocation shared expert checks its arguments like mx_expert_mlp and
+    refuses sizes whose workspace exceeds its fixed scratch, before touching the GPU."""
+    P = ctypes.c_void_p
+    z = [P(256)] * 6
+    limit = L.mx_expert_mlp_noalloc_max_bytes()
+    assert limit == 64 << 20
+    assert L.mx_expert_mlp_noalloc(P(256), 4, 200, 128, *z, None, 0, None, P(256), None) == 2
+    assert L.mx_expert_mlp_noalloc(P(256), 4, 256, 128, *z, None, 2, None, P(256), None) == 1
+    assert L.mx_expert_mlp_noalloc(None, 0, 256, 128, *([None] * 7), 0, None, None, None) == 0
+    big = 1
+    while L.mx_expert_mlp_workspace_size(big, 7168, 3072, 0) <= limit:
+        big *= 2
+    assert L.mx_expert_mlp_noalloc(P(256), big, 7168, 3072, *z, None, 0, None, P(256), None) == 5
+    assert "no-allocation" in _err(L)
