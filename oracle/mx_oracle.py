@@ -238,21 +238,28 @@ def mxfp4_quantize(x_bits):
     Reading (the pages give no quantiser): the OCP MX v1.0 shared-exponent
     rule. Keeping -0 is supported by [Q0508] "FP4 (E2M1) expert weight format
     confirmed": -0 is about as common as +0 in real weights, which a producer
-    that flushed -0 to +0 would not give. Inputs must be finite.
+    that flushed -0 to +0 would not give.
+
+    A block holding an infinity or a NaN has no finite shared exponent: it gets
+    the E8M0 NaN byte 0xFF, so that it dequantises to NaN and the NaN travels on
+    (reading: 0xFF is the NaN of the format named ``e8m0fnu`` on the pages);
+    the oracle writes zero codes for such a block (the codes do not matter).
     """
     x = bf16_to_f64(x_bits)
     if x.ndim != 2 or x.shape[1] % 32 != 0:
         raise ValueError("mxfp4_quantize wants [R, C] with C % 32 == 0")
-    if not np.all(np.isfinite(x)):
-        raise ValueError("non-finite input")
     R, C = x.shape
     blk = x.reshape(R, C // 32, 32)
+    bad = ~np.isfinite(blk).all(axis=2)
+    blk = np.where(bad[..., None], 0.0, blk)
     amax = np.abs(blk).max(axis=2)
     _, e = np.frexp(amax)
     biased = np.clip((e - 1) - 2 + 127, 0, 254)
     biased = np.where(amax == 0, 0, biased).astype(np.int64)
     v = blk / np.ldexp(1.0, biased - 127)[..., None]
     nib = e2m1_code_rne_sat(np.abs(v)) | (np.signbit(blk).astype(np.uint8) << 3)
+    nib = np.where(bad[..., None], 0, nib).astype(np.uint8)
+    biased = np.where(bad, 255, biased)
     return _pack_nibbles(nib.reshape(R, C)), biased.astype(np.uint8)
 
 
@@ -306,15 +313,16 @@ def mxfp8_quantize(x_bits):
     activation quantiser. The plainest one that the rest supports is the rule
     already taken for the MXFP4 activations (OCP shared exponent, round to
     nearest even, saturate) with E4M3 elements and 32-column E8M0 blocks.
-    Inputs must be finite.
+    A block holding an infinity or a NaN gets scale byte 0xFF (NaN) and zero
+    codes, as in ``mxfp4_quantize``.
     """
     x = bf16_to_f64(x_bits)
     if x.ndim != 2 or x.shape[1] % 32 != 0:
         raise ValueError("mxfp8_quantize wants [R, C] with C % 32 == 0")
-    if not np.all(np.isfinite(x)):
-        raise ValueError("non-finite input")
     R, C = x.shape
     blk = x.reshape(R, C // 32, 32)
+    bad = ~np.isfinite(blk).all(axis=2)
+    blk = np.where(bad[..., None], 0.0, blk)
     amax = np.abs(blk).max(axis=2)
     _, e = np.frexp(amax)
     biased = np.clip((e - 1) - 8 + 127, 0, 254)
@@ -322,6 +330,8 @@ def mxfp8_quantize(x_bits):
     v = blk / np.ldexp(1.0, biased - 127)[..., None]
     mag, _ = e4m3_rne_satfinite(np.abs(v))
     codes = (mag & 0x7F) | (np.signbit(blk).astype(np.uint8) << 7)
+    codes = np.where(bad[..., None], 0, codes)
+    biased = np.where(bad, 255, biased)
     return codes.reshape(R, C).astype(np.uint8), biased.astype(np.uint8)
 
 
@@ -344,7 +354,8 @@ def nvfp4_quantize(x_bits, g):
         t = f32(6 * g); r = f32(amax / t); s = E4M3_RNE_satfinite(r)
         s == 0 -> all codes +-0
         d = f32(s * g); v = f32(x / d); code = E2M1_RNE_sat(|v|), sign of x
-    Dequant is code * s * g.
+    Dequant is code * s * g. A block holding an infinity or a NaN gets the
+    E4M3 NaN byte 0x7F and zero codes, so that it dequantises to NaN.
     """
     g = np.float32(g)
     if not (np.isfinite(g) and g > 0 and g >= np.finfo(np.float32).tiny * 2 ** 9):
@@ -352,10 +363,10 @@ def nvfp4_quantize(x_bits, g):
     x = bf16_to_f32(x_bits)
     if x.ndim != 2 or x.shape[1] % 16 != 0:
         raise ValueError("nvfp4_quantize wants [R, C] with C % 16 == 0")
-    if not np.all(np.isfinite(x)):
-        raise ValueError("non-finite input")
     R, C = x.shape
     blk = x.reshape(R, C // 16, 16)
+    bad = ~np.isfinite(blk).all(axis=2)
+    blk = np.where(bad[..., None], np.float32(0.0), blk).astype(np.float32)
     amax = np.abs(blk).max(axis=2)
     t = np.float32(np.float32(6.0) * g)
     r = (amax / t).astype(np.float32)
@@ -366,6 +377,8 @@ def nvfp4_quantize(x_bits, g):
     mag = e2m1_code_rne_sat(np.abs(v.astype(np.float64)))
     mag = np.where((sval == 0)[..., None], 0, mag).astype(np.uint8)
     nib = mag | (np.signbit(blk).astype(np.uint8) << 3)
+    nib = np.where(bad[..., None], 0, nib).astype(np.uint8)
+    sbyte = np.where(bad, 0x7F, sbyte).astype(np.uint8)
     return _pack_nibbles(nib.reshape(R, C)), sbyte
 
 

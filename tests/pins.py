@@ -943,3 +943,188 @@ def check_grouped_nvfp4_reductions(O, seed=83):
 def bf16_to_f64_local(bits):
     return ((np.asarray(bits).astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
 
+
+
+def check_quantizers_nonfinite_blocks(O, seed=89):
+    """A block holding +inf, -inf or a NaN has no finite shared exponent: the
+    quantisers give it the format's NaN scale byte (E8M0 0xFF for MXFP4 and
+    MXFP8, E4M3 0x7F for NVFP4: the NaN encodings of the format names
+    e8m0fnu / e4m3fn) and zero codes, so it dequantises to NaN; every other
+    block is quantised exactly as on its own."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((3, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bad = x.copy()
+    poison = {0: (5, 0x7F80), 1: (40, 0xFF80), 2: (33, 0x7FC0)}    # +inf, -inf, NaN
+    for r, (col, v) in poison.items():
+        bad[r, col] = v
+    for quant, per, nan_byte, bpb in (
+            (O.mxfp4_quantize, 32, 0xFF, 16), (O.mxfp8_quantize, 32, 0xFF, 32),
+            (lambda v: O.nvfp4_quantize(v, np.float32(0.01)), 16, 0x7F, 8)):
+        c0, s0 = quant(x)
+        c1, s1 = quant(bad)
+        for r in range(3):
+            for b in range(64 // per):
+                cb = slice(b * bpb, (b + 1) * bpb)
+                if b == poison[r][0] // per:
+                    assert int(s1[r, b]) == nan_byte
+                    assert np.all(c1[r, cb] == 0)
+                else:
+                    assert s1[r, b] == s0[r, b]
+                    assert np.array_equal(c1[r, cb], c0[r, cb])
+    # dequantised, the NaN block is NaN and nothing else is
+    c, s = O.mxfp4_quantize(bad)
+    dq = O.mxfp4_dequant_f64(c, s)
+    assert np.isnan(dq[0, :32]).all() and np.isnan(dq[1, 32:]).all() and np.isnan(dq[2, 32:]).all()
+    assert np.isfinite(dq[0, 32:]).all() and np.isfinite(dq[1, :32]).all() and np.isfinite(dq[2, :32]).all()
+
+
+def check_mlp_nan_propagation(O, seed=97):
+    """NaN in the weights: the E8M0 NaN byte in one down-projection scale makes
+    exactly that output column NaN for every token (the others are unchanged);
+    in a gate scale it makes h NaN in one block of every token, which the
+    re-quantisation carries on as a NaN scale, so every output is NaN. Routed:
+    only the tokens routed to the poisoned expert are affected."""
+    rng = np.random.default_rng(seed)
+    H, I, M = 64, 64, 3
+    w = dict(w1=rng.integers(0, 256, (I, H // 2)), w3=rng.integers(0, 256, (I, H // 2)),
+             w2=rng.integers(0, 256, (H, I // 2)), w1s=rng.integers(122, 129, (I, H // 32)),
+             w3s=rng.integers(122, 129, (I, H // 32)), w2s=rng.integers(122, 129, (H, I // 32)))
+    w = {k: v.astype(np.uint8) for k, v in w.items()}
+    x = (rng.standard_normal((M, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    order = ("w1", "w1s", "w3", "w3s", "w2", "w2s")
+    nan = lambda y: np.isnan(bf16_to_f64_local(y))
+    y0 = O.expert_mlp(x, *(w[n] for n in order))
+    assert not nan(y0).any()
+    w2 = dict(w, w2s=w["w2s"].copy())
+    w2["w2s"][17, 1] = 0xFF
+    y2 = O.expert_mlp(x, *(w2[n] for n in order))
+    assert nan(y2)[:, 17].all() and not np.delete(nan(y2), 17, axis=1).any()
+    assert np.array_equal(np.delete(y2, 17, axis=1), np.delete(y0, 17, axis=1))
+    w1 = dict(w, w1s=w["w1s"].copy())
+    w1["w1s"][5, 0] = 0xFF
+    assert nan(O.expert_mlp(x, *(w1[n] for n in order))).all()
+    # routed: expert 1 poisoned in its gate scales
+    E, T, k = 3, 6, 2
+    we = {n: np.stack([v] * E) for n, v in w.items()}
+    we["w1s"] = we["w1s"].copy()
+    we["w1s"][1, 5, 0] = 0xFF
+    xt = (rng.standard_normal((T, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ids = np.array([[0, 2], [1, 0], [2, 0], [1, 2], [0, 2], [2, 1]], np.int32)
+    wt = rng.random((T, k)).astype(np.float32)
+    yr = O.grouped_expert_mlp(xt, ids, wt, *(we[n] for n in order))
+    routed1 = (ids == 1).any(axis=1)
+    assert nan(yr)[routed1].all() and not nan(yr)[~routed1].any()
+
+
+def check_nvfp4_golden_block(O):
+    """The hand-worked NVFP4 block of tests/golden/nvfp4_quantize_example.txt:
+    the fp32 rounding of 6 g decides the block scale (0x3A, not 0x39) and the
+    division by the fp32 product s g decides one code (0.5, not 1.0)."""
+    g, sbyte, rows = None, None, []
+    for parts in _lines("nvfp4_quantize_example.txt"):
+        if parts[0] == "global":
+            g = np.array([int(parts[1], 16)], np.uint32).view(np.float32)[0]
+        elif parts[0] == "scale":
+            sbyte = int(parts[1], 16)
+        else:
+            rows.append((int(parts[0], 16), float(parts[1]), int(parts[2])))
+    assert len(rows) == 16 and g == np.float32(1.0 / 3.0)
+    bits = np.array([b for b, _, _ in rows], np.uint16)
+    for b, v, _ in rows:
+        assert _same(bf16_value(b), v)
+    codes, sc = O.nvfp4_quantize(bits[None, :], g)
+    assert int(sc[0, 0]) == sbyte
+    nib = np.empty(16, np.int64)
+    nib[0::2] = codes[0] & 15
+    nib[1::2] = codes[0] >> 4
+    assert [int(n) for n in nib] == [c for _, _, c in rows]
+
+
+def _silu_mul_fraction(gv, uv):
+    """bf16(silu(g) * u) of bf16 values g, u: silu from an exact quotient with
+    math.exp, rounded once by the table-search bf16 reference."""
+    hv = [float(Fraction(a) / (1 + Fraction(math.exp(-a))) * Fraction(b)) if a > -700 else 0.0 * a * b
+          for a, b in zip(gv, uv)]
+    return bf16_rne_reference(np.array(hv))
+
+
+def check_fp8_mlp_fraction_bruteforce(O, seed=101):
+    """The FP8 shared expert from first principles on a tiny shape: weights from
+    the E4M3 bit fields times their 128 x 128 block's 2^(s-127), exact Fraction
+    sums for the three linears, each rounded to bf16 by table search, SiLU * up by
+    an exact quotient; only the MXFP8 activation quantiser is the oracle's
+    (pinned on its own). Independent of the oracle's linear and composition."""
+    rng = np.random.default_rng(seed)
+    M, H, I = 2, 256, 128
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    w1 = rng.choice(finite, size=(I, H)).astype(np.uint8)
+    w3 = rng.choice(finite, size=(I, H)).astype(np.uint8)
+    w2 = rng.choice(finite, size=(H, I)).astype(np.uint8)
+    s1 = rng.integers(110, 118, (1, 2)).astype(np.uint8)
+    s3 = rng.integers(110, 118, (1, 2)).astype(np.uint8)
+    s2 = rng.integers(110, 118, (2, 1)).astype(np.uint8)
+    x = (rng.standard_normal((M, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    P2 = [Fraction(2) ** (e - 127) for e in range(256)]
+
+    def wmat(w, s):
+        return [[_e4m3_fraction(int(w[n, k])) * P2[int(s[n // 128, k // 128])] for k in range(w.shape[1])]
+                for n in range(w.shape[0])]
+
+    def act(bits):
+        q, sc = O.mxfp8_quantize(bits)
+        return [[_e4m3_fraction(int(q[m, k])) * P2[int(sc[m, k // 32])] for k in range(bits.shape[1])]
+                for m in range(bits.shape[0])]
+
+    def linear(a, wf):
+        v = [float(sum(p * q for p, q in zip(r, wr))) for r in a for wr in wf]
+        return bf16_rne_reference(np.array(v)).reshape(len(a), len(wf))
+
+    a = act(x)
+    g = linear(a, wmat(w1, s1))
+    u = linear(a, wmat(w3, s3))
+    h = _silu_mul_fraction([bf16_value(b) for b in g.ravel()], [bf16_value(b) for b in u.ravel()]).reshape(M, I)
+    want = linear(act(h), wmat(w2, s2))
+    assert np.array_equal(O.fp8_expert_mlp(x, w1, s1, w3, s3, w2, s2), want)
+
+
+def check_nvfp4_mlp_fraction_bruteforce(O, seed=103):
+    """The expert with NVFP4 weights from first principles on a tiny shape: weight
+    and activation values code * E4M3(s) * g as exact Fractions from the bit
+    fields, exact sums for the three linears, each rounded to bf16 by table
+    search, SiLU * up by an exact quotient; only the NVFP4 quantiser is the
+    oracle's (pinned by the grid checks and the hand-worked block). Gate and up
+    carry different globals. Independent of the oracle's linear and
+    composition."""
+    rng = np.random.default_rng(seed)
+    M, H, I = 2, 128, 64
+    w = {n: rng.integers(0, 256, (r, c // 2)).astype(np.uint8) for n, (r, c) in
+         (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I)))}
+    sc = {n: rng.integers(0x20, 0x58, (r, c // 16)).astype(np.uint8) for n, (r, c) in
+          (("w1", (I, H)), ("w3", (I, H)), ("w2", (H, I)))}
+    g1, g3, g2, gx, gh = (np.float32(v) for v in (2.0 ** -6, 3 * 2.0 ** -6, 2.0 ** -5, 2.0 ** -9, 0.75))
+    x = (rng.standard_normal((M, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+    def vals(codes, scales, g):
+        G = Fraction(float(g))
+        out = []
+        for r in range(codes.shape[0]):
+            row = []
+            for k in range(2 * codes.shape[1]):
+                byte = int(codes[r, k // 2])
+                nib = (byte >> 4) if k % 2 else (byte & 15)
+                mag = Fraction(E2M1_GRID[nib & 7])
+                row.append((-mag if nib & 8 else mag) * _e4m3_fraction(int(scales[r, k // 16])) * G)
+            out.append(row)
+        return out
+
+    def linear(a, wf):
+        v = [float(sum(p * q for p, q in zip(r, wr))) for r in a for wr in wf]
+        return bf16_rne_reference(np.array(v)).reshape(len(a), len(wf))
+
+    a = vals(*O.nvfp4_quantize(x, gx), gx)
+    g = linear(a, vals(w["w1"], sc["w1"], g1))
+    u = linear(a, vals(w["w3"], sc["w3"], g3))
+    h = _silu_mul_fraction([bf16_value(b) for b in g.ravel()], [bf16_value(b) for b in u.ravel()]).reshape(M, I)
+    want = linear(vals(*O.nvfp4_quantize(h, gh), gh), vals(w["w2"], sc["w2"], g2))
+    got = O.nvfp4_expert_mlp(x, w["w1"], sc["w1"], g1, w["w3"], sc["w3"], g3, w["w2"], sc["w2"], g2, gx, gh)
+    assert np.array_equal(got, want)

@@ -166,6 +166,38 @@ def _fp8_linear_scale_per_row(x_bits, w, w_s, block=128):
     return _orig["fp8_block_linear"](x_bits, w, flat, block)
 
 
+def _fp8_linear_drop_last_k_block(x_bits, w, w_s, block=128):
+    # the last 128 columns of K left out of the product (a dropped term)
+    x = np.asarray(x_bits).copy()
+    x[:, -block:] = 0
+    return _orig["fp8_block_linear"](x, w, w_s, block)
+
+
+def _nvfp4_linear_drop_last_k_block(x_bits, w, w_s, w_global, x_global):
+    x = np.asarray(x_bits).copy()
+    x[:, -16:] = 0
+    return _orig["nvfp4_linear"](x, w, w_s, w_global, x_global)
+
+
+def _nvfp4_quantize_exact_6g(x_bits, g):
+    # the block scale from amax / (6 g) in fp64 (no fp32 rounding of 6 g)
+    codes, sc = _orig["nvfp4_quantize"](x_bits, g)
+    x = O.bf16_to_f64(x_bits)
+    blk = np.abs(x.reshape(x.shape[0], -1, 16)).max(axis=2)
+    byte = pins.e4m3_bruteforce(blk / (6.0 * float(g)))     # nearest E4M3 of the fp64 quotient
+    return codes, np.asarray(byte, np.uint8)
+
+
+def _quantize_nan_block_finite_scale(x_bits):
+    # a block holding inf or NaN keeps a finite scale byte (254)
+    x = O.bf16_to_f64(x_bits)
+    xf = np.where(np.isfinite(x), x, 0.0)
+    bits = O.f64_to_bf16(xf)
+    codes, sc = _orig["mxfp4_quantize"](bits)
+    bad = ~np.isfinite(x.reshape(x.shape[0], -1, 32)).all(axis=2)
+    return codes, np.where(bad, 254, sc).astype(np.uint8)
+
+
 LUT_POS_ZERO = np.array([0.0, 0.5, 1, 1.5, 2, 3, 4, 6, 0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
 
 MUTATIONS = [
@@ -194,6 +226,16 @@ MUTATIONS = [
     ("MXFP8 without saturation", "mxfp8_quantize", _mxfp8_no_saturation, pins.check_mxfp8_quantize_exhaustive),
     ("FP8 linear weight scale per row block only", "fp8_block_linear", _fp8_linear_scale_per_row,
      pins.check_fp8_linear_unit_rows),
+    # the composition pins recompose the MLPs from the oracle's own linears, so a
+    # fault inside the linear escapes them; the Fraction brute force does not
+    ("FP8 expert over a linear that drops a K block", "fp8_block_linear", _fp8_linear_drop_last_k_block,
+     pins.check_fp8_mlp_fraction_bruteforce),
+    ("NVFP4 expert over a linear that drops a K block", "nvfp4_linear", _nvfp4_linear_drop_last_k_block,
+     pins.check_nvfp4_mlp_fraction_bruteforce),
+    ("NVFP4 scale without the fp32 rounding of 6 g", "nvfp4_quantize", _nvfp4_quantize_exact_6g,
+     pins.check_nvfp4_golden_block),
+    ("non-finite block keeps a finite scale", "mxfp4_quantize", _quantize_nan_block_finite_scale,
+     pins.check_quantizers_nonfinite_blocks),
 ]
 
 

@@ -41,6 +41,11 @@ CHECKS = [
     pins.check_nvfp4_linear_bruteforce,
     pins.check_nvfp4_mlp_composition,
     pins.check_grouped_nvfp4_reductions,
+    pins.check_quantizers_nonfinite_blocks,
+    pins.check_mlp_nan_propagation,
+    pins.check_nvfp4_golden_block,
+    pins.check_fp8_mlp_fraction_bruteforce,
+    pins.check_nvfp4_mlp_fraction_bruteforce,
 ]
 
 
