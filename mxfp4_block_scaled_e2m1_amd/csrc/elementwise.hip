@@ -205,7 +205,8 @@ __global__ __launch_bounds__(EW_THREADS) void k_quant_nvfp4(const uint4* __restr
     uint32_t am = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) am = max(am, amax2(w[i]));
-    const uint32_t sbyte = e4m3_rne_satfinite(bf16_to_f32(am) / t6);
+    // a block holding an infinity or a NaN gets the E4M3 NaN byte 0x7F
+    const uint32_t sbyte = am >= 0x7F80u ? 0x7Fu : e4m3_rne_satfinite(bf16_to_f32(am) / t6);
     const float d = e4m3_to_f32(sbyte) * g;
     uint32_t o[2] = {0u, 0u};
 #pragma unroll

@@ -68,10 +68,12 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const uint4* __restrict__ x
     uint32_t am = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = max(am, amax2(w[i]));
-    // floor(log2 amax) - 8 + 127 from the bf16 exponent field ef: ef - 8, at least 0
+    // floor(log2 amax) - 8 + 127 from the bf16 exponent field ef: ef - 8, at
+    // least 0; a block holding an infinity or a NaN (ef = 255) gets the NaN
+    // byte 0xFF (and zero codes)
     const int ef = (int)((am >> 7) & 0xFFu);
-    const uint32_t sb = (uint32_t)(ef > 8 ? ef - 8 : 0);
-    const float inv = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb), exact multiply
+    const uint32_t sb = ef == 0xFF ? 0xFFu : (uint32_t)(ef > 8 ? ef - 8 : 0);
+    const float inv = sb == 0xFFu ? 0.0f : __uint_as_float((254u - sb) << 23);   // 2^(127 - sb), exact multiply
     uint32_t q[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

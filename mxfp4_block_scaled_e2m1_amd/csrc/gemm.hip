@@ -185,7 +185,8 @@ __device__ __forceinline__ uint32_t l1_block(const GemmArgs& a, const Tile& t, c
 #pragma unroll
       for (int i = 0; i < 4; ++i) am = max(am, amax2(hp[blk * 4 + i]));
       am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-      const uint32_t sbyte = e4m3_rne_satfinite(bf16_to_f32(am) / t6);
+      // a block holding an infinity or a NaN gets the E4M3 NaN byte 0x7F
+      const uint32_t sbyte = am >= 0x7F80u ? 0x7Fu : e4m3_rne_satfinite(bf16_to_f32(am) / t6);
       sbytes[blk] = sbyte;
       const float d = e4m3_to_f32(sbyte) * gsc;
       uint32_t w = 0;

@@ -117,9 +117,13 @@ __device__ __forceinline__ void quant_pairs_e8m0(const uint32_t* p, uint32_t sb,
 // MXFP4 shared-exponent scale byte from the bf16 bit pattern of the block's
 // largest magnitude: floor(log2 amax) - 2 + 127, clamped at 0. For a bf16
 // amax with exponent field ef this is max(ef - 2, 0); zero and subnormal
-// maxima give 0.
+// maxima give 0. A block holding an infinity or a NaN (ef = 255: those bit
+// patterns are the largest magnitudes) has no finite shared exponent and gets
+// the E8M0 NaN byte 0xFF, so that the NaN travels on; its codes are then
+// unspecified.
 __device__ __forceinline__ uint32_t mx_scale_from_amax_bits(uint32_t amax_bits) {
   int ef = (int)((amax_bits >> 7) & 0xFFu);
+  if (ef == 0xFF) return 0xFFu;
   return (uint32_t)(ef > 2 ? ef - 2 : 0);
 }
 
