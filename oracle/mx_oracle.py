@@ -481,7 +481,7 @@ def expert_mlp(x_bits, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", nv_global=Non
 
 
 def grouped_expert_mlp(x_bits, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s,
-                       requant="mxfp4", nv_global=None, tokens=None):
+                       requant="mxfp4", nv_global=None, tokens=None, intermediates=False):
     """Routed experts: y[t] = bf16(sum_k w[t,k] * expert_{ids[t,k]}(x[t])).
 
     x is quantised once per token. Each (token, slot) pair whose id lies in
@@ -492,7 +492,9 @@ def grouped_expert_mlp(x_bits, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s,
     routing, top-k and scatter added ([BUG0518] "Revised Plan", Phase 1;
     48 experts per rank in "Config values"). Router and top-k selection are
     inputs. ``tokens`` restricts the work to a subset of token indices
-    (rows of the result are in that order).
+    (rows of the result are in that order). With ``intermediates`` also a dict
+    per expert with pairs: the (token, slot) indices of its pairs in row-major
+    order of ``topk_ids`` and their re-quantised h (codes and scales).
     """
     x_bits = np.asarray(x_bits)
     ids = np.asarray(topk_ids).astype(np.int64)
@@ -506,6 +508,7 @@ def grouped_expert_mlp(x_bits, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s,
     xq, xs = mxfp4_quantize(x_bits)
     a = mxfp4_dequant_f64(xq, xs)
     acc = np.zeros((T, H), dtype=np.float64)
+    inter = {}
     for e in range(E):
         t_idx, k_idx = np.nonzero(ids == e)
         if t_idx.size == 0:
@@ -514,10 +517,13 @@ def grouped_expert_mlp(x_bits, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s,
         g = gemm_f64(ae, mxfp4_dequant_f64(w1[e], w1s[e]))
         u = gemm_f64(ae, mxfp4_dequant_f64(w3[e], w3s[e]))
         h = silu_mul_bf16(g, u)
-        _, _, hd = _requant(h, requant, nv_global)
+        hq, hs, hd = _requant(h, requant, nv_global)
         y_pair = gemm_f64(hd, mxfp4_dequant_f64(w2[e], w2s[e]))
         np.add.at(acc, t_idx, wts[t_idx, k_idx][:, None] * y_pair)
-    return f64_to_bf16(acc)
+        if intermediates:
+            inter[e] = dict(t_idx=t_idx, k_idx=k_idx, hq=hq, hs=hs)
+    y = f64_to_bf16(acc)
+    return (y, inter) if intermediates else y
 
 
 def fp8_expert_mlp(x_bits, w1, w1s, w3, w3s, w2, w2s):

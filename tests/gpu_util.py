@@ -140,3 +140,46 @@ def pack_weight_scales_ref(w1s, w3s, w2s):
             row = min(nt * 256 + r, H - 1)
             l2[:, nt, :, r, :] = d[:, row].reshape(E, nst2, 8)
     return np.concatenate([l1.reshape(-1), l2.reshape(-1)])
+
+
+def _align256(n):
+    return (n + 255) // 256 * 256
+
+
+def routed_ws_slices(ws, T, H, I, k, E, requant="mxfp4"):
+    """The routed GEMM-path workspace of mx_grouped_expert_mlp (each region
+    256-byte aligned): xq, xs, block counts, expert offsets, tile bases,
+    row_token, row_slot, row_weight, hq, hs (tile-major over the m-tiles for
+    MXFP4, row-major E4M3 per 16 for NVFP4), o (bf16 per-pair rows in slot order
+    t*k + j), xs_pk. Returns a dict of numpy views of the regions the tests read."""
+    P = T * k
+    mt = (P + E * 255) // 256
+    hs_bytes = P * I // 16 if requant == "nvfp4" else packed_scale_bytes(mt, I)
+    names = ["xq", "xs", "block_counts", "expert_off", "tile_base", "row_token", "row_slot", "row_weight", "hq",
+             "hs", "o"]
+    sizes = [T * H // 2, T * H // 32, -(-P // 1024) * E * 4, (E + 1) * 4, (E + 1) * 4, P * 4, P * 4, P * 4,
+             P * I // 2, hs_bytes, P * H * 2]
+    off, out = 0, {}
+    host = ws.cpu().numpy()
+    for n, s in zip(names, sizes):
+        out[n] = host[off:off + s]
+        off += _align256(s)
+    for n in ("expert_off", "tile_base", "row_token", "row_slot"):
+        out[n] = out[n].view(np.int32)
+    out["hq"] = out["hq"].reshape(P, I // 2)
+    out["o"] = out["o"].view(np.uint16).reshape(P, H)
+    if requant == "nvfp4":
+        out["hs"] = out["hs"].reshape(P, I // 16)
+    else:
+        # m-tile tile_base[e] + i holds the sorted rows expert_off[e] + 256 i ...
+        nst = (I + 255) // 256
+        tm = out["hs"][:mt * nst * 2048].reshape(mt, nst, 256, 8)
+        rowmaj = np.zeros((P, nst * 8), np.uint8)
+        eo, tb = out["expert_off"], out["tile_base"]
+        for e in range(E):
+            for i in range(tb[e + 1] - tb[e]):
+                r0 = eo[e] + 256 * i
+                n = min(256, eo[e + 1] - r0)
+                rowmaj[r0:r0 + n] = tm[tb[e] + i].transpose(1, 0, 2).reshape(256, nst * 8)[:n]
+        out["hs"] = rowmaj[:, :I // 32]
+    return out
