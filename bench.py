@@ -8,9 +8,9 @@ MXFP4 weights (uniform random codes, E8M0 exponents 120..130) and bf16 N(0,1)
 activations, all synthetic and resident in HBM before timing starts.
 
 Prints one JSON line. `value` is TFLOP/s over 6 * tokens * k * hidden * inter
-algorithmic FLOPs per step. `roofline` is for the dominant kernel (the L1
-GEMM), timed with HIP events recorded on the stream it runs on, during the
-timed steps; its `traffic` is the HBM byte count per launch from rocprofv3
+algorithmic FLOPs per step, timed with nothing else recorded. `roofline` is for
+the dominant kernel (the L1 GEMM), timed with HIP events recorded on the stream
+it runs on, in a second pass of the same steps; its `traffic` is the HBM byte count per launch from rocprofv3
 FETCH_SIZE / WRITE_SIZE runs scaled by a copy of known size (see
 `L1_TRAFFIC`), reported only while the GEMM sources are the ones it was
 measured on. `cpu_baseline` times the CPU oracle on a bounded sample (all
@@ -18,7 +18,9 @@ pairs routed to the first few experts). `secondary` holds the other
 configurations: the shared expert (few-token sizes replayed from a hipGraph
 over 16 rotating weight copies, so the weights come from HBM), the skewed
 16384-token batch with NVFP4 re-quantisation and its 8-token tail, and the
-dequant kernels.
+dequant kernels. `measured_peaks` holds the ceilings the library's probes reach
+on this GPU (FP4 MFMA loop, HBM reads into registers and into LDS, a device
+copy) beside the published peaks that `roofline` is quoted against.
 """
 
 from __future__ import annotations
@@ -326,24 +328,104 @@ def skewed_nvfp4(torch, mx, workloads):
     return rec
 
 
-def gpu_clocks():
-    """Current shader and memory clock levels of the first GPU, read from the
-    amdgpu sysfs tables that rocm-smi reports (the level marked '*'), right
-    after the timed steps. File reads only: no child process. None where the
-    files are missing."""
-    import glob
-    out = {}
+def gpu_clocks(torch):
+    """Current shader and memory clock levels of the GPU the bench ran on
+    (device 0 of this process), read from the amdgpu sysfs tables of its PCI
+    device (the level marked '*'), right after the timed steps. File reads
+    only: no child process. None where the files are missing."""
+    p = torch.cuda.get_device_properties(0)
+    bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    out = {"pci": bdf}
     for key, name in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
-        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/{name}")):
-            try:
-                cur = [ln.split(":", 1)[1].replace("*", "").strip() for ln in open(path).read().splitlines()
-                       if ln.rstrip().endswith("*")]
-            except OSError:
-                continue
-            if cur:
-                out[key] = cur[0]
-                break
-    return out or None
+        path = f"/sys/bus/pci/devices/{bdf}/{name}"
+        try:
+            cur = [ln.split(":", 1)[1].replace("*", "").strip() for ln in open(path).read().splitlines()
+                   if ln.rstrip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            out[key] = cur[0]
+    return out if len(out) > 1 else None
+
+
+def measured_peaks(torch, mx):
+    """The ceilings this GPU reaches, measured with the library's probes beside
+    the published peaks: the scaled FP4 MFMA in a register-only loop, a 1 GiB
+    read into registers and into LDS (the GEMMs' copy instruction), and a
+    512 MiB device copy. Each probe's result is checked before its rate is
+    reported (MFMA sums against their closed form, read checksums against
+    torch's, the copy byte for byte)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps   # ms
+
+    out = {}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    rng = np.random.default_rng(0)
+    operand_sets = {
+        # codes 3 and 5 (1.5 and 3) in every nibble of A and B: each output of a
+        # step is 32 * (1.5 * 1.5 + 3 * 3) = 360, a lane's sum 64 * 360 * iters
+        "constant": (np.full((512, 16), 0x35353535, np.uint32), 64 * 360.0 * iters),
+        # uniform random codes: the data the GEMMs see (more switching power);
+        # every workgroup must produce the same sums as workgroup 0
+        "random": (rng.integers(0, 2**32, (512, 16), dtype=np.uint64).astype(np.uint32), None),
+    }
+    for tag, (host, want) in operand_sets.items():
+        ops = torch.from_numpy(host.view(np.int32)).cuda()
+        best = None
+        for wgs in (cus, 2 * cus, 4 * cus):
+            res = mx.probe_mfma_fp4(ops, iters, wgs)
+            ms = timed(lambda: mx.probe_mfma_fp4(ops, iters, wgs, out=res), 3)
+            ok = torch.all(res == want).item() if want is not None else torch.all(res == res[0:1]).item()
+            if not ok:
+                raise RuntimeError(f"MFMA probe result check failed ({tag} operands)")
+            tf = wgs * 8 * iters * 4 * 131072 / ms / 1e9
+            if best is None or tf > best[0]:
+                best = (tf, wgs)
+        out[f"mfma_fp4_loop_{tag}_operands"] = {
+            "TFLOP/s": round(best[0], 1), "spec_TFLOP/s": PEAK_FP4_TFLOPS,
+            "frac_of_spec": round(best[0] / PEAK_FP4_TFLOPS, 4), "workgroups": best[1],
+            "note": "512-thread workgroups, 4 independent accumulators per wave, operands in registers"}
+    nbytes = 1 << 30
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    want = None
+    for mode, name in ((0, "read_to_registers"), (1, "read_to_lds_dma")):
+        best = None
+        for lpw, wgs in ((8, 8 * cus), (32, 2 * cus), (32, cus)):
+            res = mx.probe_read(src, mode, lpw, wgs)
+            ms = timed(lambda: mx.probe_read(src, mode, lpw, wgs, out=res), 5)
+            got = int(np.bitwise_xor.reduce(res.cpu().numpy().view(np.uint32)))
+            if want is None:
+                want = int(np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32)))
+            if got != want:
+                raise RuntimeError(f"read probe checksum mismatch ({name})")
+            gbs = nbytes / ms / 1e6
+            if best is None or gbs > best[0]:
+                best = (gbs, lpw, wgs)
+        out[f"hbm_{name}"] = {"GB/s": round(best[0], 1), "spec_GB/s": PEAK_HBM_GBS,
+                              "frac_of_spec": round(best[0] / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                              "loads_per_wave": best[1], "workgroups": best[2]}
+    del src
+    cb = 1 << 29
+    a = torch.randint(0, 255, (cb,), dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    ms = timed(lambda: mx.probe_copy(a, b), 5)
+    if not torch.equal(a, b):
+        raise RuntimeError("copy probe output differs from its input")
+    out["hbm_copy"] = {"GB/s": round(2 * cb / ms / 1e6, 1), "spec_GB/s": PEAK_HBM_GBS,
+                       "frac_of_spec": round(2 * cb / ms / 1e6 / PEAK_HBM_GBS, 4),
+                       "bytes_moved": 2 * cb, "note": "read + write of 512 MiB"}
+    return out
 
 
 def cpu_baseline(d, n_exp):
@@ -401,8 +483,12 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    ms, phases = time_steps(torch, step, a.steps, a.warmup, profile=(mx.profile_start, mx.profile_stop))
-    clocks = gpu_clocks()
+    # the headline: K steps with nothing else recorded
+    ms, _ = time_steps(torch, step, a.steps, a.warmup)
+    clocks = gpu_clocks(torch)
+    # the phase split: the same K steps again, every kernel bracketed by HIP
+    # events on the stream it runs on (the library's profiler)
+    ms_prof, phases = time_steps(torch, step, a.steps, 1, profile=(mx.profile_start, mx.profile_stop))
     flops = 6.0 * T * K * H * I
     value = flops / ms / 1e9   # TFLOP/s
     l1_ms, l1_n = phases["l1_gemm"]
@@ -427,11 +513,14 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "l1_gemm (gate/up GEMM + SiLU*up + MXFP4 re-quant)",
                      "achieved": round(achieved, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": traffic,
-                     "algorithmic_flops_per_launch": l1_flops, "avg_launch_ms": round(l1_avg, 4)},
+                     "algorithmic_flops_per_launch": l1_flops, "avg_launch_ms": round(l1_avg, 4),
+                     "timing": "HIP events around each launch, in a second pass of the same steps"},
         "phases_ms_per_step": {k: round(v[0] / v[1], 4) for k, v in phases.items()},
+        "ms_per_step_with_phase_events": round(ms_prof, 4),
         "gpu_clocks_after_timed_steps": clocks,
     }
     if not a.no_secondary:
+        rec["measured_peaks"] = measured_peaks(torch, mx)
         rec["secondary"] = secondary(torch, mx, workloads)
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(d, a.cpu_experts)

@@ -460,6 +460,36 @@ typedef struct mx_phase_stat {
 MX_API mx_status mx_profile_start(void);
 MX_API mx_status mx_profile_stop(mx_phase_stat* stats, int32_t max_stats, int32_t* n_stats);
 
+/*
+ * Measurement probes (not steps of the pages' pipeline): kernels whose measured
+ * rates stand beside MI355X's published peaks (10.1 PFLOP/s dense FP4 matrix
+ * math, 8 TB/s HBM3E) as the ceilings this machine reaches. Each result can be
+ * checked, so a rate never comes from work the compiler dropped.
+ *   mx_probe_mfma_fp4: `workgroups` x 8 waves, each running `iters` iterations
+ *     of four independent V_MFMA_SCALE_F32_32X32X64_F8F6F4 on FP4 operands held
+ *     in registers (scale bytes 127). FLOPs = workgroups * 8 * iters * 4 * 131072.
+ *     operands: DEVICE, 512 x 16 uint32, the same for every workgroup, 16-byte
+ *     aligned: thread t's FP4 A operand is words [16t, 16t+4) and its B operand
+ *     words [16t+8, 16t+12) (32 E2M1 codes each; the other words are not read).
+ *     out: DEVICE, workgroups * 512 floats, out[w * 512 + t] = the sum of
+ *     thread t's 64 accumulator values. 1 <= workgroups <= 65536,
+ *     1 <= iters <= 2^20.
+ *   mx_probe_read: reads `bytes` of src once. mode 0 into registers
+ *     (GLOBAL_LOAD_DWORDX4), mode 1 into LDS (GLOBAL_LOAD_LDS_DWORDX4, the copies
+ *     of the tiled GEMMs); each wave issues loads_per_wave (8 or 32) 16-byte
+ *     loads per lane at once, 256-thread workgroups. bytes > 0 and a multiple
+ *     of loads_per_wave * 1024; src 16-byte aligned; out: DEVICE, workgroups *
+ *     4 uint32 whose XOR equals the XOR of all 32-bit words of src.
+ *   mx_probe_copy: dst[0, bytes) = src[0, bytes); bytes % 16 == 0, both 16-byte
+ *     aligned, not overlapping.
+ * Errors as for every entry point (MX_ERR_NULL / SHAPE / ALIGN / VALUE / HIP).
+ */
+MX_API mx_status mx_probe_mfma_fp4(const uint32_t* operands, int64_t iters, int32_t workgroups, float* out,
+                                   void* stream);
+MX_API mx_status mx_probe_read(int32_t mode, int32_t loads_per_wave, int32_t workgroups, const void* src,
+                               int64_t bytes, uint32_t* out, void* stream);
+MX_API mx_status mx_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

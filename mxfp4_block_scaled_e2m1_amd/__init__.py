@@ -10,7 +10,7 @@ from .binding import (  # noqa: F401
     fp8_block_linear_workspace_size, fp8_expert_mlp, fp8_expert_mlp_workspace_size, grouped_expert_mlp,
     grouped_expert_mlp_workspace_size, grouped_nvfp4_expert_mlp, grouped_nvfp4_expert_mlp_workspace_size, lib, nvfp4_global_warmup, nvfp4_linear, nvfp4_linear_workspace_size,
     nvfp4_expert_mlp, nvfp4_expert_mlp_workspace_size, pack_weight_scales, packed_weight_scales_size,
-    profile_start, profile_stop, quantize_act,
+    probe_copy, probe_mfma_fp4, probe_read, profile_start, profile_stop, quantize_act,
 )
 
 __all__ = [
@@ -20,5 +20,6 @@ __all__ = [
     "grouped_expert_mlp", "grouped_expert_mlp_workspace_size",
     "grouped_nvfp4_expert_mlp", "grouped_nvfp4_expert_mlp_workspace_size", "lib", "nvfp4_global_warmup", "nvfp4_linear", "nvfp4_linear_workspace_size",
     "nvfp4_expert_mlp", "nvfp4_expert_mlp_workspace_size", "pack_weight_scales",
-    "packed_weight_scales_size", "profile_start", "profile_stop", "quantize_act",
+    "packed_weight_scales_size", "probe_copy", "probe_mfma_fp4", "probe_read", "profile_start", "profile_stop",
+    "quantize_act",
 ]

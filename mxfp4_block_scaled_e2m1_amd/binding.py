@@ -65,6 +65,9 @@ SIGNATURES = {
     "mx_last_error": (ctypes.c_char_p, []),
     "mx_profile_start": (_I32, []),
     "mx_profile_stop": (_I32, [ctypes.POINTER(PhaseStat), _I32, ctypes.POINTER(_I32)]),
+    "mx_probe_mfma_fp4": (_I32, [_P, _I64, _I32, _P, _P]),
+    "mx_probe_read": (_I32, [_I32, _I32, _I32, _P, _I64, _P, _P]),
+    "mx_probe_copy": (_I32, [_P, _P, _I64, _P]),
 }
 
 _lib = None
@@ -283,6 +286,32 @@ def profile_stop():
     n = _I32(0)
     _check(lib().mx_profile_stop(buf, 64, ctypes.byref(n)))
     return {buf[i].name.decode(): (buf[i].total_ms, int(buf[i].launches)) for i in range(min(n.value, 64))}
+
+
+def probe_mfma_fp4(operands, iters: int, workgroups: int, out=None, stream=None):
+    """mx_probe_mfma_fp4: operands uint32 [512, 16] (device); returns float32 [workgroups, 512]."""
+    if out is None:
+        out = torch.empty((workgroups, 512), dtype=torch.float32, device=operands.device)
+    _check(lib().mx_probe_mfma_fp4(_ptr(operands), iters, workgroups, _ptr(out), _stream(stream)))
+    return out
+
+
+def probe_read(src, mode: int, loads_per_wave: int, workgroups: int, out=None, stream=None):
+    """mx_probe_read over all bytes of src; returns the per-wave XOR words (int32 [workgroups * 4])."""
+    if out is None:
+        out = torch.empty(workgroups * 4, dtype=torch.int32, device=src.device)
+    nbytes = src.numel() * src.element_size()
+    _check(lib().mx_probe_read(mode, loads_per_wave, workgroups, _ptr(src), nbytes, _ptr(out), _stream(stream)))
+    return out
+
+
+def probe_copy(src, dst, stream=None):
+    """mx_probe_copy: dst = src (same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _check(lib().mx_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+    return dst
 
 
 def fp8_block_linear_workspace_size(M, K) -> int:

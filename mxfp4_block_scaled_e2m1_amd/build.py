@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxfp4.so")
-SOURCES = ["mx_api.hip", "gemm.hip", "gemm_nv.hip", "decode.hip", "elementwise.hip", "route.hip", "pack.hip", "fp8_linear.hip"]
+SOURCES = ["mx_api.hip", "gemm.hip", "gemm_nv.hip", "decode.hip", "elementwise.hip", "route.hip", "pack.hip", "fp8_linear.hip",
+           "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

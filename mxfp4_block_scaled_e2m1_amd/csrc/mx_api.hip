@@ -1309,5 +1309,53 @@ mx_status mx_moe_runner_destroy(mx_moe_runner* r) {
   return ok();
 }
 
+// ---------------------------------------------------------------- measurement probes
+mx_status mx_probe_mfma_fp4(const uint32_t* operands, int64_t iters, int32_t workgroups, float* out,
+                            void* stream) {
+  if (workgroups < 1 || workgroups > 65536) return fail(MX_ERR_VALUE, "workgroups %d not in [1, 65536]", workgroups);
+  if (iters < 1 || iters > ((int64_t)1 << 20)) return fail(MX_ERR_VALUE, "iters %lld not in [1, 2^20]", (long long)iters);
+  MX_REQUIRE_PTR(operands);
+  MX_REQUIRE_PTR(out);
+  MX_REQUIRE_ALIGN(operands, 16);
+  MX_REQUIRE_ALIGN(out, 4);
+  hipStream_t s = (hipStream_t)stream;
+  MX_HIP(phase("probe_mfma", s, [&] { return launch_probe_mfma(operands, iters, workgroups, out, s); }),
+         "probe_mfma");
+  return ok();
+}
+
+mx_status mx_probe_read(int32_t mode, int32_t loads_per_wave, int32_t workgroups, const void* src, int64_t bytes,
+                        uint32_t* out, void* stream) {
+  if (mode != 0 && mode != 1) return fail(MX_ERR_VALUE, "mode %d is not 0 (registers) or 1 (LDS)", mode);
+  if (loads_per_wave != 8 && loads_per_wave != 32)
+    return fail(MX_ERR_VALUE, "loads_per_wave %d is not 8 or 32", loads_per_wave);
+  if (workgroups < 1 || workgroups > 65536) return fail(MX_ERR_VALUE, "workgroups %d not in [1, 65536]", workgroups);
+  const int64_t chunk = (int64_t)loads_per_wave * 1024;
+  if (bytes <= 0 || bytes % chunk != 0)
+    return fail(MX_ERR_SHAPE, "bytes %lld is not a positive multiple of %lld", (long long)bytes, (long long)chunk);
+  MX_REQUIRE_PTR(src);
+  MX_REQUIRE_PTR(out);
+  MX_REQUIRE_ALIGN(src, 16);
+  MX_REQUIRE_ALIGN(out, 4);
+  hipStream_t s = (hipStream_t)stream;
+  MX_HIP(phase("probe_read", s, [&] { return launch_probe_read(mode, loads_per_wave, workgroups, src, bytes, out, s); }),
+         "probe_read");
+  return ok();
+}
+
+mx_status mx_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return fail(MX_ERR_SHAPE, "bytes %lld is not a multiple of 16", (long long)bytes);
+  if (bytes == 0) return ok();
+  MX_REQUIRE_PTR(src);
+  MX_REQUIRE_PTR(dst);
+  MX_REQUIRE_ALIGN(src, 16);
+  MX_REQUIRE_ALIGN(dst, 16);
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes) return fail(MX_ERR_VALUE, "src and dst overlap");
+  hipStream_t s = (hipStream_t)stream;
+  MX_HIP(phase("probe_copy", s, [&] { return launch_probe_copy(src, dst, bytes, s); }), "probe_copy");
+  return ok();
+}
+
 }  // extern "C"
 

@@ -201,4 +201,12 @@ bool fp8_linear_fits(int64_t K);
 // h = bf16(silu(g) * u) elementwise over n values (n % 8 == 0, 16-byte aligned).
 hipError_t launch_silu_mul_bf16(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* h, hipStream_t s);
 
+// Measurement probes (probe.hip). mode 0: reads into registers, 1: into LDS;
+// loads_per_wave 8 or 32; bytes a multiple of loads_per_wave KiB; out holds
+// workgroups * 4 words. operands: 512 x 16 words; out: workgroups * 512 floats.
+hipError_t launch_probe_mfma(const uint32_t* operands, int64_t iters, int workgroups, float* out, hipStream_t s);
+hipError_t launch_probe_read(int mode, int loads_per_wave, int workgroups, const void* src, int64_t bytes,
+                             uint32_t* out, hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
 }  // namespace mx

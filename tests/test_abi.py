@@ -275,3 +275,24 @@ def test_noalloc_validation(L):
         big *= 2
     assert L.mx_expert_mlp_noalloc(P(256), big, 7168, 3072, *z, None, 0, None, P(256), None) == 5
     assert "no-allocation" in _err(L)
+
+
+def test_probe_validation(L):
+    """The measurement probes reject bad sizes, modes and pointers on the host."""
+    P = ctypes.c_void_p
+    assert L.mx_probe_mfma_fp4(P(256), 0, 4, P(256), None) == 7
+    assert L.mx_probe_mfma_fp4(P(256), (1 << 20) + 1, 4, P(256), None) == 7
+    assert L.mx_probe_mfma_fp4(P(256), 8, 0, P(256), None) == 7
+    assert L.mx_probe_mfma_fp4(None, 8, 4, P(256), None) == 1
+    assert L.mx_probe_mfma_fp4(P(264), 8, 4, P(256), None) == 3
+    assert L.mx_probe_read(2, 8, 4, P(256), 8192, P(256), None) == 7
+    assert L.mx_probe_read(0, 16, 4, P(256), 8192, P(256), None) == 7
+    assert L.mx_probe_read(0, 8, 4, P(256), 8192 + 1024, P(256), None) == 2
+    assert L.mx_probe_read(1, 32, 4, P(256), 8192, P(256), None) == 2
+    assert L.mx_probe_read(0, 8, 4, P(256), 0, P(256), None) == 2
+    assert L.mx_probe_read(0, 8, 4, None, 8192, P(256), None) == 1
+    assert L.mx_probe_read(0, 8, 4, P(264), 8192, P(256), None) == 3
+    assert L.mx_probe_copy(P(256), P(4096), 24, None) == 2
+    assert L.mx_probe_copy(P(256), P(512), 512, None) == 7 and "overlap" in _err(L)
+    assert L.mx_probe_copy(P(256), P(4096), 0, None) == 0
+    assert L.mx_probe_copy(P(264), P(4096), 512, None) == 3
