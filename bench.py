@@ -137,14 +137,16 @@ def secondary(torch, mx, workloads):
     wbytes = sum(v.numel() for v in w0.values())
     # 16 weight copies (~561 MB) so that successive calls miss the 256 MB cache
     copies = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(15)]
-    for c in copies:   # load-time step: tile-major weight scales
+    for c in copies:   # load-time step: tile-major weight scales and codes
         c["pk"] = mx.pack_weight_scales(c["w1s"], c["w3s"], c["w2s"])
+        c["pc"] = mx.pack_weight_codes(c["w1"], c["w3"], c["w2"])
     for M in (1, 8, 128):
         x = bf16_dev(torch, workloads.activations(1, M))
         ws = torch.empty(mx.expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
         y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
         calls = [lambda w=w: mx.expert_mlp(x, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"], out=y,
-                                           workspace=ws, packed_scales=w["pk"]) for w in copies]
+                                           workspace=ws, packed_scales=w["pk"], packed_codes=w["pc"])
+                 for w in copies]
         us = graph_replay_us(torch, calls)
         out[f"shared_expert_M{M}"] = {"us_per_call": round(us, 2), "weight_GB/s": round(wbytes / us / 1e3, 1),
                                       "hbm_frac": round(wbytes / us / 1e3 / PEAK_HBM_GBS, 3),
@@ -155,7 +157,7 @@ def secondary(torch, mx, workloads):
     ws = torch.empty(mx.expert_mlp_workspace_size(M, H, I), dtype=torch.uint8, device="cuda")
     y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     fn = lambda: mx.expert_mlp(x, w0["w1"], w0["w1s"], w0["w3"], w0["w3s"], w0["w2"], w0["w2s"], out=y, workspace=ws,
-                               packed_scales=w0["pk"])
+                               packed_scales=w0["pk"], packed_codes=w0["pc"])
     ms, _ = time_steps(torch, fn, 20, 3)
     flops = 6.0 * M * H * I
     out["shared_expert_M4096"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
@@ -296,10 +298,12 @@ def skewed_nvfp4(torch, mx, workloads):
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mx.grouped_expert_mlp_workspace_size(T, H, I, K, E, "nvfp4"), dtype=torch.uint8, device="cuda")
     pk = mx.pack_weight_scales(w["w1s"], w["w3s"], w["w2s"])
+    pc = mx.pack_weight_codes(w["w1"], w["w3"], w["w2"])
 
     def step():
         mx.grouped_expert_mlp(x, w["ids"], w["w"], w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
-                              requant="nvfp4", requant_global=g, out=y, workspace=ws, packed_scales=pk)
+                              requant="nvfp4", requant_global=g, out=y, workspace=ws, packed_scales=pk,
+                              packed_codes=pc)
     ms, phases = time_steps(torch, step, 5, 2, profile=(mx.profile_start, mx.profile_stop))
     P = T * K
     flops = 6.0 * P * H * I
@@ -319,7 +323,7 @@ def skewed_nvfp4(torch, mx, workloads):
         wst = torch.empty(mx.grouped_expert_mlp_workspace_size(8, H, I, K, E, rq), dtype=torch.uint8, device="cuda")
         tail = lambda: mx.grouped_expert_mlp(xt, idt, wt, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
                                              requant=rq, requant_global=g, out=yt, workspace=wst,
-                                             packed_scales=pk)
+                                             packed_scales=pk, packed_codes=pc)
         us = graph_replay_us(torch, [tail])
         rec[f"skewed_decode_tail_t8_{rq}"] = {
             "us_per_call": round(us, 2), "active_experts": n_active, "weight_GB/s": round(tbytes / us / 1e3, 1),
@@ -472,10 +476,11 @@ def main():
     # load-time step, outside the timed region: the weight scales re-laid
     # tile-major once (mx_pack_weight_scales), as a runner does after loading
     pk = mx.pack_weight_scales(w["w1s"], w["w3s"], w["w2s"])
+    pc = mx.pack_weight_codes(w["w1"], w["w3"], w["w2"])
 
     def step():
         mx.grouped_expert_mlp(x, w["ids"], w["w"], w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"],
-                              out=y, workspace=ws, packed_scales=pk)
+                              out=y, workspace=ws, packed_scales=pk, packed_codes=pc)
 
     if a.calibration_copy:
         src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -507,8 +512,8 @@ def main():
                                "inter 3072, MXFP4 weights and activations",
                    "experts": E, "tokens": T, "top_k": K, "hidden": H, "inter": I,
                    "parallelism": "single GPU",
-                   "weight_prep": "E8M0 weight scales re-laid tile-major once after load (mx_pack_weight_scales), "
-                                  "not timed"},
+                   "weight_prep": "E8M0 weight scales and FP4 weight codes re-laid tile-major once after load "
+                                  "(mx_pack_weight_scales, mx_pack_weight_codes), not timed"},
         "frac_of_fp4_peak": round(value / PEAK_FP4_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "l1_gemm (gate/up GEMM + SiLU*up + MXFP4 re-quant)",
                      "achieved": round(achieved, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",

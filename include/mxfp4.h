@@ -156,6 +156,11 @@ MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t 
  * packed_scales: NULL, or the output of mx_pack_weight_scales() for these
  * weights (E = 1, same hidden and inter), 256-byte aligned. The GEMM path then
  * reads the weight scales from it; the results are identical either way.
+ * packed_codes: NULL, or the output of mx_pack_weight_codes() for these weights
+ * (E = 1, same hidden and inter), 256-byte aligned: the GEMM path then copies
+ * the weight codes from it (whole cache lines, one contiguous 1 KB piece per
+ * copy); the results are identical either way. w1, w3 and w2 are still
+ * required (the few-token kernels stream them row by row).
  * workspace: device memory of at least mx_expert_mlp_workspace_size() bytes,
  * 256-byte aligned; its contents are scratch. y must not alias x or workspace.
  * Alignment: x, y, codes 16 bytes; scales and requant_global 4 bytes.
@@ -163,8 +168,9 @@ MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t 
 MX_API mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter,
                         const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                         const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                        const uint8_t* packed_scales, mx_format requant, const float* requant_global,
-                        uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+                        const uint8_t* packed_scales, const uint8_t* packed_codes, mx_format requant,
+                        const float* requant_global, uint16_t* y, void* workspace, size_t ws_bytes,
+                        void* stream);
 
 /* Workspace bytes of mx_expert_mlp for these sizes (the caller-owned scratch of
  * the pages' pre-allocated runner: "Current Bug ...", "Revised Plan", Phase 1);
@@ -192,8 +198,9 @@ MX_API size_t mx_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t in
 MX_API mx_status mx_expert_mlp_noalloc(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter,
                                        const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                                        const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                                       const uint8_t* packed_scales, mx_format requant,
-                                       const float* requant_global, uint16_t* y, void* stream);
+                                       const uint8_t* packed_scales, const uint8_t* packed_codes,
+                                       mx_format requant, const float* requant_global, uint16_t* y,
+                                       void* stream);
 /* Bytes of the fixed device array behind mx_expert_mlp_noalloc (64 MiB). */
 MX_API size_t mx_expert_mlp_noalloc_max_bytes(void);
 
@@ -215,16 +222,17 @@ MX_API size_t mx_expert_mlp_noalloc_max_bytes(void);
  * weight and writes one bf16 row per pair; a final pass sums each token's k
  * rows in slot order in fp32 (deterministic: no atomics).
  * 1 <= k <= E <= 512; hidden % 128 == 0; inter % 128 == 0. requant,
- * requant_global and packed_scales (here for all E experts) as for
- * mx_expert_mlp.
+ * requant_global, packed_scales and packed_codes (here for all E experts) as
+ * for mx_expert_mlp.
  * Alignment as for mx_expert_mlp; topk_ids and topk_w 4 bytes.
  */
 MX_API mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, int64_t inter,
                                 const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                 const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                                 const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                                const uint8_t* packed_scales, mx_format requant, const float* requant_global,
-                                uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+                                const uint8_t* packed_scales, const uint8_t* packed_codes, mx_format requant,
+                                const float* requant_global, uint16_t* y, void* workspace, size_t ws_bytes,
+                                void* stream);
 
 /* Workspace bytes of mx_grouped_expert_mlp for these sizes (caller-owned
  * scratch, as for mx_expert_mlp_workspace_size); 0 for invalid sizes. */
@@ -251,6 +259,32 @@ MX_API mx_status mx_pack_weight_scales(const uint8_t* w1_s, const uint8_t* w3_s,
                                        size_t packed_bytes, void* stream);
 
 MX_API size_t mx_packed_weight_scales_size(int64_t hidden, int64_t inter, int32_t E);
+
+/*
+ * mx_pack_weight_codes -- re-lay the FP4 weight codes of E experts once, after
+ * the weights are loaded, in the order the FP4 GEMM copies them into LDS: for
+ * each 256-row weight tile (L1: the tile's gate and up rows; L2: w2 rows) and
+ * each 128-wide half stage of K, one 16 KB block that is the byte image of the
+ * GEMM's LDS slot. A copy then reads whole cache lines, 1 KB in one piece,
+ * instead of 16 rows x 64 bytes scattered over 16 rows of the matrix. As for
+ * the scales, the pages' runner prepares its weights once before serving (page
+ * "Current Bug: vLLM produces empty/garbage output", section "Revised Plan",
+ * Phase 1).
+ *   w1, w3 [E, inter, hidden/2]; w2 [E, hidden, inter/2] (E2M1 codes), 16-byte
+ *   aligned. packed: device buffer of mx_packed_weight_codes_size(hidden,
+ *   inter, E) bytes (as large as the three code tensors, rounded up to whole
+ *   tiles), 256-byte aligned, owned by the caller and passed to mx_expert_mlp
+ *   (E = 1), mx_expert_mlp_noalloc, mx_grouped_expert_mlp or
+ *   mx_moe_runner_create as packed_codes. Its layout is internal.
+ * Shapes as for mx_grouped_expert_mlp; MX_ERR_WORKSPACE if packed_bytes is too
+ * small.
+ */
+MX_API mx_status mx_pack_weight_codes(const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, int64_t hidden,
+                                      int64_t inter, int32_t E, uint8_t* packed, size_t packed_bytes,
+                                      void* stream);
+
+/* Bytes of mx_pack_weight_codes' output; 0 for invalid sizes. */
+MX_API size_t mx_packed_weight_codes_size(int64_t hidden, int64_t inter, int32_t E);
 
 /*
  * mx_nvfp4_global_warmup -- the fp32 global scale g of the NVFP4 re-quantisation
@@ -433,8 +467,9 @@ MX_API mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidd
                                       const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                       const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3,
                                       const uint8_t* w3_s, const uint8_t* w2, const uint8_t* w2_s,
-                                      const uint8_t* packed_scales, mx_format requant,
-                                      const float* requant_global, uint16_t* y, mx_moe_runner** out);
+                                      const uint8_t* packed_scales, const uint8_t* packed_codes,
+                                      mx_format requant, const float* requant_global, uint16_t* y,
+                                      mx_moe_runner** out);
 MX_API mx_status mx_moe_runner_replay(mx_moe_runner* r, void* stream);
 MX_API mx_status mx_moe_runner_destroy(mx_moe_runner* r);
 

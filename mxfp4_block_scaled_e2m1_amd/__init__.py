@@ -9,8 +9,8 @@ from .binding import (  # noqa: F401
     fp8_block_linear,
     fp8_block_linear_workspace_size, fp8_expert_mlp, fp8_expert_mlp_workspace_size, grouped_expert_mlp,
     grouped_expert_mlp_workspace_size, grouped_nvfp4_expert_mlp, grouped_nvfp4_expert_mlp_workspace_size, lib, nvfp4_global_warmup, nvfp4_linear, nvfp4_linear_workspace_size,
-    nvfp4_expert_mlp, nvfp4_expert_mlp_workspace_size, pack_weight_scales, packed_weight_scales_size,
-    probe_copy, probe_mfma_fp4, probe_read, profile_start, profile_stop, quantize_act,
+    nvfp4_expert_mlp, nvfp4_expert_mlp_workspace_size, pack_weight_codes, pack_weight_scales,
+    packed_weight_codes_size, packed_weight_scales_size, probe_copy, probe_mfma_fp4, probe_read, profile_start, profile_stop, quantize_act,
 )
 
 __all__ = [
@@ -19,7 +19,7 @@ __all__ = [
     "fp8_block_linear_workspace_size", "fp8_expert_mlp", "fp8_expert_mlp_workspace_size",
     "grouped_expert_mlp", "grouped_expert_mlp_workspace_size",
     "grouped_nvfp4_expert_mlp", "grouped_nvfp4_expert_mlp_workspace_size", "lib", "nvfp4_global_warmup", "nvfp4_linear", "nvfp4_linear_workspace_size",
-    "nvfp4_expert_mlp", "nvfp4_expert_mlp_workspace_size", "pack_weight_scales",
-    "packed_weight_scales_size", "probe_copy", "probe_mfma_fp4", "probe_read", "profile_start", "profile_stop",
+    "nvfp4_expert_mlp", "nvfp4_expert_mlp_workspace_size", "pack_weight_codes", "pack_weight_scales",
+    "packed_weight_codes_size", "packed_weight_scales_size", "probe_copy", "probe_mfma_fp4", "probe_read", "profile_start", "profile_stop",
     "quantize_act",
 ]

@@ -32,18 +32,20 @@ class PhaseStat(ctypes.Structure):
 SIGNATURES = {
     "mx_dequant": (_I32, [_I32, _P, _P, _P, _I64, _I64, _P, _P]),
     "mx_quantize_act": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P, _P]),
-    "mx_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "mx_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "mx_nvfp4_global_warmup": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                       _P]),
     "mx_nvfp4_global_warmup_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "mx_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
-    "mx_expert_mlp_noalloc": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]),
+    "mx_expert_mlp_noalloc": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]),
     "mx_expert_mlp_noalloc_max_bytes": (_SZ, []),
     "mx_grouped_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                     _P, _I32, _P, _P, _P, _SZ, _P]),
+                                     _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "mx_grouped_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
     "mx_pack_weight_scales": (_I32, [_P, _P, _P, _I64, _I64, _I32, _P, _SZ, _P]),
     "mx_packed_weight_scales_size": (_SZ, [_I64, _I64, _I32]),
+    "mx_pack_weight_codes": (_I32, [_P, _P, _P, _I64, _I64, _I32, _P, _SZ, _P]),
+    "mx_packed_weight_codes_size": (_SZ, [_I64, _I64, _I32]),
     "mx_debug_gemm_f32": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "mx_fp8_block_linear": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
     "mx_fp8_block_linear_workspace_size": (_SZ, [_I64, _I64]),
@@ -57,8 +59,8 @@ SIGNATURES = {
     "mx_grouped_nvfp4_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "mx_fp8_expert_mlp": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mx_fp8_expert_mlp_workspace_size": (_SZ, [_I64, _I64, _I64]),
-    "mx_moe_runner_create": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32,
-                                    _P, _P, ctypes.POINTER(_P)]),
+    "mx_moe_runner_create": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _I32, _P, _P, ctypes.POINTER(_P)]),
     "mx_moe_runner_replay": (_I32, [_P, _P]),
     "mx_moe_runner_destroy": (_I32, [_P]),
     "mx_status_string": (ctypes.c_char_p, [_I32]),
@@ -195,8 +197,25 @@ def pack_weight_scales(w1s, w3s, w2s, out=None, stream=None):
     return out
 
 
+def packed_weight_codes_size(hidden, inter, E=1) -> int:
+    return int(lib().mx_packed_weight_codes_size(hidden, inter, E))
+
+
+def pack_weight_codes(w1, w3, w2, out=None, stream=None):
+    """mx_pack_weight_codes: tile-major copy of the weight codes of one expert
+    (w1 [inter, hidden/2]) or of E stacked experts (w1 [E, inter, hidden/2])."""
+    E = w1.shape[0] if w1.dim() == 3 else 1
+    inter, hidden = w1.shape[-2], 2 * w1.shape[-1]
+    nbytes = packed_weight_codes_size(hidden, inter, E)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w1.device)
+    _check(lib().mx_pack_weight_codes(_ptr(w1), _ptr(w3), _ptr(w2), hidden, inter, E, _ptr(out), out.numel(),
+                                      _stream(stream)))
+    return out
+
+
 def expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global=None,
-               out=None, workspace=None, stream=None, packed_scales=None):
+               out=None, workspace=None, stream=None, packed_scales=None, packed_codes=None):
     """mx_expert_mlp: the shared expert on bf16 x [M, hidden] -> bf16 y [M, hidden].
     requant_global (NVFP4): float or one-element fp32 device tensor."""
     M, hidden = x.shape
@@ -207,13 +226,13 @@ def expert_mlp(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global=Non
     ws = _workspace(nbytes, x.device, workspace)
     g = _global(requant_global, x.device)
     _check(lib().mx_expert_mlp(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s),
-                               _ptr(w2), _ptr(w2s), _ptr(packed_scales), _fmt(requant), _ptr(g),
-                               _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+                               _ptr(w2), _ptr(w2s), _ptr(packed_scales), _ptr(packed_codes), _fmt(requant),
+                               _ptr(g), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
 def expert_mlp_noalloc(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_global=None, out=None,
-                       stream=None, packed_scales=None):
+                       stream=None, packed_scales=None, packed_codes=None):
     """mx_expert_mlp_noalloc: mx_expert_mlp on the library's fixed device scratch
     (no workspace argument; calls on one GPU must not overlap)."""
     M, hidden = x.shape
@@ -222,13 +241,14 @@ def expert_mlp_noalloc(x, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4", requant_gl
         out = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
     g = _global(requant_global, x.device)
     _check(lib().mx_expert_mlp_noalloc(_ptr(x), M, hidden, inter, _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s),
-                                       _ptr(w2), _ptr(w2s), _ptr(packed_scales), _fmt(requant), _ptr(g),
-                                       _ptr(out), _stream(stream)))
+                                       _ptr(w2), _ptr(w2s), _ptr(packed_scales), _ptr(packed_codes),
+                                       _fmt(requant), _ptr(g), _ptr(out), _stream(stream)))
     return out
 
 
 def grouped_expert_mlp(x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4",
-                       requant_global=None, out=None, workspace=None, stream=None, packed_scales=None):
+                       requant_global=None, out=None, workspace=None, stream=None, packed_scales=None,
+                       packed_codes=None):
     """mx_grouped_expert_mlp: routed experts, stacked weights [E, ...]. requant_global
     (NVFP4): float or one-element fp32 device tensor."""
     T, hidden = x.shape
@@ -241,8 +261,8 @@ def grouped_expert_mlp(x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="
     g = _global(requant_global, x.device)
     _check(lib().mx_grouped_expert_mlp(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
                                        _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2), _ptr(w2s),
-                                       _ptr(packed_scales), _fmt(requant), _ptr(g), _ptr(out),
-                                       _ptr(ws), ws.numel(), _stream(stream)))
+                                       _ptr(packed_scales), _ptr(packed_codes), _fmt(requant), _ptr(g),
+                                       _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
@@ -406,18 +426,18 @@ class MoeRunner:
     place, then replay()."""
 
     def __init__(self, x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, requant="mxfp4",
-                 requant_global=None, out=None, packed_scales=None):
+                 requant_global=None, out=None, packed_scales=None, packed_codes=None):
         T, hidden = x.shape
         k = topk_ids.shape[1]
         E, inter = w1.shape[0], w1.shape[1]
         self.out = out if out is not None else torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
         g = _global(requant_global, x.device)
         # keep the bound tensors alive as long as the runner
-        self._bound = (x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, packed_scales, self.out, g)
+        self._bound = (x, topk_ids, topk_w, w1, w1s, w3, w3s, w2, w2s, packed_scales, packed_codes, self.out, g)
         h = _P()
         _check(lib().mx_moe_runner_create(_ptr(x), T, hidden, inter, _ptr(topk_ids), _ptr(topk_w), k, E,
                                           _ptr(w1), _ptr(w1s), _ptr(w3), _ptr(w3s), _ptr(w2), _ptr(w2s),
-                                          _ptr(packed_scales), _fmt(requant), _ptr(g),
+                                          _ptr(packed_scales), _ptr(packed_codes), _fmt(requant), _ptr(g),
                                           _ptr(self.out), ctypes.byref(h)))
         self._h = h
 

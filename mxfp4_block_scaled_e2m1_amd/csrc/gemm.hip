@@ -17,21 +17,26 @@
 //    At FP4 rate the tile needs 32 B/clk/CU of operand bytes from L2.
 //  * The packed layout is already the MFMA operand layout: a lane holds 32
 //    consecutive K values of one row (16 bytes) and that block's E8M0 byte.
-//    A 256-wide K stage is four MFMA steps; in step s lane half h takes the
-//    32-column chunk 4h + s, so the lane's four scale bytes for the stage are one
-//    aligned dword and s is the byte select (op_sel) of the instruction.
+//    A 128-wide half stage is two MFMA steps; in step s lane half h takes the
+//    32-column chunk 2h + s, so the lane's two scale bytes are bytes 2h, 2h+1 of
+//    the row's scale dword for the half stage: shifted right by 16h they are
+//    bytes 0 and 1, and s is the byte select (op_sel) of the instruction.
 //    Both operands use the same K order, so the sum is unchanged.
-//  * Global -> LDS with GLOBAL_LOAD_LDS_DWORDX4 (16 B per lane, no VGPR staging),
-//    issued by every wave between its MFMAs of a stage's last K step,
-//    2 LDS slots of 68 KB: each copy brings whole 128-byte lines (8 rows x 128 B
-//    per wave instruction), which doubles the bytes per outstanding L1 miss
-//    compared with half-line copies. LDS rows are 128 B; chunk c of row r sits at
-//    slot c ^ ((r >> 1) & 7) so the 16 rows a quarter-wave reads hit distinct banks.
+//  * Global -> LDS with GLOBAL_LOAD_LDS_DWORDX4 (16 B per lane, no VGPR staging)
+//    over half stages of 128 K (64 code bytes per row), four LDS slots of 34 KB:
+//    half stages h+1 and h+2 are in flight while h is read, and the copies of
+//    h+3 go to the slot that h-1 left, spread over the MFMAs of both steps of h
+//    (a few per step, never a burst that would hold every wave at the memory
+//    issue port while the matrix core idles; measured: spreading the same copies
+//    over a stage takes L1 from 0.81 to 0.74 ms). LDS rows are 64 B; chunk c of
+//    row r sits at slot c ^ ((r >> 2) & 3) so the 16 rows a quarter-wave reads
+//    hit distinct banks.
 //  * Operand fragments are double-buffered in registers: the LDS reads of the
 //    next step are interleaved with the MFMAs of the current one.
 //  * blockIdx -> tile mapping is XCD aware: consecutive tiles (the m-tiles of one
 //    expert's weight n-tile) land on the same XCD and share its L2.
 #include <atomic>
+#include <type_traits>
 
 #include "gemm_common.h"
 
@@ -39,29 +44,30 @@ namespace mx {
 
 namespace {
 
-constexpr int ROW_BYTES = BK / 2;                     // 128 code bytes per row per stage
-constexpr int SC_BYTES = BK / 32;                     // 8 scale bytes per row per stage
-constexpr int W_BYTES = BN * ROW_BYTES;               // 32768
-constexpr int X_BYTES = BM * ROW_BYTES;               // 32768
-constexpr int WS_BYTES = BN * SC_BYTES;               // 2048
-constexpr int XS_BYTES = BM * SC_BYTES;               // 2048
+// The K loop runs over half stages of HK = 128 logical columns: 64 code bytes
+// and 4 scale bytes per row. NSLOT = 4 LDS slots hold half stages h, h+1, h+2
+// (arriving) and the one being read.
+constexpr int HK = BK / 2;                            // 128 logical columns per half stage
+constexpr int HROW = HK / 2;                          // 64 code bytes per row per half stage
+constexpr int HSC = HK / 32;                          // 4 scale bytes per row per half stage
+constexpr int NSLOT = 4;
+constexpr int W_BYTES = BN * HROW;                    // 16384
+constexpr int X_BYTES = BM * HROW;                    // 16384
+constexpr int WS_BYTES = BN * HSC;                    // 1024
+constexpr int XS_BYTES = BM * HSC;                    // 1024
 constexpr int OFF_X = W_BYTES;
 constexpr int OFF_WS = W_BYTES + X_BYTES;
 constexpr int OFF_XS = OFF_WS + WS_BYTES;
-constexpr int STAGE_BYTES = OFF_XS + XS_BYTES;        // 69632
-constexpr int SMEM_BYTES = NSTAGE * STAGE_BYTES;
+constexpr int SLOT_BYTES = OFF_XS + XS_BYTES;         // 34816
+constexpr int SMEM_BYTES = NSLOT * SLOT_BYTES;        // 139264
 constexpr int NWAVES = GEMM_THREADS / 64;             // 8: 2 along weight rows x 4 along tokens
-constexpr int W_DMA = W_BYTES / 1024 / NWAVES;        // 16-byte copies per wave per stage (W)
-constexpr int X_DMA = X_BYTES / 1024 / NWAVES;
-constexpr int VM_PER_STAGE = W_DMA + X_DMA + 2;       // + two dword copies of the scale tiles
-static_assert(VM_PER_STAGE == 10, "the vmcnt immediate below assumes 10 copies per stage");
-static_assert(NSTAGE == 2, "the pipeline below is written for 2 LDS slots");
-static_assert(WS_BYTES + XS_BYTES == GEMM_THREADS * 8, "two scale dwords per thread per stage");
+constexpr int W_DMA = W_BYTES / 1024 / NWAVES;        // 16-byte copies per wave per half stage (W): 2
+constexpr int X_DMA = X_BYTES / 1024 / NWAVES;        // 2
+constexpr int VM_PER_HALF = W_DMA + X_DMA + 1;        // + one dword copy of a scale tile (W: waves 0-3, X: 4-7)
+static_assert(VM_PER_HALF == 5, "the vmcnt immediates below assume 5 copies per half stage");
+static_assert(WS_BYTES + XS_BYTES == GEMM_THREADS * 4, "one scale dword per thread per half stage");
 static_assert(SMEM_BYTES >= TILE_LDS_TOTAL, "the bf16 epilogue stages its tile in the K-loop LDS");
-
-// Zero bytes for the upper half of a K stage when K % 256 == 128: zero codes with
-// zero scale bytes (2^-127) contribute exactly 0 to every sum.
-__device__ __attribute__((aligned(256))) uint8_t g_zero_page[256];
+static_assert(CODE_BLOCK_BYTES == W_BYTES, "a tile-major code block is the image of a W slot");
 
 // Global -> LDS copies. Lane i of the wave writes LDS bytes [m0 + i*size, +size).
 // They are issued as inline asm so that the compiler neither waits for them
@@ -96,11 +102,11 @@ struct NoCopy {
   __device__ __forceinline__ void operator()(int) const {}
 };
 
-// The eight MFMAs of K step S (chunk 4*hh + S, scale byte S) from `cur`,
-// interleaved with the six LDS reads that fill `nxt` for the next step (when
-// READ), so that the reads issue while the matrix core is busy. `copy(i)` runs
-// before MFMA i: the last step of a stage spreads the next slot's global -> LDS
-// copies over its MFMAs this way.
+// The eight MFMAs of K step S of a half stage (chunk 2*hh + S, scale byte S of
+// the lane's shifted scale dword) from `cur`, interleaved with the six LDS reads
+// that fill `nxt` for the next step (when READ), so that the reads issue while
+// the matrix core is busy. `copy(i)` runs before MFMA i: the global -> LDS
+// copies of a later half stage are spread over the MFMAs this way.
 template <int S, bool READ, class Copy>
 __device__ __forceinline__ void k_step(const Frags& cur, Frags& nxt, const uint8_t* sbn, int coffn,
                                        int wrow_off, int xrow_off, const uint32_t (&sa)[4],
@@ -119,8 +125,8 @@ __device__ __forceinline__ void k_step(const Frags& cur, Frags& nxt, const uint8
       if (READ && i < 6) {
         if (i == 0) nxt.A[0] = lds16(sbn + wrow_off + coffn);
         else if (i == 1) nxt.B[0] = lds16(sbn + xrow_off + coffn);
-        else if (i == 2) nxt.B[1] = lds16(sbn + xrow_off + 32 * ROW_BYTES + coffn);
-        else nxt.A[i - 2] = lds16(sbn + wrow_off + (i - 2) * 32 * ROW_BYTES + coffn);
+        else if (i == 2) nxt.B[1] = lds16(sbn + xrow_off + 32 * HROW + coffn);
+        else nxt.A[i - 2] = lds16(sbn + wrow_off + (i - 2) * 32 * HROW + coffn);
       }
     }
   }
@@ -169,7 +175,7 @@ __device__ __forceinline__ uint32_t l1_block(const GemmArgs& a, const Tile& t, c
       // t.mt, L2 stage j0/256, tile row ml, byte (j0/32) % 8
       const int64_t at = a.h_scales_packed
                              ? ((int64_t)t.mt * ((I + BK - 1) / BK) + (j0 >> 8)) * SC_TILE_STAGE_BYTES +
-                                   ml * SC_BYTES + ((j0 >> 5) & 7)
+                                   ml * SC_STAGE_BYTES + ((j0 >> 5) & 7)
                              : (int64_t)row * (I >> 5) + (j0 >> 5);
       a.h_scales[at] = (uint8_t)sbyte;
     }
@@ -258,10 +264,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
   const int kb = K >> 1;                    // code bytes per row
   const int ks = K >> 5;                    // scale bytes per row
   const int nst_all = (K + BK - 1) / BK;
-  // this tile's K stages [ks0, ks1): all of them, or one split's share
-  const int nst = t.ks1 - t.ks0;
-  const int kc0 = t.ks0 * ROW_BYTES;        // code byte offset of the first stage
-  const bool half_tail = (K % BK) != 0 && t.ks1 == nst_all;   // the last stage holds 128 columns only
+  // this tile's half stages: those of the 256-column stages [ks0, ks1) (all of
+  // them, or one split's share); K % 128 == 0, so every half stage is full
+  const int nh = min(2 * t.ks1, K / HK) - 2 * t.ks0;
+  const int kc0 = t.ks0 * 2 * HROW;         // code byte offset of the first half stage
   constexpr bool l1 = (EPI == EPI_SWIGLU_MXFP4 || EPI == EPI_SWIGLU_NVFP4 || EPI == EPI_PART_L1);
 
   const uint8_t* wa = a.wa + (int64_t)t.e * a.w_estride;
@@ -291,86 +297,87 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     return a.row_token ? a.row_token[r] : r;
   };
 
-  // Copy (wave, i) writes LDS bytes [(wave*W_DMA + i) * 1024, +1024): rows q*8 + lane/8,
-  // 16-byte slot lane%8 holding chunk (lane%8) ^ ((row >> 1) & 7).
+  // Copy (wave, i) writes LDS bytes [(wave*W_DMA + i) * 1024, +1024) of the W
+  // (or X) tile: 16 rows of 64 bytes, lane -> row (wave*W_DMA + i)*16 + lane/4,
+  // 16-byte slot lane%4 holding chunk (lane%4) ^ ((row >> 2) & 3). The 16 rows a
+  // quarter-wave reads then hit 16 distinct 16-byte bank groups.
+  // With the tile-major codes (pack.hip) the slot image of half stage h of this
+  // tile is one 16 KB block: copy (wave, i) reads its 1 KB of it in one piece.
   const uint8_t* wsrc[W_DMA];
-  bool whi[W_DMA];   // chunk in the upper half of the stage (columns 128..255)
+  int w_hstride;   // source bytes between consecutive half stages
+  if (a.w_cpk != nullptr) {
+    const uint8_t* tb = a.w_cpk + (int64_t)t.e * a.wcpk_estride +
+                        ((int64_t)t.nt * (K / HK) + 2 * t.ks0) * CODE_BLOCK_BYTES;
 #pragma unroll
-  for (int i = 0; i < W_DMA; ++i) {
-    const int R = (wave * W_DMA + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((R >> 1) & 7);
-    const uint8_t *base, *sbase;
-    const int row = w_row(R, base, sbase);
-    wsrc[i] = base + (int64_t)row * kb + kc0 + c * 16;
-    whi[i] = c >= 4;
+    for (int i = 0; i < W_DMA; ++i) wsrc[i] = tb + (wave * W_DMA + i) * 1024 + lane * 16;
+    w_hstride = CODE_BLOCK_BYTES;
+  } else {
+#pragma unroll
+    for (int i = 0; i < W_DMA; ++i) {
+      const int R = (wave * W_DMA + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((R >> 2) & 3);
+      const uint8_t *base, *sbase;
+      const int row = w_row(R, base, sbase);
+      wsrc[i] = base + (int64_t)row * kb + kc0 + c * 16;
+    }
+    w_hstride = HROW;
   }
   const uint8_t* xsrc[X_DMA];
-  bool xhi[X_DMA];
 #pragma unroll
   for (int i = 0; i < X_DMA; ++i) {
-    const int R = (wave * X_DMA + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((R >> 1) & 7);
+    const int R = (wave * X_DMA + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((R >> 2) & 3);
     xsrc[i] = a.x + (int64_t)x_token(R) * kb + kc0 + c * 16;
-    xhi[i] = c >= 4;
   }
-  // Scale tiles (8 bytes per row per stage): thread tid copies dword tid & 1 of
-  // weight row tid / 2 and of token row tid / 2, from the row-major scales
-  // (stage stride 8 bytes) or from a tile-major copy, where a stage of the
-  // tile is 2 KB in one piece (stage stride 2 KB).
-  const uint8_t *wssrc, *xssrc;
-  int wsc_stride = SC_BYTES, xsc_stride = SC_BYTES;
+  // Scale tiles (4 bytes per row per half stage): waves 0-3 copy the weight
+  // rows' dwords (row 64*wave + lane), waves 4-7 the token rows' (row
+  // 64*(wave-4) + lane), from the row-major scales (half stage h at byte 4h of
+  // the row) or from a tile-major copy, where a 256-column stage of the tile is
+  // 2 KB in one piece with 8 bytes per row (half stage h: piece h/2, dword h%2).
+  const bool scale_w = wave < 4;
+  const uint8_t* ssrc;
+  int piece_stride;   // bytes between the pieces of consecutive 256-column stages
   {
-    const int tid = wave * 64 + lane;
-    if (a.w_spk != nullptr) {
-      wssrc = a.w_spk + (int64_t)t.e * a.wspk_estride + ((int64_t)t.nt * nst_all + t.ks0) * SC_TILE_STAGE_BYTES +
-              tid * 4;
-      wsc_stride = SC_TILE_STAGE_BYTES;
-    } else {
-      const uint8_t *base, *sbase;
-      const int row = w_row(tid >> 1, base, sbase);
-      wssrc = sbase + (int64_t)row * ks + t.ks0 * SC_BYTES + (tid & 1) * 4;
-    }
-    if (a.x_s_packed) {
+    const int R = (wave & 3) * 64 + lane;
+    if (scale_w) {
+      if (a.w_spk != nullptr) {
+        ssrc = a.w_spk + (int64_t)t.e * a.wspk_estride + ((int64_t)t.nt * nst_all + t.ks0) * SC_TILE_STAGE_BYTES +
+               R * SC_STAGE_BYTES;
+        piece_stride = SC_TILE_STAGE_BYTES;
+      } else {
+        const uint8_t *base, *sbase;
+        const int row = w_row(R, base, sbase);
+        ssrc = sbase + (int64_t)row * ks + t.ks0 * SC_STAGE_BYTES;
+        piece_stride = SC_STAGE_BYTES;
+      }
+    } else if (a.x_s_packed) {
       // rows past the tile's end read the last valid row, as the code copies do
-      xssrc = a.x_s + ((int64_t)t.mt * nst_all + t.ks0) * SC_TILE_STAGE_BYTES + min(tid >> 1, t.rows - 1) * SC_BYTES +
-              (tid & 1) * 4;
-      xsc_stride = SC_TILE_STAGE_BYTES;
+      ssrc = a.x_s + ((int64_t)t.mt * nst_all + t.ks0) * SC_TILE_STAGE_BYTES + min(R, t.rows - 1) * SC_STAGE_BYTES;
+      piece_stride = SC_TILE_STAGE_BYTES;
     } else {
-      xssrc = a.x_s + (int64_t)x_token(tid >> 1) * ks + t.ks0 * SC_BYTES + (tid & 1) * 4;
+      ssrc = a.x_s + (int64_t)x_token(R) * ks + t.ks0 * SC_STAGE_BYTES;
+      piece_stride = SC_STAGE_BYTES;
     }
   }
-
   const uint32_t lds0 = lds_addr(smem);
-  // the zero page's address, taken once: referenced inside the K loop, the
-  // compiler reloads it there with a scalar load whose wait (lgkmcnt(0)) also
-  // drains the LDS reads in flight
-  const uint8_t* zpage = g_zero_page;
-  asm volatile("" : "+s"(zpage));
-  const bool shi = (lane & 1) != 0;   // scale dword of columns 128..255
-  // Copy c (0..9) of stage st: W_DMA weight copies, X_DMA token copies, then
-  // the two scale dwords.
-  auto copy_one = [&](int st, int c) {
-    const uint32_t sb = lds0 + (st % NSTAGE) * STAGE_BYTES;
-    const int ko = st * ROW_BYTES;
-    const bool tail = half_tail && st == nst - 1;
+  const uint32_t sc_lds = (scale_w ? OFF_WS : OFF_XS) + (wave & 3) * 256;
+  // Copy c (0..4) of half stage h into slot h % NSLOT: W_DMA weight copies,
+  // X_DMA token copies, then the scale dword.
+  auto copy_one = [&](int h, int c) {
+    const uint32_t sb = lds0 + (h % NSLOT) * SLOT_BYTES;
+    const int ko = h * HROW;
     if (c < W_DMA) {
-      lds_dma16((tail && whi[c]) ? (const void*)zpage : (const void*)(wsrc[c] + ko),
-                sb + (wave * W_DMA + c) * 1024);
+      lds_dma16(wsrc[c] + (int64_t)h * w_hstride, sb + (wave * W_DMA + c) * 1024);
     } else if (c < W_DMA + X_DMA) {
       const int i = c - W_DMA;
-      lds_dma16((tail && xhi[i]) ? (const void*)zpage : (const void*)(xsrc[i] + ko),
-                sb + OFF_X + (wave * X_DMA + i) * 1024);
-    } else if (c == W_DMA + X_DMA) {
-      lds_dma4((tail && shi) ? (const void*)zpage : (const void*)(wssrc + st * wsc_stride),
-               sb + OFF_WS + wave * 256);
+      lds_dma16(xsrc[i] + ko, sb + OFF_X + (wave * X_DMA + i) * 1024);
     } else {
-      lds_dma4((tail && shi) ? (const void*)zpage : (const void*)(xssrc + st * xsc_stride),
-               sb + OFF_XS + wave * 256);
+      lds_dma4(ssrc + (h >> 1) * piece_stride + (h & 1) * HSC, sb + sc_lds);
     }
   };
-  auto issue = [&](int st) {
+  auto issue = [&](int h) {
 #pragma unroll
-    for (int c = 0; c < VM_PER_STAGE; ++c) copy_one(st, c);
+    for (int c = 0; c < VM_PER_HALF; ++c) copy_one(h, c);
   };
 
   f32x16 acc[4][2];
@@ -381,41 +388,56 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[f][g][v] = 0.0f;
 
-  // per-lane LDS read offsets
+  // per-lane LDS read offsets: row r32 (+32 per block) of the lane's weight and
+  // token blocks; in step s lane half hh reads chunk 2*hh + s
   const int r32 = lane & 31, hh = lane >> 5;
-  const int swz = (r32 >> 1) & 7;
-  const int wrow_off = (wn * 128 + r32) * ROW_BYTES;
-  const int xrow_off = OFF_X + (wm * 64 + r32) * ROW_BYTES;
-  const int wsc_off = OFF_WS + (wn * 128 + r32) * SC_BYTES + hh * 4;
-  const int xsc_off = OFF_XS + (wm * 64 + r32) * SC_BYTES + hh * 4;
-  int coff[4];
+  const int swz = (r32 >> 2) & 3;
+  const int wrow_off = (wn * 128 + r32) * HROW;
+  const int xrow_off = OFF_X + (wm * 64 + r32) * HROW;
+  const int wsc_off = OFF_WS + (wn * 128 + r32) * HSC;
+  const int xsc_off = OFF_XS + (wm * 64 + r32) * HSC;
+  int coff[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) coff[q] = ((hh * 4 + q) ^ swz) * 16;
+  for (int s = 0; s < 2; ++s) coff[s] = ((hh * 2 + s) ^ swz) * 16;
 
-  // this lane's scale dwords of stage s
-  auto read_scales = [&](int s, uint32_t (&sa)[4], uint32_t (&sx)[2]) {
-    const uint8_t* rs = smem + (s % NSTAGE) * STAGE_BYTES;
+  // this lane's scale dwords of half stage h, shifted so that the bytes of its
+  // chunks 2*hh, 2*hh + 1 are bytes 0 and 1 (the MFMA's byte select is the step)
+  auto read_scales = [&](int h, uint32_t (&sa)[4], uint32_t (&sx)[2]) {
+    const uint8_t* rs = smem + (h % NSLOT) * SLOT_BYTES;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sa[f] = *(const uint32_t*)(rs + wsc_off + f * 32 * SC_BYTES);
+    for (int f = 0; f < 4; ++f) sa[f] = *(const uint32_t*)(rs + wsc_off + f * 32 * HSC) >> (16 * hh);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) sx[g] = *(const uint32_t*)(rs + xsc_off + g * 32 * SC_BYTES);
+    for (int g = 0; g < 2; ++g) sx[g] = *(const uint32_t*)(rs + xsc_off + g * 32 * HSC) >> (16 * hh);
   };
 
   // Output rows and gate weights of the bf16 epilogue, loaded now so that their
-  // latency hides behind the K loop (they complete before stage 0's copies,
-  // which the prologue waits for).
+  // latency hides behind the K loop (they complete before half stage 0's
+  // copies, which the prologue waits for).
   TileRows<2> rows;
   if constexpr (EPI == EPI_BF16) rows = load_tile_rows<2>(a, t, wm, lane);
 
-  // Prologue: stages 0 and 1 in flight; wait for stage 0 and read its first step.
+  // Prologue: half stages 0, 1, 2 in flight; wait for half stage 0.
   issue(0);
-  if (nst > 1) {
+  if (nh > 2) {
     issue(1);
+    issue(2);
     asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+  } else if (nh > 1) {
+    issue(1);
+    asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
+  // Half stage h, in every wave: step 0's MFMAs (reading step 1's fragments),
+  // then a wait for half stage h+1 (own copies: vmcnt; everyone's: the
+  // barrier), then step 1's MFMAs (reading half stage h+1's first fragments).
+  // Copies of half stage h+3 go to slot (h+3) % 4 = (h-1) % 4, whose last reads
+  // (step 0 of h-1) precede the barrier of h-1: three of them before MFMAs 0, 3
+  // and 6 of step 0, two before MFMAs 1 and 5 of step 1. At the barrier of h the
+  // copies allowed in flight are those of h+2 and the three of h+3: vmcnt(8);
+  // near the end, vmcnt(5) (no copies of h+3) and vmcnt(0).
+  // WAIT is that count: 8 (with copies), 5 or 0 (without).
   if (act) {
     Frags F0, F1;
     uint32_t sa[4], sx[2];
@@ -424,49 +446,62 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     // needs no longer wait than its back edge
     F0.A[0] = lds16(smem + wrow_off + coff[0]);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) F0.B[g] = lds16(smem + xrow_off + g * 32 * ROW_BYTES + coff[0]);
+    for (int g = 0; g < 2; ++g) F0.B[g] = lds16(smem + xrow_off + g * 32 * HROW + coff[0]);
 #pragma unroll
-    for (int f = 1; f < 4; ++f) F0.A[f] = lds16(smem + wrow_off + f * 32 * ROW_BYTES + coff[0]);
+    for (int f = 1; f < 4; ++f) F0.A[f] = lds16(smem + wrow_off + f * 32 * HROW + coff[0]);
 
-    // One K stage. Every read of slot st is issued by the end of step 2: retire
-    // them, wait for stage st+1 (the only copies in flight) and run the last
-    // step, whose MFMAs overlap `copy` (the refill of slot st with stage st+2)
-    // and the reads of stage st+1's first step. In the last stage those reads
-    // fetch bytes that are never used.
-    auto stage = [&](int st, const auto& copy) {
-      const uint8_t* sb = smem + (st % NSTAGE) * STAGE_BYTES;
-      k_step<0, true>(F0, F1, sb, coff[1], wrow_off, xrow_off, sa, sx, acc, NoCopy{});
-      k_step<1, true>(F1, F0, sb, coff[2], wrow_off, xrow_off, sa, sx, acc, NoCopy{});
-      k_step<2, true>(F0, F1, sb, coff[3], wrow_off, xrow_off, sa, sx, acc, NoCopy{});
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      const uint8_t* sbn = smem + ((st + 1) % NSTAGE) * STAGE_BYTES;
+    auto half = [&](int h, auto wait_tag) {
+      constexpr int WAIT = decltype(wait_tag)::value;
+      const uint8_t* sb = smem + (h % NSLOT) * SLOT_BYTES;
+      k_step<0, true>(F0, F1, sb, coff[1], wrow_off, xrow_off, sa, sx, acc, [&](int i) {
+        if constexpr (WAIT == 8) {
+          if (i == 0) copy_one(h + 3, 0);
+          else if (i == 3) copy_one(h + 3, 1);
+          else if (i == 6) copy_one(h + 3, 2);
+        }
+      });
+      if constexpr (WAIT == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if constexpr (WAIT == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const uint8_t* sbn = smem + ((h + 1) % NSLOT) * SLOT_BYTES;
       uint32_t san[4], sxn[2];
-      read_scales(st + 1, san, sxn);
-      k_step<3, true>(F1, F0, sbn, coff[0], wrow_off, xrow_off, sa, sx, acc, copy);
+      read_scales(h + 1, san, sxn);
+      k_step<1, true>(F1, F0, sbn, coff[0], wrow_off, xrow_off, sa, sx, acc, [&](int i) {
+        if constexpr (WAIT == 8) {
+          if (i == 1) copy_one(h + 3, 3);
+          else if (i == 5) copy_one(h + 3, 4);
+        }
+      });
 #pragma unroll
       for (int q = 0; q < 4; ++q) sa[q] = san[q];
       sx[0] = sxn[0];
       sx[1] = sxn[1];
     };
-    // Two loops rather than a branch per stage: with a branch the compiler hoists
-    // the last step's MFMAs (identical on both sides) above the barrier, and the
-    // copies and reads after it no longer overlap any matrix work.
-    int st = 0;
-    for (; st + 2 < nst; ++st) {
-      const int nx = st + 2;
-      stage(st, [&](int i) {   // copies 2i and 2i+1 of stage st+2 before MFMA i
-        if (2 * i < VM_PER_STAGE) copy_one(nx, 2 * i);
-        if (2 * i + 1 < VM_PER_STAGE) copy_one(nx, 2 * i + 1);
-      });
-    }
-    for (; st < nst; ++st) stage(st, NoCopy{});
+    // Separate loops rather than a branch per half stage: with a branch the
+    // compiler hoists MFMAs that are identical on both sides above the barrier,
+    // and the copies and reads after it no longer overlap any matrix work. In the
+    // last half stage the reads of the "next" slot fetch bytes never used.
+    int h = 0;
+    for (; h + 3 < nh; ++h) half(h, std::integral_constant<int, 8>{});
+    if (h + 2 < nh) half(h++, std::integral_constant<int, 5>{});
+    for (; h < nh; ++h) half(h, std::integral_constant<int, 0>{});
   } else {
-    // the same copies and barriers as `stage`, without MFMAs (accumulators stay
-    // zero): one barrier per stage, so that every wave meets the same barriers
-    for (int st = 0; st < nst; ++st) {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (st + 2 < nst) issue(st + 2);
+    // the same copies and barriers as `half`, without MFMAs (accumulators stay
+    // zero): every wave meets the same barriers
+    int h = 0;
+    for (; h + 3 < nh; ++h) {
+      copy_one(h + 3, 0);
+      copy_one(h + 3, 1);
+      copy_one(h + 3, 2);
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      copy_one(h + 3, 3);
+      copy_one(h + 3, 4);
     }
+    if (h + 2 < nh) {
+      asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      ++h;
+    }
+    for (; h < nh; ++h) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   // ---------------------------------------------------------------- epilogues

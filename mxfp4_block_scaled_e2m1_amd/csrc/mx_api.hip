@@ -221,6 +221,17 @@ PackedWeights packed_weights(int64_t H, int64_t I, int64_t E) {
   return p;
 }
 
+// The tile-major weight codes written by mx_pack_weight_codes, laid out as the
+// scales: each expert's L1 blocks, then (after all experts) the L2 blocks.
+PackedWeights packed_codes_layout(int64_t H, int64_t I, int64_t E) {
+  PackedWeights p;
+  p.l1_estride = packed_code_bytes((I + L1_J_PER_TILE - 1) / L1_J_PER_TILE, H);
+  p.l2_estride = packed_code_bytes((H + BN - 1) / BN, I);
+  p.l1_bytes = E * p.l1_estride;
+  p.bytes = p.l1_bytes + E * p.l2_estride;
+  return p;
+}
+
 // ---------------------------------------------------------------- checks
 mx_status check_mlp_dims(int64_t M, int64_t H, int64_t I) {
   if (M < 0) return fail(MX_ERR_SHAPE, "token count %lld is negative", (long long)M);
@@ -462,10 +473,40 @@ mx_status mx_pack_weight_scales(const uint8_t* w1_s, const uint8_t* w3_s, const 
   return ok();
 }
 
+mx_status mx_pack_weight_codes(const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, int64_t hidden,
+                               int64_t inter, int32_t E, uint8_t* packed, size_t packed_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  MX_TRY(check_mlp_dims(0, hidden, inter));
+  if (E < 1 || E > ROUTE_MAX_EXPERTS) return fail(MX_ERR_SHAPE, "E %d outside [1, %d]", E, ROUTE_MAX_EXPERTS);
+  MX_REQUIRE_PTR(w1);
+  MX_REQUIRE_PTR(w3);
+  MX_REQUIRE_PTR(w2);
+  MX_REQUIRE_PTR(packed);
+  MX_REQUIRE_ALIGN(w1, 16);
+  MX_REQUIRE_ALIGN(w3, 16);
+  MX_REQUIRE_ALIGN(w2, 16);
+  MX_REQUIRE_ALIGN(packed, 256);
+  const PackedWeights pc = packed_codes_layout(hidden, inter, E);
+  if (packed_bytes < (size_t)pc.bytes)
+    return fail(MX_ERR_WORKSPACE, "packed buffer %zu bytes < required %lld", packed_bytes, (long long)pc.bytes);
+  MX_HIP(phase("pack_w_codes", s, [&] {
+           hipError_t e = launch_pack_weight_codes(w1, w3, E, (int)inter, (int)hidden, packed, s);
+           if (e != hipSuccess) return e;
+           return launch_pack_weight_codes(w2, nullptr, E, (int)hidden, (int)inter, packed + pc.l1_bytes, s);
+         }), "pack_w_codes");
+  return ok();
+}
+
+size_t mx_packed_weight_codes_size(int64_t hidden, int64_t inter, int32_t E) {
+  if (hidden < 128 || inter < 128 || hidden % 128 != 0 || inter % 128 != 0 || E < 1 || E > ROUTE_MAX_EXPERTS) return 0;
+  return (size_t)packed_codes_layout(hidden, inter, E).bytes;
+}
+
 mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, const uint8_t* w1,
                         const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s, const uint8_t* w2,
-                        const uint8_t* w2_s, const uint8_t* packed_scales, mx_format requant,
-                        const float* requant_global, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+                        const uint8_t* w2_s, const uint8_t* packed_scales, const uint8_t* packed_codes,
+                        mx_format requant, const float* requant_global, uint16_t* y, void* workspace,
+                        size_t ws_bytes, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   MX_TRY(check_mlp_dims(M, hidden, inter));
   MX_TRY(check_requant(requant, requant_global));
@@ -476,6 +517,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   MX_REQUIRE_ALIGN(y, 16);
   MX_TRY(check_weights(w1, w1_s, w3, w3_s, w2, w2_s));
   MX_REQUIRE_ALIGN(packed_scales, 256);
+  MX_REQUIRE_ALIGN(packed_codes, 256);
   const size_t need = mx_expert_mlp_workspace_size(M, hidden, inter, requant);
   MX_REQUIRE_PTR(workspace);
   MX_REQUIRE_ALIGN(workspace, 256);
@@ -502,6 +544,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
 
   const int mtiles = (m + BM - 1) / BM;
   const PackedWeights pw = packed_weights(hidden, inter, 1);
+  const PackedWeights pc = packed_codes_layout(hidden, inter, 1);
   MX_HIP(phase("quant_x", s, [&] {
            hipError_t e = launch_quant_mxfp4(x, M, hidden, w.xq, w.xs, s);
            if (e != hipSuccess) return e;
@@ -511,6 +554,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   GemmArgs l1 = base_args();
   l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
   l1.w_spk = packed_scales; l1.wspk_estride = pw.l1_estride;
+  l1.w_cpk = packed_codes; l1.wcpk_estride = pc.l1_estride;
   l1.n_rows = I; l1.k = H;
   l1.x = w.xq; l1.x_s = w.xs_pk; l1.x_s_packed = 1;
   l1.m_rows = m; l1.n_experts = 1;
@@ -536,6 +580,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   GemmArgs l2 = base_args();
   l2.wa = w2; l2.wa_s = w2_s;
   l2.w_spk = packed_scales ? packed_scales + pw.l1_bytes : nullptr; l2.wspk_estride = pw.l2_estride;
+  l2.w_cpk = packed_codes ? packed_codes + pc.l1_bytes : nullptr; l2.wcpk_estride = pc.l2_estride;
   l2.n_rows = H; l2.k = I;
   l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4;
   l2.m_rows = m; l2.n_experts = 1;
@@ -555,8 +600,8 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
                                 const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                 const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
                                 const uint8_t* w2, const uint8_t* w2_s, const uint8_t* packed_scales,
-                                mx_format requant, const float* requant_global, uint16_t* y, void* workspace,
-                                size_t ws_bytes, void* stream) {
+                                const uint8_t* packed_codes, mx_format requant, const float* requant_global,
+                                uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   MX_TRY(check_mlp_dims(T, hidden, inter));
   MX_TRY(check_requant(requant, requant_global));
@@ -574,6 +619,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   MX_REQUIRE_ALIGN(topk_w, 4);
   MX_TRY(check_weights(w1, w1_s, w3, w3_s, w2, w2_s));
   MX_REQUIRE_ALIGN(packed_scales, 256);
+  MX_REQUIRE_ALIGN(packed_codes, 256);
   const size_t need = mx_grouped_expert_mlp_workspace_size(T, hidden, inter, k, E, requant);
   MX_REQUIRE_PTR(workspace);
   MX_REQUIRE_ALIGN(workspace, 256);
@@ -584,6 +630,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   const int64_t P = T * k;
   const int max_mtiles = (int)max_route_mtiles(P, E);
   const PackedWeights pw = packed_weights(hidden, inter, E);
+  const PackedWeights pc = packed_codes_layout(hidden, inter, E);
 
   MX_HIP(phase("quant_x", s, [&] { return launch_quant_mxfp4(x, T, hidden, w.xq, w.xs, s); }), "quant_x");
   if (w.stream) {
@@ -618,6 +665,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
   l1.w_estride = (int64_t)I * H / 2; l1.ws_estride = (int64_t)I * H / 32;
   l1.w_spk = packed_scales; l1.wspk_estride = pw.l1_estride;
+  l1.w_cpk = packed_codes; l1.wcpk_estride = pc.l1_estride;
   l1.n_rows = I; l1.k = H;
   l1.x = w.xq; l1.x_s = w.xs_pk; l1.x_s_packed = 1; l1.row_token = w.rb.row_token;
   l1.expert_off = w.rb.expert_off; l1.tile_base = w.rb.tile_base; l1.n_experts = E;
@@ -631,6 +679,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l2.wa = w2; l2.wa_s = w2_s;
   l2.w_estride = (int64_t)H * I / 2; l2.ws_estride = (int64_t)H * I / 32;
   l2.w_spk = packed_scales ? packed_scales + pw.l1_bytes : nullptr; l2.wspk_estride = pw.l2_estride;
+  l2.w_cpk = packed_codes ? packed_codes + pc.l1_bytes : nullptr; l2.wcpk_estride = pc.l2_estride;
   l2.n_rows = H; l2.k = I;
   l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4;
   l2.expert_off = w.rb.expert_off; l2.tile_base = w.rb.tile_base; l2.n_experts = E;
@@ -1184,8 +1233,8 @@ size_t mx_expert_mlp_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
 
 mx_status mx_expert_mlp_noalloc(const uint16_t* x, int64_t M, int64_t hidden, int64_t inter, const uint8_t* w1,
                                 const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s, const uint8_t* w2,
-                                const uint8_t* w2_s, const uint8_t* packed_scales, mx_format requant,
-                                const float* requant_global, uint16_t* y, void* stream) {
+                                const uint8_t* w2_s, const uint8_t* packed_scales, const uint8_t* packed_codes,
+                                mx_format requant, const float* requant_global, uint16_t* y, void* stream) {
   MX_TRY(check_mlp_dims(M, hidden, inter));
   MX_TRY(check_requant(requant, requant_global));
   if (M == 0) return ok();
@@ -1197,8 +1246,8 @@ mx_status mx_expert_mlp_noalloc(const uint16_t* x, int64_t M, int64_t hidden, in
                 (long long)M, (long long)hidden, (long long)inter, need, NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
   MX_TRY(scratch_ptr(&ws));
-  return mx_expert_mlp(x, M, hidden, inter, w1, w1_s, w3, w3_s, w2, w2_s, packed_scales, requant, requant_global, y,
-                       ws, NOALLOC_SCRATCH_BYTES, stream);
+  return mx_expert_mlp(x, M, hidden, inter, w1, w1_s, w3, w3_s, w2, w2_s, packed_scales, packed_codes, requant,
+                       requant_global, y, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"
@@ -1236,8 +1285,8 @@ mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidden, int
                                const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t E,
                                const uint8_t* w1, const uint8_t* w1_s, const uint8_t* w3, const uint8_t* w3_s,
                                const uint8_t* w2, const uint8_t* w2_s, const uint8_t* packed_scales,
-                               mx_format requant, const float* requant_global, uint16_t* y,
-                               mx_moe_runner** out) {
+                               const uint8_t* packed_codes, mx_format requant, const float* requant_global,
+                               uint16_t* y, mx_moe_runner** out) {
   MX_REQUIRE_PTR(out);
   *out = nullptr;
   if (T < 1) return fail(MX_ERR_SHAPE, "runner token count %lld must be positive", (long long)T);
@@ -1269,7 +1318,8 @@ mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidden, int
   // one eager call first: it validates every argument (nothing is captured if
   // it fails) and leaves y valid
   mx_status st = mx_grouped_expert_mlp(x, T, hidden, inter, topk_ids, topk_w, k, E, w1, w1_s, w3, w3_s, w2, w2_s,
-                                       packed_scales, requant, requant_global, y, r->workspace, bytes, r->capture);
+                                       packed_scales, packed_codes, requant, requant_global, y, r->workspace, bytes,
+                                       r->capture);
   if (st != MX_OK) {
     runner_release(r);
     return st;
@@ -1281,7 +1331,7 @@ mx_status mx_moe_runner_create(const uint16_t* x, int64_t T, int64_t hidden, int
     return hip_fail(e, "runner capture");
   }
   st = mx_grouped_expert_mlp(x, T, hidden, inter, topk_ids, topk_w, k, E, w1, w1_s, w3, w3_s, w2, w2_s,
-                             packed_scales, requant, requant_global, y, r->workspace, bytes, r->capture);
+                             packed_scales, packed_codes, requant, requant_global, y, r->workspace, bytes, r->capture);
   e = hipStreamEndCapture(r->capture, &r->graph);
   if (st != MX_OK) {
     runner_release(r);

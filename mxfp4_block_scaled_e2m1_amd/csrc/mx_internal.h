@@ -23,6 +23,10 @@ constexpr int SC_STAGE_BYTES = BK / 32;                           // 8
 constexpr int SC_TILE_STAGE_BYTES = 256 * SC_STAGE_BYTES;         // 2048
 // Bytes of the tile-major layout of `tiles` tiles over K.
 constexpr int64_t packed_scale_bytes(int64_t tiles, int64_t k) { return tiles * ((k + BK - 1) / BK) * SC_TILE_STAGE_BYTES; }
+// Tile-major weight codes: one block per 256-row weight tile and 128-wide half
+// stage of K, the tile's 256 rows x 64 code bytes (16 KB).
+constexpr int CODE_BLOCK_BYTES = 256 * 64;
+constexpr int64_t packed_code_bytes(int64_t tiles, int64_t k) { return tiles * (k / 128) * CODE_BLOCK_BYTES; }
 
 // Epilogue kinds of the scaled-MFMA GEMM.
 enum Epilogue : int {
@@ -50,6 +54,11 @@ struct GemmArgs {
   // GEMM reads it instead of wa_s/wb_s. Expert e starts at w_spk + e * wspk_estride.
   const uint8_t* w_spk;
   int64_t wspk_estride;
+  // Optional tile-major copy of the weight codes (pack.hip): when set, the FP4
+  // GEMM copies each half stage of its weight tile as one contiguous block laid
+  // out as its LDS slot. Expert e starts at w_cpk + e * wcpk_estride.
+  const uint8_t* w_cpk;
+  int64_t wcpk_estride;
   int n_rows;           // logical weight rows per matrix (inter for L1, hidden for L2)
   int k;                // logical K (multiple of 128)
 
@@ -107,6 +116,10 @@ hipError_t launch_pack_weight_scales(const uint8_t* a_s, const uint8_t* b_s, int
                                      uint8_t* out, hipStream_t s);
 // Activations: the m-tiles of a routed (expert_off set, tokens via row_token)
 // or dense (m_rows rows) launch; out holds max_mtiles * stages * 2048 bytes.
+// Tile-major weight codes (pack_weight_codes): L1 when b != null (gate rows in a,
+// up rows in b, the GEMM's interleaved L1 tile rows), else L2; k % 128 == 0.
+hipError_t launch_pack_weight_codes(const uint8_t* a, const uint8_t* b, int n_experts, int n_rows, int k,
+                                    uint8_t* out, hipStream_t s);
 hipError_t launch_pack_act_scales(const uint8_t* x_s, int k, const int32_t* row_token, const int32_t* expert_off,
                                   const int32_t* tile_base, int n_experts, int m_rows, int max_mtiles,
                                   uint8_t* out, hipStream_t s);

@@ -1,4 +1,4 @@
-// Tile-major copies of E8M0 scale matrices for the FP4 GEMM.
+// Tile-major copies of E8M0 scale matrices and FP4 weight codes for the FP4 GEMM.
 //
 // The GEMM copies, per 256-wide K stage, 8 scale bytes of each of the 256
 // weight rows and 256 token rows of its tile into LDS. In the row-major layout
@@ -9,7 +9,11 @@
 //
 //   packed[tile][stage][r][8]: bytes 8*stage .. 8*stage+7 of row(tile, r)
 //
-// with zero bytes past the end of a row (K % 256 == 128). The weight layout is
+// with zero bytes past the end of a row (K % 256 == 128). The weight codes have
+// a tile-major copy too (k_pack_weight_codes): per tile and 128-wide half stage,
+// the 16 KB the GEMM's LDS slot holds, in that slot's byte order, so that each
+// 16-byte copy lane reads consecutive bytes and a wave's copy is 1 KB in one
+// piece (whole cache lines). The weight layouts are
 // built once after the weights are loaded (the pages' runner prepares its
 // weights once at start-up: page "Current Bug: vLLM produces empty/garbage
 // output", section "Revised Plan", Phase 1); the activation layout is built
@@ -115,6 +119,47 @@ hipError_t launch_pack_weight_scales(const uint8_t* a_s, const uint8_t* b_s, int
   if (n_experts <= 0 || ntiles <= 0) return hipSuccess;
   dim3 grid(ntiles * nst, n_experts);
   k_pack_weight_scales<<<grid, 256, 0, s>>>(a_s, b_s, l1, n_rows, ks, ntiles, nst, (int64_t)n_rows * ks, out);
+  return hipGetLastError();
+}
+
+// Weight codes: block (tile, half stage h), expert blockIdx.y; thread R = tile
+// row, the GEMM's row order (L1: gate and up rows interleaved as for the
+// scales; rows past n_rows repeat the last row). The block is the LDS image of
+// the half stage: row R at R * 64, its 16-byte chunk c (32 K values) at slot
+// c ^ ((R >> 2) & 3), the swizzle the GEMM reads with.
+__global__ __launch_bounds__(256) void k_pack_weight_codes(const uint8_t* __restrict__ a,
+                                                           const uint8_t* __restrict__ b, int l1, int n_rows,
+                                                           int kb, int ntiles, int nh, int64_t src_estride,
+                                                           uint8_t* __restrict__ out) {
+  const int nt = blockIdx.x / nh, h = blockIdx.x - nt * nh, e = blockIdx.y, R = threadIdx.x;
+  const uint8_t* src;
+  int row;
+  if (l1) {
+    const int f = (R >> 5) & 3;
+    row = nt * L1_J_PER_TILE + (R >> 7) * 64 + (f & 1) * 32 + (R & 31);
+    src = f < 2 ? a : b;
+  } else {
+    row = nt * BN + R;
+    src = a;
+  }
+  row = min(row, n_rows - 1);
+  const uint4* p = (const uint4*)(src + (int64_t)e * src_estride + (int64_t)row * kb + h * 64);
+  uint4 v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = p[c];
+  uint8_t* dst = out + (((int64_t)e * ntiles + nt) * nh + h) * CODE_BLOCK_BYTES + R * 64;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) *(uint4*)(dst + ((c ^ ((R >> 2) & 3)) * 16)) = v[c];
+}
+
+hipError_t launch_pack_weight_codes(const uint8_t* a, const uint8_t* b, int n_experts, int n_rows, int k,
+                                    uint8_t* out, hipStream_t s) {
+  const int l1 = b != nullptr;
+  const int ntiles = l1 ? (n_rows + L1_J_PER_TILE - 1) / L1_J_PER_TILE : (n_rows + BN - 1) / BN;
+  const int nh = k / 128, kb = k / 2;
+  if (n_experts <= 0 || ntiles <= 0 || nh <= 0) return hipSuccess;
+  dim3 grid(ntiles * nh, n_experts);
+  k_pack_weight_codes<<<grid, 256, 0, s>>>(a, b, l1, n_rows, kb, ntiles, nh, (int64_t)n_rows * kb, out);
   return hipGetLastError();
 }
 

@@ -146,6 +146,36 @@ def _align256(n):
     return (n + 255) // 256 * 256
 
 
+def pack_weight_codes_ref(w1, w3, w2):
+    """Expected output of mx_pack_weight_codes (layout only: byte moves) for
+    stacked codes w1/w3 [E, I, H/2], w2 [E, H, I/2]: per expert, tile and
+    128-wide half stage, 256 rows x 64 bytes, row R at R*64 with its 16-byte
+    chunk c at (c ^ ((R >> 2) & 3)) * 16; L1 tiles interleave gate and up rows
+    as the scale layout does; rows past the end repeat the last row."""
+    E, I, hb = w1.shape
+    H = 2 * hb
+
+    def blocks(rows_of, mats, nrows, kb, ntiles):
+        nh = kb // 64
+        out = np.zeros((E, ntiles, nh, 256, 4, 16), np.uint8)
+        for nt in range(ntiles):
+            for r in range(256):
+                mat, row = rows_of(nt, r)
+                row = min(row, nrows - 1)
+                src = mats[mat][:, row].reshape(E, nh, 4, 16)
+                for c in range(4):
+                    out[:, nt, :, r, c ^ ((r >> 2) & 3)] = src[:, :, c]
+        return out.reshape(E, -1)
+
+    def l1_rows(nt, r):
+        f = (r >> 5) & 3
+        return (0 if f < 2 else 1), nt * 128 + (r >> 7) * 64 + (f & 1) * 32 + (r & 31)
+
+    l1 = blocks(l1_rows, (w1, w3), I, hb, (I + 127) // 128)
+    l2 = blocks(lambda nt, r: (0, nt * 256 + r), (w2,), H, I // 2, (H + 255) // 256)
+    return np.concatenate([l1.ravel(), l2.ravel()])
+
+
 def routed_ws_slices(ws, T, H, I, k, E, requant="mxfp4"):
     """The routed GEMM-path workspace of mx_grouped_expert_mlp (each region
     256-byte aligned): xq, xs, block counts, expert offsets, tile bases,

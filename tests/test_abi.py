@@ -74,25 +74,27 @@ def test_mlp_validation(L):
     P = ctypes.c_void_p
     z = [P(256)] * 6
     # hidden not a multiple of 128
-    assert L.mx_expert_mlp(P(256), 4, 200, 128, *z, None, 0, None, P(256), P(256), 1 << 30, None) == 2
-    assert L.mx_expert_mlp(P(256), 4, 256, 96, *z, None, 0, None, P(256), P(256), 1 << 30, None) == 2
+    assert L.mx_expert_mlp(P(256), 4, 200, 128, *z, None, None, 0, None, P(256), P(256), 1 << 30, None) == 2
+    assert L.mx_expert_mlp(P(256), 4, 256, 96, *z, None, None, 0, None, P(256), P(256), 1 << 30, None) == 2
     # NVFP4 re-quant needs its global scale (a device pointer); FP8 is not a re-quant format
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 2, None, P(256), P(256), 1 << 30, None) == 1
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 2, P(257), P(256), P(256), 1 << 30, None) == 3
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 1, None, P(256), P(256), 1 << 30, None) == 4
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, None, 2, None, P(256), P(256), 1 << 30, None) == 1
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, None, 2, P(257), P(256), P(256), 1 << 30, None) == 3
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, None, 1, None, P(256), P(256), 1 << 30, None) == 4
     # NVFP4 keeps one E4M3 byte per 16 columns of h: a larger workspace than MXFP4
     assert L.mx_expert_mlp_workspace_size(4096, 7168, 3072, 2) > L.mx_expert_mlp_workspace_size(4096, 7168, 3072, 0)
     # workspace too small
     need = L.mx_expert_mlp_workspace_size(4, 256, 128, 0)
     assert need > 0
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 0, None, P(256), P(256), need - 1, None) == 5
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, None, 0, None, P(256), P(256), need - 1, None) == 5
     # misaligned workspace, null weights
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, 0, None, P(256), P(128), need, None) == 3
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, None, *z[1:], None, 0, None, P(256), P(256), need, None) == 1
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, None, 0, None, P(256), P(128), need, None) == 3
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, None, *z[1:], None, None, 0, None, P(256), P(256), need, None) == 1
     # zero tokens is a no-op
-    assert L.mx_expert_mlp(None, 0, 256, 128, *([None] * 7), 0, None, None, None, 0, None) == 0
-    # packed weight scales must be 256-byte aligned (NULL selects the row-major scales)
-    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, P(128), 0, None, P(256), P(256), need, None) == 3
+    assert L.mx_expert_mlp(None, 0, 256, 128, *([None] * 8), 0, None, None, None, 0, None) == 0
+    # packed weight scales and codes must be 256-byte aligned (NULL selects the row-major ones)
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, P(128), None, 0, None, P(256), P(256), need, None) == 3
+    assert L.mx_expert_mlp(P(256), 4, 256, 128, *z, None, P(128), 0, None, P(256), P(256), need, None) == 3
+    assert "packed_codes" in _err(L)
 
 
 def test_pack_weight_scales_validation(L):
@@ -108,16 +110,32 @@ def test_pack_weight_scales_validation(L):
     assert L.mx_pack_weight_scales(P(256), P(256), P(256), 256, 128, 4, P(256), need - 1, None) == 5
 
 
+def test_pack_weight_codes_validation(L):
+    P = ctypes.c_void_p
+    need = L.mx_packed_weight_codes_size(256, 128, 4)
+    # per expert: L1 one tile of 128 j x 2 half stages, L2 one tile of 256 rows x 1 half stage, 16 KB each
+    assert need == 4 * (2 + 1) * 16384
+    # the headline's 48 experts: as large as the code tensors (whole tiles)
+    assert L.mx_packed_weight_codes_size(7168, 3072, 48) == 48 * (24 * 56 + 28 * 24) * 16384 == 48 * 3 * 3072 * 3584
+    assert L.mx_packed_weight_codes_size(200, 128, 4) == 0
+    assert L.mx_pack_weight_codes(P(256), P(256), P(256), 200, 128, 4, P(256), need, None) == 2
+    assert L.mx_pack_weight_codes(P(256), P(256), P(256), 256, 128, 0, P(256), need, None) == 2
+    assert L.mx_pack_weight_codes(None, P(256), P(256), 256, 128, 4, P(256), need, None) == 1
+    assert L.mx_pack_weight_codes(P(264), P(256), P(256), 256, 128, 4, P(256), need, None) == 3
+    assert L.mx_pack_weight_codes(P(256), P(256), P(256), 256, 128, 4, P(128), need, None) == 3
+    assert L.mx_pack_weight_codes(P(256), P(256), P(256), 256, 128, 4, P(256), need - 1, None) == 5
+
+
 def test_grouped_validation(L):
     P = ctypes.c_void_p
     z = [P(256)] * 6
-    args = lambda k, E, ws: (P(256), 8, 256, 128, P(256), P(256), k, E, *z, None, 0, None, P(256), P(256), ws, None)
+    args = lambda k, E, ws: (P(256), 8, 256, 128, P(256), P(256), k, E, *z, None, None, 0, None, P(256), P(256), ws, None)
     assert L.mx_grouped_expert_mlp(*args(0, 4, 1 << 30)) == 2
     assert L.mx_grouped_expert_mlp(*args(5, 4, 1 << 30)) == 2
     assert L.mx_grouped_expert_mlp(*args(2, 2000, 1 << 30)) == 2
     need = L.mx_grouped_expert_mlp_workspace_size(8, 256, 128, 2, 4, 0)
     assert L.mx_grouped_expert_mlp(*args(2, 4, need - 1)) == 5
-    nv = lambda g: (P(256), 8, 256, 128, P(256), P(256), 2, 4, *z, None, 2, g, P(256), P(256), 1 << 30, None)
+    nv = lambda g: (P(256), 8, 256, 128, P(256), P(256), 2, 4, *z, None, None, 2, g, P(256), P(256), 1 << 30, None)
     assert L.mx_grouped_expert_mlp(*nv(None)) == 1                  # NVFP4 without its global
     assert L.mx_grouped_expert_mlp(*nv(P(258))) == 3
     # workspace grows with tokens and with k
@@ -184,7 +202,7 @@ def test_runner_validation(L):
     out = P()
 
     def create(T, k, E, x=P(256), o=True):
-        return L.mx_moe_runner_create(x, T, 256, 128, P(256), P(256), k, E, *z, None, 0, None, P(256),
+        return L.mx_moe_runner_create(x, T, 256, 128, P(256), P(256), k, E, *z, None, None, 0, None, P(256),
                                       ctypes.byref(out) if o else None)
     assert create(8, 2, 4, o=False) == 1
     assert create(0, 2, 4) == 2 and out.value is None
@@ -267,13 +285,13 @@ def test_noalloc_validation(L):
     z = [P(256)] * 6
     limit = L.mx_expert_mlp_noalloc_max_bytes()
     assert limit == 64 << 20
-    assert L.mx_expert_mlp_noalloc(P(256), 4, 200, 128, *z, None, 0, None, P(256), None) == 2
-    assert L.mx_expert_mlp_noalloc(P(256), 4, 256, 128, *z, None, 2, None, P(256), None) == 1
-    assert L.mx_expert_mlp_noalloc(None, 0, 256, 128, *([None] * 7), 0, None, None, None) == 0
+    assert L.mx_expert_mlp_noalloc(P(256), 4, 200, 128, *z, None, None, 0, None, P(256), None) == 2
+    assert L.mx_expert_mlp_noalloc(P(256), 4, 256, 128, *z, None, None, 2, None, P(256), None) == 1
+    assert L.mx_expert_mlp_noalloc(None, 0, 256, 128, *([None] * 8), 0, None, None, None) == 0
     big = 1
     while L.mx_expert_mlp_workspace_size(big, 7168, 3072, 0) <= limit:
         big *= 2
-    assert L.mx_expert_mlp_noalloc(P(256), big, 7168, 3072, *z, None, 0, None, P(256), None) == 5
+    assert L.mx_expert_mlp_noalloc(P(256), big, 7168, 3072, *z, None, None, 0, None, P(256), None) == 5
     assert "no-allocation" in _err(L)
 
 

@@ -36,9 +36,10 @@ def _routed(mx, d, requant="mxfp4", g=None, packed=True):
     E, I = d["w1"].shape[0], d["w1"].shape[1]
     wd = [t(d[n]) for n in WN]
     pk = mx.pack_weight_scales(wd[1], wd[3], wd[5]) if packed else None
+    pc = mx.pack_weight_codes(wd[0], wd[2], wd[4]) if packed else None
     ws = torch.empty(mx.grouped_expert_mlp_workspace_size(T, H, I, k, E, requant), dtype=torch.uint8, device="cuda")
     y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]), *wd, requant=requant, requant_global=g,
-                              workspace=ws, packed_scales=pk)
+                              workspace=ws, packed_scales=pk, packed_codes=pc)
     torch.cuda.synchronize()
     return bits(y), routed_ws_slices(ws, T, H, I, k, E, requant)
 
@@ -98,7 +99,8 @@ def test_shared_expert_prefill_every_row(mx):
     d = W.shared_expert(M, seed=0)
     wd = [t(d[n]) for n in WN]
     pk = mx.pack_weight_scales(wd[1], wd[3], wd[5])
-    y = bits(mx.expert_mlp(bf16_t(d["x"]), *wd, packed_scales=pk))
+    pc = mx.pack_weight_codes(wd[0], wd[2], wd[4])
+    y = bits(mx.expert_mlp(bf16_t(d["x"]), *wd, packed_scales=pk, packed_codes=pc))
     ref = O.expert_mlp(d["x"], *(d[n] for n in WN))
     assert_mlp_close(y, ref)
 

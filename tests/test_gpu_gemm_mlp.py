@@ -6,7 +6,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import (as_np, assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, pack_weight_scales_ref,
+from gpu_util import (as_np, assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, pack_weight_codes_ref,
+                      pack_weight_scales_ref,
                       packed_scale_bytes, t, unpack_tile_major)
 
 _np = as_np
@@ -91,7 +92,8 @@ def _run_dense(mx, d, M, H, I, packed=False):
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     wd = [t(d[n]) for n in WN]
     pk = mx.pack_weight_scales(wd[1], wd[3], wd[5]) if packed else None
-    y = mx.expert_mlp(bf16_t(x), *wd, workspace=ws, packed_scales=pk)
+    pc = mx.pack_weight_codes(wd[0], wd[2], wd[4]) if packed == "all" else None
+    y = mx.expert_mlp(bf16_t(x), *wd, workspace=ws, packed_scales=pk, packed_codes=pc)
     torch.cuda.synchronize()
     return bits(y), _ws_slices(mx, ws, M, H, I)
 
@@ -201,8 +203,9 @@ def test_shared_expert_prefill_sampled_rows(mx):
 def _run_grouped(mx, d, packed=False, requant="mxfp4", g=0.0):
     wd = [t(d[n]) for n in WN]
     pk = mx.pack_weight_scales(wd[1], wd[3], wd[5]) if packed else None
+    pc = mx.pack_weight_codes(wd[0], wd[2], wd[4]) if packed == "all" else None
     y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]), *wd, requant=requant, requant_global=g,
-                              packed_scales=pk)
+                              packed_scales=pk, packed_codes=pc)
     torch.cuda.synchronize()
     return bits(y)
 
@@ -396,6 +399,43 @@ def test_pack_weight_scales_layout(mx, E, H, I):
     pk = mx.pack_weight_scales(t(w1s), t(w3s), t(w2s))
     assert pk.numel() == mx.packed_weight_scales_size(H, I, E)
     assert np.array_equal(pk.cpu().numpy(), pack_weight_scales_ref(w1s, w3s, w2s))
+
+
+@pytest.mark.parametrize("E,H,I", [(3, 384, 256), (2, 512, 384), (1, 7168, 3072)])
+def test_pack_weight_codes_layout(mx, E, H, I):
+    """mx_pack_weight_codes moves bytes only: compare with the layout written out
+    in numpy (the GEMM's LDS image of each tile's half stage)."""
+    rng = np.random.default_rng(E * 1000 + H + I + 1)
+    w1 = rng.integers(0, 256, (E, I, H // 2), dtype=np.uint8)
+    w3 = rng.integers(0, 256, (E, I, H // 2), dtype=np.uint8)
+    w2 = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    pc = mx.pack_weight_codes(t(w1), t(w3), t(w2))
+    assert pc.numel() == mx.packed_weight_codes_size(H, I, E)
+    assert np.array_equal(pc.cpu().numpy(), pack_weight_codes_ref(w1, w3, w2))
+
+
+@pytest.mark.parametrize("M,H,I", [(16, 256, 128), (300, 384, 384), (700, 1024, 640), (128, 7168, 3072),
+                                   (4096, 7168, 3072)])
+def test_packed_codes_same_result_dense(mx, M, H, I):
+    """The tile-major weight codes feed the same MFMAs the same bytes: output
+    bit-identical to the row-major weights' (M = 128 at 7168 x 3072 runs the
+    split-K L1, where each split starts mid-matrix)."""
+    d = W.tiny_mlp(0) if H == 256 else W.shared_expert(M, seed=12, hidden=H, inter=I)
+    d["x"] = d["x"][:M]
+    y0, _ = _run_dense(mx, d, M, H, I)
+    y1, _ = _run_dense(mx, d, M, H, I, packed="all")
+    assert np.array_equal(y0, y1)
+
+
+@pytest.mark.parametrize("requant", ["mxfp4", "nvfp4"])
+def test_packed_codes_same_result_grouped(mx, requant):
+    d = W.grouped(tokens=600, n_experts=8, k=4, seed=6, hidden=640, inter=384)
+    g = 0.05 if requant == "nvfp4" else 0.0
+    y0 = _run_grouped(mx, d, requant=requant, g=g)
+    y1 = _run_grouped(mx, d, packed="all", requant=requant, g=g)
+    assert np.array_equal(y0, y1)
+    if requant == "mxfp4":
+        assert_mlp_close(y1, _oracle_grouped(d))
 
 
 @pytest.mark.parametrize("M,H,I", [(16, 256, 128), (300, 384, 384), (128, 7168, 3072)])

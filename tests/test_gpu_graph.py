@@ -112,8 +112,12 @@ def test_runner_replays_match_eager(mx, requant, T):
     w = {n: t(d0[n]) for n in ("w1", "w1s", "w3", "w3s", "w2", "w2s")}
     x, ids, gw = bf16_t(d0["x"]), t(d0["ids"]), t(d0["w"])
     g_scale = torch.tensor([2.0 ** -6], dtype=torch.float32, device="cuda")
+    # the runner reads tile-major weight scales and codes; the eager reference
+    # reads the row-major weights (the results are the same bytes either way)
+    pk = mx.pack_weight_scales(w["w1s"], w["w3s"], w["w2s"])
+    pc = mx.pack_weight_codes(w["w1"], w["w3"], w["w2"])
     r = mx.MoeRunner(x, ids, gw, w["w1"], w["w1s"], w["w3"], w["w3s"], w["w2"], w["w2s"], requant=requant,
-                     requant_global=g_scale)
+                     requant_global=g_scale, packed_scales=pk, packed_codes=pc)
     try:
         for seed in (9, 21, 33):
             d = W.grouped(tokens=T, n_experts=E, k=k, seed=seed, hidden=H, inter=I)

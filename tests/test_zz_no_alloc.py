@@ -29,7 +29,7 @@ def _noalloc_abi(mx, x, w, y, requant=0, g=None, pk=None):
     P = lambda a: ctypes.c_void_p(a.data_ptr()) if a is not None else None
     M, H = x.shape
     I = w["w1"].shape[0]
-    st = L.mx_expert_mlp_noalloc(P(x), M, H, I, *(P(w[n]) for n in NAMES), P(pk), requant, P(g), P(y),
+    st = L.mx_expert_mlp_noalloc(P(x), M, H, I, *(P(w[n]) for n in NAMES), P(pk), None, requant, P(g), P(y),
                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     return st, L.mx_last_error().decode()
 
@@ -69,5 +69,5 @@ def test_noalloc_routes_through_the_binding_and_rejects_sizes_above_the_limit(mx
     assert L.mx_expert_mlp_workspace_size(20000, W.HIDDEN, W.INTER, 0) > limit
     P = ctypes.c_void_p
     z = [P(256)] * 6
-    st = L.mx_expert_mlp_noalloc(P(256), 20000, W.HIDDEN, W.INTER, *z, None, 0, None, P(256), None)
+    st = L.mx_expert_mlp_noalloc(P(256), 20000, W.HIDDEN, W.INTER, *z, None, None, 0, None, P(256), None)
     assert st == 5 and "no-allocation" in L.mx_last_error().decode()
