@@ -235,7 +235,14 @@ __device__ __forceinline__ uint32_t l1_block(const GemmArgs& a, const Tile& t, c
     o1 = (recv >> 16) | (bytes_hi & 0xFFFF0000u);
   }
   if (valid) {
-    *(uint2*)(a.h_codes + (int64_t)row * (I >> 1) + (j0 >> 1) + hh * 8) = make_uint2(o0, o1);
+    // row-major [rows][I/2], or tile-major for the L2's copies (h_codes_tiled):
+    // block (m-tile t.mt, half stage j0/128 of the L2's K) of 16 KB, tile row ml
+    // at ml*64, this 16-byte chunk (32 j) at ((j0/32) % 4) ^ ((ml >> 2) & 3)
+    const int64_t at = a.h_codes_tiled
+                           ? ((int64_t)t.mt * (I >> 7) + (j0 >> 7)) * CODE_BLOCK_BYTES + ml * 64 +
+                                 ((((j0 >> 5) & 3) ^ ((ml >> 2) & 3)) << 4)
+                           : (int64_t)row * (I >> 1) + (j0 >> 1);
+    *(uint2*)(a.h_codes + at + hh * 8) = make_uint2(o0, o1);
   }
   return block_amax;
 }
@@ -323,11 +330,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
     w_hstride = HROW;
   }
   const uint8_t* xsrc[X_DMA];
+  int x_hstride;
+  if (a.x_tiled) {
+    // token codes already tile-major (the L1 epilogue wrote h so): one 16 KB
+    // block per m-tile and half stage, read in 1 KB pieces as the weights
+    const uint8_t* tb = a.x + ((int64_t)t.mt * (K / HK) + 2 * t.ks0) * CODE_BLOCK_BYTES;
 #pragma unroll
-  for (int i = 0; i < X_DMA; ++i) {
-    const int R = (wave * X_DMA + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((R >> 2) & 3);
-    xsrc[i] = a.x + (int64_t)x_token(R) * kb + kc0 + c * 16;
+    for (int i = 0; i < X_DMA; ++i) xsrc[i] = tb + (wave * X_DMA + i) * 1024 + lane * 16;
+    x_hstride = CODE_BLOCK_BYTES;
+  } else {
+#pragma unroll
+    for (int i = 0; i < X_DMA; ++i) {
+      const int R = (wave * X_DMA + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((R >> 2) & 3);
+      xsrc[i] = a.x + (int64_t)x_token(R) * kb + kc0 + c * 16;
+    }
+    x_hstride = HROW;
   }
   // Scale tiles (4 bytes per row per half stage): waves 0-3 copy the weight
   // rows' dwords (row 64*wave + lane), waves 4-7 the token rows' (row
@@ -365,12 +383,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
   // X_DMA token copies, then the scale dword.
   auto copy_one = [&](int h, int c) {
     const uint32_t sb = lds0 + (h % NSLOT) * SLOT_BYTES;
-    const int ko = h * HROW;
     if (c < W_DMA) {
       lds_dma16(wsrc[c] + (int64_t)h * w_hstride, sb + (wave * W_DMA + c) * 1024);
     } else if (c < W_DMA + X_DMA) {
       const int i = c - W_DMA;
-      lds_dma16(xsrc[i] + ko, sb + OFF_X + (wave * X_DMA + i) * 1024);
+      lds_dma16(xsrc[i] + (int64_t)h * x_hstride, sb + OFF_X + (wave * X_DMA + i) * 1024);
     } else {
       lds_dma4(ssrc + (h >> 1) * piece_stride + (h & 1) * HSC, sb + sc_lds);
     }

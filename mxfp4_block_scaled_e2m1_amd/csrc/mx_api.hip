@@ -137,7 +137,9 @@ DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
     const int64_t mtiles = (M + BM - 1) / BM;
     w.xq = (uint8_t*)c.take((size_t)(M * H / 2));
     w.xs = (uint8_t*)c.take((size_t)(M * H / 32));
-    w.hq = (uint8_t*)c.take((size_t)(M * I / 2));
+    // h codes: tile-major for the L2 GEMM's copies on the MXFP4 GEMM path
+    w.hq = (uint8_t*)c.take((rq == MX_FMT_MXFP4 && w.path == DENSE_GEMM) ? (size_t)packed_code_bytes(mtiles, I)
+                                                                         : (size_t)(M * I / 2));
     if (rq == MX_FMT_NVFP4) w.hs = (uint8_t*)c.take((size_t)(M * I / 16));
     else if (w.path == DENSE_GEMM) w.hs = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, I));
     else w.hs = (uint8_t*)c.take((size_t)(M * I / 32));
@@ -158,7 +160,7 @@ DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
 
 // Routed workspace: xq, xs, the route buffers, hq, hs, o, xs_pk. As on the
 // dense GEMM path, xs_pk is the tile-major copy of the gathered xs and, with
-// MXFP4 re-quantisation, hs is tile-major over the m-tiles.
+// MXFP4 re-quantisation, hq and hs are tile-major over the m-tiles.
 //
 // With few rows per expert (routed_stream_fits) the weight-streaming kernels
 // run instead of the GEMMs: xq, xs, the route buffers, h (bf16), hq, hs
@@ -198,7 +200,8 @@ GroupWs group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E, mx_f
     w.bytes = c.off;
     return w;
   }
-  w.hq = (uint8_t*)c.take((size_t)(P * I / 2));
+  // h codes: tile-major over the m-tiles for the L2 GEMM's copies (MXFP4)
+  w.hq = (uint8_t*)c.take(rq == MX_FMT_NVFP4 ? (size_t)(P * I / 2) : (size_t)packed_code_bytes(mtiles, I));
   w.hs = (uint8_t*)c.take(rq == MX_FMT_NVFP4 ? (size_t)(P * I / 16) : (size_t)packed_scale_bytes(mtiles, I));
   w.o = (uint16_t*)c.take((size_t)(P * H * 2));
   w.xs_pk = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, H));
@@ -562,6 +565,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   l1.grid_tiles = mtiles * l1.n_tiles;
   l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_gptr = requant_global;
   l1.h_scales_packed = requant == MX_FMT_MXFP4;
+  l1.h_codes_tiled = requant == MX_FMT_MXFP4;
   const Epilogue l1_epi = requant == MX_FMT_NVFP4 ? EPI_SWIGLU_NVFP4 : EPI_SWIGLU_MXFP4;
   if (w.l1_split > 1) {
     // split-K: fp32 partials, then their sum through the same epilogue
@@ -582,7 +586,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   l2.w_spk = packed_scales ? packed_scales + pw.l1_bytes : nullptr; l2.wspk_estride = pw.l2_estride;
   l2.w_cpk = packed_codes ? packed_codes + pc.l1_bytes : nullptr; l2.wcpk_estride = pc.l2_estride;
   l2.n_rows = H; l2.k = I;
-  l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4;
+  l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4; l2.x_tiled = requant == MX_FMT_MXFP4;
   l2.m_rows = m; l2.n_experts = 1;
   l2.n_tiles = (H + BN - 1) / BN;
   l2.grid_tiles = mtiles * l2.n_tiles;
@@ -672,6 +676,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l1.n_tiles = (I + L1_J_PER_TILE - 1) / L1_J_PER_TILE;
   l1.h_codes = w.hq; l1.h_scales = w.hs; l1.nv_gptr = requant_global;
   l1.h_scales_packed = requant == MX_FMT_MXFP4;
+  l1.h_codes_tiled = requant == MX_FMT_MXFP4;
   const Epilogue l1_epi = requant == MX_FMT_NVFP4 ? EPI_SWIGLU_NVFP4 : EPI_SWIGLU_MXFP4;
   MX_HIP(phase("l1_gemm", s, [&] { return launch_gemm(l1_epi, l1, max_mtiles * l1.n_tiles, s); }), "l1_gemm");
 
@@ -681,7 +686,7 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
   l2.w_spk = packed_scales ? packed_scales + pw.l1_bytes : nullptr; l2.wspk_estride = pw.l2_estride;
   l2.w_cpk = packed_codes ? packed_codes + pc.l1_bytes : nullptr; l2.wcpk_estride = pc.l2_estride;
   l2.n_rows = H; l2.k = I;
-  l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4;
+  l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4; l2.x_tiled = requant == MX_FMT_MXFP4;
   l2.expert_off = w.rb.expert_off; l2.tile_base = w.rb.tile_base; l2.n_experts = E;
   l2.n_tiles = (H + BN - 1) / BN;
   l2.out_bf16 = w.o; l2.row_slot = w.rb.row_slot; l2.row_weight = w.rb.row_weight;

@@ -67,6 +67,8 @@ struct GemmArgs {
   const uint8_t* x_s;         // [rows, k/32], or tile-major over the m-tiles when x_s_packed
   const int32_t* row_token;   // grouped L1: sorted row -> token; null = identity
   int x_s_packed;
+  int x_tiled;                // x holds tile-major codes: per m-tile and half stage, the
+                              // LDS image of the slot (the L2's h from an L1 with h_codes_tiled)
 
   // Row groups: grouped mode has expert_off/tile_base on the device;
   // dense mode (expert_off == null) is a single group of m_rows rows.
@@ -83,6 +85,7 @@ struct GemmArgs {
   uint8_t* h_codes;           // L1: [rows, n_rows/2]
   uint8_t* h_scales;          // L1: [rows, n_rows/32] (MXFP4) or [rows, n_rows/16] (NVFP4)
   int h_scales_packed;        // L1 MXFP4: h_scales tile-major over the m-tiles (the L2's x_s)
+  int h_codes_tiled;          // L1 MXFP4: h_codes tile-major over the m-tiles (the L2's x, x_tiled)
   float nv_global;            // L1 NVFP4 global scale; bf16-MFMA GEMMs: epilogue scale
   const float* nv_gptr;       // when set, the kernel reads nv_global from this device float
   const float* e_global;      // bf16-MFMA GEMMs, optional: per-expert factor on nv_global [E]

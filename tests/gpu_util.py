@@ -101,6 +101,22 @@ def packed_scale_bytes(tiles, k):
     return tiles * ((k + 255) // 256) * 2048
 
 
+def packed_code_bytes(tiles, k):
+    return tiles * (k // 128) * 16384
+
+
+def unpack_tile_codes(buf, tiles, k):
+    """Tile-major codes [tiles][k/128][256 rows][64 bytes], 16-byte chunk c of row
+    R at slot c ^ ((R >> 2) & 3) -> row-major [tiles * 256, k/2]."""
+    nh = k // 128
+    a = np.asarray(buf, np.uint8)[:tiles * nh * 16384].reshape(tiles, nh, 256, 4, 16)
+    R = np.arange(256)
+    out = np.empty((tiles, 256, nh, 4, 16), np.uint8)
+    for c in range(4):
+        out[:, :, :, c] = a[:, :, R, c ^ ((R >> 2) & 3)].transpose(0, 2, 1, 3)
+    return out.reshape(tiles * 256, k // 2)
+
+
 def unpack_tile_major(buf, rows, k):
     """Tile-major bytes of row tiles [tiles][stage][256][8] -> row-major [rows, k/32]."""
     nst, ks = (k + 255) // 256, k // 32
@@ -185,10 +201,11 @@ def routed_ws_slices(ws, T, H, I, k, E, requant="mxfp4"):
     P = T * k
     mt = (P + E * 255) // 256
     hs_bytes = P * I // 16 if requant == "nvfp4" else packed_scale_bytes(mt, I)
+    hq_bytes = P * I // 2 if requant == "nvfp4" else packed_code_bytes(mt, I)
     names = ["xq", "xs", "block_counts", "expert_off", "tile_base", "row_token", "row_slot", "row_weight", "hq",
              "hs", "o"]
     sizes = [T * H // 2, T * H // 32, -(-P // 1024) * E * 4, (E + 1) * 4, (E + 1) * 4, P * 4, P * 4, P * 4,
-             P * I // 2, hs_bytes, P * H * 2]
+             hq_bytes, hs_bytes, P * H * 2]
     off, out = 0, {}
     host = ws.cpu().numpy()
     for n, s in zip(names, sizes):
@@ -196,11 +213,21 @@ def routed_ws_slices(ws, T, H, I, k, E, requant="mxfp4"):
         off += _align256(s)
     for n in ("expert_off", "tile_base", "row_token", "row_slot"):
         out[n] = out[n].view(np.int32)
-    out["hq"] = out["hq"].reshape(P, I // 2)
     out["o"] = out["o"].view(np.uint16).reshape(P, H)
     if requant == "nvfp4":
+        out["hq"] = out["hq"].reshape(P, I // 2)
         out["hs"] = out["hs"].reshape(P, I // 16)
     else:
+        # codes: m-tile tile_base[e] + i, tile row q holds sorted row expert_off[e] + 256 i + q
+        tc = unpack_tile_codes(out["hq"], mt, I)
+        hq = np.zeros((P, I // 2), np.uint8)
+        eo, tb = out["expert_off"], out["tile_base"]
+        for e in range(E):
+            for i in range(tb[e + 1] - tb[e]):
+                r0 = eo[e] + 256 * i
+                n = min(256, eo[e + 1] - r0)
+                hq[r0:r0 + n] = tc[(tb[e] + i) * 256:(tb[e] + i) * 256 + n]
+        out["hq"] = hq
         # m-tile tile_base[e] + i holds the sorted rows expert_off[e] + 256 i ...
         nst = (I + 255) // 256
         tm = out["hs"][:mt * nst * 2048].reshape(mt, nst, 256, 8)

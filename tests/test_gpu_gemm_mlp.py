@@ -7,8 +7,8 @@ import torch
 import oracle as O
 import workloads as W
 from gpu_util import (as_np, assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, pack_weight_codes_ref,
-                      pack_weight_scales_ref,
-                      packed_scale_bytes, t, unpack_tile_major)
+                      pack_weight_scales_ref, packed_code_bytes, packed_scale_bytes, t, unpack_tile_codes,
+                      unpack_tile_major)
 
 _np = as_np
 WN = ("w1", "w1s", "w3", "w3s", "w2", "w2s")
@@ -32,7 +32,7 @@ def _align(n):
 def _ws_slices(mx, ws, M, H, I):
     """Dense workspace layout of mx_expert_mlp, each region 256-byte aligned:
     few tokens: h (bf16 SiLU output); weight-streaming path (9..96 tokens): xq,
-    xs, hq, hs (row-major), h; GEMM path: xq, xs, hq, hs (tile-major), xs_pk,
+    xs, hq, hs (row-major), h; GEMM path: xq, xs, hq, hs (both tile-major), xs_pk,
     and split-K partials when a GEMM is split.
     Returns (xq, xs, hq, hs) with hs row-major [M, I/32], or (h,)."""
     if M <= DECODE_MAX_TOKENS:
@@ -40,13 +40,14 @@ def _ws_slices(mx, ws, M, H, I):
     mt = (M + 255) // 256
     skinny = [M * H // 2, M * H // 32, M * I // 2, M * I // 32, M * I * 2]
     tile_major = sum(_align(n) for n in skinny) != mx.expert_mlp_workspace_size(M, H, I)
-    gemm = [M * H // 2, M * H // 32, M * I // 2, packed_scale_bytes(mt, I)]
+    gemm = [M * H // 2, M * H // 32, packed_code_bytes(mt, I), packed_scale_bytes(mt, I)]
     sizes = gemm if tile_major else skinny[:4]
     off, out = 0, []
     for n in sizes:
         out.append(ws[off:off + n])
         off += _align(n)
     if tile_major:
+        out[2] = torch.from_numpy(unpack_tile_codes(out[2].cpu().numpy(), mt, I)[:M])
         out[3] = unpack_tile_major(out[3].cpu().numpy(), M, I)
     return out
 
