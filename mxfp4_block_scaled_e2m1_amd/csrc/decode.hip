@@ -258,33 +258,52 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict_
 // ---------------------------------------------------------------- 9 <= M <= 96
 // Same weight stream, with the activations quantised beforehand by the MXFP4
 // quantiser: the token rows are read as MFMA operands straight from memory
-// (they are small and stay in the L2), 16 tokens at a time. A wave keeps its
-// K run of the 16 weight rows in registers and walks the NC token chunks, the
-// loads of chunk c+1 in flight during the MFMAs of chunk c. The 8 waves'
-// partial sums meet in LDS and wave c finishes chunk c.
-constexpr int SK_MAX_CHUNKS = 8;     // up to 128 tokens per launch
+// (they are small and stay in the L2), 16 tokens at a time. A workgroup holds
+// MT 16-row weight tiles; a wave keeps its K run of every tile in registers and
+// walks the NC token chunks, the loads of chunk c+1 in flight during the MFMAs
+// of chunk c, each chunk's token operands feeding the MT tiles' MFMAs. The 8
+// waves' partial sums meet in LDS and wave c finishes chunk c. Every workgroup
+// reads all m token rows, so MT = 2 halves the token bytes per weight byte
+// (and the workgroups: one round over the CUs instead of two).
+constexpr int SK_MAX_CHUNKS = 8;     // at most 128 tokens per launch (8 chunks of 16)
 
+// LDS sized by the chunk count: a launch of few chunks leaves room for more
+// workgroups per CU (the weight stream needs many loads in flight per CU).
+template <int MT, int NC>
 struct SkinnyLds {
-  uint8_t wscale[16 * 256];                        // the tile rows' E8M0 bytes, K <= 8192
-  f32x4 red[DW][SK_MAX_CHUNKS][64];                // partial sums per wave, chunk, lane
+  uint8_t wscale[MT][16 * 256];                    // the tiles' E8M0 bytes, K <= 8192
+  f32x4 red[DW][NC][MT][64];                       // partial sums per wave, chunk, tile, lane
 };
 
-template <int NC, int NS>
-__device__ __forceinline__ f32x4 tile_times_qtokens(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
-                                                    int m, int K, RowPair wp, RowPair sp, SkinnyLds& L) {
+template <int MT>
+struct TileSums {
+  f32x4 v[MT];
+};
+
+// wrows(t) / srows(t): the code and scale rows of tile t, by value (an array of
+// them would be a private array, which the compiler places in LDS).
+template <int MT, int NC, int NS, class WRows, class SRows>
+__device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __restrict__ aq,
+                                                            const uint8_t* __restrict__ as, int m, int K,
+                                                            WRows wrows, SRows srows, SkinnyLds<MT, NC>& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int kb = K / 2, ks = K / 32, ksteps = K / 128;
 
-  ScaleRegs sr;
-  load_wscales(sp, ks, sr);
+  ScaleRegs sr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) load_wscales(srows(t), ks, sr[t]);
   int s0, n;
   wave_steps(ksteps, s0, n);
-  uint4 wa[NS];
-  const uint8_t* myrow = wp.row(r16, kb);
+  uint4 wa[MT][NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)(myrow + min(s0 + k, ksteps - 1) * 64 + q * 16);
-  store_wscales(sr, ks, L.wscale);
+  for (int t = 0; t < MT; ++t) {
+    const uint8_t* myrow = wrows(t).row(r16, kb);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) wa[t][k] = *(const uint4*)(myrow + min(s0 + k, ksteps - 1) * 64 + q * 16);
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) store_wscales(sr[t], ks, L.wscale[t]);
   lds_barrier();
 
   // token operands of chunk c, step k: token c*16 + r16 (clamped, zeroed past m)
@@ -299,9 +318,11 @@ __device__ __forceinline__ f32x4 tile_times_qtokens(const uint8_t* __restrict__ 
       ss[k] = as[(int64_t)tok * ks + s * 4 + q];
     }
   };
-  f32x4 acc[NC];
+  f32x4 acc[NC][MT];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   load_chunk(0, b[0], bsc[0]);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -313,70 +334,88 @@ __device__ __forceinline__ f32x4 tile_times_qtokens(const uint8_t* __restrict__ 
     for (int k = 0; k < NS; ++k) {
       const uint4 z = make_uint4(0u, 0u, 0u, 0u);
       const uint4 bz = tok_ok ? b[c & 1][k] : z;
-      const uint4 az = k < n ? wa[k] : z;
-      const int sa = L.wscale[r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
-      acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc[c], 4, 4, 0, sa, 0,
-                                                               (int)bsc[c & 1][k]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const uint4 az = k < n ? wa[t][k] : z;
+        const int sa = L.wscale[t][r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
+        acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc[c][t], 4, 4, 0, sa,
+                                                                     0, (int)bsc[c & 1][k]);
+      }
     }
     // keep the loads of later chunks where they are written (one chunk ahead):
     // hoisting them all would hold every chunk's operands in registers
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int c = 0; c < NC; ++c) L.red[wave][c][lane] = acc[c];
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) L.red[wave][c][t][lane] = acc[c][t];
   __syncthreads();
-  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileSums<MT> tot;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) tot.v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wave < NC) {
 #pragma unroll
-    for (int w = 0; w < DW; ++w) {
-      const f32x4 o = L.red[w][wave][lane];
-      tot[0] += o[0]; tot[1] += o[1]; tot[2] += o[2]; tot[3] += o[3];
-    }
+    for (int w = 0; w < DW; ++w)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const f32x4 o = L.red[w][wave][t][lane];
+        tot.v[t][0] += o[0]; tot.v[t][1] += o[1]; tot.v[t][2] += o[2]; tot.v[t][3] += o[3];
+      }
   }
   return tot;
 }
 
-// L1: chunk `wave` of the tokens -> h (bf16), as k_decode_l1.
-template <int NC, int NS>
+// L1: chunk `wave` of the tokens -> h (bf16), 8 * MT columns j0 .. per
+// workgroup: tile t holds gate rows j0 + 8t .. +7 (tile rows 0..7) and the up
+// rows of the same j (tile rows 8..15).
+template <int MT, int NC, int NS>
 __global__ __launch_bounds__(DT, 1) void k_skinny_l1(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                      int m, int H, int I, const uint8_t* __restrict__ w1,
                                                      const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ w3,
                                                      const uint8_t* __restrict__ w3s, uint16_t* __restrict__ h) {
-  __shared__ SkinnyLds L;
-  const int j0 = blockIdx.x * 8;
+  __shared__ SkinnyLds<MT, NC> L;
+  const int j0 = blockIdx.x * 8 * MT;
   const int kb = H / 2, ks = H / 32;
-  const RowPair wp{w1 + (int64_t)j0 * kb, w3 + (int64_t)j0 * kb};
-  const RowPair sp{w1s + (int64_t)j0 * ks, w3s + (int64_t)j0 * ks};
-  const f32x4 acc = tile_times_qtokens<NC, NS>(xq, xs, m, H, wp, sp, L);
+  auto wrows = [=](int t) { return RowPair{w1 + (int64_t)(j0 + 8 * t) * kb, w3 + (int64_t)(j0 + 8 * t) * kb}; };
+  auto srows = [=](int t) { return RowPair{w1s + (int64_t)(j0 + 8 * t) * ks, w3s + (int64_t)(j0 + 8 * t) * ks}; };
+  const TileSums<MT> acc = tiles_times_qtokens<MT, NC, NS>(xq, xs, m, H, wrows, srows, L);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float up[4];
+  const int tk = wave * 16 + (lane & 15), q = lane >> 4;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) up[v] = __shfl_xor(acc[v], 32);
-  const int t = wave * 16 + (lane & 15), q = lane >> 4;
-  if (wave < NC && q < 2 && t < m) {
-    const uint32_t p0 = bf16x2_rne(silu_mul(acc[0], up[0]), silu_mul(acc[1], up[1]));
-    const uint32_t p1 = bf16x2_rne(silu_mul(acc[2], up[2]), silu_mul(acc[3], up[3]));
-    *(uint2*)(h + (int64_t)t * I + j0 + 4 * q) = make_uint2(p0, p1);
+  for (int t = 0; t < MT; ++t) {
+    float up[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) up[v] = __shfl_xor(acc.v[t][v], 32);
+    if (wave < NC && q < 2 && tk < m) {
+      const uint32_t p0 = bf16x2_rne(silu_mul(acc.v[t][0], up[0]), silu_mul(acc.v[t][1], up[1]));
+      const uint32_t p1 = bf16x2_rne(silu_mul(acc.v[t][2], up[2]), silu_mul(acc.v[t][3], up[3]));
+      *(uint2*)(h + (int64_t)tk * I + j0 + 8 * t + 4 * q) = make_uint2(p0, p1);
+    }
   }
 }
 
-// L2: chunk `wave` of the tokens -> y (bf16), as k_decode_l2.
-template <int NC, int NS>
+// L2: chunk `wave` of the tokens -> y (bf16), 16 * MT output columns per
+// workgroup (tile t: w2 rows n0 + 16t .. +15).
+template <int MT, int NC, int NS>
 __global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
                                                      int m, int H, int I, const uint8_t* __restrict__ w2,
                                                      const uint8_t* __restrict__ w2s, uint16_t* __restrict__ y) {
-  __shared__ SkinnyLds L;
-  const int n0 = blockIdx.x * 16;
+  __shared__ SkinnyLds<MT, NC> L;
+  const int n0 = blockIdx.x * 16 * MT;
   const int kb = I / 2, ks = I / 32;
-  const RowPair wp{w2 + (int64_t)n0 * kb, w2 + (int64_t)(n0 + 8) * kb};
-  const RowPair sp{w2s + (int64_t)n0 * ks, w2s + (int64_t)(n0 + 8) * ks};
-  const f32x4 acc = tile_times_qtokens<NC, NS>(hq, hs, m, I, wp, sp, L);
+  auto wrows = [=](int t) { return RowPair{w2 + (int64_t)(n0 + 16 * t) * kb, w2 + (int64_t)(n0 + 16 * t + 8) * kb}; };
+  auto srows = [=](int t) { return RowPair{w2s + (int64_t)(n0 + 16 * t) * ks, w2s + (int64_t)(n0 + 16 * t + 8) * ks}; };
+  const TileSums<MT> acc = tiles_times_qtokens<MT, NC, NS>(hq, hs, m, I, wrows, srows, L);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = wave * 16 + (lane & 15), q = lane >> 4;
-  if (wave < NC && t < m) {
-    const uint32_t p0 = bf16x2_rne(acc[0], acc[1]);
-    const uint32_t p1 = bf16x2_rne(acc[2], acc[3]);
-    *(uint2*)(y + (int64_t)t * H + n0 + 4 * q) = make_uint2(p0, p1);
+  const int tk = wave * 16 + (lane & 15), q = lane >> 4;
+  if (wave < NC && tk < m) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint32_t p0 = bf16x2_rne(acc.v[t][0], acc.v[t][1]);
+      const uint32_t p1 = bf16x2_rne(acc.v[t][2], acc.v[t][3]);
+      *(uint2*)(y + (int64_t)tk * H + n0 + 16 * t + 4 * q) = make_uint2(p0, p1);
+    }
   }
 }
 
@@ -634,14 +673,18 @@ void launch_l2_ns(const DecodeArgs& a, hipStream_t s) {
   }
 }
 
+// Weight tiles per workgroup of the 9..128-token kernels (32 weight rows).
+constexpr int SK_TILES = 2;
+
 template <int NC, int NS>
 void launch_skinny_l1(const DecodeArgs& a, const uint8_t* xq, const uint8_t* xs, hipStream_t s) {
-  k_skinny_l1<NC, NS><<<a.I / 8, DT, 0, s>>>(xq, xs, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.h);
+  k_skinny_l1<SK_TILES, NC, NS><<<a.I / (8 * SK_TILES), DT, 0, s>>>(xq, xs, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s,
+                                                                   a.h);
 }
 
 template <int NC, int NS>
 void launch_skinny_l2(const DecodeArgs& a, const uint8_t* hq, const uint8_t* hs, hipStream_t s) {
-  k_skinny_l2<NC, NS><<<a.H / 16, DT, 0, s>>>(hq, hs, a.m, a.H, a.I, a.w2, a.w2s, a.y);
+  k_skinny_l2<SK_TILES, NC, NS><<<a.H / (16 * SK_TILES), DT, 0, s>>>(hq, hs, a.m, a.H, a.I, a.w2, a.w2s, a.y);
 }
 
 template <int NC>
@@ -688,15 +731,18 @@ void launch_routed_l2_op(const RoutedArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Every workgroup reads all m token rows, so the token traffic grows with m;
-// above 96 tokens the 256 x 256 GEMM (whose time hardly depends on m at this
-// size) is faster.
+// Every workgroup reads all m token rows, so the token traffic grows with m.
+// Measured on the shared expert (7168 x 3072, hipGraph replay over rotating
+// weight copies), two tiles per workgroup: 23.6 / 28.0 / 37.2 / 48.7 us at 16 /
+// 32 / 64 / 96 tokens (one tile per workgroup: 27.3 / 37.5 / 55.4 / 76.5),
+// against 50.4 us for the tiled GEMM at 96 tokens; at 128 the GEMM wins (51.0
+// against 55.8 us).
 constexpr int SK_MAX_TOKENS = 96;
 
 bool skinny_fits(int64_t m, int64_t hidden, int64_t inter) {
   if (m < 1 || m > SK_MAX_TOKENS) return false;
   if (hidden > DW * MAX_STEPS * 128 || inter > DW * MAX_STEPS * 128) return false;
-  if (inter % 8 != 0 || hidden % 16 != 0) return false;
+  if (inter % (8 * SK_TILES) != 0 || hidden % (16 * SK_TILES) != 0) return false;
   return 16 * (hidden / 32) <= 8 * DT && 16 * (inter / 32) <= 8 * DT;
 }
 
