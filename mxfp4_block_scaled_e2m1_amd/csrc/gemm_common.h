@@ -167,4 +167,128 @@ static __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& a, co
   }
 }
 
+// One 32 x 32 block of the L1 epilogue, as this lane holds it: gate `ga` and up
+// `ua` are D[n][m] of token row ml within the tile and j = j0 + 8*(v/4) + 4*hh + v%4.
+// h = bf16(silu(g) * u) is re-quantised per 32 j (MXFP4: one E8M0 byte; NVFP4:
+// two E4M3 bytes per 16 j and the fp32 global scale) and stored with the codes.
+// With ROUND_GU (the GEMMs whose gate and up outputs are defined as bf16, e.g.
+// NVFP4 weights) g = bf16(ga * sg) and u = bf16(ua * su) first, as two bf16
+// linears followed by the elementwise SiLU * up would give them.
+// Returns (MXFP4) the max |h| of the block row as bf16 bits, 0 for padding rows.
+template <int EPI, bool ROUND_GU = false>
+static __device__ __forceinline__ uint32_t l1_block(const GemmArgs& a, const Tile& t, const f32x16& ga,
+                                                    const f32x16& ua, int j0, int ml, int hh, float sg = 1.0f,
+                                                    float su = 1.0f) {
+  const int I = a.n_rows;
+  const bool valid = (ml < t.rows) && (j0 < I);
+  const int row = t.row0 + ml;
+  // h as bf16 pairs: hp[2q] = (v = 4q, 4q+1), hp[2q+1] = (4q+2, 4q+3)
+  uint32_t hp[8];
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) {
+    if constexpr (ROUND_GU) {
+      const uint32_t gp = bf16x2_rne(ga[v] * sg, ga[v + 1] * sg), up = bf16x2_rne(ua[v] * su, ua[v + 1] * su);
+      hp[v >> 1] = bf16x2_rne(silu_mul(bf16_to_f32(gp & 0xFFFFu), bf16_to_f32(up & 0xFFFFu)),
+                              silu_mul(bf16_to_f32(gp >> 16), bf16_to_f32(up >> 16)));
+    } else {
+      hp[v >> 1] = bf16x2_rne(silu_mul(ga[v], ua[v]), silu_mul(ga[v + 1], ua[v + 1]));
+    }
+  }
+  uint32_t bytes_lo, bytes_hi;   // this lane's 8 code bytes (positions 4q + 2hh + {0,1})
+  uint32_t block_amax = 0;
+  if constexpr (EPI == EPI_SWIGLU_MXFP4) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, amax2(hp[i]));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+    const uint32_t sbyte = mx_scale_from_amax_bits(am);
+    block_amax = valid ? am : 0u;
+    uint32_t w01[2];
+    quant_pairs_e8m0<8>(hp, sbyte, w01);
+    bytes_lo = w01[0];
+    bytes_hi = w01[1];
+    if (valid && hh == 0) {
+      // row-major [rows][I/32], or tile-major for the L2's copies: m-tile
+      // t.mt, L2 stage j0/256, tile row ml, byte (j0/32) % 8
+      const int64_t at = a.h_scales_packed
+                             ? ((int64_t)t.mt * ((I + BK - 1) / BK) + (j0 >> 8)) * SC_TILE_STAGE_BYTES +
+                                   ml * SC_STAGE_BYTES + ((j0 >> 5) & 7)
+                             : (int64_t)row * (I >> 5) + (j0 >> 5);
+      a.h_scales[at] = (uint8_t)sbyte;
+    }
+  } else {
+    // NVFP4: 16-blocks j0..j0+15 (v = 0..7) and j0+16..j0+31 (v = 8..15).
+    const float gsc = a.nv_gptr != nullptr ? *a.nv_gptr : a.h_nv_global;
+    const float t6 = 6.0f * gsc;
+    uint32_t w01[2];
+    uint32_t sbytes[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am = max(am, amax2(hp[blk * 4 + i]));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+      // a block holding an infinity or a NaN gets the E4M3 NaN byte 0x7F
+      const uint32_t sbyte = am >= 0x7F80u ? 0x7Fu : e4m3_rne_satfinite(bf16_to_f32(am) / t6);
+      sbytes[blk] = sbyte;
+      const float d = e4m3_to_f32(sbyte) * gsc;
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t pr = hp[blk * 4 + i];
+        float v0 = bf16_to_f32(pr & 0xFFFFu), v1 = bf16_to_f32(pr >> 16);
+        if (sbyte == 0) {
+          v0 *= 0.0f;
+          v1 *= 0.0f;
+        } else {
+          v0 = fminf(fmaxf(v0 / d, -6.0f), 6.0f);
+          v1 = fminf(fmaxf(v1 / d, -6.0f), 6.0f);
+        }
+        if (i == 0) w = quant_pair_f32_unit<0>(w, v0, v1);
+        else if (i == 1) w = quant_pair_f32_unit<1>(w, v0, v1);
+        else if (i == 2) w = quant_pair_f32_unit<2>(w, v0, v1);
+        else w = quant_pair_f32_unit<3>(w, v0, v1);
+      }
+      w01[blk] = w;
+    }
+    bytes_lo = w01[0];
+    bytes_hi = w01[1];
+    if (valid && hh == 0) {
+      const uint16_t two = (uint16_t)(sbytes[0] | (sbytes[1] << 8));
+      *(uint16_t*)(a.h_scales + (int64_t)row * (I >> 4) + (j0 >> 4)) = two;
+    }
+  }
+  // Lane hh=0 holds byte positions {0,1,4,5,8,9,12,13} of the 16-byte block row,
+  // hh=1 holds {2,3,6,7,10,11,14,15}; bytes_lo = q0p0,q0p1,q1p0,q1p1, bytes_hi = q2.., q3...
+  // Exchange so that hh=0 writes bytes 0..7 and hh=1 writes 8..15.
+  const uint32_t send = hh ? bytes_lo : bytes_hi;
+  const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+  uint32_t o0, o1;
+  if (hh == 0) {
+    o0 = (bytes_lo & 0xFFFFu) | ((recv & 0xFFFFu) << 16);
+    o1 = (bytes_lo >> 16) | (recv & 0xFFFF0000u);
+  } else {
+    o0 = (recv & 0xFFFFu) | ((bytes_hi & 0xFFFFu) << 16);
+    o1 = (recv >> 16) | (bytes_hi & 0xFFFF0000u);
+  }
+  if (valid) {
+    // row-major [rows][I/2], or tile-major for the L2's copies (h_codes_tiled):
+    // block (m-tile t.mt, half stage j0/128 of the L2's K) of 16 KB, tile row ml
+    // at ml*64, this 16-byte chunk (32 j) at ((j0/32) % 4) ^ ((ml >> 2) & 3)
+    const int64_t at = a.h_codes_tiled
+                           ? ((int64_t)t.mt * (I >> 7) + (j0 >> 7)) * CODE_BLOCK_BYTES + ml * 64 +
+                                 ((((j0 >> 5) & 3) ^ ((ml >> 2) & 3)) << 4)
+                           : (int64_t)row * (I >> 1) + (j0 >> 1);
+    *(uint2*)(a.h_codes + at + hh * 8) = make_uint2(o0, o1);
+  }
+  return block_amax;
+}
+
+// NVFP4 warm-up: fold this wave's max |h| into *amax (one atomic per wave).
+static __device__ __forceinline__ void wave_amax_atomic(uint32_t* amax, uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax, v);
+}
+
 }  // namespace mx

@@ -87,7 +87,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_b
 // One 256 x 256 tile of o = g * h . w^T (h NVFP4; w MXFP4, or NVFP4 when NVW,
 // whose E4M3 scales [rows, k/16] are in wa_s and whose global scale is folded
 // into g by the caller).
-template <bool NVW>
+// SWIGLU (NVFP4 weights): the fused gate/up L1. The weight tile holds gate rows
+// (wa, wa_s) and up rows (wb, wb_s) of 128 intermediate columns j, in the row
+// order of the FP4 L1 tile, so a wave's gate block acc[f][g] and up block
+// acc[f + 2][g] cover the same j; the epilogue forms g = bf16(gate * sg),
+// u = bf16(up * su), h = bf16(silu(g) * u) and re-quantises h to NVFP4 with the
+// fp32 global h_nv_global (codes and E4M3 scales row-major, as k_quant_nvfp4
+// writes them): the two bf16 GEMMs, the SiLU * up and the quantiser in one pass.
+template <bool NVW, bool SWIGLU>
 __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,10 +107,23 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
 
   // copy assignment: row R = tid / 2 of both tiles, columns (tid & 1) * 32 .. +31
   const int R = tid >> 1, half = tid & 1;
-  const int wrow = min(t.nt * BN + R, a.n_rows - 1);
-  const uint8_t* wsrc = a.wa + (int64_t)t.e * a.w_estride + (int64_t)wrow * kb + half * 16;
-  const uint8_t* wesrc = NVW ? a.wa_s + (int64_t)t.e * a.ws_estride + (int64_t)wrow * ksn + half * 2
-                             : a.wa_s + (int64_t)t.e * a.ws_estride + (int64_t)wrow * kse + half;
+  const uint8_t* wmat = a.wa;
+  const uint8_t* wsmat = a.wa_s;
+  int wrow;
+  if constexpr (SWIGLU) {
+    const int f = (R >> 5) & 3;   // tile rows of blocks f = 0, 1: gate; f = 2, 3: up (same j)
+    wrow = t.nt * L1_J_PER_TILE + (R >> 7) * 64 + (f & 1) * 32 + (R & 31);
+    if (f >= 2) {
+      wmat = a.wb;
+      wsmat = a.wb_s;
+    }
+  } else {
+    wrow = t.nt * BN + R;
+  }
+  wrow = min(wrow, a.n_rows - 1);
+  const uint8_t* wsrc = wmat + (int64_t)t.e * a.w_estride + (int64_t)wrow * kb + half * 16;
+  const uint8_t* wesrc = NVW ? wsmat + (int64_t)t.e * a.ws_estride + (int64_t)wrow * ksn + half * 2
+                             : wsmat + (int64_t)t.e * a.ws_estride + (int64_t)wrow * kse + half;
   const int hrow = t.row0 + min(R, t.rows - 1);
   const uint8_t* hsrc = a.x + (int64_t)hrow * kb + half * 16;
   const uint8_t* hssrc = a.x_s + (int64_t)hrow * ksn + half * 2;
@@ -143,7 +163,8 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
       for (int v = 0; v < 16; ++v) acc[f][g][v] = 0.0f;
 
   const int r32 = lane & 31, hh = lane >> 5;
-  const TileRows<2> rows = load_tile_rows<2>(a, t, wm, lane);   // for the epilogue, loaded early
+  TileRows<2> rows;   // for the bf16 epilogue, loaded early
+  if constexpr (!SWIGLU) rows = load_tile_rows<2>(a, t, wm, lane);
   // raw bytes of two stages in flight: stage st+2 is loaded while stage st is
   // multiplied and stage st+1 converted, so the loads have two stages of MFMAs
   // to arrive in. `cur` held stage st (already in LDS), `nxt` holds stage st+1.
@@ -179,13 +200,25 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
     stage(st, ra, rb);
     if (st + 1 < nst) stage(st + 1, rb, ra);
   }
-  const float g = a.nv_gptr != nullptr ? *a.nv_gptr : a.nv_global;
-  const float scale = a.e_global != nullptr ? g * a.e_global[t.e] : g;
-  store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, scale, smem, GEMM_THREADS);
+  if constexpr (SWIGLU) {
+    const float sg = a.e_global != nullptr ? a.nv_global * a.e_global[t.e] : a.nv_global;
+    const float su = a.e_global2 != nullptr ? a.nv_global2 * a.e_global2[t.e] : a.nv_global2;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int j0 = t.nt * L1_J_PER_TILE + wn * 64 + f * 32;   // 32-aligned block of j
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        l1_block<EPI_SWIGLU_NVFP4, true>(a, t, acc[f][g], acc[f + 2][g], j0, wm * 64 + g * 32 + r32, hh, sg, su);
+    }
+  } else {
+    const float g = a.nv_gptr != nullptr ? *a.nv_gptr : a.nv_global;
+    const float scale = a.e_global != nullptr ? g * a.e_global[t.e] : g;
+    store_tile_bf16_lds<2>(a, t, acc, rows, wn, wm, lane, scale, smem, GEMM_THREADS);
+  }
 }
 
 // Persistent kernel with the tile order and XCD mapping of the FP4 GEMM.
-template <bool NVW>
+template <bool NVW, bool SWIGLU>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm_nv(const GemmArgs a) {
   // the two K-stage slots, or the bf16 output tile of the epilogue
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_SLOT > TILE_LDS_TOTAL ? 2 * NV_SLOT : TILE_LDS_TOTAL];
@@ -197,7 +230,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void k_gemm_nv(const GemmArgs a) {
   const int per = (total + 7) >> 3;
   const int end = min((xcd + 1) * per, total);
   for (int L = xcd * per + local; L < end; L += per_xcd_wgs) {
-    nv_tile<NVW>(a, decode_tile(a, tt, L), smem);
+    nv_tile<NVW, SWIGLU>(a, decode_tile(a, tt, L), smem);
     __syncthreads();   // the next tile's first stores overwrite slot 0
   }
 }
@@ -208,7 +241,7 @@ hipError_t launch_gemm_nv_l2(const GemmArgs& a, int max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const int cus = cu_count();
   const int grid = ((max_tiles < cus ? max_tiles : cus) + 7) & ~7;
-  k_gemm_nv<false><<<grid, GEMM_THREADS, 0, s>>>(a);
+  k_gemm_nv<false, false><<<grid, GEMM_THREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -216,7 +249,15 @@ hipError_t launch_gemm_nv_w(const GemmArgs& a, int max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const int cus = cu_count();
   const int grid = ((max_tiles < cus ? max_tiles : cus) + 7) & ~7;
-  k_gemm_nv<true><<<grid, GEMM_THREADS, 0, s>>>(a);
+  k_gemm_nv<true, false><<<grid, GEMM_THREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nv_w_swiglu(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  const int cus = cu_count();
+  const int grid = ((max_tiles < cus ? max_tiles : cus) + 7) & ~7;
+  k_gemm_nv<true, true><<<grid, GEMM_THREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -921,7 +921,6 @@ size_t mx_nvfp4_expert_mlp_workspace_size(int64_t M, int64_t hidden, int64_t int
   Carve c(nullptr);
   c.take((size_t)(M * hidden / 2));
   c.take((size_t)(M * (hidden / 16)));
-  for (int i = 0; i < 3; ++i) c.take((size_t)(M * inter * 2));   // g, u, h
   c.take((size_t)(M * inter / 2));
   c.take((size_t)(M * (inter / 16)));
   return c.off;
@@ -959,9 +958,6 @@ mx_status mx_nvfp4_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int6
   Carve c(workspace);
   uint8_t* xq = (uint8_t*)c.take((size_t)(M * hidden / 2));
   uint8_t* xs = (uint8_t*)c.take((size_t)(M * (hidden / 16)));
-  uint16_t* g = (uint16_t*)c.take((size_t)(M * inter * 2));
-  uint16_t* u = (uint16_t*)c.take((size_t)(M * inter * 2));
-  uint16_t* h = (uint16_t*)c.take((size_t)(M * inter * 2));
   uint8_t* hq = (uint8_t*)c.take((size_t)(M * inter / 2));
   uint8_t* hs = (uint8_t*)c.take((size_t)(M * (inter / 16)));
   auto gemm = [&](const uint8_t* aq, const uint8_t* as, const uint8_t* w, const uint8_t* ws, int64_t N, int64_t K,
@@ -978,13 +974,17 @@ mx_status mx_nvfp4_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int6
     return launch_gemm_nv_w(a, a.grid_tiles, s);
   };
   MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(x, M, hidden, x_global, nullptr, xq, xs, s); }), "quant_x");
-  MX_HIP(phase("nv_gemm", s, [&] {
-           hipError_t e = gemm(xq, xs, w1, w1_s, inter, hidden, x_global * w1_global, g);
-           if (e != hipSuccess) return e;
-           return gemm(xq, xs, w3, w3_s, inter, hidden, x_global * w3_global, u);
-         }), "nv_gemm_l1");
-  MX_HIP(phase("silu_mul", s, [&] { return launch_silu_mul_bf16(g, u, M * inter, h, s); }), "silu_mul");
-  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(h, M, inter, h_global, nullptr, hq, hs, s); }), "quant_h");
+  // gate and up in one GEMM whose epilogue forms h and re-quantises it
+  GemmArgs l1 = base_args();
+  l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
+  l1.n_rows = (int)inter; l1.k = (int)hidden;
+  l1.x = xq; l1.x_s = xs;
+  l1.m_rows = (int)M; l1.n_experts = 1;
+  l1.n_tiles = (int)((inter + L1_J_PER_TILE - 1) / L1_J_PER_TILE);
+  l1.grid_tiles = (int)((M + BM - 1) / BM) * l1.n_tiles;
+  l1.nv_global = x_global * w1_global; l1.nv_global2 = x_global * w3_global;
+  l1.h_codes = hq; l1.h_scales = hs; l1.h_nv_global = h_global;
+  MX_HIP(phase("nv_gemm_swiglu", s, [&] { return launch_gemm_nv_w_swiglu(l1, l1.grid_tiles, s); }), "nv_gemm_l1");
   MX_HIP(phase("nv_gemm", s, [&] { return gemm(hq, hs, w2, w2_s, hidden, inter, h_global * w2_global, y); }),
          "nv_gemm_l2");
   return ok();
@@ -992,10 +992,11 @@ mx_status mx_nvfp4_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int6
 
 namespace {
 // Routed NVFP4-weight workspace: xq, xs (per token), the route buffers, the
-// gathered xq/xs (sorted rows), g, u, h (bf16), hq, hs, o (per pair row).
+// gathered xq/xs (sorted rows), hq, hs (the fused gate/up GEMM's NVFP4 h), o
+// (per pair row).
 struct NvGroupWs {
   uint8_t *xq, *xs, *gq, *gs, *hq, *hs;
-  uint16_t *g, *u, *h, *o;
+  uint16_t* o;
   RouteBuffers rb;
   size_t bytes;
 };
@@ -1014,9 +1015,6 @@ NvGroupWs nv_group_ws(void* base, int64_t T, int64_t H, int64_t I, int k, int E)
   w.rb.row_weight = (float*)c.take((size_t)P * 4);
   w.gq = (uint8_t*)c.take((size_t)(P * H / 2));
   w.gs = (uint8_t*)c.take((size_t)(P * H / 16));
-  w.g = (uint16_t*)c.take((size_t)(P * I * 2));
-  w.u = (uint16_t*)c.take((size_t)(P * I * 2));
-  w.h = (uint16_t*)c.take((size_t)(P * I * 2));
   w.hq = (uint8_t*)c.take((size_t)(P * I / 2));
   w.hs = (uint8_t*)c.take((size_t)(P * I / 16));
   w.o = (uint16_t*)c.take((size_t)(P * H * 2));
@@ -1098,14 +1096,19 @@ mx_status mx_grouped_nvfp4_expert_mlp(const uint16_t* x, int64_t T, int64_t hidd
     a.e_global = eg;
     return launch_gemm_nv_w(a, max_mtiles * a.n_tiles, s);
   };
-  MX_HIP(phase("nv_gemm", s, [&] {
-           hipError_t e = gemm(w.gq, w.gs, w1, w1_s, w1_global, inter, hidden, x_global, w.g, false);
-           if (e != hipSuccess) return e;
-           return gemm(w.gq, w.gs, w3, w3_s, w3_global, inter, hidden, x_global, w.u, false);
-         }), "nv_gemm_l1");
-  MX_HIP(phase("silu_mul", s, [&] { return launch_silu_mul_bf16(w.g, w.u, P * inter, w.h, s); }), "silu_mul");
-  MX_HIP(phase("quant_nvfp4", s, [&] { return launch_quant_nvfp4(w.h, P, inter, h_global, nullptr, w.hq, w.hs, s); }),
-         "quant_h");
+  // gate and up in one GEMM whose epilogue forms h and re-quantises it
+  GemmArgs l1 = base_args();
+  l1.wa = w1; l1.wa_s = w1_s; l1.wb = w3; l1.wb_s = w3_s;
+  l1.w_estride = inter * hidden / 2; l1.ws_estride = inter * hidden / 16;
+  l1.n_rows = (int)inter; l1.k = (int)hidden;
+  l1.x = w.gq; l1.x_s = w.gs;
+  l1.expert_off = w.rb.expert_off; l1.tile_base = w.rb.tile_base; l1.n_experts = E;
+  l1.n_tiles = (int)((inter + L1_J_PER_TILE - 1) / L1_J_PER_TILE);
+  l1.nv_global = x_global; l1.e_global = w1_global;
+  l1.nv_global2 = x_global; l1.e_global2 = w3_global;
+  l1.h_codes = w.hq; l1.h_scales = w.hs; l1.h_nv_global = h_global;
+  MX_HIP(phase("nv_gemm_swiglu", s, [&] { return launch_gemm_nv_w_swiglu(l1, max_mtiles * l1.n_tiles, s); }),
+         "nv_gemm_l1");
   MX_HIP(phase("nv_gemm", s, [&] {
            return gemm(w.hq, w.hs, w2, w2_s, w2_global, hidden, inter, h_global, w.o, true);
          }), "nv_gemm_l2");

@@ -86,9 +86,12 @@ struct GemmArgs {
   uint8_t* h_scales;          // L1: [rows, n_rows/32] (MXFP4) or [rows, n_rows/16] (NVFP4)
   int h_scales_packed;        // L1 MXFP4: h_scales tile-major over the m-tiles (the L2's x_s)
   int h_codes_tiled;          // L1 MXFP4: h_codes tile-major over the m-tiles (the L2's x, x_tiled)
-  float nv_global;            // L1 NVFP4 global scale; bf16-MFMA GEMMs: epilogue scale
+  float nv_global;            // bf16-MFMA GEMMs: epilogue scale (fused gate/up: the gate's)
+  float nv_global2;           // bf16-MFMA fused gate/up: the up GEMM's epilogue scale
+  float h_nv_global;          // L1 NVFP4 re-quant global scale when nv_gptr is null
   const float* nv_gptr;       // when set, the kernel reads nv_global from this device float
   const float* e_global;      // bf16-MFMA GEMMs, optional: per-expert factor on nv_global [E]
+  const float* e_global2;     // bf16-MFMA fused gate/up: per-expert factor on nv_global2 [E]
   uint32_t* h_amax;           // L1 MXFP4, optional: running max of |h| (bf16 bits) over the valid rows
   uint16_t* out_bf16;         // EPI_BF16: dense y [m_rows, n_rows]; grouped o [slots, n_rows]
   const int32_t* row_slot;    // grouped L2: sorted row -> slot (t*k + j)
