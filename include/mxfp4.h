@@ -82,14 +82,23 @@ typedef enum mx_status {
   MX_ERR_FORMAT = 4,     /* format not valid for this entry point */
   MX_ERR_WORKSPACE = 5,  /* workspace smaller than the matching *_workspace_size() */
   MX_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
-  MX_ERR_VALUE = 7       /* a scalar argument is out of range (e.g. a non-finite global scale) */
+  MX_ERR_VALUE = 7,      /* a scalar argument is out of range (e.g. a non-finite global scale) */
+  /* not statuses: they make every int32 value a valid mx_status
+   * (mx_status_string of an unknown value is defined) */
+  MX_STATUS_RESERVED_MIN_ = -2147483647 - 1,
+  MX_STATUS_RESERVED_MAX_ = 2147483647
 } mx_status;
 
 typedef enum mx_format {
   MX_FMT_MXFP4 = 0,      /* E2M1 codes + E8M0 per 1x32 */
   MX_FMT_FP8_B128 = 1,   /* float8_e4m3fn + E8M0 per 128x128 block (dequant only) */
   MX_FMT_NVFP4 = 2,      /* E2M1 codes + E4M3 per 1x16 + fp32 global scale */
-  MX_FMT_MXFP8 = 3       /* float8_e4m3fn codes + E8M0 per 1x32 (activation quantisation only) */
+  MX_FMT_MXFP8 = 3,      /* float8_e4m3fn codes + E8M0 per 1x32 (activation quantisation only) */
+  /* not formats: they make every int32 value a valid mx_format, so a caller's
+   * unknown value reaches the library's check (MX_ERR_FORMAT) with defined
+   * behaviour in C++ as in C */
+  MX_FMT_RESERVED_MIN_ = -2147483647 - 1,
+  MX_FMT_RESERVED_MAX_ = 2147483647
 } mx_format;
 
 /*

@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmxfp4.so")
+# MXFP4_LIB selects another build of the same library (the host-sanitized copy
+# the CPU tests load); by default the in-tree libmxfp4.so.
+LIB_PATH = os.environ.get("MXFP4_LIB") or os.path.join(HERE, "libmxfp4.so")
 
 MX_FMT = {"mxfp4": 0, "fp8_b128": 1, "nvfp4": 2, "mxfp8": 3}
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_FORMAT",

@@ -43,13 +43,46 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmxfp4")
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C-ABI layer
+# (argument checks, workspace carving, runner, profiler): every flag applies to
+# the host compilation only (device code is built as usual). The library is
+# loaded into a process that preloads the compiler's ASan runtime.
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+BUILD_SAN = os.path.join(HERE, "_build_san")
+LIB_SAN = os.path.join(BUILD_SAN, "libmxfp4_san.so")
+
+
+def asan_runtime() -> str:
+    """The compiler's shared ASan runtime (to preload into a process that loads
+    the sanitized library)."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    hits = sorted(glob.glob(os.path.join(root, "..", "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")) +
+                  glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+    return os.path.realpath(hits[0])
+
+
+def build(jobs: int = 4, verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source and link the library (in place next to this file),
+    or, with sanitize, the host-sanitized copy under _build_san/."""
+    out_dir = BUILD_SAN if sanitize else BUILD
+    lib = LIB_SAN if sanitize else LIB
+    extra = SANITIZE_FLAGS if sanitize else []
+    os.makedirs(out_dir, exist_ok=True)
     cc = hipcc()
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        cmd = [cc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,19 +92,22 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    tmp = lib + ".tmp"
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-shared-libasan"] if sanitize else []
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--sanitize", action="store_true", help="host ASan + UBSan copy under _build_san/")
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, a.sanitize))
     sys.exit(0)

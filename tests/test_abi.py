@@ -51,6 +51,7 @@ def test_dequant_validation(L):
     assert L.mx_dequant(0, None, None, None, 4, 33, None, None) == 2 and "32" in _err(L)
     assert L.mx_dequant(0, None, None, None, 4, 64, None, None) == 1 and "codes" in _err(L)
     assert L.mx_dequant(9, None, None, None, 4, 64, None, None) == 4
+    assert L.mx_dequant(-1, None, None, None, 4, 64, None, None) == 4   # any int32 is a checked format
     assert L.mx_dequant(1, None, None, None, 4, 24, None, None) == 2
     assert L.mx_dequant(0, None, None, None, -1, 64, None, None) == 2
     assert L.mx_dequant(0, None, None, None, 0, 64, None, None) == 0      # empty: nothing to do
@@ -314,3 +315,58 @@ def test_probe_validation(L):
     assert L.mx_probe_copy(P(256), P(512), 512, None) == 7 and "overlap" in _err(L)
     assert L.mx_probe_copy(P(256), P(4096), 0, None) == 0
     assert L.mx_probe_copy(P(264), P(4096), 512, None) == 3
+
+
+def test_status_strings_every_value(L):
+    names = [L.mx_status_string(s).decode() for s in range(8)]
+    assert len(set(names)) == 8 and "unknown status" not in names
+    for s in (8, 99, -1, 2**31 - 1):
+        assert L.mx_status_string(s) == b"unknown status"
+
+
+def test_size_queries_over_shapes(L):
+    """Every workspace and packing size query over a grid of shapes: positive for
+    valid sizes, 0 for invalid ones (the host carving code, also under the
+    sanitizers)."""
+    for M in (1, 8, 9, 96, 97, 128, 300, 4096):
+        for H, I in ((256, 128), (640, 384), (7168, 3072)):
+            for rq in (0, 2):
+                assert L.mx_expert_mlp_workspace_size(M, H, I, rq) > 0
+            assert L.mx_nvfp4_expert_mlp_workspace_size(M, H, I) > 0
+            assert L.mx_fp8_expert_mlp_workspace_size(M, H, I) > 0
+            assert L.mx_fp8_block_linear_workspace_size(M, H) > 0
+            assert L.mx_nvfp4_linear_workspace_size(M, H) > 0
+            assert L.mx_nvfp4_global_warmup_workspace_size(M, H, I, 0, 1) > 0
+            for k, E in ((1, 1), (2, 8), (8, 48)):
+                for rq in (0, 2):
+                    assert L.mx_grouped_expert_mlp_workspace_size(M, H, I, k, E, rq) > 0
+                assert L.mx_grouped_nvfp4_expert_mlp_workspace_size(M, H, I, k, E) > 0
+                assert L.mx_nvfp4_global_warmup_workspace_size(M, H, I, k, E) > 0
+                assert L.mx_packed_weight_scales_size(H, I, E) > 0
+                assert L.mx_packed_weight_codes_size(H, I, E) > 0
+    assert L.mx_expert_mlp_workspace_size(-1, 256, 128, 0) == 0
+    assert L.mx_grouped_expert_mlp_workspace_size(8, 256, 128, 0, 4, 0) == 0
+    assert L.mx_packed_weight_codes_size(256, 128, 0) == 0
+
+
+def test_profiler_toggle_without_launches(L):
+    from mxfp4_block_scaled_e2m1_amd import binding
+    n = ctypes.c_int32(-1)
+    buf = (binding.PhaseStat * 4)()
+    assert L.mx_profile_start() == 0
+    assert L.mx_profile_stop(buf, 4, ctypes.byref(n)) == 0 and n.value == 0
+    assert L.mx_profile_stop(None, 0, ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_runner_create_reaches_allocation(L):
+    """Arguments that pass the checks reach the runner's allocation: on a machine
+    without a GPU that fails with MX_ERR_HIP and the partly built runner is
+    released (host paths only)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("needs a machine without a GPU")
+    P = ctypes.c_void_p
+    out = P()
+    st = L.mx_moe_runner_create(P(256), 8, 256, 128, P(256), P(256), 2, 4, *([P(256)] * 6), None, None, 0, None,
+                                P(256), ctypes.byref(out))
+    assert st == 6 and out.value is None and _err(L)
