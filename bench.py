@@ -50,11 +50,16 @@ CALIB_COPY_BYTES = 1 << 28    # --calibration-copy: one device copy of 256 MiB (
 # counter reads for the calibration copy. Valid for the GEMM sources whose
 # digest is recorded; None otherwise.
 L1_TRAFFIC = {
-    "gemm_digest": "4ad6281c8e418531",
-    "bytes_per_launch": 1724682818,          # 815062 KiB fetched x 1.99942 + 54606 KiB written x 1.000
+    "gemm_digest": "ad315724bc24c9c7",
+    "bytes_per_launch": 1700912959,          # 804351 KiB fetched x 1.99948 + 52763 KiB written x 1.000
     "profile": "profiles/grouped_e48_t4096_hbm_bytes.md",
 }
 GEMM_SOURCES = ("gemm.hip", "gemm_common.h", "mx_device.h", "mx_internal.h")
+
+
+def log(msg):
+    """Progress on stderr (the JSON line stays alone on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def parse():
@@ -291,7 +296,10 @@ def skewed_nvfp4(torch, mx, workloads):
     done, so a fixed power of two stands in for the warm-up value here."""
     T, E, K = 16384, workloads.N_LOCAL_EXPERTS, workloads.TOP_K
     H, I = workloads.HIDDEN, workloads.INTER
-    g = 2.0 ** -6
+    # the global as the library reads it: one fp32 in device memory, written
+    # once (a Python float would be copied to the device on every call, which
+    # a captured graph cannot hold)
+    g = torch.tensor([2.0 ** -6], dtype=torch.float32, device="cuda")
     d = workloads.skewed(tokens=T, seed=0)
     w = dev_tensors(torch, d, ("w1", "w1s", "w3", "w3s", "w2", "w2s", "ids", "w"))
     x = bf16_dev(torch, d["x"])
@@ -488,6 +496,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    log("inputs resident; timing the headline")
     # the headline: K steps with nothing else recorded
     ms, _ = time_steps(torch, step, a.steps, a.warmup)
     clocks = gpu_clocks(torch)
@@ -524,11 +533,15 @@ def main():
         "ms_per_step_with_phase_events": round(ms_prof, 4),
         "gpu_clocks_after_timed_steps": clocks,
     }
+    log(f"headline {ms:.4f} ms per step")
     if not a.no_secondary:
         rec["measured_peaks"] = measured_peaks(torch, mx)
+        log("measured peaks done")
         rec["secondary"] = secondary(torch, mx, workloads)
+        log("secondary configurations done")
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(d, a.cpu_experts)
+        log("cpu baseline done")
     print(json.dumps(rec), flush=True)
 
 

@@ -40,10 +40,17 @@ static_assert(BN == 256 && BM == 256, "the copy assignment below assumes 256-row
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// LDS byte offset of 16-byte chunk c (0..7) of row r of an operand tile. The
-// chunk index is XORed with (r/2) % 8 so the 16 rows a quarter-wave reads for
-// one MFMA fall in distinct banks.
-__device__ __forceinline__ int nv_off(int r, int c) { return r * NV_ROW + ((c ^ ((r >> 1) & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..7) of row r of an operand tile: chunk
+// c sits at slot c ^ s(r), s(r) = 2 * ((r / 2) % 4) + (r / 8) % 2. Measured on
+// gfx950: a 16-byte read is served 16 lanes at a time over 256 bytes of banks,
+// a 16-byte write 8 consecutive lanes at a time over 128 bytes (the slot,
+// address bits 4..6). The fragment reads (lane l: row l % 32, chunk 2k + l / 32)
+// hit 16 distinct 16-byte bank groups per cycle, for either grouping of the
+// read lanes; the stores below give each 8 lanes 8 distinct slots. With the
+// former layout ((r / 2) % 8, no reordering of the stores) the writes were 2-way
+// conflicted: 29 % of the LDS cycles.
+__device__ __forceinline__ int nv_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int nv_off(int r, int c) { return r * NV_ROW + ((c ^ nv_swz(r)) << 4); }
 
 // One thread's raw bytes of a stage: 32 logical columns of a weight row and of
 // a token row.
@@ -146,11 +153,18 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
       w0 = e4m3_to_f32(r.we & 0xFFu);
       w1 = e4m3_to_f32(r.we >> 8);
     }
+    // store i writes chunk half*4 + (i ^ swap): odd rows swap the chunks of each
+    // pair (a pair shares its E4M3 scale), so the 8 lanes of rows 4q .. 4q+3
+    // that one write cycle serves hit 8 distinct slots
+    const bool swap = R & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (NVW) *(uint4*)(wt + nv_off(R, half * 4 + i)) = h_to_bf16(wd[i], i < 2 ? w0 : w1);
-      else *(uint4*)(wt + nv_off(R, half * 4 + i)) = w_to_bf16(wd[i], r.we);
-      *(uint4*)(ht + nv_off(R, half * 4 + i)) = h_to_bf16(hd[i], i < 2 ? s0 : s1);
+      const int c = half * 4 + (i ^ (swap ? 1 : 0));
+      const uint32_t wdi = swap ? wd[i ^ 1] : wd[i];
+      const uint32_t hdi = swap ? hd[i ^ 1] : hd[i];
+      if constexpr (NVW) *(uint4*)(wt + nv_off(R, c)) = h_to_bf16(wdi, i < 2 ? w0 : w1);
+      else *(uint4*)(wt + nv_off(R, c)) = w_to_bf16(wdi, r.we);
+      *(uint4*)(ht + nv_off(R, c)) = h_to_bf16(hdi, i < 2 ? s0 : s1);
     }
   };
 
