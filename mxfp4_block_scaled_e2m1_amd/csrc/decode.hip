@@ -113,6 +113,60 @@ struct RowPair {
   }
 };
 
+// Where the code bytes of a 16-row weight tile are: lane (row r16, quarter q)
+// of K step s (128 columns) reads the 16 bytes of columns 128 s + 32 q .. +31
+// of tile row r16 at at(r16, s, q).
+//  * Row-major codes [rows, K/2]: rows 0..7 at lo + r * kb, rows 8..15 at
+//    hi + (r - 8) * kb, step s 64 bytes further per step.
+//  * The GEMM's tile-major copy (mx_pack_weight_codes): per GEMM tile and step
+//    a 16 KB block with row R at R * 64 and its 16-byte chunk c at slot
+//    c ^ ((R / 4) % 4); blocks of consecutive steps 16 KB apart. lo and hi point
+//    at the places of the first row of each half in the step-0 block, sw_lo and
+//    sw_hi are those rows' R / 4. Each half of a tile is then 512 consecutive
+//    bytes per step (a 16-row group of a GEMM tile 1 KB), where the row-major
+//    layout gives 16 separate 64-byte pieces.
+struct WTile {
+  const uint8_t* lo;
+  const uint8_t* hi;
+  int row_stride;    // kb (row-major) or 64 (tile-major)
+  int step_stride;   // 64 (row-major) or 16384 (tile-major)
+  int sw_lo, sw_hi;  // tile-major: R / 4 of the first row of each half; -1: row-major
+  __device__ __forceinline__ const uint8_t* at(int r16, int s, int q) const {
+    const int i = r16 & 7, sw = r16 < 8 ? sw_lo : sw_hi;
+    const int slot = sw < 0 ? q : (q ^ ((sw + (i >> 2)) & 3));
+    return (r16 < 8 ? lo : hi) + (int64_t)i * row_stride + (int64_t)s * step_stride + slot * 16;
+  }
+};
+
+__device__ __forceinline__ WTile wtile_rows(const uint8_t* lo, const uint8_t* hi, int kb) {
+  return WTile{lo, hi, kb, 64, -1, -1};
+}
+
+// Row R of its GEMM tile, and that tile, of L1 weight row j of the gate (up =
+// false) or up matrix: the L1 tile order (128 intermediate columns per tile;
+// per 64 of them 32 gate rows, 32 more gate rows, then the 64 up rows).
+__device__ __forceinline__ int l1_tile_row(int j, bool up) {
+  const int jj = j & (L1_J_PER_TILE - 1);
+  return (jj >> 6) * 128 + (up ? 64 : 0) + (jj & 63);
+}
+
+// Tile-major halves: L1 rows (j_lo, up_lo) .. +7 and (j_hi, up_hi) .. +7 (both
+// in one GEMM tile), of the expert's L1 blocks at pk; K = hidden.
+__device__ __forceinline__ WTile wtile_l1_packed(const uint8_t* pk, int K, int j_lo, bool up_lo, int j_hi,
+                                                 bool up_hi) {
+  const uint8_t* blk = pk + (int64_t)(j_lo / L1_J_PER_TILE) * (K / 128) * CODE_BLOCK_BYTES;
+  const int rl = l1_tile_row(j_lo, up_lo), rh = l1_tile_row(j_hi, up_hi);
+  return WTile{blk + rl * 64, blk + rh * 64, 64, CODE_BLOCK_BYTES, rl >> 2, rh >> 2};
+}
+
+// Tile-major L2 rows n0 .. n0+15 (n0 % 16 == 0) of the expert's L2 blocks at
+// pk; K = intermediate.
+__device__ __forceinline__ WTile wtile_l2_packed(const uint8_t* pk, int K, int n0) {
+  const uint8_t* blk = pk + (int64_t)(n0 / BN) * (K / 128) * CODE_BLOCK_BYTES;
+  const int r = n0 & (BN - 1);
+  return WTile{blk + r * 64, blk + (r + 8) * 64, 64, CODE_BLOCK_BYTES, r >> 2, (r + 8) >> 2};
+}
+
 // The tile rows' scale bytes (ks per row), two dwords per thread at most
 // (16 * ks <= 4 KB).
 struct ScaleRegs {
@@ -149,7 +203,7 @@ __device__ __forceinline__ void lds_barrier() {
 // into LDS. Wave 0 returns the workgroup's total for lane (token lane%16, tile
 // rows 4*(lane/16) + v).
 template <int XR, int NS>
-__device__ __forceinline__ f32x4 tile_times_tokens(const uint16_t* __restrict__ act, int m, int K, RowPair wp,
+__device__ __forceinline__ f32x4 tile_times_tokens(const uint16_t* __restrict__ act, int m, int K, WTile wp,
                                                    RowPair sp, uint8_t* lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
@@ -171,9 +225,8 @@ __device__ __forceinline__ f32x4 tile_times_tokens(const uint16_t* __restrict__ 
   // NS >= n steps per wave; steps past the wave's run re-read a valid step
   // (unconditional loads, as load_x) and are not multiplied.
   uint4 wa[NS];
-  const uint8_t* myrow = wp.row(r16, kb);
 #pragma unroll
-  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)(myrow + min(s0 + k, ksteps - 1) * 64 + q * 16);
+  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)wp.at(r16, min(s0 + k, ksteps - 1), q);
   __builtin_amdgcn_sched_barrier(0);
 
   quant_x_to_lds<XR>(xb, m, K, xq, xstride, xs);
@@ -214,11 +267,12 @@ template <int XR, int NS>
 __global__ __launch_bounds__(DT, 1) void k_decode_l1(const uint16_t* __restrict__ x, int m, int H, int I,
                                                      const uint8_t* __restrict__ w1, const uint8_t* __restrict__ w1s,
                                                      const uint8_t* __restrict__ w3, const uint8_t* __restrict__ w3s,
-                                                     uint16_t* __restrict__ h) {
+                                                     const uint8_t* __restrict__ pk, uint16_t* __restrict__ h) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int j0 = blockIdx.x * 8;
   const int kb = H / 2, ks = H / 32;
-  const RowPair wp{w1 + (int64_t)j0 * kb, w3 + (int64_t)j0 * kb};
+  const WTile wp = pk != nullptr ? wtile_l1_packed(pk, H, j0, false, j0, true)
+                                 : wtile_rows(w1 + (int64_t)j0 * kb, w3 + (int64_t)j0 * kb, kb);
   const RowPair sp{w1s + (int64_t)j0 * ks, w3s + (int64_t)j0 * ks};
   f32x4 acc = tile_times_tokens<XR, NS>(x, m, H, wp, sp, lds);
   const int lane = threadIdx.x & 63;
@@ -239,11 +293,12 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l1(const uint16_t* __restrict_
 template <int XR, int NS>
 __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict__ h, int m, int H, int I,
                                                      const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
-                                                     uint16_t* __restrict__ y) {
+                                                     const uint8_t* __restrict__ pk, uint16_t* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n0 = blockIdx.x * 16;
   const int kb = I / 2, ks = I / 32;
-  const RowPair wp{w2 + (int64_t)n0 * kb, w2 + (int64_t)(n0 + 8) * kb};
+  const WTile wp = pk != nullptr ? wtile_l2_packed(pk, I, n0)
+                                 : wtile_rows(w2 + (int64_t)n0 * kb, w2 + (int64_t)(n0 + 8) * kb, kb);
   const RowPair sp{w2s + (int64_t)n0 * ks, w2s + (int64_t)(n0 + 8) * ks};
   f32x4 acc = tile_times_tokens<XR, NS>(h, m, I, wp, sp, lds);
   const int lane = threadIdx.x & 63;
@@ -255,16 +310,20 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict_
   }
 }
 
-// ---------------------------------------------------------------- 9 <= M <= 96
-// Same weight stream, with the activations quantised beforehand by the MXFP4
-// quantiser: the token rows are read as MFMA operands straight from memory
-// (they are small and stay in the L2), 16 tokens at a time. A workgroup holds
-// MT 16-row weight tiles; a wave keeps its K run of every tile in registers and
-// walks the NC token chunks, the loads of chunk c+1 in flight during the MFMAs
-// of chunk c, each chunk's token operands feeding the MT tiles' MFMAs. The 8
-// waves' partial sums meet in LDS and wave c finishes chunk c. Every workgroup
-// reads all m token rows, so MT = 2 halves the token bytes per weight byte
-// (and the workgroups: one round over the CUs instead of two).
+// ---------------------------------------------------------------- 9 <= M <= 128
+// Same weight stream, with the activations quantised beforehand into the
+// chunked layout (launch_quant_mxfp4_chunked): the token operand of a wave's
+// load instruction is one 1 KB block of codes (and a 64-byte block of scales)
+// per 16-token chunk and K step, read straight from memory (the token rows are
+// small and stay in the L2). Row-major token rows would make each such load 16
+// separate 64-byte pieces 3.5 KB apart, which measured nearly twice as slow at
+// 64..128 tokens. A workgroup holds MT 16-row weight tiles; a wave keeps its
+// K run of every tile in registers and walks the NC token chunks, the loads of
+// chunk c+1 in flight during the MFMAs of chunk c, each chunk's token operands
+// feeding the MT tiles' MFMAs. The 8 waves' partial sums meet in LDS and wave
+// c finishes chunk c. Every workgroup reads all m token rows, so MT = 2 halves
+// the token bytes per weight byte (and the workgroups: one round over the CUs
+// instead of two).
 constexpr int SK_MAX_CHUNKS = 8;     // at most 128 tokens per launch (8 chunks of 16)
 
 // LDS sized by the chunk count: a launch of few chunks leaves room for more
@@ -280,15 +339,18 @@ struct TileSums {
   f32x4 v[MT];
 };
 
-// wrows(t) / srows(t): the code and scale rows of tile t, by value (an array of
-// them would be a private array, which the compiler places in LDS).
-template <int MT, int NC, int NS, class WRows, class SRows>
+// wtile(t) / srows(t): where tile t's codes and scale rows are, by value (an
+// array of them would be a private array, which the compiler places in LDS).
+// aq / as: the m token rows' codes and scales in the chunked layout, which
+// holds ceil(m / 16) chunks; chunks c of the launch's NC beyond those re-read
+// the last one (their rows are not written out).
+template <int MT, int NC, int NS, class WTiles, class SRows>
 __device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __restrict__ aq,
                                                             const uint8_t* __restrict__ as, int m, int K,
-                                                            WRows wrows, SRows srows, SkinnyLds<MT, NC>& L) {
+                                                            WTiles wtile, SRows srows, SkinnyLds<MT, NC>& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
-  const int kb = K / 2, ks = K / 32, ksteps = K / 128;
+  const int ks = K / 32, ksteps = K / 128;
 
   ScaleRegs sr[MT];
 #pragma unroll
@@ -298,24 +360,25 @@ __device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __res
   uint4 wa[MT][NS];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    const uint8_t* myrow = wrows(t).row(r16, kb);
+    const WTile w = wtile(t);
 #pragma unroll
-    for (int k = 0; k < NS; ++k) wa[t][k] = *(const uint4*)(myrow + min(s0 + k, ksteps - 1) * 64 + q * 16);
+    for (int k = 0; k < NS; ++k) wa[t][k] = *(const uint4*)w.at(r16, min(s0 + k, ksteps - 1), q);
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t) store_wscales(sr[t], ks, L.wscale[t]);
   lds_barrier();
 
-  // token operands of chunk c, step k: token c*16 + r16 (clamped, zeroed past m)
+  // token operands of chunk c, step k: lane's 16 bytes of the (chunk, step)
+  // block (the padding rows of the last chunk hold zero codes)
   uint4 b[2][NS];
   uint32_t bsc[2][NS];
+  const int last_chunk = (m + 15) / 16 - 1;
   auto load_chunk = [&](int c, uint4 (&bb)[NS], uint32_t (&ss)[NS]) {
-    const int tok = min(c * 16 + r16, m - 1);
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const int s = min(s0 + k, ksteps - 1);
-      bb[k] = *(const uint4*)(aq + (int64_t)tok * kb + s * 64 + q * 16);
-      ss[k] = as[(int64_t)tok * ks + s * 4 + q];
+      const int64_t blk = (int64_t)min(c, last_chunk) * ksteps + min(s0 + k, ksteps - 1);
+      bb[k] = *(const uint4*)(aq + blk * 1024 + lane * 16);
+      ss[k] = as[blk * 64 + lane];
     }
   };
   f32x4 acc[NC][MT];
@@ -327,19 +390,17 @@ __device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __res
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (c + 1 < NC) load_chunk(c + 1, b[(c + 1) & 1], bsc[(c + 1) & 1]);
-    const bool tok_ok = c * 16 + r16 < m;
     // steps past the wave's run (k >= n) multiply zero codes: no branch around
     // the MFMAs, which would make the compiler copy the accumulators
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      const uint4 bz = tok_ok ? b[c & 1][k] : z;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const uint4 az = k < n ? wa[t][k] : z;
         const int sa = L.wscale[t][r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
-        acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc[c][t], 4, 4, 0, sa,
-                                                                     0, (int)bsc[c & 1][k]);
+        acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(b[c & 1][k]), acc[c][t], 4, 4,
+                                                                     0, sa, 0, (int)bsc[c & 1][k]);
       }
     }
     // keep the loads of later chunks where they are written (one chunk ahead):
@@ -366,47 +427,57 @@ __device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __res
   return tot;
 }
 
-// L1: chunk `wave` of the tokens -> h (bf16), 8 * MT columns j0 .. per
-// workgroup: tile t holds gate rows j0 + 8t .. +7 (tile rows 0..7) and the up
-// rows of the same j (tile rows 8..15).
-template <int MT, int NC, int NS>
+// L1: chunk `wave` of the tokens -> h (bf16) for 16 intermediate columns
+// j0 .. j0+15 per workgroup: tile 0 holds their gate rows (w1), tile 1 their up
+// rows (w3), so a lane holds g and u of the same (token, j) and forms
+// h = bf16(silu(g) * u) in place. pk: the tile-major L1 codes, or null.
+template <int NC, int NS>
 __global__ __launch_bounds__(DT, 1) void k_skinny_l1(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                      int m, int H, int I, const uint8_t* __restrict__ w1,
                                                      const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ w3,
-                                                     const uint8_t* __restrict__ w3s, uint16_t* __restrict__ h) {
-  __shared__ SkinnyLds<MT, NC> L;
-  const int j0 = blockIdx.x * 8 * MT;
+                                                     const uint8_t* __restrict__ w3s,
+                                                     const uint8_t* __restrict__ pk, uint16_t* __restrict__ h) {
+  __shared__ SkinnyLds<2, NC> L;
+  const int j0 = blockIdx.x * 16;
   const int kb = H / 2, ks = H / 32;
-  auto wrows = [=](int t) { return RowPair{w1 + (int64_t)(j0 + 8 * t) * kb, w3 + (int64_t)(j0 + 8 * t) * kb}; };
-  auto srows = [=](int t) { return RowPair{w1s + (int64_t)(j0 + 8 * t) * ks, w3s + (int64_t)(j0 + 8 * t) * ks}; };
-  const TileSums<MT> acc = tiles_times_qtokens<MT, NC, NS>(xq, xs, m, H, wrows, srows, L);
+  auto wtile = [=](int t) {
+    if (pk != nullptr) return wtile_l1_packed(pk, H, j0, t == 1, j0 + 8, t == 1);
+    const uint8_t* w = t == 0 ? w1 : w3;
+    return wtile_rows(w + (int64_t)j0 * kb, w + (int64_t)(j0 + 8) * kb, kb);
+  };
+  auto srows = [=](int t) {
+    const uint8_t* s = t == 0 ? w1s : w3s;
+    return RowPair{s + (int64_t)j0 * ks, s + (int64_t)(j0 + 8) * ks};
+  };
+  const TileSums<2> acc = tiles_times_qtokens<2, NC, NS>(xq, xs, m, H, wtile, srows, L);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tk = wave * 16 + (lane & 15), q = lane >> 4;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    float up[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) up[v] = __shfl_xor(acc.v[t][v], 32);
-    if (wave < NC && q < 2 && tk < m) {
-      const uint32_t p0 = bf16x2_rne(silu_mul(acc.v[t][0], up[0]), silu_mul(acc.v[t][1], up[1]));
-      const uint32_t p1 = bf16x2_rne(silu_mul(acc.v[t][2], up[2]), silu_mul(acc.v[t][3], up[3]));
-      *(uint2*)(h + (int64_t)tk * I + j0 + 8 * t + 4 * q) = make_uint2(p0, p1);
-    }
+  // lane (token, q): rows 4q + v of both tiles, j = j0 + 4q + v
+  if (wave < NC && tk < m) {
+    const uint32_t p0 = bf16x2_rne(silu_mul(acc.v[0][0], acc.v[1][0]), silu_mul(acc.v[0][1], acc.v[1][1]));
+    const uint32_t p1 = bf16x2_rne(silu_mul(acc.v[0][2], acc.v[1][2]), silu_mul(acc.v[0][3], acc.v[1][3]));
+    *(uint2*)(h + (int64_t)tk * I + j0 + 4 * q) = make_uint2(p0, p1);
   }
 }
 
 // L2: chunk `wave` of the tokens -> y (bf16), 16 * MT output columns per
-// workgroup (tile t: w2 rows n0 + 16t .. +15).
+// workgroup (tile t: w2 rows n0 + 16t .. +15). pk: the tile-major L2 codes, or
+// null.
 template <int MT, int NC, int NS>
 __global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
                                                      int m, int H, int I, const uint8_t* __restrict__ w2,
-                                                     const uint8_t* __restrict__ w2s, uint16_t* __restrict__ y) {
+                                                     const uint8_t* __restrict__ w2s,
+                                                     const uint8_t* __restrict__ pk, uint16_t* __restrict__ y) {
   __shared__ SkinnyLds<MT, NC> L;
   const int n0 = blockIdx.x * 16 * MT;
   const int kb = I / 2, ks = I / 32;
-  auto wrows = [=](int t) { return RowPair{w2 + (int64_t)(n0 + 16 * t) * kb, w2 + (int64_t)(n0 + 16 * t + 8) * kb}; };
+  auto wtile = [=](int t) {
+    const int n = n0 + 16 * t;
+    if (pk != nullptr) return wtile_l2_packed(pk, I, n);
+    return wtile_rows(w2 + (int64_t)n * kb, w2 + (int64_t)(n + 8) * kb, kb);
+  };
   auto srows = [=](int t) { return RowPair{w2s + (int64_t)(n0 + 16 * t) * ks, w2s + (int64_t)(n0 + 16 * t + 8) * ks}; };
-  const TileSums<MT> acc = tiles_times_qtokens<MT, NC, NS>(hq, hs, m, I, wrows, srows, L);
+  const TileSums<MT> acc = tiles_times_qtokens<MT, NC, NS>(hq, hs, m, I, wtile, srows, L);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tk = wave * 16 + (lane & 15), q = lane >> 4;
   if (wave < NC && tk < m) {
@@ -640,17 +711,19 @@ int steps_bucket(int cols) {
 struct DecodeArgs {
   const uint16_t* x; int m, H, I;
   const uint8_t *w1, *w1s, *w3, *w3s, *w2, *w2s;
+  const uint8_t *pk1, *pk2;   // tile-major L1 / L2 codes, or null
   uint16_t *h, *y;
 };
 
 template <int XR, int NS>
 void launch_l1(const DecodeArgs& a, hipStream_t s) {
-  k_decode_l1<XR, NS><<<a.I / 8, DT, decode_lds(a.H), s>>>(a.x, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.h);
+  k_decode_l1<XR, NS><<<a.I / 8, DT, decode_lds(a.H), s>>>(a.x, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.pk1,
+                                                           a.h);
 }
 
 template <int XR, int NS>
 void launch_l2(const DecodeArgs& a, hipStream_t s) {
-  k_decode_l2<XR, NS><<<a.H / 16, DT, decode_lds(a.I), s>>>(a.h, a.m, a.H, a.I, a.w2, a.w2s, a.y);
+  k_decode_l2<XR, NS><<<a.H / 16, DT, decode_lds(a.I), s>>>(a.h, a.m, a.H, a.I, a.w2, a.w2s, a.pk2, a.y);
 }
 
 template <int XR>
@@ -673,18 +746,19 @@ void launch_l2_ns(const DecodeArgs& a, hipStream_t s) {
   }
 }
 
-// Weight tiles per workgroup of the 9..128-token kernels (32 weight rows).
+// Weight tiles per workgroup of the 9..128-token L2 kernel (32 w2 rows); the
+// L1 kernel holds two as well, the gate and up rows of 16 intermediate columns.
 constexpr int SK_TILES = 2;
 
 template <int NC, int NS>
 void launch_skinny_l1(const DecodeArgs& a, const uint8_t* xq, const uint8_t* xs, hipStream_t s) {
-  k_skinny_l1<SK_TILES, NC, NS><<<a.I / (8 * SK_TILES), DT, 0, s>>>(xq, xs, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s,
-                                                                   a.h);
+  k_skinny_l1<NC, NS><<<a.I / 16, DT, 0, s>>>(xq, xs, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.pk1, a.h);
 }
 
 template <int NC, int NS>
 void launch_skinny_l2(const DecodeArgs& a, const uint8_t* hq, const uint8_t* hs, hipStream_t s) {
-  k_skinny_l2<SK_TILES, NC, NS><<<a.H / (16 * SK_TILES), DT, 0, s>>>(hq, hs, a.m, a.H, a.I, a.w2, a.w2s, a.y);
+  k_skinny_l2<SK_TILES, NC, NS><<<a.H / (16 * SK_TILES), DT, 0, s>>>(hq, hs, a.m, a.H, a.I, a.w2, a.w2s, a.pk2,
+                                                                    a.y);
 }
 
 template <int NC>
@@ -732,33 +806,31 @@ void launch_routed_l2_op(const RoutedArgs& a, hipStream_t s) {
 }  // namespace
 
 // Every workgroup reads all m token rows, so the token traffic grows with m.
-// Measured on the shared expert (7168 x 3072, hipGraph replay over rotating
-// weight copies), two tiles per workgroup: 23.6 / 28.0 / 37.2 / 48.7 us at 16 /
-// 32 / 64 / 96 tokens (one tile per workgroup: 27.3 / 37.5 / 55.4 / 76.5),
-// against 50.4 us for the tiled GEMM at 96 tokens; at 128 the GEMM wins (51.0
-// against 55.8 us).
-constexpr int SK_MAX_TOKENS = 96;
+// Up to 128 tokens (8 chunks, the register budget of the accumulators) the
+// weight stream beats the tiled GEMM, whose 256-row token tiles are half
+// padding at 128 tokens.
+constexpr int SK_MAX_TOKENS = 16 * SK_MAX_CHUNKS;
 
 bool skinny_fits(int64_t m, int64_t hidden, int64_t inter) {
   if (m < 1 || m > SK_MAX_TOKENS) return false;
   if (hidden > DW * MAX_STEPS * 128 || inter > DW * MAX_STEPS * 128) return false;
-  if (inter % (8 * SK_TILES) != 0 || hidden % (16 * SK_TILES) != 0) return false;
+  if (inter % 16 != 0 || hidden % (16 * SK_TILES) != 0) return false;
   return 16 * (hidden / 32) <= 8 * DT && 16 * (inter / 32) <= 8 * DT;
 }
 
 hipError_t launch_skinny_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
                              const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
-                             uint8_t* xq, uint8_t* xs, uint16_t* h, uint8_t* hq, uint8_t* hs, uint16_t* y,
-                             hipStream_t s) {
-  const DecodeArgs a{x, m, H, I, w1, w1s, w3, w3s, w2, w2s, h, y};
-  hipError_t e = launch_quant_mxfp4(x, m, H, xq, xs, s);
+                             const uint8_t* pk1, const uint8_t* pk2, uint8_t* xq, uint8_t* xs, uint16_t* h,
+                             uint8_t* hq, uint8_t* hs, uint16_t* y, hipStream_t s) {
+  const DecodeArgs a{x, m, H, I, w1, w1s, w3, w3s, w2, w2s, pk1, pk2, h, y};
+  hipError_t e = launch_quant_mxfp4_chunked(x, m, H, xq, xs, s);
   if (e != hipSuccess) return e;
   const int nc = (m + 15) / 16;
   if (nc <= 1) launch_skinny_l1_ns<1>(a, xq, xs, s);
   else if (nc <= 2) launch_skinny_l1_ns<2>(a, xq, xs, s);
   else if (nc <= 4) launch_skinny_l1_ns<4>(a, xq, xs, s);
   else launch_skinny_l1_ns<8>(a, xq, xs, s);
-  e = launch_quant_mxfp4(h, m, I, hq, hs, s);
+  e = launch_quant_mxfp4_chunked(h, m, I, hq, hs, s);
   if (e != hipSuccess) return e;
   if (nc <= 1) launch_skinny_l2_ns<1>(a, hq, hs, s);
   else if (nc <= 2) launch_skinny_l2_ns<2>(a, hq, hs, s);
@@ -780,8 +852,8 @@ bool decode_fits(int64_t m, int64_t hidden, int64_t inter) {
 
 hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
                              const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
-                             uint16_t* h, uint16_t* y, hipStream_t s) {
-  const DecodeArgs a{x, m, H, I, w1, w1s, w3, w3s, w2, w2s, h, y};
+                             const uint8_t* pk1, const uint8_t* pk2, uint16_t* h, uint16_t* y, hipStream_t s) {
+  const DecodeArgs a{x, m, H, I, w1, w1s, w3, w3s, w2, w2s, pk1, pk2, h, y};
   const int r1 = x_rounds(m, H), r2 = x_rounds(m, I);
   if (r1 <= 1) launch_l1_ns<1>(a, s);
   else if (r1 <= 2) launch_l1_ns<2>(a, s);

@@ -170,13 +170,25 @@ __global__ __launch_bounds__(EW_THREADS) void k_dequant_nvfp4(const uint2* __res
 // MXFP4 quantise. Unit u = 8 elements (16 bytes of bf16 in, one code dword
 // out); the 4 units of a 32-block are 4 consecutive lanes, which combine their
 // amax with two lane exchanges. The first lane of the four writes the scale.
+// CHUNKED writes the layout the weight-streaming kernels read their token
+// operand in: rows in chunks of 16, and per chunk c and 128-wide K step s one
+// 1 KB block of codes, lane l = 16 q + r at bytes 16 l .. 16 l + 15 holding
+// columns 128 s + 32 q .. +31 of row 16 c + r, and one 64-byte block of scales,
+// byte l for the same row and 32 columns. Rows past the input (up to a
+// multiple of 16) are written as zero codes with scale byte 0.
+template <bool CHUNKED>
 __global__ __launch_bounds__(EW_THREADS) void k_quant_mxfp4(const uint4* __restrict__ x,
                                                             uint32_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales, int64_t units) {
+                                                            uint8_t* __restrict__ scales, int64_t in_units,
+                                                            int64_t units, uint32_t row_units, uint32_t ksteps) {
   EW_FOR_PASSES(units) {
     uint4 v[EW_UNROLL];
 #pragma unroll
-    for (int j = 0; j < EW_UNROLL; ++j) v[j] = x[min(base + j * EW_THREADS + (int64_t)threadIdx.x, units - 1)];
+    for (int j = 0; j < EW_UNROLL; ++j) {
+      const int64_t u = base + j * EW_THREADS + (int64_t)threadIdx.x;
+      v[j] = x[min(u, in_units - 1)];
+      if (CHUNKED && u >= in_units) v[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
 #pragma unroll
     for (int j = 0; j < EW_UNROLL; ++j) {
       const int64_t u = base + j * EW_THREADS + (int64_t)threadIdx.x;
@@ -188,8 +200,16 @@ __global__ __launch_bounds__(EW_THREADS) void k_quant_mxfp4(const uint4* __restr
       uint32_t r;
       quant_pairs_e8m0<4>(w, sb, &r);
       if (u < units) {
-        codes[u] = r;
-        if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sb;
+        if constexpr (CHUNKED) {
+          // u < 2^32: the chunked layout serves at most 256 rows
+          const uint32_t row = (uint32_t)u / row_units, i = (uint32_t)u - row * row_units;
+          const uint32_t blk = ((row >> 4) * ksteps + (i >> 4)) * 64 + ((i >> 2) & 3) * 16 + (row & 15);
+          codes[blk * 4 + (i & 3)] = r;
+          if ((i & 3) == 0) scales[blk] = (uint8_t)sb;
+        } else {
+          codes[u] = r;
+          if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sb;
+        }
       }
     }
   }
@@ -293,7 +313,19 @@ hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uin
                               uint8_t* scales, hipStream_t s) {
   const int64_t units = rows * (cols / 8);
   if (units == 0) return hipSuccess;
-  k_quant_mxfp4<<<ew_grid_units(units), EW_THREADS, 0, s>>>((const uint4*)x, (uint32_t*)codes, scales, units);
+  k_quant_mxfp4<false><<<ew_grid_units(units), EW_THREADS, 0, s>>>((const uint4*)x, (uint32_t*)codes, scales,
+                                                                  units, units, 0u, 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mxfp4_chunked(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                                      uint8_t* scales, hipStream_t s) {
+  const int64_t in_units = rows * (cols / 8);
+  const int64_t units = (rows + 15) / 16 * 16 * (cols / 8);
+  if (in_units == 0) return hipSuccess;
+  k_quant_mxfp4<true><<<ew_grid_units(units), EW_THREADS, 0, s>>>((const uint4*)x, (uint32_t*)codes, scales,
+                                                                 in_units, units, (uint32_t)(cols / 8),
+                                                                 (uint32_t)(cols / 128));
   return hipGetLastError();
 }
 

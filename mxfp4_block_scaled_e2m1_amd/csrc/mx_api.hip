@@ -135,14 +135,16 @@ DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
   } else {
     w.path = (rq == MX_FMT_MXFP4 && skinny_fits(M, H, I)) ? DENSE_SKINNY : DENSE_GEMM;
     const int64_t mtiles = (M + BM - 1) / BM;
-    w.xq = (uint8_t*)c.take((size_t)(M * H / 2));
-    w.xs = (uint8_t*)c.take((size_t)(M * H / 32));
+    // the weight-streaming path's token operands: chunked, whole 16-row chunks
+    const int64_t mq = w.path == DENSE_SKINNY ? (M + 15) / 16 * 16 : M;
+    w.xq = (uint8_t*)c.take((size_t)(mq * H / 2));
+    w.xs = (uint8_t*)c.take((size_t)(mq * H / 32));
     // h codes: tile-major for the L2 GEMM's copies on the MXFP4 GEMM path
     w.hq = (uint8_t*)c.take((rq == MX_FMT_MXFP4 && w.path == DENSE_GEMM) ? (size_t)packed_code_bytes(mtiles, I)
-                                                                         : (size_t)(M * I / 2));
+                                                                         : (size_t)(mq * I / 2));
     if (rq == MX_FMT_NVFP4) w.hs = (uint8_t*)c.take((size_t)(M * I / 16));
     else if (w.path == DENSE_GEMM) w.hs = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, I));
-    else w.hs = (uint8_t*)c.take((size_t)(M * I / 32));
+    else w.hs = (uint8_t*)c.take((size_t)(mq * I / 32));
     if (w.path == DENSE_SKINNY) {
       w.h = (uint16_t*)c.take((size_t)(M * I * 2));
     } else {
@@ -528,11 +530,14 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
     return fail(MX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   DenseWs w = dense_ws(workspace, M, hidden, inter, requant);
   const int H = (int)hidden, I = (int)inter, m = (int)M;
+  const PackedWeights pc = packed_codes_layout(hidden, inter, 1);
+  const uint8_t* pk1 = packed_codes;
+  const uint8_t* pk2 = packed_codes ? packed_codes + pc.l1_bytes : nullptr;
 
   if (w.path == DENSE_DECODE) {
     // few tokens: two weight-streaming kernels, activations quantised in LDS
     MX_HIP(phase("decode_mlp", s, [&] {
-             return launch_decode_mlp(x, m, H, I, w1, w1_s, w3, w3_s, w2, w2_s, w.h, y, s);
+             return launch_decode_mlp(x, m, H, I, w1, w1_s, w3, w3_s, w2, w2_s, pk1, pk2, w.h, y, s);
            }), "decode_mlp");
     return ok();
   }
@@ -540,14 +545,14 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
     // up to 96 tokens: quantise x, stream the weights with the token rows as
     // operands, quantise h, stream w2
     MX_HIP(phase("skinny_mlp", s, [&] {
-             return launch_skinny_mlp(x, m, H, I, w1, w1_s, w3, w3_s, w2, w2_s, w.xq, w.xs, w.h, w.hq, w.hs, y, s);
+             return launch_skinny_mlp(x, m, H, I, w1, w1_s, w3, w3_s, w2, w2_s, pk1, pk2, w.xq, w.xs, w.h, w.hq,
+                                      w.hs, y, s);
            }), "skinny_mlp");
     return ok();
   }
 
   const int mtiles = (m + BM - 1) / BM;
   const PackedWeights pw = packed_weights(hidden, inter, 1);
-  const PackedWeights pc = packed_codes_layout(hidden, inter, 1);
   MX_HIP(phase("quant_x", s, [&] {
            hipError_t e = launch_quant_mxfp4(x, M, hidden, w.xq, w.xs, s);
            if (e != hipSuccess) return e;
@@ -584,7 +589,7 @@ mx_status mx_expert_mlp(const uint16_t* x, int64_t M, int64_t hidden, int64_t in
   GemmArgs l2 = base_args();
   l2.wa = w2; l2.wa_s = w2_s;
   l2.w_spk = packed_scales ? packed_scales + pw.l1_bytes : nullptr; l2.wspk_estride = pw.l2_estride;
-  l2.w_cpk = packed_codes ? packed_codes + pc.l1_bytes : nullptr; l2.wcpk_estride = pc.l2_estride;
+  l2.w_cpk = pk2; l2.wcpk_estride = pc.l2_estride;
   l2.n_rows = H; l2.k = I;
   l2.x = w.hq; l2.x_s = w.hs; l2.x_s_packed = requant == MX_FMT_MXFP4; l2.x_tiled = requant == MX_FMT_MXFP4;
   l2.m_rows = m; l2.n_experts = 1;

@@ -141,6 +141,11 @@ hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, flo
                                 int64_t rows, int64_t cols, uint16_t* out, hipStream_t s);
 hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
+// The same codes and scales in the chunked layout of the weight-streaming
+// kernels (16-row chunks, 1 KB per chunk and 128-wide K step; rows padded to a
+// multiple of 16 with zero codes). cols % 128 == 0, rows <= 256.
+hipError_t launch_quant_mxfp4_chunked(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                                      uint8_t* scales, hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, float global, const float* gptr,
                               uint8_t* codes, uint8_t* scales, hipStream_t s);
 // NVFP4 warm-up: clear the |h| max word; turn it into g = f32(max / (6 * 448)).
@@ -171,20 +176,22 @@ hipError_t launch_gather_rows(const uint8_t* src, int width, const int32_t* row_
 hipError_t launch_combine(const uint16_t* o, const int32_t* topk_ids, int64_t tokens, int k,
                           int n_experts, int hidden, uint16_t* y, hipStream_t s);
 
-// ---- Few-token path (M <= 32): weight streaming, see decode.hip ----------------
+// ---- Few-token paths: weight streaming, see decode.hip ----------------------
+// pk1 / pk2: the expert's tile-major L1 / L2 weight codes (mx_pack_weight_codes)
+// or null: the kernels then read the row-major codes. Up to 8 tokens the
+// activations are quantised in LDS; h: bf16 scratch [m, inter].
 bool decode_fits(int64_t m, int64_t hidden, int64_t inter);
-// h: bf16 scratch [m, inter]
-// 9 <= M <= 96: x and h quantised by the MXFP4 quantiser into the workspace,
-// the weights streamed once by two kernels that read the token rows as MFMA
-// operands, 16 at a time (see decode.hip).
+// 9 <= M <= 128: x and h quantised by the MXFP4 quantiser into the workspace in
+// the chunked layout (xq, hq: ceil(m/16)*16 rows), the weights streamed once by
+// two kernels that read the token rows as MFMA operands, 16 at a time.
 bool skinny_fits(int64_t m, int64_t hidden, int64_t inter);
 hipError_t launch_skinny_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
                              const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
-                             uint8_t* xq, uint8_t* xs, uint16_t* h, uint8_t* hq, uint8_t* hs, uint16_t* y,
-                             hipStream_t s);
+                             const uint8_t* pk1, const uint8_t* pk2, uint8_t* xq, uint8_t* xs, uint16_t* h,
+                             uint8_t* hq, uint8_t* hs, uint16_t* y, hipStream_t s);
 hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8_t* w1, const uint8_t* w1s,
                              const uint8_t* w3, const uint8_t* w3s, const uint8_t* w2, const uint8_t* w2s,
-                             uint16_t* h, uint16_t* y, hipStream_t s);
+                             const uint8_t* pk1, const uint8_t* pk2, uint16_t* h, uint16_t* y, hipStream_t s);
 
 // Routed experts with few rows each (mean T*k/E at most 2 with MXFP4, 12 with
 // NVFP4 re-quantisation): the weights of each

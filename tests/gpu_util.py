@@ -117,6 +117,20 @@ def unpack_tile_codes(buf, tiles, k):
     return out.reshape(tiles * 256, k // 2)
 
 
+def unpack_chunked(codes, scales, rows, k):
+    """Chunked token operand of the weight-streaming kernels -> row-major codes
+    [rows, k/2] and scales [rows, k/32]. Per 16-row chunk c and 128-wide K step
+    s: a 1 KB code block whose 16 bytes at lane l = 16 q + r are columns
+    128 s + 32 q .. +31 of row 16 c + r, and a 64-byte scale block whose byte l
+    is the scale of the same row and 32 columns."""
+    ks, nck = k // 128, (rows + 15) // 16
+    c = np.asarray(codes, np.uint8)[:nck * ks * 1024].reshape(nck, ks, 4, 16, 16)
+    s = np.asarray(scales, np.uint8)[:nck * ks * 64].reshape(nck, ks, 4, 16)
+    c = c.transpose(0, 3, 1, 2, 4).reshape(nck * 16, k // 2)
+    s = s.transpose(0, 3, 1, 2).reshape(nck * 16, k // 32)
+    return c[:rows], s[:rows]
+
+
 def unpack_tile_major(buf, rows, k):
     """Tile-major bytes of row tiles [tiles][stage][256][8] -> row-major [rows, k/32]."""
     nst, ks = (k + 255) // 256, k // 32

@@ -7,8 +7,8 @@ import torch
 import oracle as O
 import workloads as W
 from gpu_util import (as_np, assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, pack_weight_codes_ref,
-                      pack_weight_scales_ref, packed_code_bytes, packed_scale_bytes, t, unpack_tile_codes,
-                      unpack_tile_major)
+                      pack_weight_scales_ref, packed_code_bytes, packed_scale_bytes, t, unpack_chunked,
+                      unpack_tile_codes, unpack_tile_major)
 
 _np = as_np
 WN = ("w1", "w1s", "w3", "w3s", "w2", "w2s")
@@ -31,14 +31,15 @@ def _align(n):
 
 def _ws_slices(mx, ws, M, H, I):
     """Dense workspace layout of mx_expert_mlp, each region 256-byte aligned:
-    few tokens: h (bf16 SiLU output); weight-streaming path (9..96 tokens): xq,
-    xs, hq, hs (row-major), h; GEMM path: xq, xs, hq, hs (both tile-major), xs_pk,
-    and split-K partials when a GEMM is split.
-    Returns (xq, xs, hq, hs) with hs row-major [M, I/32], or (h,)."""
+    few tokens: h (bf16 SiLU output); weight-streaming path (9..128 tokens): xq,
+    xs, hq, hs (chunked: 16-row chunks, whole chunks), h; GEMM path: xq, xs
+    (row-major), hq, hs (both tile-major), xs_pk, and split-K partials when a
+    GEMM is split.
+    Returns (xq, xs, hq, hs), hq [M, I/2] and hs [M, I/32] row-major, or (h,)."""
     if M <= DECODE_MAX_TOKENS:
         return [ws[:M * I * 2]]
-    mt = (M + 255) // 256
-    skinny = [M * H // 2, M * H // 32, M * I // 2, M * I // 32, M * I * 2]
+    mt, mq = (M + 255) // 256, (M + 15) // 16 * 16
+    skinny = [mq * H // 2, mq * H // 32, mq * I // 2, mq * I // 32, M * I * 2]
     tile_major = sum(_align(n) for n in skinny) != mx.expert_mlp_workspace_size(M, H, I)
     gemm = [M * H // 2, M * H // 32, packed_code_bytes(mt, I), packed_scale_bytes(mt, I)]
     sizes = gemm if tile_major else skinny[:4]
@@ -49,6 +50,10 @@ def _ws_slices(mx, ws, M, H, I):
     if tile_major:
         out[2] = torch.from_numpy(unpack_tile_codes(out[2].cpu().numpy(), mt, I)[:M])
         out[3] = unpack_tile_major(out[3].cpu().numpy(), M, I)
+    else:
+        for i, k in ((0, H), (2, I)):
+            q, s = unpack_chunked(out[i].cpu().numpy(), out[i + 1].cpu().numpy(), M, k)
+            out[i], out[i + 1] = torch.from_numpy(np.ascontiguousarray(q)), torch.from_numpy(np.ascontiguousarray(s))
     return out
 
 
@@ -415,12 +420,15 @@ def test_pack_weight_codes_layout(mx, E, H, I):
     assert np.array_equal(pc.cpu().numpy(), pack_weight_codes_ref(w1, w3, w2))
 
 
-@pytest.mark.parametrize("M,H,I", [(16, 256, 128), (300, 384, 384), (700, 1024, 640), (128, 7168, 3072),
+@pytest.mark.parametrize("M,H,I", [(16, 256, 128), (300, 384, 384), (700, 1024, 640), (1, 7168, 3072),
+                                   (8, 7168, 3072), (40, 7168, 3072), (128, 7168, 3072), (200, 7168, 3072),
                                    (4096, 7168, 3072)])
 def test_packed_codes_same_result_dense(mx, M, H, I):
     """The tile-major weight codes feed the same MFMAs the same bytes: output
-    bit-identical to the row-major weights' (M = 128 at 7168 x 3072 runs the
-    split-K L1, where each split starts mid-matrix)."""
+    bit-identical to the row-major weights', on every path: the few-token
+    kernels (1, 8), the weight-streaming kernels (16, 40: a partial last chunk
+    of a 4-chunk launch; 128), the split-K L1 (200 at 7168 x 3072, each split
+    starting mid-matrix) and the tiled GEMMs."""
     d = W.tiny_mlp(0) if H == 256 else W.shared_expert(M, seed=12, hidden=H, inter=I)
     d["x"] = d["x"][:M]
     y0, _ = _run_dense(mx, d, M, H, I)
