@@ -32,6 +32,7 @@ namespace {
 
 constexpr int DT = 512;             // threads per workgroup
 constexpr int DW = DT / 64;         // waves
+static_assert(DW == STREAM_WAVES, "the chunked token scales are laid out per wave of these kernels");
 constexpr int MAX_STEPS = 8;        // K steps of 128 per wave held in registers
 constexpr int MAX_TOK = 8;          // tokens per call on this path
 
@@ -313,11 +314,12 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict_
 // ---------------------------------------------------------------- 9 <= M <= 128
 // Same weight stream, with the activations quantised beforehand into the
 // chunked layout (launch_quant_mxfp4_chunked): the token operand of a wave's
-// load instruction is one 1 KB block of codes (and a 64-byte block of scales)
-// per 16-token chunk and K step, read straight from memory (the token rows are
-// small and stay in the L2). Row-major token rows would make each such load 16
-// separate 64-byte pieces 3.5 KB apart, which measured nearly twice as slow at
-// 64..128 tokens. A workgroup holds MT 16-row weight tiles; a wave keeps its
+// load instruction is one 1 KB block of codes per 16-token chunk and K step,
+// read straight from memory (the token rows are small and stay in the L2), and
+// one 8-byte load per lane and chunk brings its scales for the wave's whole K
+// run. Row-major token rows would make each code load 16 separate 64-byte
+// pieces 3.5 KB apart (measured nearly twice as slow at 64..128 tokens), and a
+// scale byte per step costs the address unit as much as a code load. A workgroup holds MT 16-row weight tiles; a wave keeps its
 // K run of every tile in registers and walks the NC token chunks, the loads of
 // chunk c+1 in flight during the MFMAs of chunk c, each chunk's token operands
 // feeding the MT tiles' MFMAs. The 8 waves' partial sums meet in LDS and wave
@@ -368,18 +370,20 @@ __device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __res
   for (int t = 0; t < MT; ++t) store_wscales(sr[t], ks, L.wscale[t]);
   lds_barrier();
 
-  // token operands of chunk c, step k: lane's 16 bytes of the (chunk, step)
-  // block (the padding rows of the last chunk hold zero codes)
+  // token operands of chunk c: the lane's 16 bytes of each (chunk, step) code
+  // block (the padding rows of the last chunk hold zero codes) and its 8 scale
+  // bytes of the wave's run, step k in byte k
   uint4 b[2][NS];
-  uint32_t bsc[2][NS];
+  uint2 bsc[2];
   const int last_chunk = (m + 15) / 16 - 1;
-  auto load_chunk = [&](int c, uint4 (&bb)[NS], uint32_t (&ss)[NS]) {
+  auto load_chunk = [&](int c, uint4 (&bb)[NS], uint2& ss) {
+    const int cc = min(c, last_chunk);
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const int64_t blk = (int64_t)min(c, last_chunk) * ksteps + min(s0 + k, ksteps - 1);
+      const int64_t blk = (int64_t)cc * ksteps + min(s0 + k, ksteps - 1);
       bb[k] = *(const uint4*)(aq + blk * 1024 + lane * 16);
-      ss[k] = as[blk * 64 + lane];
     }
+    ss = *(const uint2*)(as + (((int64_t)cc * DW + wave) * 64 + lane) * 8);
   };
   f32x4 acc[NC][MT];
 #pragma unroll
@@ -391,16 +395,18 @@ __device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __res
   for (int c = 0; c < NC; ++c) {
     if (c + 1 < NC) load_chunk(c + 1, b[(c + 1) & 1], bsc[(c + 1) & 1]);
     // steps past the wave's run (k >= n) multiply zero codes: no branch around
-    // the MFMAs, which would make the compiler copy the accumulators
+    // the MFMAs, which would make the compiler copy the accumulators; their
+    // token scale bytes are not written by the quantiser, so 2^0 stands in
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      const int sb = k < n ? (int)((k < 4 ? bsc[c & 1].x : bsc[c & 1].y) >> (8 * (k & 3))) : 0x7F;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const uint4 az = k < n ? wa[t][k] : z;
         const int sa = L.wscale[t][r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
         acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(b[c & 1][k]), acc[c][t], 4, 4,
-                                                                     0, sa, 0, (int)bsc[c & 1][k]);
+                                                                     0, sa, 0, sb);
       }
     }
     // keep the loads of later chunks where they are written (one chunk ahead):

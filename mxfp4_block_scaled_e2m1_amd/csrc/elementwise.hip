@@ -171,10 +171,10 @@ __global__ __launch_bounds__(EW_THREADS) void k_dequant_nvfp4(const uint2* __res
 // out); the 4 units of a 32-block are 4 consecutive lanes, which combine their
 // amax with two lane exchanges. The first lane of the four writes the scale.
 // CHUNKED writes the layout the weight-streaming kernels read their token
-// operand in: rows in chunks of 16, and per chunk c and 128-wide K step s one
-// 1 KB block of codes, lane l = 16 q + r at bytes 16 l .. 16 l + 15 holding
-// columns 128 s + 32 q .. +31 of row 16 c + r, and one 64-byte block of scales,
-// byte l for the same row and 32 columns. Rows past the input (up to a
+// operand in (launch_quant_mxfp4_chunked): rows in chunks of 16, per chunk and
+// 128-wide K step one 1 KB block of codes, and per chunk, wave of the reading
+// kernel and lane 8 scale bytes, one per step of that wave's run, so that a
+// lane loads its scales for a chunk at once. Rows past the input (up to a
 // multiple of 16) are written as zero codes with scale byte 0.
 template <bool CHUNKED>
 __global__ __launch_bounds__(EW_THREADS) void k_quant_mxfp4(const uint4* __restrict__ x,
@@ -203,9 +203,22 @@ __global__ __launch_bounds__(EW_THREADS) void k_quant_mxfp4(const uint4* __restr
         if constexpr (CHUNKED) {
           // u < 2^32: the chunked layout serves at most 256 rows
           const uint32_t row = (uint32_t)u / row_units, i = (uint32_t)u - row * row_units;
-          const uint32_t blk = ((row >> 4) * ksteps + (i >> 4)) * 64 + ((i >> 2) & 3) * 16 + (row & 15);
-          codes[blk * 4 + (i & 3)] = r;
-          if ((i & 3) == 0) scales[blk] = (uint8_t)sb;
+          const uint32_t s = i >> 4, lane = ((i >> 2) & 3) * 16 + (row & 15);
+          codes[(((row >> 4) * ksteps + s) * 64 + lane) * 4 + (i & 3)] = r;
+          if ((i & 3) == 0) {
+            // step s -> (wave w, place k in its run) of the balanced split
+            const uint32_t base = ksteps / STREAM_WAVES, extra = ksteps - base * STREAM_WAVES;
+            uint32_t w, k;
+            if (s < extra * (base + 1)) {
+              w = s / (base + 1);
+              k = s - w * (base + 1);
+            } else {
+              const uint32_t t = s - extra * (base + 1);
+              w = extra + t / base;
+              k = t - (w - extra) * base;
+            }
+            scales[(((row >> 4) * STREAM_WAVES + w) * 64 + lane) * 8 + k] = (uint8_t)sb;
+          }
         } else {
           codes[u] = r;
           if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sb;

@@ -138,13 +138,13 @@ DenseWs dense_ws(void* base, int64_t M, int64_t H, int64_t I, mx_format rq) {
     // the weight-streaming path's token operands: chunked, whole 16-row chunks
     const int64_t mq = w.path == DENSE_SKINNY ? (M + 15) / 16 * 16 : M;
     w.xq = (uint8_t*)c.take((size_t)(mq * H / 2));
-    w.xs = (uint8_t*)c.take((size_t)(mq * H / 32));
+    w.xs = (uint8_t*)c.take(w.path == DENSE_SKINNY ? (size_t)chunked_scale_bytes(M) : (size_t)(M * H / 32));
     // h codes: tile-major for the L2 GEMM's copies on the MXFP4 GEMM path
     w.hq = (uint8_t*)c.take((rq == MX_FMT_MXFP4 && w.path == DENSE_GEMM) ? (size_t)packed_code_bytes(mtiles, I)
                                                                          : (size_t)(mq * I / 2));
     if (rq == MX_FMT_NVFP4) w.hs = (uint8_t*)c.take((size_t)(M * I / 16));
     else if (w.path == DENSE_GEMM) w.hs = (uint8_t*)c.take((size_t)packed_scale_bytes(mtiles, I));
-    else w.hs = (uint8_t*)c.take((size_t)(mq * I / 32));
+    else w.hs = (uint8_t*)c.take((size_t)chunked_scale_bytes(M));
     if (w.path == DENSE_SKINNY) {
       w.h = (uint16_t*)c.take((size_t)(M * I * 2));
     } else {

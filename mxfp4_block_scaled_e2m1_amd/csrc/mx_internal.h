@@ -142,8 +142,16 @@ hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, flo
 hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
 // The same codes and scales in the chunked layout of the weight-streaming
-// kernels (16-row chunks, 1 KB per chunk and 128-wide K step; rows padded to a
-// multiple of 16 with zero codes). cols % 128 == 0, rows <= 256.
+// kernels (rows in chunks of 16, padded with zero codes; cols % 128 == 0, rows
+// <= 256). Codes: per chunk c and 128-wide K step s one 1 KB block, lane
+// l = 16 q + r at bytes 16 l .. +15 holding columns 128 s + 32 q .. +31 of row
+// 16 c + r. Scales: the K steps are split over the kernels' STREAM_WAVES waves
+// in balanced runs (the first ksteps % STREAM_WAVES waves take one more), and
+// per chunk c, wave w and lane l the 8 bytes at ((c * STREAM_WAVES + w) * 64 +
+// l) * 8 are the scales of lane l's 32 columns in the steps of w's run (bytes
+// past the run are not written).
+constexpr int STREAM_WAVES = 8;
+inline int64_t chunked_scale_bytes(int64_t rows) { return (rows + 15) / 16 * STREAM_WAVES * 64 * 8; }
 hipError_t launch_quant_mxfp4_chunked(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
                                       uint8_t* scales, hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, float global, const float* gptr,

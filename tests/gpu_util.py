@@ -117,18 +117,40 @@ def unpack_tile_codes(buf, tiles, k):
     return out.reshape(tiles * 256, k // 2)
 
 
+STREAM_WAVES = 8   # waves of the weight-streaming kernels; the chunked scales follow their K split
+
+
+def stream_wave_runs(ksteps, waves=STREAM_WAVES):
+    """The kernels' balanced split of ksteps K steps over the waves: (first step,
+    count) per wave, the first ksteps % waves waves taking one more."""
+    base, extra = divmod(ksteps, waves)
+    runs, s = [], 0
+    for w in range(waves):
+        n = base + (1 if w < extra else 0)
+        runs.append((s, n))
+        s += n
+    return runs
+
+
+def chunked_scale_bytes(rows):
+    return (rows + 15) // 16 * STREAM_WAVES * 64 * 8
+
+
 def unpack_chunked(codes, scales, rows, k):
     """Chunked token operand of the weight-streaming kernels -> row-major codes
-    [rows, k/2] and scales [rows, k/32]. Per 16-row chunk c and 128-wide K step
-    s: a 1 KB code block whose 16 bytes at lane l = 16 q + r are columns
-    128 s + 32 q .. +31 of row 16 c + r, and a 64-byte scale block whose byte l
-    is the scale of the same row and 32 columns."""
+    [rows, k/2] and scales [rows, k/32]. Codes: per 16-row chunk c and 128-wide
+    K step s a 1 KB block whose 16 bytes at lane l = 16 q + r are columns
+    128 s + 32 q .. +31 of row 16 c + r. Scales: per chunk c, wave w and lane l
+    8 bytes, byte j the scale of lane l's 32 columns in step s0(w) + j of the
+    wave's run."""
     ks, nck = k // 128, (rows + 15) // 16
     c = np.asarray(codes, np.uint8)[:nck * ks * 1024].reshape(nck, ks, 4, 16, 16)
-    s = np.asarray(scales, np.uint8)[:nck * ks * 64].reshape(nck, ks, 4, 16)
     c = c.transpose(0, 3, 1, 2, 4).reshape(nck * 16, k // 2)
-    s = s.transpose(0, 3, 1, 2).reshape(nck * 16, k // 32)
-    return c[:rows], s[:rows]
+    a = np.asarray(scales, np.uint8)[:chunked_scale_bytes(rows)].reshape(nck, STREAM_WAVES, 4, 16, 8)
+    s = np.zeros((nck, 16, ks, 4), np.uint8)
+    for w, (s0, n) in enumerate(stream_wave_runs(ks)):
+        s[:, :, s0:s0 + n, :] = a[:, w, :, :, :n].transpose(0, 2, 3, 1)
+    return c[:rows], s.reshape(nck * 16, k // 32)[:rows]
 
 
 def unpack_tile_major(buf, rows, k):

@@ -6,7 +6,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import (as_np, assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, pack_weight_codes_ref,
+from gpu_util import (as_np, assert_mlp_close, assert_requant_close, bf16_f64, bf16_t, bits, chunked_scale_bytes,
+                      pack_weight_codes_ref,
                       pack_weight_scales_ref, packed_code_bytes, packed_scale_bytes, t, unpack_chunked,
                       unpack_tile_codes, unpack_tile_major)
 
@@ -32,14 +33,15 @@ def _align(n):
 def _ws_slices(mx, ws, M, H, I):
     """Dense workspace layout of mx_expert_mlp, each region 256-byte aligned:
     few tokens: h (bf16 SiLU output); weight-streaming path (9..128 tokens): xq,
-    xs, hq, hs (chunked: 16-row chunks, whole chunks), h; GEMM path: xq, xs
+    xs, hq, hs (chunked: whole 16-row chunks, scales per wave), h; GEMM path: xq,
+    xs
     (row-major), hq, hs (both tile-major), xs_pk, and split-K partials when a
     GEMM is split.
     Returns (xq, xs, hq, hs), hq [M, I/2] and hs [M, I/32] row-major, or (h,)."""
     if M <= DECODE_MAX_TOKENS:
         return [ws[:M * I * 2]]
     mt, mq = (M + 255) // 256, (M + 15) // 16 * 16
-    skinny = [mq * H // 2, mq * H // 32, mq * I // 2, mq * I // 32, M * I * 2]
+    skinny = [mq * H // 2, chunked_scale_bytes(M), mq * I // 2, chunked_scale_bytes(M), M * I * 2]
     tile_major = sum(_align(n) for n in skinny) != mx.expert_mlp_workspace_size(M, H, I)
     gemm = [M * H // 2, M * H // 32, packed_code_bytes(mt, I), packed_scale_bytes(mt, I)]
     sizes = gemm if tile_major else skinny[:4]
@@ -105,8 +107,15 @@ def _run_dense(mx, d, M, H, I, packed=False):
 
 
 def _check_gemm_path(mx, d, M, H, I):
-    y, (xq, xs, hq, hs) = _run_dense(mx, d, M, H, I)
+    """The output, and the quantised x and re-quantised h the workspace holds
+    (only h in bf16 when the kernels quantise in registers)."""
+    y, sl = _run_dense(mx, d, M, H, I)
     ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
+    if len(sl) == 1:
+        _check_h_and_requant(mx, sl[0], M, I, inter)
+        assert_mlp_close(y, ref)
+        return
+    xq, xs, hq, hs = sl
     assert np.array_equal(xq.cpu().numpy().reshape(M, H // 2), inter["xq"])
     assert np.array_equal(xs.cpu().numpy().reshape(M, H // 32), inter["xs"])
     assert_requant_close(hq.cpu().numpy().reshape(M, I // 2), _np(hs).reshape(M, I // 32),
@@ -115,7 +124,7 @@ def _check_gemm_path(mx, d, M, H, I):
 
 
 def test_tiny_expert_mlp(mx):
-    """The tiny configuration: 16 tokens, hidden 256, intermediate 128 (GEMM path)."""
+    """The tiny configuration: 16 tokens, hidden 256, intermediate 128."""
     _check_gemm_path(mx, W.tiny_mlp(0), 16, 256, 128)
 
 
@@ -141,7 +150,7 @@ def test_shared_expert_real_shape(mx, M):
     d = W.shared_expert(M, seed=0)
     y, sl = _run_dense(mx, d, M, 7168, 3072)
     ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
-    if M <= DECODE_MAX_TOKENS:
+    if len(sl) == 1:
         _check_h_and_requant(mx, sl[0], M, 3072, inter)
     else:
         _, _, hq, hs = sl
