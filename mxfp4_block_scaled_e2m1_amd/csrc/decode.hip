@@ -311,7 +311,7 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict_
   }
 }
 
-// ---------------------------------------------------------------- 9 <= M <= 128
+// ---------------------------------------------------------------- 9 <= M <= 512
 // Same weight stream, with the activations quantised beforehand into the
 // chunked layout (launch_quant_mxfp4_chunked): the token operand of a wave's
 // load instruction is one 1 KB block of codes per 16-token chunk and K step,
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict_
 // c finishes chunk c. Every workgroup reads all m token rows, so MT = 2 halves
 // the token bytes per weight byte (and the workgroups: one round over the CUs
 // instead of two).
-constexpr int SK_MAX_CHUNKS = 8;     // at most 128 tokens per launch (8 chunks of 16)
+constexpr int SK_MAX_CHUNKS = 8;     // chunks of 16 tokens per group (registers of the accumulators)
 
 // LDS sized by the chunk count: a launch of few chunks leaves room for more
 // workgroups per CU (the weight stream needs many loads in flight per CU).
@@ -346,10 +346,10 @@ struct TileSums {
 // aq / as: the m token rows' codes and scales in the chunked layout, which
 // holds ceil(m / 16) chunks; chunks c of the launch's NC beyond those re-read
 // the last one (their rows are not written out).
-template <int MT, int NC, int NS, class WTiles, class SRows>
-__device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __restrict__ aq,
-                                                            const uint8_t* __restrict__ as, int m, int K,
-                                                            WTiles wtile, SRows srows, SkinnyLds<MT, NC>& L) {
+template <int MT, int NC, int NS, class WTiles, class SRows, class Emit>
+__device__ __forceinline__ void tiles_times_qtokens(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
+                                                    int m, int K, WTiles wtile, SRows srows, SkinnyLds<MT, NC>& L,
+                                                    Emit&& emit) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int ks = K / 32, ksteps = K / 128;
@@ -375,7 +375,7 @@ __device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __res
   // bytes of the wave's run, step k in byte k
   uint4 b[2][NS];
   uint2 bsc[2];
-  const int last_chunk = (m + 15) / 16 - 1;
+  const int nchunks = (m + 15) / 16, last_chunk = nchunks - 1;
   auto load_chunk = [&](int c, uint4 (&bb)[NS], uint2& ss) {
     const int cc = min(c, last_chunk);
 #pragma unroll
@@ -385,55 +385,62 @@ __device__ __forceinline__ TileSums<MT> tiles_times_qtokens(const uint8_t* __res
     }
     ss = *(const uint2*)(as + (((int64_t)cc * DW + wave) * 64 + lane) * 8);
   };
-  f32x4 acc[NC][MT];
+  // groups of NC chunks (more than one only past 16 * NC tokens): the weight
+  // runs stay in registers, the partial sums' LDS is reused per group
+  for (int c0 = 0; c0 < nchunks; c0 += NC) {
+    f32x4 acc[NC][MT];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  load_chunk(0, b[0], bsc[0]);
+      for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load_chunk(c0, b[0], bsc[0]);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (c + 1 < NC) load_chunk(c + 1, b[(c + 1) & 1], bsc[(c + 1) & 1]);
-    // steps past the wave's run (k >= n) multiply zero codes: no branch around
-    // the MFMAs, which would make the compiler copy the accumulators; their
-    // token scale bytes are not written by the quantiser, so 2^0 stands in
+    for (int c = 0; c < NC; ++c) {
+      if (c + 1 < NC) load_chunk(c0 + c + 1, b[(c + 1) & 1], bsc[(c + 1) & 1]);
+      // steps past the wave's run (k >= n) multiply zero codes: no branch around
+      // the MFMAs, which would make the compiler copy the accumulators; their
+      // token scale bytes are not written by the quantiser, so 2^0 stands in
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      const int sb = k < n ? (int)((k < 4 ? bsc[c & 1].x : bsc[c & 1].y) >> (8 * (k & 3))) : 0x7F;
+      for (int k = 0; k < NS; ++k) {
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        const int sb = k < n ? (int)((k < 4 ? bsc[c & 1].x : bsc[c & 1].y) >> (8 * (k & 3))) : 0x7F;
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const uint4 az = k < n ? wa[t][k] : z;
-        const int sa = L.wscale[t][r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
-        acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(b[c & 1][k]), acc[c][t], 4, 4,
-                                                                     0, sa, 0, sb);
+        for (int t = 0; t < MT; ++t) {
+          const uint4 az = k < n ? wa[t][k] : z;
+          const int sa = L.wscale[t][r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
+          acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(b[c & 1][k]), acc[c][t], 4, 4,
+                                                                       0, sa, 0, sb);
+        }
       }
+      // keep the loads of later chunks where they are written (one chunk ahead):
+      // hoisting them all would hold every chunk's operands in registers
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // keep the loads of later chunks where they are written (one chunk ahead):
-    // hoisting them all would hold every chunk's operands in registers
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) L.red[wave][c][t][lane] = acc[c][t];
+    __syncthreads();
+    TileSums<MT> tot;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) tot.v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (wave < NC) {
+#pragma unroll
+      for (int w = 0; w < DW; ++w)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const f32x4 o = L.red[w][wave][t][lane];
+          tot.v[t][0] += o[0]; tot.v[t][1] += o[1]; tot.v[t][2] += o[2]; tot.v[t][3] += o[3];
+        }
+    }
+    // lane (token c0 * 16 + 16 * wave + lane % 16, tile rows 4 * (lane / 16) + v)
+    // in waves < NC
+    emit(c0 * 16 + wave * 16 + r16, tot);
+    if (c0 + NC < nchunks) __syncthreads();   // the next group rewrites L.red
   }
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) L.red[wave][c][t][lane] = acc[c][t];
-  __syncthreads();
-  TileSums<MT> tot;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) tot.v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (wave < NC) {
-#pragma unroll
-    for (int w = 0; w < DW; ++w)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const f32x4 o = L.red[w][wave][t][lane];
-        tot.v[t][0] += o[0]; tot.v[t][1] += o[1]; tot.v[t][2] += o[2]; tot.v[t][3] += o[3];
-      }
-  }
-  return tot;
 }
 
-// L1: chunk `wave` of the tokens -> h (bf16) for 16 intermediate columns
+// L1: chunk `wave` of each token group -> h (bf16) for 16 intermediate columns
 // j0 .. j0+15 per workgroup: tile 0 holds their gate rows (w1), tile 1 their up
 // rows (w3), so a lane holds g and u of the same (token, j) and forms
 // h = bf16(silu(g) * u) in place. pk: the tile-major L1 codes, or null.
@@ -455,18 +462,18 @@ __global__ __launch_bounds__(DT, 1) void k_skinny_l1(const uint8_t* __restrict__
     const uint8_t* s = t == 0 ? w1s : w3s;
     return RowPair{s + (int64_t)j0 * ks, s + (int64_t)(j0 + 8) * ks};
   };
-  const TileSums<2> acc = tiles_times_qtokens<2, NC, NS>(xq, xs, m, H, wtile, srows, L);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tk = wave * 16 + (lane & 15), q = lane >> 4;
-  // lane (token, q): rows 4q + v of both tiles, j = j0 + 4q + v
-  if (wave < NC && tk < m) {
-    const uint32_t p0 = bf16x2_rne(silu_mul(acc.v[0][0], acc.v[1][0]), silu_mul(acc.v[0][1], acc.v[1][1]));
-    const uint32_t p1 = bf16x2_rne(silu_mul(acc.v[0][2], acc.v[1][2]), silu_mul(acc.v[0][3], acc.v[1][3]));
-    *(uint2*)(h + (int64_t)tk * I + j0 + 4 * q) = make_uint2(p0, p1);
-  }
+  const int wave = threadIdx.x >> 6, q = (threadIdx.x & 63) >> 4;
+  tiles_times_qtokens<2, NC, NS>(xq, xs, m, H, wtile, srows, L, [&](int tk, const TileSums<2>& acc) {
+    // lane (token, q): rows 4q + v of both tiles, j = j0 + 4q + v
+    if (wave < NC && tk < m) {
+      const uint32_t p0 = bf16x2_rne(silu_mul(acc.v[0][0], acc.v[1][0]), silu_mul(acc.v[0][1], acc.v[1][1]));
+      const uint32_t p1 = bf16x2_rne(silu_mul(acc.v[0][2], acc.v[1][2]), silu_mul(acc.v[0][3], acc.v[1][3]));
+      *(uint2*)(h + (int64_t)tk * I + j0 + 4 * q) = make_uint2(p0, p1);
+    }
+  });
 }
 
-// L2: chunk `wave` of the tokens -> y (bf16), 16 * MT output columns per
+// L2: chunk `wave` of each token group -> y (bf16), 16 * MT output columns per
 // workgroup (tile t: w2 rows n0 + 16t .. +15). pk: the tile-major L2 codes, or
 // null.
 template <int MT, int NC, int NS>
@@ -483,17 +490,17 @@ __global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__
     return wtile_rows(w2 + (int64_t)n * kb, w2 + (int64_t)(n + 8) * kb, kb);
   };
   auto srows = [=](int t) { return RowPair{w2s + (int64_t)(n0 + 16 * t) * ks, w2s + (int64_t)(n0 + 16 * t + 8) * ks}; };
-  const TileSums<MT> acc = tiles_times_qtokens<MT, NC, NS>(hq, hs, m, I, wtile, srows, L);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tk = wave * 16 + (lane & 15), q = lane >> 4;
-  if (wave < NC && tk < m) {
+  const int wave = threadIdx.x >> 6, q = (threadIdx.x & 63) >> 4;
+  tiles_times_qtokens<MT, NC, NS>(hq, hs, m, I, wtile, srows, L, [&](int tk, const TileSums<MT>& acc) {
+    if (wave < NC && tk < m) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint32_t p0 = bf16x2_rne(acc.v[t][0], acc.v[t][1]);
-      const uint32_t p1 = bf16x2_rne(acc.v[t][2], acc.v[t][3]);
-      *(uint2*)(y + (int64_t)tk * H + n0 + 16 * t + 4 * q) = make_uint2(p0, p1);
+      for (int t = 0; t < MT; ++t) {
+        const uint32_t p0 = bf16x2_rne(acc.v[t][0], acc.v[t][1]);
+        const uint32_t p1 = bf16x2_rne(acc.v[t][2], acc.v[t][3]);
+        *(uint2*)(y + (int64_t)tk * H + n0 + 16 * t + 4 * q) = make_uint2(p0, p1);
+      }
     }
-  }
+  });
 }
 
 // ---------------------------------------------------------------- routed, few tokens
@@ -752,7 +759,7 @@ void launch_l2_ns(const DecodeArgs& a, hipStream_t s) {
   }
 }
 
-// Weight tiles per workgroup of the 9..128-token L2 kernel (32 w2 rows); the
+// Weight tiles per workgroup of the 9..512-token L2 kernel (32 w2 rows); the
 // L1 kernel holds two as well, the gate and up rows of 16 intermediate columns.
 constexpr int SK_TILES = 2;
 
@@ -811,11 +818,13 @@ void launch_routed_l2_op(const RoutedArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Every workgroup reads all m token rows, so the token traffic grows with m.
-// Up to 128 tokens (8 chunks, the register budget of the accumulators) the
-// weight stream beats the tiled GEMM, whose 256-row token tiles are half
-// padding at 128 tokens.
-constexpr int SK_MAX_TOKENS = 16 * SK_MAX_CHUNKS;
+// Every workgroup reads all m token rows, so the token traffic grows with m;
+// past 128 tokens the kernels take them in groups of 128 (the accumulators'
+// register budget) with the weights still read once. Measured on the shared
+// expert (7168 x 3072, hipGraph replay over rotating weight copies): 28.7 /
+// 40.3 / 49.7 / 62.4 / 74.0 us at 128 / 256 / 300 / 512 / 640 tokens, against
+// 51 / 64 / 69 / 77 / 71 us for the tiled GEMMs.
+constexpr int SK_MAX_TOKENS = 512;
 
 bool skinny_fits(int64_t m, int64_t hidden, int64_t inter) {
   if (m < 1 || m > SK_MAX_TOKENS) return false;

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(EW_THREADS) void k_quant_mxfp4(const uint4* __restr
       quant_pairs_e8m0<4>(w, sb, &r);
       if (u < units) {
         if constexpr (CHUNKED) {
-          // u < 2^32: the chunked layout serves at most 256 rows
+          // u < 2^32: the chunked layout serves at most 512 rows
           const uint32_t row = (uint32_t)u / row_units, i = (uint32_t)u - row * row_units;
           const uint32_t s = i >> 4, lane = ((i >> 2) & 3) * 16 + (row & 15);
           codes[(((row >> 4) * ksteps + s) * 64 + lane) * 4 + (i & 3)] = r;

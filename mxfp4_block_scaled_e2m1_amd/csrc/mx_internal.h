@@ -143,7 +143,7 @@ hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, uin
                               uint8_t* scales, hipStream_t s);
 // The same codes and scales in the chunked layout of the weight-streaming
 // kernels (rows in chunks of 16, padded with zero codes; cols % 128 == 0, rows
-// <= 256). Codes: per chunk c and 128-wide K step s one 1 KB block, lane
+// <= 512). Codes: per chunk c and 128-wide K step s one 1 KB block, lane
 // l = 16 q + r at bytes 16 l .. +15 holding columns 128 s + 32 q .. +31 of row
 // 16 c + r. Scales: the K steps are split over the kernels' STREAM_WAVES waves
 // in balanced runs (the first ksteps % STREAM_WAVES waves take one more), and
@@ -189,7 +189,7 @@ hipError_t launch_combine(const uint16_t* o, const int32_t* topk_ids, int64_t to
 // or null: the kernels then read the row-major codes. Up to 8 tokens the
 // activations are quantised in LDS; h: bf16 scratch [m, inter].
 bool decode_fits(int64_t m, int64_t hidden, int64_t inter);
-// 9 <= M <= 128: x and h quantised by the MXFP4 quantiser into the workspace in
+// 9 <= M <= 512: x and h quantised by the MXFP4 quantiser into the workspace in
 // the chunked layout (xq, hq: ceil(m/16)*16 rows), the weights streamed once by
 // two kernels that read the token rows as MFMA operands, 16 at a time.
 bool skinny_fits(int64_t m, int64_t hidden, int64_t inter);

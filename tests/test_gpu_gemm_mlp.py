@@ -32,7 +32,7 @@ def _align(n):
 
 def _ws_slices(mx, ws, M, H, I):
     """Dense workspace layout of mx_expert_mlp, each region 256-byte aligned:
-    few tokens: h (bf16 SiLU output); weight-streaming path (9..128 tokens): xq,
+    few tokens: h (bf16 SiLU output); weight-streaming path (9..512 tokens): xq,
     xs, hq, hs (chunked: whole 16-row chunks, scales per wave), h; GEMM path: xq,
     xs
     (row-major), hq, hs (both tile-major), xs_pk, and split-K partials when a
@@ -145,7 +145,7 @@ def test_tiny_expert_mlp_few_tokens(mx, M):
     assert_mlp_close(y, ref)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17, 32, 33, 96, 97, 128, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17, 32, 33, 96, 97, 128, 300, 600])
 def test_shared_expert_real_shape(mx, M):
     d = W.shared_expert(M, seed=0)
     y, sl = _run_dense(mx, d, M, 7168, 3072)
@@ -189,13 +189,14 @@ def test_few_tokens_calls_in_a_row(mx):
     assert_mlp_close(fresh[3], O.expert_mlp(W.activations(13, 3), *[d[n] for n in WN]))
 
 
-@pytest.mark.parametrize("M,H,I", [(130, 2176, 384), (200, 4224, 256), (256, 7168, 3072), (257, 7168, 3072)])
+@pytest.mark.parametrize("M,H,I", [(130, 8320, 384), (200, 8448, 256), (256, 7168, 3072), (257, 7168, 3072)])
 def test_shared_expert_split_k(mx, M, H, I):
-    """A dense L1 of one m-tile splits K over several workgroups (fp32 partials
-    summed in split order, then the usual epilogue): 2 splits of 8.5 stages
-    (H = 2176) and 4 of 16.5 (H = 4224), each ending in a half-width stage, and
-    7 splits over a full m-tile at the real shape. M = 257 (two m-tiles, the
-    second of one row) takes the unsplit path next to it."""
+    """Up to 256 tokens with hidden beyond the weight-streaming kernels' 8192,
+    the dense L1 of one m-tile splits K over several workgroups (fp32 partials
+    summed in split order, then the usual epilogue): 8 splits of 32.5 stages
+    (H = 8320, ending in a half-width stage) and of 33 (H = 8448). At the real
+    shape 256 and 257 tokens take the weight-streaming kernels in two and three
+    groups of up to 128 (the third of one row)."""
     d = W.shared_expert(M, seed=4, hidden=H, inter=I)
     y, sl = _run_dense(mx, d, M, H, I)
     ref, inter = O.expert_mlp(d["x"], d["w1"], d["w1s"], d["w3"], d["w3s"], d["w2"], d["w2s"], intermediates=True)
@@ -431,13 +432,13 @@ def test_pack_weight_codes_layout(mx, E, H, I):
 
 @pytest.mark.parametrize("M,H,I", [(16, 256, 128), (300, 384, 384), (700, 1024, 640), (1, 7168, 3072),
                                    (8, 7168, 3072), (40, 7168, 3072), (128, 7168, 3072), (200, 7168, 3072),
-                                   (4096, 7168, 3072)])
+                                   (130, 8320, 384), (4096, 7168, 3072)])
 def test_packed_codes_same_result_dense(mx, M, H, I):
     """The tile-major weight codes feed the same MFMAs the same bytes: output
     bit-identical to the row-major weights', on every path: the few-token
     kernels (1, 8), the weight-streaming kernels (16, 40: a partial last chunk
-    of a 4-chunk launch; 128), the split-K L1 (200 at 7168 x 3072, each split
-    starting mid-matrix) and the tiled GEMMs."""
+    of a 4-chunk launch; 128; 200: two token groups), the split-K L1 (130 at
+    hidden 8320, each split starting mid-matrix) and the tiled GEMMs."""
     d = W.tiny_mlp(0) if H == 256 else W.shared_expert(M, seed=12, hidden=H, inter=I)
     d["x"] = d["x"][:M]
     y0, _ = _run_dense(mx, d, M, H, I)
