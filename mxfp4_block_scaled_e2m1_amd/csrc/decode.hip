@@ -440,35 +440,86 @@ __device__ __forceinline__ void tiles_times_qtokens(const uint8_t* __restrict__ 
   }
 }
 
-// L1: chunk `wave` of each token group -> h (bf16) for 16 intermediate columns
-// j0 .. j0+15 per workgroup: tile 0 holds their gate rows (w1), tile 1 their up
-// rows (w3), so a lane holds g and u of the same (token, j) and forms
-// h = bf16(silu(g) * u) in place. pk: the tile-major L1 codes, or null.
-template <int NC, int NS>
+// L1: chunk `wave` of each token group -> h for 16 * P intermediate columns j0 ..
+// per workgroup: tiles 2p and 2p + 1 hold the gate (w1) and up (w3) rows of
+// columns j0 + 16p .. +15, so a lane holds g and u of the same (token, j) and
+// forms h = bf16(silu(g) * u) in place. pk: the tile-major L1 codes, or null.
+//  * RQ = false: h is written in bf16, row-major [m, I].
+//  * RQ = true (P = 2): a token's 32 columns j0 .. j0+31 are one MXFP4 block,
+//    held by its 4 lanes (8 values each), so the workgroup re-quantises h
+//    itself with the MXFP4 quantiser's steps (block max over the 4 lanes,
+//    the same scale and code rounding) into the chunked layout the L2 reads:
+//    hq codes and hs scales of K = I, rows up to the last whole chunk (rows
+//    past m as zero codes with scale byte 0, as the quantiser writes them).
+template <int P, int NC, int NS, bool RQ>
 __global__ __launch_bounds__(DT, 1) void k_skinny_l1(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                      int m, int H, int I, const uint8_t* __restrict__ w1,
                                                      const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ w3,
                                                      const uint8_t* __restrict__ w3s,
-                                                     const uint8_t* __restrict__ pk, uint16_t* __restrict__ h) {
-  __shared__ SkinnyLds<2, NC> L;
-  const int j0 = blockIdx.x * 16;
+                                                     const uint8_t* __restrict__ pk, uint16_t* __restrict__ h,
+                                                     uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+  static_assert(!RQ || P == 2, "a 32-column MXFP4 block needs two gate/up pairs");
+  __shared__ SkinnyLds<2 * P, NC> L;
+  const int j0 = blockIdx.x * 16 * P;
   const int kb = H / 2, ks = H / 32;
   auto wtile = [=](int t) {
-    if (pk != nullptr) return wtile_l1_packed(pk, H, j0, t == 1, j0 + 8, t == 1);
-    const uint8_t* w = t == 0 ? w1 : w3;
-    return wtile_rows(w + (int64_t)j0 * kb, w + (int64_t)(j0 + 8) * kb, kb);
+    const int j = j0 + 16 * (t >> 1);
+    if (pk != nullptr) return wtile_l1_packed(pk, H, j, (t & 1) == 1, j + 8, (t & 1) == 1);
+    const uint8_t* w = (t & 1) == 0 ? w1 : w3;
+    return wtile_rows(w + (int64_t)j * kb, w + (int64_t)(j + 8) * kb, kb);
   };
   auto srows = [=](int t) {
-    const uint8_t* s = t == 0 ? w1s : w3s;
-    return RowPair{s + (int64_t)j0 * ks, s + (int64_t)(j0 + 8) * ks};
+    const int j = j0 + 16 * (t >> 1);
+    const uint8_t* s = (t & 1) == 0 ? w1s : w3s;
+    return RowPair{s + (int64_t)j * ks, s + (int64_t)(j + 8) * ks};
   };
-  const int wave = threadIdx.x >> 6, q = (threadIdx.x & 63) >> 4;
-  tiles_times_qtokens<2, NC, NS>(xq, xs, m, H, wtile, srows, L, [&](int tk, const TileSums<2>& acc) {
-    // lane (token, q): rows 4q + v of both tiles, j = j0 + 4q + v
-    if (wave < NC && tk < m) {
-      const uint32_t p0 = bf16x2_rne(silu_mul(acc.v[0][0], acc.v[1][0]), silu_mul(acc.v[0][1], acc.v[1][1]));
-      const uint32_t p1 = bf16x2_rne(silu_mul(acc.v[0][2], acc.v[1][2]), silu_mul(acc.v[0][3], acc.v[1][3]));
-      *(uint2*)(h + (int64_t)tk * I + j0 + 4 * q) = make_uint2(p0, p1);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4;
+  const int mrows = (m + 15) / 16 * 16;   // rows of the chunked layout
+  tiles_times_qtokens<2 * P, NC, NS>(xq, xs, m, H, wtile, srows, L, [&](int tk, const TileSums<2 * P>& acc) {
+    // lane (token, q): rows 4q + v of every tile, j = j0 + 16p + 4q + v
+    uint32_t hp[2 * P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const f32x4& g = acc.v[2 * p];
+      const f32x4& u = acc.v[2 * p + 1];
+      hp[2 * p] = bf16x2_rne(silu_mul(g[0], u[0]), silu_mul(g[1], u[1]));
+      hp[2 * p + 1] = bf16x2_rne(silu_mul(g[2], u[2]), silu_mul(g[3], u[3]));
+    }
+    if constexpr (!RQ) {
+      if (wave < NC && tk < m) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+          *(uint2*)(h + (int64_t)tk * I + j0 + 16 * p + 4 * q) = make_uint2(hp[2 * p], hp[2 * p + 1]);
+      }
+    } else {
+      if (tk >= m) hp[0] = hp[1] = hp[2] = hp[3] = 0u;   // padding rows of the last chunk
+      uint32_t am = max(max(amax2(hp[0]), amax2(hp[1])), max(amax2(hp[2]), amax2(hp[3])));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+      const uint32_t sb = mx_scale_from_amax_bits(am);
+      uint32_t w;
+      quant_pairs_e8m0<4>(hp, sb, &w);   // codes of j0 + 4q .. +3 (bytes 0, 1), j0 + 16 + 4q .. +3 (2, 3)
+      if (wave < NC && tk < mrows) {
+        // the L2's K step s = j0 / 128 and lane quarter (j0 / 32) % 4
+        const int ksteps = I / 128, s = j0 >> 7, lq = (j0 >> 5) & 3, r = tk & 15, c = tk >> 4;
+        uint8_t* blk = hq + (((int64_t)c * ksteps + s) * 64 + lq * 16 + r) * 16;
+        *(uint16_t*)(blk + 2 * q) = (uint16_t)(w & 0xFFFFu);
+        *(uint16_t*)(blk + 8 + 2 * q) = (uint16_t)(w >> 16);
+        if (q == 0) {
+          // step s -> (wave w2, place k2 in its run) of the L2's balanced split
+          const int base = ksteps / DW, extra = ksteps - base * DW;
+          int w2, k2;
+          if (s < extra * (base + 1)) {
+            w2 = s / (base + 1);
+            k2 = s - w2 * (base + 1);
+          } else {
+            const int e = s - extra * (base + 1);
+            w2 = extra + e / base;
+            k2 = e - (w2 - extra) * base;
+          }
+          hs[(((int64_t)c * DW + w2) * 64 + lq * 16 + r) * 8 + k2] = (uint8_t)sb;
+        }
+      }
     }
   });
 }
@@ -763,9 +814,27 @@ void launch_l2_ns(const DecodeArgs& a, hipStream_t s) {
 // L1 kernel holds two as well, the gate and up rows of 16 intermediate columns.
 constexpr int SK_TILES = 2;
 
+// Up to 2 chunks (32 tokens) the L1 takes two gate/up pairs per workgroup and
+// re-quantises h itself, which saves the h quantiser's launch; past that the
+// halved workgroup count (96 for the expert's 3072 columns, on 256 CUs) costs
+// more than the launch, and the L1 takes one pair per workgroup and writes h
+// in bf16 for the quantiser. Measured on the shared expert (7168 x 3072): 18.9
+// against 20.5 us at 16 tokens, 20.3 against 21.1 at 32; 24.0 against 23.6 at
+// 64, 32.2 against 28.6 at 128.
+constexpr int SK_L1_FUSED_CHUNKS = 2;
+
+bool skinny_l1_fused(int m) { return (m + 15) / 16 <= SK_L1_FUSED_CHUNKS; }
+
 template <int NC, int NS>
-void launch_skinny_l1(const DecodeArgs& a, const uint8_t* xq, const uint8_t* xs, hipStream_t s) {
-  k_skinny_l1<NC, NS><<<a.I / 16, DT, 0, s>>>(xq, xs, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.pk1, a.h);
+void launch_skinny_l1(const DecodeArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
+                      hipStream_t s) {
+  if constexpr (NC <= SK_L1_FUSED_CHUNKS) {
+    k_skinny_l1<2, NC, NS, true><<<a.I / 32, DT, 0, s>>>(xq, xs, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.pk1,
+                                                          a.h, hq, hs);
+  } else {
+    k_skinny_l1<1, NC, NS, false><<<a.I / 16, DT, 0, s>>>(xq, xs, a.m, a.H, a.I, a.w1, a.w1s, a.w3, a.w3s, a.pk1,
+                                                           a.h, hq, hs);
+  }
 }
 
 template <int NC, int NS>
@@ -775,12 +844,13 @@ void launch_skinny_l2(const DecodeArgs& a, const uint8_t* hq, const uint8_t* hs,
 }
 
 template <int NC>
-void launch_skinny_l1_ns(const DecodeArgs& a, const uint8_t* xq, const uint8_t* xs, hipStream_t s) {
+void launch_skinny_l1_ns(const DecodeArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
+                         hipStream_t s) {
   switch (steps_bucket(a.H)) {
-    case 1: launch_skinny_l1<NC, 1>(a, xq, xs, s); break;
-    case 3: launch_skinny_l1<NC, 3>(a, xq, xs, s); break;
-    case 7: launch_skinny_l1<NC, 7>(a, xq, xs, s); break;
-    default: launch_skinny_l1<NC, MAX_STEPS>(a, xq, xs, s); break;
+    case 1: launch_skinny_l1<NC, 1>(a, xq, xs, hq, hs, s); break;
+    case 3: launch_skinny_l1<NC, 3>(a, xq, xs, hq, hs, s); break;
+    case 7: launch_skinny_l1<NC, 7>(a, xq, xs, hq, hs, s); break;
+    default: launch_skinny_l1<NC, MAX_STEPS>(a, xq, xs, hq, hs, s); break;
   }
 }
 
@@ -829,7 +899,7 @@ constexpr int SK_MAX_TOKENS = 512;
 bool skinny_fits(int64_t m, int64_t hidden, int64_t inter) {
   if (m < 1 || m > SK_MAX_TOKENS) return false;
   if (hidden > DW * MAX_STEPS * 128 || inter > DW * MAX_STEPS * 128) return false;
-  if (inter % 16 != 0 || hidden % (16 * SK_TILES) != 0) return false;
+  if (inter % 32 != 0 || hidden % (16 * SK_TILES) != 0) return false;
   return 16 * (hidden / 32) <= 8 * DT && 16 * (inter / 32) <= 8 * DT;
 }
 
@@ -841,12 +911,14 @@ hipError_t launch_skinny_mlp(const uint16_t* x, int m, int H, int I, const uint8
   hipError_t e = launch_quant_mxfp4_chunked(x, m, H, xq, xs, s);
   if (e != hipSuccess) return e;
   const int nc = (m + 15) / 16;
-  if (nc <= 1) launch_skinny_l1_ns<1>(a, xq, xs, s);
-  else if (nc <= 2) launch_skinny_l1_ns<2>(a, xq, xs, s);
-  else if (nc <= 4) launch_skinny_l1_ns<4>(a, xq, xs, s);
-  else launch_skinny_l1_ns<8>(a, xq, xs, s);
-  e = launch_quant_mxfp4_chunked(h, m, I, hq, hs, s);
-  if (e != hipSuccess) return e;
+  if (nc <= 1) launch_skinny_l1_ns<1>(a, xq, xs, hq, hs, s);
+  else if (nc <= 2) launch_skinny_l1_ns<2>(a, xq, xs, hq, hs, s);
+  else if (nc <= 4) launch_skinny_l1_ns<4>(a, xq, xs, hq, hs, s);
+  else launch_skinny_l1_ns<8>(a, xq, xs, hq, hs, s);
+  if (!skinny_l1_fused(m)) {
+    e = launch_quant_mxfp4_chunked(h, m, I, hq, hs, s);
+    if (e != hipSuccess) return e;
+  }
   if (nc <= 1) launch_skinny_l2_ns<1>(a, hq, hs, s);
   else if (nc <= 2) launch_skinny_l2_ns<2>(a, hq, hs, s);
   else if (nc <= 4) launch_skinny_l2_ns<4>(a, hq, hs, s);
