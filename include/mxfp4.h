@@ -152,7 +152,10 @@ MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t 
  * hidden % 128 == 0 and inter % 128 == 0.
  * requant selects the format of the intermediate h between the two GEMMs:
  *   MX_FMT_MXFP4: E8M0 per 32 (requant_global ignored); both GEMMs run on FP4
- *     matrix cores. M <= 8 takes the weight-streaming few-token kernels.
+ *     matrix cores. Up to 512 tokens the weights are streamed once by two
+ *     kernels that take the tokens as the MFMA's second operand (M <= 8:
+ *     activations quantised in LDS; 9..512: quantised beforehand, in 16-token
+ *     chunks); larger M runs the tiled GEMMs.
  *   MX_FMT_NVFP4: E4M3 per 16 with the fp32 global scale g at the DEVICE
  *     pointer requant_global (required; g finite and >= 2^-117, not checked,
  *     read in stream order, e.g. straight from mx_nvfp4_global_warmup); the L2
@@ -166,10 +169,11 @@ MX_API mx_status mx_quantize_act(mx_format fmt, const uint16_t* x_bf16, int64_t 
  * weights (E = 1, same hidden and inter), 256-byte aligned. The GEMM path then
  * reads the weight scales from it; the results are identical either way.
  * packed_codes: NULL, or the output of mx_pack_weight_codes() for these weights
- * (E = 1, same hidden and inter), 256-byte aligned: the GEMM path then copies
- * the weight codes from it (whole cache lines, one contiguous 1 KB piece per
- * copy); the results are identical either way. w1, w3 and w2 are still
- * required (the few-token kernels stream them row by row).
+ * (E = 1, same hidden and inter), 256-byte aligned: every path then reads the
+ * weight codes from it (the GEMMs copy whole 1 KB pieces, the weight-streaming
+ * kernels read 512 or 1024 contiguous bytes per 128-wide K step instead of 16
+ * separate 64-byte row pieces); the results are identical either way. w1, w3
+ * and w2 are still required.
  * workspace: device memory of at least mx_expert_mlp_workspace_size() bytes,
  * 256-byte aligned; its contents are scratch. y must not alias x or workspace.
  * Alignment: x, y, codes 16 bytes; scales and requant_global 4 bytes.

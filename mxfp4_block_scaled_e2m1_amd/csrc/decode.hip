@@ -607,7 +607,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 template <int OP, int NS, class Emit>
 __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
                                                  const int32_t* __restrict__ gather,
-                                                 int base, int rows, int K, RowPair wp, RowPair sp, RoutedLds& L,
+                                                 int base, int rows, int K, WTile wp, RowPair sp, RoutedLds& L,
                                                  Emit&& emit) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
@@ -618,9 +618,8 @@ __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq,
   int s0, n;
   wave_steps(ksteps, s0, n);
   uint4 wa[NS];
-  const uint8_t* myrow = wp.row(r16, kb);
 #pragma unroll
-  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)(myrow + min(s0 + k, ksteps - 1) * 64 + q * 16);
+  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)wp.at(r16, min(s0 + k, ksteps - 1), q);
   store_wscales(sr, ks, L.wscale);
   lds_barrier();
   int sa[NS];
@@ -700,6 +699,7 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__
                                                      const int32_t* __restrict__ expert_off, int H, int I,
                                                      const uint8_t* __restrict__ w1, const uint8_t* __restrict__ w1s,
                                                      const uint8_t* __restrict__ w3, const uint8_t* __restrict__ w3s,
+                                                     const uint8_t* __restrict__ pk, int64_t pk_estride,
                                                      uint16_t* __restrict__ h) {
   __shared__ RoutedLds L;
   const int e = blockIdx.y;
@@ -708,7 +708,8 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__
   const int j0 = blockIdx.x * 8;
   const int64_t kb = H / 2, ks = H / 32;
   const int64_t we = (int64_t)e * I * kb, se = (int64_t)e * I * ks;
-  const RowPair wp{w1 + we + j0 * kb, w3 + we + j0 * kb};
+  const WTile wp = pk != nullptr ? wtile_l1_packed(pk + e * pk_estride, H, j0, false, j0, true)
+                                 : wtile_rows(w1 + we + j0 * kb, w3 + we + j0 * kb, kb);
   const RowPair sp{w1s + se + j0 * ks, w3s + se + j0 * ks};
   routed_tile_rows<RT_FP4, NS>(xq, xs, row_token, base, rows, H, wp, sp, L, [&](int c0, const f32x4& acc) {
     const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
@@ -733,6 +734,7 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__
                                                      const float* __restrict__ row_weight, float scale_val,
                                                      const float* __restrict__ scale_ptr, int H, int I,
                                                      const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
+                                                     const uint8_t* __restrict__ pk, int64_t pk_estride,
                                                      uint16_t* __restrict__ o) {
   __shared__ RoutedLds L;
   const int e = blockIdx.y;
@@ -742,7 +744,8 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__
   const int n0 = blockIdx.x * 16;
   const int64_t kb = I / 2, ks = I / 32;
   const int64_t we = (int64_t)e * H * kb, se = (int64_t)e * H * ks;
-  const RowPair wp{w2 + we + n0 * kb, w2 + we + (n0 + 8) * kb};
+  const WTile wp = pk != nullptr ? wtile_l2_packed(pk + e * pk_estride, I, n0)
+                                 : wtile_rows(w2 + we + n0 * kb, w2 + we + (n0 + 8) * kb, kb);
   const RowPair sp{w2s + se + n0 * ks, w2s + se + (n0 + 8) * ks};
   routed_tile_rows<OP, NS>(hq, hs, nullptr, base, rows, I, wp, sp, L, [&](int c0, const f32x4& acc) {
     const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
@@ -867,13 +870,14 @@ void launch_skinny_l2_ns(const DecodeArgs& a, const uint8_t* hq, const uint8_t* 
 template <int NS>
 void launch_routed_l1_ns(const RoutedArgs& a, hipStream_t s) {
   k_routed_l1<NS><<<dim3(a.I / 8, a.E), DT, 0, s>>>(a.xq, a.xs, a.row_token, a.expert_off, a.H, a.I, a.w1, a.w1s,
-                                                      a.w3, a.w3s, a.h);
+                                                      a.w3, a.w3s, a.pk1, a.pk1_estride, a.h);
 }
 
 template <int OP, int NS>
 void launch_routed_l2_ns(const RoutedArgs& a, hipStream_t s) {
   k_routed_l2<OP, NS><<<dim3(a.H / 16, a.E), DT, 0, s>>>(a.hq, a.hs, a.expert_off, a.row_slot, a.row_weight,
-                                                          a.scale, a.scale_ptr, a.H, a.I, a.w2, a.w2s, a.o);
+                                                          a.scale, a.scale_ptr, a.H, a.I, a.w2, a.w2s, a.pk2,
+                                                          a.pk2_estride, a.o);
 }
 
 template <int OP>

@@ -650,6 +650,8 @@ mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hidden, in
     ra.row_token = w.rb.row_token; ra.row_slot = w.rb.row_slot; ra.expert_off = w.rb.expert_off;
     ra.row_weight = w.rb.row_weight;
     ra.w1 = w1; ra.w1s = w1_s; ra.w3 = w3; ra.w3s = w3_s; ra.w2 = w2; ra.w2s = w2_s;
+    ra.pk1 = packed_codes; ra.pk1_estride = pc.l1_estride;
+    ra.pk2 = packed_codes ? packed_codes + pc.l1_bytes : nullptr; ra.pk2_estride = pc.l2_estride;
     ra.h = w.h; ra.hq = w.hq; ra.hs = w.hs; ra.nvfp4 = requant == MX_FMT_NVFP4;
     ra.scale = 1.0f;
     ra.scale_ptr = requant == MX_FMT_NVFP4 ? requant_global : nullptr;

@@ -214,6 +214,8 @@ struct RoutedArgs {
   const int32_t *row_token, *row_slot, *expert_off;
   const float* row_weight;
   const uint8_t *w1, *w1s, *w3, *w3s, *w2, *w2s;
+  const uint8_t *pk1, *pk2;          // tile-major L1 / L2 codes of expert 0 (mx_pack_weight_codes), or null
+  int64_t pk1_estride, pk2_estride;  // their bytes per expert
   uint16_t* h;
   const uint8_t *hq, *hs;
   bool nvfp4;           // hq/hs are NVFP4 (E4M3 per 16), else MXFP4

@@ -404,6 +404,23 @@ def test_grouped_stream_decode_real_shape(mx):
     assert_mlp_close(_run_grouped(mx, tail, packed=True), _oracle_grouped(tail))
 
 
+@pytest.mark.parametrize("requant", ["mxfp4", "nvfp4"])
+def test_grouped_stream_packed_codes(mx, requant):
+    """The routed weight-streaming kernels read the tile-major codes when given:
+    bit-identical output, on the 16-row-chunk case (expert 0 with two chunks, the
+    last expert empty) and on 8 tokens of the real-shape batch."""
+    g = 0.05 if requant == "nvfp4" else 0.0
+    d = _stream_case(21)
+    assert np.array_equal(_run_grouped(mx, d, requant=requant, g=g),
+                          _run_grouped(mx, d, packed="all", requant=requant, g=g))
+    full = W.grouped(tokens=4096, n_experts=48, k=8, seed=0)
+    tail = dict(full, x=full["x"][:8], ids=full["ids"][:8], w=full["w"][:8])
+    y1 = _run_grouped(mx, tail, packed="all", requant=requant, g=g)
+    assert np.array_equal(_run_grouped(mx, tail, requant=requant, g=g), y1)
+    if requant == "mxfp4":
+        assert_mlp_close(y1, _oracle_grouped(tail))
+
+
 @pytest.mark.parametrize("E,H,I", [(3, 384, 256), (2, 512, 384), (1, 7168, 3072)])
 def test_pack_weight_scales_layout(mx, E, H, I):
     """mx_pack_weight_scales moves bytes only: compare with the layout written out in numpy
