@@ -248,7 +248,8 @@ MX_API mx_status mx_grouped_expert_mlp(const uint16_t* x, int64_t T, int64_t hid
                                 void* stream);
 
 /* Workspace bytes of mx_grouped_expert_mlp for these sizes (caller-owned
- * scratch, as for mx_expert_mlp_workspace_size); 0 for invalid sizes. */
+ * scratch of the pages' pre-allocated runner: "Current Bug: vLLM produces
+ * empty/garbage output", "Revised Plan", Phase 1); 0 for invalid sizes. */
 MX_API size_t mx_grouped_expert_mlp_workspace_size(int64_t T, int64_t hidden, int64_t inter, int32_t k,
                                             int32_t E, mx_format requant);
 
@@ -296,7 +297,9 @@ MX_API mx_status mx_pack_weight_codes(const uint8_t* w1, const uint8_t* w3, cons
                                       int64_t inter, int32_t E, uint8_t* packed, size_t packed_bytes,
                                       void* stream);
 
-/* Bytes of mx_pack_weight_codes' output; 0 for invalid sizes. */
+/* Bytes of mx_pack_weight_codes' output (the re-laid E2M1 codes of
+ * "2026-05-08 DeepSeek V4 Pro NVFP4 Quantization", "FP4 (E2M1) expert weight
+ * format confirmed"); 0 for invalid sizes. */
 MX_API size_t mx_packed_weight_codes_size(int64_t hidden, int64_t inter, int32_t E);
 
 /*
