@@ -162,10 +162,10 @@ hipError_t launch_nvfp4_global(const uint32_t* amax, float* g, hipStream_t s);
 
 // ---- Routing ----------------------------------------------------------------
 constexpr int ROUTE_CHUNK = 1024;    // pairs per counting/scatter block
-constexpr int ROUTE_MAX_EXPERTS = 512;   // LDS of the scatter: 19 * E ints
+constexpr int ROUTE_MAX_EXPERTS = 512;   // LDS of the scatter: 16 * E ints
 
 struct RouteBuffers {
-  int32_t* block_counts;   // [nblocks, E]
+  int32_t* block_counts;   // [nblocks, E] chunk histograms, scanned in place into chunk bases
   int32_t* expert_off;     // [E+1]
   int32_t* tile_base;      // [E+1]
   int32_t* row_token;      // [P]

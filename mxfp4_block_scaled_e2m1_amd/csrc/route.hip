@@ -7,9 +7,11 @@
 // stays in BF16 per Phase 3). Router logits and top-k selection are inputs.
 //
 // Route: pairs p = t*k + j (token t, slot j) are ordered by expert, and by p
-// within an expert (stable, so the layout is the same on every run). Two kernels:
+// within an expert (stable, so the layout is the same on every run). Three kernels:
 //   1. per-chunk expert histogram (LDS counters),
-//   2. scatter with the scan folded in (see k_route_scatter).
+//   2. one block turns the histograms into each chunk's base within every expert
+//      and the expert offsets and m-tile bases,
+//   3. scatter: every pair's place is its chunk's base plus its rank in the chunk.
 // Ids outside [0, E) belong to experts on other ranks and are skipped.
 #include "mx_device.h"
 #include "mx_internal.h"
@@ -37,35 +39,99 @@ __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__
   for (int e = threadIdx.x; e < E; e += 256) block_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
+// One block of ROUTE_SCAN_THREADS threads over the [nblocks, E] chunk
+// histograms. Thread (g, e) owns expert e in the g-th of G = threads / E
+// contiguous runs of chunks: it sums its run, the run sums are scanned over g,
+// and it rewrites its run in place as exclusive prefixes, so that
+// block_counts[c * E + e] becomes the number of expert-e pairs in chunks before
+// c. Wave 0 then scans the expert totals into expert_off (pair offsets) and
+// tile_base (offsets in m-tiles of BM rows), each with a final entry E.
+constexpr int ROUTE_SCAN_THREADS = 1024;
+static_assert(ROUTE_SCAN_THREADS >= 2 * ROUTE_MAX_EXPERTS, "two chunk runs per expert at least");
+
+__global__ __launch_bounds__(ROUTE_SCAN_THREADS) void k_route_scan(int32_t* __restrict__ block_counts,
+                                                                    int64_t nblocks, int E,
+                                                                    int32_t* __restrict__ expert_off,
+                                                                    int32_t* __restrict__ tile_base) {
+  __shared__ int part[ROUTE_SCAN_THREADS];   // [G][E] run sums, then their exclusive prefix over g
+  __shared__ int tot[ROUTE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  const int G = ROUTE_SCAN_THREADS / E;
+  const int g = tid / E, e = tid - g * E;
+  const bool on = g < G;
+  const int64_t lo = nblocks * g / G, hi = nblocks * (g + 1) / G;
+  if (on) {
+    int sum = 0;
+    for (int64_t c = lo; c < hi; ++c) sum += block_counts[c * E + e];
+    part[tid] = sum;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int acc = 0;
+    for (int x = 0; x < G; ++x) {
+      const int v = part[x * E + tid];
+      part[x * E + tid] = acc;
+      acc += v;
+    }
+    tot[tid] = acc;
+  }
+  __syncthreads();
+  if (on) {
+    int acc = part[tid];
+    for (int64_t c = lo; c < hi; ++c) {
+      const int v = block_counts[c * E + e];
+      block_counts[c * E + e] = acc;
+      acc += v;
+    }
+  }
+  if (tid < 64) {
+    // lane l scans experts [l * per, (l + 1) * per) after the lanes below it
+    const int per = (E + 63) / 64;
+    const int x0 = min(tid * per, E), x1 = min(x0 + per, E);
+    int ps = 0, ts = 0;
+    for (int x = x0; x < x1; ++x) {
+      ps += tot[x];
+      ts += (tot[x] + BM - 1) / BM;
+    }
+    int pi = ps, ti = ts;   // inclusive scans over the lanes
+    for (int d = 1; d < 64; d <<= 1) {
+      const int pu = __shfl_up(pi, d), tu = __shfl_up(ti, d);
+      if (tid >= d) {
+        pi += pu;
+        ti += tu;
+      }
+    }
+    int o = pi - ps, tb = ti - ts;
+    for (int x = x0; x < x1; ++x) {
+      expert_off[x] = o;
+      tile_base[x] = tb;
+      o += tot[x];
+      tb += (tot[x] + BM - 1) / BM;
+    }
+    if (tid == 63) {
+      expert_off[E] = pi;
+      tile_base[E] = ti;
+    }
+  }
+}
+
 // One block of ROUTE_CHUNK threads (16 waves) per chunk of pairs, one pair per
-// thread. Each block recomputes, from the chunk histograms, the expert totals
-// (-> expert offsets and m-tile bases, written by block 0) and its own base
-// within every expert. Inside the block a pair's rank among the earlier pairs
-// of its expert is the sum of the counts of the earlier waves plus its rank in
-// its own wave: lanes that share an expert find each other with a ballot and
-// count the set bits below them. Order within an expert is pair order.
+// thread. A pair's place is its expert's offset, plus the expert's pairs in
+// earlier chunks (the scanned histograms), plus its rank in this chunk: the
+// counts of the earlier waves plus its rank in its own wave, where lanes that
+// share an expert find each other with a ballot and count the set bits below
+// them. Order within an expert is pair order.
 __global__ __launch_bounds__(ROUTE_CHUNK) void k_route_scatter(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t P, int k, int E,
-    const int32_t* __restrict__ block_counts, int nblocks, int32_t* __restrict__ expert_off,
-    int32_t* __restrict__ tile_base, int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
-    float* __restrict__ row_weight) {
-  extern __shared__ int sm[];
+    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ expert_off,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot, float* __restrict__ row_weight) {
+  extern __shared__ int wc[];   // [NW][E] pairs per expert in each wave of this chunk
   constexpr int NW = ROUTE_CHUNK / 64;
-  int* tot = sm;              // [E] pairs per expert (all chunks)
-  int* pre = sm + E;          // [E] pairs per expert in earlier chunks
-  int* off = sm + 2 * E;      // [E] exclusive prefix of tot
-  int* wc = sm + 3 * E;       // [NW][E] pairs per expert in each wave of this chunk
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = blockIdx.x;
-  for (int i = tid; i < (3 + NW) * E; i += ROUTE_CHUNK) sm[i] = 0;
+  const int64_t b = blockIdx.x;
+  for (int i = tid; i < NW * E; i += ROUTE_CHUNK) wc[i] = 0;
   __syncthreads();
-  for (int i = tid; i < nblocks * E; i += ROUTE_CHUNK) {
-    const int c = block_counts[i];
-    const int e = i % E;
-    atomicAdd(&tot[e], c);
-    if (i / E < b) atomicAdd(&pre[e], c);
-  }
-  const int64_t p = (int64_t)b * ROUTE_CHUNK + tid;
+  const int64_t p = b * ROUTE_CHUNK + tid;
   const int e = (p < P) ? ids[p] : -1;
   const bool valid = (p < P) && ((unsigned)e < (unsigned)E);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -80,25 +146,8 @@ __global__ __launch_bounds__(ROUTE_CHUNK) void k_route_scatter(
     todo &= ~m;
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0, tb = 0;
-    for (int x = 0; x < E; ++x) {
-      off[x] = o;
-      if (b == 0) {
-        expert_off[x] = o;
-        tile_base[x] = tb;
-      }
-      o += tot[x];
-      tb += (tot[x] + BM - 1) / BM;
-    }
-    if (b == 0) {
-      expert_off[E] = o;
-      tile_base[E] = tb;
-    }
-  }
-  __syncthreads();
   if (valid) {
-    int pos = off[e] + pre[e] + rank;
+    int pos = expert_off[e] + chunk_base[b * E + e] + rank;
     for (int x = 0; x < w; ++x) pos += wc[x * E + e];
     row_token[pos] = (int)(p / k);
     row_slot[pos] = (int)p;
@@ -178,10 +227,10 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, int64_t to
   const int nblocks = (int)((P + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
   if (nblocks == 0) return hipSuccess;
   k_route_count<<<nblocks, 256, 0, s>>>(topk_ids, P, n_experts, rb.block_counts);
-  const size_t lds = (size_t)(3 + ROUTE_CHUNK / 64) * n_experts * sizeof(int);
-  k_route_scatter<<<nblocks, ROUTE_CHUNK, lds, s>>>(topk_ids, topk_w, P, k, n_experts, rb.block_counts, nblocks,
-                                                    rb.expert_off, rb.tile_base, rb.row_token, rb.row_slot,
-                                                    rb.row_weight);
+  k_route_scan<<<1, ROUTE_SCAN_THREADS, 0, s>>>(rb.block_counts, nblocks, n_experts, rb.expert_off, rb.tile_base);
+  const size_t lds = (size_t)(ROUTE_CHUNK / 64) * n_experts * sizeof(int);
+  k_route_scatter<<<nblocks, ROUTE_CHUNK, lds, s>>>(topk_ids, topk_w, P, k, n_experts, rb.block_counts,
+                                                    rb.expert_off, rb.row_token, rb.row_slot, rb.row_weight);
   return hipGetLastError();
 }
 
