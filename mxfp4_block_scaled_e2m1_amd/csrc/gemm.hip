@@ -363,6 +363,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const Tile& t, uint
           else if (i == 6) copy_one(h + 3, 2);
         }
       });
+      // keep all eight MFMAs of step 0 above the wait: moved below it (the
+      // wait's asm does not order register-only instructions), they leave the
+      // matrix core idle while the wave waits for its last fragment read
+      // (measured: L1 0.786 -> 0.767 ms, L2 0.432 -> 0.425 ms)
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (WAIT == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else if constexpr (WAIT == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
