@@ -1,4 +1,5 @@
-// L2 down GEMM of the NVFP4 re-quantisation variant, on bf16 matrix cores.
+// GEMMs with NVFP4 operands, on bf16 or fp16 matrix cores: the L2 down GEMM of
+// the NVFP4 re-quantisation variant (bf16) and the GEMMs of NVFP4 weights (fp16).
 //
 // The intermediate h arrives as NVFP4: E2M1 codes, one E4M3 scale per 16
 // columns and an fp32 global scale g (page "Current Bug: vLLM produces
@@ -10,21 +11,24 @@
 //
 // The scaled FP4 MFMA of gfx950 takes one E8M0 (power of two) scale per 32 K
 // values, which cannot carry an E4M3 scale per 16. Both operands are therefore
-// dequantised into bf16, exactly:
-//  * w: code * 2^(e-127) has at most 2 significant bits; exact in bf16 for
-//    scale bytes up to 252 (above that, 6 * 2^126 exceeds the bf16 range).
-//  * h: code * s with s an E4M3 value: at most 2 + 4 significant bits, exact.
-// The product sum runs in fp32 (V_MFMA_F32_32X32X16_BF16) and the epilogue
+// dequantised exactly into a 16-bit type:
+//  * MXFP4 w: code * 2^(e-127) has at most 2 significant bits; exact in bf16
+//    for scale bytes up to 252 (above that, 6 * 2^126 exceeds the bf16 range),
+//    and far outside the fp16 range, so MXFP4 weights take bf16.
+//  * NVFP4 (h, or NVFP4 w): code * s with s an E4M3 value: at most 2 + 4
+//    significant bits in [2^-10, 2688] (or 0), exact in bf16 and in fp16.
+// With NVFP4 weights both operands are fp16 (a cheaper conversion, below). The
+// product sum runs in fp32 (V_MFMA_F32_32X32X16_BF16 / _F16) and the epilogue
 // multiplies by g (and, for routed experts, by the gate weight), so
-// y = g * sum_k (code_h * s_h)(code_w * 2^e_w) up to fp32 summation order.
+// y = g * sum_k (code_h * s_h)(code_w * scale_w) up to fp32 summation order.
 //
 // Design: persistent 512-thread workgroups on 256 x 256 tiles, the same tile
 // order and XCD mapping as the FP4 kernel. Per 64-wide K stage each thread
 // loads 16 code bytes of one weight row and 16 of one token row (plus their
-// scale bytes) into registers two stages ahead, and after the MFMAs of the
-// current stage converts the next stage's bytes and writes the bf16 tile into
-// the other of two 64 KB LDS slots. Every operand element is converted once
-// per workgroup.
+// scale bytes) into registers two stages ahead, and in the current stage
+// converts the next stage's bytes (before or after its MFMAs, by wave) and
+// writes the 16-bit tile into the other of two 64 KB LDS slots. Every operand
+// element is converted once per workgroup.
 #include "gemm_common.h"
 #include "nv_linear.h"
 
@@ -91,6 +95,36 @@ __device__ __forceinline__ uint4 h_to_bf16(uint32_t d, float s) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// NVFP4 codes -> fp16 for one dword (8 columns) with block scale s (an E4M3
+// value, exact in fp16): unit-scale conversion, then one packed fp16 multiply
+// per pair. code * s has at most 6 significant bits and lies in [2^-10, 2688]
+// (or is 0), so it is exact and normal in fp16. The scaled conversion
+// instruction applies only the power of two of its scale operand (measured on
+// gfx950 over all codes and E4M3 scales), so s cannot go into it.
+__device__ __forceinline__ uint4 nv_to_f16(uint32_t d, _Float16 s) {
+  const f16x2 sc = {s, s};
+  f16x2 v[4];
+  v[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sc;
+  v[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sc;
+  v[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sc;
+  v[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sc;
+  return make_uint4(__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                    __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3]));
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(const uint4& v) { return __builtin_bit_cast(f16x8, v); }
+
+// One MFMA of a K step: fp16 operands when both are NVFP4 (NVW), bf16 when the
+// weights are MXFP4 (their E8M0 scales reach far outside the fp16 range).
+template <bool NVW>
+__device__ __forceinline__ f32x16 nv_mfma(const uint4& a, const uint4& b, const f32x16& c) {
+  if constexpr (NVW) return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 // One 256 x 256 tile of o = g * h . w^T (h NVFP4; w MXFP4, or NVFP4 when NVW,
 // whose E4M3 scales [rows, k/16] are in wa_s and whose global scale is folded
 // into g by the caller).
@@ -148,10 +182,12 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
     const uint32_t wd[4] = {r.wc.x, r.wc.y, r.wc.z, r.wc.w};
     const uint32_t hd[4] = {r.hc.x, r.hc.y, r.hc.z, r.hc.w};
     const float s0 = e4m3_to_f32(r.hs & 0xFFu), s1 = e4m3_to_f32(r.hs >> 8);
-    float w0 = 0.f, w1 = 0.f;
+    _Float16 w0 = 0, w1 = 0, t0 = 0, t1 = 0;
     if constexpr (NVW) {
-      w0 = e4m3_to_f32(r.we & 0xFFu);
-      w1 = e4m3_to_f32(r.we >> 8);
+      w0 = (_Float16)e4m3_to_f32(r.we & 0xFFu);
+      w1 = (_Float16)e4m3_to_f32(r.we >> 8);
+      t0 = (_Float16)s0;
+      t1 = (_Float16)s1;
     }
     // store i writes chunk half*4 + (i ^ swap): odd rows swap the chunks of each
     // pair (a pair shares its E4M3 scale), so the 8 lanes of rows 4q .. 4q+3
@@ -162,9 +198,13 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
       const int c = half * 4 + (i ^ (swap ? 1 : 0));
       const uint32_t wdi = swap ? wd[i ^ 1] : wd[i];
       const uint32_t hdi = swap ? hd[i ^ 1] : hd[i];
-      if constexpr (NVW) *(uint4*)(wt + nv_off(R, c)) = h_to_bf16(wdi, i < 2 ? w0 : w1);
-      else *(uint4*)(wt + nv_off(R, c)) = w_to_bf16(wdi, r.we);
-      *(uint4*)(ht + nv_off(R, c)) = h_to_bf16(hdi, i < 2 ? s0 : s1);
+      if constexpr (NVW) {
+        *(uint4*)(wt + nv_off(R, c)) = nv_to_f16(wdi, i < 2 ? w0 : w1);
+        *(uint4*)(ht + nv_off(R, c)) = nv_to_f16(hdi, i < 2 ? t0 : t1);
+      } else {
+        *(uint4*)(wt + nv_off(R, c)) = w_to_bf16(wdi, r.we);
+        *(uint4*)(ht + nv_off(R, c)) = h_to_bf16(hdi, i < 2 ? s0 : s1);
+      }
     }
   };
 
@@ -182,27 +222,75 @@ __device__ __forceinline__ void nv_tile(const GemmArgs& a, const Tile& t, uint8_
   // raw bytes of two stages in flight: stage st+2 is loaded while stage st is
   // multiplied and stage st+1 converted, so the loads have two stages of MFMAs
   // to arrive in. `cur` held stage st (already in LDS), `nxt` holds stage st+1.
-  auto stage = [&](int st, NvRaw& cur, NvRaw& nxt) {
-    if (st + 2 < nst) load(st + 2, cur);
+  // The load is unconditional (the last two stages re-read stage nst-1): with a
+  // branch around it, the compiler's wait before the conversion was vmcnt(0),
+  // a wait for the loads of stage st+2 just issued.
+  // One stage's 32 MFMAs per wave (4 K steps of 16). The fragments of step
+  // k16+1 are read between the MFMAs of step k16: token fragment g after MFMA
+  // 2g, weight fragment f after MFMA 2f+1, the last one that reads the register
+  // it replaces (so the weight fragments need one register set, the token
+  // fragments two). Every read then has at least five MFMAs of this wave before
+  // its first use; only the first step of a stage waits for its reads.
+  auto mfmas = [&](int st) {
     const uint8_t* wt = smem + (st & 1) * NV_SLOT;
     const uint8_t* ht = wt + NV_OPND;
-    if (act) {
+    // rows wn*128 + f*32 + r32 and wm*64 + g*32 + r32 all have the swizzle of
+    // r32 (it depends on row bits 1..3 only): a fragment's address is a lane
+    // base, an immediate row offset and the swizzled chunk of the step
+    const int swz = nv_swz(r32);
+    const uint8_t* wb = wt + (wn * 128 + r32) * NV_ROW;
+    const uint8_t* hb = ht + (wm * 64 + r32) * NV_ROW;
+    uint4 A[4], B[2][2];
 #pragma unroll
-      for (int k16 = 0; k16 < NV_BK / 16; ++k16) {
-        const int c = k16 * 2 + hh;   // lane half hh holds K values 8*hh .. 8*hh+7 of the step
-        uint4 A[4], B[2];
+    for (int f = 0; f < 4; ++f) A[f] = *(const uint4*)(wb + f * 32 * NV_ROW + ((hh ^ swz) << 4));
 #pragma unroll
-        for (int f = 0; f < 4; ++f) A[f] = *(const uint4*)(wt + nv_off(wn * 128 + f * 32 + r32, c));
+    for (int g = 0; g < 2; ++g) B[0][g] = *(const uint4*)(hb + g * 32 * NV_ROW + ((hh ^ swz) << 4));
 #pragma unroll
-        for (int g = 0; g < 2; ++g) B[g] = *(const uint4*)(ht + nv_off(wm * 64 + g * 32 + r32, c));
+    for (int k16 = 0; k16 < NV_BK / 16; ++k16) {
+      const int p = k16 & 1, q = p ^ 1;
+      // chunk of step k16+1: lane half hh holds K values 8*hh .. 8*hh+7 of a step
+      const int co = (((k16 + 1) * 2 + hh) ^ swz) << 4;
+      const bool more = k16 + 1 < NV_BK / 16;
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[f]), as_bf16x8(B[g]), acc[f][g], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const int f = i >> 1, g = i & 1;
+        acc[f][g] = nv_mfma<NVW>(A[f], B[p][g], acc[f][g]);
+        if (more) {
+          if (i == 0) B[q][0] = *(const uint4*)(hb + co);
+          else if (i == 2) B[q][1] = *(const uint4*)(hb + 32 * NV_ROW + co);
+          if (g == 1) A[f] = *(const uint4*)(wb + f * 32 * NV_ROW + co);
+        }
+      }
+      if (more) {
+        // MFMA 0, B0, MFMA 1, A0, MFMA 2, B1, MFMA 3, A1, MFMA 4, MFMA 5, A2, MFMA 6, MFMA 7, A3
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
-    if (st + 1 < nst) store((st + 1) & 1, nxt);   // the other slot: its last reads were before the previous barrier
+  };
+  // Waves w and w + 4 share a SIMD. In every stage waves 0-3 run their MFMAs
+  // before converting the next stage and waves 4-7 after it, so that on each
+  // SIMD one wave's conversion (VALU work) overlaps the other wave's MFMAs,
+  // instead of all eight waves converting while the matrix cores idle. The
+  // conversion writes the other slot (its last reads were before the previous
+  // barrier) and the MFMAs read this stage's slot, so the order is free.
+  const bool conv_first = wave >= 4;
+  auto stage = [&](int st, NvRaw& cur, NvRaw& nxt) {
+    load(min(st + 2, nst - 1), cur);   // unconditional: see below
+    const bool conv = st + 1 < nst;
+    if (conv_first && conv) store((st + 1) & 1, nxt);
+    if (act) mfmas(st);
+    if (!conv_first && conv) store((st + 1) & 1, nxt);
     __syncthreads();
   };
   NvRaw ra, rb;

@@ -148,13 +148,15 @@ __device__ __forceinline__ uint32_t e4m3_rne_satfinite(float r) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// E4M3 (e4m3fn) byte -> fp32, exact; 0x7F and 0xFF give the NaN 0x7FC00000.
+// Selects only (no branches), so that it can be scheduled among MFMAs.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  uint32_t s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
-  float mag;
-  if (e == 15u && m == 7u) return __uint_as_float(0x7FC00000u);
-  if (e == 0u) mag = (float)m * 0x1p-9f;
-  else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return s ? -mag : mag;
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float sub = (float)m * 0x1p-9f;
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float mag = e == 0u ? sub : nrm;
+  const float v = (b & 0x80u) ? -mag : mag;
+  return (e == 15u && m == 7u) ? __uint_as_float(0x7FC00000u) : v;
 }
 
 // silu(g) * u = g / (1 + e^-g) * u in fp32 with the hardware exp2 and
