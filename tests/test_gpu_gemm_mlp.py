@@ -264,6 +264,44 @@ def test_grouped_permutation_empty_and_foreign_ids(mx):
     assert_mlp_close(y2, _oracle_grouped(d2))
 
 
+@pytest.mark.parametrize("E,k,T", [(1, 1, 1 << 20), (7, 4, 1 << 18), (512, 8, 1 << 17)])
+def test_route_many_chunks(mx, E, k, T):
+    """The route at 2^20 pairs (1024 chunks of 1024): one expert (the scan's
+    1024 runs of one chunk), 7 (runs of 7 experts, which do not divide the
+    scan block) and 512 (two runs of 512 chunks), with 2 % of the ids outside
+    [0, E). Expert offsets, m-tile bases and every sorted row's token, slot and
+    gate weight against a stable sort of the pairs by expert (the route of
+    "Current Bug: vLLM produces empty/garbage output", "Revised Plan", Phase 1:
+    pairs in expert order, pair order within an expert)."""
+    from gpu_util import routed_ws_slices
+    H = I = 128
+    rng = np.random.default_rng(E)
+    d = W.expert_weights(3, H, I, E)
+    d["x"] = W.activations(4, T, H)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    foreign = rng.random((T, k)) < 0.02
+    ids[foreign] = rng.choice(np.array([-1, E, E + 5], np.int32), int(foreign.sum()))
+    w = rng.random((T, k)).astype(np.float32)
+    wd = [t(d[n]) for n in WN]
+    ws = torch.empty(mx.grouped_expert_mlp_workspace_size(T, H, I, k, E), dtype=torch.uint8, device="cuda")
+    mx.grouped_expert_mlp(bf16_t(d["x"]), t(ids), t(w), *wd, workspace=ws)
+    torch.cuda.synchronize()
+    s = routed_ws_slices(ws, T, H, I, k, E)
+    flat = ids.ravel()
+    valid = (flat >= 0) & (flat < E)
+    p = np.nonzero(valid)[0]
+    order = p[np.argsort(flat[p], kind="stable")]
+    counts = np.bincount(flat[valid], minlength=E)
+    eo = np.concatenate([[0], np.cumsum(counts)])
+    tb = np.concatenate([[0], np.cumsum((counts + 255) // 256)])
+    assert np.array_equal(s["expert_off"], eo)
+    assert np.array_equal(s["tile_base"], tb)
+    n = int(eo[-1])
+    assert np.array_equal(s["row_slot"][:n], order)
+    assert np.array_equal(s["row_token"][:n], order // k)
+    assert np.array_equal(s["row_weight"][:4 * n].view(np.float32), w.ravel()[order])
+
+
 def test_grouped_headline_sampled_tokens(mx):
     d = W.grouped(tokens=4096, n_experts=48, k=8, seed=0)
     y = _run_grouped(mx, d, packed=True)
