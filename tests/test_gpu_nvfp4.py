@@ -244,6 +244,18 @@ def test_nvfp4_linear_matches_oracle(mx, M, N, K):
     _nv_linear_check(bits(y), d)
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 256, 512), (300, 384, 1024)])
+def test_nvfp4_linear_full_e4m3_range(mx, M, N, K):
+    """Weight scales over every finite E4M3 byte and activation blocks over
+    2^-20 .. 2^4 (their scales reach zero, the subnormals and 448): the fp16
+    operands code x scale of the NVFP4-weight GEMM are exact and normal over
+    that whole range (6 x 448 at most, 2^-10 at least), so the same bars hold."""
+    d = W.nvfp4_linear_wide(M, N, K, seed=M + K)
+    y = mx.nvfp4_linear(bf16_t(d["x"]), t(d["w"]), t(d["ws"]), float(d["wg"]), float(d["xg"]))
+    torch.cuda.synchronize()
+    _nv_linear_check(bits(y), d)
+
+
 def test_nvfp4_linear_real_shape_sampled_rows(mx):
     """4096 tokens through the down projection's shape [7168, 3072]; rows from every m-tile."""
     d = W.nvfp4_linear(4096, seed=0)

@@ -199,6 +199,19 @@ def nvfp4_linear(tokens, n=HIDDEN, k=INTER, seed=0):
     return dict(w=w, ws=ws, wg=np.float32(2.0 ** -6), x=activations(seed + 1, tokens, k), xg=np.float32(2.0 ** -9))
 
 
+def nvfp4_linear_wide(tokens, n, k, seed=0):
+    """``nvfp4_linear`` with the E4M3 weight scales uniform over every finite
+    byte (0x00 .. 0x7E: zero, the subnormals up to 448) and each 16-block of
+    activations N(0, 1) times 2^e, e uniform in -20 .. 4, so that the
+    activations' own block scales reach zero, the subnormals and saturation."""
+    rng = np.random.default_rng(seed)
+    w = rng.integers(0, 256, (n, k // 2)).astype(np.uint8)
+    ws = rng.integers(0x00, 0x7F, (n, k // 16)).astype(np.uint8)
+    e = rng.integers(-20, 5, (tokens, k // 16)).repeat(16, axis=1)
+    x = _bf16_bits((rng.standard_normal((tokens, k)) * np.exp2(e)).astype(np.float32))
+    return dict(w=w, ws=ws, wg=np.float32(2.0 ** -6), x=x, xg=np.float32(2.0 ** -9))
+
+
 def nvfp4_expert(tokens, hidden=HIDDEN, inter=INTER, seed=0):
     """One expert with NVFP4 weights: codes and E4M3 scales as ``nvfp4_linear``,
     weight globals 2^-6 (w1), 2^-5 (w3, a different one: the dual gate/up
