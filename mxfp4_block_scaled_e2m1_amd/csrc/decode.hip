@@ -376,6 +376,18 @@ __device__ __forceinline__ void tiles_times_qtokens(const uint8_t* __restrict__ 
   uint4 b[2][NS];
   uint2 bsc[2];
   const int nchunks = (m + 15) / 16, last_chunk = nchunks - 1;
+  // this lane's weight scale bytes (row r16, quarter q of each step of the
+  // run) are the same for every token chunk: read from LDS once into registers
+  // when they fit (up to 16: two tiles of up to 8 steps), else per chunk
+  constexpr bool HOIST = MT * NS <= 16;
+  auto wsc_byte = [&](int t, int k) { return (int)L.wscale[t][r16 * ks + min(s0 + k, ksteps - 1) * 4 + q]; };
+  int sar[HOIST ? MT : 1][HOIST ? NS : 1];
+  if constexpr (HOIST) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int k = 0; k < NS; ++k) sar[t][k] = wsc_byte(t, k);
+  }
   auto load_chunk = [&](int c, uint4 (&bb)[NS], uint2& ss) {
     const int cc = min(c, last_chunk);
 #pragma unroll
@@ -407,9 +419,8 @@ __device__ __forceinline__ void tiles_times_qtokens(const uint8_t* __restrict__ 
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           const uint4 az = k < n ? wa[t][k] : z;
-          const int sa = L.wscale[t][r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
           acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(b[c & 1][k]), acc[c][t], 4, 4,
-                                                                       0, sa, 0, sb);
+                                                                       0, HOIST ? sar[HOIST ? t : 0][HOIST ? k : 0] : wsc_byte(t, k), 0, sb);
         }
       }
       // keep the loads of later chunks where they are written (one chunk ahead):
