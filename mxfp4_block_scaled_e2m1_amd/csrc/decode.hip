@@ -321,8 +321,9 @@ __global__ __launch_bounds__(DT, 1) void k_decode_l2(const uint16_t* __restrict_
 // pieces 3.5 KB apart (measured nearly twice as slow at 64..128 tokens), and a
 // scale byte per step costs the address unit as much as a code load. A workgroup holds MT 16-row weight tiles; a wave keeps its
 // K run of every tile in registers and walks the NC token chunks, the loads of
-// chunks c+1 and c+2 in flight during the MFMAs of chunk c (one chunk ahead
-// measured 2-5 % slower from 128 tokens on), each chunk's token operands
+// the next two chunks (three for runs of up to 3 K steps, whose registers
+// allow it) in flight during the MFMAs of chunk c (one chunk ahead measured
+// 2-5 % slower from 128 tokens on), each chunk's token operands
 // feeding the MT tiles' MFMAs. The 8 waves' partial sums meet in LDS and wave
 // c finishes chunk c. Every workgroup reads all m token rows, so MT = 2 halves
 // the token bytes per weight byte (and the workgroups: one round over the CUs
@@ -374,8 +375,9 @@ __device__ __forceinline__ void tiles_times_qtokens(const uint8_t* __restrict__ 
   // token operands of chunk c: the lane's 16 bytes of each (chunk, step) code
   // block (the padding rows of the last chunk hold zero codes) and its 8 scale
   // bytes of the wave's run, step k in byte k
-  uint4 b[3][NS];
-  uint2 bsc[3];
+  constexpr int PD = NS <= 3 ? 3 : 2;   // chunks in flight ahead of the MFMAs
+  uint4 b[PD + 1][NS];
+  uint2 bsc[PD + 1];
   const int nchunks = (m + 15) / 16, last_chunk = nchunks - 1;
   // this lane's weight scale bytes (row r16, quarter q of each step of the
   // run) are the same for every token chunk: read from LDS once into registers
@@ -406,26 +408,27 @@ __device__ __forceinline__ void tiles_times_qtokens(const uint8_t* __restrict__ 
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    load_chunk(c0, b[0], bsc[0]);
-    if (NC > 1) load_chunk(c0 + 1, b[1], bsc[1]);
+#pragma unroll
+    for (int c = 0; c < PD; ++c)
+      if (c < NC) load_chunk(c0 + c, b[c], bsc[c]);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (c + 2 < NC) load_chunk(c0 + c + 2, b[(c + 2) % 3], bsc[(c + 2) % 3]);
+      if (c + PD < NC) load_chunk(c0 + c + PD, b[(c + PD) % (PD + 1)], bsc[(c + PD) % (PD + 1)]);
       // steps past the wave's run (k >= n) multiply zero codes: no branch around
       // the MFMAs, which would make the compiler copy the accumulators; their
       // token scale bytes are not written by the quantiser, so 2^0 stands in
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        const int sb = k < n ? (int)((k < 4 ? bsc[c % 3].x : bsc[c % 3].y) >> (8 * (k & 3))) : 0x7F;
+        const int sb = k < n ? (int)((k < 4 ? bsc[c % (PD + 1)].x : bsc[c % (PD + 1)].y) >> (8 * (k & 3))) : 0x7F;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           const uint4 az = k < n ? wa[t][k] : z;
-          acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(b[c % 3][k]), acc[c][t], 4, 4,
+          acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(b[c % (PD + 1)][k]), acc[c][t], 4, 4,
                                                                        0, HOIST ? sar[HOIST ? t : 0][HOIST ? k : 0] : wsc_byte(t, k), 0, sb);
         }
       }
-      // keep the loads of later chunks where they are written (two chunks ahead):
+      // keep the loads of later chunks where they are written (PD chunks ahead):
       // hoisting them all would hold every chunk's operands in registers
       __builtin_amdgcn_sched_barrier(0);
     }
