@@ -60,9 +60,20 @@ __global__ __launch_bounds__(ROUTE_SCAN_THREADS) void k_route_scan(int32_t* __re
   const int g = tid / E, e = tid - g * E;
   const bool on = g < G;
   const int64_t lo = nblocks * g / G, hi = nblocks * (g + 1) / G;
+  // runs can be long (16384 chunks of 48 experts: ~780 per thread), so the
+  // loads go eight at a time, independent of the sums
+  constexpr int U = 8;
   if (on) {
     int sum = 0;
-    for (int64_t c = lo; c < hi; ++c) sum += block_counts[c * E + e];
+    int64_t c = lo;
+    for (; c + U <= hi; c += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = block_counts[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) sum += v[u];
+    }
+    for (; c < hi; ++c) sum += block_counts[c * E + e];
     part[tid] = sum;
   }
   __syncthreads();
@@ -78,7 +89,18 @@ __global__ __launch_bounds__(ROUTE_SCAN_THREADS) void k_route_scan(int32_t* __re
   __syncthreads();
   if (on) {
     int acc = part[tid];
-    for (int64_t c = lo; c < hi; ++c) {
+    int64_t c = lo;
+    for (; c + U <= hi; c += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = block_counts[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        block_counts[(c + u) * E + e] = acc;
+        acc += v[u];
+      }
+    }
+    for (; c < hi; ++c) {
       const int v = block_counts[c * E + e];
       block_counts[c * E + e] = acc;
       acc += v;
