@@ -576,10 +576,11 @@ __global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__
 // holding a handful of rows and wait out one copy latency per K stage, so the
 // weights are streamed once instead, as on the dense few-token path. The rows
 // of expert e are the sorted pair rows expert_off[e] .. expert_off[e+1] of the
-// route kernels. Grid: (16-row weight tiles) x (experts); the workgroups of
-// experts without rows leave at once. A workgroup keeps its weight tile in
-// registers (each wave a run of K steps) and multiplies it by the expert's
-// rows 16 at a time; the 8 waves' partial sums meet in LDS in wave order.
+// route kernels. Grid: (groups of RT_TILES 16-row weight tiles) x (experts);
+// the workgroups of experts without rows leave at once. A workgroup keeps its
+// weight tiles in registers (each wave a run of K steps) and multiplies them
+// by the expert's rows 16 at a time; the 8 waves' partial sums meet in LDS and
+// wave t adds those of tile t in wave order.
 //  * L1 gathers the MXFP4 token rows by row_token and writes h (bf16) in
 //    sorted row order.
 //  * L2 reads re-quantised h rows in sorted order: MXFP4 codes through the
@@ -592,9 +593,12 @@ __global__ __launch_bounds__(DT, 1) void k_skinny_l2(const uint8_t* __restrict__
 //    the GEMM's epilogue.
 enum RoutedOperand { RT_FP4 = 0, RT_NV = 1 };
 
+// MT tiles of 16 weight rows per workgroup; the partial sums of one chunk of
+// 16 token rows at a time.
+template <int MT>
 struct RoutedLds {
-  uint8_t wscale[16 * 256];     // the tile rows' E8M0 bytes, K <= 8192
-  f32x4 red[2][DW][64];         // partial sums per chunk parity, wave, lane
+  uint8_t wscale[MT][16 * 256];   // the tiles' E8M0 bytes, K <= 8192
+  f32x4 red[DW][MT][64];          // partial sums per wave, tile, lane
 };
 
 __device__ __forceinline__ uint4 dequant16_bf16(uint32_t codes, float scale) {
@@ -615,39 +619,54 @@ __device__ __forceinline__ uint4 nv8_bf16(uint32_t d, float s) {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-// The expert's `rows` token rows times one 16-row weight tile. Token row i of
-// the expert is row gather[base + i] (gather != nullptr) or base + i of the
-// operand: FP4 codes `aq` [.., K/2] with E8M0 scales `as` [.., K/32] (RT_FP4)
-// or E4M3 scales `as` [.., K/16] (RT_NV). `emit(c0, tot)` runs in wave 0 for every chunk of 16 rows
-// starting at c0, with lane (row c0 + lane%16, tile rows 4*(lane/16) + v).
-template <int OP, int NS, class Emit>
+// The expert's `rows` token rows times MT 16-row weight tiles, tile t's codes
+// at wtile(t) and scale rows at srows(t) (by value, as on the dense path).
+// Token row i of the expert is row gather[base + i] (gather != nullptr) or
+// base + i of the operand: FP4 codes `aq` [.., K/2] with E8M0 scales `as`
+// [.., K/32] (RT_FP4) or E4M3 scales `as` [.., K/16] (RT_NV). A lane's token
+// operand of a step is loaded (and, for RT_NV, converted to bf16) once and
+// serves all MT tiles. `emit(c0, t, tot)` runs in wave t (MT <= DW) for every
+// chunk of 16 rows starting at c0, with lane (row c0 + lane%16, rows
+// 4*(lane/16) + v of tile t).
+template <int OP, int NS, int MT, class WTiles, class SRows, class Emit>
 __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
                                                  const int32_t* __restrict__ gather,
-                                                 int base, int rows, int K, WTile wp, RowPair sp, RoutedLds& L,
-                                                 Emit&& emit) {
+                                                 int base, int rows, int K, WTiles wtile, SRows srows,
+                                                 RoutedLds<MT>& L, Emit&& emit) {
+  static_assert(MT <= DW, "one wave per tile reduces the partial sums");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int kb = K / 2, ks = K / 32, ksteps = K / 128;
 
-  ScaleRegs sr;
-  load_wscales(sp, ks, sr);
+  ScaleRegs sr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) load_wscales(srows(t), ks, sr[t]);
   int s0, n;
   wave_steps(ksteps, s0, n);
-  uint4 wa[NS];
+  uint4 wa[MT][NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) wa[k] = *(const uint4*)wp.at(r16, min(s0 + k, ksteps - 1), q);
-  store_wscales(sr, ks, L.wscale);
+  for (int t = 0; t < MT; ++t) {
+    const WTile w = wtile(t);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) wa[t][k] = *(const uint4*)w.at(r16, min(s0 + k, ksteps - 1), q);
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) store_wscales(sr[t], ks, L.wscale[t]);
   lds_barrier();
-  int sa[NS];
+  int sa[MT][NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) sa[k] = L.wscale[r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int k = 0; k < NS; ++k) sa[t][k] = L.wscale[t][r16 * ks + min(s0 + k, ksteps - 1) * 4 + q];
 
-  for (int c0 = 0, par = 0; c0 < rows; c0 += 16, par ^= 1) {
+  for (int c0 = 0; c0 < rows; c0 += 16) {
     const int i = min(c0 + r16, rows - 1);
     const int64_t tok = gather != nullptr ? (int64_t)gather[base + i] : (int64_t)(base + i);
     const bool tok_ok = c0 + r16 < rows;
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (OP == RT_FP4) {
       uint4 b[NS];
       int sb[NS];
@@ -662,14 +681,18 @@ __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq,
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         const uint4 bz = tok_ok ? b[k] : z;
-        const uint4 az = k < n ? wa[k] : z;
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc, 4, 4, 0, sa[k], 0, sb[k]);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const uint4 az = k < n ? wa[t][k] : z;
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc[t], 4, 4, 0, sa[t][k],
+                                                                     0, sb[k]);
+        }
       }
     } else {
       // A lane's 32 K values of a step (K = 128 s + 32 q + 0..31, code dwords
       // j = 0..3 of 8 values each, NVFP4 blocks j / 2) feed four 16x16x32
-      // MFMAs, dword j in the j-th; the token row uses the same order, so each
-      // MFMA contracts matching K.
+      // MFMAs per tile, dword j in the j-th; the token row uses the same
+      // order, so each MFMA contracts matching K.
       uint4 b[NS];
       uint32_t bs[NS];
 #pragma unroll
@@ -680,36 +703,42 @@ __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq,
       }
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
-        const float scale = e8m0_to_f32((uint32_t)sa[k]);
-        const uint32_t wv[4] = {wa[k].x, wa[k].y, wa[k].z, wa[k].w};
         const uint32_t hv[4] = {b[k].x, b[k].y, b[k].z, b[k].w};
         const float hs0 = e4m3_to_f32(bs[k] & 0xFFu), hs1 = e4m3_to_f32(bs[k] >> 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint4 av = k < n ? dequant16_bf16(wv[j], scale) : z;
           const uint4 bv = tok_ok ? nv8_bf16(hv[j], j < 2 ? hs0 : hs1) : z;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                        __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const uint32_t wv[4] = {wa[t][k].x, wa[t][k].y, wa[t][k].z, wa[t][k].w};
+            const uint4 av = k < n ? dequant16_bf16(wv[j], e8m0_to_f32((uint32_t)sa[t][k])) : z;
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                             __builtin_bit_cast(bf16x8_t, bv), acc[t], 0, 0, 0);
+          }
         }
       }
     }
-    L.red[par][wave][lane] = acc;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) L.red[wave][t][lane] = acc[t];
     __syncthreads();
-    if (wave == 0) {
+    if (wave < MT) {
       f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < DW; ++w) {
-        const f32x4 o = L.red[par][w][lane];
+        const f32x4 o = L.red[w][wave][lane];
         tot[0] += o[0]; tot[1] += o[1]; tot[2] += o[2]; tot[3] += o[3];
       }
-      emit(c0, tot);
+      emit(c0, wave, tot);
     }
+    // the next chunk overwrites the partial sums
+    if (c0 + 16 < rows) __syncthreads();
   }
 }
 
-// L1 of expert blockIdx.y for 8 intermediate columns j0 .. j0+7 (tile rows
-// 0..7 of w1, 8..15 of w3): h[r][j] = bf16(silu(g) * u) for its sorted rows r.
-template <int NS>
+// L1 of expert blockIdx.y for 8 MT intermediate columns from j0 (tile t: rows
+// 0..7 of w1 and 8..15 of w3 for columns j0 + 8 t ..): h[r][j] =
+// bf16(silu(g) * u) for its sorted rows r.
+template <int NS, int MT>
 __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                      const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ expert_off, int H, int I,
@@ -717,17 +746,24 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__
                                                      const uint8_t* __restrict__ w3, const uint8_t* __restrict__ w3s,
                                                      const uint8_t* __restrict__ pk, int64_t pk_estride,
                                                      uint16_t* __restrict__ h) {
-  __shared__ RoutedLds L;
+  __shared__ RoutedLds<MT> L;
   const int e = blockIdx.y;
   const int base = expert_off[e], rows = expert_off[e + 1] - base;
   if (rows <= 0) return;
-  const int j0 = blockIdx.x * 8;
+  const int j0 = blockIdx.x * 8 * MT;
   const int64_t kb = H / 2, ks = H / 32;
   const int64_t we = (int64_t)e * I * kb, se = (int64_t)e * I * ks;
-  const WTile wp = pk != nullptr ? wtile_l1_packed(pk + e * pk_estride, H, j0, false, j0, true)
-                                 : wtile_rows(w1 + we + j0 * kb, w3 + we + j0 * kb, kb);
-  const RowPair sp{w1s + se + j0 * ks, w3s + se + j0 * ks};
-  routed_tile_rows<RT_FP4, NS>(xq, xs, row_token, base, rows, H, wp, sp, L, [&](int c0, const f32x4& acc) {
+  auto wtile = [&](int t) {
+    const int j = j0 + 8 * t;
+    return pk != nullptr ? wtile_l1_packed(pk + e * pk_estride, H, j, false, j, true)
+                         : wtile_rows(w1 + we + j * kb, w3 + we + j * kb, kb);
+  };
+  auto srows = [&](int t) {
+    const int j = j0 + 8 * t;
+    return RowPair{w1s + se + j * ks, w3s + se + j * ks};
+  };
+  routed_tile_rows<RT_FP4, NS, MT>(xq, xs, row_token, base, rows, H, wtile, srows, L,
+                                   [&](int c0, int tile, const f32x4& acc) {
     const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
     float up[4];
 #pragma unroll
@@ -735,15 +771,15 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__
     if (q < 2 && c0 + t < rows) {
       const uint32_t p0 = bf16x2_rne(silu_mul(acc[0], up[0]), silu_mul(acc[1], up[1]));
       const uint32_t p1 = bf16x2_rne(silu_mul(acc[2], up[2]), silu_mul(acc[3], up[3]));
-      *(uint2*)(h + (int64_t)(base + c0 + t) * I + j0 + 4 * q) = make_uint2(p0, p1);
+      *(uint2*)(h + (int64_t)(base + c0 + t) * I + j0 + 8 * tile + 4 * q) = make_uint2(p0, p1);
     }
   });
 }
 
-// L2 of expert blockIdx.y for 16 output columns n0 .. n0+15, from the
-// re-quantised h rows (FP4 codes + E8M0 or E4M3 scales): o[row_slot[r]][n] =
-// bf16(acc * (scale * row_weight[r])).
-template <int OP, int NS>
+// L2 of expert blockIdx.y for 16 MT output columns from n0 (tile t: n0 + 16 t
+// ..), from the re-quantised h rows (FP4 codes + E8M0 or E4M3 scales):
+// o[row_slot[r]][n] = bf16(acc * (scale * row_weight[r])).
+template <int OP, int NS, int MT>
 __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
                                                      const int32_t* __restrict__ expert_off,
                                                      const int32_t* __restrict__ row_slot,
@@ -752,25 +788,32 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__
                                                      const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s,
                                                      const uint8_t* __restrict__ pk, int64_t pk_estride,
                                                      uint16_t* __restrict__ o) {
-  __shared__ RoutedLds L;
+  __shared__ RoutedLds<MT> L;
   const int e = blockIdx.y;
   const int base = expert_off[e], rows = expert_off[e + 1] - base;
   if (rows <= 0) return;
   const float scale = scale_ptr != nullptr ? *scale_ptr : scale_val;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * MT;
   const int64_t kb = I / 2, ks = I / 32;
   const int64_t we = (int64_t)e * H * kb, se = (int64_t)e * H * ks;
-  const WTile wp = pk != nullptr ? wtile_l2_packed(pk + e * pk_estride, I, n0)
-                                 : wtile_rows(w2 + we + n0 * kb, w2 + we + (n0 + 8) * kb, kb);
-  const RowPair sp{w2s + se + n0 * ks, w2s + se + (n0 + 8) * ks};
-  routed_tile_rows<OP, NS>(hq, hs, nullptr, base, rows, I, wp, sp, L, [&](int c0, const f32x4& acc) {
+  auto wtile = [&](int t) {
+    const int n = n0 + 16 * t;
+    return pk != nullptr ? wtile_l2_packed(pk + e * pk_estride, I, n)
+                         : wtile_rows(w2 + we + n * kb, w2 + we + (n + 8) * kb, kb);
+  };
+  auto srows = [&](int t) {
+    const int n = n0 + 16 * t;
+    return RowPair{w2s + se + n * ks, w2s + se + (n + 8) * ks};
+  };
+  routed_tile_rows<OP, NS, MT>(hq, hs, nullptr, base, rows, I, wtile, srows, L,
+                               [&](int c0, int tile, const f32x4& acc) {
     const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
     if (c0 + t < rows) {
       const int r = base + c0 + t;
       const float wgt = scale * row_weight[r];
       const uint32_t p0 = bf16x2_rne(acc[0] * wgt, acc[1] * wgt);
       const uint32_t p1 = bf16x2_rne(acc[2] * wgt, acc[3] * wgt);
-      *(uint2*)(o + (int64_t)row_slot[r] * H + n0 + 4 * q) = make_uint2(p0, p1);
+      *(uint2*)(o + (int64_t)row_slot[r] * H + n0 + 16 * tile + 4 * q) = make_uint2(p0, p1);
     }
   });
 }
@@ -883,17 +926,29 @@ void launch_skinny_l2_ns(const DecodeArgs& a, const uint8_t* hq, const uint8_t* 
   }
 }
 
+// Weight tiles per workgroup of the routed kernels: two. The token operand of
+// a step is loaded once for both, and the NVFP4 L2 converts it to bf16 once
+// for both (it does so in every workgroup of the expert). Measured on the
+// 8-token tail of the skewed batch (28 experts of 7168 x 3072, hipGraph
+// replay), one / two / four tiles: NVFP4 277 / 242 / 252 us (four take 163
+// VGPRs, one workgroup per CU); at 72 tokens 575 / 458 us with two tiles in
+// both kernels. Hidden and intermediate sizes are multiples of 128, so 8 and
+// 16 RT_TILES divide them.
+constexpr int RT_TILES = 2;
+
 template <int NS>
 void launch_routed_l1_ns(const RoutedArgs& a, hipStream_t s) {
-  k_routed_l1<NS><<<dim3(a.I / 8, a.E), DT, 0, s>>>(a.xq, a.xs, a.row_token, a.expert_off, a.H, a.I, a.w1, a.w1s,
-                                                      a.w3, a.w3s, a.pk1, a.pk1_estride, a.h);
+  constexpr int MT = RT_TILES;
+  k_routed_l1<NS, MT><<<dim3(a.I / (8 * MT), a.E), DT, 0, s>>>(a.xq, a.xs, a.row_token, a.expert_off, a.H, a.I, a.w1,
+                                                               a.w1s, a.w3, a.w3s, a.pk1, a.pk1_estride, a.h);
 }
 
 template <int OP, int NS>
 void launch_routed_l2_ns(const RoutedArgs& a, hipStream_t s) {
-  k_routed_l2<OP, NS><<<dim3(a.H / 16, a.E), DT, 0, s>>>(a.hq, a.hs, a.expert_off, a.row_slot, a.row_weight,
-                                                          a.scale, a.scale_ptr, a.H, a.I, a.w2, a.w2s, a.pk2,
-                                                          a.pk2_estride, a.o);
+  constexpr int MT = RT_TILES;
+  k_routed_l2<OP, NS, MT><<<dim3(a.H / (16 * MT), a.E), DT, 0, s>>>(a.hq, a.hs, a.expert_off, a.row_slot,
+                                                                    a.row_weight, a.scale, a.scale_ptr, a.H, a.I,
+                                                                    a.w2, a.w2s, a.pk2, a.pk2_estride, a.o);
 }
 
 template <int OP>
@@ -975,19 +1030,19 @@ hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8
 // instead of the tiled GEMMs. Each workgroup reads all rows of its expert, so
 // their load instructions and MFMAs grow with the rows, while the GEMMs' time
 // at this size hardly depends on them. Measured over 48 experts of 7168 x 3072
-// (hipGraph replay, uniform top-8): with MXFP4 re-quantisation the two paths
-// meet near 2 rows per expert (8 tokens: 331 against 344 us, 16 tokens: 406
-// against 395 us); with NVFP4, whose GEMM L2 converts both operands to bf16
-// per tile, near 13 (8 tokens: 390 against 589 us, 64 tokens: 641 against
-// 715 us, 96 tokens: 762 against 719 us).
+// (hipGraph replay, uniform top-8), streaming against GEMMs: with MXFP4
+// re-quantisation 245 / 305 / 366 / 388 against 276 / 308 / 365 / 366 us at
+// 8 / 16 / 32 / 48 tokens; with NVFP4, whose GEMM L2 converts both operands
+// to bf16 per tile, 284 / 433 / 604 / 739 against 511 / 694 / 699 / 704 us at
+// 8 / 64 / 128 / 192 tokens.
 constexpr int64_t RT_MAX_MEAN_ROWS_MXFP4 = 2;
-constexpr int64_t RT_MAX_MEAN_ROWS_NVFP4 = 12;
+constexpr int64_t RT_MAX_MEAN_ROWS_NVFP4 = 24;
 
 bool routed_stream_fits(int64_t T, int64_t hidden, int64_t inter, int k, int E, bool nvfp4) {
   const int64_t mean_rows = nvfp4 ? RT_MAX_MEAN_ROWS_NVFP4 : RT_MAX_MEAN_ROWS_MXFP4;
   if (T < 1 || T * (int64_t)k > mean_rows * E) return false;
   if (hidden > DW * MAX_STEPS * 128 || inter > DW * MAX_STEPS * 128) return false;
-  if (inter % 8 != 0 || hidden % 16 != 0) return false;
+  if (inter % 128 != 0 || hidden % 128 != 0) return false;
   return 16 * (hidden / 32) <= 8 * DT && 16 * (inter / 32) <= 8 * DT;
 }
 
