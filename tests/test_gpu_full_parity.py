@@ -4,7 +4,9 @@ re-quantised intermediate of every one of its 32768 (token, expert) pairs; all
 4096 rows of the shared expert's prefill; the skewed 16384-token batch's heaviest
 expert and an expert whose last m-tile is partial, pair by pair, in both
 re-quantisation formats; a routed batch at hidden 1024 (more K stages than the
-copy prologue) with experts of more than 256 rows, compared in full.
+copy prologue) with experts of more than 256 rows, compared in full; the
+most tokens the routed weight-streaming kernels take with NVFP4 re-quantisation
+at the real shape, compared in full.
 
 The pages ask for a standalone test of the pipeline against a reference before
 anything else (page "Current Bug: vLLM produces empty/garbage output", section
@@ -164,3 +166,30 @@ def test_routed_hidden_1024_full(mx, requant):
                                       intermediates=True)
     assert_mlp_close(y, ref)
     _check_requant_all_pairs(d, sl, inter, requant, g)
+
+
+@pytest.mark.timeout(600)
+def test_routed_stream_nvfp4_most_tokens_real_shape(mx):
+    """The most tokens the routed weight-streaming kernels take with NVFP4
+    re-quantisation (T k = 24 E: 144 tokens of the uniform 48-expert batch,
+    top-8, hidden 7168, intermediate 3072), with expert 0 given 40+ rows (three
+    16-row chunks); the whole output against the oracle."""
+    full = W.grouped(tokens=4096, n_experts=48, k=8, seed=0)
+    T, E, k = 144, 48, 8
+    d = dict(full, x=full["x"][:T], ids=full["ids"][:T].copy(), w=full["w"][:T])
+    for i in range(48):
+        if not (d["ids"][i] == 0).any():
+            d["ids"][i, k - 1] = 0
+    counts = np.bincount(d["ids"].ravel(), minlength=E)
+    assert T * k == 24 * E and counts[0] > 32
+    g = _warmup_pairs(d, np.arange(T))
+    wd = [t(d[n]) for n in WN]
+    pk = mx.pack_weight_scales(wd[1], wd[3], wd[5])
+    pc = mx.pack_weight_codes(wd[0], wd[2], wd[4])
+    H, I = d["x"].shape[1], d["w1"].shape[1]
+    ws = torch.empty(mx.grouped_expert_mlp_workspace_size(T, H, I, k, E, "nvfp4"), dtype=torch.uint8, device="cuda")
+    y = mx.grouped_expert_mlp(bf16_t(d["x"]), t(d["ids"]), t(d["w"]), *wd, requant="nvfp4", requant_global=g,
+                              workspace=ws, packed_scales=pk, packed_codes=pc)
+    torch.cuda.synchronize()
+    ref = O.grouped_expert_mlp(d["x"], d["ids"], d["w"], *(d[n] for n in WN), requant="nvfp4", nv_global=g)
+    assert_mlp_close(bits(y), ref)
