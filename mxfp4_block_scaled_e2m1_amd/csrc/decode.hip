@@ -627,8 +627,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 // operand of a step is loaded (and, for RT_NV, converted to bf16) once and
 // serves all MT tiles. `emit(c0, t, tot)` runs in wave t (MT <= DW) for every
 // chunk of 16 rows starting at c0, with lane (row c0 + lane%16, rows
-// 4*(lane/16) + v of tile t).
-template <int OP, int NS, int MT, class WTiles, class SRows, class Emit>
+// 4*(lane/16) + v of tile t). EVEN: K / 128 = DW NS, every wave's run is NS
+// steps (no step to zero).
+template <int OP, int NS, int MT, bool EVEN, class WTiles, class SRows, class Emit>
 __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as,
                                                  const int32_t* __restrict__ gather,
                                                  int base, int rows, int K, WTiles wtile, SRows srows,
@@ -661,8 +662,9 @@ __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq,
 
   for (int c0 = 0; c0 < rows; c0 += 16) {
     const int i = min(c0 + r16, rows - 1);
+    // rows past the expert's (the last chunk's padding) re-read its last row:
+    // they feed only their own output columns, which emit does not write
     const int64_t tok = gather != nullptr ? (int64_t)gather[base + i] : (int64_t)(base + i);
-    const bool tok_ok = c0 + r16 < rows;
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     f32x4 acc[MT];
 #pragma unroll
@@ -680,11 +682,10 @@ __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq,
       // around the MFMAs
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
-        const uint4 bz = tok_ok ? b[k] : z;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const uint4 az = k < n ? wa[t][k] : z;
-          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(bz), acc[t], 4, 4, 0, sa[t][k],
+          const uint4 az = EVEN || k < n ? wa[t][k] : z;
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(az), opnd(b[k]), acc[t], 4, 4, 0, sa[t][k],
                                                                      0, sb[k]);
         }
       }
@@ -707,11 +708,11 @@ __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq,
         const float hs0 = e4m3_to_f32(bs[k] & 0xFFu), hs1 = e4m3_to_f32(bs[k] >> 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint4 bv = tok_ok ? nv8_bf16(hv[j], j < 2 ? hs0 : hs1) : z;
+          const uint4 bv = nv8_bf16(hv[j], j < 2 ? hs0 : hs1);
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
             const uint32_t wv[4] = {wa[t][k].x, wa[t][k].y, wa[t][k].z, wa[t][k].w};
-            const uint4 av = k < n ? dequant16_bf16(wv[j], e8m0_to_f32((uint32_t)sa[t][k])) : z;
+            const uint4 av = EVEN || k < n ? dequant16_bf16(wv[j], e8m0_to_f32((uint32_t)sa[t][k])) : z;
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                              __builtin_bit_cast(bf16x8_t, bv), acc[t], 0, 0, 0);
           }
@@ -738,7 +739,7 @@ __device__ __forceinline__ void routed_tile_rows(const uint8_t* __restrict__ aq,
 // L1 of expert blockIdx.y for 8 MT intermediate columns from j0 (tile t: rows
 // 0..7 of w1 and 8..15 of w3 for columns j0 + 8 t ..): h[r][j] =
 // bf16(silu(g) * u) for its sorted rows r.
-template <int NS, int MT>
+template <int NS, int MT, bool EVEN>
 __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                      const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ expert_off, int H, int I,
@@ -762,7 +763,7 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__
     const int j = j0 + 8 * t;
     return RowPair{w1s + se + j * ks, w3s + se + j * ks};
   };
-  routed_tile_rows<RT_FP4, NS, MT>(xq, xs, row_token, base, rows, H, wtile, srows, L,
+  routed_tile_rows<RT_FP4, NS, MT, EVEN>(xq, xs, row_token, base, rows, H, wtile, srows, L,
                                    [&](int c0, int tile, const f32x4& acc) {
     const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
     float up[4];
@@ -779,7 +780,7 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l1(const uint8_t* __restrict__
 // L2 of expert blockIdx.y for 16 MT output columns from n0 (tile t: n0 + 16 t
 // ..), from the re-quantised h rows (FP4 codes + E8M0 or E4M3 scales):
 // o[row_slot[r]][n] = bf16(acc * (scale * row_weight[r])).
-template <int OP, int NS, int MT>
+template <int OP, int NS, int MT, bool EVEN>
 __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
                                                      const int32_t* __restrict__ expert_off,
                                                      const int32_t* __restrict__ row_slot,
@@ -805,7 +806,7 @@ __global__ __launch_bounds__(DT, 1) void k_routed_l2(const uint8_t* __restrict__
     const int n = n0 + 16 * t;
     return RowPair{w2s + se + n * ks, w2s + se + (n + 8) * ks};
   };
-  routed_tile_rows<OP, NS, MT>(hq, hs, nullptr, base, rows, I, wtile, srows, L,
+  routed_tile_rows<OP, NS, MT, EVEN>(hq, hs, nullptr, base, rows, I, wtile, srows, L,
                                [&](int c0, int tile, const f32x4& acc) {
     const int lane = threadIdx.x & 63, t = lane & 15, q = lane >> 4;
     if (c0 + t < rows) {
@@ -939,16 +940,30 @@ constexpr int RT_TILES = 2;
 template <int NS>
 void launch_routed_l1_ns(const RoutedArgs& a, hipStream_t s) {
   constexpr int MT = RT_TILES;
-  k_routed_l1<NS, MT><<<dim3(a.I / (8 * MT), a.E), DT, 0, s>>>(a.xq, a.xs, a.row_token, a.expert_off, a.H, a.I, a.w1,
-                                                               a.w1s, a.w3, a.w3s, a.pk1, a.pk1_estride, a.h);
+  const dim3 grid(a.I / (8 * MT), a.E);
+  if (a.H / 128 == DW * NS)
+    k_routed_l1<NS, MT, true><<<grid, DT, 0, s>>>(a.xq, a.xs, a.row_token, a.expert_off, a.H, a.I, a.w1, a.w1s,
+                                                  a.w3, a.w3s, a.pk1, a.pk1_estride, a.h);
+  else
+    k_routed_l1<NS, MT, false><<<grid, DT, 0, s>>>(a.xq, a.xs, a.row_token, a.expert_off, a.H, a.I, a.w1, a.w1s,
+                                                   a.w3, a.w3s, a.pk1, a.pk1_estride, a.h);
 }
 
 template <int OP, int NS>
 void launch_routed_l2_ns(const RoutedArgs& a, hipStream_t s) {
   constexpr int MT = RT_TILES;
-  k_routed_l2<OP, NS, MT><<<dim3(a.H / (16 * MT), a.E), DT, 0, s>>>(a.hq, a.hs, a.expert_off, a.row_slot,
-                                                                    a.row_weight, a.scale, a.scale_ptr, a.H, a.I,
-                                                                    a.w2, a.w2s, a.pk2, a.pk2_estride, a.o);
+  const dim3 grid(a.H / (16 * MT), a.E);
+  // the NVFP4 operand keeps the zero steps: without them the compiler hoists
+  // every conversion of the run (162 VGPRs, one workgroup per CU; the 8-token
+  // tail 246 -> 253 us); the FP4 one gains (MXFP4 tail 218.5 -> 214.6 us)
+  constexpr bool FP4 = OP == RT_FP4;
+  if (FP4 && a.I / 128 == DW * NS)
+    k_routed_l2<OP, NS, MT, FP4><<<grid, DT, 0, s>>>(a.hq, a.hs, a.expert_off, a.row_slot, a.row_weight, a.scale,
+                                                      a.scale_ptr, a.H, a.I, a.w2, a.w2s, a.pk2, a.pk2_estride, a.o);
+  else
+    k_routed_l2<OP, NS, MT, false><<<grid, DT, 0, s>>>(a.hq, a.hs, a.expert_off, a.row_slot, a.row_weight, a.scale,
+                                                       a.scale_ptr, a.H, a.I, a.w2, a.w2s, a.pk2, a.pk2_estride,
+                                                       a.o);
 }
 
 template <int OP>
