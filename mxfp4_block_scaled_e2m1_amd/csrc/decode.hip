@@ -1046,11 +1046,11 @@ hipError_t launch_decode_mlp(const uint16_t* x, int m, int H, int I, const uint8
 // their load instructions and MFMAs grow with the rows, while the GEMMs' time
 // at this size hardly depends on them. Measured over 48 experts of 7168 x 3072
 // (hipGraph replay, uniform top-8), streaming against GEMMs: with MXFP4
-// re-quantisation 245 / 305 / 366 / 388 against 276 / 308 / 365 / 366 us at
-// 8 / 16 / 32 / 48 tokens; with NVFP4, whose GEMM L2 converts both operands
-// to bf16 per tile, 284 / 433 / 604 / 739 against 511 / 694 / 699 / 704 us at
-// 8 / 64 / 128 / 192 tokens.
-constexpr int64_t RT_MAX_MEAN_ROWS_MXFP4 = 2;
+// re-quantisation 239 / 275 / 294 / 337 / 352 / 368 against 277 / 300 / 308 /
+// 362 / 364 / 366 us at 8 / 12 / 16 / 24 / 32 / 48 tokens; with NVFP4, whose
+// GEMM L2 converts both operands to bf16 per tile, 284 / 433 / 604 / 739
+// against 511 / 694 / 699 / 704 us at 8 / 64 / 128 / 192 tokens.
+constexpr int64_t RT_MAX_MEAN_ROWS_MXFP4 = 6;
 constexpr int64_t RT_MAX_MEAN_ROWS_NVFP4 = 24;
 
 bool routed_stream_fits(int64_t T, int64_t hidden, int64_t inter, int k, int E, bool nvfp4) {

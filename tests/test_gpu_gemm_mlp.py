@@ -326,7 +326,7 @@ def test_grouped_skewed_sampled_tokens(mx):
 # ---------------------------------------------------------------- tile-major weight scales
 # ---------------------------------------------------------------- routed, few rows per expert
 # The routed weight-streaming kernels run while T * k <= mean_rows * E:
-STREAM_MEAN_ROWS = {"mxfp4": 2, "nvfp4": 24}
+STREAM_MEAN_ROWS = {"mxfp4": 6, "nvfp4": 24}
 
 
 def _stream_ws_h(ws, T, H, I, k, E):
@@ -409,11 +409,11 @@ def test_grouped_stream_single_expert_equals_shared(mx):
     assert_mlp_close(yg, _oracle_grouped(g))
 
 
-@pytest.mark.parametrize("requant,T", [("mxfp4", 4), ("mxfp4", 5), ("nvfp4", 48), ("nvfp4", 49)])
+@pytest.mark.parametrize("requant,T", [("mxfp4", 12), ("mxfp4", 13), ("nvfp4", 48), ("nvfp4", 49)])
 def test_grouped_stream_threshold(mx, requant, T):
     """T * k = mean_rows * E runs the weight-streaming kernels, one token more the GEMMs."""
     d = W.grouped(tokens=T, n_experts=4, k=2, seed=8, hidden=384, inter=256)
-    assert (T * 2 <= STREAM_MEAN_ROWS[requant] * 4) == (T in (4, 48))
+    assert (T * 2 <= STREAM_MEAN_ROWS[requant] * 4) == (T in (12, 48))
     g = 0.0
     if requant == "nvfp4":
         h = [O.expert_mlp(d["x"], *(d[n][e] for n in WN), intermediates=True)[1]["h"] for e in range(4)]
